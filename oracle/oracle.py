@@ -1,0 +1,131 @@
+"""Test infrastructure only: Python side of the fp64 CPU oracle.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg import
+this module.  The GPU library never does, and nothing here imports the GPU
+library: the two share no code.
+
+``forward`` runs the token-by-token Kimi Delta Attention recurrence in
+``kda_oracle.c`` (decay the state per key channel, predict the value for the
+normalised key from the decayed state, write the scaled error along the key,
+read out with the normalised query; Kimi-K3 深度解析 blog, section 三, and the
+KDA paragraph of the 深入 Kimi-K3 thread for the in-kernel L2 normalisation and
+the per-channel decay).  Inputs are widened to float64 from whatever exact
+values the caller holds (for GPU parity: the very bf16/fp32 bytes the GPU
+consumed), so input quantisation never counts as error.
+
+Layouts follow the library's: q, k, v, g, o are ``[B, T, H, D]``; beta is
+``[B, T, H]``; h0 and hT are ``[B, H, Dk, Dv]`` (key channel = row).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "_kda_oracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the C oracle with gcc (always; cheap)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O3", "-std=c99", "-Wall", "-shared", "-fPIC", "-pthread",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.kda_oracle_run.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_double, dp, dp, dp,
+        ctypes.c_int]
+    lib.kda_oracle_run.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(x):
+    """Widen to a C-contiguous float64 numpy array (accepts torch tensors)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: widen exactly, then hand over
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def run_sequences(q, k, v, g, beta, scale, h0=None, eps=1e-6, threads=None):
+    """Sequence-major entry: q, k, g ``[N, T, Dk]``; v ``[N, T, Dv]``;
+    beta ``[N, T]``; h0 ``[N, Dk, Dv]`` or None.  Returns (o, hT)."""
+    q, k, v, g, beta, h0 = map(_f64, (q, k, v, g, beta, h0))
+    n, T, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (n, T, dk) and g.shape == (n, T, dk)
+    assert v.shape == (n, T, dv) and beta.shape == (n, T)
+    if h0 is not None:
+        assert h0.shape == (n, dk, dv)
+    o = np.zeros((n, T, dv), dtype=np.float64)
+    hT = np.zeros((n, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_run(
+        n, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        float(scale), float(eps), _ptr(h0), _ptr(o), _ptr(hT),
+        int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_run failed with {rc}")
+    return o, hT
+
+
+def forward(q, k, v, g, beta, scale, h0=None, eps=1e-6, threads=None):
+    """Library layout entry: q, k, v, g ``[B, T, H, D]``, beta ``[B, T, H]``,
+    h0 ``[B, H, Dk, Dv]`` or None.  Returns (o ``[B, T, H, Dv]``, hT)."""
+    q, k, v, g, beta, h0 = map(_f64, (q, k, v, g, beta, h0))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+
+    def seq(x):  # [B, T, H, D] -> [B*H, T, D]
+        return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(B * H, T, -1))
+
+    o, hT = run_sequences(
+        seq(q), seq(k), seq(v), seq(g),
+        np.ascontiguousarray(beta.transpose(0, 2, 1).reshape(B * H, T)),
+        scale, None if h0 is None else h0.reshape(B * H, dk, dv), eps, threads)
+    o = o.reshape(B, H, T, dv).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(o), hT.reshape(B, H, dk, dv)
+
+
+def step(q, k, v, g, beta, scale, S, eps=1e-6, threads=None):
+    """One decode step: q, k, v, g ``[B, H, D]``, beta ``[B, H]``,
+    S ``[B, H, Dk, Dv]``.  Returns (o ``[B, H, Dv]``, S_new)."""
+    q, k, v, g, beta, S = map(_f64, (q, k, v, g, beta, S))
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    o, hT = run_sequences(
+        q.reshape(B * H, 1, dk), k.reshape(B * H, 1, dk), v.reshape(B * H, 1, dv),
+        g.reshape(B * H, 1, dk), beta.reshape(B * H, 1), scale,
+        S.reshape(B * H, dk, dv), eps, threads)
+    return o.reshape(B, H, dv), hT.reshape(B, H, dk, dv)

@@ -1,0 +1,260 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test fixes the oracle to something the pages or plain mathematics state:
+a hand-derived worked example, the materialised product of per-token
+transition matrices, closed forms of special cases (orthonormal recall, beta=1
+exact recall, pure decay, pure read-out), structural invariants (chaining,
+normalisation invariance, linearity) and the state-size arithmetic quoted by
+the 深入 Kimi-K3 thread.  Everything here runs on the CPU.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle, transition_product as tp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_case(rng, B, T, H, dk, dv, g_shift=4.0, with_h0=True):
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    g = -5.0 / (1.0 + np.exp(-(rng.standard_normal((B, T, H, dk)) - g_shift)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    h0 = rng.standard_normal((B, H, dk, dv)) * 0.1 if with_h0 else None
+    return q, k, v, g, beta, h0
+
+
+def _rel(a, b):
+    den = np.abs(b).max()
+    return np.abs(a - b).max() / (den if den > 0 else 1.0)
+
+
+def test_golden_hand_example():
+    """Hand-derived two-token example; catches decay on the wrong side, a
+    prediction from the undecayed state, a read-out before the write and a
+    dropped beta (each changes the printed numbers)."""
+    with open(os.path.join(GOLDEN, "kda_tiny_hand.json")) as f:
+        case = json.load(f)
+    arr = lambda key: np.array(case[key], dtype=np.float64)
+    q, k, v, g = (arr(x)[None, :, None, :] for x in ("q", "k", "v", "g"))
+    beta = arr("beta")[None, :, None]
+    o, hT = oracle.forward(q, k, v, g, beta, case["scale"], eps=case["eps"], threads=1)
+    np.testing.assert_allclose(o[0, :, 0], arr("o"), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(hT[0, 0], arr("hT"), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("dk,dv,T", [(4, 3, 1), (8, 8, 5), (16, 12, 8), (128, 128, 6)])
+def test_transition_product(dk, dv, T):
+    """P1: the oracle equals the product of materialised per-token matrices
+    M_t = (I - beta kh kh^T) Diag(exp g) applied to h0 plus the injections."""
+    rng = np.random.default_rng(100 + dk + T)
+    q, k, v, g, beta, h0 = _rand_case(rng, 1, T, 1, dk, dv)
+    o, hT = oracle.forward(q, k, v, g, beta, 0.37, h0, threads=1)
+    o2, hT2 = tp.run(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0],
+                     0.37, h0[0, 0])
+    assert _rel(o[0, :, 0], o2) < 1e-12
+    assert _rel(hT[0, 0], hT2) < 1e-12
+
+
+def test_transition_product_at_bound():
+    """P1 with the decay at its lower bound (g = -5) and at 0, alternating."""
+    rng = np.random.default_rng(7)
+    T, d = 8, 32
+    q, k, v, _, beta, h0 = _rand_case(rng, 1, T, 1, d, d)
+    g = np.where((np.arange(T)[:, None] + np.arange(d)[None, :]) % 2 == 0, -5.0, 0.0)
+    g = g[None, :, None, :]
+    o, hT = oracle.forward(q, k, v, g, beta, 1.0, h0, threads=1)
+    o2, hT2 = tp.run(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0],
+                     1.0, h0[0, 0])
+    assert _rel(o[0, :, 0], o2) < 1e-12
+    assert _rel(hT[0, 0], hT2) < 1e-12
+
+
+def _signed_basis_keys(rng, T, d):
+    perm = rng.permutation(d)[:T]
+    sign = rng.choice([-1.0, 1.0], size=T)
+    keys = np.zeros((T, d))
+    keys[np.arange(T), perm] = sign * rng.uniform(0.5, 3.0, size=T)  # any length
+    return keys
+
+
+def _hadamard(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+@pytest.mark.parametrize("kind", ["basis", "hadamard"])
+def test_orthonormal_recall(kind):
+    """P2: with g = 0, beta = 1, h0 = 0 and mutually orthogonal keys the
+    recurrence is plain linear attention over a key-value memory: a query equal
+    to an earlier key returns scale * its value, and hT^T kh_j = v_j."""
+    rng = np.random.default_rng(11)
+    d, T = 64, 48
+    if kind == "basis":
+        keys = _signed_basis_keys(rng, T, d)
+    else:
+        keys = _hadamard(d)[rng.permutation(d)[:T]] * rng.uniform(0.5, 2.0, (T, 1))
+    v = rng.standard_normal((T, d))
+    pick = np.array([rng.integers(0, t + 1) for t in range(T)])
+    q = keys[pick] * rng.uniform(0.2, 4.0, (T, 1))
+    g = np.zeros((T, d))
+    beta = np.ones(T)
+    scale = 0.125
+    o, hT = oracle.forward(q[None, :, None], keys[None, :, None], v[None, :, None],
+                           g[None, :, None], beta[None, :, None], scale, eps=0.0, threads=1)
+    np.testing.assert_allclose(o[0, :, 0], scale * v[pick], rtol=0, atol=1e-13)
+    kh = keys / np.linalg.norm(keys, axis=1, keepdims=True)
+    np.testing.assert_allclose(kh @ hT[0, 0], v, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("gmode", ["random", "bound", "zero"])
+def test_beta_one_exact_recall(gmode):
+    """P3: with beta = 1 every write makes S_t^T kh_t = v_t exactly, whatever
+    the decay; with q_t = k_t the read-out is scale * v_t at every t."""
+    rng = np.random.default_rng(12)
+    T, d = 300, 128
+    q, k, v, g, _, h0 = _rand_case(rng, 1, T, 1, d, d)
+    if gmode == "bound":
+        g = np.full_like(g, -5.0)
+    elif gmode == "zero":
+        g = np.zeros_like(g)
+    beta = np.ones((1, T, 1))
+    o, _ = oracle.forward(k, k, v, g, beta, 0.25, h0, eps=0.0, threads=1)
+    np.testing.assert_allclose(o, 0.25 * v, rtol=0, atol=1e-12)
+
+
+def test_beta_zero_pure_decay():
+    """P4: with beta = 0 nothing is written: S_t = Diag(exp(sum_{s<=t} g_s)) h0
+    (decay on key rows) and o_t = scale S_t^T qh_t."""
+    rng = np.random.default_rng(13)
+    B, T, H, dk, dv = 2, 40, 3, 16, 8
+    q, k, v, g, _, h0 = _rand_case(rng, B, T, H, dk, dv)
+    beta = np.zeros((B, T, H))
+    eps = 1e-6
+    o, hT = oracle.forward(q, k, v, g, beta, 0.5, h0, eps=eps, threads=2)
+    G = np.cumsum(g, axis=1)  # [B, T, H, dk]
+    qh = q / np.sqrt((q * q).sum(-1, keepdims=True) + eps)
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                St = np.exp(G[b, t, h])[:, None] * h0[b, h]
+                np.testing.assert_allclose(o[b, t, h], 0.5 * St.T @ qh[b, t, h],
+                                           rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(hT[b, h], np.exp(G[b, -1, h])[:, None] * h0[b, h],
+                                       rtol=1e-12, atol=1e-300)
+    o0, hT0 = oracle.forward(q, k, v, g, beta, 0.5, None, threads=2)
+    assert not o0.any() and not hT0.any()
+
+
+def test_read_only():
+    """P5: g = 0 and beta = 0 leave the state alone: o_t = scale h0^T qh_t."""
+    rng = np.random.default_rng(14)
+    B, T, H, dk, dv = 1, 20, 2, 32, 24
+    q, k, v, _, _, h0 = _rand_case(rng, B, T, H, dk, dv)
+    g = np.zeros((B, T, H, dk))
+    beta = np.zeros((B, T, H))
+    o, hT = oracle.forward(q, k, v, g, beta, 0.3, h0, eps=0.0, threads=1)
+    qh = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    want = 0.3 * np.einsum("bthi,bhij->bthj", qh, h0)
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(hT, h0)
+
+
+def test_state_size_invariants():
+    """P6: the thread's figures for 69 KDA layers of 96 heads with 128x128
+    fp32 states: about 1.09e8 values and about 434 MB per sequence, whatever
+    the context length.  The oracle's final state has that per-layer shape for
+    any T."""
+    layers, heads, d = 69, 96, 128
+    values = layers * heads * d * d
+    assert values == 108_527_616 and round(values / 1e8, 2) == 1.09
+    assert values * 4 == 434_110_464 and round(values * 4 / 1e6) == 434
+    rng = np.random.default_rng(15)
+    for T in (1, 7, 33):
+        q, k, v, g, beta, _ = _rand_case(rng, 1, T, 2, d, d, with_h0=False)
+        _, hT = oracle.forward(q, k, v, g, beta, 1.0, threads=2)
+        assert hT.shape == (1, 2, d, d)
+
+
+def test_chaining_is_exact():
+    """P7: running T1 tokens, then T2 tokens from the carried state, gives the
+    same outputs and final state as one run over T1 + T2 tokens."""
+    rng = np.random.default_rng(16)
+    B, T, H, d = 1, 50, 2, 32
+    q, k, v, g, beta, h0 = _rand_case(rng, B, T, H, d, d)
+    o, hT = oracle.forward(q, k, v, g, beta, 0.2, h0, threads=2)
+    s = 23
+    oa, ha = oracle.forward(q[:, :s], k[:, :s], v[:, :s], g[:, :s], beta[:, :s], 0.2, h0)
+    ob, hb = oracle.forward(q[:, s:], k[:, s:], v[:, s:], g[:, s:], beta[:, s:], 0.2, ha)
+    np.testing.assert_array_equal(np.concatenate([oa, ob], axis=1), o)
+    np.testing.assert_array_equal(hb, hT)
+
+
+def test_norm_invariance():
+    """P9: q and k are L2-normalised inside the operation, so positive scalings
+    of them (per token) change nothing (exactly so at eps = 0)."""
+    rng = np.random.default_rng(17)
+    B, T, H, d = 1, 30, 2, 16
+    q, k, v, g, beta, h0 = _rand_case(rng, B, T, H, d, d)
+    cq = rng.uniform(0.1, 10.0, (B, T, H, 1))
+    ck = rng.uniform(0.1, 10.0, (B, T, H, 1))
+    o, hT = oracle.forward(q, k, v, g, beta, 1.0, h0, eps=0.0, threads=1)
+    o2, hT2 = oracle.forward(q * cq, k * ck, v, g, beta, 1.0, h0, eps=0.0, threads=1)
+    assert _rel(o2, o) < 1e-13 and _rel(hT2, hT) < 1e-13
+
+
+def test_linearity_in_values_and_state():
+    """P10: for fixed q, k, g, beta the map (V, h0) -> (O, hT) is linear, and
+    value column j only ever touches column j."""
+    rng = np.random.default_rng(18)
+    B, T, H, d = 1, 40, 1, 16
+    q, k, v1, g, beta, h1 = _rand_case(rng, B, T, H, d, d)
+    v2 = rng.standard_normal(v1.shape)
+    h2 = rng.standard_normal(h1.shape)
+    a, b = 0.7, -1.3
+    o1, s1 = oracle.forward(q, k, v1, g, beta, 1.0, h1, threads=1)
+    o2, s2 = oracle.forward(q, k, v2, g, beta, 1.0, h2, threads=1)
+    o3, s3 = oracle.forward(q, k, a * v1 + b * v2, g, beta, 1.0, a * h1 + b * h2, threads=1)
+    assert _rel(o3, a * o1 + b * o2) < 1e-12 and _rel(s3, a * s1 + b * s2) < 1e-12
+    v4 = v1.copy()
+    v4[..., 5] += 1.0
+    o4, s4 = oracle.forward(q, k, v4, g, beta, 1.0, h1, threads=1)
+    cols = np.arange(d) != 5
+    np.testing.assert_array_equal(o4[..., cols], o1[..., cols])
+    np.testing.assert_array_equal(s4[..., cols], s1[..., cols])
+    assert np.abs(o4[..., 5] - o1[..., 5]).max() > 1e-3
+
+
+def test_contractive_transition():
+    """P14: for g <= 0, beta in [0, 2] and a unit key, the per-token
+    transition (I - beta kh kh^T) Diag(exp g) has spectral norm <= 1, so the
+    state grows by at most beta |v| per token and errors do not amplify."""
+    rng = np.random.default_rng(19)
+    d = 32
+    for _ in range(50):
+        k = rng.standard_normal((1, d))
+        g = -rng.uniform(0, 5, (1, d))
+        beta = rng.uniform(0, 2, 1)
+        Ms, _ = tp.transition_matrices(k, g, beta, eps=0.0)
+        assert np.linalg.norm(Ms[0], 2) <= 1.0 + 1e-12
+    q, k, v, g, beta, h0 = _rand_case(rng, 1, 1, 1, d, d)
+    _, hT = oracle.forward(q, k, v, g, beta, 1.0, h0, eps=0.0, threads=1)
+    bound = np.linalg.norm(h0[0, 0], 2) + beta[0, 0, 0] * np.linalg.norm(v[0, 0, 0])
+    assert np.linalg.norm(hT[0, 0], 2) <= bound + 1e-12
+
+
+def test_decode_step_matches_forward():
+    """One decode step is one token of the recurrence applied to S."""
+    rng = np.random.default_rng(20)
+    B, H, d = 3, 2, 16
+    q, k, v, g, beta, S = _rand_case(rng, B, 1, H, d, d)
+    o, hT = oracle.forward(q, k, v, g, beta, 0.9, S, threads=1)
+    o1, S1 = oracle.step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], 0.9, S, threads=1)
+    np.testing.assert_array_equal(o1, o[:, 0])
+    np.testing.assert_array_equal(S1, hT)
