@@ -1,0 +1,132 @@
+/*
+ * libkda: the Kimi Delta Attention (KDA) forward pass on AMD MI355X (gfx950).
+ *
+ * KDA is a gated delta-rule linear attention.  Per batch entry b and head h a
+ * 128 x 128 fp32 state S (row = key channel, column = value channel) evolves
+ * token by token:
+ *
+ *   qh = q_t / |q_t|,  kh = k_t / |k_t|          (L2 norm, eps 1e-6 under the
+ *                                                 square root, done inside)
+ *   S  = Diag(exp g_t) S                          (per-channel decay, g <= 0)
+ *   S += beta_t kh (v_t - S^T kh)^T               (delta-rule write)
+ *   o_t = scale S^T qh                            (read-out after the write)
+ *
+ * Sources: Kimi-K3 深度解析 (d7kj.com blog), section 三 "KDA 的关键改进" for the
+ * decay-then-correct recurrence and section 三 "Triton 实现" for the
+ * chunkwise prefill; 深入 Kimi-K3 (xitter thread), KDA paragraph, for the
+ * in-kernel q/k L2 normalisation, the per-channel decay with a -5 lower bound
+ * on its logarithm, 96 heads of dimension 128 and the context-independent
+ * state; Kimi K3 架构全景 page, section 02, for the two operations' names
+ * (chunk_kda for prefill, fused_recurrent_kda for decode).
+ *
+ * Conventions for every entry point
+ *   - d_k = d_v = 128 (KDA_HEAD_DIM), fixed.
+ *   - bf16 tensors are raw uint16_t bit patterns (round-to-nearest-even when
+ *     produced here).
+ *   - Every pointer is DEVICE memory owned by the caller.  The library never
+ *     frees, retains or reallocates a caller pointer after it returns.
+ *   - Work is enqueued on `stream` and the call returns without
+ *     synchronising.  A device fault surfaces at the caller's next sync.
+ *   - Offsets are 64-bit: B*T*H*128 may exceed 2^31.
+ *   - Precondition (documented, not checked): g lies in [-5, 0].  The chunked
+ *     path relies on the lower bound to keep its factorised decay in range;
+ *     it is the bound the pages give for the decay gate.
+ *   - Arguments are validated before any HIP call, so every
+ *     KDA_ERR_INVALID_ARG case is reported without touching a GPU.
+ *   - No exceptions cross the ABI; nothing is printed; nothing aborts.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+
+#if defined(__GNUC__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad scale */
+    KDA_ERR_UNSUPPORTED = 2, /* a size the library cannot index (e.g. T > 2^31-1) */
+    KDA_ERR_HIP = 3,         /* a HIP runtime call or launch failed */
+    KDA_ERR_NO_MEMORY = 4    /* internal workspace could not be allocated */
+} kda_status_t;
+
+/*
+ * kda_chunk_fwd — chunkwise-parallel prefill (the pages' chunk_kda).
+ *
+ *   q, k, v : [B, T, H, 128] bf16, row-major (channel fastest).
+ *   g       : [B, T, H, 128] fp32 log-decay per key channel, in [-5, 0].
+ *   beta    : [B, T, H] fp32, one scalar per token and head.
+ *   scale   : read-out scale (finite); multiplies o only, never the state.
+ *   h0      : [B, H, 128, 128] fp32 initial state (row = key channel), or
+ *             NULL for a zero state.
+ *   out     : [B, T, H, 128] bf16 output o.  Must not alias any input.
+ *   hT      : [B, H, 128, 128] fp32 final state, or NULL to skip it.  hT may
+ *             equal h0 (in-place carry of the state).
+ *
+ * Any T >= 0 is valid: T need not be a multiple of the internal chunk of 64
+ * tokens.  T == 0 writes hT = h0 (zeros if h0 is NULL).  B == 0 or H == 0 is
+ * a no-op.  Pointers must be 16-byte aligned.  The result equals the
+ * token-by-token recurrence above up to floating-point rounding: the chunk
+ * form is an exact rearrangement (UT/WY representation of the in-chunk
+ * triangular system, products on bf16 matrix cores with fp32 accumulation,
+ * state kept in fp32).  Internal workspace is taken from a library-owned,
+ * stream-ordered memory pool and is bounded by splitting T into segments.
+ */
+KDA_API kda_status_t kda_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const float *g, const float *beta, float scale,
+                           const float *h0, uint16_t *out, float *hT,
+                           int B, int T, int H, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_f32 — as kda_chunk_fwd, with fp32 q, k, v and out and fp32
+ * matrix-core products throughout (the fp32-input accuracy mode).
+ */
+KDA_API kda_status_t kda_chunk_fwd_f32(const float *q, const float *k, const float *v,
+                               const float *g, const float *beta, float scale,
+                               const float *h0, float *out, float *hT,
+                               int B, int T, int H, hipStream_t stream);
+
+/*
+ * kda_recurrent_step — one decode token over a maintained state (the pages'
+ * fused_recurrent_kda).  The state replaces a KV cache: its size does not
+ * depend on how many tokens came before.
+ *
+ *   q, k, v : [B, H, 128] bf16.
+ *   g       : [B, H, 128] fp32 in [-5, 0].
+ *   beta    : [B, H] fp32.
+ *   scale   : finite read-out scale.
+ *   S_inout : [B, H, 128, 128] fp32 state, updated in place.
+ *   out     : [B, H, 128] bf16.  Must not alias any input or the state.
+ *
+ * B == 0 or H == 0 is a no-op.  Pointers must be 16-byte aligned.
+ */
+KDA_API kda_status_t kda_recurrent_step(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *g, const float *beta, float scale,
+                                float *S_inout, uint16_t *out,
+                                int B, int H, hipStream_t stream);
+
+/* kda_recurrent_step_f32 — as kda_recurrent_step with fp32 q, k, v, out. */
+KDA_API kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float *v,
+                                    const float *g, const float *beta, float scale,
+                                    float *S_inout, float *out,
+                                    int B, int H, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+KDA_API const char *kda_status_string(kda_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,235 @@
+// The libkda C-ABI: argument validation, segmentation of long sequences,
+// workspace from a library-owned stream-ordered pool, and kernel launches.
+// Every KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED decision is taken before the
+// first HIP call, so it can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxBlocks = (int64_t)1 << 23;  // keeps blocks * threads < 2^32
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Workspace budget for one segment of the chunked path.  The default keeps
+// the per-segment records of a 96-head layer around a few hundred MB;
+// KDA_WORKSPACE_MB overrides it (read once).
+size_t workspace_budget() {
+    static size_t budget = [] {
+        size_t mb = 512;
+        if (const char* s = getenv("KDA_WORKSPACE_MB")) {
+            const long v = strtol(s, nullptr, 10);
+            if (v > 0) mb = (size_t)v;
+        }
+        return mb << 20;
+    }();
+    return budget;
+}
+
+// One memory pool per device, created on first use, that keeps freed blocks
+// cached so repeated calls do not go back to the driver.
+hipError_t pool_for_device(hipMemPool_t* pool) {
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        e = hipMemPoolCreate(&p, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) return e;
+        pools[dev] = p;
+    }
+    *pool = pools[dev];
+    return hipSuccess;
+}
+
+template <bool F32>
+kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float scale, const float* h0, void* out, float* hT,
+                       int B, int T, int H, hipStream_t stream) {
+    constexpr size_t es = F32 ? 4 : 2;
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    const size_t state_bytes = (size_t)B * H * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
+    if ((h0 && !aligned(h0, 16)) || (hT && !aligned(hT, 16))) return KDA_ERR_INVALID_ARG;
+    if (h0 && hT && h0 != hT && overlap(h0, state_bytes, hT, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+
+    if (T == 0) {
+        if (!hT || hT == h0) return KDA_OK;
+        const hipError_t e =
+            kda::launch_copy_or_zero(h0, hT, state_bytes / sizeof(float), stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(out, 16) || !aligned(beta, 4))
+        return KDA_ERR_INVALID_ARG;
+    const size_t n_tok = (size_t)B * T * H;
+    const size_t io_bytes = n_tok * KDA_HEAD_DIM * es;
+    const void* ins[] = {q, k, v};
+    for (const void* p : ins)
+        if (overlap(out, io_bytes, p, io_bytes)) return KDA_ERR_INVALID_ARG;
+    if (overlap(out, io_bytes, g, n_tok * KDA_HEAD_DIM * 4) ||
+        overlap(out, io_bytes, beta, n_tok * 4) || overlap(out, io_bytes, h0, state_bytes) ||
+        overlap(out, io_bytes, hT, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+
+    const int nch = (T + 63) / 64;
+    const size_t rec = kda::chunk_record_bytes(F32);
+    const size_t per_chunk = (size_t)B * H * rec;
+    int seg = (int)(workspace_budget() / per_chunk);
+    if (seg < 1) seg = 1;
+    if (seg > nch) seg = nch;
+    if ((int64_t)B * H * seg > kMaxBlocks) seg = (int)(kMaxBlocks / ((int64_t)B * H));
+    if (seg < 1) return KDA_ERR_UNSUPPORTED;
+    const bool multi = seg < nch;
+
+    hipMemPool_t pool = nullptr;
+    if (pool_for_device(&pool) != hipSuccess) return KDA_ERR_HIP;
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, per_chunk * seg, pool, stream) != hipSuccess)
+        return KDA_ERR_NO_MEMORY;
+    float* carry = nullptr;
+    if (multi) {
+        if (hipMallocFromPoolAsync((void**)&carry, state_bytes, pool, stream) != hipSuccess) {
+            (void)hipFreeAsync(ws, stream);
+            return KDA_ERR_NO_MEMORY;
+        }
+    }
+
+    kda_status_t st = KDA_OK;
+    for (int c0 = 0; c0 < nch; c0 += seg) {
+        const int n = (nch - c0 < seg) ? nch - c0 : seg;
+        const bool last = c0 + n >= nch;
+        if (kda::launch_chunk_prep<F32>(q, k, g, beta, B, T, H, c0, n, ws, stream) !=
+            hipSuccess) {
+            st = KDA_ERR_HIP;
+            break;
+        }
+        const float* h_in = (c0 == 0) ? h0 : carry;
+        float* h_out = last ? (hT ? hT : nullptr) : carry;
+        if (kda::launch_chunk_scan<F32>(ws, v, h_in, h_out, out, scale, B, T, H, c0, n, stream) !=
+            hipSuccess) {
+            st = KDA_ERR_HIP;
+            break;
+        }
+    }
+    if (carry) (void)hipFreeAsync(carry, stream);
+    (void)hipFreeAsync(ws, stream);
+    return st;
+}
+
+template <bool F32>
+kda_status_t recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, float scale, float* S, void* out, int B, int H,
+                            hipStream_t stream) {
+    constexpr size_t es = F32 ? 4 : 2;
+    if (B < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !S || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(S, 16) || !aligned(out, 16) || !aligned(beta, 4))
+        return KDA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const size_t nbh = (size_t)B * H;
+    const size_t vec = nbh * KDA_HEAD_DIM * es;
+    const size_t sbytes = nbh * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
+    const void* ins[] = {q, k, v};
+    for (const void* p : ins)
+        if (overlap(out, vec, p, vec) || overlap(S, sbytes, p, vec)) return KDA_ERR_INVALID_ARG;
+    if (overlap(out, vec, g, nbh * KDA_HEAD_DIM * 4) || overlap(out, vec, beta, nbh * 4) ||
+        overlap(out, vec, S, sbytes) || overlap(S, sbytes, g, nbh * KDA_HEAD_DIM * 4) ||
+        overlap(S, sbytes, beta, nbh * 4))
+        return KDA_ERR_INVALID_ARG;
+    const hipError_t e = kda::launch_decode<F32>(q, k, v, g, beta, scale, S, out, B, H, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+namespace kda {
+
+__global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                    size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream) {
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src,
+                       dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace kda
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* g, const float* beta, float scale, const float* h0,
+                           uint16_t* out, float* hT, int B, int T, int H, hipStream_t stream) {
+    return chunk_fwd<false>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream);
+}
+
+kda_status_t kda_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* g,
+                               const float* beta, float scale, const float* h0, float* out,
+                               float* hT, int B, int T, int H, hipStream_t stream) {
+    return chunk_fwd<true>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream);
+}
+
+kda_status_t kda_recurrent_step(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const float* g, const float* beta, float scale, float* S_inout,
+                                uint16_t* out, int B, int H, hipStream_t stream) {
+    return recurrent_step<false>(q, k, v, g, beta, scale, S_inout, out, B, H, stream);
+}
+
+kda_status_t kda_recurrent_step_f32(const float* q, const float* k, const float* v,
+                                    const float* g, const float* beta, float scale,
+                                    float* S_inout, float* out, int B, int H,
+                                    hipStream_t stream) {
+    return recurrent_step<true>(q, k, v, g, beta, scale, S_inout, out, B, H, stream);
+}
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK: success";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: size not supported";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime or launch error";
+        case KDA_ERR_NO_MEMORY: return "KDA_ERR_NO_MEMORY: workspace allocation failed";
+    }
+    return "KDA: unknown status";
+}
+
+}  // extern "C"

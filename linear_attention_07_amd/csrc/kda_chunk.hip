@@ -1,0 +1,682 @@
+// Chunkwise-parallel KDA prefill (the pages' chunk_kda).
+//
+// The recurrence (Kimi-K3 深度解析 blog, section 三) is evaluated 64 tokens at a
+// time.  The chunk form below is an exact rearrangement of it; the blog's
+// "Triton 实现" paragraph describes a chunked kernel with an inner-chunk part and
+// a cross-chunk part, and the ai-pulse-lab summary of the technical report
+// (architecture section) explains why the -5 lower bound on the log-decay is
+// what lets the diagonal blocks run as dense matrix-core products.
+//
+// For one (batch, head) and one chunk of tokens r = 0..63 entering with state S
+// (key channel x value channel), let Gam_r = sum_{s<=r} g_s (per channel), and
+//   Kt_r = exp(Gam_r) * kh_r       Qt_r = exp(Gam_r) * qh_r
+//   Kb_r = exp(Gam_63 - Gam_r) * kh_r,   gamma = exp(Gam_63)
+//   (KK)_ri = sum_c kh_rc kh_ic exp(Gam_rc - Gam_ic),  (QK)_ri likewise with qh_r
+//   A = strict-lower(diag(beta) KK),  M = lower-incl(QK)
+//   T = (I + A)^-1 diag(beta)                              (UT / WY form)
+//   W = T Kt,   Q' = Qt - M W,   MT = M T.
+// Token by token the errors u_r = beta_r (v_r - prediction_r) stack into
+//   U = T V - W S,
+//   O = scale (Qt S + M U) = scale (Q' S + MT V),
+//   S <- Diag(gamma) S + Kb^T U.
+//
+// Range of the decay factors.  exp(Gam_r - Gam_i) is formed as a product of a
+// row factor and a column factor about a reference token.  The reference for
+// the 16-token column block b is its last token e_b = 16b + 15:
+//   column factor exp(Gam_{e_b} - Gam_i) <= 1 for every i in block b,
+//   row factor    exp(Gam_r - Gam_{e_b}) <= 1 for r in a later block,
+//                 in [1, exp(75)] for r in block b itself (15 steps of at most
+//                 5 each): finite in fp32 and bf16 because g >= -5.
+// Values that underflow are bounded by the true (tiny) products.
+//
+// Precision.  Products whose result reaches the output directly use the exact
+// bf16 inputs or bf16 hi + lo pairs (about 16 mantissa bits): T and MT are kept
+// as hi/lo pairs, T V and MT V use the bf16 V exactly, U enters the state update
+// as hi + lo.  The in-chunk inverse is done in fp32.
+//
+// Two kernels:
+//   prep (one workgroup per chunk, fully parallel) computes W, Q', Kb^T, T, MT
+//        and gamma from q, k, g, beta and writes them to a per-chunk record;
+//   scan (one workgroup per head and 64 value columns) walks the chunks in
+//        order with its slice of S in registers, on matrix cores.
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <bool F32>
+struct Rec {
+    using st = typename Prec<F32>::st_t;
+    static constexpr size_t kLo = F32 ? 0 : 1;  // bf16 keeps lo parts of T, MT
+    static constexpr size_t W = 0;                                   // [64][128] W
+    static constexpr size_t QP = W + kChunk * kD * sizeof(st);       // [64][128] Q'
+    static constexpr size_t KT = QP + kChunk * kD * sizeof(st);      // [128][64] Kb^T
+    static constexpr size_t TH = KT + kD * kChunk * sizeof(st);      // [64][64]  T (hi)
+    static constexpr size_t TL = TH + kChunk * kChunk * sizeof(st);  // [64][64]  T lo
+    static constexpr size_t MH = TL + kLo * kChunk * kChunk * sizeof(st);  // MT (hi)
+    static constexpr size_t ML = MH + kChunk * kChunk * sizeof(st);  // MT lo
+    static constexpr size_t G = ML + kLo * kChunk * kChunk * sizeof(st);   // [128] gamma
+    static constexpr size_t BYTES = ((G + kD * sizeof(float)) + 255) / 256 * 256;
+};
+
+size_t chunk_record_bytes(bool f32) { return f32 ? Rec<true>::BYTES : Rec<false>::BYTES; }
+
+constexpr int kScanSlices = 2;          // value-column slices per head
+constexpr int kSliceCols = kD / kScanSlices;
+constexpr int kScanThreads = 64 * (kSliceCols / 16);
+int scan_slices() { return kScanSlices; }
+
+// k32 A-operand fragment of row `row` of a row-major matrix: values 0..3 carry
+// k = k0 + 4g + e, values 4..7 carry k = k0 + 16 + 4g + e.
+template <bool F32>
+__device__ __forceinline__ typename Prec<F32>::F8 frag_row(const typename Prec<F32>::st_t* base,
+                                                           int pitch, int row, int k0, int gq) {
+    typename Prec<F32>::F8 f;
+    const auto* p = base + (size_t)row * pitch + k0 + 4 * gq;
+    if constexpr (F32) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 16);
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    } else {
+        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+        const uint4 u = {a.x, a.y, b.x, b.y};
+        f.v = __builtin_bit_cast(bf16x8, u);
+    }
+    return f;
+}
+
+// k32 B-operand fragment of column `col` of a row-major [k][col] matrix, with
+// the same k order as frag_row.
+template <bool F32>
+__device__ __forceinline__ typename Prec<F32>::F8 frag_col(const typename Prec<F32>::st_t* base,
+                                                           int pitch, int col, int k0, int gq) {
+    typename Prec<F32>::F8 f;
+    const auto* p = base + (size_t)(k0 + 4 * gq) * pitch + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (F32) {
+            f.v[e] = p[(size_t)e * pitch];
+            f.v[4 + e] = p[(size_t)(16 + e) * pitch];
+        } else {
+            f.v[e] = __builtin_bit_cast(__bf16, p[(size_t)e * pitch]);
+            f.v[4 + e] = __builtin_bit_cast(__bf16, p[(size_t)(16 + e) * pitch]);
+        }
+    }
+    return f;
+}
+
+// acc += A B with A given in fp32 and split into bf16 hi + lo (two products);
+// in fp32 mode a single fp32 product.
+template <bool F32>
+__device__ __forceinline__ f32x4 mma16_split_a(f32x4 acc, f32x4 a, const typename Prec<F32>::F4& b) {
+    using P = Prec<F32>;
+    if constexpr (F32) {
+        return P::mma16(acc, P::pack4(a), b);
+    } else {
+        f32x4 hi, lo;
+        split_bf16(a, hi, lo);
+        acc = P::mma16(acc, P::pack4(hi), b);
+        return P::mma16(acc, P::pack4(lo), b);
+    }
+}
+
+// acc += A B with both operands split (three products: hi*hi + lo*hi + hi*lo).
+template <bool F32>
+__device__ __forceinline__ f32x4 mma16_split_ab(f32x4 acc, f32x4 a, f32x4 b) {
+    using P = Prec<F32>;
+    if constexpr (F32) {
+        return P::mma16(acc, P::pack4(a), P::pack4(b));
+    } else {
+        f32x4 ah, al, bh, bl;
+        split_bf16(a, ah, al);
+        split_bf16(b, bh, bl);
+        const auto fah = P::pack4(ah), fbh = P::pack4(bh);
+        acc = P::mma16(acc, fah, fbh);
+        acc = P::mma16(acc, P::pack4(al), fbh);
+        return P::mma16(acc, fah, P::pack4(bl));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prep: one workgroup = one chunk of one (b, h).  Wave a owns chunk rows
+// 16a..16a+15; lane (n = lane%16, g = lane/16) owns row 16a+n and the 32
+// channels 32s + 8g + e (s, e = 0..3, 0..7), i.e. exactly the A-operand
+// fragment of that row for the four k32 steps over the 128 channels.
+// ---------------------------------------------------------------------------
+template <bool F32>
+__global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
+    const typename Prec<F32>::io_t* __restrict__ q, const typename Prec<F32>::io_t* __restrict__ k,
+    const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int chunk0,
+    int nchunks, uint8_t* __restrict__ ws) {
+    using P = Prec<F32>;
+    using PF = Prec<true>;
+    using st = typename P::st_t;
+    using F8 = typename P::F8;
+    using R = Rec<F32>;
+
+    const int cl = blockIdx.x % nchunks;
+    const int bh = blockIdx.x / nchunks;
+    const int h = bh % H, b = bh / H;
+    const int c = chunk0 + cl;
+    const int L = min(kChunk, T - c * kChunk);
+    uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * R::BYTES;
+    st* Wg = reinterpret_cast<st*>(rec + R::W);
+    st* QPg = reinterpret_cast<st*>(rec + R::QP);
+    st* KTg = reinterpret_cast<st*>(rec + R::KT);
+    st* THg = reinterpret_cast<st*>(rec + R::TH);
+    st* TLg = reinterpret_cast<st*>(rec + R::TL);
+    st* MHg = reinterpret_cast<st*>(rec + R::MH);
+    st* MLg = reinterpret_cast<st*>(rec + R::ML);
+    float* Gg = reinterpret_cast<float*>(rec + R::G);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    const int r = 16 * wv + n;
+    const bool valid = r < L;
+    const int64_t tok = (int64_t)c * kChunk + r;
+    const int64_t rowoff = (((int64_t)b * T + tok) * H + h) * kD;
+
+    constexpr int FP = kD + 4;      // fp32 pitch of Kt / Qt rows
+    constexpr int SP = kChunk + 1;  // fp32 pitch of the 64 x 64 matrices
+    constexpr size_t kZfBytes = sizeof(F8) * 4 * 4 * 64;
+    constexpr size_t kXBytes = sizeof(float) * kChunk * SP;
+    __shared__ float tau_s[4][kD];
+    __shared__ float etau_s[4][kD];
+    __shared__ float beta_s[kChunk];
+    __shared__ float kt_s[kChunk * FP];
+    __shared__ float qt_s[kChunk * FP];
+    __shared__ float a_s[kChunk * SP];
+    __shared__ float m_s[kChunk * SP];
+    // the column operands of the decay-weighted products, later reused for
+    // X = (I + A)^-1 and then T = X diag(beta)
+    __shared__ __align__(16) uint8_t zx_raw[kZfBytes > kXBytes ? kZfBytes : kXBytes];
+    F8(*zf_s)[4][64] = reinterpret_cast<F8(*)[4][64]>(zx_raw);
+    float* x_s = reinterpret_cast<float*>(zx_raw);
+
+    // ---- load the lane's row: 32 channels of q, k, g -----------------------
+    float qf[32], kf[32], lam[32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cb = 32 * s + 8 * gq;
+        if (valid) {
+            load8(q + rowoff + cb, qf + 8 * s);
+            load8(k + rowoff + cb, kf + 8 * s);
+            load8(g + rowoff + cb, lam + 8 * s);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[8 * s + e] = kf[8 * s + e] = lam[8 * s + e] = 0.f;
+        }
+    }
+    const float bet = valid ? beta[((int64_t)b * T + tok) * H + h] : 0.f;
+
+    // ---- L2 normalisation of q and k (row spread over lanes n, n+16, +32, +48)
+    float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        ssq += qf[j] * qf[j];
+        ssk += kf[j] * kf[j];
+    }
+    ssq += __shfl_xor(ssq, 16);
+    ssk += __shfl_xor(ssk, 16);
+    ssq += __shfl_xor(ssq, 32);
+    ssk += __shfl_xor(ssk, 32);
+    const float iq = 1.0f / sqrtf(ssq + kNormEps), ik = 1.0f / sqrtf(ssk + kNormEps);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        qf[j] *= iq;
+        kf[j] *= ik;
+    }
+
+    // ---- in-block inclusive cumsum of g over the 16 rows (lanes of a DPP row)
+#pragma unroll
+    for (int j = 0; j < 32; ++j) lam[j] = row16_inclusive_scan(lam[j]);
+    if (n == 15) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) tau_s[wv][32 * (j >> 3) + 8 * gq + (j & 7)] = lam[j];
+    }
+    if (gq == 0) beta_s[r] = bet;
+    __syncthreads();
+
+    for (int idx = tid; idx < 4 * kD; idx += 256)
+        etau_s[idx >> 7][idx & 127] = fast_exp(tau_s[idx >> 7][idx & 127]);
+    if (tid < kD) Gg[tid] = fast_exp(tau_s[0][tid] + tau_s[1][tid] + tau_s[2][tid] + tau_s[3][tid]);
+    __syncthreads();
+
+    // ---- decay factors and the derived operands -----------------------------
+    // e0 = exp(Gam_r - Gam_{16a-1}) <= 1, e1 = exp(Gam_r - Gam_{e_a}) >= 1,
+    // z = exp(Gam_{e_a} - Gam_r) <= 1 (a = this wave's block)
+    float e0[32], e1[32];
+    {
+        float zc[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int ch = 32 * (j >> 3) + 8 * gq + (j & 7);
+            const float ta = tau_s[wv][ch];
+            e0[j] = fast_exp(lam[j]);
+            e1[j] = fast_exp(lam[j] - ta);
+            const float z = fast_exp(ta - lam[j]);
+            float ePa = 1.f, eKb = 1.f;
+#pragma unroll
+            for (int a2 = 0; a2 < 4; ++a2) {
+                if (a2 < wv) ePa *= etau_s[a2][ch];
+                if (a2 > wv) eKb *= etau_s[a2][ch];
+            }
+            zc[j] = kf[j] * z;
+            KTg[(size_t)ch * kChunk + r] = P::to_st(kf[j] * z * eKb);
+            const float g0 = e0[j] * ePa;
+            kt_s[r * FP + ch] = kf[j] * g0;
+            qt_s[r * FP + ch] = qf[j] * g0;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) zf_s[wv][s][lane] = P::pack8(zc + 8 * s);
+    }
+    __syncthreads();
+
+    // ---- (KK) and (QK) tiles of row block wv against column blocks b <= wv --
+    for (int cb = 0; cb <= wv; ++cb) {
+        float t[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int ch = 32 * (j >> 3) + 8 * gq + (j & 7);
+            if (cb == wv) {
+                t[j] = e1[j];
+            } else {
+                float f = e0[j];
+                for (int a2 = cb + 1; a2 < wv; ++a2) f *= etau_s[a2][ch];
+                t[j] = f;
+            }
+        }
+        f32x4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float rk[8], rq[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                rk[e] = kf[8 * s + e] * t[8 * s + e];
+                rq[e] = qf[8 * s + e] * t[8 * s + e];
+            }
+            const F8 fz = zf_s[cb][s][lane];
+            accK = P::mma32(accK, P::pack8(rk), fz);
+            accQ = P::mma32(accQ, P::pack8(rq), fz);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ri = 16 * wv + 4 * gq + e, ci = 16 * cb + n;
+            const bool strict = (cb < wv) || (ci < ri);
+            const bool incl = (cb < wv) || (ci <= ri);
+            a_s[ri * SP + ci] = strict ? beta_s[ri] * accK[e] : 0.f;
+            m_s[ri * SP + ci] = incl ? accQ[e] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- X = (I + A)^-1: diagonal blocks by forward substitution (fp32) ----
+    {
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float s = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < rr; ++cc) s += a_s[(16 * wv + rr) * SP + 16 * wv + cc] * x[cc];
+            x[rr] = (rr == n) ? 1.f : -s;
+        }
+        if (gq == 0) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) x_s[(16 * wv + rr) * SP + 16 * wv + n] = x[rr];
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance: X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
+    for (int d = 1; d < 4; ++d) {
+        if (wv >= d) {
+            const int a = wv, bb = wv - d;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int cc = bb; cc < a; ++cc) {
+                typename PF::F4 fa, fb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    fa.v[e] = a_s[(16 * a + n) * SP + 16 * cc + 4 * gq + e];
+                    fb.v[e] = x_s[(16 * cc + 4 * gq + e) * SP + 16 * bb + n];
+                }
+                acc = PF::mma16(acc, fa, fb);
+            }
+            typename PF::F4 fx;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fx.v[e] = x_s[(16 * a + n) * SP + 16 * a + 4 * gq + e];
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 xab = PF::mma16(zero, fx, PF::pack4(acc));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x_s[(16 * a + 4 * gq + e) * SP + 16 * bb + n] = -xab[e];
+        }
+        __syncthreads();
+    }
+    // T = X diag(beta), zero above the diagonal; write T (hi / lo)
+    for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
+        const int rr = idx >> 6, cc = idx & 63;
+        const float tv = (cc <= rr) ? x_s[rr * SP + cc] * beta_s[cc] : 0.f;
+        x_s[rr * SP + cc] = tv;
+        if constexpr (F32) {
+            THg[idx] = tv;
+        } else {
+            float hi, lo;
+            split_bf16(tv, hi, lo);
+            THg[idx] = f2bf(hi);
+            TLg[idx] = f2bf(lo);
+        }
+    }
+    __syncthreads();
+
+    // ---- W = T Kt and Q' = Qt - M W for channels [32 wv, 32 wv + 32) --------
+    {
+        f32x4 Wt[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = 32 * wv + 16 * ct + n;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= rt; ++kb) {
+                    f32x4 ta, kv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ta[e] = x_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
+                        kv[e] = kt_s[(16 * kb + 4 * gq + e) * FP + col];
+                    }
+                    acc = mma16_split_a<F32>(acc, ta, P::pack4(kv));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float wq = P::from_st(P::to_st(acc[e]));  // W as the scan sees it
+                    Wt[rt][ct][e] = wq;
+                    Wg[(size_t)(16 * rt + 4 * gq + e) * kD + col] = P::to_st(acc[e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = 32 * wv + 16 * ct + n;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= rt; ++kb) {
+                    f32x4 ma;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ma[e] = m_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
+                    acc = mma16_split_a<F32>(acc, ma, P::pack4(Wt[kb][ct]));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * rt + 4 * gq + e;
+                    QPg[(size_t)row * kD + col] = P::to_st(qt_s[row * FP + col] - acc[e]);
+                }
+            }
+        }
+    }
+
+    // ---- MT = M T, row block wv -------------------------------------------
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = ct; kb <= wv; ++kb) {
+            f32x4 ma, tb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ma[e] = m_s[(16 * wv + n) * SP + 16 * kb + 4 * gq + e];
+                tb[e] = x_s[(16 * kb + 4 * gq + e) * SP + 16 * ct + n];
+            }
+            acc = mma16_split_ab<F32>(acc, ma, tb);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t idx = (size_t)(16 * wv + 4 * gq + e) * kChunk + 16 * ct + n;
+            if constexpr (F32) {
+                MHg[idx] = acc[e];
+            } else {
+                float hi, lo;
+                split_bf16(acc[e], hi, lo);
+                MHg[idx] = f2bf(hi);
+                MLg[idx] = f2bf(lo);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan: one workgroup per (b, h, 64-column slice); wave w owns value columns
+// j0 = 64*slice + 16w .. +15 of the state, as eight 16x16 accumulator tiles
+// (key rows 16t + 4g + e, column j0 + n).  Chunks are visited in order.
+// k order of every k32 product here: values 0..3 of a lane carry k = k0 + 4g
+// + e, values 4..7 carry k = k0 + 16 + 4g + e, i.e. the rows of accumulator
+// tiles 2s and 2s+1 — so S and U feed the B operand straight from registers.
+// bf16 mode stages each chunk's record in LDS; fp32 mode (small problems
+// only) reads it from global memory directly.
+// ---------------------------------------------------------------------------
+template <bool F32>
+__global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
+    const uint8_t* __restrict__ ws, const typename Prec<F32>::io_t* __restrict__ v,
+    const float* h_in, float* h_out, typename Prec<F32>::io_t* __restrict__ out, float scale,
+    int T, int H, int chunk0, int nchunks) {
+    using P = Prec<F32>;
+    using st = typename P::st_t;
+    using F8 = typename P::F8;
+    using R = Rec<F32>;
+
+    const int slice = blockIdx.x % kScanSlices;
+    const int bh = blockIdx.x / kScanSlices;
+    const int h = bh % H, b = bh / H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    const int c0 = kSliceCols * slice;       // first value column of the slice
+    const int jl = 16 * wv + n;              // this lane's column within the slice
+    const int j0 = c0 + 16 * wv;
+
+    constexpr int AP = kD + 8;       // LDS pitch of W / Q' rows
+    constexpr int KP = kChunk + 8;   // LDS pitch of 64-wide rows
+    constexpr int VP = kSliceCols + 8;
+    constexpr int NL = F32 ? 1 : kChunk;  // LDS arrays only used in bf16 mode
+    __shared__ st w_s[NL * AP];
+    __shared__ st qp_s[NL * AP];
+    __shared__ st kt_s[(F32 ? 1 : kD) * KP];
+    __shared__ st th_s[NL * KP], tl_s[NL * KP], mh_s[NL * KP], ml_s[NL * KP];
+    __shared__ st v_s[kChunk * VP];
+    __shared__ float gam_s[kD];
+
+    f32x4 S[8];
+    const float* hin = h_in ? h_in + (size_t)bh * kD * kD : nullptr;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
+
+    for (int cl = 0; cl < nchunks; ++cl) {
+        const int c = chunk0 + cl;
+        const uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * R::BYTES;
+        const st *wp, *qpp, *ktp, *thp, *tlp, *mhp, *mlp;
+        int ap, kp;
+        __syncthreads();
+        if constexpr (F32) {
+            wp = reinterpret_cast<const st*>(rec + R::W);
+            qpp = reinterpret_cast<const st*>(rec + R::QP);
+            ktp = reinterpret_cast<const st*>(rec + R::KT);
+            thp = reinterpret_cast<const st*>(rec + R::TH);
+            tlp = thp;
+            mhp = reinterpret_cast<const st*>(rec + R::MH);
+            mlp = mhp;
+            ap = kD;
+            kp = kChunk;
+        } else {
+            // 16-byte vectors: 16 per 128-wide row, 8 per 64-wide row
+            const uint4* Wv = reinterpret_cast<const uint4*>(rec + R::W);
+            const uint4* Qv = reinterpret_cast<const uint4*>(rec + R::QP);
+            const uint4* Kv = reinterpret_cast<const uint4*>(rec + R::KT);
+            const uint4* THv = reinterpret_cast<const uint4*>(rec + R::TH);
+            const uint4* TLv = reinterpret_cast<const uint4*>(rec + R::TL);
+            const uint4* MHv = reinterpret_cast<const uint4*>(rec + R::MH);
+            const uint4* MLv = reinterpret_cast<const uint4*>(rec + R::ML);
+            for (int i = tid; i < kChunk * 16; i += kScanThreads) {
+                const int row = i >> 4, cv = i & 15;
+                *reinterpret_cast<uint4*>(&w_s[row * AP + cv * 8]) = Wv[i];
+                *reinterpret_cast<uint4*>(&qp_s[row * AP + cv * 8]) = Qv[i];
+            }
+            for (int i = tid; i < kD * 8; i += kScanThreads) {
+                const int row = i >> 3, cv = i & 7;
+                *reinterpret_cast<uint4*>(&kt_s[row * KP + cv * 8]) = Kv[i];
+            }
+            for (int i = tid; i < kChunk * 8; i += kScanThreads) {
+                const int row = i >> 3, cv = i & 7;
+                *reinterpret_cast<uint4*>(&th_s[row * KP + cv * 8]) = THv[i];
+                *reinterpret_cast<uint4*>(&tl_s[row * KP + cv * 8]) = TLv[i];
+                *reinterpret_cast<uint4*>(&mh_s[row * KP + cv * 8]) = MHv[i];
+                *reinterpret_cast<uint4*>(&ml_s[row * KP + cv * 8]) = MLv[i];
+            }
+            wp = w_s; qpp = qp_s; ktp = kt_s; thp = th_s; tlp = tl_s; mhp = mh_s; mlp = ml_s;
+            ap = AP;
+            kp = KP;
+        }
+        {
+            // V slice of this chunk (zero past the end of the sequence)
+            constexpr int EV = 16 / sizeof(st);
+            constexpr int VR = kSliceCols / EV;
+            for (int i = tid; i < kChunk * VR; i += kScanThreads) {
+                const int row = i / VR, cv = i % VR;
+                const int64_t tok = (int64_t)c * kChunk + row;
+                uint4 val = {0u, 0u, 0u, 0u};
+                if (tok < T)
+                    val = *reinterpret_cast<const uint4*>(
+                        v + (((int64_t)b * T + tok) * H + h) * kD + c0 + cv * EV);
+                *reinterpret_cast<uint4*>(&v_s[row * VP + cv * EV]) = val;
+            }
+        }
+        if (tid < kD) gam_s[tid] = reinterpret_cast<const float*>(rec + R::G)[tid];
+        __syncthreads();
+
+        // S-independent: Ut = T V and Oh = MT V for this wave's 16 columns
+        f32x4 Ut[4], Oh[4];
+        {
+            const F8 vb0 = frag_col<F32>(v_s, VP, jl, 0, gq);
+            const F8 vb1 = frag_col<F32>(v_s, VP, jl, 32, gq);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
+                const int row = 16 * rt + n;
+                u = P::mma32(u, frag_row<F32>(thp, kp, row, 0, gq), vb0);
+                o = P::mma32(o, frag_row<F32>(mhp, kp, row, 0, gq), vb0);
+                if constexpr (!F32) {
+                    u = P::mma32(u, frag_row<F32>(tlp, kp, row, 0, gq), vb0);
+                    o = P::mma32(o, frag_row<F32>(mlp, kp, row, 0, gq), vb0);
+                }
+                if (rt >= 2) {
+                    u = P::mma32(u, frag_row<F32>(thp, kp, row, 32, gq), vb1);
+                    o = P::mma32(o, frag_row<F32>(mhp, kp, row, 32, gq), vb1);
+                    if constexpr (!F32) {
+                        u = P::mma32(u, frag_row<F32>(tlp, kp, row, 32, gq), vb1);
+                        o = P::mma32(o, frag_row<F32>(mlp, kp, row, 32, gq), vb1);
+                    }
+                }
+                Ut[rt] = u;
+                Oh[rt] = o;
+            }
+        }
+
+        // Pm = [W; Q'] S   (8 row tiles of 16 tokens x this wave's 16 columns)
+        f32x4 Pm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Pm[i] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const F8 bS = P::pack8(S[2 * s], S[2 * s + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Pm[rt] = P::mma32(Pm[rt], frag_row<F32>(wp, ap, 16 * rt + n, 32 * s, gq), bS);
+                Pm[4 + rt] = P::mma32(Pm[4 + rt], frag_row<F32>(qpp, ap, 16 * rt + n, 32 * s, gq), bS);
+            }
+        }
+
+        // U = T V - W S ;  O = scale (Q' S + MT V)
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            U[rt] = Ut[rt] - Pm[rt];
+            const f32x4 o = Pm[4 + rt] + Oh[rt];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t tok = (int64_t)c * kChunk + 16 * rt + 4 * gq + e;
+                if (tok < T) out[(((int64_t)b * T + tok) * H + h) * kD + j0 + n] = P::to_io(scale * o[e]);
+            }
+        }
+
+        // S <- Diag(gamma) S + Kb^T U   (U as bf16 hi + lo in bf16 mode)
+        F8 bUh[2], bUl[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            if constexpr (F32) {
+                bUh[s2] = P::pack8(U[2 * s2], U[2 * s2 + 1]);
+            } else {
+                f32x4 h0v, l0v, h1v, l1v;
+                split_bf16(U[2 * s2], h0v, l0v);
+                split_bf16(U[2 * s2 + 1], h1v, l1v);
+                bUh[s2] = P::pack8(h0v, h1v);
+                bUl[s2] = P::pack8(l0v, l1v);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[t][e] *= gam_s[16 * t + 4 * gq + e];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const F8 fa = frag_row<F32>(ktp, kp, 16 * t + n, 32 * s2, gq);
+                S[t] = P::mma32(S[t], fa, bUh[s2]);
+                if constexpr (!F32) S[t] = P::mma32(S[t], fa, bUl[s2]);
+            }
+        }
+    }
+
+    if (h_out) {
+        float* ho = h_out + (size_t)bh * kD * kD;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
+    }
+}
+
+template <bool F32>
+hipError_t launch_chunk_prep(const void* q, const void* k, const float* g, const float* beta,
+                             int B, int T, int H, int chunk0, int nchunks, void* ws,
+                             hipStream_t stream) {
+    using io = typename Prec<F32>::io_t;
+    const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
+    hipLaunchKernelGGL(kda_chunk_prep_kernel<F32>, dim3(nblk), dim3(256), 0, stream,
+                       static_cast<const io*>(q), static_cast<const io*>(k), g, beta, T, H,
+                       chunk0, nchunks, static_cast<uint8_t*>(ws));
+    return hipGetLastError();
+}
+
+template <bool F32>
+hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, float* h_out,
+                             void* out, float scale, int B, int T, int H, int chunk0,
+                             int nchunks, hipStream_t stream) {
+    using io = typename Prec<F32>::io_t;
+    const unsigned nblk = (unsigned)((int64_t)B * H * kScanSlices);
+    hipLaunchKernelGGL(kda_chunk_scan_kernel<F32>, dim3(nblk), dim3(kScanThreads), 0, stream,
+                       static_cast<const uint8_t*>(ws), static_cast<const io*>(v), h_in, h_out,
+                       static_cast<io*>(out), scale, T, H, chunk0, nchunks);
+    return hipGetLastError();
+}
+
+template hipError_t launch_chunk_prep<false>(const void*, const void*, const float*, const float*,
+                                             int, int, int, int, int, void*, hipStream_t);
+template hipError_t launch_chunk_prep<true>(const void*, const void*, const float*, const float*,
+                                            int, int, int, int, int, void*, hipStream_t);
+template hipError_t launch_chunk_scan<false>(const void*, const void*, const float*, float*,
+                                             void*, float, int, int, int, int, int, hipStream_t);
+template hipError_t launch_chunk_scan<true>(const void*, const void*, const float*, float*,
+                                            void*, float, int, int, int, int, int, hipStream_t);
+
+}  // namespace kda

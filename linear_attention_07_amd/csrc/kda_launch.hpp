@@ -1,0 +1,42 @@
+// Internal host-side launch interface between the C-ABI layer (kda_api.hip)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Bytes of one per-(batch, head, chunk) record written by the chunk-prep
+// kernel and read by the chunk-scan kernel.
+size_t chunk_record_bytes(bool f32);
+
+// Number of value-column slices a head's state is split into by the scan
+// kernel (one workgroup per slice).
+int scan_slices();
+
+template <bool F32>
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, float* S, void* out,
+                         int B, int H, hipStream_t stream);
+
+// prep: per-chunk records (W, Q', Kb^T, T, MT, gamma) for chunks
+// [chunk0, chunk0 + nchunks) of every (b, h), from q, k, g, beta.
+template <bool F32>
+hipError_t launch_chunk_prep(const void* q, const void* k, const float* g, const float* beta,
+                             int B, int T, int H, int chunk0, int nchunks, void* ws,
+                             hipStream_t stream);
+
+// scan: walks those chunks in order, reading v, the records and h_in (NULL =
+// zero state); writes out and, if h_out is not NULL, the final state.
+template <bool F32>
+hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, float* h_out,
+                             void* out, float scale, int B, int T, int H, int chunk0,
+                             int nchunks, hipStream_t stream);
+
+// dst[i] = src ? src[i] : 0 for i < n (fp32), as a kernel so that it can be
+// captured in a graph.
+hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,155 @@
+"""Thin Python binding of the libkda C-ABI (``include/kda.h``).
+
+Argument marshalling only: shapes, dtypes, contiguity and device are checked,
+outputs are allocated with torch (device memory), and ``data_ptr()`` plus the
+current HIP stream are handed to the C entry points.  Every step of the KDA
+computation runs in the library's kernels; there is no fallback of any kind:
+if ``libkda.so`` is missing this module raises on import of the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so libkda binds to the HIP runtime torch already holds
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libkda.so")
+HEAD_DIM = 128
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_HIP = 3
+KDA_ERR_NO_MEMORY = 4
+
+EXPORTS = (
+    "kda_chunk_fwd",
+    "kda_chunk_fwd_f32",
+    "kda_recurrent_step",
+    "kda_recurrent_step_f32",
+    "kda_status_string",
+)
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (built by ``linear_attention_07_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m linear_attention_07_amd.build`"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, f, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    chunk_args = [vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, vp]
+    step_args = [vp, vp, vp, vp, vp, f, vp, vp, i, i, vp]
+    for name, args in (("kda_chunk_fwd", chunk_args), ("kda_chunk_fwd_f32", chunk_args),
+                       ("kda_recurrent_step", step_args), ("kda_recurrent_step_f32", step_args)):
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=True):
+    """Chunkwise prefill.  q, k, v: [B, T, H, 128] bf16 (or all fp32 for the
+    fp32 mode); g: [B, T, H, 128] fp32; beta: [B, T, H] fp32; h0: optional
+    [B, H, 128, 128] fp32.  Returns (out, hT); hT is None when final_state is
+    False and no hT buffer is given."""
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q: expected [B, T, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    B, T, H, _ = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda tensors must live on a GPU")
+    io = q.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q: dtype {io} not supported")
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.shape, io, dev)
+    _check(q, "q", q.shape, io, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    sshape = (B, H, HEAD_DIM, HEAD_DIM)
+    if h0 is not None:
+        _check(h0, "h0", sshape, torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _check(out, "out", q.shape, io, dev)
+    if hT is None and final_state:
+        hT = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif hT is not None:
+        _check(hT, "hT", sshape, torch.float32, dev)
+    fn = load().kda_chunk_fwd if io == torch.bfloat16 else load().kda_chunk_fwd_f32
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(h0),
+            _ptr(out), _ptr(hT), B, T, H, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return out, hT
+
+
+def recurrent_step(q, k, v, g, beta, scale, S, out=None):
+    """One decode step.  q, k, v: [B, H, 128] bf16 (or fp32); g: [B, H, 128]
+    fp32; beta: [B, H] fp32; S: [B, H, 128, 128] fp32, updated in place.
+    Returns out [B, H, 128]."""
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q: expected [B, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    B, H, _ = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda tensors must live on a GPU")
+    io = q.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q: dtype {io} not supported")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.shape, io, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _check(out, "out", q.shape, io, dev)
+    fn = load().kda_recurrent_step if io == torch.bfloat16 else load().kda_recurrent_step_f32
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(S), _ptr(out),
+            B, H, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_step")
+    return out
