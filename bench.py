@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward pass on one MI355X.
+
+A step is one kda_chunk_fwd over the 64K-token, 96-head prefill batch
+(B=1, H=96, T=65536, d=128; bf16 q/k/v, fp32 g/beta, fp32 state with a
+random initial state) with every input already resident in HBM.  The value is
+prefill Mtok/s (B*T tokens per step, all 96 heads).  The same run also times
+the batched decode step (B=256, H=96, fp32 state streamed in place) and
+reports its state bandwidth, and times the fp64 CPU oracle on a bounded
+sample of the prefill workload as a baseline.
+
+Roofline (per call of the timed op, algorithmic bytes only):
+  prefill: 1540 B per token-head (q, k, v, o in bf16 = 4 x 256 B; g 512 B;
+           beta 4 B) plus 64 KB of initial and 64 KB of final state per head;
+  decode:  132,612 B per (sequence, head): the 64 KB state read and written,
+           q, k, v (768 B), g (512 B), beta (4 B), o (256 B).
+Both are HBM-bound (about 117 and 0.86 flop/B, under the 312 flop/B ridge
+of 2.5 PFLOP/s bf16 over 8 TB/s), so the peak is 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
+STATE_BYTES = 128 * 128 * 4
+DECODE_BYTES_PER_SEQ_HEAD = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="timed decode steps (default: --steps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    return ap.parse_args()
+
+
+def time_op(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def cpu_baseline(inp, n_tokens):
+    """fp64 oracle on `threads` heads of the same prefill input, first
+    n_tokens tokens, one head per host thread."""
+    from oracle import oracle
+    threads = oracle.default_threads()
+    H = inp["q"].shape[2]
+    heads = list(range(min(3 * threads, H)))
+    t_sl = slice(0, n_tokens)
+
+    def host(x):
+        return x[:, t_sl][:, :, heads].detach().to("cpu").double().numpy()
+
+    args = [host(inp[k]) for k in ("q", "k", "v", "g", "beta")]
+    h0 = inp.get("h0")
+    h0 = None if h0 is None else h0[:, heads].detach().to("cpu").double().numpy()
+    t0 = time.perf_counter()
+    oracle.forward(*args, inp["scale"], h0, threads=threads)
+    dt = time.perf_counter() - t0
+    token_heads = len(heads) * n_tokens
+    # the metric counts tokens of a full 96-head layer
+    mtok = token_heads / H / dt / 1e6
+    return {"value": mtok, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {H} heads x first {n_tokens} tokens of the 64K "
+                      f"prefill input, fp64 token-by-token recurrence, {dt:.2f} s; "
+                      f"Mtok/s = token-heads/s / {H}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of the path is a design note, not a run.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from linear_attention_07_amd import libkda, synth
+
+    libkda.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # ---- prefill ------------------------------------------------------------
+    w = synth.WORKLOADS["prefill_64k"]
+    inp = synth.workload_inputs(w, dev)
+    out = torch.empty_like(inp["v"])
+    hT = torch.empty((w.B, w.H, 128, 128), dtype=torch.float32, device=dev)
+
+    def prefill():
+        libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                         inp["h0"], out=out, hT=hT)
+
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ms = time_op(torch, prefill, args.steps, args.warmup)
+    t_wall = time.perf_counter() - t_wall0
+    tokens = w.B * w.T
+    mtok = tokens / (ms / 1e3) / 1e6
+    token_heads = w.B * w.T * w.H
+    pre_bytes = token_heads * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * STATE_BYTES
+    pre_gbps = pre_bytes / (ms / 1e3) / 1e9
+    print(f"# prefill: {ms:.3f} ms/step, {mtok:.2f} Mtok/s, {pre_gbps:.0f} GB/s algorithmic "
+          f"(wall {t_wall:.2f} s)", file=sys.stderr, flush=True)
+
+    # ---- decode -------------------------------------------------------------
+    wd = synth.WORKLOADS["decode_b256"]
+    S = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
+    xs = [synth.decode_step_inputs(wd.B, wd.H, wd.io, seed=wd.seed, step=t, device=dev)
+          for t in range(4)]
+    dout = torch.empty_like(xs[0]["v"])
+    it = [0]
+
+    def decode():
+        x = xs[it[0] & 3]
+        it[0] += 1
+        libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S,
+                              out=dout)
+
+    dsteps = args.decode_steps or args.steps
+    dms = time_op(torch, decode, dsteps, args.warmup)
+    nbh = wd.B * wd.H
+    state_gbps = nbh * 2 * STATE_BYTES / (dms / 1e3) / 1e9
+    dec_gbps = nbh * DECODE_BYTES_PER_SEQ_HEAD / (dms / 1e3) / 1e9
+    print(f"# decode: {dms:.3f} ms/step, state {state_gbps:.0f} GB/s, "
+          f"total {dec_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, min(args.cpu_sample_tokens, w.T))
+        print(f"# cpu oracle: {cpu['value']:.5f} Mtok/s on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "KDA chunk-fwd Mtok/s at H=96,T=64K; decode state GB/s; % of roofline",
+        "value": round(mtok, 3),
+        "unit": "Mtok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill_64k: one KDA layer, B=1 H=96 T=65536 d=128, bf16 q/k/v, "
+                        "fp32 g/beta, fp32 state, h0 ~ N(0, 0.1^2), seed 2",
+            "B": w.B, "H": w.H, "T": w.T, "head_dim": 128, "chunk": 64,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kda_chunk_fwd (prep + scan kernels, one call)",
+            "achieved": round(pre_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_call": pre_bytes,
+        },
+        "decode": {
+            "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v",
+            "ms_per_step": round(dms, 4),
+            "state_GBps": round(state_gbps, 1),
+            "roofline": {
+                "bound": "hbm",
+                "kernel": "kda_decode_kernel",
+                "achieved": round(dec_gbps, 1),
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": None,
+                "algorithmic_bytes_per_call": nbh * DECODE_BYTES_PER_SEQ_HEAD,
+            },
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

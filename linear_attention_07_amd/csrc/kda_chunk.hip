@@ -144,9 +144,10 @@ __device__ __forceinline__ f32x4 mma16_split_ab(f32x4 acc, f32x4 a, f32x4 b) {
 // 16a..16a+15; lane (n = lane%16, g = lane/16) owns row 16a+n and the 32
 // channels 32s + 8g + e (s, e = 0..3, 0..7), i.e. exactly the A-operand
 // fragment of that row for the four k32 steps over the 128 channels.
+// Two workgroups fit on a CU in bf16 mode (about 77 KB of LDS each).
 // ---------------------------------------------------------------------------
 template <bool F32>
-__global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
+__global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
     const typename Prec<F32>::io_t* __restrict__ q, const typename Prec<F32>::io_t* __restrict__ k,
     const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int chunk0,
     int nchunks, uint8_t* __restrict__ ws) {
@@ -178,22 +179,33 @@ __global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
     const int64_t tok = (int64_t)c * kChunk + r;
     const int64_t rowoff = (((int64_t)b * T + tok) * H + h) * kD;
 
-    constexpr int FP = kD + 4;      // fp32 pitch of Kt / Qt rows
-    constexpr int SP = kChunk + 1;  // fp32 pitch of the 64 x 64 matrices
+    constexpr int SP = kChunk + 1;   // fp32 pitch of the 64 x 64 matrices
+    constexpr int KTP = kD + 8;      // pitch of the Kt rows (st elements)
+    constexpr int MWP = kD + 4;      // fp32 pitch of the M W rows
     constexpr size_t kZfBytes = sizeof(F8) * 4 * 4 * 64;
     constexpr size_t kXBytes = sizeof(float) * kChunk * SP;
+    constexpr size_t kKtBytes = (sizeof(st) * kChunk * KTP + 15) / 16 * 16;
+    constexpr size_t kABytes = sizeof(float) * kChunk * SP;
+    constexpr size_t kMwBytes = sizeof(float) * kChunk * MWP;
+    constexpr size_t kKaBytes = kKtBytes + kABytes > kMwBytes ? kKtBytes + kABytes : kMwBytes;
+    // decay tables per channel (exp of sums of block totals tau_a):
+    //   EP_a = exp(sum_{a'<a} tau), EK_a = exp(sum_{a'>a} tau), IE_a = exp(-tau_a),
+    //   TF(a,b) = exp(sum_{b<a'<a} tau) for a - b >= 2: (2,0), (3,0), (3,1)
+    enum { kEP = 0, kEK = 4, kIE = 8, kTF20 = 12, kTF30 = 13, kTF31 = 14, kTabs = 15 };
     __shared__ float tau_s[4][kD];
-    __shared__ float etau_s[4][kD];
+    __shared__ __align__(16) float tab_s[kTabs][kD];
     __shared__ float beta_s[kChunk];
-    __shared__ float kt_s[kChunk * FP];
-    __shared__ float qt_s[kChunk * FP];
-    __shared__ float a_s[kChunk * SP];
     __shared__ float m_s[kChunk * SP];
-    // the column operands of the decay-weighted products, later reused for
-    // X = (I + A)^-1 and then T = X diag(beta)
+    // column operands of the decay-weighted products, later X = (I + A)^-1
+    // and T = X diag(beta)
     __shared__ __align__(16) uint8_t zx_raw[kZfBytes > kXBytes ? kZfBytes : kXBytes];
+    // Kt (bf16 operand) and A, later reused for M W
+    __shared__ __align__(16) uint8_t ka_raw[kKaBytes];
     F8(*zf_s)[4][64] = reinterpret_cast<F8(*)[4][64]>(zx_raw);
     float* x_s = reinterpret_cast<float*>(zx_raw);
+    st* kt_s = reinterpret_cast<st*>(ka_raw);
+    float* a_s = reinterpret_cast<float*>(ka_raw + kKtBytes);
+    float* mw_s = reinterpret_cast<float*>(ka_raw);
 
     // ---- load the lane's row: 32 channels of q, k, g -----------------------
     float qf[32], kf[32], lam[32];
@@ -234,68 +246,102 @@ __global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
     for (int j = 0; j < 32; ++j) lam[j] = row16_inclusive_scan(lam[j]);
     if (n == 15) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) tau_s[wv][32 * (j >> 3) + 8 * gq + (j & 7)] = lam[j];
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tau_s[wv][32 * s + 8 * gq + e] = lam[8 * s + e];
     }
     if (gq == 0) beta_s[r] = bet;
     __syncthreads();
 
-    for (int idx = tid; idx < 4 * kD; idx += 256)
-        etau_s[idx >> 7][idx & 127] = fast_exp(tau_s[idx >> 7][idx & 127]);
-    if (tid < kD) Gg[tid] = fast_exp(tau_s[0][tid] + tau_s[1][tid] + tau_s[2][tid] + tau_s[3][tid]);
+    for (int idx = tid; idx < (kTabs + 1) * kD; idx += 256) {
+        const int tb = idx >> 7, ch = idx & 127;
+        const float t0 = tau_s[0][ch], t1 = tau_s[1][ch], t2 = tau_s[2][ch], t3 = tau_s[3][ch];
+        float x;
+        switch (tb) {
+            case kEP + 0: x = 0.f; break;
+            case kEP + 1: x = t0; break;
+            case kEP + 2: x = t0 + t1; break;
+            case kEP + 3: x = t0 + t1 + t2; break;
+            case kEK + 0: x = t1 + t2 + t3; break;
+            case kEK + 1: x = t2 + t3; break;
+            case kEK + 2: x = t3; break;
+            case kEK + 3: x = 0.f; break;
+            case kIE + 0: x = -t0; break;
+            case kIE + 1: x = -t1; break;
+            case kIE + 2: x = -t2; break;
+            case kIE + 3: x = -t3; break;
+            case kTF20: x = t1; break;
+            case kTF30: x = t1 + t2; break;
+            case kTF31: x = t2; break;
+            default: x = t0 + t1 + t2 + t3; break;  // chunk decay gamma
+        }
+        const float ex = fast_exp(x);
+        if (tb < kTabs) tab_s[tb][ch] = ex;
+        else Gg[ch] = ex;
+    }
     __syncthreads();
 
     // ---- decay factors and the derived operands -----------------------------
-    // e0 = exp(Gam_r - Gam_{16a-1}) <= 1, e1 = exp(Gam_r - Gam_{e_a}) >= 1,
-    // z = exp(Gam_{e_a} - Gam_r) <= 1 (a = this wave's block)
-    float e0[32], e1[32];
+    // e0 = exp(Gam_r - Gam_{16a-1}) <= 1, z = exp(Gam_{e_a} - Gam_r) <= 1
+    // (a = this wave's block).  Kept: rk0 = kh e0, rq0 = qh e0, Qt.
+    float qtil[32];
     {
         float zc[32];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int ch = 32 * (j >> 3) + 8 * gq + (j & 7);
-            const float ta = tau_s[wv][ch];
-            e0[j] = fast_exp(lam[j]);
-            e1[j] = fast_exp(lam[j] - ta);
-            const float z = fast_exp(ta - lam[j]);
-            float ePa = 1.f, eKb = 1.f;
+        for (int s = 0; s < 4; ++s) {
+            const int cb = 32 * s + 8 * gq;
+            float ep[8], ek[8], ta[8];
+            *reinterpret_cast<float4*>(ep) = *reinterpret_cast<const float4*>(&tab_s[kEP + wv][cb]);
+            *reinterpret_cast<float4*>(ep + 4) = *reinterpret_cast<const float4*>(&tab_s[kEP + wv][cb + 4]);
+            *reinterpret_cast<float4*>(ek) = *reinterpret_cast<const float4*>(&tab_s[kEK + wv][cb]);
+            *reinterpret_cast<float4*>(ek + 4) = *reinterpret_cast<const float4*>(&tab_s[kEK + wv][cb + 4]);
 #pragma unroll
-            for (int a2 = 0; a2 < 4; ++a2) {
-                if (a2 < wv) ePa *= etau_s[a2][ch];
-                if (a2 > wv) eKb *= etau_s[a2][ch];
+            for (int e = 0; e < 8; ++e) ta[e] = tau_s[wv][cb + e];
+            st kt8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 8 * s + e;
+                const float e0 = fast_exp(lam[j]);
+                const float z = fast_exp(ta[e] - lam[j]);
+                zc[j] = kf[j] * z;
+                KTg[(size_t)(cb + e) * kChunk + r] = P::to_st(kf[j] * z * ek[e]);
+                kt8[e] = P::to_st(kf[j] * e0 * ep[e]);
+                qtil[j] = qf[j] * e0 * ep[e];
+                kf[j] *= e0;  // rk0
+                qf[j] *= e0;  // rq0
             }
-            zc[j] = kf[j] * z;
-            KTg[(size_t)ch * kChunk + r] = P::to_st(kf[j] * z * eKb);
-            const float g0 = e0[j] * ePa;
-            kt_s[r * FP + ch] = kf[j] * g0;
-            qt_s[r * FP + ch] = qf[j] * g0;
+            st* dst = kt_s + r * KTP + cb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = kt8[e];
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) zf_s[wv][s][lane] = P::pack8(zc + 8 * s);
     }
     __syncthreads();
 
-    // ---- (KK) and (QK) tiles of row block wv against column blocks b <= wv --
+    // ---- (KK) and (QK) tiles of row block wv against column blocks cb <= wv -
+    // row factor exp(Gam_r - Gam_{e_cb}) = e0 * f_cb with f = IE_wv (cb = wv),
+    // 1 (cb = wv - 1), TF(wv, cb) otherwise
     for (int cb = 0; cb <= wv; ++cb) {
-        float t[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int ch = 32 * (j >> 3) + 8 * gq + (j & 7);
-            if (cb == wv) {
-                t[j] = e1[j];
-            } else {
-                float f = e0[j];
-                for (int a2 = cb + 1; a2 < wv; ++a2) f *= etau_s[a2][ch];
-                t[j] = f;
-            }
-        }
+        const int tix = (cb == wv) ? kIE + wv : (wv - cb == 2) ? (wv == 2 ? kTF20 : kTF31) : kTF30;
+        const bool unit = (cb == wv - 1);
         f32x4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            const int cbase = 32 * s + 8 * gq;
+            float f[8];
+            if (unit) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = 1.f;
+            } else {
+                *reinterpret_cast<float4*>(f) = *reinterpret_cast<const float4*>(&tab_s[tix][cbase]);
+                *reinterpret_cast<float4*>(f + 4) = *reinterpret_cast<const float4*>(&tab_s[tix][cbase + 4]);
+            }
             float rk[8], rq[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                rk[e] = kf[8 * s + e] * t[8 * s + e];
-                rq[e] = qf[8 * s + e] * t[8 * s + e];
+                rk[e] = kf[8 * s + e] * f[e];
+                rq[e] = qf[8 * s + e] * f[e];
             }
             const F8 fz = zf_s[cb][s][lane];
             accK = P::mma32(accK, P::pack8(rk), fz);
@@ -314,12 +360,15 @@ __global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
 
     // ---- X = (I + A)^-1: diagonal blocks by forward substitution (fp32) ----
     {
+        float arow[16];
         float x[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
+#pragma unroll
+            for (int cc = 0; cc < rr; ++cc) arow[cc] = a_s[(16 * wv + rr) * SP + 16 * wv + cc];
             float s = 0.f;
 #pragma unroll
-            for (int cc = 0; cc < rr; ++cc) s += a_s[(16 * wv + rr) * SP + 16 * wv + cc] * x[cc];
+            for (int cc = 0; cc < rr; ++cc) s += arow[cc] * x[cc];
             x[rr] = (rr == n) ? 1.f : -s;
         }
         if (gq == 0) {
@@ -368,51 +417,30 @@ __global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
     }
     __syncthreads();
 
-    // ---- W = T Kt and Q' = Qt - M W for channels [32 wv, 32 wv + 32) --------
-    {
-        f32x4 Wt[4][2];
+    // ---- W = T Kt for channels [32 wv, 32 wv + 32) ---------------------------
+    f32x4 Wt[4][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = 32 * wv + 16 * ct + n;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < 2; ++ct) {
+            const int col = 32 * wv + 16 * ct + n;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb <= rt; ++kb) {
-                    f32x4 ta, kv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ta[e] = x_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
-                        kv[e] = kt_s[(16 * kb + 4 * gq + e) * FP + col];
-                    }
-                    acc = mma16_split_a<F32>(acc, ta, P::pack4(kv));
-                }
+            for (int kb = 0; kb <= rt; ++kb) {
+                f32x4 ta;
+                typename P::F4 kv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float wq = P::from_st(P::to_st(acc[e]));  // W as the scan sees it
-                    Wt[rt][ct][e] = wq;
-                    Wg[(size_t)(16 * rt + 4 * gq + e) * kD + col] = P::to_st(acc[e]);
+                    ta[e] = x_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
+                    if constexpr (F32) kv.v[e] = kt_s[(16 * kb + 4 * gq + e) * KTP + col];
+                    else kv.v[e] = (short)kt_s[(16 * kb + 4 * gq + e) * KTP + col];
                 }
+                acc = mma16_split_a<F32>(acc, ta, kv);
             }
-        }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = 32 * wv + 16 * ct + n;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb <= rt; ++kb) {
-                    f32x4 ma;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ma[e] = m_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
-                    acc = mma16_split_a<F32>(acc, ma, P::pack4(Wt[kb][ct]));
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * rt + 4 * gq + e;
-                    QPg[(size_t)row * kD + col] = P::to_st(qt_s[row * FP + col] - acc[e]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                Wt[rt][ct][e] = P::from_st(P::to_st(acc[e]));  // W as the scan sees it
+                Wg[(size_t)(16 * rt + 4 * gq + e) * kD + col] = P::to_st(acc[e]);
             }
         }
     }
@@ -443,6 +471,49 @@ __global__ __launch_bounds__(256) void kda_chunk_prep_kernel(
             }
         }
     }
+    __syncthreads();  // Kt and A are dead: their space takes M W
+
+    // ---- M W for channels [32 wv, 32 wv + 32), then Q' = Qt - M W per row ---
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int col = 32 * wv + 16 * ct + n;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb <= rt; ++kb) {
+                f32x4 ma;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ma[e] = m_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
+                acc = mma16_split_a<F32>(acc, ma, P::pack4(Wt[kb][ct]));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mw_s[(16 * rt + 4 * gq + e) * MWP + col] = acc[e];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cb = 32 * s + 8 * gq;
+        float mw[8];
+        *reinterpret_cast<float4*>(mw) = *reinterpret_cast<const float4*>(&mw_s[r * MWP + cb]);
+        *reinterpret_cast<float4*>(mw + 4) = *reinterpret_cast<const float4*>(&mw_s[r * MWP + cb + 4]);
+        st o8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = P::to_st(qtil[8 * s + e] - mw[e]);
+        st* dst = QPg + (size_t)r * kD + cb;
+        if constexpr (F32) {
+            *reinterpret_cast<float4*>(dst) = make_float4(o8[0], o8[1], o8[2], o8[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
+        } else {
+            uint4 u;
+            u.x = (uint32_t)o8[0] | ((uint32_t)o8[1] << 16);
+            u.y = (uint32_t)o8[2] | ((uint32_t)o8[3] << 16);
+            u.z = (uint32_t)o8[4] | ((uint32_t)o8[5] << 16);
+            u.w = (uint32_t)o8[6] | ((uint32_t)o8[7] << 16);
+            *reinterpret_cast<uint4*>(dst) = u;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -465,8 +536,22 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
     using F8 = typename P::F8;
     using R = Rec<F32>;
 
-    const int slice = blockIdx.x % kScanSlices;
-    const int bh = blockIdx.x / kScanSlices;
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
+    // map ids so that all slices of one head sit on one XCD and the chunk
+    // records they all read are fetched from HBM once.
+    int slice, bh;
+    {
+        const int nblk = gridDim.x, id = blockIdx.x;
+        const int per_xcd = nblk / 8;
+        if (nblk % (8 * kScanSlices) == 0) {
+            const int xcd = id % 8, idx = id / 8;
+            bh = xcd * (per_xcd / kScanSlices) + idx / kScanSlices;
+            slice = idx % kScanSlices;
+        } else {
+            slice = id % kScanSlices;
+            bh = id / kScanSlices;
+        }
+    }
     const int h = bh % H, b = bh / H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
@@ -493,6 +578,42 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
         for (int e = 0; e < 4; ++e)
             S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
 
+    // bf16 mode: the next chunk's record and V slice are loaded into registers
+    // while the current chunk computes (22 x 16 B per thread + gamma).
+    u32x4 pf[22];
+    u32x4 pg = {0u, 0u, 0u, 0u};
+#define KDA_SCAN_ISSUE(cl_)                                                                     \
+    do {                                                                                        \
+        const uint8_t* rec_ = ws + ((size_t)bh * nchunks + (cl_)) * R::BYTES;                   \
+        const int64_t cbase = (int64_t)(chunk0 + (cl_)) * kChunk;                               \
+        const u32x4* Wv = reinterpret_cast<const u32x4*>(rec_ + R::W);                          \
+        const u32x4* Qv = reinterpret_cast<const u32x4*>(rec_ + R::QP);                         \
+        const u32x4* Kv = reinterpret_cast<const u32x4*>(rec_ + R::KT);                         \
+        const u32x4* THv = reinterpret_cast<const u32x4*>(rec_ + R::TH);                        \
+        const u32x4* TLv = reinterpret_cast<const u32x4*>(rec_ + R::TL);                        \
+        const u32x4* MHv = reinterpret_cast<const u32x4*>(rec_ + R::MH);                        \
+        const u32x4* MLv = reinterpret_cast<const u32x4*>(rec_ + R::ML);                        \
+        _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                         \
+            pf[m] = Wv[tid + 256 * m];                                                          \
+            pf[4 + m] = Qv[tid + 256 * m];                                                      \
+            pf[8 + m] = Kv[tid + 256 * m];                                                      \
+        }                                                                                       \
+        _Pragma("unroll") for (int m = 0; m < 2; ++m) {                                         \
+            pf[12 + m] = THv[tid + 256 * m];                                                    \
+            pf[14 + m] = TLv[tid + 256 * m];                                                    \
+            pf[16 + m] = MHv[tid + 256 * m];                                                    \
+            pf[18 + m] = MLv[tid + 256 * m];                                                    \
+            const int i_ = tid + 256 * m;                                                       \
+            const int64_t tk_ = cbase + (i_ >> 3);                                              \
+            const int64_t vo_ = (((int64_t)b * T + (tk_ < T ? tk_ : 0)) * H + h) * kD + c0 +    \
+                                (i_ & 7) * 8;                                                   \
+            const u32x4 vv_ = *reinterpret_cast<const u32x4*>(v + vo_);                         \
+            pf[20 + m] = tk_ < T ? vv_ : u32x4{0u, 0u, 0u, 0u};                                 \
+        }                                                                                       \
+        if (tid < 32) pg = reinterpret_cast<const u32x4*>(rec_ + R::G)[tid];                    \
+    } while (0)
+    if constexpr (!F32) KDA_SCAN_ISSUE(0);
+
     for (int cl = 0; cl < nchunks; ++cl) {
         const int c = chunk0 + cl;
         const uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * R::BYTES;
@@ -509,51 +630,44 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
             mlp = mhp;
             ap = kD;
             kp = kChunk;
+            // V slice of this chunk (zero past the end of the sequence)
+            constexpr int VR = kSliceCols / 4;
+            for (int i = tid; i < kChunk * VR; i += kScanThreads) {
+                const int row = i / VR, cv = i % VR;
+                const int64_t tok = (int64_t)c * kChunk + row;
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (tok < T)
+                    val = *reinterpret_cast<const u32x4*>(
+                        v + (((int64_t)b * T + tok) * H + h) * kD + c0 + cv * 4);
+                *reinterpret_cast<u32x4*>(&v_s[row * VP + cv * 4]) = val;
+            }
+            if (tid < kD) gam_s[tid] = reinterpret_cast<const float*>(rec + R::G)[tid];
         } else {
-            // 16-byte vectors: 16 per 128-wide row, 8 per 64-wide row
-            const uint4* Wv = reinterpret_cast<const uint4*>(rec + R::W);
-            const uint4* Qv = reinterpret_cast<const uint4*>(rec + R::QP);
-            const uint4* Kv = reinterpret_cast<const uint4*>(rec + R::KT);
-            const uint4* THv = reinterpret_cast<const uint4*>(rec + R::TH);
-            const uint4* TLv = reinterpret_cast<const uint4*>(rec + R::TL);
-            const uint4* MHv = reinterpret_cast<const uint4*>(rec + R::MH);
-            const uint4* MLv = reinterpret_cast<const uint4*>(rec + R::ML);
-            for (int i = tid; i < kChunk * 16; i += kScanThreads) {
-                const int row = i >> 4, cv = i & 15;
-                *reinterpret_cast<uint4*>(&w_s[row * AP + cv * 8]) = Wv[i];
-                *reinterpret_cast<uint4*>(&qp_s[row * AP + cv * 8]) = Qv[i];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = tid + 256 * m;
+                *reinterpret_cast<u32x4*>(&w_s[(i >> 4) * AP + (i & 15) * 8]) = pf[m];
+                *reinterpret_cast<u32x4*>(&qp_s[(i >> 4) * AP + (i & 15) * 8]) = pf[4 + m];
+                *reinterpret_cast<u32x4*>(&kt_s[(i >> 3) * KP + (i & 7) * 8]) = pf[8 + m];
             }
-            for (int i = tid; i < kD * 8; i += kScanThreads) {
-                const int row = i >> 3, cv = i & 7;
-                *reinterpret_cast<uint4*>(&kt_s[row * KP + cv * 8]) = Kv[i];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int i = tid + 256 * m, o = (i >> 3) * KP + (i & 7) * 8;
+                *reinterpret_cast<u32x4*>(&th_s[o]) = pf[12 + m];
+                *reinterpret_cast<u32x4*>(&tl_s[o]) = pf[14 + m];
+                *reinterpret_cast<u32x4*>(&mh_s[o]) = pf[16 + m];
+                *reinterpret_cast<u32x4*>(&ml_s[o]) = pf[18 + m];
+                *reinterpret_cast<u32x4*>(&v_s[(i >> 3) * VP + (i & 7) * 8]) = pf[20 + m];
             }
-            for (int i = tid; i < kChunk * 8; i += kScanThreads) {
-                const int row = i >> 3, cv = i & 7;
-                *reinterpret_cast<uint4*>(&th_s[row * KP + cv * 8]) = THv[i];
-                *reinterpret_cast<uint4*>(&tl_s[row * KP + cv * 8]) = TLv[i];
-                *reinterpret_cast<uint4*>(&mh_s[row * KP + cv * 8]) = MHv[i];
-                *reinterpret_cast<uint4*>(&ml_s[row * KP + cv * 8]) = MLv[i];
-            }
+            if (tid < 32) *reinterpret_cast<u32x4*>(&gam_s[4 * tid]) = pg;
             wp = w_s; qpp = qp_s; ktp = kt_s; thp = th_s; tlp = tl_s; mhp = mh_s; mlp = ml_s;
             ap = AP;
             kp = KP;
         }
-        {
-            // V slice of this chunk (zero past the end of the sequence)
-            constexpr int EV = 16 / sizeof(st);
-            constexpr int VR = kSliceCols / EV;
-            for (int i = tid; i < kChunk * VR; i += kScanThreads) {
-                const int row = i / VR, cv = i % VR;
-                const int64_t tok = (int64_t)c * kChunk + row;
-                uint4 val = {0u, 0u, 0u, 0u};
-                if (tok < T)
-                    val = *reinterpret_cast<const uint4*>(
-                        v + (((int64_t)b * T + tok) * H + h) * kD + c0 + cv * EV);
-                *reinterpret_cast<uint4*>(&v_s[row * VP + cv * EV]) = val;
-            }
-        }
-        if (tid < kD) gam_s[tid] = reinterpret_cast<const float*>(rec + R::G)[tid];
         __syncthreads();
+        if constexpr (!F32) {
+            if (cl + 1 < nchunks) KDA_SCAN_ISSUE(cl + 1);
+        }
 
         // S-independent: Ut = T V and Oh = MT V for this wave's 16 columns
         f32x4 Ut[4], Oh[4];
@@ -590,23 +704,32 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const F8 bS = P::pack8(S[2 * s], S[2 * s + 1]);
+            F8 fw[4], fq[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                Pm[rt] = P::mma32(Pm[rt], frag_row<F32>(wp, ap, 16 * rt + n, 32 * s, gq), bS);
-                Pm[4 + rt] = P::mma32(Pm[4 + rt], frag_row<F32>(qpp, ap, 16 * rt + n, 32 * s, gq), bS);
+                fw[rt] = frag_row<F32>(wp, ap, 16 * rt + n, 32 * s, gq);
+                fq[rt] = frag_row<F32>(qpp, ap, 16 * rt + n, 32 * s, gq);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Pm[rt] = P::mma32(Pm[rt], fw[rt], bS);
+                Pm[4 + rt] = P::mma32(Pm[4 + rt], fq[rt], bS);
             }
         }
 
         // U = T V - W S ;  O = scale (Q' S + MT V)
         f32x4 U[4];
+        const bool full = (int64_t)(c + 1) * kChunk <= T;
+        auto* outc = out + (((int64_t)b * T + (int64_t)c * kChunk) * H + h) * kD + j0 + n;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             U[rt] = Ut[rt] - Pm[rt];
             const f32x4 o = Pm[4 + rt] + Oh[rt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t tok = (int64_t)c * kChunk + 16 * rt + 4 * gq + e;
-                if (tok < T) out[(((int64_t)b * T + tok) * H + h) * kD + j0 + n] = P::to_io(scale * o[e]);
+                const int row = 16 * rt + 4 * gq + e;
+                if (full || (int64_t)c * kChunk + row < T)
+                    outc[(int64_t)row * H * kD] = P::to_io(scale * o[e]);
             }
         }
 
@@ -644,6 +767,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
     }
+#undef KDA_SCAN_ISSUE
 }
 
 template <bool F32>

@@ -30,6 +30,7 @@ constexpr float kNormEps = 1e-6f;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
     // v_cvt_pk_bf16_f32: round to nearest even, NaN preserved
