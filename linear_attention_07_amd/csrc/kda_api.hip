@@ -23,19 +23,17 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Workspace budget for one segment of the chunked path (4 GB: a 64K-token,
-// 96-head layer in one segment; longer sequences are split);
-// KDA_WORKSPACE_MB overrides it (read once).
+// Workspace budget for one segment of the chunked path: 4 GB by default (a
+// 64K-token, 96-head layer in one segment; longer sequences are split).  The
+// environment variable KDA_WORKSPACE_MB overrides it; it is read on every
+// call, so a caller can force small segments.
 size_t workspace_budget() {
-    static size_t budget = [] {
-        size_t mb = 4096;
-        if (const char* s = getenv("KDA_WORKSPACE_MB")) {
-            const long v = strtol(s, nullptr, 10);
-            if (v > 0) mb = (size_t)v;
-        }
-        return mb << 20;
-    }();
-    return budget;
+    size_t mb = 4096;
+    if (const char* s = getenv("KDA_WORKSPACE_MB")) {
+        const long v = strtol(s, nullptr, 10);
+        if (v > 0) mb = (size_t)v;
+    }
+    return mb << 20;
 }
 
 // One memory pool per device, created on first use, that keeps freed blocks

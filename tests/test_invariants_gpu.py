@@ -1,0 +1,216 @@
+"""GPU checks of structural properties of the KDA recurrence and of the
+boundary's edge cases, through the C-ABI.
+
+Each property is a fact of the recurrence (Kimi-K3 深度解析 blog, section 三)
+that holds at any size, so it also covers shapes too large for the oracle:
+exact recall with beta = 1, pure decay with beta = 0, chaining of the carried
+state, chunked = token-by-token, value columns independent, the -5 bound on
+the log-decay, determinism.  Where an oracle comparison is cheap it is made
+as well.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from kda_check import TOL_BF16, TOL_F32, host64, oracle_prefill, rel_out, rel_state, say
+from linear_attention_07_amd import libkda, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def chunk(inp, h0="inp", **kw):
+    h = inp.get("h0") if h0 == "inp" else h0
+    out, hT = libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                               h, **kw)
+    torch.cuda.synchronize()
+    return out, hT
+
+
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_beta_one_exact_recall(io):
+    """beta = 1 and q_t = k_t make every read-out return scale * v_t exactly
+    (up to rounding), whatever the decay and the initial state."""
+    B, T, H = 1, 1000, 4
+    inp = synth.prefill_inputs(B, T, H, io, seed=31, h0_std=0.1, device=DEV)
+    inp["q"] = inp["k"]
+    inp["beta"] = torch.ones_like(inp["beta"])
+    out, _ = chunk(inp)
+    want = inp["scale"] * inp["v"].double()
+    err = (out.double() - want).abs().max().item() / want.abs().max().item()
+    say(f"beta=1 recall {io}: {err:.2e}")
+    assert err <= (TOL_BF16 if io == torch.bfloat16 else TOL_F32)
+
+
+def test_beta_zero_pure_decay():
+    """beta = 0: nothing is written; the state only decays per key channel and
+    the outputs read the decayed initial state (checked against the oracle)."""
+    B, T, H = 2, 300, 3
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=32, h0_std=0.1, device=DEV)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    out, hT = chunk(inp)
+    o_ref, h_ref = oracle_prefill(inp)
+    G = np.cumsum(host64(inp["g"]), axis=1)[:, -1]            # [B, H, 128]
+    h_closed = np.exp(G)[..., None] * host64(inp["h0"])       # decay on key rows
+    assert np.abs(h_ref - h_closed).max() <= 1e-12 * np.abs(h_closed).max()
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"beta=0: out {eo:.2e} state {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    out0, hT0 = chunk(inp, h0=None)
+    assert not out0.any().item() and not hT0.any().item()
+
+
+@pytest.mark.parametrize("split", [64, 100, 1])
+def test_chaining_matches_one_call(split):
+    """Running T1 tokens and then T2 tokens from the returned state equals one
+    call over T1 + T2 tokens (state carry = resume)."""
+    B, T, H = 1, 640, 4
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=33, h0_std=0.1, device=DEV)
+    out, hT = chunk(inp)
+    a = {k_: (v_[:, :split].contiguous() if k_ in ("q", "k", "v", "g", "beta") else v_)
+         for k_, v_ in inp.items()}
+    b = {k_: (v_[:, split:].contiguous() if k_ in ("q", "k", "v", "g", "beta") else v_)
+         for k_, v_ in inp.items()}
+    oa, ha = chunk(a)
+    ob, hb = chunk(b, h0=ha)
+    o2 = torch.cat([oa, ob], dim=1)
+    eo = rel_out(host64(o2), host64(out))
+    es = rel_state(host64(hb), host64(hT))
+    say(f"chaining at {split}: out {eo:.2e} state {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_segmented_workspace_matches():
+    """A tiny workspace budget forces the library to split T into many
+    segments (state carried between them); results equal the single-segment
+    run up to rounding."""
+    B, T, H = 1, 2000, 3
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=34, h0_std=0.1, device=DEV)
+    out1, h1 = chunk(inp)
+    old = os.environ.get("KDA_WORKSPACE_MB")
+    os.environ["KDA_WORKSPACE_MB"] = "1"   # 1 MB: a few chunks per segment
+    try:
+        out2, h2 = chunk(inp)
+    finally:
+        if old is None:
+            del os.environ["KDA_WORKSPACE_MB"]
+        else:
+            os.environ["KDA_WORKSPACE_MB"] = old
+    assert torch.equal(out1, out2) and torch.equal(h1, h2)
+    o_ref, h_ref = oracle_prefill(inp)
+    assert rel_out(host64(out2), o_ref) <= TOL_BF16 and rel_state(host64(h2), h_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_chunk_equals_recurrent(io):
+    """T calls of the decode step reproduce one chunked prefill."""
+    B, T, H = 2, 150, 3
+    inp = synth.prefill_inputs(B, T, H, io, seed=35, h0_std=0.1, device=DEV)
+    out, hT = chunk(inp)
+    S = inp["h0"].clone()
+    outs = []
+    for t in range(T):
+        outs.append(libkda.recurrent_step(*(inp[n][:, t].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                                          inp["scale"], S))
+    torch.cuda.synchronize()
+    o2 = torch.stack(outs, 1)
+    tol = TOL_BF16 if io == torch.bfloat16 else TOL_F32
+    eo, es = rel_out(host64(o2), host64(out)), rel_state(host64(S), host64(hT))
+    say(f"chunk vs recurrent {io}: out {eo:.2e} state {es:.2e}")
+    assert eo <= 2 * tol and es <= 2 * tol
+
+
+def test_value_columns_independent():
+    """The map V -> (O, hT) acts column by column: changing value channel j
+    changes only output column j and state column j."""
+    B, T, H = 1, 200, 2
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=36, h0_std=0.1, device=DEV)
+    out, hT = chunk(inp)
+    inp2 = dict(inp)
+    v2 = inp["v"].clone()
+    v2[..., 70] = v2[..., 70] * -3.0 + 1.0
+    inp2["v"] = v2
+    out2, hT2 = chunk(inp2)
+    others = [j for j in range(128) if j != 70]
+    assert torch.equal(out[..., others], out2[..., others])
+    assert torch.equal(hT[..., others], hT2[..., others])
+    assert not torch.equal(out[..., 70], out2[..., 70])
+
+
+@pytest.mark.parametrize("mode", ["bound", "alternate", "zero"])
+def test_decay_at_its_bound(mode):
+    """g at the -5 lower bound (the largest factor exp(75) inside a 16-token
+    block), alternating -5 / 0, and no decay at all, against the oracle."""
+    B, T, H = 1, 333, 3
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=37, h0_std=0.1, device=DEV)
+    g = inp["g"]
+    if mode == "bound":
+        inp["g"] = torch.full_like(g, -5.0)
+    elif mode == "alternate":
+        t = torch.arange(T, device=DEV).view(1, T, 1, 1)
+        c = torch.arange(128, device=DEV).view(1, 1, 1, 128)
+        inp["g"] = torch.where((t + c) % 2 == 0, -5.0, 0.0).expand_as(g).contiguous()
+    else:
+        inp["g"] = torch.zeros_like(g)
+    out, hT = chunk(inp)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(hT).all()
+    o_ref, h_ref = oracle_prefill(inp)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"g {mode}: out {eo:.2e} state {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_deterministic():
+    """No atomics on the path: repeated runs are bitwise identical."""
+    inp = synth.prefill_inputs(1, 777, 4, torch.bfloat16, seed=38, h0_std=0.1, device=DEV)
+    o1, h1 = chunk(inp)
+    o2, h2 = chunk(inp)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    S1 = inp["h0"].clone()
+    S2 = inp["h0"].clone()
+    x = synth.decode_step_inputs(1, 4, torch.bfloat16, seed=38, device=DEV)
+    d1 = libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S1)
+    d2 = libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S2)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(S1, S2)
+
+
+def test_state_in_place_and_optional():
+    """hT may alias h0 (in-place carry); hT may be omitted."""
+    inp = synth.prefill_inputs(2, 130, 3, torch.bfloat16, seed=39, h0_std=0.1, device=DEV)
+    out, hT = chunk(inp)
+    S = inp["h0"].clone()
+    out2, hT2 = libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                 inp["scale"], S, hT=S)
+    out3, none = libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                  inp["scale"], inp["h0"], final_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(out, out2) and torch.equal(out, out3) and torch.equal(hT, S)
+
+
+def test_empty_inputs():
+    """T = 0 copies h0 to hT (zeros without h0); B = 0 or H = 0 is a no-op."""
+    inp = synth.prefill_inputs(2, 0, 3, torch.bfloat16, seed=40, h0_std=0.1, device=DEV)
+    out, hT = chunk(inp)
+    assert out.numel() == 0 and torch.equal(hT, inp["h0"])
+    out, hT = chunk(inp, h0=None)
+    assert not hT.any().item()
+    inp = synth.prefill_inputs(0, 10, 3, torch.bfloat16, seed=40, device=DEV)
+    out, hT = chunk(inp)
+    assert out.numel() == 0
+    x = synth.decode_step_inputs(0, 5, torch.bfloat16, seed=40, device=DEV)
+    S = torch.zeros((0, 5, 128, 128), device=DEV)
+    assert libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], 1.0, S).numel() == 0
+
+
+def test_state_size_independent_of_context():
+    """The carried state is 96 x 128 x 128 fp32 = 6,291,456 B per layer for a
+    4-token and a 4096-token prefill alike (the thread's 434 MB for 69 layers)."""
+    for T in (4, 4096):
+        inp = synth.prefill_inputs(1, T, 96, torch.bfloat16, seed=41, device=DEV)
+        _, hT = chunk(inp)
+        assert hT.numel() * hT.element_size() == 6_291_456
+    assert 69 * 6_291_456 == 434_110_464
