@@ -41,7 +41,37 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, copy 1 GiB once (reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources: a traffic figure measured on other
+    sources is not reported."""
+    import hashlib
+    d = hashlib.sha256()
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_attention_07_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(src, name), "rb") as f:
+                d.update(name.encode() + b"\0" + f.read())
+    return d.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per call from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_digest():
+        return None
+    return rec.get(key, {}).get("bytes_per_call")
 
 
 def time_op(torch, fn, steps, warmup):
@@ -144,6 +174,13 @@ def main():
     print(f"# decode: {dms:.3f} ms/step, state {state_gbps:.0f} GB/s, "
           f"total {dec_gbps:.0f} GB/s", file=sys.stderr, flush=True)
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, min(args.cpu_sample_tokens, w.T))
@@ -176,7 +213,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill_64k"),
             "algorithmic_bytes_per_call": pre_bytes,
         },
         "decode": {
@@ -190,7 +227,7 @@ def main():
                 "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s",
                 "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic("decode_b256"),
                 "algorithmic_bytes_per_call": nbh * DECODE_BYTES_PER_SEQ_HEAD,
             },
         },
