@@ -1,0 +1,618 @@
+// Chunkwise KDA prefill for bf16 q/k/v/o in two kernels (the pages' chunk_kda).
+//
+// The recurrence (Kimi-K3 深度解析 blog, section 三: decay the state per key
+// channel, predict v from the decayed state, write beta times the error along
+// the key; read out with the L2-normalised query, 深入 Kimi-K3 thread, KDA
+// paragraph) is evaluated 64 tokens at a time.  For one chunk of tokens
+// r = 0..63 entering with state S (key channel x value channel), with
+// Gam_r = sum_{s<=r} g_s per channel:
+//   Kt_r = exp(Gam_r) kh_r,  Qt_r = exp(Gam_r) qh_r,
+//   Kb_r = exp(Gam_63 - Gam_r) kh_r,  gamma = exp(Gam_63),
+//   A = strict-lower(diag(beta) (KK)),  M = lower-incl(QK), where
+//   (KK)_ri = sum_c kh_rc kh_ic exp(Gam_rc - Gam_ic) and (QK) likewise,
+//   T = (I + A)^-1 diag(beta).
+// Token by token the errors u_r = beta_r (v_r - prediction_r) stack into
+//   U = T (V - Kt S),   O = scale (Qt S + M U),   S <- Diag(gamma) S + Kb^T U,
+// an exact rearrangement of the recurrence.  The -5 lower bound on the
+// log-decay (ai-pulse-lab summary of the technical report, KDA paragraph)
+// keeps every factor of the 16x16 diagonal blocks of KK and QK finite, so all
+// of them are dense matrix-core products: exp(Gam_r - Gam_i) is formed as a
+// row factor times a column factor about the last token of each 16-token
+// column block (row factors up to exp(75), column factors <= 1).
+//
+// prep (kda_prep16_kernel): one workgroup per (batch, head, chunk), all chunks
+//   in parallel.  It normalises q and k, forms the decay sums and factor
+//   tables, the KK / QK blocks on MFMA, the inverse of I + A in fp32, and
+//   writes the chunk's record: Kt, Qt, Kb^T (bf16), T and M (bf16 hi + lo) and
+//   gamma.
+// scan (kda_scan16_kernel): one workgroup per (batch, head, 64 value columns),
+//   walking the chunks in order.  Four loader waves stream each record from
+//   global memory into LDS one chunk ahead; four scan waves each keep a
+//   128 x 16 fp32 slice of the state in registers and run the three products
+//   of the chunk on MFMA.  The two roles hand the record over through LDS
+//   counters (Kt / Qt first, the rest second), so the scan waves never wait
+//   for a workgroup barrier.
+//
+// Precision: Kt, Qt, Kb and the state enter the products as bf16; V - Kt S,
+// T, M and U as bf16 hi + lo pairs (about 16 mantissa bits, three products
+// per pair); accumulation is fp32.
+#include "kda_bf16.hpp"
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+using namespace b16;
+
+constexpr int kSlices = 2;             // value-column slices per head
+constexpr int kCols = kD / kSlices;    // value columns per scan workgroup
+// Row pitches of the record in the scan's LDS: 68 and 36 dwords, so that the
+// 16 rows x 2 k-groups of one half-wave's 8-byte fragment reads hit 64
+// distinct banks.
+constexpr int KP = kD + 8;
+constexpr int TP = kChunk + 8;
+constexpr int SP = kChunk + 1;         // fp32 pitch of A and X in the prep kernel
+constexpr float kLog2e = 1.4426950408889634f;  // decay sums are kept in log2 units
+
+// decay tables per channel (exp of sums of the four block totals tau_a):
+//   EP_a = exp(sum_{a'<a} tau), EK_a = exp(sum_{a'>a} tau), IE_a = exp(-tau_a),
+//   TF(a,b) = exp(sum_{b<a'<a} tau) for a - b >= 2, and gamma.
+enum { kEP = 0, kEK = 4, kIE = 8, kTF20 = 12, kTF30 = 13, kTF31 = 14, kGam = 15, kTabs = 16 };
+
+// Record of one (batch, head, chunk) in global memory, unpadded, bf16 unless
+// noted: Kt [64][128], Qt [64][128], Kb^T [128][64], T hi / lo and M hi / lo
+// [64][64] each, gamma [128] fp32.
+struct Rec16 {
+    static constexpr size_t KT = 0;
+    static constexpr size_t QT = KT + kChunk * kD * 2;
+    static constexpr size_t KB = QT + kChunk * kD * 2;
+    static constexpr size_t TH = KB + kD * kChunk * 2;
+    static constexpr size_t TL = TH + kChunk * kChunk * 2;
+    static constexpr size_t MH = TL + kChunk * kChunk * 2;
+    static constexpr size_t ML = MH + kChunk * kChunk * 2;
+    static constexpr size_t G = ML + kChunk * kChunk * 2;
+    static constexpr size_t BYTES = G + kD * 4;
+};
+static_assert(Rec16::BYTES % 256 == 0, "records stay 256-byte aligned");
+// the scan's loaders move a record as 16-byte pieces: 2048 of Kt / Qt, 3072 of
+// Kb^T / T / M, 32 of gamma, 256 threads
+static_assert(Rec16::KB / 16 == 2048 && (Rec16::G - Rec16::KB) / 16 == 12 * 256 &&
+                  Rec16::G / 16 + 32 == Rec16::BYTES / 16,
+              "loader piece counts match the record layout");
+
+}  // namespace
+
+size_t chunk16_record_bytes() { return Rec16::BYTES; }
+int chunk16_slices() { return kSlices; }
+
+// ---------------------------------------------------------------------------
+// prep: wave p owns chunk rows 16p..16p+15; lane (n, gq) owns row r = 16p + n
+// and the 32 channels 32s + 8gq + e (s = 0..3, e = 0..7), i.e. its A-operand
+// fragments of the four k32 steps over the 128 channels.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
+    uint8_t* __restrict__ ws) {
+    __shared__ __align__(16) float tau_s[4][kD];      // block totals of g (log2 units)
+    __shared__ __align__(16) float tab_s[kTabs][kD];  // factor tables
+    __shared__ float beta_s[kChunk];
+    __shared__ float a_s[kChunk * SP];                 // diag(beta) strict-lower KK
+    __shared__ float x_s[kChunk * SP];                 // X = (I + A)^-1
+    // column operands of KK / QK; afterwards the Kb^T staging area
+    __shared__ __align__(16) bf16x8 zf_s[4][4][64];
+    uint16_t* kbT_s = reinterpret_cast<uint16_t*>(&zf_s[0][0][0]);
+
+    const int cl = blockIdx.x % nchunks;
+    const int bh = blockIdx.x / nchunks;
+    const int h = bh % H, b = bh / H;
+    const int c = chunk0 + cl;
+    uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * Rec16::BYTES;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int p = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int r = 16 * p + n;
+    const int64_t tok = (int64_t)c * kChunk + r;
+    const bool valid = tok < T;
+    const int64_t rowoff = (((int64_t)b * T + (valid ? tok : 0)) * H + h) * kD;
+
+    // ---- load the lane's row: 32 channels of q, k (bf16 pairs) and g ---------
+    u32x4 pq[4], pk[4];
+    f32x4 pg[8];
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const f32x4 zf4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cb = 32 * s + 8 * gq;
+        pq[s] = valid ? *reinterpret_cast<const u32x4*>(q + rowoff + cb) : z4;
+        pk[s] = valid ? *reinterpret_cast<const u32x4*>(k + rowoff + cb) : z4;
+        pg[2 * s] = valid ? *reinterpret_cast<const f32x4*>(g + rowoff + cb) : zf4;
+        pg[2 * s + 1] = valid ? *reinterpret_cast<const f32x4*>(g + rowoff + cb + 4) : zf4;
+    }
+    const float bet = valid ? beta[((int64_t)b * T + tok) * H + h] : 0.f;
+
+    // ---- norms of q and k; in-block cumsum of g over the 16 rows -------------
+    float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float q0 = __builtin_bit_cast(float, pq[s][w] << 16);
+            const float q1 = __builtin_bit_cast(float, pq[s][w] & 0xffff0000u);
+            const float k0 = __builtin_bit_cast(float, pk[s][w] << 16);
+            const float k1 = __builtin_bit_cast(float, pk[s][w] & 0xffff0000u);
+            ssq += q0 * q0 + q1 * q1;
+            ssk += k0 * k0 + k1 * k1;
+        }
+    }
+    ssq += __shfl_xor(ssq, 16);
+    ssk += __shfl_xor(ssk, 16);
+    ssq += __shfl_xor(ssq, 32);
+    ssk += __shfl_xor(ssk, 32);
+    const float iq = __builtin_amdgcn_rsqf(ssq + kNormEps);
+    const float ik = __builtin_amdgcn_rsqf(ssk + kNormEps);
+    float lam[32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lam[8 * s + e] = row16_inclusive_scan(pg[2 * s][e] * kLog2e);
+            lam[8 * s + 4 + e] = row16_inclusive_scan(pg[2 * s + 1][e] * kLog2e);
+        }
+    }
+    if (n == 15) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tau_s[p][32 * s + 8 * gq + e] = lam[8 * s + e];
+    }
+    if (gq == 0) beta_s[r] = bet;
+    __syncthreads();
+
+    // ---- factor tables ---------------------------------------------------------
+#pragma unroll
+    for (int m = 0; m < kTabs / 2; ++m) {
+        const int idx = tid + 256 * m, tb = idx >> 7, ch = idx & 127;
+        const float t0 = tau_s[0][ch], t1 = tau_s[1][ch], t2 = tau_s[2][ch], t3 = tau_s[3][ch];
+        float x;
+        switch (tb) {
+            case kEP + 0: x = 0.f; break;
+            case kEP + 1: x = t0; break;
+            case kEP + 2: x = t0 + t1; break;
+            case kEP + 3: x = t0 + t1 + t2; break;
+            case kEK + 0: x = t1 + t2 + t3; break;
+            case kEK + 1: x = t2 + t3; break;
+            case kEK + 2: x = t3; break;
+            case kEK + 3: x = 0.f; break;
+            case kIE + 0: x = -t0; break;
+            case kIE + 1: x = -t1; break;
+            case kIE + 2: x = -t2; break;
+            case kIE + 3: x = -t3; break;
+            case kTF20: x = t1; break;
+            case kTF30: x = t1 + t2; break;
+            case kTF31: x = t2; break;
+            default: x = t0 + t1 + t2 + t3; break;  // gamma
+        }
+        tab_s[tb][ch] = __builtin_amdgcn_exp2f(x);
+    }
+    __syncthreads();
+
+    // ---- decay factors; the Kt / Qt rows of the record ----------------------
+    // e0 = exp(Gam_r - Gam_{16p-1}) <= 1, z = exp(Gam_{16p+15} - Gam_r) <= 1;
+    // rk0 = kh e0 and rq0 = qh e0 are the KK / QK row operands before the
+    // per-block factor; Kt = rk0 EP_p, Qt = rq0 EP_p, Kb = kh z EK_p.
+    float rk0[32], rq0[32];
+    uint32_t kbw[16];  // this row of Kb, as bf16 pairs
+    {
+        uint16_t* ktg = reinterpret_cast<uint16_t*>(rec + Rec16::KT) + r * kD;
+        uint16_t* qtg = reinterpret_cast<uint16_t*>(rec + Rec16::QT) + r * kD;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cb = 32 * s + 8 * gq;
+            float ep[8], ek[8], ta[8], zc[8];
+            *reinterpret_cast<f32x4*>(ep) = *reinterpret_cast<const f32x4*>(&tab_s[kEP + p][cb]);
+            *reinterpret_cast<f32x4*>(ep + 4) = *reinterpret_cast<const f32x4*>(&tab_s[kEP + p][cb + 4]);
+            *reinterpret_cast<f32x4*>(ek) = *reinterpret_cast<const f32x4*>(&tab_s[kEK + p][cb]);
+            *reinterpret_cast<f32x4*>(ek + 4) = *reinterpret_cast<const f32x4*>(&tab_s[kEK + p][cb + 4]);
+            *reinterpret_cast<f32x4*>(ta) = *reinterpret_cast<const f32x4*>(&tau_s[p][cb]);
+            *reinterpret_cast<f32x4*>(ta + 4) = *reinterpret_cast<const f32x4*>(&tau_s[p][cb + 4]);
+            uint32_t ktw[4], qtw[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float kh0 = __builtin_bit_cast(float, pk[s][w] << 16) * ik;
+                const float kh1 = __builtin_bit_cast(float, pk[s][w] & 0xffff0000u) * ik;
+                const float qh0 = __builtin_bit_cast(float, pq[s][w] << 16) * iq;
+                const float qh1 = __builtin_bit_cast(float, pq[s][w] & 0xffff0000u) * iq;
+                const int j = 8 * s + 2 * w;
+                const float e00 = __builtin_amdgcn_exp2f(lam[j]);
+                const float e01 = __builtin_amdgcn_exp2f(lam[j + 1]);
+                const float z0 = __builtin_amdgcn_exp2f(ta[2 * w] - lam[j]);
+                const float z1 = __builtin_amdgcn_exp2f(ta[2 * w + 1] - lam[j + 1]);
+                zc[2 * w] = kh0 * z0;
+                zc[2 * w + 1] = kh1 * z1;
+                rk0[j] = kh0 * e00;
+                rk0[j + 1] = kh1 * e01;
+                rq0[j] = qh0 * e00;
+                rq0[j + 1] = qh1 * e01;
+                ktw[w] = pack2(rk0[j] * ep[2 * w], rk0[j + 1] * ep[2 * w + 1]);
+                qtw[w] = pack2(rq0[j] * ep[2 * w], rq0[j + 1] * ep[2 * w + 1]);
+                kbw[4 * s + w] = pack2(zc[2 * w] * ek[2 * w], zc[2 * w + 1] * ek[2 * w + 1]);
+            }
+            *reinterpret_cast<u32x4*>(ktg + cb) = u32x4{ktw[0], ktw[1], ktw[2], ktw[3]};
+            *reinterpret_cast<u32x4*>(qtg + cb) = u32x4{qtw[0], qtw[1], qtw[2], qtw[3]};
+            zf_s[p][s][lane] = pack8(zc);
+        }
+    }
+    __syncthreads();
+
+    // ---- KK and QK blocks of row block p against column blocks cb <= p ---------
+    // row factor exp(Gam_r - Gam_{16cb+15}) = e0 * f with f = IE_p (cb = p),
+    // 1 (cb = p - 1), TF(p, cb) otherwise.  The products are taken transposed
+    // (column operand as A), so that a lane ends up with row r and the four
+    // consecutive columns 16cb + 4g + e.
+    f32x4 Mt[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        Mt[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (cb > p) continue;
+        const int tix = (cb == p) ? kIE + p : (p - cb == 2) ? (p == 2 ? kTF20 : kTF31) : kTF30;
+        const bool unit = (cb == p - 1);
+        f32x4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cbase = 32 * s + 8 * gq;
+            bf16x8 rk, rq;
+            if (unit) {
+                rk = pack8(rk0 + 8 * s);
+                rq = pack8(rq0 + 8 * s);
+            } else {
+                float f[8], tk[8], tq[8];
+                *reinterpret_cast<f32x4*>(f) = *reinterpret_cast<const f32x4*>(&tab_s[tix][cbase]);
+                *reinterpret_cast<f32x4*>(f + 4) = *reinterpret_cast<const f32x4*>(&tab_s[tix][cbase + 4]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    tk[e] = rk0[8 * s + e] * f[e];
+                    tq[e] = rq0[8 * s + e] * f[e];
+                }
+                rk = pack8(tk);
+                rq = pack8(tq);
+            }
+            const bf16x8 fz = zf_s[cb][s][lane];
+            accK = mma(accK, fz, rk);
+            accQ = mma(accQ, fz, rq);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ci = 16 * cb + 4 * gq + e;
+            const bool strict = (cb < p) || (ci < r);
+            const bool incl = (cb < p) || (ci <= r);
+            a_s[r * SP + ci] = strict ? bet * accK[e] : 0.f;
+            Mt[cb][e] = incl ? accQ[e] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- X = (I + A)^-1: diagonal blocks by forward substitution --------------
+    {
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float s = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < rr; ++cc) s += a_s[(16 * p + rr) * SP + 16 * p + cc] * x[cc];
+            x[rr] = (rr == n) ? 1.f : -s;
+        }
+        if (gq == 0) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) x_s[(16 * p + rr) * SP + 16 * p + n] = x[rr];
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance: X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
+    // (fp32 matrix-core products, 16x16x4)
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        if (p >= d) {
+            const int a = p, bb = p - d;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int cc = bb; cc < a; ++cc) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        a_s[(16 * a + n) * SP + 16 * cc + 4 * gq + e],
+                        x_s[(16 * cc + 4 * gq + e) * SP + 16 * bb + n], acc, 0, 0, 0);
+            }
+            f32x4 xab = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                xab = __builtin_amdgcn_mfma_f32_16x16x4f32(x_s[(16 * a + n) * SP + 16 * a + 4 * gq + e],
+                                                          acc[e], xab, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x_s[(16 * a + 4 * gq + e) * SP + 16 * bb + n] = -xab[e];
+        }
+        __syncthreads();
+    }
+
+    // ---- the rest of the record -------------------------------------------------
+    // T = X diag(beta) (zero above the diagonal) and M as hi / lo: row r,
+    // columns 16ct + 4g .. +3 per lane
+    {
+        uint16_t* th = reinterpret_cast<uint16_t*>(rec + Rec16::TH) + r * kChunk;
+        uint16_t* tl = reinterpret_cast<uint16_t*>(rec + Rec16::TL) + r * kChunk;
+        uint16_t* mh = reinterpret_cast<uint16_t*>(rec + Rec16::MH) + r * kChunk;
+        uint16_t* ml = reinterpret_cast<uint16_t*>(rec + Rec16::ML) + r * kChunk;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            float tv[4], mv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = 16 * ct + 4 * gq + e;
+                tv[e] = (col <= r) ? x_s[r * SP + col] * beta_s[col] : 0.f;
+                mv[e] = Mt[ct][e];
+            }
+            const int o = 16 * ct + 4 * gq;
+            split4(tv, *reinterpret_cast<uint2*>(th + o), *reinterpret_cast<uint2*>(tl + o));
+            split4(mv, *reinterpret_cast<uint2*>(mh + o), *reinterpret_cast<uint2*>(ml + o));
+        }
+    }
+    // Kb^T through LDS: column r of the [channel][token] matrix, then rows out
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cb = 32 * s + 8 * gq;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            kbT_s[(cb + 2 * w) * kChunk + r] = (uint16_t)(kbw[4 * s + w] & 0xffffu);
+            kbT_s[(cb + 2 * w + 1) * kChunk + r] = (uint16_t)(kbw[4 * s + w] >> 16);
+        }
+    }
+    if (p == 0) {
+        float* gg = reinterpret_cast<float*>(rec + Rec16::G);
+        gg[lane] = tab_s[kGam][lane];
+        gg[lane + 64] = tab_s[kGam][lane + 64];
+    }
+    __syncthreads();
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(kbT_s);
+        u32x4* dst = reinterpret_cast<u32x4*>(rec + Rec16::KB);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[tid + 256 * m] = src[tid + 256 * m];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan: waves 0..3 load records, waves 4..7 scan (wave w owns value columns
+// j0 .. j0+15 of the state as eight 16x16 accumulator tiles, key rows
+// 16t + 4g + e, column j0 + n).  k order of every product: values 0..3 of a
+// lane carry k = k0 + 4g + e, values 4..7 carry k0 + 16 + 4g + e, i.e. the
+// rows of accumulator tiles 2s and 2s+1, so S, X and U feed the B operand from
+// registers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
+    const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, float scale,
+    const float* h_in, float* h_out, uint16_t* __restrict__ out, int T, int H, int chunk0,
+    int nchunks) {
+    __shared__ __align__(16) uint16_t kt_s[kChunk * KP];  // Kt, [token][channel]
+    __shared__ __align__(16) uint16_t qt_s[kChunk * KP];  // Qt
+    __shared__ __align__(16) uint16_t kb_s[kD * TP];      // Kb^T, [channel][token]
+    __shared__ __align__(16) uint16_t th_s[kChunk * TP];  // T hi / lo, [token][token]
+    __shared__ __align__(16) uint16_t tl_s[kChunk * TP];
+    __shared__ __align__(16) uint16_t mh_s[kChunk * TP];  // M hi / lo
+    __shared__ __align__(16) uint16_t ml_s[kChunk * TP];
+    __shared__ __align__(16) float gam_s[kD];
+    // Kt/Qt ready; Kt/Qt consumed; rest ready; rest consumed; abort
+    __shared__ unsigned sync_s[5];
+
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
+    // both slices of a head go to one XCD, so the records that both read come
+    // from HBM once.
+    int slice, bh;
+    {
+        const int nblk = gridDim.x, id = blockIdx.x;
+        if (nblk % (8 * kSlices) == 0) {
+            const int per_xcd = nblk / 8, xcd = id % 8, idx = id / 8;
+            bh = xcd * (per_xcd / kSlices) + idx / kSlices;
+            slice = idx % kSlices;
+        } else {
+            slice = id % kSlices;
+            bh = id / kSlices;
+        }
+    }
+    const int h = bh % H, b = bh / H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+
+    if (tid < 5) sync_s[tid] = 0u;
+    __syncthreads();  // the only workgroup barrier: roles split below
+
+    if (wv < 4) {
+        // =====================================================================
+        // loaders: 16-byte pieces tid + 256 m of each record part, one chunk
+        // ahead in registers
+        // =====================================================================
+        u32x4 ra[8], rb[12];
+        u32x4 rg = {0u, 0u, 0u, 0u};
+#define KDA_LOAD_ISSUE(cl_)                                                                      \
+    do {                                                                                         \
+        const u32x4* src_ = reinterpret_cast<const u32x4*>(                                      \
+            ws + ((size_t)bh * nchunks + (cl_)) * Rec16::BYTES);                                 \
+        _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) ra[m_] = src_[tid + 256 * m_];          \
+        _Pragma("unroll") for (int m_ = 0; m_ < 12; ++m_) rb[m_] = src_[2048 + tid + 256 * m_];  \
+        if (tid < 32) rg = src_[(Rec16::G / 16) + tid];                                          \
+    } while (0)
+        KDA_LOAD_ISSUE(0);
+        for (int i = 0; i < nchunks; ++i) {
+            // Kt, Qt: pieces 0..1023 and 1024..2047, 16 per 128-channel row
+            wait_for(&sync_s[1], 4u * i, &sync_s[4]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int idx = tid + 256 * m;
+                uint16_t* dst = (idx < 1024) ? kt_s : qt_s;
+                const int j = idx & 1023;
+                *reinterpret_cast<u32x4*>(&dst[(j >> 4) * KP + (j & 15) * 8]) = ra[m];
+            }
+            signal(&sync_s[0], lane);
+            // Kb^T (pieces 0..1023, 8 per 64-token row), T hi / lo, M hi / lo
+            // (512 pieces each), gamma
+            wait_for(&sync_s[3], 4u * i, &sync_s[4]);
+#pragma unroll
+            for (int m = 0; m < 12; ++m) {
+                const int idx = tid + 256 * m;
+                uint16_t* dst;
+                int j;
+                if (idx < 1024) {
+                    dst = kb_s;
+                    j = idx;
+                } else {
+                    const int part = (idx - 1024) >> 9;
+                    dst = part == 0 ? th_s : part == 1 ? tl_s : part == 2 ? mh_s : ml_s;
+                    j = (idx - 1024) & 511;
+                }
+                *reinterpret_cast<u32x4*>(&dst[(j >> 3) * TP + (j & 7) * 8]) = rb[m];
+            }
+            if (tid < 32) *reinterpret_cast<u32x4*>(&gam_s[4 * tid]) = rg;
+            signal(&sync_s[2], lane);
+            if (i + 1 < nchunks) KDA_LOAD_ISSUE(i + 1);
+        }
+#undef KDA_LOAD_ISSUE
+    } else {
+        // =====================================================================
+        // scan waves
+        // =====================================================================
+        const int w = wv - 4;
+        const int j0 = kCols * slice + 16 * w;
+        f32x4 S[8];
+        const float* hin = h_in ? h_in + (size_t)bh * kD * kD : nullptr;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
+
+        // this lane's 16 values of V for the next chunk: rows 16rt + 4g + e,
+        // column j0 + n (rows past the end load row 0 and are zeroed when used)
+        uint16_t pv[16];
+#define KDA_SCAN_ISSUE(c_)                                                                       \
+    do {                                                                                         \
+        _Pragma("unroll") for (int rt_ = 0; rt_ < 4; ++rt_) {                                    \
+            _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) {                                   \
+                const int64_t tok_ = (int64_t)(c_) * kChunk + 16 * rt_ + 4 * gq + e_;            \
+                pv[4 * rt_ + e_] =                                                               \
+                    v[(((int64_t)b * T + (tok_ < T ? tok_ : 0)) * H + h) * kD + j0 + n];         \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
+        KDA_SCAN_ISSUE(chunk0);
+
+        for (int i = 0; i < nchunks; ++i) {
+            const int64_t c0 = (int64_t)(chunk0 + i) * kChunk;
+            wait_for(&sync_s[0], 4u * (i + 1), &sync_s[4]);
+            f32x4 Vt[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Vt[rt][e] = (c0 + 16 * rt + 4 * gq + e < T) ? bf2f(pv[4 * rt + e]) : 0.f;
+            if (i + 1 < nchunks) KDA_SCAN_ISSUE(chunk0 + i + 1);
+
+            // Pk = Kt S, Pq = Qt S (S as bf16)
+            f32x4 Pk[4], Pq[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Pk[rt] = Pq[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 bS = pack_b(S[2 * s], S[2 * s + 1]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    Pk[rt] = mma(Pk[rt], frag_row(kt_s, KP, 16 * rt + n, 32 * s, gq), bS);
+                    Pq[rt] = mma(Pq[rt], frag_row(qt_s, KP, 16 * rt + n, 32 * s, gq), bS);
+                }
+            }
+            signal(&sync_s[1], lane);  // Kt, Qt consumed
+            wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4]);
+
+            // U = T (V - Kt S), both factors as hi + lo (T lower triangular)
+            bf16x8 bh_[2], bl_[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                split_b(Vt[2 * s2] - Pk[2 * s2], Vt[2 * s2 + 1] - Pk[2 * s2 + 1], bh_[s2], bl_[s2]);
+            f32x4 U[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+                    const bf16x8 fh = frag_row(th_s, TP, 16 * rt + n, 32 * s2, gq);
+                    const bf16x8 fl = frag_row(tl_s, TP, 16 * rt + n, 32 * s2, gq);
+                    U[rt] = mma(U[rt], fh, bh_[s2]);
+                    U[rt] = mma(U[rt], fl, bh_[s2]);
+                    U[rt] = mma(U[rt], fh, bl_[s2]);
+                }
+            }
+
+            // O = scale (Qt S + M U);  S <- Diag(gamma) S + Kb^T U   (U as hi + lo)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) split_b(U[2 * s2], U[2 * s2 + 1], bh_[s2], bl_[s2]);
+            const bool full = c0 + kChunk <= T;
+            uint16_t* outc = out + (((int64_t)b * T + c0) * H + h) * kD + j0 + n;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 o = Pq[rt];
+#pragma unroll
+                for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+                    const bf16x8 fh = frag_row(mh_s, TP, 16 * rt + n, 32 * s2, gq);
+                    const bf16x8 fl = frag_row(ml_s, TP, 16 * rt + n, 32 * s2, gq);
+                    o = mma(o, fh, bh_[s2]);
+                    o = mma(o, fl, bh_[s2]);
+                    o = mma(o, fh, bl_[s2]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * rt + 4 * gq + e;
+                    if (full || c0 + row < T) outc[(int64_t)row * H * kD] = f2bf(scale * o[e]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&gam_s[16 * t + 4 * gq]);
+                S[t] *= gm;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const bf16x8 fa = frag_row(kb_s, TP, 16 * t + n, 32 * s2, gq);
+                    S[t] = mma(S[t], fa, bh_[s2]);
+                    S[t] = mma(S[t], fa, bl_[s2]);
+                }
+            }
+            signal(&sync_s[3], lane);  // the rest consumed
+        }
+#undef KDA_SCAN_ISSUE
+        if (h_out) {
+            float* ho = h_out + (size_t)bh * kD * kD;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
+        }
+    }
+}
+
+hipError_t launch_prep16(const void* q, const void* k, const float* g, const float* beta, int B,
+                         int T, int H, int chunk0, int nchunks, void* ws, hipStream_t stream) {
+    const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
+    hipLaunchKernelGGL(kda_prep16_kernel, dim3(nblk), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), g, beta,
+                       T, H, chunk0, nchunks, static_cast<uint8_t*>(ws));
+    return hipGetLastError();
+}
+
+hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
+                         void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
+                         hipStream_t stream) {
+    const unsigned nblk = (unsigned)((int64_t)B * H * kSlices);
+    hipLaunchKernelGGL(kda_scan16_kernel, dim3(nblk), dim3(512), 0, stream,
+                       static_cast<const uint8_t*>(ws), static_cast<const uint16_t*>(v), scale,
+                       h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks);
+    return hipGetLastError();
+}
+
+}  // namespace kda

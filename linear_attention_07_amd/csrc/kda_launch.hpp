@@ -35,6 +35,24 @@ hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, f
                              void* out, float scale, int B, int T, int H, int chunk0,
                              int nchunks, hipStream_t stream);
 
+// fused chunked prefill for bf16 q/k/v/o: one launch over the whole sequence,
+// no workspace; h_in NULL = zero state, h_out NULL = final state not stored.
+hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float scale, const float* h_in, float* h_out,
+                              void* out, int B, int T, int H, hipStream_t stream);
+int fused_slices();
+
+// two-kernel chunked prefill for bf16 q/k/v/o: prep writes one record per
+// (batch, head, chunk) of chunks [chunk0, chunk0 + nchunks) into ws; scan walks
+// them in order (h_in NULL = zero state, h_out NULL = final state not stored).
+size_t chunk16_record_bytes();
+int chunk16_slices();
+hipError_t launch_prep16(const void* q, const void* k, const float* g, const float* beta, int B,
+                         int T, int H, int chunk0, int nchunks, void* ws, hipStream_t stream);
+hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
+                         void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
+                         hipStream_t stream);
+
 // dst[i] = src ? src[i] : 0 for i < n (fp32), as a kernel so that it can be
 // captured in a graph.
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);

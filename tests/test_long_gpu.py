@@ -1,23 +1,23 @@
 """Million-token prefill (B=1, H=96, T=1,048,576, bf16 q/k/v, slow decay
 g = -5 sigmoid(x - 6)) with all inputs resident on the device (about 155 GB).
 
-The fp64 oracle follows 16 heads (including heads 0 and 47) over the whole
-length, streamed in segments with the state carried between them: outputs of
-heads 0 and 47 at every token and the final state of all 16 heads are
-compared.  The remaining heads are covered by a property that holds at any
-size: with beta = 1 and q = k every output equals scale * v exactly.
+The fp64 oracle follows all 96 heads over the whole length, streamed in
+segments of 32,768 tokens with the state carried between them: the outputs of
+heads 0 and 47 are compared at every token and the final state of every head
+is compared.  The outputs of the other heads are covered by a property that
+holds at any size: with beta = 1 and q = k every output equals scale * v.
 """
 import numpy as np
 import pytest
 import torch
 
-from kda_check import TOL_BF16, oracle_threads, say
+from kda_check import TOL_BF16, host64, oracle_threads, rel_state, say
 from linear_attention_07_amd import libkda, synth
 from oracle import oracle
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = "cuda"
-HEADS = [0, 47] + [h for h in range(3, 96, 7) if h != 47][:14]
+OUT_HEADS = (0, 47)
 
 
 @pytest.fixture(scope="module")
@@ -33,32 +33,34 @@ def million():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(1200)
 def test_prefill_1m_against_oracle(million):
     w, inp = million
     out, hT = libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"])
     torch.cuda.synchronize()
-    say("GPU done; streaming the oracle over 16 heads")
-    seg = 1 << 17
+    say("GPU done; streaming the oracle over all 96 heads")
+    seg = 1 << 15
     S = None
-    err = {h: 0.0 for h in (0, 47)}
-    ref = {h: 0.0 for h in (0, 47)}
+    err = {h: 0.0 for h in OUT_HEADS}
+    ref = {h: 0.0 for h in OUT_HEADS}
     for t0 in range(0, w.T, seg):
         t1 = min(w.T, t0 + seg)
 
-        def host(x):
-            return x[:, t0:t1][:, :, HEADS].to(torch.float64).cpu().numpy()
+        def seqs(x):  # [1, t, H, D] on the device -> [H, t, D] on the host
+            return x[0, t0:t1].transpose(0, 1).contiguous().cpu()
 
-        o_ref, S = oracle.forward(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]),
-                                  host(inp["beta"]), inp["scale"], S, threads=oracle_threads())
-        for idx, h in enumerate(HEADS[:2]):
-            got = out[:, t0:t1, h].to(torch.float64).cpu().numpy()
-            err[h] = max(err[h], float(np.abs(got - o_ref[:, :, idx]).max()))
-            ref[h] = max(ref[h], float(np.abs(o_ref[:, :, idx]).max()))
-        say(f"  tokens {t1}: head0 {err[0] / ref[0]:.2e} head47 {err[47] / ref[47]:.2e}")
+        o_ref, S = oracle.run_sequences(seqs(inp["q"]), seqs(inp["k"]), seqs(inp["v"]),
+                                        seqs(inp["g"]), inp["beta"][0, t0:t1].t().contiguous().cpu(),
+                                        inp["scale"], S, threads=oracle_threads())
+        for h in OUT_HEADS:
+            got = out[0, t0:t1, h].to(torch.float64).cpu().numpy()
+            err[h] = max(err[h], float(np.abs(got - o_ref[h]).max()))
+            ref[h] = max(ref[h], float(np.abs(o_ref[h]).max()))
+        if (t1 // seg) % 4 == 0 or t1 == w.T:
+            say(f"  tokens {t1}: head0 {err[0] / ref[0]:.2e} head47 {err[47] / ref[47]:.2e}")
     eo = max(err[h] / ref[h] for h in err)
-    hg = hT[:, HEADS].to(torch.float64).cpu().numpy()
-    es = float((np.abs(hg - S).max(axis=(2, 3)) / np.abs(S).max(axis=(2, 3))).max())
-    say(f"1M: out err (heads 0, 47) {eo:.2e}; final-state err (16 heads) {es:.2e}")
+    es = rel_state(host64(hT), S.reshape(1, w.H, 128, 128))
+    say(f"1M: out err (heads 0, 47) {eo:.2e}; final-state err (all 96 heads) {es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
