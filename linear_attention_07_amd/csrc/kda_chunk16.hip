@@ -490,16 +490,27 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
 
         // this lane's 16 values of V for the next chunk: rows 16rt + 4g + e,
-        // column j0 + n (rows past the end load row 0 and are zeroed when used)
+        // column j0 + n.  Row pointers are wave-uniform; the lane adds a 32-bit
+        // offset.  In the last chunk, rows past the end of the sequence load the
+        // last row and are zeroed when used, so nothing waits on the loads
+        // before then.
+        const int64_t rstride = (int64_t)H * kD;  // elements between tokens
+        const uint32_t vlane = (uint32_t)(4 * gq * rstride + j0 + n);
+        const uint16_t* vhead = v + ((int64_t)b * T * H + h) * kD;
         uint16_t pv[16];
 #define KDA_SCAN_ISSUE(c_)                                                                       \
     do {                                                                                         \
-        _Pragma("unroll") for (int rt_ = 0; rt_ < 4; ++rt_) {                                    \
-            _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) {                                   \
-                const int64_t tok_ = (int64_t)(c_) * kChunk + 16 * rt_ + 4 * gq + e_;            \
-                pv[4 * rt_ + e_] =                                                               \
-                    v[(((int64_t)b * T + (tok_ < T ? tok_ : 0)) * H + h) * kD + j0 + n];         \
-            }                                                                                    \
+        const int64_t t0_ = (int64_t)(c_) * kChunk;                                              \
+        if (t0_ + kChunk <= T) {                                                                 \
+            _Pragma("unroll") for (int rt_ = 0; rt_ < 4; ++rt_)                                  \
+                _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_)                                 \
+                    pv[4 * rt_ + e_] = (vhead + (t0_ + 16 * rt_ + e_) * rstride)[vlane];        \
+        } else {                                                                                 \
+            _Pragma("unroll") for (int rt_ = 0; rt_ < 4; ++rt_)                                  \
+                _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) {                               \
+                    const int64_t tk_ = t0_ + 16 * rt_ + 4 * gq + e_;                            \
+                    pv[4 * rt_ + e_] = vhead[(tk_ < T ? tk_ : T - 1) * rstride + j0 + n];        \
+                }                                                                                \
         }                                                                                        \
     } while (0)
         KDA_SCAN_ISSUE(chunk0);
@@ -515,7 +526,10 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     Vt[rt][e] = (c0 + 16 * rt + 4 * gq + e < T) ? bf2f(pv[4 * rt + e]) : 0.f;
             if (i + 1 < nchunks) KDA_SCAN_ISSUE(chunk0 + i + 1);
 
-            // Pk = Kt S, Pq = Qt S (S as bf16)
+            // Pk = Kt S (rows token 4g + e, column n) and Pq = (Qt S)^T (rows
+            // column 4g + e, column token n): the S slice serves as the B
+            // operand of the first and, transposed, as the A operand of the
+            // second, with the same registers
             f32x4 Pk[4], Pq[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) Pk[rt] = Pq[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -525,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     Pk[rt] = mma(Pk[rt], frag_row(kt_s, KP, 16 * rt + n, 32 * s, gq), bS);
-                    Pq[rt] = mma(Pq[rt], frag_row(qt_s, KP, 16 * rt + n, 32 * s, gq), bS);
+                    Pq[rt] = mma(Pq[rt], bS, frag_row(qt_s, KP, 16 * rt + n, 32 * s, gq));
                 }
             }
             signal(&sync_s[1], lane);  // Kt, Qt consumed
@@ -550,11 +564,12 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 }
             }
 
-            // O = scale (Qt S + M U);  S <- Diag(gamma) S + Kb^T U   (U as hi + lo)
+            // O^T = (Qt S)^T + U^T M^T, so that a lane holds token 16rt + n and
+            // the four consecutive columns j0 + 4g .. +3 (one 8-byte store);
+            // S <- Diag(gamma) S + Kb^T U   (U as hi + lo)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) split_b(U[2 * s2], U[2 * s2 + 1], bh_[s2], bl_[s2]);
-            const bool full = c0 + kChunk <= T;
-            uint16_t* outc = out + (((int64_t)b * T + c0) * H + h) * kD + j0 + n;
+            uint16_t* outc = out + ((int64_t)b * T * H + h) * kD + j0 + 4 * gq;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 o = Pq[rt];
@@ -562,15 +577,14 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
                     const bf16x8 fh = frag_row(mh_s, TP, 16 * rt + n, 32 * s2, gq);
                     const bf16x8 fl = frag_row(ml_s, TP, 16 * rt + n, 32 * s2, gq);
-                    o = mma(o, fh, bh_[s2]);
-                    o = mma(o, fl, bh_[s2]);
-                    o = mma(o, fh, bl_[s2]);
+                    o = mma(o, bh_[s2], fh);
+                    o = mma(o, bh_[s2], fl);
+                    o = mma(o, bl_[s2], fh);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * rt + 4 * gq + e;
-                    if (full || c0 + row < T) outc[(int64_t)row * H * kD] = f2bf(scale * o[e]);
-                }
+                const int64_t tk = c0 + 16 * rt + n;
+                if (tk < T)
+                    *reinterpret_cast<uint2*>(outc + tk * rstride) =
+                        uint2{pack2(scale * o[0], scale * o[1]), pack2(scale * o[2], scale * o[3])};
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
