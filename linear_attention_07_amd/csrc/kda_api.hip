@@ -5,7 +5,6 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
-#include <string.h>
 
 #include <mutex>
 
@@ -99,22 +98,9 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float*
         overlap(out, io_bytes, hT, state_bytes))
         return KDA_ERR_INVALID_ARG;
 
-    // bf16: two-kernel path by default; KDA_CHUNK_KERNEL=fused or two_pass_v1
-    // selects the other implementations (kept for comparison)
-    int path = 0;
-    if constexpr (!F32) {
+    if constexpr (!F32)
         if ((int64_t)B * H * kda::chunk16_slices() > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
-        if (const char* e = getenv("KDA_CHUNK_KERNEL")) {
-            if (strcmp(e, "fused") == 0) path = 1;
-            if (strcmp(e, "two_pass_v1") == 0) path = 2;
-        }
-        if (path == 1) {
-            const hipError_t e =
-                kda::launch_chunk_fused(q, k, v, g, beta, scale, h0, hT, out, B, T, H, stream);
-            return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-        }
-    }
-    const bool v16 = !F32 && path == 0;
+    constexpr bool v16 = !F32;  // bf16: prep16 / scan16; fp32 I/O: the fp32 kernels
     const int nch = (T + 63) / 64;
     const size_t rec = v16 ? kda::chunk16_record_bytes() : kda::chunk_record_bytes(F32);
     const size_t per_chunk = (size_t)B * H * rec;
@@ -145,7 +131,7 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float*
         const float* h_in = (c0 == 0) ? h0 : carry;
         float* h_out = last ? (hT ? hT : nullptr) : carry;
         hipError_t e1, e2;
-        if (v16) {
+        if constexpr (v16) {
             e1 = kda::launch_prep16(q, k, g, beta, B, T, H, c0, n, ws, stream);
             e2 = e1 == hipSuccess
                      ? kda::launch_scan16(ws, v, h_in, h_out, out, scale, B, T, H, c0, n, stream)

@@ -1,4 +1,6 @@
-// Chunkwise-parallel KDA prefill (the pages' chunk_kda).
+// Chunkwise-parallel KDA prefill (the pages' chunk_kda) for fp32 q/k/v/o.
+// Only the fp32 instantiation (Prec<true>, fp32 matrix-core products) is
+// built; bf16 inputs take the prep16 / scan16 kernels.
 //
 // The recurrence (Kimi-K3 深度解析 blog, section 三) is evaluated 64 tokens at a
 // time.  The chunk form below is an exact rearrangement of it; the blog's
@@ -794,12 +796,8 @@ hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, f
     return hipGetLastError();
 }
 
-template hipError_t launch_chunk_prep<false>(const void*, const void*, const float*, const float*,
-                                             int, int, int, int, int, void*, hipStream_t);
 template hipError_t launch_chunk_prep<true>(const void*, const void*, const float*, const float*,
                                             int, int, int, int, int, void*, hipStream_t);
-template hipError_t launch_chunk_scan<false>(const void*, const void*, const float*, float*,
-                                             void*, float, int, int, int, int, int, hipStream_t);
 template hipError_t launch_chunk_scan<true>(const void*, const void*, const float*, float*,
                                             void*, float, int, int, int, int, int, hipStream_t);
 

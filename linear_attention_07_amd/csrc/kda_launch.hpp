@@ -35,13 +35,6 @@ hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, f
                              void* out, float scale, int B, int T, int H, int chunk0,
                              int nchunks, hipStream_t stream);
 
-// fused chunked prefill for bf16 q/k/v/o: one launch over the whole sequence,
-// no workspace; h_in NULL = zero state, h_out NULL = final state not stored.
-hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* g,
-                              const float* beta, float scale, const float* h_in, float* h_out,
-                              void* out, int B, int T, int H, hipStream_t stream);
-int fused_slices();
-
 // two-kernel chunked prefill for bf16 q/k/v/o: prep writes one record per
 // (batch, head, chunk) of chunks [chunk0, chunk0 + nchunks) into ws; scan walks
 // them in order (h_in NULL = zero state, h_out NULL = final state not stored).
