@@ -401,6 +401,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     __shared__ __align__(16) uint16_t mh_s[kChunk * TP];  // M hi / lo
     __shared__ __align__(16) uint16_t ml_s[kChunk * TP];
     __shared__ __align__(16) float gam_s[kD];
+    __shared__ __align__(16) uint16_t vT_s[kCols * TP];   // V slice, [column][token]
     // Kt/Qt ready; Kt/Qt consumed; rest ready; rest consumed; abort
     __shared__ unsigned sync_s[5];
 
@@ -431,8 +432,12 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // loaders: 16-byte pieces tid + 256 m of each record part, one chunk
         // ahead in registers
         // =====================================================================
-        u32x4 ra[8], rb[12];
+        // V of the slice: 64 tokens x 64 columns = 512 pieces of 8 columns, two
+        // per thread (piece tid + 256 m: token piece >> 3, columns 8 (piece & 7))
+        u32x4 ra[8], rb[12], rv[2];
         u32x4 rg = {0u, 0u, 0u, 0u};
+        const int64_t vstride = (int64_t)H * kD;
+        const uint16_t* vslice = v + ((int64_t)b * T * H + h) * kD + kCols * slice;
 #define KDA_LOAD_ISSUE(cl_)                                                                      \
     do {                                                                                         \
         const u32x4* src_ = reinterpret_cast<const u32x4*>(                                      \
@@ -440,6 +445,12 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) ra[m_] = src_[tid + 256 * m_];          \
         _Pragma("unroll") for (int m_ = 0; m_ < 12; ++m_) rb[m_] = src_[2048 + tid + 256 * m_];  \
         if (tid < 32) rg = src_[(Rec16::G / 16) + tid];                                          \
+        _Pragma("unroll") for (int m_ = 0; m_ < 2; ++m_) {                                       \
+            const int pc_ = tid + 256 * m_;                                                      \
+            const int64_t tk_ = (int64_t)(chunk0 + (cl_)) * kChunk + (pc_ >> 3);                 \
+            rv[m_] = *reinterpret_cast<const u32x4*>(vslice + (tk_ < T ? tk_ : 0) * vstride +    \
+                                                     (pc_ & 7) * 8);                             \
+        }                                                                                        \
     } while (0)
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
@@ -476,6 +487,18 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 d2[1] = uint2{rb[m][2], rb[m][3]};
             }
             if (tid < 32) *reinterpret_cast<u32x4*>(&gam_s[4 * tid]) = rg;
+            // V transposed; tokens past the end of the sequence are zero
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int pc = tid + 256 * m, tk = pc >> 3, c8 = (pc & 7) * 8;
+                const bool ok = (int64_t)(chunk0 + i) * kChunk + tk < T;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t x = ok ? rv[m][w] : 0u;
+                    vT_s[(c8 + 2 * w) * TP + tk] = (uint16_t)(x & 0xffffu);
+                    vT_s[(c8 + 2 * w + 1) * TP + tk] = (uint16_t)(x >> 16);
+                }
+            }
             signal(&sync_s[2], lane);
             if (i + 1 < nchunks) KDA_LOAD_ISSUE(i + 1);
         }
@@ -494,42 +517,11 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             for (int e = 0; e < 4; ++e)
                 S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
 
-        // this lane's 16 values of V for the next chunk: rows 16rt + 4g + e,
-        // column j0 + n.  Row pointers are wave-uniform; the lane adds a 32-bit
-        // offset.  In the last chunk, rows past the end of the sequence load the
-        // last row and are zeroed when used, so nothing waits on the loads
-        // before then.
         const int64_t rstride = (int64_t)H * kD;  // elements between tokens
-        const uint32_t vlane = (uint32_t)(4 * gq * rstride + j0 + n);
-        const uint16_t* vhead = v + ((int64_t)b * T * H + h) * kD;
-        uint16_t pv[16];
-#define KDA_SCAN_ISSUE(c_)                                                                       \
-    do {                                                                                         \
-        const int64_t t0_ = (int64_t)(c_) * kChunk;                                              \
-        if (t0_ + kChunk <= T) {                                                                 \
-            _Pragma("unroll") for (int rt_ = 0; rt_ < 4; ++rt_)                                  \
-                _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_)                                 \
-                    pv[4 * rt_ + e_] = (vhead + (t0_ + 16 * rt_ + e_) * rstride)[vlane];        \
-        } else {                                                                                 \
-            _Pragma("unroll") for (int rt_ = 0; rt_ < 4; ++rt_)                                  \
-                _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) {                               \
-                    const int64_t tk_ = t0_ + 16 * rt_ + 4 * gq + e_;                            \
-                    pv[4 * rt_ + e_] = vhead[(tk_ < T ? tk_ : T - 1) * rstride + j0 + n];        \
-                }                                                                                \
-        }                                                                                        \
-    } while (0)
-        KDA_SCAN_ISSUE(chunk0);
 
         for (int i = 0; i < nchunks; ++i) {
             const int64_t c0 = (int64_t)(chunk0 + i) * kChunk;
             wait_for(&sync_s[0], 4u * (i + 1), &sync_s[4]);
-            f32x4 Vt[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Vt[rt][e] = (c0 + 16 * rt + 4 * gq + e < T) ? bf2f(pv[4 * rt + e]) : 0.f;
-            if (i + 1 < nchunks) KDA_SCAN_ISSUE(chunk0 + i + 1);
 
             // Pk = Kt S (rows token 4g + e, column n) and Pq = (Qt S)^T (rows
             // column 4g + e, column token n): the S slice serves as the B
@@ -566,6 +558,16 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             signal(&sync_s[1], lane);  // Kt, Qt consumed
             wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4]);
 
+            // this lane's V: tokens 16rt + 4g .. +3 of column 16w + n
+            f32x4 Vt[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const uint2 x = *reinterpret_cast<const uint2*>(&vT_s[(16 * w + n) * TP + 16 * rt + 4 * gq]);
+                Vt[rt][0] = __builtin_bit_cast(float, x.x << 16);
+                Vt[rt][1] = __builtin_bit_cast(float, x.x & 0xffff0000u);
+                Vt[rt][2] = __builtin_bit_cast(float, x.y << 16);
+                Vt[rt][3] = __builtin_bit_cast(float, x.y & 0xffff0000u);
+            }
             // U = T (V - Kt S), both factors as hi + lo (T lower triangular);
             // the six T fragment pairs are read before X is split
             bf16x8 fth[6], ftl[6];
@@ -652,7 +654,6 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             }
             signal(&sync_s[3], lane);  // the rest consumed
         }
-#undef KDA_SCAN_ISSUE
         if (h_out) {
             float* ho = h_out + (size_t)bh * kD * kD;
 #pragma unroll
