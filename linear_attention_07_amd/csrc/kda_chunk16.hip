@@ -61,25 +61,27 @@ constexpr float kLog2e = 1.4426950408889634f;  // decay sums are kept in log2 un
 enum { kEP = 0, kEK = 4, kIE = 8, kTF20 = 12, kTF30 = 13, kTF31 = 14, kGam = 15, kTabs = 16 };
 
 // Record of one (batch, head, chunk) in global memory, unpadded, bf16 unless
-// noted: Kt [64][128], Qt [64][128], Kb^T [128][64], T hi / lo and M hi / lo
-// [64][64] each, gamma [128] fp32.
+// noted: Kt [64][128], Qt [64][128], Kb^T [128][64]; T hi, T lo, M hi, M lo as
+// their ten lower 16x16 blocks each (block (a, b), b <= a, in the order
+// (0,0) (1,0) (1,1) (2,0) ... (3,3), each [16][16]); gamma [128] fp32.
 struct Rec16 {
     static constexpr size_t KT = 0;
     static constexpr size_t QT = KT + kChunk * kD * 2;
     static constexpr size_t KB = QT + kChunk * kD * 2;
-    static constexpr size_t TH = KB + kD * kChunk * 2;
-    static constexpr size_t TL = TH + kChunk * kChunk * 2;
-    static constexpr size_t MH = TL + kChunk * kChunk * 2;
-    static constexpr size_t ML = MH + kChunk * kChunk * 2;
-    static constexpr size_t G = ML + kChunk * kChunk * 2;
+    static constexpr size_t TM = KB + kD * kChunk * 2;       // 4 matrices x 10 blocks
+    static constexpr size_t kBlock = 16 * 16 * 2;
+    static constexpr size_t G = TM + 4 * 10 * kBlock;
     static constexpr size_t BYTES = G + kD * 4;
 };
 static_assert(Rec16::BYTES % 256 == 0, "records stay 256-byte aligned");
-// the scan's loaders move a record as 16-byte pieces: 2048 of Kt / Qt, 3072 of
-// Kb^T / T / M, 32 of gamma, 256 threads
-static_assert(Rec16::KB / 16 == 2048 && (Rec16::G - Rec16::KB) / 16 == 12 * 256 &&
+// the scan's loaders move a record as 16-byte pieces: 2048 of Kt / Qt, 1024 of
+// Kb^T plus 1280 of the T / M blocks (9 per thread), 32 of gamma, 256 threads
+static_assert(Rec16::KB / 16 == 2048 && (Rec16::G - Rec16::KB) / 16 == 9 * 256 &&
                   Rec16::G / 16 + 32 == Rec16::BYTES / 16,
               "loader piece counts match the record layout");
+
+// index of the lower block (a, b), b <= a, in the record's block order
+__host__ __device__ constexpr int tri_block(int a, int b) { return a * (a + 1) / 2 + b; }
 
 }  // namespace
 
@@ -337,14 +339,17 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
 
     // ---- the rest of the record -------------------------------------------------
     // T = X diag(beta) (zero above the diagonal) and M as hi / lo: row r,
-    // columns 16ct + 4g .. +3 per lane
+    // columns 16ct + 4g .. +3 per lane, lower blocks (p, ct <= p) only
     {
-        uint16_t* th = reinterpret_cast<uint16_t*>(rec + Rec16::TH) + r * kChunk;
-        uint16_t* tl = reinterpret_cast<uint16_t*>(rec + Rec16::TL) + r * kChunk;
-        uint16_t* mh = reinterpret_cast<uint16_t*>(rec + Rec16::MH) + r * kChunk;
-        uint16_t* ml = reinterpret_cast<uint16_t*>(rec + Rec16::ML) + r * kChunk;
+        uint8_t* tm = rec + Rec16::TM + (size_t)n * 32 + 8 * gq;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
+            if (ct > p) continue;
+            const size_t blk = (size_t)tri_block(p, ct) * Rec16::kBlock;
+            uint2* th = reinterpret_cast<uint2*>(tm + 0 * 10 * Rec16::kBlock + blk);
+            uint2* tl = reinterpret_cast<uint2*>(tm + 1 * 10 * Rec16::kBlock + blk);
+            uint2* mh = reinterpret_cast<uint2*>(tm + 2 * 10 * Rec16::kBlock + blk);
+            uint2* ml = reinterpret_cast<uint2*>(tm + 3 * 10 * Rec16::kBlock + blk);
             float tv[4], mv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -352,9 +357,8 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
                 tv[e] = (col <= r) ? x_s[r * SP + col] * beta_s[col] : 0.f;
                 mv[e] = Mt[ct][e];
             }
-            const int o = 16 * ct + 4 * gq;
-            split4(tv, *reinterpret_cast<uint2*>(th + o), *reinterpret_cast<uint2*>(tl + o));
-            split4(mv, *reinterpret_cast<uint2*>(mh + o), *reinterpret_cast<uint2*>(ml + o));
+            split4(tv, *th, *tl);
+            split4(mv, *mh, *ml);
         }
     }
     // Kb^T through LDS: column r of the [channel][token] matrix, then rows out
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // =====================================================================
         // V of the slice: 64 tokens x 64 columns = 512 pieces of 8 columns, two
         // per thread (piece tid + 256 m: token piece >> 3, columns 8 (piece & 7))
-        u32x4 ra[8], rb[12], rv[2];
+        u32x4 ra[8], rb[9], rv[2];
         u32x4 rg = {0u, 0u, 0u, 0u};
         const int64_t vstride = (int64_t)H * kD;
         const uint16_t* vslice = v + ((int64_t)b * T * H + h) * kD + kCols * slice;
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         const u32x4* src_ = reinterpret_cast<const u32x4*>(                                      \
             ws + ((size_t)bh * nchunks + (cl_)) * Rec16::BYTES);                                 \
         _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) ra[m_] = src_[tid + 256 * m_];          \
-        _Pragma("unroll") for (int m_ = 0; m_ < 12; ++m_) rb[m_] = src_[2048 + tid + 256 * m_];  \
+        _Pragma("unroll") for (int m_ = 0; m_ < 9; ++m_) rb[m_] = src_[2048 + tid + 256 * m_];   \
         if (tid < 32) rg = src_[(Rec16::G / 16) + tid];                                          \
         _Pragma("unroll") for (int m_ = 0; m_ < 2; ++m_) {                                       \
             const int pc_ = tid + 256 * m_;                                                      \
@@ -452,6 +456,14 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                                                      (pc_ & 7) * 8);                             \
         }                                                                                        \
     } while (0)
+        // blocks (0,1) and (2,3) of T and M are read by the k32 products but
+        // never written by a record: zero them once
+        for (int idx = tid; idx < 4 * 2 * 16 * 4; idx += 256) {
+            const int mat = idx >> 7, blk = (idx >> 6) & 1, row = (idx >> 2) & 15, q4 = idx & 3;
+            uint16_t* base = mat == 0 ? th_s : mat == 1 ? tl_s : mat == 2 ? mh_s : ml_s;
+            const int r0 = blk ? 32 : 0, c0 = blk ? 48 : 16;
+            *reinterpret_cast<uint2*>(&base[(r0 + row) * TP + c0 + 4 * q4]) = uint2{0u, 0u};
+        }
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
             // Kt, Qt: pieces 0..1023 and 1024..2047, 16 per 128-channel row
@@ -466,23 +478,24 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 d2[1] = uint2{ra[m][2], ra[m][3]};
             }
             signal(&sync_s[0], lane);
-            // Kb^T (pieces 0..1023, 8 per 64-token row), T hi / lo, M hi / lo
-            // (512 pieces each), gamma
+            // Kb^T (pieces 0..1023, 8 per 64-token row), then the 40 lower blocks
+            // of T hi / lo, M hi / lo (32 pieces each: row = piece / 2), gamma
             wait_for(&sync_s[3], 4u * i, &sync_s[4]);
 #pragma unroll
-            for (int m = 0; m < 12; ++m) {
+            for (int m = 0; m < 9; ++m) {
                 const int idx = tid + 256 * m;
-                uint16_t* dst;
-                int j;
+                uint16_t* d;
                 if (idx < 1024) {
-                    dst = kb_s;
-                    j = idx;
+                    d = &kb_s[(idx >> 3) * TP + (idx & 7) * 8];
                 } else {
-                    const int part = (idx - 1024) >> 9;
-                    dst = part == 0 ? th_s : part == 1 ? tl_s : part == 2 ? mh_s : ml_s;
-                    j = (idx - 1024) & 511;
+                    const int bi = (idx - 1024) >> 5, pc = (idx - 1024) & 31;
+                    const int mat = bi / 10, t = bi % 10;
+                    const int a = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+                    const int bb = t - a * (a + 1) / 2;
+                    uint16_t* base = mat == 0 ? th_s : mat == 1 ? tl_s : mat == 2 ? mh_s : ml_s;
+                    d = &base[(16 * a + (pc >> 1)) * TP + 16 * bb + 8 * (pc & 1)];
                 }
-                uint2* d2 = reinterpret_cast<uint2*>(&dst[(j >> 3) * TP + (j & 7) * 8]);
+                uint2* d2 = reinterpret_cast<uint2*>(d);
                 d2[0] = uint2{rb[m][0], rb[m][1]};
                 d2[1] = uint2{rb[m][2], rb[m][3]};
             }
