@@ -46,12 +46,11 @@ using namespace b16;
 
 constexpr int kSlices = 2;             // value-column slices per head
 constexpr int kCols = kD / kSlices;    // value columns per scan workgroup
-// Row pitches of the record in the scan's LDS: 66 and 34 dwords.  A pitch of
-// 2 mod 4 dwords makes the 8-byte fragment reads of 16 rows x 4 k-groups
+// Row pitch of the V slice in the scan's LDS: 34 dwords.  A pitch of 2 mod 4
+// dwords makes the 8-byte fragment reads of 16 rows x 4 k-groups
 // conflict-free on gfx950 (measured: about 110-120 B/clk per CU, against 62
-// at 68 or 36 dwords).  Rows are then 8-byte aligned.
-constexpr int KP = kD + 4;
-constexpr int TP = kChunk + 4;
+// at 32 or 36 dwords).
+constexpr int VP = kCols + 4;
 constexpr int SP = kChunk + 1;         // fp32 pitch of A and X in the prep kernel
 constexpr float kLog2e = 1.4426950408889634f;  // decay sums are kept in log2 units
 
@@ -60,28 +59,45 @@ constexpr float kLog2e = 1.4426950408889634f;  // decay sums are kept in log2 un
 //   TF(a,b) = exp(sum_{b<a'<a} tau) for a - b >= 2, and gamma.
 enum { kEP = 0, kEK = 4, kIE = 8, kTF20 = 12, kTF30 = 13, kTF31 = 14, kGam = 15, kTabs = 16 };
 
-// Record of one (batch, head, chunk) in global memory, unpadded, bf16 unless
-// noted: Kt [64][128], Qt [64][128], Kb^T [128][64]; T hi, T lo, M hi, M lo as
-// their ten lower 16x16 blocks each (block (a, b), b <= a, in the order
-// (0,0) (1,0) (1,1) (2,0) ... (3,3), each [16][16]); gamma [128] fp32.
+// Record of one (batch, head, chunk) in global memory: the image of the scan
+// kernel's LDS, so that the scan's loaders copy it verbatim.  Every matrix is
+// stored as the k32 operand fragments the scan's products read: a fragment is
+// 16 rows x 32 k of bf16, 1 KB, lane (n, g) of the reading wave at byte
+// 16 (n + 16 g) holding row n with k = k0 + 4g + e (values 0..3) and
+// k0 + 16 + 4g + e (values 4..7), so that every fragment read is one
+// conflict-free 16-byte LDS read per lane.
+//   Kt, Qt:  fragment 4 rt + s = tokens 16 rt .., channels 32 s ..   (16 KB each)
+//   Kb^T:    fragment 2 t + s2 = channels 16 t .., tokens 32 s2 ..  (16 KB)
+//   T hi, T lo, M hi, M lo (5 KB each): the six fragments (rt, s2) = (0,0)
+//     (1,0) (2,0) (2,1) (3,0) (3,1) of the lower-triangular [token][token]
+//     matrix; (0,0) and (2,1) have zero values 4..7 (blocks above the
+//     diagonal) and are stored as half fragments, 8 bytes per lane;
+//   gamma [128] fp32.
 struct Rec16 {
+    static constexpr size_t kFrag = 1024;
     static constexpr size_t KT = 0;
-    static constexpr size_t QT = KT + kChunk * kD * 2;
-    static constexpr size_t KB = QT + kChunk * kD * 2;
-    static constexpr size_t TM = KB + kD * kChunk * 2;       // 4 matrices x 10 blocks
-    static constexpr size_t kBlock = 16 * 16 * 2;
-    static constexpr size_t G = TM + 4 * 10 * kBlock;
+    static constexpr size_t QT = KT + 16 * kFrag;
+    static constexpr size_t KB = QT + 16 * kFrag;
+    static constexpr size_t TM = KB + 16 * kFrag;
+    static constexpr size_t kTM = 5 * kFrag;                 // one of the four matrices
+    static constexpr size_t G = TM + 4 * kTM;
     static constexpr size_t BYTES = G + kD * 4;
 };
 static_assert(Rec16::BYTES % 256 == 0, "records stay 256-byte aligned");
-// the scan's loaders move a record as 16-byte pieces: 2048 of Kt / Qt, 1024 of
-// Kb^T plus 1280 of the T / M blocks (9 per thread), 32 of gamma, 256 threads
+// the scan's loaders move a record as 16-byte pieces: 2048 of Kt / Qt, then
+// 1024 of Kb^T plus 1280 of T / M (9 per thread), 32 of gamma, 256 threads
 static_assert(Rec16::KB / 16 == 2048 && (Rec16::G - Rec16::KB) / 16 == 9 * 256 &&
                   Rec16::G / 16 + 32 == Rec16::BYTES / 16,
               "loader piece counts match the record layout");
 
-// index of the lower block (a, b), b <= a, in the record's block order
-__host__ __device__ constexpr int tri_block(int a, int b) { return a * (a + 1) / 2 + b; }
+// fragment f = 0..5 of a T / M matrix: (rt, s2) and byte offset in the matrix
+__host__ __device__ constexpr int tm_rt(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
+__host__ __device__ constexpr int tm_s2(int f) { return f < 2 ? 0 : (f - 2) & 1; }
+__host__ __device__ constexpr bool tm_half(int f) { return f == 0 || f == 3; }
+__host__ __device__ constexpr int tm_off(int f) {
+    return f == 0 ? 0 : f == 1 ? 512 : f == 2 ? 1536 : f == 3 ? 2560 : f == 4 ? 3072 : 4096;
+}
+static_assert(tm_off(5) + 1024 == (int)Rec16::kTM, "T / M fragment offsets");
 
 }  // namespace
 
@@ -93,18 +109,23 @@ int chunk16_slices() { return kSlices; }
 // and the 32 channels 32s + 8gq + e (s = 0..3, e = 0..7), i.e. its A-operand
 // fragments of the four k32 steps over the 128 channels.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
+__global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
     uint8_t* __restrict__ ws) {
     __shared__ __align__(16) float tau_s[4][kD];      // block totals of g (log2 units)
     __shared__ __align__(16) float tab_s[kTabs][kD];  // factor tables
     __shared__ float beta_s[kChunk];
+    // Two areas, each used by two phases that a barrier separates, so that
+    // three workgroups fit on a CU (43 KB of LDS each):
+    // The column operands of KK / QK and X = (I + A)^-1 share one area (a
+    // barrier separates their uses), so that three workgroups fit on a CU.
+    __shared__ __align__(16) float u1_s[kChunk * SP];
     __shared__ float a_s[kChunk * SP];                 // diag(beta) strict-lower KK
-    __shared__ float x_s[kChunk * SP];                 // X = (I + A)^-1
-    // column operands of KK / QK; afterwards the Kb^T staging area
-    __shared__ __align__(16) bf16x8 zf_s[4][4][64];
-    uint16_t* kbT_s = reinterpret_cast<uint16_t*>(&zf_s[0][0][0]);
+    static_assert(sizeof(bf16x8) * 4 * 4 * 64 <= sizeof(float) * kChunk * SP,
+                  "column operands fit the shared area");
+    bf16x8 (*zf_s)[4][64] = reinterpret_cast<bf16x8 (*)[4][64]>(u1_s);
+    float* x_s = u1_s;
 
     const int cl = blockIdx.x % nchunks;
     const int bh = blockIdx.x / nchunks;
@@ -201,15 +222,32 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
     }
     __syncthreads();
 
-    // ---- decay factors; the Kt / Qt rows of the record ----------------------
+    // ---- decay factors; Kt, Qt and Kb^T of the record ------------------------
     // e0 = exp(Gam_r - Gam_{16p-1}) <= 1, z = exp(Gam_{16p+15} - Gam_r) <= 1;
     // rk0 = kh e0 and rq0 = qh e0 are the KK / QK row operands before the
     // per-block factor; Kt = rk0 EP_p, Qt = rq0 EP_p, Kb = kh z EK_p.
+    // Channels 8gq .. 8gq+3 and 8gq+4 .. +7 of k-step s land in lanes
+    // 2 (gq & 1) and 2 (gq & 1) + 1 of fragment (p, s), in the upper half of
+    // the values for gq >= 2.  Kb is transposed on the matrix cores: a product
+    // with a 0/1 selection matrix as B (value e of lane (j, gq) is 1 where
+    // 8 gq + e = 16 h + j) returns lane (j, g) the tokens 16p + 4g .. +3 of
+    // channel 32s + 16h + j, exactly: 8 bytes of Kb^T fragment (2s + h, p / 2).
     float rk0[32], rq0[32];
-    uint32_t kbw[16];  // this row of Kb, as bf16 pairs
     {
-        uint16_t* ktg = reinterpret_cast<uint16_t*>(rec + Rec16::KT) + r * kD;
-        uint16_t* qtg = reinterpret_cast<uint16_t*>(rec + Rec16::QT) + r * kD;
+        const size_t kq0 = (size_t)(16 * (2 * (gq & 1)) + n) * 16 + 8 * (gq >> 1);
+        uint8_t* ktg = rec + Rec16::KT + 4 * p * Rec16::kFrag + kq0;
+        uint8_t* qtg = rec + Rec16::QT + 4 * p * Rec16::kFrag + kq0;
+        uint8_t* kbg = rec + Rec16::KB + (p >> 1) * Rec16::kFrag + (n + 16 * gq) * 16 + 8 * (p & 1);
+        bf16x8 sel[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            u32x4 u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                u[w] = (8 * gq + 2 * w == 16 * hh + n ? 0x3f80u : 0u) |
+                       (8 * gq + 2 * w + 1 == 16 * hh + n ? 0x3f800000u : 0u);
+            sel[hh] = __builtin_bit_cast(bf16x8, u);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int cb = 32 * s + 8 * gq;
@@ -220,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
             *reinterpret_cast<f32x4*>(ek + 4) = *reinterpret_cast<const f32x4*>(&tab_s[kEK + p][cb + 4]);
             *reinterpret_cast<f32x4*>(ta) = *reinterpret_cast<const f32x4*>(&tau_s[p][cb]);
             *reinterpret_cast<f32x4*>(ta + 4) = *reinterpret_cast<const f32x4*>(&tau_s[p][cb + 4]);
-            uint32_t ktw[4], qtw[4];
+            uint32_t ktw[4], qtw[4], kbw[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const float kh0 = __builtin_bit_cast(float, pk[s][w] << 16) * ik;
@@ -240,11 +278,20 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
                 rq0[j + 1] = qh1 * e01;
                 ktw[w] = pack2(rk0[j] * ep[2 * w], rk0[j + 1] * ep[2 * w + 1]);
                 qtw[w] = pack2(rq0[j] * ep[2 * w], rq0[j + 1] * ep[2 * w + 1]);
-                kbw[4 * s + w] = pack2(zc[2 * w] * ek[2 * w], zc[2 * w + 1] * ek[2 * w + 1]);
+                kbw[w] = pack2(zc[2 * w] * ek[2 * w], zc[2 * w + 1] * ek[2 * w + 1]);
             }
-            *reinterpret_cast<u32x4*>(ktg + cb) = u32x4{ktw[0], ktw[1], ktw[2], ktw[3]};
-            *reinterpret_cast<u32x4*>(qtg + cb) = u32x4{qtw[0], qtw[1], qtw[2], qtw[3]};
+            *reinterpret_cast<uint2*>(ktg + s * Rec16::kFrag) = uint2{ktw[0], ktw[1]};
+            *reinterpret_cast<uint2*>(ktg + s * Rec16::kFrag + 256) = uint2{ktw[2], ktw[3]};
+            *reinterpret_cast<uint2*>(qtg + s * Rec16::kFrag) = uint2{qtw[0], qtw[1]};
+            *reinterpret_cast<uint2*>(qtg + s * Rec16::kFrag + 256) = uint2{qtw[2], qtw[3]};
             zf_s[p][s][lane] = pack8(zc);
+            const bf16x8 kbf = __builtin_bit_cast(bf16x8, u32x4{kbw[0], kbw[1], kbw[2], kbw[3]});
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const f32x4 t = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kbf, sel[hh]);
+                *reinterpret_cast<uint2*>(kbg + 2 * (2 * s + hh) * Rec16::kFrag) =
+                    uint2{pack2(t[0], t[1]), pack2(t[2], t[3])};
+            }
         }
     }
     __syncthreads();
@@ -339,17 +386,20 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
 
     // ---- the rest of the record -------------------------------------------------
     // T = X diag(beta) (zero above the diagonal) and M as hi / lo: row r,
-    // columns 16ct + 4g .. +3 per lane, lower blocks (p, ct <= p) only
+    // columns 16ct + 4g .. +3 per lane, lower blocks (p, ct <= p) only: value
+    // half ct & 1 of lane (n, g) of fragment (p, ct / 2)
     {
-        uint8_t* tm = rec + Rec16::TM + (size_t)n * 32 + 8 * gq;
+        uint8_t* tm = rec + Rec16::TM;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             if (ct > p) continue;
-            const size_t blk = (size_t)tri_block(p, ct) * Rec16::kBlock;
-            uint2* th = reinterpret_cast<uint2*>(tm + 0 * 10 * Rec16::kBlock + blk);
-            uint2* tl = reinterpret_cast<uint2*>(tm + 1 * 10 * Rec16::kBlock + blk);
-            uint2* mh = reinterpret_cast<uint2*>(tm + 2 * 10 * Rec16::kBlock + blk);
-            uint2* ml = reinterpret_cast<uint2*>(tm + 3 * 10 * Rec16::kBlock + blk);
+            const int f = p < 2 ? p : 2 + 2 * (p - 2) + (ct >> 1);
+            const size_t off = tm_off(f) + (tm_half(f) ? (size_t)lane * 8
+                                                       : (size_t)lane * 16 + 8 * (ct & 1));
+            uint2* th = reinterpret_cast<uint2*>(tm + 0 * Rec16::kTM + off);
+            uint2* tl = reinterpret_cast<uint2*>(tm + 1 * Rec16::kTM + off);
+            uint2* mh = reinterpret_cast<uint2*>(tm + 2 * Rec16::kTM + off);
+            uint2* ml = reinterpret_cast<uint2*>(tm + 3 * Rec16::kTM + off);
             float tv[4], mv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -361,27 +411,10 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
             split4(mv, *mh, *ml);
         }
     }
-    // Kb^T through LDS: column r of the [channel][token] matrix, then rows out
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int cb = 32 * s + 8 * gq;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            kbT_s[(cb + 2 * w) * kChunk + r] = (uint16_t)(kbw[4 * s + w] & 0xffffu);
-            kbT_s[(cb + 2 * w + 1) * kChunk + r] = (uint16_t)(kbw[4 * s + w] >> 16);
-        }
-    }
     if (p == 0) {
         float* gg = reinterpret_cast<float*>(rec + Rec16::G);
         gg[lane] = tab_s[kGam][lane];
         gg[lane + 64] = tab_s[kGam][lane + 64];
-    }
-    __syncthreads();
-    {
-        const u32x4* src = reinterpret_cast<const u32x4*>(kbT_s);
-        u32x4* dst = reinterpret_cast<u32x4*>(rec + Rec16::KB);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) dst[tid + 256 * m] = src[tid + 256 * m];
     }
 }
 
@@ -393,20 +426,25 @@ __global__ __launch_bounds__(256, 2) void kda_prep16_kernel(
 // rows of accumulator tiles 2s and 2s+1, so S, X and U feed the B operand from
 // registers.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 frag(const u32x4* base, int f, int lane) {
+    return __builtin_bit_cast(bf16x8, base[64 * f + lane]);
+}
+// T / M fragment f (half fragments carry zero values 4..7)
+__device__ __forceinline__ bf16x8 frag_tm(const u32x4* mat, int f, int lane) {
+    if (tm_half(f)) {
+        const uint2 x = reinterpret_cast<const uint2*>(mat + tm_off(f) / 16)[lane];
+        return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, 0u, 0u});
+    }
+    return __builtin_bit_cast(bf16x8, mat[tm_off(f) / 16 + lane]);
+}
+
 __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, float scale,
     const float* h_in, float* h_out, uint16_t* __restrict__ out, int T, int H, int chunk0,
     int nchunks) {
-    __shared__ __align__(16) uint16_t kt_s[kChunk * KP];  // Kt, [token][channel]
-    __shared__ __align__(16) uint16_t qt_s[kChunk * KP];  // Qt
-    __shared__ __align__(16) uint16_t kb_s[kD * TP];      // Kb^T, [channel][token]
-    __shared__ __align__(16) uint16_t th_s[kChunk * TP];  // T hi / lo, [token][token]
-    __shared__ __align__(16) uint16_t tl_s[kChunk * TP];
-    __shared__ __align__(16) uint16_t mh_s[kChunk * TP];  // M hi / lo
-    __shared__ __align__(16) uint16_t ml_s[kChunk * TP];
-    __shared__ __align__(16) float gam_s[kD];
-    __shared__ __align__(16) uint16_t vT_s[kCols * TP];   // V slice, [column][token]
-    // Kt/Qt ready; Kt/Qt consumed; rest ready; rest consumed; abort
+    __shared__ u32x4 rec_s[Rec16::BYTES / 16];             // the record, verbatim
+    __shared__ __align__(16) uint16_t v_s[kChunk * VP];    // V slice, [token][column]
+    // Kt/Qt/V ready; Kt/Qt/V consumed; rest ready; rest consumed; abort
     __shared__ unsigned sync_s[5];
 
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
@@ -456,62 +494,27 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                                                      (pc_ & 7) * 8);                             \
         }                                                                                        \
     } while (0)
-        // blocks (0,1) and (2,3) of T and M are read by the k32 products but
-        // never written by a record: zero them once
-        for (int idx = tid; idx < 4 * 2 * 16 * 4; idx += 256) {
-            const int mat = idx >> 7, blk = (idx >> 6) & 1, row = (idx >> 2) & 15, q4 = idx & 3;
-            uint16_t* base = mat == 0 ? th_s : mat == 1 ? tl_s : mat == 2 ? mh_s : ml_s;
-            const int r0 = blk ? 32 : 0, c0 = blk ? 48 : 16;
-            *reinterpret_cast<uint2*>(&base[(r0 + row) * TP + c0 + 4 * q4]) = uint2{0u, 0u};
-        }
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
-            // Kt, Qt: pieces 0..1023 and 1024..2047, 16 per 128-channel row
+            // Kt, Qt (pieces 0..2047) and V; tokens past the end of the
+            // sequence have zero V
             wait_for(&sync_s[1], 4u * i, &sync_s[4]);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int idx = tid + 256 * m;
-                uint16_t* dst = (idx < 1024) ? kt_s : qt_s;
-                const int j = idx & 1023;
-                uint2* d2 = reinterpret_cast<uint2*>(&dst[(j >> 4) * KP + (j & 15) * 8]);
-                d2[0] = uint2{ra[m][0], ra[m][1]};
-                d2[1] = uint2{ra[m][2], ra[m][3]};
-            }
-            signal(&sync_s[0], lane);
-            // Kb^T (pieces 0..1023, 8 per 64-token row), then the 40 lower blocks
-            // of T hi / lo, M hi / lo (32 pieces each: row = piece / 2), gamma
-            wait_for(&sync_s[3], 4u * i, &sync_s[4]);
-#pragma unroll
-            for (int m = 0; m < 9; ++m) {
-                const int idx = tid + 256 * m;
-                uint16_t* d;
-                if (idx < 1024) {
-                    d = &kb_s[(idx >> 3) * TP + (idx & 7) * 8];
-                } else {
-                    const int bi = (idx - 1024) >> 5, pc = (idx - 1024) & 31;
-                    const int mat = bi / 10, t = bi % 10;
-                    const int a = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-                    const int bb = t - a * (a + 1) / 2;
-                    uint16_t* base = mat == 0 ? th_s : mat == 1 ? tl_s : mat == 2 ? mh_s : ml_s;
-                    d = &base[(16 * a + (pc >> 1)) * TP + 16 * bb + 8 * (pc & 1)];
-                }
-                uint2* d2 = reinterpret_cast<uint2*>(d);
-                d2[0] = uint2{rb[m][0], rb[m][1]};
-                d2[1] = uint2{rb[m][2], rb[m][3]};
-            }
-            if (tid < 32) *reinterpret_cast<u32x4*>(&gam_s[4 * tid]) = rg;
-            // V transposed; tokens past the end of the sequence are zero
+            for (int m = 0; m < 8; ++m) rec_s[tid + 256 * m] = ra[m];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int pc = tid + 256 * m, tk = pc >> 3, c8 = (pc & 7) * 8;
+                const int pc = tid + 256 * m, tk = pc >> 3;
                 const bool ok = (int64_t)(chunk0 + i) * kChunk + tk < T;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t x = ok ? rv[m][w] : 0u;
-                    vT_s[(c8 + 2 * w) * TP + tk] = (uint16_t)(x & 0xffffu);
-                    vT_s[(c8 + 2 * w + 1) * TP + tk] = (uint16_t)(x >> 16);
-                }
+                uint2* d2 = reinterpret_cast<uint2*>(&v_s[tk * VP + (pc & 7) * 8]);
+                d2[0] = ok ? uint2{rv[m][0], rv[m][1]} : uint2{0u, 0u};
+                d2[1] = ok ? uint2{rv[m][2], rv[m][3]} : uint2{0u, 0u};
             }
+            signal(&sync_s[0], lane);
+            // Kb^T and T / M (pieces 2048 .. 4351), gamma
+            wait_for(&sync_s[3], 4u * i, &sync_s[4]);
+#pragma unroll
+            for (int m = 0; m < 9; ++m) rec_s[2048 + tid + 256 * m] = rb[m];
+            if (tid < 32) rec_s[Rec16::G / 16 + tid] = rg;
             signal(&sync_s[2], lane);
             if (i + 1 < nchunks) KDA_LOAD_ISSUE(i + 1);
         }
@@ -522,6 +525,31 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // =====================================================================
         const int w = wv - 4;
         const int j0 = kCols * slice + 16 * w;
+        const u32x4* kt_s = rec_s + Rec16::KT / 16;
+        const u32x4* qt_s = rec_s + Rec16::QT / 16;
+        const u32x4* kb_s = rec_s + Rec16::KB / 16;
+        const u32x4* th_s = rec_s + (Rec16::TM + 0 * Rec16::kTM) / 16;
+        const u32x4* tl_s = rec_s + (Rec16::TM + 1 * Rec16::kTM) / 16;
+        const u32x4* mh_s = rec_s + (Rec16::TM + 2 * Rec16::kTM) / 16;
+        const u32x4* ml_s = rec_s + (Rec16::TM + 3 * Rec16::kTM) / 16;
+        const float* gam_s = reinterpret_cast<const float*>(rec_s + Rec16::G / 16);
+        // V to accumulator layout on the matrix cores: fragment rows are tokens,
+        // k the 32 columns 32 (w / 2) ..; the 0/1 selection B (value e of lane
+        // (j, gq) is 1 where its column is 16 (w & 1) + j) returns lane (j, g)
+        // the tokens 16rt + 4g .. +3 of column 16w + j, exactly.
+        bf16x8 selv;
+        {
+            u32x4 u;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int e0 = 2 * x, e1 = 2 * x + 1;
+                const int c0 = (e0 < 4 ? 4 * gq + e0 : 16 + 4 * gq + e0 - 4);
+                const int c1 = (e1 < 4 ? 4 * gq + e1 : 16 + 4 * gq + e1 - 4);
+                u[x] = (c0 == 16 * (w & 1) + n ? 0x3f80u : 0u) |
+                       (c1 == 16 * (w & 1) + n ? 0x3f800000u : 0u);
+            }
+            selv = __builtin_bit_cast(bf16x8, u);
+        }
         f32x4 S[8];
         const float* hin = h_in ? h_in + (size_t)bh * kD * kD : nullptr;
 #pragma unroll
@@ -541,22 +569,28 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             // operand of the first and, transposed, as the A operand of the
             // second, with the same registers
             // (fragments of k-step s + 1 are read while step s multiplies)
-            f32x4 Pk[4], Pq[4];
+            f32x4 Pk[4], Pq[4], Vt[4];
+            bf16x8 fv[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) Pk[rt] = Pq[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 4; ++rt) {
+                Pk[rt] = Pq[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                fv[rt] = frag_row(v_s, VP, 16 * rt + n, 32 * (w >> 1), gq);
+            }
             bf16x8 fk[2][4], fq[2][4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                fk[0][rt] = frag_row(kt_s, KP, 16 * rt + n, 0, gq);
-                fq[0][rt] = frag_row(qt_s, KP, 16 * rt + n, 0, gq);
+                fk[0][rt] = frag(kt_s, 4 * rt, lane);
+                fq[0][rt] = frag(qt_s, 4 * rt, lane);
             }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Vt[rt] = mma(f32x4{0.f, 0.f, 0.f, 0.f}, fv[rt], selv);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s < 3) {
 #pragma unroll
                     for (int rt = 0; rt < 4; ++rt) {
-                        fk[(s + 1) & 1][rt] = frag_row(kt_s, KP, 16 * rt + n, 32 * (s + 1), gq);
-                        fq[(s + 1) & 1][rt] = frag_row(qt_s, KP, 16 * rt + n, 32 * (s + 1), gq);
+                        fk[(s + 1) & 1][rt] = frag(kt_s, 4 * rt + s + 1, lane);
+                        fq[(s + 1) & 1][rt] = frag(qt_s, 4 * rt + s + 1, lane);
                     }
                 }
                 // keep these reads ahead of this step's products
@@ -568,27 +602,16 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     Pq[rt] = mma(Pq[rt], bS, fq[s & 1][rt]);
                 }
             }
-            signal(&sync_s[1], lane);  // Kt, Qt consumed
+            signal(&sync_s[1], lane);  // Kt, Qt, V consumed
             wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4]);
 
-            // this lane's V: tokens 16rt + 4g .. +3 of column 16w + n
-            f32x4 Vt[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const uint2 x = *reinterpret_cast<const uint2*>(&vT_s[(16 * w + n) * TP + 16 * rt + 4 * gq]);
-                Vt[rt][0] = __builtin_bit_cast(float, x.x << 16);
-                Vt[rt][1] = __builtin_bit_cast(float, x.x & 0xffff0000u);
-                Vt[rt][2] = __builtin_bit_cast(float, x.y << 16);
-                Vt[rt][3] = __builtin_bit_cast(float, x.y & 0xffff0000u);
-            }
             // U = T (V - Kt S), both factors as hi + lo (T lower triangular);
             // the six T fragment pairs are read before X is split
             bf16x8 fth[6], ftl[6];
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
-                const int rt = f < 2 ? f : 2 + ((f - 2) >> 1), s2 = f < 2 ? 0 : (f - 2) & 1;
-                fth[f] = frag_row(th_s, TP, 16 * rt + n, 32 * s2, gq);
-                ftl[f] = frag_row(tl_s, TP, 16 * rt + n, 32 * s2, gq);
+                fth[f] = frag_tm(th_s, f, lane);
+                ftl[f] = frag_tm(tl_s, f, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 bh_[2], bl_[2];
@@ -598,7 +621,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             f32x4 U[4];
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
-                const int rt = f < 2 ? f : 2 + ((f - 2) >> 1), s2 = f < 2 ? 0 : (f - 2) & 1;
+                const int rt = tm_rt(f), s2 = tm_s2(f);
                 if (s2 == 0) U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 U[rt] = mma(U[rt], fth[f], bh_[s2]);
                 U[rt] = mma(U[rt], ftl[f], bh_[s2]);
@@ -608,9 +631,8 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             bf16x8 fmh[6], fml[6];
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
-                const int rt = f < 2 ? f : 2 + ((f - 2) >> 1), s2 = f < 2 ? 0 : (f - 2) & 1;
-                fmh[f] = frag_row(mh_s, TP, 16 * rt + n, 32 * s2, gq);
-                fml[f] = frag_row(ml_s, TP, 16 * rt + n, 32 * s2, gq);
+                fmh[f] = frag_tm(mh_s, f, lane);
+                fml[f] = frag_tm(ml_s, f, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
 
@@ -625,15 +647,15 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) fkb[0][t][s2] = frag_row(kb_s, TP, 16 * t + n, 32 * s2, gq);
+                for (int s2 = 0; s2 < 2; ++s2) fkb[0][t][s2] = frag(kb_s, 2 * t + s2, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 o = Pq[rt];
 #pragma unroll
                 for (int f = 0; f < 6; ++f) {
-                    const int frt = f < 2 ? f : 2 + ((f - 2) >> 1), s2 = f < 2 ? 0 : (f - 2) & 1;
-                    if (frt != rt) continue;
+                    if (tm_rt(f) != rt) continue;
+                    const int s2 = tm_s2(f);
                     o = mma(o, bh_[s2], fmh[f]);
                     o = mma(o, bh_[s2], fml[f]);
                     o = mma(o, bl_[s2], fmh[f]);
@@ -650,7 +672,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     for (int t = 0; t < 4; ++t)
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2)
-                            fkb[1][t][s2] = frag_row(kb_s, TP, 16 * (t + 4) + n, 32 * s2, gq);
+                            fkb[1][t][s2] = frag(kb_s, 2 * (t + 4) + s2, lane);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
