@@ -442,7 +442,12 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, float scale,
     const float* h_in, float* h_out, uint16_t* __restrict__ out, int T, int H, int chunk0,
     int nchunks) {
-    __shared__ u32x4 rec_s[Rec16::BYTES / 16];             // the record, verbatim
+    // The record, verbatim: Kt / Qt once, the rest (Kb^T, T / M, gamma) in two
+    // buffers by chunk parity, so that the rest of chunk i + 1 is in place
+    // while chunk i is scanned.
+    constexpr int kRest = (Rec16::BYTES - Rec16::KB) / 16;  // pieces
+    __shared__ u32x4 kq_s[Rec16::KB / 16];
+    __shared__ u32x4 rest_s[2][kRest];
     __shared__ __align__(16) uint16_t v_s[kChunk * VP];    // V slice, [token][column]
     // Kt/Qt/V ready; Kt/Qt/V consumed; rest ready; rest consumed; abort
     __shared__ unsigned sync_s[5];
@@ -494,13 +499,24 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                                                      (pc_ & 7) * 8);                             \
         }                                                                                        \
     } while (0)
+        // Per chunk i: the rest into buffer i & 1 (released by chunk i - 2),
+        // Kt / Qt / V once chunk i - 1 has multiplied them, and the loads of
+        // chunk i + 1 once chunk i - 1 is complete, i.e. while the scan waves
+        // run the Kt / Qt products of chunk i, which touch no global memory
+        // (loads issued beside the output stores hold those up).
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
+            if (i >= 2) wait_for(&sync_s[3], 4u * (i - 1), &sync_s[4]);
+            u32x4* rs = rest_s[i & 1];
+#pragma unroll
+            for (int m = 0; m < 9; ++m) rs[tid + 256 * m] = rb[m];
+            if (tid < 32) rs[(Rec16::G - Rec16::KB) / 16 + tid] = rg;
+            signal(&sync_s[2], lane);
             // Kt, Qt (pieces 0..2047) and V; tokens past the end of the
             // sequence have zero V
             wait_for(&sync_s[1], 4u * i, &sync_s[4]);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) rec_s[tid + 256 * m] = ra[m];
+            for (int m = 0; m < 8; ++m) kq_s[tid + 256 * m] = ra[m];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int pc = tid + 256 * m, tk = pc >> 3;
@@ -510,13 +526,10 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 d2[1] = ok ? uint2{rv[m][2], rv[m][3]} : uint2{0u, 0u};
             }
             signal(&sync_s[0], lane);
-            // Kb^T and T / M (pieces 2048 .. 4351), gamma
-            wait_for(&sync_s[3], 4u * i, &sync_s[4]);
-#pragma unroll
-            for (int m = 0; m < 9; ++m) rec_s[2048 + tid + 256 * m] = rb[m];
-            if (tid < 32) rec_s[Rec16::G / 16 + tid] = rg;
-            signal(&sync_s[2], lane);
-            if (i + 1 < nchunks) KDA_LOAD_ISSUE(i + 1);
+            if (i + 1 < nchunks) {
+                wait_for(&sync_s[3], 4u * i, &sync_s[4]);
+                KDA_LOAD_ISSUE(i + 1);
+            }
         }
 #undef KDA_LOAD_ISSUE
     } else {
@@ -525,14 +538,8 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // =====================================================================
         const int w = wv - 4;
         const int j0 = kCols * slice + 16 * w;
-        const u32x4* kt_s = rec_s + Rec16::KT / 16;
-        const u32x4* qt_s = rec_s + Rec16::QT / 16;
-        const u32x4* kb_s = rec_s + Rec16::KB / 16;
-        const u32x4* th_s = rec_s + (Rec16::TM + 0 * Rec16::kTM) / 16;
-        const u32x4* tl_s = rec_s + (Rec16::TM + 1 * Rec16::kTM) / 16;
-        const u32x4* mh_s = rec_s + (Rec16::TM + 2 * Rec16::kTM) / 16;
-        const u32x4* ml_s = rec_s + (Rec16::TM + 3 * Rec16::kTM) / 16;
-        const float* gam_s = reinterpret_cast<const float*>(rec_s + Rec16::G / 16);
+        const u32x4* kt_s = kq_s + Rec16::KT / 16;
+        const u32x4* qt_s = kq_s + Rec16::QT / 16;
         // V to accumulator layout on the matrix cores: fragment rows are tokens,
         // k the 32 columns 32 (w / 2) ..; the 0/1 selection B (value e of lane
         // (j, gq) is 1 where its column is 16 (w & 1) + j) returns lane (j, g)
@@ -604,6 +611,13 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             }
             signal(&sync_s[1], lane);  // Kt, Qt, V consumed
             wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4]);
+            const u32x4* rs = rest_s[i & 1];
+            const u32x4* kb_s = rs;
+            const u32x4* th_s = rs + (Rec16::TM - Rec16::KB + 0 * Rec16::kTM) / 16;
+            const u32x4* tl_s = rs + (Rec16::TM - Rec16::KB + 1 * Rec16::kTM) / 16;
+            const u32x4* mh_s = rs + (Rec16::TM - Rec16::KB + 2 * Rec16::kTM) / 16;
+            const u32x4* ml_s = rs + (Rec16::TM - Rec16::KB + 3 * Rec16::kTM) / 16;
+            const float* gam_s = reinterpret_cast<const float*>(rs + (Rec16::G - Rec16::KB) / 16);
 
             // U = T (V - Kt S), both factors as hi + lo (T lower triangular);
             // the six T fragment pairs are read before X is split
