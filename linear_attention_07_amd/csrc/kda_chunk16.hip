@@ -127,11 +127,25 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     bf16x8 (*zf_s)[4][64] = reinterpret_cast<bf16x8 (*)[4][64]>(u1_s);
     float* x_s = u1_s;
 
-    const int cl = blockIdx.x % nchunks;
-    const int bh = blockIdx.x / nchunks;
+    // Chunk-major order, XCD-aware: workgroups are dealt round-robin to the 8
+    // XCDs, so the k-th workgroup of XCD x takes chunk k / (BH / 8) and head
+    // x BH / 8 + k % (BH / 8).  The heads of one chunk then run together, and
+    // consecutive heads on one XCD: their q / k / g rows are one contiguous
+    // stream and a cache line of beta (32 heads of one token) is fetched by
+    // few XCDs instead of once per head.  Records are stored chunk-major too.
+    const int BH = gridDim.x / nchunks;
+    int cl, bh;
+    if (BH % 8 == 0) {
+        const int id = blockIdx.x, hx = BH / 8, k = id / 8;
+        cl = k / hx;
+        bh = (id % 8) * hx + k % hx;
+    } else {
+        cl = blockIdx.x / BH;
+        bh = blockIdx.x % BH;
+    }
     const int h = bh % H, b = bh / H;
     const int c = chunk0 + cl;
-    uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * Rec16::BYTES;
+    uint8_t* rec = ws + ((size_t)cl * BH + bh) * Rec16::BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int p = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -455,6 +469,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
     // both slices of a head go to one XCD, so the records that both read come
     // from HBM once.
+    const int BH = gridDim.x / kSlices;  // records are stored chunk-major
     int slice, bh;
     {
         const int nblk = gridDim.x, id = blockIdx.x;
@@ -488,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 #define KDA_LOAD_ISSUE(cl_)                                                                      \
     do {                                                                                         \
         const u32x4* src_ = reinterpret_cast<const u32x4*>(                                      \
-            ws + ((size_t)bh * nchunks + (cl_)) * Rec16::BYTES);                                 \
+            ws + ((size_t)(cl_) * BH + bh) * Rec16::BYTES);                                      \
         _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) ra[m_] = src_[tid + 256 * m_];          \
         _Pragma("unroll") for (int m_ = 0; m_ < 9; ++m_) rb[m_] = src_[2048 + tid + 256 * m_];   \
         if (tid < 32) rg = src_[(Rec16::G / 16) + tid];                                          \
