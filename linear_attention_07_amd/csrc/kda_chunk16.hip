@@ -24,14 +24,14 @@
 //   in parallel.  It normalises q and k, forms the decay sums and factor
 //   tables, the KK / QK blocks on MFMA, the inverse of I + A in fp32, and
 //   writes the chunk's record: Kt, Qt, Kb^T (bf16), T and M (bf16 hi + lo) and
-//   gamma.
+//   gamma, laid out as the scan kernel's LDS image.
 // scan (kda_scan16_kernel): one workgroup per (batch, head, 64 value columns),
-//   walking the chunks in order.  Four loader waves stream each record from
+//   walking the chunks in order.  Four loader waves copy each record from
 //   global memory into LDS one chunk ahead; four scan waves each keep a
-//   128 x 16 fp32 slice of the state in registers and run the three products
-//   of the chunk on MFMA.  The two roles hand the record over through LDS
-//   counters (Kt / Qt first, the rest second), so the scan waves never wait
-//   for a workgroup barrier.
+//   128 x 16 fp32 slice of the state in registers and run the chunk's products
+//   on MFMA.  The two roles hand the record over through LDS counters (Kt / Qt
+//   / V first, the rest second, the rest in two buffers by chunk parity), so
+//   the scan waves never wait for a workgroup barrier.
 //
 // Precision: Kt, Qt, Kb and the state enter the products as bf16; V - Kt S,
 // T, M and U as bf16 hi + lo pairs (about 16 mantissa bits, three products
