@@ -549,8 +549,10 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 #undef KDA_LOAD_ISSUE
     } else {
         // =====================================================================
-        // scan waves
+        // scan waves: they carry the serial chain, so they win issue over the
+        // loader wave that shares their SIMD
         // =====================================================================
+        __builtin_amdgcn_s_setprio(3);
         const int w = wv - 4;
         const int j0 = kCols * slice + 16 * w;
         const u32x4* kt_s = kq_s + Rec16::KT / 16;
