@@ -463,8 +463,9 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     __shared__ u32x4 kq_s[Rec16::KB / 16];
     __shared__ u32x4 rest_s[2][kRest];
     __shared__ __align__(16) uint16_t v_s[kChunk * VP];    // V slice, [token][column]
-    // Kt/Qt/V ready; Kt/Qt/V consumed; rest ready; rest consumed; abort
-    __shared__ unsigned sync_s[5];
+    // Kt/Qt/V ready; Kt/Qt/V consumed; rest ready; rest consumed; abort;
+    // output stored
+    __shared__ unsigned sync_s[6];
 
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
     // both slices of a head go to one XCD, so the records that both read come
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
 
-    if (tid < 5) sync_s[tid] = 0u;
+    if (tid < 6) sync_s[tid] = 0u;
     __syncthreads();  // the only workgroup barrier: roles split below
 
     if (wv < 4) {
@@ -516,9 +517,10 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     } while (0)
         // Per chunk i: the rest into buffer i & 1 (released by chunk i - 2),
         // Kt / Qt / V once chunk i - 1 has multiplied them, and the loads of
-        // chunk i + 1 once chunk i - 1 is complete, i.e. while the scan waves
-        // run the Kt / Qt products of chunk i, which touch no global memory
-        // (loads issued beside the output stores hold those up).
+        // chunk i + 1 once the output of chunk i - 1 is stored: the burst of
+        // loads then runs beside the state update of chunk i - 1 and the
+        // products of chunk i, which touch no global memory (loads issued
+        // beside the output stores hold those up).
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
             if (i >= 2) wait_for(&sync_s[3], 4u * (i - 1), &sync_s[4]);
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             }
             signal(&sync_s[0], lane);
             if (i + 1 < nchunks) {
-                wait_for(&sync_s[3], 4u * i, &sync_s[4]);
+                wait_for(&sync_s[5], 4u * i, &sync_s[4]);
                 KDA_LOAD_ISSUE(i + 1);
             }
         }
@@ -696,6 +698,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     *reinterpret_cast<uint2*>(outc + tk * rstride) =
                         uint2{pack2(scale * o[0], scale * o[1]), pack2(scale * o[2], scale * o[3])};
             }
+            signal(&sync_s[5], lane);  // the output is stored
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 if (half == 0) {
