@@ -98,11 +98,11 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float*
         overlap(out, io_bytes, hT, state_bytes))
         return KDA_ERR_INVALID_ARG;
 
-    if constexpr (!F32)
-        if ((int64_t)B * H * kda::chunk16_slices() > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const int slices = F32 ? kda::chunk_f32_slices() : kda::chunk16_slices();
+    if ((int64_t)B * H * slices > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
     constexpr bool v16 = !F32;  // bf16: prep16 / scan16; fp32 I/O: the fp32 kernels
     const int nch = (T + 63) / 64;
-    const size_t rec = v16 ? kda::chunk16_record_bytes() : kda::chunk_record_bytes(F32);
+    const size_t rec = v16 ? kda::chunk16_record_bytes() : kda::chunk_f32_record_bytes();
     const size_t per_chunk = (size_t)B * H * rec;
     int seg = (int)(workspace_budget() / per_chunk);
     if (seg < 1) seg = 1;
@@ -137,10 +137,14 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float*
                      ? kda::launch_scan16(ws, v, h_in, h_out, out, scale, B, T, H, c0, n, stream)
                      : e1;
         } else {
-            e1 = kda::launch_chunk_prep<F32>(q, k, g, beta, B, T, H, c0, n, ws, stream);
-            e2 = e1 == hipSuccess ? kda::launch_chunk_scan<F32>(ws, v, h_in, h_out, out, scale, B,
-                                                                 T, H, c0, n, stream)
-                                  : e1;
+            e1 = kda::launch_chunk_prep_f32(static_cast<const float*>(q),
+                                            static_cast<const float*>(k), g, beta, B, T, H, c0, n,
+                                            ws, stream);
+            e2 = e1 == hipSuccess
+                     ? kda::launch_chunk_scan_f32(ws, static_cast<const float*>(v), h_in, h_out,
+                                                  static_cast<float*>(out), scale, B, T, H, c0, n,
+                                                  stream)
+                     : e1;
         }
         if (e2 != hipSuccess) {
             st = KDA_ERR_HIP;

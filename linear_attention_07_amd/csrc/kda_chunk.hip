@@ -1,6 +1,6 @@
-// Chunkwise-parallel KDA prefill (the pages' chunk_kda) for fp32 q/k/v/o.
-// Only the fp32 instantiation (Prec<true>, fp32 matrix-core products) is
-// built; bf16 inputs take the prep16 / scan16 kernels.
+// Chunkwise-parallel KDA prefill (the pages' chunk_kda) for fp32 q/k/v/o, in
+// fp32 arithmetic throughout (16x16x4 fp32 matrix-core products).  bf16 inputs
+// take the kernels of kda_chunk16.hip.
 //
 // The recurrence (Kimi-K3 深度解析 blog, section 三) is evaluated 64 tokens at a
 // time.  The chunk form below is an exact rearrangement of it; the blog's
@@ -31,133 +31,83 @@
 //                 5 each): finite in fp32 and bf16 because g >= -5.
 // Values that underflow are bounded by the true (tiny) products.
 //
-// Precision.  Products whose result reaches the output directly use the exact
-// bf16 inputs or bf16 hi + lo pairs (about 16 mantissa bits): T and MT are kept
-// as hi/lo pairs, T V and MT V use the bf16 V exactly, U enters the state update
-// as hi + lo.  The in-chunk inverse is done in fp32.
+// Precision.  Every operand and every product is fp32 (the in-chunk inverse
+// included), so the result matches the recurrence to fp32 rounding.
 //
 // Two kernels:
 //   prep (one workgroup per chunk, fully parallel) computes W, Q', Kb^T, T, MT
 //        and gamma from q, k, g, beta and writes them to a per-chunk record;
 //   scan (one workgroup per head and 64 value columns) walks the chunks in
-//        order with its slice of S in registers, on matrix cores.
+//        order with its slice of S in registers, on matrix cores, reading each
+//        record straight from global memory (this path serves small fp32
+//        problems).
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
+namespace {
 
-template <bool F32>
-struct Rec {
-    using st = typename Prec<F32>::st_t;
-    static constexpr size_t kLo = F32 ? 0 : 1;  // bf16 keeps lo parts of T, MT
-    static constexpr size_t W = 0;                                   // [64][128] W
-    static constexpr size_t QP = W + kChunk * kD * sizeof(st);       // [64][128] Q'
-    static constexpr size_t KT = QP + kChunk * kD * sizeof(st);      // [128][64] Kb^T
-    static constexpr size_t TH = KT + kD * kChunk * sizeof(st);      // [64][64]  T (hi)
-    static constexpr size_t TL = TH + kChunk * kChunk * sizeof(st);  // [64][64]  T lo
-    static constexpr size_t MH = TL + kLo * kChunk * kChunk * sizeof(st);  // MT (hi)
-    static constexpr size_t ML = MH + kChunk * kChunk * sizeof(st);  // MT lo
-    static constexpr size_t G = ML + kLo * kChunk * kChunk * sizeof(st);   // [128] gamma
+using P = Prec<true>;
+using F8 = P::F8;
+using F4 = P::F4;
+
+// Record of one (batch, head, chunk), fp32.
+struct RecF {
+    static constexpr size_t W = 0;                                      // [64][128] W
+    static constexpr size_t QP = W + kChunk * kD * sizeof(float);       // [64][128] Q'
+    static constexpr size_t KT = QP + kChunk * kD * sizeof(float);      // [128][64] Kb^T
+    static constexpr size_t TH = KT + kD * kChunk * sizeof(float);      // [64][64]  T
+    static constexpr size_t MH = TH + kChunk * kChunk * sizeof(float);  // [64][64]  MT
+    static constexpr size_t G = MH + kChunk * kChunk * sizeof(float);   // [128] gamma
     static constexpr size_t BYTES = ((G + kD * sizeof(float)) + 255) / 256 * 256;
 };
-
-size_t chunk_record_bytes(bool f32) { return f32 ? Rec<true>::BYTES : Rec<false>::BYTES; }
 
 constexpr int kScanSlices = 2;          // value-column slices per head
 constexpr int kSliceCols = kD / kScanSlices;
 constexpr int kScanThreads = 64 * (kSliceCols / 16);
-int scan_slices() { return kScanSlices; }
 
 // k32 A-operand fragment of row `row` of a row-major matrix: values 0..3 carry
 // k = k0 + 4g + e, values 4..7 carry k = k0 + 16 + 4g + e.
-template <bool F32>
-__device__ __forceinline__ typename Prec<F32>::F8 frag_row(const typename Prec<F32>::st_t* base,
-                                                           int pitch, int row, int k0, int gq) {
-    typename Prec<F32>::F8 f;
-    const auto* p = base + (size_t)row * pitch + k0 + 4 * gq;
-    if constexpr (F32) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 16);
-        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    } else {
-        const uint2 a = *reinterpret_cast<const uint2*>(p);
-        const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
-        const uint4 u = {a.x, a.y, b.x, b.y};
-        f.v = __builtin_bit_cast(bf16x8, u);
-    }
+__device__ __forceinline__ F8 frag_row(const float* base, int pitch, int row, int k0, int gq) {
+    F8 f;
+    const float* p = base + (size_t)row * pitch + k0 + 4 * gq;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 16);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
     return f;
 }
 
 // k32 B-operand fragment of column `col` of a row-major [k][col] matrix, with
 // the same k order as frag_row.
-template <bool F32>
-__device__ __forceinline__ typename Prec<F32>::F8 frag_col(const typename Prec<F32>::st_t* base,
-                                                           int pitch, int col, int k0, int gq) {
-    typename Prec<F32>::F8 f;
-    const auto* p = base + (size_t)(k0 + 4 * gq) * pitch + col;
+__device__ __forceinline__ F8 frag_col(const float* base, int pitch, int col, int k0, int gq) {
+    F8 f;
+    const float* p = base + (size_t)(k0 + 4 * gq) * pitch + col;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        if constexpr (F32) {
-            f.v[e] = p[(size_t)e * pitch];
-            f.v[4 + e] = p[(size_t)(16 + e) * pitch];
-        } else {
-            f.v[e] = __builtin_bit_cast(__bf16, p[(size_t)e * pitch]);
-            f.v[4 + e] = __builtin_bit_cast(__bf16, p[(size_t)(16 + e) * pitch]);
-        }
+        f.v[e] = p[(size_t)e * pitch];
+        f.v[4 + e] = p[(size_t)(16 + e) * pitch];
     }
     return f;
 }
 
-// acc += A B with A given in fp32 and split into bf16 hi + lo (two products);
-// in fp32 mode a single fp32 product.
-template <bool F32>
-__device__ __forceinline__ f32x4 mma16_split_a(f32x4 acc, f32x4 a, const typename Prec<F32>::F4& b) {
-    using P = Prec<F32>;
-    if constexpr (F32) {
-        return P::mma16(acc, P::pack4(a), b);
-    } else {
-        f32x4 hi, lo;
-        split_bf16(a, hi, lo);
-        acc = P::mma16(acc, P::pack4(hi), b);
-        return P::mma16(acc, P::pack4(lo), b);
-    }
-}
+}  // namespace
 
-// acc += A B with both operands split (three products: hi*hi + lo*hi + hi*lo).
-template <bool F32>
-__device__ __forceinline__ f32x4 mma16_split_ab(f32x4 acc, f32x4 a, f32x4 b) {
-    using P = Prec<F32>;
-    if constexpr (F32) {
-        return P::mma16(acc, P::pack4(a), P::pack4(b));
-    } else {
-        f32x4 ah, al, bh, bl;
-        split_bf16(a, ah, al);
-        split_bf16(b, bh, bl);
-        const auto fah = P::pack4(ah), fbh = P::pack4(bh);
-        acc = P::mma16(acc, fah, fbh);
-        acc = P::mma16(acc, P::pack4(al), fbh);
-        return P::mma16(acc, fah, P::pack4(bl));
-    }
-}
+size_t chunk_f32_record_bytes() { return RecF::BYTES; }
+int chunk_f32_slices() { return kScanSlices; }
 
 // ---------------------------------------------------------------------------
 // prep: one workgroup = one chunk of one (b, h).  Wave a owns chunk rows
 // 16a..16a+15; lane (n = lane%16, g = lane/16) owns row 16a+n and the 32
 // channels 32s + 8g + e (s, e = 0..3, 0..7), i.e. exactly the A-operand
 // fragment of that row for the four k32 steps over the 128 channels.
-// Two workgroups fit on a CU in bf16 mode (about 77 KB of LDS each).
 // ---------------------------------------------------------------------------
-template <bool F32>
-__global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
-    const typename Prec<F32>::io_t* __restrict__ q, const typename Prec<F32>::io_t* __restrict__ k,
-    const float* __restrict__ g, const float* __restrict__ beta, int T, int H, int chunk0,
-    int nchunks, uint8_t* __restrict__ ws) {
-    using P = Prec<F32>;
-    using PF = Prec<true>;
-    using st = typename P::st_t;
-    using F8 = typename P::F8;
-    using R = Rec<F32>;
+__global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
+    uint8_t* __restrict__ ws) {
+    using st = float;
+    using R = RecF;
 
     const int cl = blockIdx.x % nchunks;
     const int bh = blockIdx.x / nchunks;
@@ -169,9 +119,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
     st* QPg = reinterpret_cast<st*>(rec + R::QP);
     st* KTg = reinterpret_cast<st*>(rec + R::KT);
     st* THg = reinterpret_cast<st*>(rec + R::TH);
-    st* TLg = reinterpret_cast<st*>(rec + R::TL);
     st* MHg = reinterpret_cast<st*>(rec + R::MH);
-    st* MLg = reinterpret_cast<st*>(rec + R::ML);
     float* Gg = reinterpret_cast<float*>(rec + R::G);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -201,7 +149,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
     // column operands of the decay-weighted products, later X = (I + A)^-1
     // and T = X diag(beta)
     __shared__ __align__(16) uint8_t zx_raw[kZfBytes > kXBytes ? kZfBytes : kXBytes];
-    // Kt (bf16 operand) and A, later reused for M W
+    // Kt and A, later reused for M W
     __shared__ __align__(16) uint8_t ka_raw[kKaBytes];
     F8(*zf_s)[4][64] = reinterpret_cast<F8(*)[4][64]>(zx_raw);
     float* x_s = reinterpret_cast<float*>(zx_raw);
@@ -299,15 +247,15 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
             *reinterpret_cast<float4*>(ek + 4) = *reinterpret_cast<const float4*>(&tab_s[kEK + wv][cb + 4]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) ta[e] = tau_s[wv][cb + e];
-            st kt8[8];
+            float kt8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 8 * s + e;
                 const float e0 = fast_exp(lam[j]);
                 const float z = fast_exp(ta[e] - lam[j]);
                 zc[j] = kf[j] * z;
-                KTg[(size_t)(cb + e) * kChunk + r] = P::to_st(kf[j] * z * ek[e]);
-                kt8[e] = P::to_st(kf[j] * e0 * ep[e]);
+                KTg[(size_t)(cb + e) * kChunk + r] = kf[j] * z * ek[e];
+                kt8[e] = kf[j] * e0 * ep[e];
                 qtil[j] = qf[j] * e0 * ep[e];
                 kf[j] *= e0;  // rk0
                 qf[j] *= e0;  // rq0
@@ -385,37 +333,30 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
             const int a = wv, bb = wv - d;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int cc = bb; cc < a; ++cc) {
-                typename PF::F4 fa, fb;
+                F4 fa, fb;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     fa.v[e] = a_s[(16 * a + n) * SP + 16 * cc + 4 * gq + e];
                     fb.v[e] = x_s[(16 * cc + 4 * gq + e) * SP + 16 * bb + n];
                 }
-                acc = PF::mma16(acc, fa, fb);
+                acc = P::mma16(acc, fa, fb);
             }
-            typename PF::F4 fx;
+            F4 fx;
 #pragma unroll
             for (int e = 0; e < 4; ++e) fx.v[e] = x_s[(16 * a + n) * SP + 16 * a + 4 * gq + e];
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 xab = PF::mma16(zero, fx, PF::pack4(acc));
+            const f32x4 xab = P::mma16(zero, fx, P::pack4(acc));
 #pragma unroll
             for (int e = 0; e < 4; ++e) x_s[(16 * a + 4 * gq + e) * SP + 16 * bb + n] = -xab[e];
         }
         __syncthreads();
     }
-    // T = X diag(beta), zero above the diagonal; write T (hi / lo)
+    // T = X diag(beta), zero above the diagonal
     for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
         const int rr = idx >> 6, cc = idx & 63;
         const float tv = (cc <= rr) ? x_s[rr * SP + cc] * beta_s[cc] : 0.f;
         x_s[rr * SP + cc] = tv;
-        if constexpr (F32) {
-            THg[idx] = tv;
-        } else {
-            float hi, lo;
-            split_bf16(tv, hi, lo);
-            THg[idx] = f2bf(hi);
-            TLg[idx] = f2bf(lo);
-        }
+        THg[idx] = tv;
     }
     __syncthreads();
 
@@ -430,19 +371,18 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
 #pragma unroll
             for (int kb = 0; kb <= rt; ++kb) {
                 f32x4 ta;
-                typename P::F4 kv;
+                F4 kv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     ta[e] = x_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
-                    if constexpr (F32) kv.v[e] = kt_s[(16 * kb + 4 * gq + e) * KTP + col];
-                    else kv.v[e] = (short)kt_s[(16 * kb + 4 * gq + e) * KTP + col];
+                    kv.v[e] = kt_s[(16 * kb + 4 * gq + e) * KTP + col];
                 }
-                acc = mma16_split_a<F32>(acc, ta, kv);
+                acc = P::mma16(acc, P::pack4(ta), kv);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Wt[rt][ct][e] = P::from_st(P::to_st(acc[e]));  // W as the scan sees it
-                Wg[(size_t)(16 * rt + 4 * gq + e) * kD + col] = P::to_st(acc[e]);
+                Wt[rt][ct][e] = acc[e];
+                Wg[(size_t)(16 * rt + 4 * gq + e) * kD + col] = acc[e];
             }
         }
     }
@@ -458,20 +398,10 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
                 ma[e] = m_s[(16 * wv + n) * SP + 16 * kb + 4 * gq + e];
                 tb[e] = x_s[(16 * kb + 4 * gq + e) * SP + 16 * ct + n];
             }
-            acc = mma16_split_ab<F32>(acc, ma, tb);
+            acc = P::mma16(acc, P::pack4(ma), P::pack4(tb));
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t idx = (size_t)(16 * wv + 4 * gq + e) * kChunk + 16 * ct + n;
-            if constexpr (F32) {
-                MHg[idx] = acc[e];
-            } else {
-                float hi, lo;
-                split_bf16(acc[e], hi, lo);
-                MHg[idx] = f2bf(hi);
-                MLg[idx] = f2bf(lo);
-            }
-        }
+        for (int e = 0; e < 4; ++e) MHg[(size_t)(16 * wv + 4 * gq + e) * kChunk + 16 * ct + n] = acc[e];
     }
     __syncthreads();  // Kt and A are dead: their space takes M W
 
@@ -487,7 +417,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
                 f32x4 ma;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ma[e] = m_s[(16 * rt + n) * SP + 16 * kb + 4 * gq + e];
-                acc = mma16_split_a<F32>(acc, ma, P::pack4(Wt[kb][ct]));
+                acc = P::mma16(acc, P::pack4(ma), P::pack4(Wt[kb][ct]));
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) mw_s[(16 * rt + 4 * gq + e) * MWP + col] = acc[e];
@@ -500,21 +430,12 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
         float mw[8];
         *reinterpret_cast<float4*>(mw) = *reinterpret_cast<const float4*>(&mw_s[r * MWP + cb]);
         *reinterpret_cast<float4*>(mw + 4) = *reinterpret_cast<const float4*>(&mw_s[r * MWP + cb + 4]);
-        st o8[8];
+        float o8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = P::to_st(qtil[8 * s + e] - mw[e]);
-        st* dst = QPg + (size_t)r * kD + cb;
-        if constexpr (F32) {
-            *reinterpret_cast<float4*>(dst) = make_float4(o8[0], o8[1], o8[2], o8[3]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
-        } else {
-            uint4 u;
-            u.x = (uint32_t)o8[0] | ((uint32_t)o8[1] << 16);
-            u.y = (uint32_t)o8[2] | ((uint32_t)o8[3] << 16);
-            u.z = (uint32_t)o8[4] | ((uint32_t)o8[5] << 16);
-            u.w = (uint32_t)o8[6] | ((uint32_t)o8[7] << 16);
-            *reinterpret_cast<uint4*>(dst) = u;
-        }
+        for (int e = 0; e < 8; ++e) o8[e] = qtil[8 * s + e] - mw[e];
+        float* dst = QPg + (size_t)r * kD + cb;
+        *reinterpret_cast<float4*>(dst) = make_float4(o8[0], o8[1], o8[2], o8[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
     }
 }
 
@@ -525,18 +446,13 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void kda_chunk_prep_kernel(
 // k order of every k32 product here: values 0..3 of a lane carry k = k0 + 4g
 // + e, values 4..7 carry k = k0 + 16 + 4g + e, i.e. the rows of accumulator
 // tiles 2s and 2s+1 — so S and U feed the B operand straight from registers.
-// bf16 mode stages each chunk's record in LDS; fp32 mode (small problems
-// only) reads it from global memory directly.
+// Each chunk's record is read from global memory directly; the V slice is
+// staged in LDS.
 // ---------------------------------------------------------------------------
-template <bool F32>
 __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
-    const uint8_t* __restrict__ ws, const typename Prec<F32>::io_t* __restrict__ v,
-    const float* h_in, float* h_out, typename Prec<F32>::io_t* __restrict__ out, float scale,
-    int T, int H, int chunk0, int nchunks) {
-    using P = Prec<F32>;
-    using st = typename P::st_t;
-    using F8 = typename P::F8;
-    using R = Rec<F32>;
+    const uint8_t* __restrict__ ws, const float* __restrict__ v, const float* h_in,
+    float* h_out, float* __restrict__ out, float scale, int T, int H, int chunk0, int nchunks) {
+    using R = RecF;
 
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
     // map ids so that all slices of one head sit on one XCD and the chunk
@@ -561,15 +477,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
     const int jl = 16 * wv + n;              // this lane's column within the slice
     const int j0 = c0 + 16 * wv;
 
-    constexpr int AP = kD + 8;       // LDS pitch of W / Q' rows
-    constexpr int KP = kChunk + 8;   // LDS pitch of 64-wide rows
     constexpr int VP = kSliceCols + 8;
-    constexpr int NL = F32 ? 1 : kChunk;  // LDS arrays only used in bf16 mode
-    __shared__ st w_s[NL * AP];
-    __shared__ st qp_s[NL * AP];
-    __shared__ st kt_s[(F32 ? 1 : kD) * KP];
-    __shared__ st th_s[NL * KP], tl_s[NL * KP], mh_s[NL * KP], ml_s[NL * KP];
-    __shared__ st v_s[kChunk * VP];
+    __shared__ float v_s[kChunk * VP];
     __shared__ float gam_s[kD];
 
     f32x4 S[8];
@@ -580,58 +489,17 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
         for (int e = 0; e < 4; ++e)
             S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
 
-    // bf16 mode: the next chunk's record and V slice are loaded into registers
-    // while the current chunk computes (22 x 16 B per thread + gamma).
-    u32x4 pf[22];
-    u32x4 pg = {0u, 0u, 0u, 0u};
-#define KDA_SCAN_ISSUE(cl_)                                                                     \
-    do {                                                                                        \
-        const uint8_t* rec_ = ws + ((size_t)bh * nchunks + (cl_)) * R::BYTES;                   \
-        const int64_t cbase = (int64_t)(chunk0 + (cl_)) * kChunk;                               \
-        const u32x4* Wv = reinterpret_cast<const u32x4*>(rec_ + R::W);                          \
-        const u32x4* Qv = reinterpret_cast<const u32x4*>(rec_ + R::QP);                         \
-        const u32x4* Kv = reinterpret_cast<const u32x4*>(rec_ + R::KT);                         \
-        const u32x4* THv = reinterpret_cast<const u32x4*>(rec_ + R::TH);                        \
-        const u32x4* TLv = reinterpret_cast<const u32x4*>(rec_ + R::TL);                        \
-        const u32x4* MHv = reinterpret_cast<const u32x4*>(rec_ + R::MH);                        \
-        const u32x4* MLv = reinterpret_cast<const u32x4*>(rec_ + R::ML);                        \
-        _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                         \
-            pf[m] = Wv[tid + 256 * m];                                                          \
-            pf[4 + m] = Qv[tid + 256 * m];                                                      \
-            pf[8 + m] = Kv[tid + 256 * m];                                                      \
-        }                                                                                       \
-        _Pragma("unroll") for (int m = 0; m < 2; ++m) {                                         \
-            pf[12 + m] = THv[tid + 256 * m];                                                    \
-            pf[14 + m] = TLv[tid + 256 * m];                                                    \
-            pf[16 + m] = MHv[tid + 256 * m];                                                    \
-            pf[18 + m] = MLv[tid + 256 * m];                                                    \
-            const int i_ = tid + 256 * m;                                                       \
-            const int64_t tk_ = cbase + (i_ >> 3);                                              \
-            const int64_t vo_ = (((int64_t)b * T + (tk_ < T ? tk_ : 0)) * H + h) * kD + c0 +    \
-                                (i_ & 7) * 8;                                                   \
-            const u32x4 vv_ = *reinterpret_cast<const u32x4*>(v + vo_);                         \
-            pf[20 + m] = tk_ < T ? vv_ : u32x4{0u, 0u, 0u, 0u};                                 \
-        }                                                                                       \
-        if (tid < 32) pg = reinterpret_cast<const u32x4*>(rec_ + R::G)[tid];                    \
-    } while (0)
-    if constexpr (!F32) KDA_SCAN_ISSUE(0);
-
     for (int cl = 0; cl < nchunks; ++cl) {
         const int c = chunk0 + cl;
         const uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * R::BYTES;
-        const st *wp, *qpp, *ktp, *thp, *tlp, *mhp, *mlp;
-        int ap, kp;
+        const float* wp = reinterpret_cast<const float*>(rec + R::W);
+        const float* qpp = reinterpret_cast<const float*>(rec + R::QP);
+        const float* ktp = reinterpret_cast<const float*>(rec + R::KT);
+        const float* thp = reinterpret_cast<const float*>(rec + R::TH);
+        const float* mhp = reinterpret_cast<const float*>(rec + R::MH);
+        constexpr int ap = kD, kp = kChunk;
         __syncthreads();
-        if constexpr (F32) {
-            wp = reinterpret_cast<const st*>(rec + R::W);
-            qpp = reinterpret_cast<const st*>(rec + R::QP);
-            ktp = reinterpret_cast<const st*>(rec + R::KT);
-            thp = reinterpret_cast<const st*>(rec + R::TH);
-            tlp = thp;
-            mhp = reinterpret_cast<const st*>(rec + R::MH);
-            mlp = mhp;
-            ap = kD;
-            kp = kChunk;
+        {
             // V slice of this chunk (zero past the end of the sequence)
             constexpr int VR = kSliceCols / 4;
             for (int i = tid; i < kChunk * VR; i += kScanThreads) {
@@ -644,55 +512,23 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
                 *reinterpret_cast<u32x4*>(&v_s[row * VP + cv * 4]) = val;
             }
             if (tid < kD) gam_s[tid] = reinterpret_cast<const float*>(rec + R::G)[tid];
-        } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int i = tid + 256 * m;
-                *reinterpret_cast<u32x4*>(&w_s[(i >> 4) * AP + (i & 15) * 8]) = pf[m];
-                *reinterpret_cast<u32x4*>(&qp_s[(i >> 4) * AP + (i & 15) * 8]) = pf[4 + m];
-                *reinterpret_cast<u32x4*>(&kt_s[(i >> 3) * KP + (i & 7) * 8]) = pf[8 + m];
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int i = tid + 256 * m, o = (i >> 3) * KP + (i & 7) * 8;
-                *reinterpret_cast<u32x4*>(&th_s[o]) = pf[12 + m];
-                *reinterpret_cast<u32x4*>(&tl_s[o]) = pf[14 + m];
-                *reinterpret_cast<u32x4*>(&mh_s[o]) = pf[16 + m];
-                *reinterpret_cast<u32x4*>(&ml_s[o]) = pf[18 + m];
-                *reinterpret_cast<u32x4*>(&v_s[(i >> 3) * VP + (i & 7) * 8]) = pf[20 + m];
-            }
-            if (tid < 32) *reinterpret_cast<u32x4*>(&gam_s[4 * tid]) = pg;
-            wp = w_s; qpp = qp_s; ktp = kt_s; thp = th_s; tlp = tl_s; mhp = mh_s; mlp = ml_s;
-            ap = AP;
-            kp = KP;
         }
         __syncthreads();
-        if constexpr (!F32) {
-            if (cl + 1 < nchunks) KDA_SCAN_ISSUE(cl + 1);
-        }
 
         // S-independent: Ut = T V and Oh = MT V for this wave's 16 columns
         f32x4 Ut[4], Oh[4];
         {
-            const F8 vb0 = frag_col<F32>(v_s, VP, jl, 0, gq);
-            const F8 vb1 = frag_col<F32>(v_s, VP, jl, 32, gq);
+            const F8 vb0 = frag_col(v_s, VP, jl, 0, gq);
+            const F8 vb1 = frag_col(v_s, VP, jl, 32, gq);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 u = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
                 const int row = 16 * rt + n;
-                u = P::mma32(u, frag_row<F32>(thp, kp, row, 0, gq), vb0);
-                o = P::mma32(o, frag_row<F32>(mhp, kp, row, 0, gq), vb0);
-                if constexpr (!F32) {
-                    u = P::mma32(u, frag_row<F32>(tlp, kp, row, 0, gq), vb0);
-                    o = P::mma32(o, frag_row<F32>(mlp, kp, row, 0, gq), vb0);
-                }
+                u = P::mma32(u, frag_row(thp, kp, row, 0, gq), vb0);
+                o = P::mma32(o, frag_row(mhp, kp, row, 0, gq), vb0);
                 if (rt >= 2) {
-                    u = P::mma32(u, frag_row<F32>(thp, kp, row, 32, gq), vb1);
-                    o = P::mma32(o, frag_row<F32>(mhp, kp, row, 32, gq), vb1);
-                    if constexpr (!F32) {
-                        u = P::mma32(u, frag_row<F32>(tlp, kp, row, 32, gq), vb1);
-                        o = P::mma32(o, frag_row<F32>(mlp, kp, row, 32, gq), vb1);
-                    }
+                    u = P::mma32(u, frag_row(thp, kp, row, 32, gq), vb1);
+                    o = P::mma32(o, frag_row(mhp, kp, row, 32, gq), vb1);
                 }
                 Ut[rt] = u;
                 Oh[rt] = o;
@@ -709,8 +545,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
             F8 fw[4], fq[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                fw[rt] = frag_row<F32>(wp, ap, 16 * rt + n, 32 * s, gq);
-                fq[rt] = frag_row<F32>(qpp, ap, 16 * rt + n, 32 * s, gq);
+                fw[rt] = frag_row(wp, ap, 16 * rt + n, 32 * s, gq);
+                fq[rt] = frag_row(qpp, ap, 16 * rt + n, 32 * s, gq);
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -731,33 +567,21 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * rt + 4 * gq + e;
                 if (full || (int64_t)c * kChunk + row < T)
-                    outc[(int64_t)row * H * kD] = P::to_io(scale * o[e]);
+                    outc[(int64_t)row * H * kD] = scale * o[e];
             }
         }
 
-        // S <- Diag(gamma) S + Kb^T U   (U as bf16 hi + lo in bf16 mode)
-        F8 bUh[2], bUl[2];
+        // S <- Diag(gamma) S + Kb^T U
+        F8 bU[2];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            if constexpr (F32) {
-                bUh[s2] = P::pack8(U[2 * s2], U[2 * s2 + 1]);
-            } else {
-                f32x4 h0v, l0v, h1v, l1v;
-                split_bf16(U[2 * s2], h0v, l0v);
-                split_bf16(U[2 * s2 + 1], h1v, l1v);
-                bUh[s2] = P::pack8(h0v, h1v);
-                bUl[s2] = P::pack8(l0v, l1v);
-            }
-        }
+        for (int s2 = 0; s2 < 2; ++s2) bU[s2] = P::pack8(U[2 * s2], U[2 * s2 + 1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[t][e] *= gam_s[16 * t + 4 * gq + e];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const F8 fa = frag_row<F32>(ktp, kp, 16 * t + n, 32 * s2, gq);
-                S[t] = P::mma32(S[t], fa, bUh[s2]);
-                if constexpr (!F32) S[t] = P::mma32(S[t], fa, bUl[s2]);
+                S[t] = P::mma32(S[t], frag_row(ktp, kp, 16 * t + n, 32 * s2, gq), bU[s2]);
             }
         }
     }
@@ -769,36 +593,25 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
     }
-#undef KDA_SCAN_ISSUE
 }
 
-template <bool F32>
-hipError_t launch_chunk_prep(const void* q, const void* k, const float* g, const float* beta,
-                             int B, int T, int H, int chunk0, int nchunks, void* ws,
-                             hipStream_t stream) {
-    using io = typename Prec<F32>::io_t;
+hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
+                                 const float* beta, int B, int T, int H, int chunk0, int nchunks,
+                                 void* ws, hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
-    hipLaunchKernelGGL(kda_chunk_prep_kernel<F32>, dim3(nblk), dim3(256), 0, stream,
-                       static_cast<const io*>(q), static_cast<const io*>(k), g, beta, T, H,
-                       chunk0, nchunks, static_cast<uint8_t*>(ws));
+    hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3(nblk), dim3(256), 0, stream, q, k, g, beta, T,
+                       H, chunk0, nchunks, static_cast<uint8_t*>(ws));
     return hipGetLastError();
 }
 
-template <bool F32>
-hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, float* h_out,
-                             void* out, float scale, int B, int T, int H, int chunk0,
-                             int nchunks, hipStream_t stream) {
-    using io = typename Prec<F32>::io_t;
+hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
+                                 float* out, float scale, int B, int T, int H, int chunk0,
+                                 int nchunks, hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * kScanSlices);
-    hipLaunchKernelGGL(kda_chunk_scan_kernel<F32>, dim3(nblk), dim3(kScanThreads), 0, stream,
-                       static_cast<const uint8_t*>(ws), static_cast<const io*>(v), h_in, h_out,
-                       static_cast<io*>(out), scale, T, H, chunk0, nchunks);
+    hipLaunchKernelGGL(kda_chunk_scan_kernel, dim3(nblk), dim3(kScanThreads), 0, stream,
+                       static_cast<const uint8_t*>(ws), v, h_in, h_out, out, scale, T, H, chunk0,
+                       nchunks);
     return hipGetLastError();
 }
-
-template hipError_t launch_chunk_prep<true>(const void*, const void*, const float*, const float*,
-                                            int, int, int, int, int, void*, hipStream_t);
-template hipError_t launch_chunk_scan<true>(const void*, const void*, const float*, float*,
-                                            void*, float, int, int, int, int, int, hipStream_t);
 
 }  // namespace kda

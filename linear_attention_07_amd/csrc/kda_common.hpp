@@ -29,7 +29,6 @@ constexpr float kNormEps = 1e-6f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -59,52 +58,18 @@ __device__ __forceinline__ float fast_exp(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand precision policies.  BF16: bf16 operands on 16x16x32 / 16x16x16
-// MFMAs, bf16 intermediates.  F32: fp32 operands on 16x16x4 MFMAs, fp32
-// intermediates.  Accumulation is fp32 in both.
+// Element policies by I/O type.  Prec<false>: bf16 q / k / v / out (the
+// decode step converts on load and store).  Prec<true>: fp32 I/O, and the fp32
+// operands and 16x16x4 fp32 products of the fp32 chunked prefill.
 // ---------------------------------------------------------------------------
 template <bool F32>
 struct Prec;
 
 template <>
-struct Prec<false> {
-    using io_t = uint16_t;   // q, k, v, out element
-    using st_t = uint16_t;   // stored intermediate element
-    struct F8 { bf16x8 v; };
-    struct F4 { s16x4 v; };
-
-    __device__ static __forceinline__ st_t to_st(float x) { return f2bf(x); }
-    __device__ static __forceinline__ float from_st(st_t x) { return bf2f(x); }
+struct Prec<false> {  // bf16 I/O (the decode step)
+    using io_t = uint16_t;
     __device__ static __forceinline__ float from_io(io_t x) { return bf2f(x); }
     __device__ static __forceinline__ io_t to_io(float x) { return f2bf(x); }
-
-    __device__ static __forceinline__ F8 pack8(const float* x) {
-        F8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f.v[e] = (__bf16)x[e];
-        return f;
-    }
-    __device__ static __forceinline__ F8 pack8(f32x4 lo, f32x4 hi) {
-        F8 f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            f.v[e] = (__bf16)lo[e];
-            f.v[4 + e] = (__bf16)hi[e];
-        }
-        return f;
-    }
-    __device__ static __forceinline__ F4 pack4(f32x4 x) {
-        F4 f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f.v[e] = (short)f2bf(x[e]);
-        return f;
-    }
-    __device__ static __forceinline__ f32x4 mma32(f32x4 acc, const F8& a, const F8& b) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
-    }
-    __device__ static __forceinline__ f32x4 mma16(f32x4 acc, const F4& a, const F4& b) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, acc, 0, 0, 0);
-    }
 };
 
 template <>
@@ -153,19 +118,6 @@ struct Prec<true> {
         return acc;
     }
 };
-
-// Split an fp32 value into bf16 hi + lo parts (hi + lo carries ~16 mantissa bits).
-__device__ __forceinline__ void split_bf16(float x, float& hi, float& lo) {
-    hi = bf2f(f2bf(x));
-    lo = x - hi;
-}
-__device__ __forceinline__ void split_bf16(f32x4 x, f32x4& hi, f32x4& lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        hi[e] = bf2f(f2bf(x[e]));
-        lo[e] = x[e] - hi[e];
-    }
-}
 
 // Load 8 consecutive io elements as fp32 (16-byte aligned bf16 / 2 x 16 B fp32).
 __device__ __forceinline__ void load8(const uint16_t* p, float* x) {

@@ -8,32 +8,24 @@
 
 namespace kda {
 
-// Bytes of one per-(batch, head, chunk) record written by the chunk-prep
-// kernel and read by the chunk-scan kernel.
-size_t chunk_record_bytes(bool f32);
-
-// Number of value-column slices a head's state is split into by the scan
-// kernel (one workgroup per slice).
-int scan_slices();
-
 template <bool F32>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float scale, float* S, void* out,
                          int B, int H, hipStream_t stream);
 
-// prep: per-chunk records (W, Q', Kb^T, T, MT, gamma) for chunks
-// [chunk0, chunk0 + nchunks) of every (b, h), from q, k, g, beta.
-template <bool F32>
-hipError_t launch_chunk_prep(const void* q, const void* k, const float* g, const float* beta,
-                             int B, int T, int H, int chunk0, int nchunks, void* ws,
-                             hipStream_t stream);
-
-// scan: walks those chunks in order, reading v, the records and h_in (NULL =
-// zero state); writes out and, if h_out is not NULL, the final state.
-template <bool F32>
-hipError_t launch_chunk_scan(const void* ws, const void* v, const float* h_in, float* h_out,
-                             void* out, float scale, int B, int T, int H, int chunk0,
-                             int nchunks, hipStream_t stream);
+// two-kernel chunked prefill for fp32 q/k/v/o, fp32 arithmetic throughout.
+// prep writes one record (W, Q', Kb^T, T, MT, gamma) per (batch, head, chunk)
+// of chunks [chunk0, chunk0 + nchunks) into ws, from q, k, g, beta; scan walks
+// them in order, reading v, the records and h_in (NULL = zero state), and
+// writes out and, if h_out is not NULL, the final state.
+size_t chunk_f32_record_bytes();
+int chunk_f32_slices();
+hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
+                                 const float* beta, int B, int T, int H, int chunk0, int nchunks,
+                                 void* ws, hipStream_t stream);
+hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
+                                 float* out, float scale, int B, int T, int H, int chunk0,
+                                 int nchunks, hipStream_t stream);
 
 // two-kernel chunked prefill for bf16 q/k/v/o: prep writes one record per
 // (batch, head, chunk) of chunks [chunk0, chunk0 + nchunks) into ws; scan walks
