@@ -119,6 +119,22 @@ def test_chunk_lengths(io, T):
     assert eo <= tol and es <= tol
 
 
+@pytest.mark.parametrize("workspace_mb", [None, 2])
+def test_chunk_batched_heads_segments(workspace_mb, monkeypatch):
+    """B=2, H=8 (B*H a multiple of 8: the XCD-aware workgroup orders of both
+    kernels, with two batch entries), ragged T=700, nonzero initial state; in
+    one workspace segment and in one-chunk segments (2 MB workspace)."""
+    if workspace_mb is not None:
+        monkeypatch.setenv("KDA_WORKSPACE_MB", str(workspace_mb))
+    B, T, H = 2, 700, 8
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=77, h0_std=0.1, device=DEV)
+    o_ref, h_ref = oracle_prefill(inp)
+    out, hT = _run_chunk(inp)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"B={B} H={H} T={T} workspace={workspace_mb}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 def test_layer_4k_all_heads():
     """One 96-head layer, T=4096, bf16, zero state: every head checked."""
     w = synth.WORKLOADS["layer_4k"]
