@@ -15,7 +15,10 @@ Roofline (per call of the timed op, algorithmic bytes only):
   decode:  132,612 B per (sequence, head): the 64 KB state read and written,
            q, k, v (768 B), g (512 B), beta (4 B), o (256 B).
 Both are HBM-bound (about 117 and 0.86 flop/B, under the 312 flop/B ridge
-of 2.5 PFLOP/s bf16 over 8 TB/s), so the peak is 8 TB/s.
+of 2.5 PFLOP/s bf16 over 8 TB/s), so the peak is 8 TB/s.  The prefill's
+algorithmic matrix work, 180,224 flop per token-head at a fixed 64-token chunk
+(five 64x64x128 products and three 128x128x64 state products), is reported
+beside it as a fraction of the 2.5 PFLOP/s dense bf16 peak.
 """
 from __future__ import annotations
 
@@ -26,6 +29,8 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_FLOP_PER_TOKEN_HEAD = 10 * 64 * 128 + 6 * 128 * 128
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
 STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_SEQ_HEAD = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256
@@ -75,18 +80,20 @@ def measured_traffic(key):
 
 
 def time_op(torch, fn, steps, warmup):
+    """Mean ms per call over `steps` calls bracketed by two events on the
+    launch stream, and the median and minimum of the per-call event times."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms per call
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2], per[0]
 
 
 def cpu_baseline(inp, n_tokens):
@@ -113,7 +120,13 @@ def cpu_baseline(inp, n_tokens):
         dt += time.perf_counter() - t0
         del args, s0
     mtok = n_tokens / dt / 1e6
-    return {"value": mtok, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": mtok, "unit": "Mtok/s", "cores": threads, "kind": "oracle", "cpu_model": model,
             "sample": f"all {H} heads x first {n_tokens} tokens of the 64K prefill input "
                       f"(the whole workload at the default), fp64 token-by-token recurrence, "
                       f"{dt:.2f} s of oracle time"}
@@ -145,13 +158,14 @@ def main():
 
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    ms = time_op(torch, prefill, args.steps, args.warmup)
+    ms, ms_med, ms_min = time_op(torch, prefill, args.steps, args.warmup)
     t_wall = time.perf_counter() - t_wall0
     tokens = w.B * w.T
     mtok = tokens / (ms / 1e3) / 1e6
     token_heads = w.B * w.T * w.H
     pre_bytes = token_heads * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * STATE_BYTES
     pre_gbps = pre_bytes / (ms / 1e3) / 1e9
+    pre_tflops = token_heads * PREFILL_FLOP_PER_TOKEN_HEAD / (ms / 1e3) / 1e12
     print(f"# prefill: {ms:.3f} ms/step, {mtok:.2f} Mtok/s, {pre_gbps:.0f} GB/s algorithmic "
           f"(wall {t_wall:.2f} s)", file=sys.stderr, flush=True)
 
@@ -170,7 +184,7 @@ def main():
                               out=dout)
 
     dsteps = args.decode_steps or args.steps
-    dms = time_op(torch, decode, dsteps, args.warmup)
+    dms, dms_med, dms_min = time_op(torch, decode, dsteps, args.warmup)
     nbh = wd.B * wd.H
     state_gbps = nbh * 2 * STATE_BYTES / (dms / 1e3) / 1e9
     dec_gbps = nbh * DECODE_BYTES_PER_SEQ_HEAD / (dms / 1e3) / 1e9
@@ -198,6 +212,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_med, 4),
+        "ms_per_step_min": round(ms_min, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -219,9 +235,18 @@ def main():
             "traffic": measured_traffic("prefill_64k"),
             "algorithmic_bytes_per_call": pre_bytes,
         },
+        "mfma": {
+            "algorithmic_flop_per_call": token_heads * PREFILL_FLOP_PER_TOKEN_HEAD,
+            "achieved_TFLOPs": round(pre_tflops, 1),
+            "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+            "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "note": "algorithmic flops at a fixed 64-token chunk; the binding roofline is HBM",
+        },
         "decode": {
             "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v",
             "ms_per_step": round(dms, 4),
+            "ms_per_step_median": round(dms_med, 4),
+            "ms_per_step_min": round(dms_min, 4),
             "state_GBps": round(state_gbps, 1),
             "roofline": {
                 "bound": "hbm",
