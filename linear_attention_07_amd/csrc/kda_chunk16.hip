@@ -116,10 +116,9 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     __shared__ __align__(16) float tau_s[4][kD];      // block totals of g (log2 units)
     __shared__ __align__(16) float tab_s[kTabs][kD];  // factor tables
     __shared__ float beta_s[kChunk];
-    // Two areas, each used by two phases that a barrier separates, so that
-    // three workgroups fit on a CU (43 KB of LDS each):
     // The column operands of KK / QK and X = (I + A)^-1 share one area (a
-    // barrier separates their uses), so that three workgroups fit on a CU.
+    // barrier separates their uses), so that three workgroups fit on a CU
+    // (43 KB of LDS each).
     __shared__ __align__(16) float u1_s[kChunk * SP];
     __shared__ float a_s[kChunk * SP];                 // diag(beta) strict-lower KK
     static_assert(sizeof(bf16x8) * 4 * 4 * 64 <= sizeof(float) * kChunk * SP,
