@@ -5,7 +5,7 @@ A step is one kda_chunk_fwd over the 64K-token, 96-head prefill batch
 (B=1, H=96, T=65536, d=128; bf16 q/k/v, fp32 g/beta, fp32 state with a
 random initial state) with every input already resident in HBM.  The value is
 prefill Mtok/s (B*T tokens per step, all 96 heads).  The same run also times
-the batched decode step (B=256, H=96, fp32 state streamed in place) and
+the same prefill with g in bf16 (kda_chunk_fwd_g16), the batched decode step (B=256, H=96, fp32 state streamed in place) and
 reports its state bandwidth, and times the fp64 CPU oracle on a bounded
 sample of the prefill workload as a baseline.
 
@@ -32,6 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_FLOP_PER_TOKEN_HEAD = 10 * 64 * 128 + 6 * 128 * 128
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
+PREFILL_G16_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
 STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_SEQ_HEAD = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256
 
@@ -169,6 +170,20 @@ def main():
     print(f"# prefill: {ms:.3f} ms/step, {mtok:.2f} Mtok/s, {pre_gbps:.0f} GB/s algorithmic "
           f"(wall {t_wall:.2f} s)", file=sys.stderr, flush=True)
 
+    # ---- prefill with g in bf16 ---------------------------------------------
+    g16 = inp["g"].to(torch.bfloat16)
+
+    def prefill_g16():
+        libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], g16, inp["beta"], inp["scale"],
+                         inp["h0"], out=out, hT=hT)
+
+    gms, gms_med, gms_min = time_op(torch, prefill_g16, args.steps, args.warmup)
+    g16_bytes = token_heads * PREFILL_G16_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * STATE_BYTES
+    g16_gbps = g16_bytes / (gms / 1e3) / 1e9
+    print(f"# prefill, bf16 g: {gms:.3f} ms/step, {tokens / (gms / 1e3) / 1e6:.2f} Mtok/s, "
+          f"{g16_gbps:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+    del g16
+
     # ---- decode -------------------------------------------------------------
     wd = synth.WORKLOADS["decode_b256"]
     S = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
@@ -241,6 +256,21 @@ def main():
             "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "note": "algorithmic flops at a fixed 64-token chunk; the binding roofline is HBM",
+        },
+        "prefill_g16": {
+            "workload": "prefill_64k with g in bf16 (kda_chunk_fwd_g16): 1,284 B per token-head",
+            "ms_per_step": round(gms, 4),
+            "ms_per_step_median": round(gms_med, 4),
+            "ms_per_step_min": round(gms_min, 4),
+            "Mtok_s": round(tokens / (gms / 1e3) / 1e6, 3),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(g16_gbps, 1),
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": round(g16_gbps / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes_per_call": g16_bytes,
+            },
         },
         "decode": {
             "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v",

@@ -89,6 +89,23 @@ KDA_API kda_status_t kda_chunk_fwd(const uint16_t *q, const uint16_t *k, const u
                            int B, int T, int H, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_g16 — as kda_chunk_fwd, with the log-decay in bf16:
+ *
+ *   g       : [B, T, H, 128] bf16 log-decay per key channel, in [-5, 0].
+ *
+ * Every other argument, the layout, the validation and the result are those
+ * of kda_chunk_fwd; the bf16 values of g are used exactly (widened to fp32).
+ * The decay is an input of the operation (its gate, a full-rank projection
+ * bounded below by -5 on the Kimi K3 架构全景 page, section 02, is computed
+ * before it), and the fp32 g stream is a third of the prefill's compulsory
+ * bytes: in bf16 a token-head moves 1,284 instead of 1,540 bytes.
+ */
+KDA_API kda_status_t kda_chunk_fwd_g16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const uint16_t *g, const float *beta, float scale,
+                               const float *h0, uint16_t *out, float *hT,
+                               int B, int T, int H, hipStream_t stream);
+
+/*
  * kda_chunk_fwd_f32 — as kda_chunk_fwd, with fp32 q, k, v and out and fp32
  * matrix-core products throughout (the fp32-input accuracy mode).
  */

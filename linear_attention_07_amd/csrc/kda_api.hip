@@ -64,11 +64,14 @@ hipError_t pool_for_device(hipMemPool_t* pool) {
     return hipSuccess;
 }
 
-template <bool F32>
-kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+// F32: fp32 q / k / v / out (else bf16); G16: bf16 g (else fp32; bf16 I/O only)
+template <bool F32, bool G16 = false>
+kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                        const float* beta, float scale, const float* h0, void* out, float* hT,
                        int B, int T, int H, hipStream_t stream) {
+    static_assert(!(F32 && G16), "bf16 g is offered with bf16 q / k / v only");
     constexpr size_t es = F32 ? 4 : 2;
+    constexpr size_t gs = G16 ? 2 : 4;
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     if (B == 0 || H == 0) return KDA_OK;
@@ -93,7 +96,7 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float*
     const void* ins[] = {q, k, v};
     for (const void* p : ins)
         if (overlap(out, io_bytes, p, io_bytes)) return KDA_ERR_INVALID_ARG;
-    if (overlap(out, io_bytes, g, n_tok * KDA_HEAD_DIM * 4) ||
+    if (overlap(out, io_bytes, g, n_tok * KDA_HEAD_DIM * gs) ||
         overlap(out, io_bytes, beta, n_tok * 4) || overlap(out, io_bytes, h0, state_bytes) ||
         overlap(out, io_bytes, hT, state_bytes))
         return KDA_ERR_INVALID_ARG;
@@ -132,13 +135,14 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const float*
         float* h_out = last ? (hT ? hT : nullptr) : carry;
         hipError_t e1, e2;
         if constexpr (v16) {
-            e1 = kda::launch_prep16(q, k, g, beta, B, T, H, c0, n, ws, stream);
+            e1 = kda::launch_prep16(q, k, g, G16, beta, B, T, H, c0, n, ws, stream);
             e2 = e1 == hipSuccess
                      ? kda::launch_scan16(ws, v, h_in, h_out, out, scale, B, T, H, c0, n, stream)
                      : e1;
         } else {
             e1 = kda::launch_chunk_prep_f32(static_cast<const float*>(q),
-                                            static_cast<const float*>(k), g, beta, B, T, H, c0, n,
+                                            static_cast<const float*>(k),
+                                            static_cast<const float*>(g), beta, B, T, H, c0, n,
                                             ws, stream);
             e2 = e1 == hipSuccess
                      ? kda::launch_chunk_scan_f32(ws, static_cast<const float*>(v), h_in, h_out,
@@ -211,6 +215,12 @@ kda_status_t kda_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const float* g, const float* beta, float scale, const float* h0,
                            uint16_t* out, float* hT, int B, int T, int H, hipStream_t stream) {
     return chunk_fwd<false>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream);
+}
+
+kda_status_t kda_chunk_fwd_g16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint16_t* g, const float* beta, float scale, const float* h0,
+                               uint16_t* out, float* hT, int B, int T, int H, hipStream_t stream) {
+    return chunk_fwd<false, true>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream);
 }
 
 kda_status_t kda_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* g,

@@ -107,10 +107,12 @@ int chunk16_slices() { return kSlices; }
 // ---------------------------------------------------------------------------
 // prep: wave p owns chunk rows 16p..16p+15; lane (n, gq) owns row r = 16p + n
 // and the 32 channels 32s + 8gq + e (s = 0..3, e = 0..7), i.e. its A-operand
-// fragments of the four k32 steps over the 128 channels.
+// fragments of the four k32 steps over the 128 channels.  G16: g arrives as
+// bf16 (widened to fp32 on load) instead of fp32.
 // ---------------------------------------------------------------------------
+template <bool G16>
 __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ g,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const void* __restrict__ g,
     const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
     uint8_t* __restrict__ ws) {
     __shared__ __align__(16) float tau_s[4][kD];      // block totals of g (log2 units)
@@ -164,8 +166,22 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
         const int cb = 32 * s + 8 * gq;
         pq[s] = valid ? *reinterpret_cast<const u32x4*>(q + rowoff + cb) : z4;
         pk[s] = valid ? *reinterpret_cast<const u32x4*>(k + rowoff + cb) : z4;
-        pg[2 * s] = valid ? *reinterpret_cast<const f32x4*>(g + rowoff + cb) : zf4;
-        pg[2 * s + 1] = valid ? *reinterpret_cast<const f32x4*>(g + rowoff + cb + 4) : zf4;
+        if constexpr (G16) {
+            const u32x4 x = valid
+                ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g) + rowoff + cb)
+                : z4;
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                pg[2 * s + w] = f32x4{__builtin_bit_cast(float, x[2 * w] << 16),
+                                      __builtin_bit_cast(float, x[2 * w] & 0xffff0000u),
+                                      __builtin_bit_cast(float, x[2 * w + 1] << 16),
+                                      __builtin_bit_cast(float, x[2 * w + 1] & 0xffff0000u)};
+            }
+        } else {
+            const float* gf = static_cast<const float*>(g);
+            pg[2 * s] = valid ? *reinterpret_cast<const f32x4*>(gf + rowoff + cb) : zf4;
+            pg[2 * s + 1] = valid ? *reinterpret_cast<const f32x4*>(gf + rowoff + cb + 4) : zf4;
+        }
     }
     const float bet = valid ? beta[((int64_t)b * T + tok) * H + h] : 0.f;
 
@@ -732,12 +748,18 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     }
 }
 
-hipError_t launch_prep16(const void* q, const void* k, const float* g, const float* beta, int B,
-                         int T, int H, int chunk0, int nchunks, void* ws, hipStream_t stream) {
+hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
+                         const float* beta, int B, int T, int H, int chunk0, int nchunks, void* ws,
+                         hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
-    hipLaunchKernelGGL(kda_prep16_kernel, dim3(nblk), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), g, beta,
-                       T, H, chunk0, nchunks, static_cast<uint8_t*>(ws));
+    if (g_bf16)
+        hipLaunchKernelGGL(kda_prep16_kernel<true>, dim3(nblk), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), g,
+                           beta, T, H, chunk0, nchunks, static_cast<uint8_t*>(ws));
+    else
+        hipLaunchKernelGGL(kda_prep16_kernel<false>, dim3(nblk), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), g,
+                           beta, T, H, chunk0, nchunks, static_cast<uint8_t*>(ws));
     return hipGetLastError();
 }
 

@@ -28,12 +28,14 @@ hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_
                                  int nchunks, hipStream_t stream);
 
 // two-kernel chunked prefill for bf16 q/k/v/o: prep writes one record per
-// (batch, head, chunk) of chunks [chunk0, chunk0 + nchunks) into ws; scan walks
-// them in order (h_in NULL = zero state, h_out NULL = final state not stored).
+// (batch, head, chunk) of chunks [chunk0, chunk0 + nchunks) into ws, from g in
+// fp32 or (g_bf16) bf16; scan walks them in order (h_in NULL = zero state,
+// h_out NULL = final state not stored).
 size_t chunk16_record_bytes();
 int chunk16_slices();
-hipError_t launch_prep16(const void* q, const void* k, const float* g, const float* beta, int B,
-                         int T, int H, int chunk0, int nchunks, void* ws, hipStream_t stream);
+hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
+                         const float* beta, int B, int T, int H, int chunk0, int nchunks, void* ws,
+                         hipStream_t stream);
 hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
                          void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
                          hipStream_t stream);

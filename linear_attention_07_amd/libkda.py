@@ -26,6 +26,7 @@ KDA_ERR_NO_MEMORY = 4
 EXPORTS = (
     "kda_chunk_fwd",
     "kda_chunk_fwd_f32",
+    "kda_chunk_fwd_g16",
     "kda_recurrent_step",
     "kda_recurrent_step_f32",
     "kda_status_string",
@@ -54,6 +55,7 @@ def load() -> ctypes.CDLL:
     chunk_args = [vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, vp]
     step_args = [vp, vp, vp, vp, vp, f, vp, vp, i, i, vp]
     for name, args in (("kda_chunk_fwd", chunk_args), ("kda_chunk_fwd_f32", chunk_args),
+                       ("kda_chunk_fwd_g16", chunk_args),
                        ("kda_recurrent_step", step_args), ("kda_recurrent_step_f32", step_args)):
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -89,9 +91,10 @@ def _stream(device):
 
 def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=True):
     """Chunkwise prefill.  q, k, v: [B, T, H, 128] bf16 (or all fp32 for the
-    fp32 mode); g: [B, T, H, 128] fp32; beta: [B, T, H] fp32; h0: optional
-    [B, H, 128, 128] fp32.  Returns (out, hT); hT is None when final_state is
-    False and no hT buffer is given."""
+    fp32 mode); g: [B, T, H, 128] fp32, or bf16 with bf16 q / k / v
+    (kda_chunk_fwd_g16); beta: [B, T, H] fp32; h0: optional [B, H, 128, 128]
+    fp32.  Returns (out, hT); hT is None when final_state is False and no hT
+    buffer is given."""
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
         raise ValueError(f"q: expected [B, T, H, {HEAD_DIM}], got {tuple(q.shape)}")
     B, T, H, _ = q.shape
@@ -104,7 +107,8 @@ def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=T
     for name, t in (("k", k), ("v", v)):
         _check(t, name, q.shape, io, dev)
     _check(q, "q", q.shape, io, dev)
-    _check(g, "g", q.shape, torch.float32, dev)
+    g16 = io == torch.bfloat16 and g.dtype == torch.bfloat16
+    _check(g, "g", q.shape, torch.bfloat16 if g16 else torch.float32, dev)
     _check(beta, "beta", (B, T, H), torch.float32, dev)
     sshape = (B, H, HEAD_DIM, HEAD_DIM)
     if h0 is not None:
@@ -117,7 +121,9 @@ def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=T
         hT = torch.empty(sshape, dtype=torch.float32, device=dev)
     elif hT is not None:
         _check(hT, "hT", sshape, torch.float32, dev)
-    fn = load().kda_chunk_fwd if io == torch.bfloat16 else load().kda_chunk_fwd_f32
+    lib = load()
+    fn = (lib.kda_chunk_fwd_g16 if g16 else lib.kda_chunk_fwd) if io == torch.bfloat16 \
+        else lib.kda_chunk_fwd_f32
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(h0),
             _ptr(out), _ptr(hT), B, T, H, _stream(dev))
     if st != KDA_OK:

@@ -60,7 +60,7 @@ def step(lib, fn="kda_recurrent_step", q=P[0], k=P[1], v=P[2], g=P[3], beta=P[4]
     return getattr(lib, fn)(q, k, v, g, beta, scale, S, out, B, H, None)
 
 
-@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_fwd_f32"])
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_g16"])
 def test_chunk_invalid_arguments(lib, fn):
     INV = libkda.KDA_ERR_INVALID_ARG
     assert chunk(lib, fn, B=-1) == INV
@@ -80,7 +80,7 @@ def test_chunk_invalid_arguments(lib, fn):
     assert chunk(lib, fn, h0=P[7], hT=ctypes.c_void_p(A * 8 + 4096)) == INV
 
 
-@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_fwd_f32"])
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_g16"])
 def test_chunk_empty_is_a_no_op(lib, fn):
     assert chunk(lib, fn, B=0) == libkda.KDA_OK
     assert chunk(lib, fn, H=0) == libkda.KDA_OK

@@ -135,6 +135,46 @@ def test_chunk_batched_heads_segments(workspace_mb, monkeypatch):
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+@pytest.mark.parametrize("B,T,H", [(2, 1, 3), (2, 65, 3), (2, 1000, 3), (2, 700, 8)])
+def test_chunk_g16_against_oracle(B, T, H):
+    """g in bf16 (kda_chunk_fwd_g16), nonzero initial state: the oracle reads
+    the same bf16 values of g, widened to fp64."""
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=300 + T + H, h0_std=0.1, device=DEV)
+    inp["g"] = inp["g"].to(torch.bfloat16)
+    o_ref, h_ref = oracle_prefill(inp)
+    out, hT = _run_chunk(inp)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"g16 B={B} T={T} H={H}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_chunk_g16_equals_fp32_g():
+    """kda_chunk_fwd_g16 on bf16 g and kda_chunk_fwd on the same values in
+    fp32 run the same arithmetic after the (exact) widening: bit-identical
+    outputs and final states."""
+    B, T, H = 1, 1000, 96
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=311, h0_std=0.1, device=DEV)
+    g16 = inp["g"].to(torch.bfloat16)
+    inp["g"] = g16
+    out16, hT16 = _run_chunk(inp)
+    inp["g"] = g16.float()
+    out32, hT32 = _run_chunk(inp)
+    assert torch.equal(out16, out32)
+    assert torch.equal(hT16, hT32)
+
+
+def test_layer_4k_g16_all_heads():
+    """The 96-head T=4096 layer with g in bf16: every head checked."""
+    w = synth.WORKLOADS["layer_4k"]
+    inp = synth.workload_inputs(w, DEV)
+    inp["g"] = inp["g"].to(torch.bfloat16)
+    out, hT = _run_chunk(inp)
+    o_ref, h_ref = oracle_prefill(inp)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"  g16 out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 def test_layer_4k_all_heads():
     """One 96-head layer, T=4096, bf16, zero state: every head checked."""
     w = synth.WORKLOADS["layer_4k"]
