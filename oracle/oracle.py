@@ -129,3 +129,52 @@ def step(q, k, v, g, beta, scale, S, eps=1e-6, threads=None):
         g.reshape(B * H, 1, dk), beta.reshape(B * H, 1), scale,
         S.reshape(B * H, dk, dv), eps, threads)
     return o.reshape(B, H, dv), hT.reshape(B, H, dk, dv)
+
+
+# ---------------------------------------------------------------------------
+# Short convolution in front of the attention (the KDA paragraph of the
+# 深入 Kimi-K3 thread: q, k and v each pass through a short convolution with
+# SiLU before the kernel; the Kimi K3 architecture page's config table: a
+# kernel of 4 taps).  Read here as the plainest form those passages support:
+# depthwise (one 4-tap filter per head and channel), causal, no bias, SiLU on
+# the filtered value, and a state of the 3 raw tokens that precede the first
+# one (zeros for a fresh sequence).
+# ---------------------------------------------------------------------------
+CONV_TAPS = 4
+
+
+def silu(x):
+    """x * logistic(x), in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def short_conv_silu(x, w, state=None):
+    """x ``[B, T, H, D]`` raw values; w ``[H, D, 4]`` taps, tap j weighting
+    the token j - 3 steps from the current one (tap 3 = the current token);
+    state ``[B, 3, H, D]`` the raw tokens before x (oldest first) or None for
+    zeros.  Returns (y ``[B, T, H, D]`` = silu(sum_j w_j x_{t-3+j}), the new
+    state: the last 3 raw tokens of state followed by x)."""
+    x, w = _f64(x), _f64(w)
+    B, T, H, D = x.shape
+    assert w.shape == (H, D, CONV_TAPS)
+    prev = np.zeros((B, CONV_TAPS - 1, H, D)) if state is None else _f64(state)
+    assert prev.shape == (B, CONV_TAPS - 1, H, D)
+    full = np.concatenate([prev, x], axis=1)  # token t of x sits at index t + 3
+    pre = np.zeros((B, T, H, D))
+    for j in range(CONV_TAPS):
+        pre += w[None, None, :, :, j] * full[:, j:j + T]
+    return silu(pre), np.ascontiguousarray(full[:, T:])
+
+
+def forward_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_state=None, eps=1e-6,
+                 threads=None):
+    """The attention on the short-convolved q, k, v.  conv_state is None or a
+    triple of ``[B, 3, H, D]`` states for q, k, v.  Returns (o, hT, the three
+    new conv states)."""
+    cs = (None, None, None) if conv_state is None else conv_state
+    qc, sq = short_conv_silu(q, wq, cs[0])
+    kc, sk = short_conv_silu(k, wk, cs[1])
+    vc, sv = short_conv_silu(v, wv, cs[2])
+    o, hT = forward(qc, kc, vc, g, beta, scale, h0, eps, threads)
+    return o, hT, (sq, sk, sv)

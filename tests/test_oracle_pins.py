@@ -8,6 +8,7 @@ normalisation invariance, linearity) and the state-size arithmetic quoted by
 the 深入 Kimi-K3 thread.  Everything here runs on the CPU.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -258,3 +259,59 @@ def test_decode_step_matches_forward():
     o1, S1 = oracle.step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], 0.9, S, threads=1)
     np.testing.assert_array_equal(o1, o[:, 0])
     np.testing.assert_array_equal(S1, hT)
+
+
+# ---------------------------------------------------------------------------
+# short convolution + SiLU in front of the attention
+# ---------------------------------------------------------------------------
+def test_silu_textbook_values():
+    """With the current-token tap 1 and the others 0 the filter is the
+    identity, so the output is SiLU of the input: x * logistic(x), checked
+    against logistic values written out (1/(1+e) and friends)."""
+    xs = np.array([0.0, 1.0, -1.0, 2.0, -3.0])
+    # x / (1 + e^-x): 0, 0.7310585786300049, -0.2689414213699951,
+    # 1.7615941559557649, -0.14227761953270035
+    want = np.array([0.0, 0.7310585786300049, -0.2689414213699951, 1.7615941559557649,
+                     -0.14227761953270035])
+    x = xs.reshape(1, -1, 1, 1)
+    w = np.zeros((1, 1, 4))
+    w[0, 0, 3] = 1.0
+    y, _ = oracle.short_conv_silu(x, w)
+    np.testing.assert_allclose(y.reshape(-1), want, rtol=1e-15, atol=1e-16)
+
+
+def test_short_conv_impulse_response():
+    """An impulse a at token t0 reaches token t0 + m (m = 0..3) through tap
+    3 - m: the output there is SiLU(w[3 - m] a) and zero everywhere else.
+    This fixes the tap order (tap 3 = current token, tap 0 = three back)."""
+    T, t0, a = 10, 4, 1.5
+    w = np.array([0.3, -0.7, 1.1, 0.5]).reshape(1, 1, 4)
+    x = np.zeros((1, T, 1, 1))
+    x[0, t0, 0, 0] = a
+    y, _ = oracle.short_conv_silu(x, w)
+    want = np.zeros(T)
+    for m in range(4):
+        z = w[0, 0, 3 - m] * a
+        want[t0 + m] = z / (1.0 + math.exp(-z))
+    np.testing.assert_allclose(y.reshape(-1), want, rtol=1e-15, atol=1e-17)
+
+
+def test_short_conv_state_and_split():
+    """Causal with a 3-token state: filtering x[:t1] and then x[t1:] from the
+    state the first call returns equals filtering x whole, for every split;
+    and the first output of a zero input reads only the state."""
+    rng = np.random.default_rng(7)
+    B, T, H, D = 2, 11, 3, 5
+    x = rng.standard_normal((B, T, H, D))
+    w = rng.standard_normal((H, D, 4))
+    s0 = rng.standard_normal((B, 3, H, D))
+    whole, s_end = oracle.short_conv_silu(x, w, s0)
+    for t1 in range(0, T + 1):
+        y1, s1 = oracle.short_conv_silu(x[:, :t1], w, s0)
+        y2, s2 = oracle.short_conv_silu(x[:, t1:], w, s1)
+        np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), whole, rtol=0, atol=0)
+        np.testing.assert_array_equal(s2, s_end)
+    np.testing.assert_array_equal(s_end, x[:, T - 3:])
+    y, _ = oracle.short_conv_silu(np.zeros((B, 1, H, D)), w, s0)
+    pre = w[None, :, :, 0] * s0[:, 0] + w[None, :, :, 1] * s0[:, 1] + w[None, :, :, 2] * s0[:, 2]
+    np.testing.assert_allclose(y[:, 0], pre / (1.0 + np.exp(-pre)), rtol=1e-14, atol=1e-15)
