@@ -106,6 +106,41 @@ KDA_API kda_status_t kda_chunk_fwd_g16(const uint16_t *q, const uint16_t *k, con
                                int B, int T, int H, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_conv — kda_chunk_fwd with the short convolution and SiLU that
+ * the KDA layer puts in front of the attention (the KDA paragraph of the
+ * 深入 Kimi-K3 thread; a 4-tap kernel in the config table of the Kimi K3
+ * architecture page), fused into the kernels' loads.  Read as depthwise and
+ * causal with no bias: for each of q, k and v,
+ *
+ *   x'[b,t,h,c] = silu( sum_{j=0..3} w[h,c,j] * x[b,t-3+j,h,c] ),
+ *   silu(a) = a / (1 + exp(-a)),
+ *
+ * where the tokens before t = 0 come from conv_in (zeros when it is NULL).
+ * x' is rounded to bf16 and is then the q, k or v of kda_chunk_fwd.
+ *
+ *   q, k, v  : [B, T, H, 128] bf16 RAW values (before the convolution).
+ *   wq/wk/wv : [H, 128, 4] fp32 taps; tap 3 weights the current token, tap j
+ *              the token 3 - j steps before it.  Required; 16-byte aligned.
+ *   conv_in  : NULL (a fresh sequence) or [3][B][3][H][128] bf16: for q, k, v
+ *              in that order, the 3 raw tokens before the first one, oldest
+ *              first.
+ *   conv_out : NULL, or the same layout: receives the last 3 raw tokens of
+ *              each tensor (taken from conv_in where T < 3), for the next
+ *              call.  May equal conv_in (updated in place); otherwise must
+ *              not overlap it, the weights or the inputs.
+ *
+ * g, beta, scale, h0, out, hT and the validation are those of kda_chunk_fwd;
+ * out must not overlap the weights or the conv buffers either.  T == 0 copies
+ * conv_in (or zeros) to conv_out and h0 (or zeros) to hT.
+ */
+KDA_API kda_status_t kda_chunk_fwd_conv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *wq, const float *wk, const float *wv,
+                                const uint16_t *conv_in, uint16_t *conv_out,
+                                const float *g, const float *beta, float scale,
+                                const float *h0, uint16_t *out, float *hT,
+                                int B, int T, int H, hipStream_t stream);
+
+/*
  * kda_chunk_fwd_f32 — as kda_chunk_fwd, with fp32 q, k, v and out and fp32
  * matrix-core products throughout (the fp32-input accuracy mode).
  */

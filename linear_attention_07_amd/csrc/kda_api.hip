@@ -64,12 +64,16 @@ hipError_t pool_for_device(hipMemPool_t* pool) {
     return hipSuccess;
 }
 
-// F32: fp32 q / k / v / out (else bf16); G16: bf16 g (else fp32; bf16 I/O only)
+// F32: fp32 q / k / v / out (else bf16); G16: bf16 g (else fp32; bf16 I/O only).
+// conv.wq != NULL: q, k, v are raw values before the short convolution (bf16
+// I/O only); conv_out (or NULL) receives the conv state after the sequence.
 template <bool F32, bool G16 = false>
 kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                        const float* beta, float scale, const float* h0, void* out, float* hT,
-                       int B, int T, int H, hipStream_t stream) {
+                       int B, int T, int H, hipStream_t stream, kda::ConvArgs conv = {},
+                       void* conv_out = nullptr) {
     static_assert(!(F32 && G16), "bf16 g is offered with bf16 q / k / v only");
+    const bool cv = conv.wq != nullptr;
     constexpr size_t es = F32 ? 4 : 2;
     constexpr size_t gs = G16 ? 2 : 4;
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
@@ -80,8 +84,27 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     if (h0 && hT && h0 != hT && overlap(h0, state_bytes, hT, state_bytes))
         return KDA_ERR_INVALID_ARG;
     if ((int64_t)B * H > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    // the short convolution's taps and state buffers
+    const size_t wbytes = (size_t)H * KDA_HEAD_DIM * 4 * sizeof(float);
+    const size_t cbytes = (size_t)3 * B * 3 * H * KDA_HEAD_DIM * sizeof(uint16_t);
+    if (cv) {
+        if (!conv.wk || !conv.wv) return KDA_ERR_INVALID_ARG;
+        if (!aligned(conv.wq, 16) || !aligned(conv.wk, 16) || !aligned(conv.wv, 16) ||
+            (conv.state && !aligned(conv.state, 16)) || (conv_out && !aligned(conv_out, 16)))
+            return KDA_ERR_INVALID_ARG;
+        if (conv.state && conv_out && conv.state != conv_out &&
+            overlap(conv.state, cbytes, conv_out, cbytes))
+            return KDA_ERR_INVALID_ARG;
+        conv.B = B;
+    }
 
     if (T == 0) {
+        if (cv && conv_out && conv_out != conv.state) {
+            // no tokens: the state passes through (zeros if there is none)
+            const hipError_t e = kda::launch_conv_state_out(nullptr, nullptr, nullptr, B, 0, H,
+                                                            conv, conv_out, stream);
+            if (e != hipSuccess) return KDA_ERR_HIP;
+        }
         if (!hT || hT == h0) return KDA_OK;
         const hipError_t e =
             kda::launch_copy_or_zero(h0, hT, state_bytes / sizeof(float), stream);
@@ -100,6 +123,16 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
         overlap(out, io_bytes, beta, n_tok * 4) || overlap(out, io_bytes, h0, state_bytes) ||
         overlap(out, io_bytes, hT, state_bytes))
         return KDA_ERR_INVALID_ARG;
+    if (cv) {
+        const void* ws_[] = {conv.wq, conv.wk, conv.wv};
+        for (const void* p : ws_)
+            if (overlap(out, io_bytes, p, wbytes) || overlap(conv_out, cbytes, p, wbytes))
+                return KDA_ERR_INVALID_ARG;
+        if (overlap(out, io_bytes, conv.state, cbytes) || overlap(out, io_bytes, conv_out, cbytes))
+            return KDA_ERR_INVALID_ARG;
+        for (const void* p : ins)
+            if (overlap(conv_out, cbytes, p, io_bytes)) return KDA_ERR_INVALID_ARG;
+    }
 
     const int slices = F32 ? kda::chunk_f32_slices() : kda::chunk16_slices();
     if ((int64_t)B * H * slices > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
@@ -135,10 +168,10 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
         float* h_out = last ? (hT ? hT : nullptr) : carry;
         hipError_t e1, e2;
         if constexpr (v16) {
-            e1 = kda::launch_prep16(q, k, g, G16, beta, B, T, H, c0, n, ws, stream);
-            e2 = e1 == hipSuccess
-                     ? kda::launch_scan16(ws, v, h_in, h_out, out, scale, B, T, H, c0, n, stream)
-                     : e1;
+            e1 = kda::launch_prep16(q, k, g, G16, beta, B, T, H, c0, n, ws, conv, stream);
+            e2 = e1 == hipSuccess ? kda::launch_scan16(ws, v, h_in, h_out, out, scale, B, T, H, c0,
+                                                       n, conv, stream)
+                                  : e1;
         } else {
             e1 = kda::launch_chunk_prep_f32(static_cast<const float*>(q),
                                             static_cast<const float*>(k),
@@ -155,6 +188,11 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
             break;
         }
     }
+    // the conv state after the sequence, once every segment has read the one
+    // before it (conv_out may be the same buffer)
+    if (st == KDA_OK && cv && conv_out &&
+        kda::launch_conv_state_out(q, k, v, B, T, H, conv, conv_out, stream) != hipSuccess)
+        st = KDA_ERR_HIP;
     if (carry) (void)hipFreeAsync(carry, stream);
     (void)hipFreeAsync(ws, stream);
     return st;
@@ -221,6 +259,21 @@ kda_status_t kda_chunk_fwd_g16(const uint16_t* q, const uint16_t* k, const uint1
                                const uint16_t* g, const float* beta, float scale, const float* h0,
                                uint16_t* out, float* hT, int B, int T, int H, hipStream_t stream) {
     return chunk_fwd<false, true>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream);
+}
+
+kda_status_t kda_chunk_fwd_conv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const float* wq, const float* wk, const float* wv,
+                                const uint16_t* conv_in, uint16_t* conv_out, const float* g,
+                                const float* beta, float scale, const float* h0, uint16_t* out,
+                                float* hT, int B, int T, int H, hipStream_t stream) {
+    if (!wq || !wk || !wv) return KDA_ERR_INVALID_ARG;
+    kda::ConvArgs conv;
+    conv.wq = wq;
+    conv.wk = wk;
+    conv.wv = wv;
+    conv.state = conv_in;
+    return chunk_fwd<false>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream, conv,
+                            conv_out);
 }
 
 kda_status_t kda_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* g,

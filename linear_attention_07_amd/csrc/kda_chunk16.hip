@@ -99,6 +99,42 @@ __host__ __device__ constexpr int tm_off(int f) {
 }
 static_assert(tm_off(5) + 1024 == (int)Rec16::kTM, "T / M fragment offsets");
 
+// Short convolution + SiLU of 8 consecutive channels cb.. of token tok of a
+// [B, T, H, 128] bf16 tensor x: silu(sum_j w_j x_{tok-3+j}) per channel, taps
+// w [H][128][4] (tap 3 = the current token), tokens before the sequence from
+// st ([B][3][H][128] bf16, the raw tokens -3 .. -1) or zero.  Every load is
+// issued from a valid address (a clamped one where the value is unused) and
+// masked at use, so none waits on a select.  Returns the 8 results as bf16.
+__device__ __forceinline__ u32x4 conv_silu8(const uint16_t* x, const float* w,
+                                            const uint16_t* st, int b, int64_t tok, int T,
+                                            int H, int h, int cb) {
+    u32x4 xr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t t = tok - 3 + j;
+        const uint16_t* src = t >= 0 ? x + (((int64_t)b * T + t) * H + h) * kD + cb
+                              : st   ? st + (((int64_t)b * 3 + (3 + t)) * H + h) * kD + cb
+                                     : x + ((int64_t)b * T * H + h) * kD + cb;
+        xr[j] = *reinterpret_cast<const u32x4*>(src);
+    }
+    const float* wr = w + ((size_t)h * kD + cb) * 4;  // 8 channels x 4 taps
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const f32x4 we = *reinterpret_cast<const f32x4*>(wr + 4 * e);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool live = tok - 3 + j >= 0 || st != nullptr;
+            const uint32_t wd = xr[j][e >> 1];
+            const float xv = __builtin_bit_cast(float, (e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+            acc += live ? we[j] * xv : 0.f;
+        }
+        y[e] = acc * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * acc));
+    }
+    return u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
+}
+
 }  // namespace
 
 size_t chunk16_record_bytes() { return Rec16::BYTES; }
@@ -108,13 +144,15 @@ int chunk16_slices() { return kSlices; }
 // prep: wave p owns chunk rows 16p..16p+15; lane (n, gq) owns row r = 16p + n
 // and the 32 channels 32s + 8gq + e (s = 0..3, e = 0..7), i.e. its A-operand
 // fragments of the four k32 steps over the 128 channels.  G16: g arrives as
-// bf16 (widened to fp32 on load) instead of fp32.
+// bf16 (widened to fp32 on load) instead of fp32.  CONV: q and k are the raw
+// values before the short convolution, which is applied on load (the
+// filtered values rounded to bf16).
 // ---------------------------------------------------------------------------
-template <bool G16>
+template <bool G16, bool CONV>
 __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const void* __restrict__ g,
     const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
-    uint8_t* __restrict__ ws) {
+    uint8_t* __restrict__ ws, ConvArgs conv) {
     __shared__ __align__(16) float tau_s[4][kD];      // block totals of g (log2 units)
     __shared__ __align__(16) float tab_s[kTabs][kD];  // factor tables
     __shared__ float beta_s[kChunk];
@@ -164,8 +202,17 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int cb = 32 * s + 8 * gq;
-        pq[s] = valid ? *reinterpret_cast<const u32x4*>(q + rowoff + cb) : z4;
-        pk[s] = valid ? *reinterpret_cast<const u32x4*>(k + rowoff + cb) : z4;
+        if constexpr (CONV) {
+            const size_t st_n = (size_t)conv.B * 3 * H * kD;  // one tensor's state
+            const uint16_t* sq = conv.state;
+            const uint16_t* sk = conv.state ? conv.state + st_n : nullptr;
+            const int64_t tk = valid ? tok : 0;
+            pq[s] = valid ? conv_silu8(q, conv.wq, sq, b, tk, T, H, h, cb) : z4;
+            pk[s] = valid ? conv_silu8(k, conv.wk, sk, b, tk, T, H, h, cb) : z4;
+        } else {
+            pq[s] = valid ? *reinterpret_cast<const u32x4*>(q + rowoff + cb) : z4;
+            pk[s] = valid ? *reinterpret_cast<const u32x4*>(k + rowoff + cb) : z4;
+        }
         if constexpr (G16) {
             const u32x4 x = valid
                 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g) + rowoff + cb)
@@ -467,10 +514,13 @@ __device__ __forceinline__ bf16x8 frag_tm(const u32x4* mat, int f, int lane) {
     return __builtin_bit_cast(bf16x8, mat[tm_off(f) / 16 + lane]);
 }
 
+// CONV: v holds the raw values before the short convolution, which the
+// loaders apply to each V piece before it goes to LDS (rounded to bf16).
+template <bool CONV>
 __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, float scale,
     const float* h_in, float* h_out, uint16_t* __restrict__ out, int T, int H, int chunk0,
-    int nchunks) {
+    int nchunks, ConvArgs conv) {
     // The record, verbatim: Kt / Qt once, the rest (Kb^T, T / M, gamma) in two
     // buffers by chunk parity, so that the rest of chunk i + 1 is in place
     // while chunk i is scanned.
@@ -516,6 +566,20 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         u32x4 rg = {0u, 0u, 0u, 0u};
         const int64_t vstride = (int64_t)H * kD;
         const uint16_t* vslice = v + ((int64_t)b * T * H + h) * kD + kCols * slice;
+        // short convolution of V: the 4 token rows of each piece, the taps of
+        // this thread's 8 columns (the same for both of its pieces), the state
+        // rows of the slice (tokens -3 .. -1)
+        u32x4 rv4[2][4];
+        f32x4 wcol[8];
+        const uint16_t* vst = nullptr;
+        if constexpr (CONV) {
+            const float* wr = conv.wv + ((size_t)h * kD + kCols * slice + (tid & 7) * 8) * 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wcol[e] = *reinterpret_cast<const f32x4*>(wr + 4 * e);
+            if (conv.state)
+                vst = conv.state + (size_t)2 * conv.B * 3 * H * kD +
+                      ((int64_t)b * 3 * H + h) * kD + kCols * slice;
+        }
 #define KDA_LOAD_ISSUE(cl_)                                                                      \
     do {                                                                                         \
         const u32x4* src_ = reinterpret_cast<const u32x4*>(                                      \
@@ -526,8 +590,19 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         _Pragma("unroll") for (int m_ = 0; m_ < 2; ++m_) {                                       \
             const int pc_ = tid + 256 * m_;                                                      \
             const int64_t tk_ = (int64_t)(chunk0 + (cl_)) * kChunk + (pc_ >> 3);                 \
-            rv[m_] = *reinterpret_cast<const u32x4*>(vslice + (tk_ < T ? tk_ : 0) * vstride +    \
-                                                     (pc_ & 7) * 8);                             \
+            if constexpr (CONV) {                                                                \
+                _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                               \
+                    const int64_t t_ = tk_ - 3 + j_;                                             \
+                    const uint16_t* src_ =                                                       \
+                        t_ >= 0 ? vslice + (t_ < T ? t_ : T - 1) * vstride + (pc_ & 7) * 8       \
+                        : vst   ? vst + (3 + t_) * vstride + (pc_ & 7) * 8                       \
+                                : vslice + (pc_ & 7) * 8;                                        \
+                    rv4[m_][j_] = *reinterpret_cast<const u32x4*>(src_);                         \
+                }                                                                                \
+            } else {                                                                             \
+                rv[m_] = *reinterpret_cast<const u32x4*>(vslice + (tk_ < T ? tk_ : 0) * vstride + \
+                                                         (pc_ & 7) * 8);                         \
+            }                                                                                    \
         }                                                                                        \
     } while (0)
         // Per chunk i: the rest into buffer i & 1 (released by chunk i - 2),
@@ -552,10 +627,32 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int pc = tid + 256 * m, tk = pc >> 3;
-                const bool ok = (int64_t)(chunk0 + i) * kChunk + tk < T;
+                const int64_t tkg = (int64_t)(chunk0 + i) * kChunk + tk;
+                const bool ok = tkg < T;
+                u32x4 x = rv[m];
+                if constexpr (CONV) {
+                    // silu(sum_j w_j v_{t-3+j}) per column, taps before the
+                    // sequence from the state or zero
+                    float y[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const bool live = tkg - 3 + j >= 0 || vst != nullptr;
+                            const uint32_t wd = rv4[m][j][e >> 1];
+                            const float xv =
+                                __builtin_bit_cast(float, (e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                            acc += live ? wcol[e][j] * xv : 0.f;
+                        }
+                        y[e] = acc * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * acc));
+                    }
+                    x = u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]),
+                              pack2(y[6], y[7])};
+                }
                 uint2* d2 = reinterpret_cast<uint2*>(&v_s[tk * VP + (pc & 7) * 8]);
-                d2[0] = ok ? uint2{rv[m][0], rv[m][1]} : uint2{0u, 0u};
-                d2[1] = ok ? uint2{rv[m][2], rv[m][3]} : uint2{0u, 0u};
+                d2[0] = ok ? uint2{x[0], x[1]} : uint2{0u, 0u};
+                d2[1] = ok ? uint2{x[2], x[3]} : uint2{0u, 0u};
             }
             signal(&sync_s[0], lane);
             if (i + 1 < nchunks) {
@@ -750,26 +847,78 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 
 hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
                          const float* beta, int B, int T, int H, int chunk0, int nchunks, void* ws,
-                         hipStream_t stream) {
+                         const ConvArgs& conv, hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
-    if (g_bf16)
-        hipLaunchKernelGGL(kda_prep16_kernel<true>, dim3(nblk), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), g,
-                           beta, T, H, chunk0, nchunks, static_cast<uint8_t*>(ws));
+    const uint16_t* q16 = static_cast<const uint16_t*>(q);
+    const uint16_t* k16 = static_cast<const uint16_t*>(k);
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    const bool cv = conv.wq != nullptr;
+    if (g_bf16 && cv)
+        hipLaunchKernelGGL((kda_prep16_kernel<true, true>), dim3(nblk), dim3(256), 0, stream,
+                           q16, k16, g, beta, T, H, chunk0, nchunks, w8, conv);
+    else if (g_bf16)
+        hipLaunchKernelGGL((kda_prep16_kernel<true, false>), dim3(nblk), dim3(256), 0, stream,
+                           q16, k16, g, beta, T, H, chunk0, nchunks, w8, conv);
+    else if (cv)
+        hipLaunchKernelGGL((kda_prep16_kernel<false, true>), dim3(nblk), dim3(256), 0, stream,
+                           q16, k16, g, beta, T, H, chunk0, nchunks, w8, conv);
     else
-        hipLaunchKernelGGL(kda_prep16_kernel<false>, dim3(nblk), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), g,
-                           beta, T, H, chunk0, nchunks, static_cast<uint8_t*>(ws));
+        hipLaunchKernelGGL((kda_prep16_kernel<false, false>), dim3(nblk), dim3(256), 0, stream,
+                           q16, k16, g, beta, T, H, chunk0, nchunks, w8, conv);
     return hipGetLastError();
 }
 
 hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
                          void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
-                         hipStream_t stream) {
+                         const ConvArgs& conv, hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * kSlices);
-    hipLaunchKernelGGL(kda_scan16_kernel, dim3(nblk), dim3(512), 0, stream,
-                       static_cast<const uint8_t*>(ws), static_cast<const uint16_t*>(v), scale,
-                       h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks);
+    if (conv.wq)
+        hipLaunchKernelGGL(kda_scan16_kernel<true>, dim3(nblk), dim3(512), 0, stream,
+                           static_cast<const uint8_t*>(ws), static_cast<const uint16_t*>(v), scale,
+                           h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks, conv);
+    else
+        hipLaunchKernelGGL(kda_scan16_kernel<false>, dim3(nblk), dim3(512), 0, stream,
+                           static_cast<const uint8_t*>(ws), static_cast<const uint16_t*>(v), scale,
+                           h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks, conv);
+    return hipGetLastError();
+}
+
+// one thread per (tensor, batch, head, channel): its 3 values are read before
+// any is written, so st_out may equal conv.state
+__global__ void kda_conv_state_out_kernel(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                          int B, int T, int H, const uint16_t* st_in,
+                                          uint16_t* st_out) {
+    const int64_t n = (int64_t)3 * B * H * kD;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(idx % kD);
+        const int h = (int)((idx / kD) % H);
+        const int b = (int)((idx / ((int64_t)kD * H)) % B);
+        const int ten = (int)(idx / ((int64_t)kD * H * B));
+        const uint16_t* x = ten == 0 ? q : ten == 1 ? k : v;
+        uint16_t val[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int64_t t = (int64_t)T - 3 + j;
+            val[j] = t >= 0 ? x[(((int64_t)b * T + t) * H + h) * kD + c]
+                   : st_in ? st_in[((((int64_t)ten * B + b) * 3 + (3 + t)) * H + h) * kD + c]
+                           : (uint16_t)0;
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) st_out[((((int64_t)ten * B + b) * 3 + j) * H + h) * kD + c] = val[j];
+    }
+}
+
+hipError_t launch_conv_state_out(const void* q, const void* k, const void* v, int B, int T,
+                                 int H, const ConvArgs& conv, void* st_out, hipStream_t stream) {
+    const int64_t n = (int64_t)3 * B * H * kD;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_conv_state_out_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), B, T, H, conv.state,
+                       static_cast<uint16_t*>(st_out));
     return hipGetLastError();
 }
 

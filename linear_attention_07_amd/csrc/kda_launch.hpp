@@ -27,6 +27,18 @@ hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_
                                  float* out, float scale, int B, int T, int H, int chunk0,
                                  int nchunks, hipStream_t stream);
 
+// Short convolution in front of the attention: depthwise 4-tap causal filter
+// per head and channel, then SiLU, on q, k and v.  wq == NULL: none.  state:
+// the 3 raw tokens before the sequence, [3 (q, k, v)][B][3][H][128] bf16, or
+// NULL for zeros.
+struct ConvArgs {
+    const float* wq = nullptr;  // [H][128][4] fp32, tap 3 = the current token
+    const float* wk = nullptr;
+    const float* wv = nullptr;
+    const uint16_t* state = nullptr;
+    int B = 0;
+};
+
 // two-kernel chunked prefill for bf16 q/k/v/o: prep writes one record per
 // (batch, head, chunk) of chunks [chunk0, chunk0 + nchunks) into ws, from g in
 // fp32 or (g_bf16) bf16; scan walks them in order (h_in NULL = zero state,
@@ -35,10 +47,15 @@ size_t chunk16_record_bytes();
 int chunk16_slices();
 hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
                          const float* beta, int B, int T, int H, int chunk0, int nchunks, void* ws,
-                         hipStream_t stream);
+                         const ConvArgs& conv, hipStream_t stream);
 hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
                          void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
-                         hipStream_t stream);
+                         const ConvArgs& conv, hipStream_t stream);
+// the conv state after the sequence: the last 3 raw tokens of q, k, v (from
+// the inputs, or from conv.state where T < 3), [3][B][3][H][128]; safe in
+// place (st_out == conv.state)
+hipError_t launch_conv_state_out(const void* q, const void* k, const void* v, int B, int T,
+                                 int H, const ConvArgs& conv, void* st_out, hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < n (fp32), as a kernel so that it can be
 // captured in a graph.

@@ -25,6 +25,7 @@ KDA_ERR_NO_MEMORY = 4
 
 EXPORTS = (
     "kda_chunk_fwd",
+    "kda_chunk_fwd_conv",
     "kda_chunk_fwd_f32",
     "kda_chunk_fwd_g16",
     "kda_recurrent_step",
@@ -54,8 +55,9 @@ def load() -> ctypes.CDLL:
     vp, f, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     chunk_args = [vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, vp]
     step_args = [vp, vp, vp, vp, vp, f, vp, vp, i, i, vp]
+    conv_args = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, vp]
     for name, args in (("kda_chunk_fwd", chunk_args), ("kda_chunk_fwd_f32", chunk_args),
-                       ("kda_chunk_fwd_g16", chunk_args),
+                       ("kda_chunk_fwd_g16", chunk_args), ("kda_chunk_fwd_conv", conv_args),
                        ("kda_recurrent_step", step_args), ("kda_recurrent_step_f32", step_args)):
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -129,6 +131,52 @@ def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=T
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
     return out, hT
+
+
+def chunk_fwd_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_in=None,
+                   conv_out=None, out=None, hT=None, final_state=True, final_conv=True):
+    """Chunkwise prefill with the 4-tap short convolution + SiLU applied to the
+    raw q, k, v first (kda_chunk_fwd_conv).  q, k, v: [B, T, H, 128] bf16 raw
+    values; wq, wk, wv: [H, 128, 4] fp32 taps; conv_in / conv_out: optional
+    [3, B, 3, H, 128] bf16 (q, k, v; the 3 raw tokens before the first, oldest
+    first); the rest as chunk_fwd with fp32 g.  Returns (out, hT, conv_out);
+    conv_out is None when final_conv is False and no buffer is given."""
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q: expected [B, T, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    B, T, H, _ = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda tensors must live on a GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.shape, torch.bfloat16, dev)
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _check(t, name, (H, HEAD_DIM, 4), torch.float32, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    sshape = (B, H, HEAD_DIM, HEAD_DIM)
+    cshape = (3, B, 3, H, HEAD_DIM)
+    if h0 is not None:
+        _check(h0, "h0", sshape, torch.float32, dev)
+    if conv_in is not None:
+        _check(conv_in, "conv_in", cshape, torch.bfloat16, dev)
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _check(out, "out", q.shape, torch.bfloat16, dev)
+    if hT is None and final_state:
+        hT = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif hT is not None:
+        _check(hT, "hT", sshape, torch.float32, dev)
+    if conv_out is None and final_conv:
+        conv_out = torch.empty(cshape, dtype=torch.bfloat16, device=dev)
+    elif conv_out is not None:
+        _check(conv_out, "conv_out", cshape, torch.bfloat16, dev)
+    st = load().kda_chunk_fwd_conv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(conv_in), _ptr(conv_out),
+        _ptr(g), _ptr(beta), float(scale), _ptr(h0), _ptr(out), _ptr(hT), B, T, H, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_conv")
+    return out, hT, conv_out
 
 
 def recurrent_step(q, k, v, g, beta, scale, S, out=None):

@@ -14,6 +14,14 @@ bytes).  The recipes:
   initial state ~ N(0, sigma^2) per entry, sigma = 0.1 ("N(0, 0.01)" read as
         mean and variance), or zero.
 
+For the short convolution in front of the attention (kda_chunk_fwd_conv):
+
+  raw q, k, v ~ N(0, 1) per entry (the projections' outputs, not normalised:
+        the convolution comes first);
+  taps ~ U(-0.5, 0.5), i.e. +-1/sqrt(4) for 4 taps (a conv layer's usual
+        initial range), [H, 128, 4] fp32 per tensor;
+  conv state ~ N(0, 1) raw tokens [3, B, 3, H, 128], or none (zeros).
+
 Random numbers come from torch's seeded generator on the target device and
 are drawn block by block over tokens so that million-token inputs never need
 an fp32 temporary of the whole tensor.
@@ -119,3 +127,22 @@ def workload_inputs(w: Workload, device="cuda"):
     if w.kind != "prefill":
         raise ValueError("decode workloads are drawn per step with decode_step_inputs")
     return prefill_inputs(w.B, w.T, w.H, w.io, w.seed, w.g_shift, w.h0_std, device)
+
+
+def conv_inputs(B, T, H, seed=0, with_state=True, h0_std=0.1, device="cuda"):
+    """Inputs of the attention with its short convolution: raw q, k, v
+    [B, T, H, 128] bf16; wq, wk, wv [H, 128, 4] fp32; conv_in
+    [3, B, 3, H, 128] bf16 or None; g, beta, h0, scale as prefill_inputs."""
+    inp = prefill_inputs(B, T, H, torch.bfloat16, seed, h0_std=h0_std, device=device)
+    dev = torch.device(device)
+    gen = _gen(dev, 7_919 * (int(seed) + 1) + 17)
+    shp = (B, T, H, HEAD_DIM)
+    for name in ("q", "k", "v"):
+        inp[name] = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+    for name in ("wq", "wk", "wv"):
+        inp[name] = torch.rand((H, HEAD_DIM, 4), generator=gen, device=dev) - 0.5
+    inp["conv_in"] = None
+    if with_state:
+        inp["conv_in"] = torch.randn((3, B, 3, H, HEAD_DIM), generator=gen,
+                                     device=dev).to(torch.bfloat16)
+    return inp

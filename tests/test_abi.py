@@ -90,6 +90,38 @@ def test_chunk_empty_is_a_no_op(lib, fn):
     assert chunk(lib, fn, T=0, h0=P[7], hT=P[7]) == libkda.KDA_OK
 
 
+def conv(lib, q=P[0], k=P[1], v=P[2], wq=P[8], wk=P[9], wv=P[10], conv_in=NULL, conv_out=NULL,
+         g=P[3], beta=P[4], scale=1.0, h0=NULL, out=P[5], hT=NULL, B=1, T=4, H=1):
+    return lib.kda_chunk_fwd_conv(q, k, v, wq, wk, wv, conv_in, conv_out, g, beta, scale, h0, out,
+                                  hT, B, T, H, None)
+
+
+def test_conv_invalid_arguments(lib):
+    INV = libkda.KDA_ERR_INVALID_ARG
+    assert conv(lib, B=-1) == INV
+    assert conv(lib, scale=math.nan) == INV
+    for name in ("q", "k", "v", "g", "beta", "out", "wq", "wk", "wv"):
+        assert conv(lib, **{name: NULL}) == INV, name
+    for name in ("wq", "wk", "wv", "conv_in", "conv_out"):
+        assert conv(lib, **{name: ctypes.c_void_p(A * 12 + 8)}) == INV, name
+    # conv_in and conv_out partly overlapping (equal is the in-place update)
+    assert conv(lib, conv_in=P[11], conv_out=ctypes.c_void_p(A * 12 + 512)) == INV
+    # out over a weight or a conv buffer; conv_out over a weight or an input
+    assert conv(lib, out=ctypes.c_void_p(A * 9 + 256)) == INV
+    assert conv(lib, conv_in=P[11], out=ctypes.c_void_p(A * 12 + 1024)) == INV
+    assert conv(lib, conv_out=ctypes.c_void_p(A * 10 + 1024)) == INV
+    assert conv(lib, conv_out=ctypes.c_void_p(A * 2 + 512)) == INV
+
+
+def test_conv_empty_is_a_no_op(lib):
+    assert conv(lib, B=0) == libkda.KDA_OK
+    assert conv(lib, H=0) == libkda.KDA_OK
+    # no tokens, no state to produce
+    assert conv(lib, T=0, q=NULL, k=NULL, v=NULL, g=NULL, beta=NULL, out=NULL) == libkda.KDA_OK
+    # no tokens, conv state updated in place: already there
+    assert conv(lib, T=0, conv_in=P[11], conv_out=P[11], h0=P[7], hT=P[7]) == libkda.KDA_OK
+
+
 @pytest.mark.parametrize("fn", ["kda_recurrent_step", "kda_recurrent_step_f32"])
 def test_step_invalid_arguments(lib, fn):
     INV = libkda.KDA_ERR_INVALID_ARG
@@ -114,6 +146,9 @@ def test_binding_rejects_bad_tensors():
         libkda.chunk_fwd(q, q, q, q.float(), torch.zeros(1, 4, 1), 1.0)  # CPU tensors
     with pytest.raises(ValueError):
         libkda.chunk_fwd(q[..., :64], q, q, q.float(), torch.zeros(1, 4, 1), 1.0)
+    w = torch.zeros(1, 128, 4)
+    with pytest.raises(ValueError):
+        libkda.chunk_fwd_conv(q, q, q, w, w, w, q.float(), torch.zeros(1, 4, 1), 1.0)
     with pytest.raises(ValueError):
         libkda.recurrent_step(q[0], q[0], q[0], q[0].float(), torch.zeros(4, 1),
                               1.0, torch.zeros(4, 1, 128, 128))
