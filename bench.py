@@ -5,9 +5,11 @@ A step is one kda_chunk_fwd over the 64K-token, 96-head prefill batch
 (B=1, H=96, T=65536, d=128; bf16 q/k/v, fp32 g/beta, fp32 state with a
 random initial state) with every input already resident in HBM.  The value is
 prefill Mtok/s (B*T tokens per step, all 96 heads).  The same run also times
-the same prefill with g in bf16 (kda_chunk_fwd_g16), the batched decode step (B=256, H=96, fp32 state streamed in place) and
-reports its state bandwidth, and times the fp64 CPU oracle on a bounded
-sample of the prefill workload as a baseline.
+the same prefill with g in bf16 (kda_chunk_fwd_g16) and with the short
+convolution in front (kda_chunk_fwd_conv), the batched decode step (B=256,
+H=96, fp32 state streamed in place; also with the short convolution,
+kda_recurrent_step_conv) and reports its state bandwidth, and times the fp64
+CPU oracle on a bounded sample of the prefill workload as a baseline.
 
 Roofline (per call of the timed op, algorithmic bytes only):
   prefill: 1540 B per token-head (q, k, v, o in bf16 = 4 x 256 B; g 512 B;
@@ -35,6 +37,11 @@ PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
 PREFILL_G16_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
 STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_SEQ_HEAD = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256
+# the short convolution's state: 3 raw bf16 tokens of q, k and v per
+# (sequence, head), read and written once per decode step; its taps
+# (3 x [H, 128, 4] fp32) are read once per call
+CONV_STATE_BYTES = 3 * 3 * 128 * 2
+CONV_TAP_BYTES_PER_HEAD = 3 * 128 * 4 * 4
 
 
 def parse():
@@ -184,6 +191,22 @@ def main():
           f"{g16_gbps:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
     del g16
 
+    # ---- prefill with the short convolution ---------------------------------
+    cp = synth.conv_params(w.B, w.H, seed=w.seed, device=dev)
+    cout = torch.empty_like(cp["conv_state"])
+
+    def prefill_conv():
+        libkda.chunk_fwd_conv(inp["q"], inp["k"], inp["v"], cp["wq"], cp["wk"], cp["wv"],
+                              inp["g"], inp["beta"], inp["scale"], inp["h0"],
+                              conv_in=cp["conv_state"], conv_out=cout, out=out, hT=hT)
+
+    cms, cms_med, cms_min = time_op(torch, prefill_conv, args.steps, args.warmup)
+    conv_bytes = pre_bytes + w.B * w.H * 2 * CONV_STATE_BYTES + w.H * CONV_TAP_BYTES_PER_HEAD
+    conv_gbps = conv_bytes / (cms / 1e3) / 1e9
+    print(f"# prefill, short conv: {cms:.3f} ms/step, {tokens / (cms / 1e3) / 1e6:.2f} Mtok/s, "
+          f"{conv_gbps:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+    del cp, cout
+
     # ---- decode -------------------------------------------------------------
     wd = synth.WORKLOADS["decode_b256"]
     S = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
@@ -205,6 +228,26 @@ def main():
     dec_gbps = nbh * DECODE_BYTES_PER_SEQ_HEAD / (dms / 1e3) / 1e9
     print(f"# decode: {dms:.3f} ms/step, state {state_gbps:.0f} GB/s, "
           f"total {dec_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # ---- decode with the short convolution ----------------------------------
+    dcp = synth.conv_params(wd.B, wd.H, seed=wd.seed, device=dev)
+    xcs = [synth.decode_conv_inputs(wd.B, wd.H, seed=wd.seed, step=t, device=dev)
+           for t in range(4)]
+
+    def decode_conv():
+        x = xcs[it[0] & 3]
+        it[0] += 1
+        libkda.recurrent_step_conv(x["q"], x["k"], x["v"], dcp["wq"], dcp["wk"], dcp["wv"],
+                                   dcp["conv_state"], x["g"], x["beta"], x["scale"], S,
+                                   out=dout)
+
+    cdms, cdms_med, cdms_min = time_op(torch, decode_conv, dsteps, args.warmup)
+    dconv_bytes = nbh * (DECODE_BYTES_PER_SEQ_HEAD + 2 * CONV_STATE_BYTES) + \
+        wd.H * CONV_TAP_BYTES_PER_HEAD
+    dconv_gbps = dconv_bytes / (cdms / 1e3) / 1e9
+    print(f"# decode, short conv: {cdms:.3f} ms/step, total {dconv_gbps:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    del dcp, xcs
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -270,6 +313,37 @@ def main():
                 "unit": "GB/s",
                 "frac": round(g16_gbps / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_call": g16_bytes,
+            },
+        },
+        "prefill_conv": {
+            "workload": "prefill_64k with the 4-tap short convolution + SiLU on q, k, v "
+                        "(kda_chunk_fwd_conv), conv state in and out",
+            "ms_per_step": round(cms, 4),
+            "ms_per_step_median": round(cms_med, 4),
+            "ms_per_step_min": round(cms_min, 4),
+            "Mtok_s": round(tokens / (cms / 1e3) / 1e6, 3),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(conv_gbps, 1),
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": round(conv_gbps / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes_per_call": conv_bytes,
+            },
+        },
+        "decode_conv": {
+            "workload": "decode_b256 with the short convolution (kda_recurrent_step_conv): "
+                        "conv state advanced in place",
+            "ms_per_step": round(cdms, 4),
+            "ms_per_step_median": round(cdms_med, 4),
+            "ms_per_step_min": round(cdms_min, 4),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(dconv_gbps, 1),
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": round(dconv_gbps / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes_per_call": dconv_bytes,
             },
         },
         "decode": {

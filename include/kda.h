@@ -168,6 +168,34 @@ KDA_API kda_status_t kda_recurrent_step(const uint16_t *q, const uint16_t *k, co
                                 float *S_inout, uint16_t *out,
                                 int B, int H, hipStream_t stream);
 
+/*
+ * kda_recurrent_step_conv — kda_recurrent_step with the short convolution and
+ * SiLU in front of the attention (the same filter as kda_chunk_fwd_conv, read
+ * as depthwise, causal, 4 taps, no bias), for decoding after a
+ * kda_chunk_fwd_conv prefill:
+ *
+ *   x'[b,h,c] = silu( w[h,c,3] * x[b,h,c] + sum_{j=0..2} w[h,c,j] * st_x[b,j,h,c] ),
+ *
+ * rounded to bf16, is the q, k or v of kda_recurrent_step.
+ *
+ *   q, k, v    : [B, H, 128] bf16 RAW values of the new token.
+ *   wq/wk/wv   : [H, 128, 4] fp32 taps, as in kda_chunk_fwd_conv.  Required.
+ *   conv_state : [3][B][3][H][128] bf16, the layout kda_chunk_fwd_conv's
+ *                conv_out writes: for q, k, v, the 3 raw tokens before this
+ *                one, oldest first.  Required.  Updated in place: on return
+ *                it holds the last 3 raw tokens including this one.  Must not
+ *                overlap any other argument.
+ *
+ * g, beta, scale, S_inout, out and the validation are those of
+ * kda_recurrent_step; out must not overlap the taps or the conv state.
+ */
+KDA_API kda_status_t kda_recurrent_step_conv(const uint16_t *q, const uint16_t *k,
+                                     const uint16_t *v, const float *wq, const float *wk,
+                                     const float *wv, uint16_t *conv_state,
+                                     const float *g, const float *beta, float scale,
+                                     float *S_inout, uint16_t *out,
+                                     int B, int H, hipStream_t stream);
+
 /* kda_recurrent_step_f32 — as kda_recurrent_step with fp32 q, k, v, out. */
 KDA_API kda_status_t kda_recurrent_step_f32(const float *q, const float *k, const float *v,
                                     const float *g, const float *beta, float scale,

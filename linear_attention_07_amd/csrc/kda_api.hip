@@ -198,10 +198,12 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     return st;
 }
 
+// conv != NULL: q, k, v are raw values before the short convolution (bf16 I/O
+// only), and conv->state is advanced by one token in place.
 template <bool F32>
 kda_status_t recurrent_step(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, float scale, float* S, void* out, int B, int H,
-                            hipStream_t stream) {
+                            hipStream_t stream, kda::DecodeConv* conv = nullptr) {
     constexpr size_t es = F32 ? 4 : 2;
     if (B < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
@@ -221,7 +223,30 @@ kda_status_t recurrent_step(const void* q, const void* k, const void* v, const f
         overlap(out, vec, S, sbytes) || overlap(S, sbytes, g, nbh * KDA_HEAD_DIM * 4) ||
         overlap(S, sbytes, beta, nbh * 4))
         return KDA_ERR_INVALID_ARG;
-    const hipError_t e = kda::launch_decode<F32>(q, k, v, g, beta, scale, S, out, B, H, stream);
+    if (conv) {
+        if (F32 || !conv->wq || !conv->wk || !conv->wv || !conv->state) return KDA_ERR_INVALID_ARG;
+        if (!aligned(conv->wq, 16) || !aligned(conv->wk, 16) || !aligned(conv->wv, 16) ||
+            !aligned(conv->state, 16))
+            return KDA_ERR_INVALID_ARG;
+        // the state is written: it may overlap nothing else
+        const size_t cbytes = (size_t)3 * B * 3 * H * KDA_HEAD_DIM * sizeof(uint16_t);
+        const size_t wbytes = (size_t)H * KDA_HEAD_DIM * 4 * sizeof(float);
+        uint16_t* cs = conv->state;
+        for (const void* p : ins)
+            if (overlap(cs, cbytes, p, vec)) return KDA_ERR_INVALID_ARG;
+        const void* taps[] = {conv->wq, conv->wk, conv->wv};
+        for (const void* p : taps)
+            if (overlap(cs, cbytes, p, wbytes) || overlap(out, vec, p, wbytes) ||
+                overlap(S, sbytes, p, wbytes))
+                return KDA_ERR_INVALID_ARG;
+        if (overlap(cs, cbytes, g, nbh * KDA_HEAD_DIM * 4) || overlap(cs, cbytes, beta, nbh * 4) ||
+            overlap(cs, cbytes, S, sbytes) || overlap(cs, cbytes, out, vec))
+            return KDA_ERR_INVALID_ARG;
+        conv->B = B;
+        conv->H = H;
+    }
+    const hipError_t e =
+        kda::launch_decode<F32>(q, k, v, g, beta, scale, S, out, B, H, conv, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -286,6 +311,19 @@ kda_status_t kda_recurrent_step(const uint16_t* q, const uint16_t* k, const uint
                                 const float* g, const float* beta, float scale, float* S_inout,
                                 uint16_t* out, int B, int H, hipStream_t stream) {
     return recurrent_step<false>(q, k, v, g, beta, scale, S_inout, out, B, H, stream);
+}
+
+kda_status_t kda_recurrent_step_conv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const float* wq, const float* wk, const float* wv,
+                                     uint16_t* conv_state, const float* g, const float* beta,
+                                     float scale, float* S_inout, uint16_t* out, int B, int H,
+                                     hipStream_t stream) {
+    kda::DecodeConv conv;
+    conv.wq = wq;
+    conv.wk = wk;
+    conv.wv = wv;
+    conv.state = conv_state;
+    return recurrent_step<false>(q, k, v, g, beta, scale, S_inout, out, B, H, stream, &conv);
 }
 
 kda_status_t kda_recurrent_step_f32(const float* q, const float* k, const float* v,

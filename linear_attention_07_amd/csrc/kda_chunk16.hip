@@ -52,7 +52,6 @@ constexpr int kCols = kD / kSlices;    // value columns per scan workgroup
 // at 32 or 36 dwords).
 constexpr int VP = kCols + 4;
 constexpr int SP = kChunk + 1;         // fp32 pitch of A and X in the prep kernel
-constexpr float kLog2e = 1.4426950408889634f;  // decay sums are kept in log2 units
 
 // decay tables per channel (exp of sums of the four block totals tau_a):
 //   EP_a = exp(sum_{a'<a} tau), EK_a = exp(sum_{a'>a} tau), IE_a = exp(-tau_a),
@@ -99,40 +98,68 @@ __host__ __device__ constexpr int tm_off(int f) {
 }
 static_assert(tm_off(5) + 1024 == (int)Rec16::kTM, "T / M fragment offsets");
 
-// Short convolution + SiLU of 8 consecutive channels cb.. of token tok of a
-// [B, T, H, 128] bf16 tensor x: silu(sum_j w_j x_{tok-3+j}) per channel, taps
-// w [H][128][4] (tap 3 = the current token), tokens before the sequence from
-// st ([B][3][H][128] bf16, the raw tokens -3 .. -1) or zero.  Every load is
-// issued from a valid address (a clamped one where the value is unused) and
-// masked at use, so none waits on a select.  Returns the 8 results as bf16.
-__device__ __forceinline__ u32x4 conv_silu8(const uint16_t* x, const float* w,
-                                            const uint16_t* st, int b, int64_t tok, int T,
-                                            int H, int h, int cb) {
-    u32x4 xr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t t = tok - 3 + j;
-        const uint16_t* src = t >= 0 ? x + (((int64_t)b * T + t) * H + h) * kD + cb
-                              : st   ? st + (((int64_t)b * 3 + (3 + t)) * H + h) * kD + cb
-                                     : x + ((int64_t)b * T * H + h) * kD + cb;
-        xr[j] = *reinterpret_cast<const u32x4*>(src);
+// Short convolution + SiLU of the 8 channels cb.. of token tok = t0 + n of a
+// [B, T, H, 128] bf16 tensor x, where the 16 lanes n = 0..15 of each DPP row
+// hold 16 consecutive tokens with the same channels: silu(sum_j w_j
+// x_{tok-3+j}) per channel, taps wr [8][4] of these channels (tap 3 = the
+// current token),
+// tokens before the sequence from st ([B][3][H][128] bf16, the raw tokens
+// -3 .. -1) or zero.  Each lane loads its own row; lanes 13..15 also load the
+// row 16 tokens back.  A row rotation by j then hands lane n the row of lane
+// n - j, or, for n < j, the back row of lane n - j + 16, i.e. token tok - j
+// in both cases.  Every lane of the row must call this; rows past the end
+// return zeros.  Returns the 8 results as bf16.
+__device__ __forceinline__ u32x4 conv_silu8_row16(const uint16_t* x, const float* wr,
+                                                  const uint16_t* st, int b, int64_t tok, int n,
+                                                  int T, int H, int h, int cb) {
+    const int64_t tc = tok < T ? tok : T - 1;
+    const u32x4 xr =
+        *reinterpret_cast<const u32x4*>(x + (((int64_t)b * T + tc) * H + h) * kD + cb);
+    u32x4 hr = {0u, 0u, 0u, 0u};
+    const int64_t th = tok - 16;  // >= -3: only the first block of a sequence reaches back
+    if (n >= 13 && th < T) {      // a back row at or past the end feeds only rows past it
+        if (th >= 0)
+            hr = *reinterpret_cast<const u32x4*>(x + (((int64_t)b * T + th) * H + h) * kD + cb);
+        else if (st)
+            hr = *reinterpret_cast<const u32x4*>(st + (((int64_t)b * 3 + (3 + th)) * H + h) * kD +
+                                                 cb);
     }
-    const float* wr = w + ((size_t)h * kD + cb) * 4;  // 8 channels x 4 taps
-    float y[8];
+    // the 3 earlier tokens of each register (all lanes take part in the
+    // rotations); then, on rows before the end only, the filter (the branch
+    // also keeps the register demand of the caller within its budget)
+    uint32_t xa[4][4];  // xa[r][j]: register r of token tok - 3 + j
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const f32x4 we = *reinterpret_cast<const f32x4*>(wr + 4 * e);
-        float acc = 0.f;
+    for (int r2 = 0; r2 < 4; ++r2) {
+        xa[r2][3] = xr[r2];
+#define KDA_ROW_ROR(d)                                                                      \
+        xa[r2][3 - (d)] = (uint32_t)__builtin_amdgcn_update_dpp(                            \
+            0, (int)(n >= 16 - (d) ? hr[r2] : xr[r2]), 0x120 + (d), 0xf, 0xf, false)  /* row_ror:d */
+        KDA_ROW_ROR(1);
+        KDA_ROW_ROR(2);
+        KDA_ROW_ROR(3);
+#undef KDA_ROW_ROR
+    }
+    u32x4 res = {0u, 0u, 0u, 0u};
+    if (tok >= T) return res;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool live = tok - 3 + j >= 0 || st != nullptr;
-            const uint32_t wd = xr[j][e >> 1];
-            const float xv = __builtin_bit_cast(float, (e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-            acc += live ? we[j] * xv : 0.f;
+    for (int r2 = 0; r2 < 4; ++r2) {
+        const uint32_t* xj = xa[r2];
+        float y[2];
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const f32x4 we = *reinterpret_cast<const f32x4*>(wr + 4 * (2 * r2 + hi));
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float xv =
+                    __builtin_bit_cast(float, hi ? (xj[j] & 0xffff0000u) : (xj[j] << 16));
+                acc += we[j] * xv;
+            }
+            y[hi] = acc * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * acc));
         }
-        y[e] = acc * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * acc));
+        res[r2] = pack2(y[0], y[1]);
     }
-    return u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
+    return res;
 }
 
 }  // namespace
@@ -161,6 +188,8 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     // (43 KB of LDS each).
     __shared__ __align__(16) float u1_s[kChunk * SP];
     __shared__ float a_s[kChunk * SP];                 // diag(beta) strict-lower KK
+    // CONV: the short convolution's taps of q and k for this head, [2][128][4]
+    __shared__ __align__(16) float taps_s[CONV ? 2 * kD * 4 : 4];
     static_assert(sizeof(bf16x8) * 4 * 4 * 64 <= sizeof(float) * kChunk * SP,
                   "column operands fit the shared area");
     bf16x8 (*zf_s)[4][64] = reinterpret_cast<bf16x8 (*)[4][64]>(u1_s);
@@ -202,14 +231,7 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int cb = 32 * s + 8 * gq;
-        if constexpr (CONV) {
-            const size_t st_n = (size_t)conv.B * 3 * H * kD;  // one tensor's state
-            const uint16_t* sq = conv.state;
-            const uint16_t* sk = conv.state ? conv.state + st_n : nullptr;
-            const int64_t tk = valid ? tok : 0;
-            pq[s] = valid ? conv_silu8(q, conv.wq, sq, b, tk, T, H, h, cb) : z4;
-            pk[s] = valid ? conv_silu8(k, conv.wk, sk, b, tk, T, H, h, cb) : z4;
-        } else {
+        if constexpr (!CONV) {
             pq[s] = valid ? *reinterpret_cast<const u32x4*>(q + rowoff + cb) : z4;
             pk[s] = valid ? *reinterpret_cast<const u32x4*>(k + rowoff + cb) : z4;
         }
@@ -231,6 +253,24 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
         }
     }
     const float bet = valid ? beta[((int64_t)b * T + tok) * H + h] : 0.f;
+    if constexpr (CONV) {
+        // the taps into LDS (one 16-byte piece per thread) while the g loads
+        // are in flight, then q and k through the filter
+        {
+            const float* wsrc = (tid < kD ? conv.wq : conv.wk) + ((size_t)h * kD + (tid & (kD - 1))) * 4;
+            *reinterpret_cast<f32x4*>(&taps_s[4 * tid]) = *reinterpret_cast<const f32x4*>(wsrc);
+        }
+        __syncthreads();
+        const size_t st_n = (size_t)conv.B * 3 * H * kD;  // one tensor's state
+        const uint16_t* sq = conv.state;
+        const uint16_t* sk = conv.state ? conv.state + st_n : nullptr;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cb = 32 * s + 8 * gq;
+            pq[s] = conv_silu8_row16(q, &taps_s[4 * cb], sq, b, tok, n, T, H, h, cb);
+            pk[s] = conv_silu8_row16(k, &taps_s[4 * (kD + cb)], sk, b, tok, n, T, H, h, cb);
+        }
+    }
 
     // ---- norms of q and k; in-block cumsum of g over the 16 rows -------------
     float ssq = 0.f, ssk = 0.f;
@@ -566,10 +606,13 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         u32x4 rg = {0u, 0u, 0u, 0u};
         const int64_t vstride = (int64_t)H * kD;
         const uint16_t* vslice = v + ((int64_t)b * T * H + h) * kD + kCols * slice;
-        // short convolution of V: the 4 token rows of each piece, the taps of
-        // this thread's 8 columns (the same for both of its pieces), the state
-        // rows of the slice (tokens -3 .. -1)
-        u32x4 rv4[2][4];
+        // short convolution of V: a wave's piece m holds 8 consecutive tokens
+        // (lane L: token L / 8, columns 8 (L % 8)), so the 3 tokens before a
+        // lane's token sit 8, 16, 24 lanes down; lanes of tokens 5..7 also
+        // load the rows 8 tokens back (rh), which the shifts hand to the
+        // lanes of tokens 0..2.  The taps of this thread's 8 columns are the
+        // same for both pieces; the state rows of the slice are tokens -3..-1.
+        u32x4 rh[2];
         f32x4 wcol[8];
         const uint16_t* vst = nullptr;
         if constexpr (CONV) {
@@ -590,18 +633,20 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         _Pragma("unroll") for (int m_ = 0; m_ < 2; ++m_) {                                       \
             const int pc_ = tid + 256 * m_;                                                      \
             const int64_t tk_ = (int64_t)(chunk0 + (cl_)) * kChunk + (pc_ >> 3);                 \
+            rv[m_] = *reinterpret_cast<const u32x4*>(vslice + (tk_ < T ? tk_ : 0) * vstride +     \
+                                                     (pc_ & 7) * 8);                             \
             if constexpr (CONV) {                                                                \
-                _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                               \
-                    const int64_t t_ = tk_ - 3 + j_;                                             \
+                /* token 8 back, for lanes of tokens 5..7: >= -3, and only the */                \
+                /* first piece of a sequence reaches before it; a clamped */                     \
+                /* address where the value is unused, zeroed at use */                           \
+                if ((pc_ >> 3) % 8 >= 5) {                                                       \
+                    const int64_t t_ = tk_ - 8;                                                  \
                     const uint16_t* src_ =                                                       \
                         t_ >= 0 ? vslice + (t_ < T ? t_ : T - 1) * vstride + (pc_ & 7) * 8       \
                         : vst   ? vst + (3 + t_) * vstride + (pc_ & 7) * 8                       \
                                 : vslice + (pc_ & 7) * 8;                                        \
-                    rv4[m_][j_] = *reinterpret_cast<const u32x4*>(src_);                         \
+                    rh[m_] = *reinterpret_cast<const u32x4*>(src_);                              \
                 }                                                                                \
-            } else {                                                                             \
-                rv[m_] = *reinterpret_cast<const u32x4*>(vslice + (tk_ < T ? tk_ : 0) * vstride + \
-                                                         (pc_ & 7) * 8);                         \
             }                                                                                    \
         }                                                                                        \
     } while (0)
@@ -619,11 +664,10 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             for (int m = 0; m < 9; ++m) rs[tid + 256 * m] = rb[m];
             if (tid < 32) rs[(Rec16::G - Rec16::KB) / 16 + tid] = rg;
             signal(&sync_s[2], lane);
-            // Kt, Qt (pieces 0..2047) and V; tokens past the end of the
-            // sequence have zero V
-            wait_for(&sync_s[1], 4u * i, &sync_s[4]);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) kq_s[tid + 256 * m] = ra[m];
+            // V of the chunk, filtered before the wait below so that the
+            // filter does not hold up the scan waves; tokens past the end of
+            // the sequence have zero V
+            u32x4 vx[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int pc = tid + 256 * m, tk = pc >> 3;
@@ -632,27 +676,52 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 u32x4 x = rv[m];
                 if constexpr (CONV) {
                     // silu(sum_j w_j v_{t-3+j}) per column, taps before the
-                    // sequence from the state or zero
+                    // sequence from the state or zero.  xj[j]: token t - 3 + j,
+                    // from lane L - 8 (3 - j) of the own rows, or, across the
+                    // piece's start, of the back rows
+                    const int u = lane >> 3;
+                    const bool zero_back = tkg - 8 < 0 && vst == nullptr;
+                    u32x4 back = rh[m];
+                    if (zero_back) back = u32x4{0u, 0u, 0u, 0u};
+                    u32x4 xj[4];
+                    xj[3] = x;
+#pragma unroll
+                    for (int d = 1; d <= 3; ++d) {
+                        const int from = ((lane - 8 * d) & 63) << 2;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            xj[3 - d][e] = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                                from, (int)(u + d >= 8 ? back[e] : x[e]));
+                    }
                     float y[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         float acc = 0.f;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const bool live = tkg - 3 + j >= 0 || vst != nullptr;
-                            const uint32_t wd = rv4[m][j][e >> 1];
+                            const uint32_t wd = xj[j][e >> 1];
                             const float xv =
                                 __builtin_bit_cast(float, (e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-                            acc += live ? wcol[e][j] * xv : 0.f;
+                            acc += wcol[e][j] * xv;
                         }
                         y[e] = acc * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * acc));
                     }
                     x = u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]),
                               pack2(y[6], y[7])};
                 }
+                vx[m] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+            }
+            // Kt, Qt (pieces 0..2047) and V, once the scan waves are done
+            // with the previous ones
+            wait_for(&sync_s[1], 4u * i, &sync_s[4]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) kq_s[tid + 256 * m] = ra[m];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int pc = tid + 256 * m, tk = pc >> 3;
                 uint2* d2 = reinterpret_cast<uint2*>(&v_s[tk * VP + (pc & 7) * 8]);
-                d2[0] = ok ? uint2{x[0], x[1]} : uint2{0u, 0u};
-                d2[1] = ok ? uint2{x[2], x[3]} : uint2{0u, 0u};
+                d2[0] = uint2{vx[m][0], vx[m][1]};
+                d2[1] = uint2{vx[m][2], vx[m][3]};
             }
             signal(&sync_s[0], lane);
             if (i + 1 < nchunks) {

@@ -26,6 +26,7 @@ constexpr int kD = 128;     // head dimension (d_k = d_v)
 constexpr int kChunk = 64;  // tokens per chunk
 constexpr int kSub = 16;    // rows per sub-block of a chunk
 constexpr float kNormEps = 1e-6f;
+constexpr float kLog2e = 1.4426950408889634f;  // exp(x) = exp2(x log2 e)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

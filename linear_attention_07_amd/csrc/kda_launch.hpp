@@ -8,10 +8,23 @@
 
 namespace kda {
 
+// The decode step's short convolution (bf16 I/O only): taps [H][128][4] fp32
+// (tap 3 = the current token) and the conv state [3 (q, k, v)][B][3][H][128]
+// bf16 (the 3 previous raw tokens, oldest first), advanced in place.
+struct DecodeConv {
+    const float* wq = nullptr;
+    const float* wk = nullptr;
+    const float* wv = nullptr;
+    uint16_t* state = nullptr;
+    int B = 0;
+    int H = 0;
+};
+
+// conv == NULL: q, k, v enter the attention as given
 template <bool F32>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float scale, float* S, void* out,
-                         int B, int H, hipStream_t stream);
+                         int B, int H, const DecodeConv* conv, hipStream_t stream);
 
 // two-kernel chunked prefill for fp32 q/k/v/o, fp32 arithmetic throughout.
 // prep writes one record (W, Q', Kb^T, T, MT, gamma) per (batch, head, chunk)

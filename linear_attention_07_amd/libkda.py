@@ -29,6 +29,7 @@ EXPORTS = (
     "kda_chunk_fwd_f32",
     "kda_chunk_fwd_g16",
     "kda_recurrent_step",
+    "kda_recurrent_step_conv",
     "kda_recurrent_step_f32",
     "kda_status_string",
 )
@@ -62,6 +63,9 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.kda_recurrent_step_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, i, i,
+                                            vp]
+    lib.kda_recurrent_step_conv.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -206,4 +210,36 @@ def recurrent_step(q, k, v, g, beta, scale, S, out=None):
             B, H, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_recurrent_step")
+    return out
+
+
+def recurrent_step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, out=None):
+    """One decode step with the short convolution + SiLU on the raw q, k, v
+    (kda_recurrent_step_conv).  q, k, v: [B, H, 128] bf16 raw values; wq, wk,
+    wv: [H, 128, 4] fp32 taps; conv_state: [3, B, 3, H, 128] bf16 (the layout
+    chunk_fwd_conv returns as conv_out), advanced in place; g, beta, S as
+    recurrent_step.  Returns out [B, H, 128] bf16."""
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q: expected [B, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    B, H, _ = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda tensors must live on a GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.shape, torch.bfloat16, dev)
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _check(t, name, (H, HEAD_DIM, 4), torch.float32, dev)
+    _check(conv_state, "conv_state", (3, B, 3, H, HEAD_DIM), torch.bfloat16, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _check(out, "out", q.shape, torch.bfloat16, dev)
+    st = load().kda_recurrent_step_conv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(conv_state), _ptr(g),
+        _ptr(beta), float(scale), _ptr(S), _ptr(out), B, H, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_step_conv")
     return out

@@ -146,3 +146,26 @@ def conv_inputs(B, T, H, seed=0, with_state=True, h0_std=0.1, device="cuda"):
         inp["conv_in"] = torch.randn((3, B, 3, H, HEAD_DIM), generator=gen,
                                      device=dev).to(torch.bfloat16)
     return inp
+
+
+def decode_conv_inputs(B, H, seed=0, step=0, device="cuda"):
+    """One decode token before its short convolution: raw q, k, v [B, H, 128]
+    bf16 ~ N(0, 1); g, beta, scale as decode_step_inputs."""
+    inp = decode_step_inputs(B, H, torch.bfloat16, seed, step, device=device)
+    dev = torch.device(device)
+    gen = _gen(dev, 7_919 * (int(seed) + 1) + 104_729 * (int(step) + 1) + 29)
+    for name in ("q", "k", "v"):
+        inp[name] = torch.randn((B, H, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+    return inp
+
+
+def conv_params(B, H, seed=0, device="cuda"):
+    """Taps wq, wk, wv [H, 128, 4] fp32 ~ U(-0.5, 0.5) and a conv state
+    [3, B, 3, H, 128] bf16 ~ N(0, 1)."""
+    dev = torch.device(device)
+    gen = _gen(dev, 7_919 * (int(seed) + 1) + 31)
+    out = {name: torch.rand((H, HEAD_DIM, 4), generator=gen, device=dev) - 0.5
+           for name in ("wq", "wk", "wv")}
+    out["conv_state"] = torch.randn((3, B, 3, H, HEAD_DIM), generator=gen,
+                                    device=dev).to(torch.bfloat16)
+    return out

@@ -149,12 +149,24 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
-def short_conv_silu(x, w, state=None):
+def round_bf16(x):
+    """x rounded to fp32 and then to bf16, each to nearest with ties to even,
+    returned as fp64: the bf16 value an fp32 computation of x stores (finite
+    x only)."""
+    bits = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    r = (bits + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32).astype(np.float64)
+
+
+def short_conv_silu(x, w, state=None, round_out=False):
     """x ``[B, T, H, D]`` raw values; w ``[H, D, 4]`` taps, tap j weighting
     the token j - 3 steps from the current one (tap 3 = the current token);
     state ``[B, 3, H, D]`` the raw tokens before x (oldest first) or None for
     zeros.  Returns (y ``[B, T, H, D]`` = silu(sum_j w_j x_{t-3+j}), the new
-    state: the last 3 raw tokens of state followed by x)."""
+    state: the last 3 raw tokens of state followed by x).  round_out: y is
+    rounded to bf16 (round_bf16), the type in which a bf16 attention takes
+    its q, k and v."""
     x, w = _f64(x), _f64(w)
     B, T, H, D = x.shape
     assert w.shape == (H, D, CONV_TAPS)
@@ -164,17 +176,37 @@ def short_conv_silu(x, w, state=None):
     pre = np.zeros((B, T, H, D))
     for j in range(CONV_TAPS):
         pre += w[None, None, :, :, j] * full[:, j:j + T]
-    return silu(pre), np.ascontiguousarray(full[:, T:])
+    y = silu(pre)
+    return (round_bf16(y) if round_out else y), np.ascontiguousarray(full[:, T:])
 
 
 def forward_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_state=None, eps=1e-6,
-                 threads=None):
+                 threads=None, round_bf16_inputs=False):
     """The attention on the short-convolved q, k, v.  conv_state is None or a
-    triple of ``[B, 3, H, D]`` states for q, k, v.  Returns (o, hT, the three
-    new conv states)."""
+    triple of ``[B, 3, H, D]`` states for q, k, v.  round_bf16_inputs: the
+    filtered q, k, v are rounded to bf16 before the attention.  Returns (o,
+    hT, the three new conv states)."""
     cs = (None, None, None) if conv_state is None else conv_state
-    qc, sq = short_conv_silu(q, wq, cs[0])
-    kc, sk = short_conv_silu(k, wk, cs[1])
-    vc, sv = short_conv_silu(v, wv, cs[2])
+    r = round_bf16_inputs
+    qc, sq = short_conv_silu(q, wq, cs[0], r)
+    kc, sk = short_conv_silu(k, wk, cs[1], r)
+    vc, sv = short_conv_silu(v, wv, cs[2], r)
     o, hT = forward(qc, kc, vc, g, beta, scale, h0, eps, threads)
     return o, hT, (sq, sk, sv)
+
+
+def step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, eps=1e-6, threads=None,
+              round_bf16_inputs=False):
+    """One decode token of the attention on the short-convolved q, k, v: the
+    filter of short_conv_silu applied to the single new token ``[B, H, D]``
+    with the carried conv states (a triple of ``[B, 3, H, D]``: the raw tokens
+    before it, oldest first), then one step of the recurrence.
+    round_bf16_inputs as forward_conv.  Returns (o, new S, the three new conv
+    states)."""
+    ys, states = [], []
+    for x, w, st in ((q, wq, conv_state[0]), (k, wk, conv_state[1]), (v, wv, conv_state[2])):
+        y, ns = short_conv_silu(_f64(x)[:, None], w, st, round_bf16_inputs)
+        ys.append(y[:, 0])
+        states.append(ns)
+    o, S_new = step(ys[0], ys[1], ys[2], g, beta, scale, S, eps, threads)
+    return o, S_new, tuple(states)

@@ -139,6 +139,31 @@ def test_step_invalid_arguments(lib, fn):
     assert step(lib, fn, H=0) == libkda.KDA_OK
 
 
+def step_conv(lib, q=P[0], k=P[1], v=P[2], wq=P[8], wk=P[9], wv=P[10], cs=P[11], g=P[3],
+              beta=P[4], scale=1.0, S=P[6], out=P[5], B=1, H=1):
+    return lib.kda_recurrent_step_conv(q, k, v, wq, wk, wv, cs, g, beta, scale, S, out, B, H,
+                                       None)
+
+
+def test_step_conv_invalid_arguments(lib):
+    INV = libkda.KDA_ERR_INVALID_ARG
+    assert step_conv(lib, B=-1) == INV
+    assert step_conv(lib, scale=math.nan) == INV
+    for name in ("q", "k", "v", "wq", "wk", "wv", "cs", "g", "beta", "S", "out"):
+        assert step_conv(lib, **{name: NULL}) == INV, name
+    for name in ("wq", "wk", "wv", "cs"):
+        assert step_conv(lib, **{name: ctypes.c_void_p(A * 12 + 8)}) == INV, name
+    # the conv state over an input, a tap, the attention state or out
+    assert step_conv(lib, cs=ctypes.c_void_p(A * 1 + 128)) == INV
+    assert step_conv(lib, cs=ctypes.c_void_p(A * 9 + 16)) == INV
+    assert step_conv(lib, cs=ctypes.c_void_p(A * 7 + 1024)) == INV
+    assert step_conv(lib, cs=ctypes.c_void_p(A * 6 - 256)) == INV
+    # out over a tap
+    assert step_conv(lib, out=ctypes.c_void_p(A * 10 + 256)) == INV
+    assert step_conv(lib, B=0) == libkda.KDA_OK
+    assert step_conv(lib, H=0) == libkda.KDA_OK
+
+
 def test_binding_rejects_bad_tensors():
     import torch
     q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
@@ -152,6 +177,11 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         libkda.recurrent_step(q[0], q[0], q[0], q[0].float(), torch.zeros(4, 1),
                               1.0, torch.zeros(4, 1, 128, 128))
+    with pytest.raises(ValueError):
+        libkda.recurrent_step_conv(q[0], q[0], q[0], w, w, w,
+                                   torch.zeros(3, 4, 3, 1, 128, dtype=torch.bfloat16),
+                                   q[0].float(), torch.zeros(4, 1), 1.0,
+                                   torch.zeros(4, 1, 128, 128))
 
 
 def test_oracle_is_not_reachable_from_the_product():

@@ -1,10 +1,14 @@
-"""GPU parity of kda_chunk_fwd_conv (the 4-tap short convolution + SiLU in
-front of the attention, fused into the prefill's loads) against the fp64
-oracle, through the C-ABI; plus its state hand-over and edge cases.
+"""GPU parity of kda_chunk_fwd_conv and kda_recurrent_step_conv (the 4-tap
+short convolution + SiLU in front of the attention, fused into the prefill's
+and the decode step's loads) against the fp64 oracle, through the C-ABI; plus
+the conv state hand-over from prefill to decode, and edge cases.
 
-The library rounds the filtered q, k, v to bf16 before the attention; the
-oracle keeps them in fp64.  That rounding (relative 2^-9 per entry) sits well
-inside the bf16 tolerance the other prefill tests use.
+The library rounds the filtered q, k, v to bf16 before the attention (its
+documented input type); the oracle does the same rounding (round_bf16_inputs),
+so the comparison measures the kernels, as with plain bf16 inputs.  Where the
+fp32 filter of the library and the fp64 filter of the oracle fall on either
+side of a bf16 rounding boundary the two inputs differ by one bf16 ulp, on a
+few entries in 10^4.
 """
 import os
 
@@ -37,7 +41,8 @@ def oracle_conv(inp):
     return oracle.forward_conv(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]),
                                host64(inp["wq"]), host64(inp["wk"]), host64(inp["wv"]),
                                host64(inp["g"]), host64(inp["beta"]), inp["scale"],
-                               None if h0 is None else host64(h0), cs, threads=oracle_threads())
+                               None if h0 is None else host64(h0), cs, threads=oracle_threads(),
+                               round_bf16_inputs=True)
 
 
 def sub(inp, t0, t1):
@@ -149,8 +154,86 @@ def test_conv_filtered_values_match_oracle_closely():
     inp["conv_in"][1] = inp["conv_in"][0]
     inp["beta"] = torch.ones_like(inp["beta"])
     out, _, _ = run(inp)
-    vf, _ = oracle.short_conv_silu(host64(inp["v"]), host64(inp["wv"]), host64(inp["conv_in"][2]))
+    vf, _ = oracle.short_conv_silu(host64(inp["v"]), host64(inp["wv"]), host64(inp["conv_in"][2]),
+                                   round_out=True)
     want = inp["scale"] * vf
     err = np.abs(host64(out) - want).max() / np.abs(want).max()
     say(f"conv recall: {err:.2e}")
     assert err <= TOL_BF16
+
+
+def decode_conv_oracle(x, p, S):
+    cs = tuple(host64(p["conv_state"][i]) for i in range(3))
+    return oracle.step_conv(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(p["wq"]),
+                            host64(p["wk"]), host64(p["wv"]), cs, host64(x["g"]),
+                            host64(x["beta"]), x["scale"], S, threads=oracle_threads(),
+                            round_bf16_inputs=True)
+
+
+@pytest.mark.parametrize("B,H", [(3, 5), (2, 8)])
+def test_decode_conv_against_oracle(B, H):
+    """Four decode steps with fresh raw tokens, the conv state and the
+    attention state carried on the device; B * H = 15 leaves the last
+    workgroup half empty."""
+    p = synth.conv_params(B, H, seed=600 + B, device=DEV)
+    S = synth.decode_state(B, H, seed=601, h0_std=0.1, device=DEV)
+    S_ref = host64(S)
+    for step in range(4):
+        x = synth.decode_conv_inputs(B, H, seed=602, step=step, device=DEV)
+        o_ref, S_ref, cs_ref = decode_conv_oracle(x, p, S_ref)
+        out = libkda.recurrent_step_conv(x["q"], x["k"], x["v"], p["wq"], p["wk"], p["wv"],
+                                         p["conv_state"], x["g"], x["beta"], x["scale"], S)
+        torch.cuda.synchronize()
+        eo = rel_out(host64(out)[:, None], o_ref[:, None])
+        say(f"decode conv B={B} H={H} step {step}: out err {eo:.2e}")
+        assert eo <= TOL_BF16
+        for i in range(3):   # raw tokens: exact
+            assert np.array_equal(host64(p["conv_state"][i]), cs_ref[i]), (step, i)
+    es = rel_state(host64(S), S_ref)
+    say(f"  state err {es:.2e}")
+    assert es <= TOL_BF16
+
+
+def test_prefill_then_decode_conv():
+    """A prefill over T tokens followed by decode steps from its attention
+    and conv states equals one prefill over all the tokens."""
+    B, T, H, n = 2, 130, 3, 5
+    inp = synth.conv_inputs(B, T + n, H, seed=610, with_state=True, device=DEV)
+    out_all, h_all, c_all = run(inp)
+    out_a, S, cs = run(sub(inp, 0, T))
+    outs = []
+    for t in range(T, T + n):
+        outs.append(libkda.recurrent_step_conv(
+            inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(), inp["v"][:, t].contiguous(),
+            inp["wq"], inp["wk"], inp["wv"], cs, inp["g"][:, t].contiguous(),
+            inp["beta"][:, t].contiguous(), inp["scale"], S))
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, dim=1)
+    assert torch.equal(cs, c_all)
+    eo = rel_out(host64(o_dec), host64(out_all[:, T:]))
+    es = rel_state(host64(S), host64(h_all))
+    say(f"prefill {T} + decode {n}: out {eo:.2e} state {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_decode_conv_b256_all_heads():
+    """The batched decode shape (B = 256, H = 96) with the convolution: two
+    steps, every output and every state checked."""
+    B, H = 256, 96
+    p = synth.conv_params(B, H, seed=620, device=DEV)
+    S = synth.decode_state(B, H, seed=621, h0_std=0.1, device=DEV)
+    S_ref = host64(S)
+    for step in range(2):
+        x = synth.decode_conv_inputs(B, H, seed=622, step=step, device=DEV)
+        o_ref, S_ref, cs_ref = decode_conv_oracle(x, p, S_ref)
+        out = libkda.recurrent_step_conv(x["q"], x["k"], x["v"], p["wq"], p["wk"], p["wv"],
+                                         p["conv_state"], x["g"], x["beta"], x["scale"], S)
+        torch.cuda.synchronize()
+        eo = rel_out(host64(out)[:, None], o_ref[:, None])
+        say(f"decode conv b256 step {step}: out err {eo:.2e}")
+        assert eo <= TOL_BF16
+        for i in range(3):
+            assert np.array_equal(host64(p["conv_state"][i]), cs_ref[i]), (step, i)
+    es = rel_state(host64(S), S_ref)
+    say(f"  state err {es:.2e}")
+    assert es <= TOL_BF16

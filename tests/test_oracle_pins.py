@@ -315,3 +315,55 @@ def test_short_conv_state_and_split():
     y, _ = oracle.short_conv_silu(np.zeros((B, 1, H, D)), w, s0)
     pre = w[None, :, :, 0] * s0[:, 0] + w[None, :, :, 1] * s0[:, 1] + w[None, :, :, 2] * s0[:, 2]
     np.testing.assert_allclose(y[:, 0], pre / (1.0 + np.exp(-pre)), rtol=1e-14, atol=1e-15)
+
+
+def test_decode_conv_steps_match_forward_conv():
+    """Decoding token by token with the carried conv state and attention
+    state reproduces the prefill over the same tokens: step_conv is the
+    filter of one new token plus one step, and both agree with forward_conv
+    (whose filter and recurrence are pinned above) at every token."""
+    rng = np.random.default_rng(11)
+    B, T, H, D = 2, 6, 3, 8
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    wq, wk, wv = (rng.standard_normal((H, D, 4)) for _ in range(3))
+    g = -5.0 / (1.0 + np.exp(-(rng.standard_normal((B, T, H, D)) - 1.0)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    S0 = 0.1 * rng.standard_normal((B, H, D, D))
+    cs0 = tuple(rng.standard_normal((B, 3, H, D)) for _ in range(3))
+    o, hT, cs_end = oracle.forward_conv(q, k, v, wq, wk, wv, g, beta, 0.7, S0, cs0, threads=1)
+    S, cs = S0.copy(), cs0
+    for t in range(T):
+        ot, S, cs = oracle.step_conv(q[:, t], k[:, t], v[:, t], wq, wk, wv, cs, g[:, t],
+                                     beta[:, t], 0.7, S, threads=1)
+        np.testing.assert_allclose(ot, o[:, t], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, hT, rtol=1e-12, atol=1e-13)
+    for a, b in zip(cs, cs_end):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_round_bf16_matches_torch_conversion():
+    """round_bf16 equals torch's fp32 -> bfloat16 conversion (round to
+    nearest, ties to even) on random values, on exact ties in both
+    directions, and below the fp32 -> bf16 rounding of fp64 inputs."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -2.5, 3.0e38, 1e-40]])
+    # ties: bf16 value plus half an ulp, with an even and an odd last bit
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                     -(1.0 + 3 * 2.0 ** -8)])
+    x = np.concatenate([x, ties])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(x), want)
+    np.testing.assert_array_equal(oracle.round_bf16(ties), [1.0, 1.0 + 2.0 ** -6, -1.0,
+                                                           -(1.0 + 2.0 ** -6)])
+
+
+def test_short_conv_rounded_output_is_the_bf16_of_the_exact_output():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, 9, 2, 4))
+    w = rng.standard_normal((2, 4, 4))
+    y, _ = oracle.short_conv_silu(x, w)
+    yr, _ = oracle.short_conv_silu(x, w, round_out=True)
+    np.testing.assert_array_equal(yr, oracle.round_bf16(y))
+    assert np.abs(yr - y).max() <= 2.0 ** -8 * np.abs(y).max()  # half an ulp of 8 bits
