@@ -6,9 +6,9 @@ A step is one kda_chunk_fwd over the 64K-token, 96-head prefill batch
 random initial state) with every input already resident in HBM.  The value is
 prefill Mtok/s (B*T tokens per step, all 96 heads).  The same run also times
 the same prefill with g in bf16 (kda_chunk_fwd_g16) and with the short
-convolution in front (kda_chunk_fwd_conv), the batched decode step (B=256,
-H=96, fp32 state streamed in place; also with the short convolution,
-kda_recurrent_step_conv) and reports its state bandwidth, and times the fp64
+convolution in front and the output gate behind (kda_chunk_fwd_conv), the
+batched decode step (B=256, H=96, fp32 state streamed in place; also with the
+short convolution and the gate, kda_recurrent_step_conv) and reports its state bandwidth, and times the fp64
 CPU oracle on a bounded sample of the prefill workload as a baseline.
 
 Roofline (per call of the timed op, algorithmic bytes only):
@@ -42,6 +42,8 @@ DECODE_BYTES_PER_SEQ_HEAD = 2 * STATE_BYTES + 3 * 256 + 512 + 4 + 256
 # (3 x [H, 128, 4] fp32) are read once per call
 CONV_STATE_BYTES = 3 * 3 * 128 * 2
 CONV_TAP_BYTES_PER_HEAD = 3 * 128 * 4 * 4
+# the output gate's bf16 logits, one per output value
+GATE_BYTES_PER_TOKEN_HEAD = 128 * 2
 
 
 def parse():
@@ -195,17 +197,20 @@ def main():
     cp = synth.conv_params(w.B, w.H, seed=w.seed, device=dev)
     cout = torch.empty_like(cp["conv_state"])
 
+    zg = synth.gate_logits(inp["v"].shape, seed=w.seed, device=dev)
+
     def prefill_conv():
         libkda.chunk_fwd_conv(inp["q"], inp["k"], inp["v"], cp["wq"], cp["wk"], cp["wv"],
                               inp["g"], inp["beta"], inp["scale"], inp["h0"],
-                              conv_in=cp["conv_state"], conv_out=cout, out=out, hT=hT)
+                              conv_in=cp["conv_state"], conv_out=cout, out=out, hT=hT, gate=zg)
 
     cms, cms_med, cms_min = time_op(torch, prefill_conv, args.steps, args.warmup)
-    conv_bytes = pre_bytes + w.B * w.H * 2 * CONV_STATE_BYTES + w.H * CONV_TAP_BYTES_PER_HEAD
+    conv_bytes = pre_bytes + token_heads * GATE_BYTES_PER_TOKEN_HEAD + \
+        w.B * w.H * 2 * CONV_STATE_BYTES + w.H * CONV_TAP_BYTES_PER_HEAD
     conv_gbps = conv_bytes / (cms / 1e3) / 1e9
-    print(f"# prefill, short conv: {cms:.3f} ms/step, {tokens / (cms / 1e3) / 1e6:.2f} Mtok/s, "
+    print(f"# prefill, short conv + gate: {cms:.3f} ms/step, {tokens / (cms / 1e3) / 1e6:.2f} Mtok/s, "
           f"{conv_gbps:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
-    del cp, cout
+    del cp, cout, zg
 
     # ---- decode -------------------------------------------------------------
     wd = synth.WORKLOADS["decode_b256"]
@@ -233,21 +238,22 @@ def main():
     dcp = synth.conv_params(wd.B, wd.H, seed=wd.seed, device=dev)
     xcs = [synth.decode_conv_inputs(wd.B, wd.H, seed=wd.seed, step=t, device=dev)
            for t in range(4)]
+    zds = [synth.gate_logits((wd.B, wd.H, 128), seed=wd.seed + t, device=dev) for t in range(4)]
 
     def decode_conv():
-        x = xcs[it[0] & 3]
+        x, z = xcs[it[0] & 3], zds[it[0] & 3]
         it[0] += 1
         libkda.recurrent_step_conv(x["q"], x["k"], x["v"], dcp["wq"], dcp["wk"], dcp["wv"],
                                    dcp["conv_state"], x["g"], x["beta"], x["scale"], S,
-                                   out=dout)
+                                   out=dout, gate=z)
 
     cdms, cdms_med, cdms_min = time_op(torch, decode_conv, dsteps, args.warmup)
-    dconv_bytes = nbh * (DECODE_BYTES_PER_SEQ_HEAD + 2 * CONV_STATE_BYTES) + \
-        wd.H * CONV_TAP_BYTES_PER_HEAD
+    dconv_bytes = nbh * (DECODE_BYTES_PER_SEQ_HEAD + 2 * CONV_STATE_BYTES +
+                         GATE_BYTES_PER_TOKEN_HEAD) + wd.H * CONV_TAP_BYTES_PER_HEAD
     dconv_gbps = dconv_bytes / (cdms / 1e3) / 1e9
-    print(f"# decode, short conv: {cdms:.3f} ms/step, total {dconv_gbps:.0f} GB/s",
+    print(f"# decode, short conv + gate: {cdms:.3f} ms/step, total {dconv_gbps:.0f} GB/s",
           file=sys.stderr, flush=True)
-    del dcp, xcs
+    del dcp, xcs, zds
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -316,8 +322,9 @@ def main():
             },
         },
         "prefill_conv": {
-            "workload": "prefill_64k with the 4-tap short convolution + SiLU on q, k, v "
-                        "(kda_chunk_fwd_conv), conv state in and out",
+            "workload": "prefill_64k as one KDA layer: the 4-tap short convolution + SiLU on "
+                        "q, k, v in front, the sigmoid output gate behind (kda_chunk_fwd_conv), "
+                        "conv state in and out",
             "ms_per_step": round(cms, 4),
             "ms_per_step_median": round(cms_med, 4),
             "ms_per_step_min": round(cms_min, 4),
@@ -332,8 +339,8 @@ def main():
             },
         },
         "decode_conv": {
-            "workload": "decode_b256 with the short convolution (kda_recurrent_step_conv): "
-                        "conv state advanced in place",
+            "workload": "decode_b256 as one KDA layer: short convolution in front, output "
+                        "gate behind (kda_recurrent_step_conv), conv state advanced in place",
             "ms_per_step": round(cdms, 4),
             "ms_per_step_median": round(cdms_med, 4),
             "ms_per_step_min": round(cdms_min, 4),

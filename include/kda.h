@@ -107,7 +107,8 @@ KDA_API kda_status_t kda_chunk_fwd_g16(const uint16_t *q, const uint16_t *k, con
 
 /*
  * kda_chunk_fwd_conv — kda_chunk_fwd with the short convolution and SiLU that
- * the KDA layer puts in front of the attention (the KDA paragraph of the
+ * the KDA layer puts in front of the attention, and optionally its output
+ * gate behind it (the KDA paragraph of the
  * 深入 Kimi-K3 thread; a 4-tap kernel in the config table of the Kimi K3
  * architecture page), fused into the kernels' loads.  Read as depthwise and
  * causal with no bias: for each of q, k and v,
@@ -129,6 +130,15 @@ KDA_API kda_status_t kda_chunk_fwd_g16(const uint16_t *q, const uint16_t *k, con
  *              call.  May equal conv_in (updated in place); otherwise must
  *              not overlap it, the weights or the inputs.
  *
+ *   gate     : NULL, or [B, T, H, 128] bf16 logits z of the output gate
+ *              behind the attention: out = o * sigmoid(z), elementwise, then
+ *              rounded to bf16.  The 深入 Kimi-K3 thread (KDA paragraph) says
+ *              only that K3's KDA output gate is full-rank, and that its
+ *              global layers gate their output with a sigmoid; read here as
+ *              a sigmoid of one logit per output channel (the projection
+ *              that makes z, and any norm, stay outside).  16-byte aligned;
+ *              must not overlap out or conv_out.
+ *
  * g, beta, scale, h0, out, hT and the validation are those of kda_chunk_fwd;
  * out must not overlap the weights or the conv buffers either.  T == 0 copies
  * conv_in (or zeros) to conv_out and h0 (or zeros) to hT.
@@ -137,8 +147,8 @@ KDA_API kda_status_t kda_chunk_fwd_conv(const uint16_t *q, const uint16_t *k, co
                                 const float *wq, const float *wk, const float *wv,
                                 const uint16_t *conv_in, uint16_t *conv_out,
                                 const float *g, const float *beta, float scale,
-                                const float *h0, uint16_t *out, float *hT,
-                                int B, int T, int H, hipStream_t stream);
+                                const float *h0, const uint16_t *gate, uint16_t *out,
+                                float *hT, int B, int T, int H, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_f32 — as kda_chunk_fwd, with fp32 q, k, v and out and fp32
@@ -186,14 +196,18 @@ KDA_API kda_status_t kda_recurrent_step(const uint16_t *q, const uint16_t *k, co
  *                it holds the last 3 raw tokens including this one.  Must not
  *                overlap any other argument.
  *
+ *   gate       : NULL, or [B, H, 128] bf16 logits of the output gate, as in
+ *                kda_chunk_fwd_conv: out = o * sigmoid(gate).
+ *
  * g, beta, scale, S_inout, out and the validation are those of
- * kda_recurrent_step; out must not overlap the taps or the conv state.
+ * kda_recurrent_step; out must not overlap the taps, the conv state or the
+ * gate.
  */
 KDA_API kda_status_t kda_recurrent_step_conv(const uint16_t *q, const uint16_t *k,
                                      const uint16_t *v, const float *wq, const float *wk,
                                      const float *wv, uint16_t *conv_state,
                                      const float *g, const float *beta, float scale,
-                                     float *S_inout, uint16_t *out,
+                                     float *S_inout, const uint16_t *gate, uint16_t *out,
                                      int B, int H, hipStream_t stream);
 
 /* kda_recurrent_step_f32 — as kda_recurrent_step with fp32 q, k, v, out. */

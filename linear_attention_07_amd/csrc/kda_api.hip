@@ -130,6 +130,9 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
                 return KDA_ERR_INVALID_ARG;
         if (overlap(out, io_bytes, conv.state, cbytes) || overlap(out, io_bytes, conv_out, cbytes))
             return KDA_ERR_INVALID_ARG;
+        if (conv.gate && (!aligned(conv.gate, 16) || overlap(out, io_bytes, conv.gate, io_bytes) ||
+                          overlap(conv_out, cbytes, conv.gate, io_bytes)))
+            return KDA_ERR_INVALID_ARG;
         for (const void* p : ins)
             if (overlap(conv_out, cbytes, p, io_bytes)) return KDA_ERR_INVALID_ARG;
     }
@@ -242,6 +245,10 @@ kda_status_t recurrent_step(const void* q, const void* k, const void* v, const f
         if (overlap(cs, cbytes, g, nbh * KDA_HEAD_DIM * 4) || overlap(cs, cbytes, beta, nbh * 4) ||
             overlap(cs, cbytes, S, sbytes) || overlap(cs, cbytes, out, vec))
             return KDA_ERR_INVALID_ARG;
+        if (conv->gate && (!aligned(conv->gate, 16) || overlap(out, vec, conv->gate, vec) ||
+                           overlap(cs, cbytes, conv->gate, vec) ||
+                           overlap(S, sbytes, conv->gate, vec)))
+            return KDA_ERR_INVALID_ARG;
         conv->B = B;
         conv->H = H;
     }
@@ -289,14 +296,16 @@ kda_status_t kda_chunk_fwd_g16(const uint16_t* q, const uint16_t* k, const uint1
 kda_status_t kda_chunk_fwd_conv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* wq, const float* wk, const float* wv,
                                 const uint16_t* conv_in, uint16_t* conv_out, const float* g,
-                                const float* beta, float scale, const float* h0, uint16_t* out,
-                                float* hT, int B, int T, int H, hipStream_t stream) {
+                                const float* beta, float scale, const float* h0,
+                                const uint16_t* gate, uint16_t* out, float* hT, int B, int T,
+                                int H, hipStream_t stream) {
     if (!wq || !wk || !wv) return KDA_ERR_INVALID_ARG;
     kda::ConvArgs conv;
     conv.wq = wq;
     conv.wk = wk;
     conv.wv = wv;
     conv.state = conv_in;
+    conv.gate = gate;
     return chunk_fwd<false>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream, conv,
                             conv_out);
 }
@@ -316,13 +325,14 @@ kda_status_t kda_recurrent_step(const uint16_t* q, const uint16_t* k, const uint
 kda_status_t kda_recurrent_step_conv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const float* wq, const float* wk, const float* wv,
                                      uint16_t* conv_state, const float* g, const float* beta,
-                                     float scale, float* S_inout, uint16_t* out, int B, int H,
-                                     hipStream_t stream) {
+                                     float scale, float* S_inout, const uint16_t* gate,
+                                     uint16_t* out, int B, int H, hipStream_t stream) {
     kda::DecodeConv conv;
     conv.wq = wq;
     conv.wk = wk;
     conv.wv = wv;
     conv.state = conv_state;
+    conv.gate = gate;
     return recurrent_step<false>(q, k, v, g, beta, scale, S_inout, out, B, H, stream, &conv);
 }
 

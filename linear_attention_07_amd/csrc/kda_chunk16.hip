@@ -767,6 +767,36 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 
         const int64_t rstride = (int64_t)H * kD;  // elements between tokens
 
+        // The output gate, off the chain from one state to the next: the
+        // logits of this lane's outputs (token 16 rt + n, columns j0 + 4 gq
+        // ..) are loaded a chunk ahead (zr) and turned into sigmoids (sg)
+        // beside the previous chunk's state-update products.
+        const uint16_t* gate = CONV ? conv.gate : nullptr;
+        const uint16_t* gatec = gate ? gate + ((int64_t)b * T * H + h) * kD + j0 + 4 * gq : nullptr;
+        uint2 zr[4];
+        f32x4 sg[4];
+        auto gate_load = [&](int ci) {  // logits of local chunk ci (clamped rows)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int64_t tk = (int64_t)(chunk0 + ci) * kChunk + 16 * rt + n;
+                zr[rt] = *reinterpret_cast<const uint2*>(gatec + (tk < T ? tk : T - 1) * rstride);
+            }
+        };
+        auto gate_sigmoid = [&]() {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float z[4] = {bf2f((uint16_t)zr[rt].x), bf2f((uint16_t)(zr[rt].x >> 16)),
+                                    bf2f((uint16_t)zr[rt].y), bf2f((uint16_t)(zr[rt].y >> 16))};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sg[rt][e] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * z[e]));
+            }
+        };
+        if (gatec) {
+            gate_load(0);
+            gate_sigmoid();
+            gate_load(1);
+        }
         for (int i = 0; i < nchunks; ++i) {
             const int64_t c0 = (int64_t)(chunk0 + i) * kChunk;
             wait_for(&sync_s[0], 4u * (i + 1), &sync_s[4]);
@@ -875,9 +905,11 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     o = mma(o, bl_[s2], fmh[f]);
                 }
                 const int64_t tk = c0 + 16 * rt + n;
+                f32x4 y = scale * o;
+                if (gatec) y *= sg[rt];  // out = o * sigmoid(z)
                 if (tk < T)
                     *reinterpret_cast<uint2*>(outc + tk * rstride) =
-                        uint2{pack2(scale * o[0], scale * o[1]), pack2(scale * o[2], scale * o[3])};
+                        uint2{pack2(y[0], y[1]), pack2(y[2], y[3])};
             }
             signal(&sync_s[5], lane);  // the output is stored
 #pragma unroll
@@ -889,6 +921,12 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                         for (int s2 = 0; s2 < 2; ++s2)
                             fkb[1][t][s2] = frag(kb_s, 2 * (t + 4) + s2, lane);
                     __builtin_amdgcn_sched_barrier(0);
+                    // the next chunk's gate beside these products; then the
+                    // logits of the one after
+                    if (gatec) {
+                        gate_sigmoid();
+                        gate_load(i + 2);
+                    }
                 }
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4) {

@@ -25,7 +25,8 @@
 // from the conv state, which the step then advances by one token in place.
 // Both waves of a (b, h) read the q / k rows of that state, so it is written
 // only after a workgroup barrier; every wave reaches it (a wave past the end
-// computes on a valid (b, h) and stores nothing).
+// computes on a valid (b, h) and stores nothing).  An optional output gate
+// multiplies o by sigmoid of its logits before the store.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -205,8 +206,22 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     for (int c = 0; c < 4; ++c) u[c] = bt * (vv[c] - p[c] * ik);
     if (CONV && !live) return;
     if (rg == 0) {
+        float gt[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (CONV) {
+            if (conv.gate) {
+                // the output gate: out = o * sigmoid(z)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) out[bh * kD + col + c] = P::to_io(scale * (r[c] * iq + kq * u[c]));
+                for (int c = 0; c < 4; ++c)
+                    gt[c] = __builtin_amdgcn_rcpf(
+                        1.f + __builtin_amdgcn_exp2f(-kLog2e * bf2f(conv.gate[bh * kD + col + c])));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float y = scale * (r[c] * iq + kq * u[c]);
+            if constexpr (CONV) y *= gt[c];
+            out[bh * kD + col + c] = P::to_io(y);
+        }
     }
 #pragma unroll
     for (int m = 0; m < 32; ++m) {

@@ -16,6 +16,7 @@ struct DecodeConv {
     const float* wk = nullptr;
     const float* wv = nullptr;
     uint16_t* state = nullptr;
+    const uint16_t* gate = nullptr;  // [B, H, 128] bf16 logits of the output gate, or NULL
     int B = 0;
     int H = 0;
 };
@@ -49,6 +50,9 @@ struct ConvArgs {
     const float* wk = nullptr;
     const float* wv = nullptr;
     const uint16_t* state = nullptr;
+    // optional output gate behind the attention: out = o * sigmoid(gate),
+    // gate [B, T, H, 128] bf16 logits, or NULL for none
+    const uint16_t* gate = nullptr;
     int B = 0;
 };
 

@@ -56,15 +56,15 @@ def load() -> ctypes.CDLL:
     vp, f, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     chunk_args = [vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, vp]
     step_args = [vp, vp, vp, vp, vp, f, vp, vp, i, i, vp]
-    conv_args = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, vp]
+    conv_args = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, vp]
     for name, args in (("kda_chunk_fwd", chunk_args), ("kda_chunk_fwd_f32", chunk_args),
                        ("kda_chunk_fwd_g16", chunk_args), ("kda_chunk_fwd_conv", conv_args),
                        ("kda_recurrent_step", step_args), ("kda_recurrent_step_f32", step_args)):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.kda_recurrent_step_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, i, i,
-                                            vp]
+    lib.kda_recurrent_step_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, i,
+                                            i, vp]
     lib.kda_recurrent_step_conv.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -138,13 +138,16 @@ def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=T
 
 
 def chunk_fwd_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_in=None,
-                   conv_out=None, out=None, hT=None, final_state=True, final_conv=True):
+                   conv_out=None, out=None, hT=None, final_state=True, final_conv=True,
+                   gate=None):
     """Chunkwise prefill with the 4-tap short convolution + SiLU applied to the
     raw q, k, v first (kda_chunk_fwd_conv).  q, k, v: [B, T, H, 128] bf16 raw
     values; wq, wk, wv: [H, 128, 4] fp32 taps; conv_in / conv_out: optional
     [3, B, 3, H, 128] bf16 (q, k, v; the 3 raw tokens before the first, oldest
-    first); the rest as chunk_fwd with fp32 g.  Returns (out, hT, conv_out);
-    conv_out is None when final_conv is False and no buffer is given."""
+    first); gate: optional [B, T, H, 128] bf16 logits of the output gate (out =
+    o * sigmoid(gate)); the rest as chunk_fwd with fp32 g.  Returns (out, hT,
+    conv_out); conv_out is None when final_conv is False and no buffer is
+    given."""
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
         raise ValueError(f"q: expected [B, T, H, {HEAD_DIM}], got {tuple(q.shape)}")
     B, T, H, _ = q.shape
@@ -163,6 +166,8 @@ def chunk_fwd_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_in=None,
         _check(h0, "h0", sshape, torch.float32, dev)
     if conv_in is not None:
         _check(conv_in, "conv_in", cshape, torch.bfloat16, dev)
+    if gate is not None:
+        _check(gate, "gate", q.shape, torch.bfloat16, dev)
     if out is None:
         out = torch.empty_like(v)
     else:
@@ -177,7 +182,8 @@ def chunk_fwd_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_in=None,
         _check(conv_out, "conv_out", cshape, torch.bfloat16, dev)
     st = load().kda_chunk_fwd_conv(
         _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(conv_in), _ptr(conv_out),
-        _ptr(g), _ptr(beta), float(scale), _ptr(h0), _ptr(out), _ptr(hT), B, T, H, _stream(dev))
+        _ptr(g), _ptr(beta), float(scale), _ptr(h0), _ptr(gate), _ptr(out), _ptr(hT), B, T, H,
+        _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_conv")
     return out, hT, conv_out
@@ -213,12 +219,14 @@ def recurrent_step(q, k, v, g, beta, scale, S, out=None):
     return out
 
 
-def recurrent_step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, out=None):
+def recurrent_step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, out=None,
+                        gate=None):
     """One decode step with the short convolution + SiLU on the raw q, k, v
     (kda_recurrent_step_conv).  q, k, v: [B, H, 128] bf16 raw values; wq, wk,
     wv: [H, 128, 4] fp32 taps; conv_state: [3, B, 3, H, 128] bf16 (the layout
-    chunk_fwd_conv returns as conv_out), advanced in place; g, beta, S as
-    recurrent_step.  Returns out [B, H, 128] bf16."""
+    chunk_fwd_conv returns as conv_out), advanced in place; gate: optional
+    [B, H, 128] bf16 logits of the output gate; g, beta, S as recurrent_step.
+    Returns out [B, H, 128] bf16."""
     if q.dim() != 3 or q.shape[-1] != HEAD_DIM:
         raise ValueError(f"q: expected [B, H, {HEAD_DIM}], got {tuple(q.shape)}")
     B, H, _ = q.shape
@@ -233,13 +241,15 @@ def recurrent_step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, out=
     _check(g, "g", q.shape, torch.float32, dev)
     _check(beta, "beta", (B, H), torch.float32, dev)
     _check(S, "S", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
+    if gate is not None:
+        _check(gate, "gate", q.shape, torch.bfloat16, dev)
     if out is None:
         out = torch.empty_like(v)
     else:
         _check(out, "out", q.shape, torch.bfloat16, dev)
     st = load().kda_recurrent_step_conv(
         _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(conv_state), _ptr(g),
-        _ptr(beta), float(scale), _ptr(S), _ptr(out), B, H, _stream(dev))
+        _ptr(beta), float(scale), _ptr(S), _ptr(gate), _ptr(out), B, H, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_recurrent_step_conv")
     return out

@@ -169,3 +169,11 @@ def conv_params(B, H, seed=0, device="cuda"):
     out["conv_state"] = torch.randn((3, B, 3, H, HEAD_DIM), generator=gen,
                                     device=dev).to(torch.bfloat16)
     return out
+
+
+def gate_logits(shape, seed=0, device="cuda"):
+    """Logits of the output gate ~ N(0, 1), bf16, of the given shape
+    ([B, T, H, 128] for a prefill, [B, H, 128] for a decode step)."""
+    dev = torch.device(device)
+    gen = _gen(dev, 7_919 * (int(seed) + 1) + 43)
+    return torch.randn(tuple(shape), generator=gen, device=dev).to(torch.bfloat16)

@@ -180,33 +180,45 @@ def short_conv_silu(x, w, state=None, round_out=False):
     return (round_bf16(y) if round_out else y), np.ascontiguousarray(full[:, T:])
 
 
+def output_gate(o, z):
+    """The output gate behind the attention: o * sigmoid(z) elementwise, z the
+    gate's logits (one per output channel: the thread's full-rank gate, read
+    as the sigmoid gate it names for the global layers)."""
+    return _f64(o) / (1.0 + np.exp(-_f64(z)))
+
+
 def forward_conv(q, k, v, wq, wk, wv, g, beta, scale, h0=None, conv_state=None, eps=1e-6,
-                 threads=None, round_bf16_inputs=False):
+                 threads=None, round_bf16_inputs=False, gate=None):
     """The attention on the short-convolved q, k, v.  conv_state is None or a
     triple of ``[B, 3, H, D]`` states for q, k, v.  round_bf16_inputs: the
-    filtered q, k, v are rounded to bf16 before the attention.  Returns (o,
-    hT, the three new conv states)."""
+    filtered q, k, v are rounded to bf16 before the attention.  gate: None or
+    the ``[B, T, H, D]`` logits of the output gate.  Returns (o, hT, the three
+    new conv states)."""
     cs = (None, None, None) if conv_state is None else conv_state
     r = round_bf16_inputs
     qc, sq = short_conv_silu(q, wq, cs[0], r)
     kc, sk = short_conv_silu(k, wk, cs[1], r)
     vc, sv = short_conv_silu(v, wv, cs[2], r)
     o, hT = forward(qc, kc, vc, g, beta, scale, h0, eps, threads)
+    if gate is not None:
+        o = output_gate(o, gate)
     return o, hT, (sq, sk, sv)
 
 
 def step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, eps=1e-6, threads=None,
-              round_bf16_inputs=False):
+              round_bf16_inputs=False, gate=None):
     """One decode token of the attention on the short-convolved q, k, v: the
     filter of short_conv_silu applied to the single new token ``[B, H, D]``
     with the carried conv states (a triple of ``[B, 3, H, D]``: the raw tokens
     before it, oldest first), then one step of the recurrence.
-    round_bf16_inputs as forward_conv.  Returns (o, new S, the three new conv
-    states)."""
+    round_bf16_inputs and gate (``[B, H, D]``) as forward_conv.  Returns (o,
+    new S, the three new conv states)."""
     ys, states = [], []
     for x, w, st in ((q, wq, conv_state[0]), (k, wk, conv_state[1]), (v, wv, conv_state[2])):
         y, ns = short_conv_silu(_f64(x)[:, None], w, st, round_bf16_inputs)
         ys.append(y[:, 0])
         states.append(ns)
     o, S_new = step(ys[0], ys[1], ys[2], g, beta, scale, S, eps, threads)
+    if gate is not None:
+        o = output_gate(o, gate)
     return o, S_new, tuple(states)

@@ -91,9 +91,9 @@ def test_chunk_empty_is_a_no_op(lib, fn):
 
 
 def conv(lib, q=P[0], k=P[1], v=P[2], wq=P[8], wk=P[9], wv=P[10], conv_in=NULL, conv_out=NULL,
-         g=P[3], beta=P[4], scale=1.0, h0=NULL, out=P[5], hT=NULL, B=1, T=4, H=1):
-    return lib.kda_chunk_fwd_conv(q, k, v, wq, wk, wv, conv_in, conv_out, g, beta, scale, h0, out,
-                                  hT, B, T, H, None)
+         g=P[3], beta=P[4], scale=1.0, h0=NULL, gate=NULL, out=P[5], hT=NULL, B=1, T=4, H=1):
+    return lib.kda_chunk_fwd_conv(q, k, v, wq, wk, wv, conv_in, conv_out, g, beta, scale, h0, gate,
+                                  out, hT, B, T, H, None)
 
 
 def test_conv_invalid_arguments(lib):
@@ -111,6 +111,10 @@ def test_conv_invalid_arguments(lib):
     assert conv(lib, conv_in=P[11], out=ctypes.c_void_p(A * 12 + 1024)) == INV
     assert conv(lib, conv_out=ctypes.c_void_p(A * 10 + 1024)) == INV
     assert conv(lib, conv_out=ctypes.c_void_p(A * 2 + 512)) == INV
+    # the gate: misaligned, under out, under conv_out
+    assert conv(lib, gate=ctypes.c_void_p(A * 12 + 8)) == INV
+    assert conv(lib, gate=ctypes.c_void_p(A * 6 - 256)) == INV
+    assert conv(lib, conv_out=P[11], gate=ctypes.c_void_p(A * 12 + 256)) == INV
 
 
 def test_conv_empty_is_a_no_op(lib):
@@ -140,9 +144,9 @@ def test_step_invalid_arguments(lib, fn):
 
 
 def step_conv(lib, q=P[0], k=P[1], v=P[2], wq=P[8], wk=P[9], wv=P[10], cs=P[11], g=P[3],
-              beta=P[4], scale=1.0, S=P[6], out=P[5], B=1, H=1):
-    return lib.kda_recurrent_step_conv(q, k, v, wq, wk, wv, cs, g, beta, scale, S, out, B, H,
-                                       None)
+              beta=P[4], scale=1.0, S=P[6], gate=NULL, out=P[5], B=1, H=1):
+    return lib.kda_recurrent_step_conv(q, k, v, wq, wk, wv, cs, g, beta, scale, S, gate, out, B,
+                                       H, None)
 
 
 def test_step_conv_invalid_arguments(lib):
@@ -158,8 +162,11 @@ def test_step_conv_invalid_arguments(lib):
     assert step_conv(lib, cs=ctypes.c_void_p(A * 9 + 16)) == INV
     assert step_conv(lib, cs=ctypes.c_void_p(A * 7 + 1024)) == INV
     assert step_conv(lib, cs=ctypes.c_void_p(A * 6 - 256)) == INV
-    # out over a tap
+    # out over a tap; the gate misaligned or under out / the conv state
     assert step_conv(lib, out=ctypes.c_void_p(A * 10 + 256)) == INV
+    assert step_conv(lib, gate=ctypes.c_void_p(A * 12 + 8)) == INV
+    assert step_conv(lib, gate=ctypes.c_void_p(A * 6 - 128)) == INV
+    assert step_conv(lib, gate=ctypes.c_void_p(A * 12 + 512)) == INV
     assert step_conv(lib, B=0) == libkda.KDA_OK
     assert step_conv(lib, H=0) == libkda.KDA_OK
 

@@ -34,7 +34,7 @@ def run(inp, conv_in="inp", h0="inp", **kw):
     return out, hT, cout
 
 
-def oracle_conv(inp):
+def oracle_conv(inp, gate=None):
     ci = inp["conv_in"]
     cs = None if ci is None else tuple(host64(ci[i]) for i in range(3))
     h0 = inp["h0"]
@@ -42,7 +42,8 @@ def oracle_conv(inp):
                                host64(inp["wq"]), host64(inp["wk"]), host64(inp["wv"]),
                                host64(inp["g"]), host64(inp["beta"]), inp["scale"],
                                None if h0 is None else host64(h0), cs, threads=oracle_threads(),
-                               round_bf16_inputs=True)
+                               round_bf16_inputs=True,
+                               gate=None if gate is None else host64(gate))
 
 
 def sub(inp, t0, t1):
@@ -162,12 +163,12 @@ def test_conv_filtered_values_match_oracle_closely():
     assert err <= TOL_BF16
 
 
-def decode_conv_oracle(x, p, S):
+def decode_conv_oracle(x, p, S, gate=None):
     cs = tuple(host64(p["conv_state"][i]) for i in range(3))
     return oracle.step_conv(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(p["wq"]),
                             host64(p["wk"]), host64(p["wv"]), cs, host64(x["g"]),
                             host64(x["beta"]), x["scale"], S, threads=oracle_threads(),
-                            round_bf16_inputs=True)
+                            round_bf16_inputs=True, gate=None if gate is None else host64(gate))
 
 
 @pytest.mark.parametrize("B,H", [(3, 5), (2, 8)])
@@ -237,3 +238,64 @@ def test_decode_conv_b256_all_heads():
     es = rel_state(host64(S), S_ref)
     say(f"  state err {es:.2e}")
     assert es <= TOL_BF16
+
+
+
+# ---------------------------------------------------------------------------
+# the output gate behind the attention (out = o * sigmoid(z))
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,H", [(2, 1, 3), (2, 130, 3), (1, 1000, 8)])
+def test_gated_conv_against_oracle(B, T, H):
+    inp = synth.conv_inputs(B, T, H, seed=700 + T, with_state=True, device=DEV)
+    z = synth.gate_logits((B, T, H, 128), seed=701 + T, device=DEV)
+    out, hT, cout = run(inp, gate=z)
+    out0, hT0, _ = run(inp)
+    assert torch.equal(hT, hT0)           # the gate touches the output only
+    o_ref, h_ref, _ = oracle_conv(inp, gate=z)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"gated conv B={B} T={T} H={H}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    # logits of 0 halve the ungated output (up to the bf16 rounding of each)
+    half, _, _ = run(inp, gate=torch.zeros_like(z))
+    d = (host64(half) - 0.5 * host64(out0))
+    assert np.abs(d).max() <= 2.0 ** -8 * np.abs(host64(out0)).max()
+
+
+def test_gated_decode_and_prefill_chaining():
+    """Prefill over T tokens and decode steps after it, all gated, against
+    the oracle and against one gated prefill over every token."""
+    B, T, H, n = 2, 130, 3, 4
+    inp = synth.conv_inputs(B, T + n, H, seed=710, with_state=True, device=DEV)
+    z = synth.gate_logits((B, T + n, H, 128), seed=711, device=DEV)
+    out_all, h_all, c_all = run(inp, gate=z)
+    o_ref, h_ref, _ = oracle_conv(inp, gate=z)
+    assert rel_out(host64(out_all), o_ref) <= TOL_BF16
+    _, S, cs = run(sub(inp, 0, T), gate=z[:, :T].contiguous())
+    outs = []
+    for t in range(T, T + n):
+        outs.append(libkda.recurrent_step_conv(
+            inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(), inp["v"][:, t].contiguous(),
+            inp["wq"], inp["wk"], inp["wv"], cs, inp["g"][:, t].contiguous(),
+            inp["beta"][:, t].contiguous(), inp["scale"], S, gate=z[:, t].contiguous()))
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, dim=1)
+    eo = rel_out(host64(o_dec), o_ref[:, T:])
+    es = rel_state(host64(S), h_ref)
+    say(f"gated prefill {T} + decode {n} vs oracle: out {eo:.2e} state {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and torch.equal(cs, c_all)
+
+
+def test_gated_decode_b256():
+    B, H = 256, 96
+    p = synth.conv_params(B, H, seed=720, device=DEV)
+    S = synth.decode_state(B, H, seed=721, h0_std=0.1, device=DEV)
+    S_ref = host64(S)
+    x = synth.decode_conv_inputs(B, H, seed=722, step=0, device=DEV)
+    z = synth.gate_logits((B, H, 128), seed=723, device=DEV)
+    o_ref, S_ref, _ = decode_conv_oracle(x, p, S_ref, gate=z)
+    out = libkda.recurrent_step_conv(x["q"], x["k"], x["v"], p["wq"], p["wk"], p["wv"],
+                                     p["conv_state"], x["g"], x["beta"], x["scale"], S, gate=z)
+    torch.cuda.synchronize()
+    eo, es = rel_out(host64(out)[:, None], o_ref[:, None]), rel_state(host64(S), S_ref)
+    say(f"gated decode b256: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16

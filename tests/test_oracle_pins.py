@@ -367,3 +367,43 @@ def test_short_conv_rounded_output_is_the_bf16_of_the_exact_output():
     yr, _ = oracle.short_conv_silu(x, w, round_out=True)
     np.testing.assert_array_equal(yr, oracle.round_bf16(y))
     assert np.abs(yr - y).max() <= 2.0 ** -8 * np.abs(y).max()  # half an ulp of 8 bits
+
+
+def test_output_gate_values():
+    """The gate is the logistic function of its logit: at 0 it halves the
+    output exactly, at a large logit it passes it (1 / (1 + e^-40) rounds to
+    1 in fp64), and at +-1, 2, -3 it takes the logistic values written out
+    (the SiLU pin's values divided by x)."""
+    o = np.array([[2.0, -3.0, 5.0, 7.0, 1.0, -1.0]])
+    z = np.array([[0.0, 0.0, 40.0, 1.0, -1.0, 2.0]])
+    want = np.array([[1.0, -1.5, 5.0, 7.0 * 0.7310585786300049, 0.2689414213699951,
+                      -0.8807970779778823]])
+    np.testing.assert_allclose(oracle.output_gate(o, z), want, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(oracle.output_gate(np.array([3.0]), np.array([-3.0])),
+                               [3.0 * 0.04742587317756678], rtol=1e-14)
+
+
+def test_gated_conv_forward_and_steps():
+    """forward_conv with a gate equals the ungated output times the gate's
+    logistic; with zero logits exactly half; and step_conv with the same
+    gate per token reproduces it."""
+    rng = np.random.default_rng(13)
+    B, T, H, D = 1, 5, 2, 8
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    wq, wk, wv = (rng.standard_normal((H, D, 4)) for _ in range(3))
+    g = -5.0 / (1.0 + np.exp(-(rng.standard_normal((B, T, H, D)) - 1.0)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    z = rng.standard_normal((B, T, H, D))
+    o, hT, _ = oracle.forward_conv(q, k, v, wq, wk, wv, g, beta, 0.7, threads=1)
+    og, hg, _ = oracle.forward_conv(q, k, v, wq, wk, wv, g, beta, 0.7, threads=1, gate=z)
+    oh, _, _ = oracle.forward_conv(q, k, v, wq, wk, wv, g, beta, 0.7, threads=1,
+                                   gate=np.zeros_like(z))
+    np.testing.assert_array_equal(hg, hT)
+    np.testing.assert_array_equal(oh, 0.5 * o)
+    np.testing.assert_allclose(og, o / (1.0 + np.exp(-z)), rtol=1e-15)
+    S = np.zeros((B, H, D, D))
+    cs = tuple(np.zeros((B, 3, H, D)) for _ in range(3))
+    for t in range(T):
+        ot, S, cs = oracle.step_conv(q[:, t], k[:, t], v[:, t], wq, wk, wv, cs, g[:, t],
+                                     beta[:, t], 0.7, S, threads=1, gate=z[:, t])
+        np.testing.assert_allclose(ot, og[:, t], rtol=1e-12, atol=1e-13)
