@@ -62,16 +62,20 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the measured forward kernels and their launches are built from
+MEASURED_SOURCES = ("kda_api.hip", "kda_bf16.hpp", "kda_chunk16.hip", "kda_common.hpp",
+                    "kda_decode.hip", "kda_launch.hpp")
+
+
 def kernel_sources_digest():
-    """sha256 over the HIP sources: a traffic figure measured on other
-    sources is not reported."""
+    """sha256 over the sources of the measured kernels: a traffic figure
+    measured on other sources is not reported."""
     import hashlib
     d = hashlib.sha256()
     src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_attention_07_amd", "csrc")
-    for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(src, name), "rb") as f:
-                d.update(name.encode() + b"\0" + f.read())
+    for name in MEASURED_SOURCES:
+        with open(os.path.join(src, name), "rb") as f:
+            d.update(name.encode() + b"\0" + f.read())
     return d.hexdigest()
 
 
