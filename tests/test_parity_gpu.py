@@ -135,6 +135,19 @@ def test_chunk_batched_heads_segments(workspace_mb, monkeypatch):
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+def test_chunk_more_scan_workgroups_than_cus():
+    """B=3, H=96: 576 scan workgroups (one per head and 64-column slice), more
+    than the chip's 256 CUs hold at once, so they run in rounds; 3 x 96 x 4
+    prep workgroups per chunk row.  Every head checked against the oracle."""
+    B, T, H = 3, 200, 96
+    inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=78, h0_std=0.1, device=DEV)
+    out, hT = _run_chunk(inp)
+    o_ref, h_ref = oracle_prefill(inp)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"B={B} H={H} T={T}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 @pytest.mark.parametrize("B,T,H", [(2, 1, 3), (2, 65, 3), (2, 1000, 3), (2, 700, 8)])
 def test_chunk_g16_against_oracle(B, T, H):
     """g in bf16 (kda_chunk_fwd_g16), nonzero initial state: the oracle reads
