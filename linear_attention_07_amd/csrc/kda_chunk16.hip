@@ -23,7 +23,7 @@
 // prep (kda_prep16_kernel): one workgroup per (batch, head, chunk), all chunks
 //   in parallel.  It normalises q and k, forms the decay sums and factor
 //   tables, the KK / QK blocks on MFMA, the inverse of I + A in fp32, and
-//   writes the chunk's record: Kt, Qt, Kb^T (bf16), T and M (bf16 hi + lo) and
+//   writes the chunk's record: Kt, Qt, Kb^T, M (bf16), T (bf16 hi + lo) and
 //   gamma, laid out as the scan kernel's LDS image.
 // scan (kda_scan16_kernel): one workgroup per (batch, head, 64 value columns),
 //   walking the chunks in order.  Four loader waves copy each record from
@@ -33,9 +33,10 @@
 //   / V first, the rest second, the rest in two buffers by chunk parity), so
 //   the scan waves never wait for a workgroup barrier.
 //
-// Precision: Kt, Qt, Kb and the state enter the products as bf16; V - Kt S,
-// T, M and U as bf16 hi + lo pairs (about 16 mantissa bits, three products
-// per pair); accumulation is fp32.
+// Precision: Kt, Qt, Kb, M and the state enter the products as bf16; V - Kt S,
+// T and U as bf16 hi + lo pairs (about 16 mantissa bits, three products per
+// pair, two where the other factor is plain bf16); accumulation is fp32.  M
+// feeds only the output, so its rounding does not build up in the state.
 #include "kda_bf16.hpp"
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
@@ -67,7 +68,7 @@ enum { kEP = 0, kEK = 4, kIE = 8, kTF20 = 12, kTF30 = 13, kTF31 = 14, kGam = 15,
 // conflict-free 16-byte LDS read per lane.
 //   Kt, Qt:  fragment 4 rt + s = tokens 16 rt .., channels 32 s ..   (16 KB each)
 //   Kb^T:    fragment 2 t + s2 = channels 16 t .., tokens 32 s2 ..  (16 KB)
-//   T hi, T lo, M hi, M lo (5 KB each): the six fragments (rt, s2) = (0,0)
+//   T hi, T lo, M (5 KB each): the six fragments (rt, s2) = (0,0)
 //     (1,0) (2,0) (2,1) (3,0) (3,1) of the lower-triangular [token][token]
 //     matrix; (0,0) and (2,1) have zero values 4..7 (blocks above the
 //     diagonal) and are stored as half fragments, 8 bytes per lane;
@@ -78,15 +79,17 @@ struct Rec16 {
     static constexpr size_t QT = KT + 16 * kFrag;
     static constexpr size_t KB = QT + 16 * kFrag;
     static constexpr size_t TM = KB + 16 * kFrag;
-    static constexpr size_t kTM = 5 * kFrag;                 // one of the four matrices
-    static constexpr size_t G = TM + 4 * kTM;
+    static constexpr size_t kTM = 5 * kFrag;                 // one of the three matrices
+    static constexpr size_t G = TM + 3 * kTM;
     static constexpr size_t BYTES = G + kD * 4;
 };
 static_assert(Rec16::BYTES % 256 == 0, "records stay 256-byte aligned");
 // the scan's loaders move a record as 16-byte pieces: 2048 of Kt / Qt, then
-// 1024 of Kb^T plus 1280 of T / M (9 per thread), 32 of gamma, 256 threads
-static_assert(Rec16::KB / 16 == 2048 && (Rec16::G - Rec16::KB) / 16 == 9 * 256 &&
-                  Rec16::G / 16 + 32 == Rec16::BYTES / 16,
+// the rest, 1024 of Kb^T, 960 of T / M and 32 of gamma: 7 per thread and 224
+// more, 256 threads
+constexpr int kRestFull = 7, kRestTail = 224;
+static_assert(Rec16::KB / 16 == 2048 && Rec16::G / 16 + 32 == Rec16::BYTES / 16 &&
+                  (Rec16::BYTES - Rec16::KB) / 16 == kRestFull * 256 + kRestTail,
               "loader piece counts match the record layout");
 
 // fragment f = 0..5 of a T / M matrix: (rt, s2) and byte offset in the matrix
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     }
 
     // ---- the rest of the record -------------------------------------------------
-    // T = X diag(beta) (zero above the diagonal) and M as hi / lo: row r,
+    // T = X diag(beta) (zero above the diagonal) as hi / lo and M: row r,
     // columns 16ct + 4g .. +3 per lane, lower blocks (p, ct <= p) only: value
     // half ct & 1 of lane (n, g) of fragment (p, ct / 2)
     {
@@ -515,7 +518,6 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
             uint2* th = reinterpret_cast<uint2*>(tm + 0 * Rec16::kTM + off);
             uint2* tl = reinterpret_cast<uint2*>(tm + 1 * Rec16::kTM + off);
             uint2* mh = reinterpret_cast<uint2*>(tm + 2 * Rec16::kTM + off);
-            uint2* ml = reinterpret_cast<uint2*>(tm + 3 * Rec16::kTM + off);
             float tv[4], mv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
                 mv[e] = Mt[ct][e];
             }
             split4(tv, *th, *tl);
-            split4(mv, *mh, *ml);
+            *mh = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
         }
     }
     if (p == 0) {
@@ -602,8 +604,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // =====================================================================
         // V of the slice: 64 tokens x 64 columns = 512 pieces of 8 columns, two
         // per thread (piece tid + 256 m: token piece >> 3, columns 8 (piece & 7))
-        u32x4 ra[8], rb[9], rv[2];
-        u32x4 rg = {0u, 0u, 0u, 0u};
+        u32x4 ra[8], rb[kRestFull + 1], rv[2];
         const int64_t vstride = (int64_t)H * kD;
         const uint16_t* vslice = v + ((int64_t)b * T * H + h) * kD + kCols * slice;
         // short convolution of V: a wave's piece m holds 8 consecutive tokens
@@ -628,8 +629,9 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         const u32x4* src_ = reinterpret_cast<const u32x4*>(                                      \
             ws + ((size_t)(cl_) * BH + bh) * Rec16::BYTES);                                      \
         _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) ra[m_] = src_[tid + 256 * m_];          \
-        _Pragma("unroll") for (int m_ = 0; m_ < 9; ++m_) rb[m_] = src_[2048 + tid + 256 * m_];   \
-        if (tid < 32) rg = src_[(Rec16::G / 16) + tid];                                          \
+        _Pragma("unroll") for (int m_ = 0; m_ < kRestFull; ++m_)                                \
+            rb[m_] = src_[2048 + tid + 256 * m_];                                                \
+        rb[kRestFull] = src_[2048 + 256 * kRestFull + (tid < kRestTail ? tid : 0)];              \
         _Pragma("unroll") for (int m_ = 0; m_ < 2; ++m_) {                                       \
             const int pc_ = tid + 256 * m_;                                                      \
             const int64_t tk_ = (int64_t)(chunk0 + (cl_)) * kChunk + (pc_ >> 3);                 \
@@ -661,8 +663,8 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             if (i >= 2) wait_for(&sync_s[3], 4u * (i - 1), &sync_s[4]);
             u32x4* rs = rest_s[i & 1];
 #pragma unroll
-            for (int m = 0; m < 9; ++m) rs[tid + 256 * m] = rb[m];
-            if (tid < 32) rs[(Rec16::G - Rec16::KB) / 16 + tid] = rg;
+            for (int m = 0; m < kRestFull; ++m) rs[tid + 256 * m] = rb[m];
+            if (tid < kRestTail) rs[tid + 256 * kRestFull] = rb[kRestFull];
             signal(&sync_s[2], lane);
             // V of the chunk, filtered before the wait below so that the
             // filter does not hold up the scan waves; tokens past the end of
@@ -846,7 +848,6 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             const u32x4* th_s = rs + (Rec16::TM - Rec16::KB + 0 * Rec16::kTM) / 16;
             const u32x4* tl_s = rs + (Rec16::TM - Rec16::KB + 1 * Rec16::kTM) / 16;
             const u32x4* mh_s = rs + (Rec16::TM - Rec16::KB + 2 * Rec16::kTM) / 16;
-            const u32x4* ml_s = rs + (Rec16::TM - Rec16::KB + 3 * Rec16::kTM) / 16;
             const float* gam_s = reinterpret_cast<const float*>(rs + (Rec16::G - Rec16::KB) / 16);
 
             // U = T (V - Kt S), both factors as hi + lo (T lower triangular);
@@ -872,16 +873,16 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 U[rt] = mma(U[rt], fth[f], bl_[s2]);
             }
             // the M fragments (same six positions) are read while U is split
-            bf16x8 fmh[6], fml[6];
+            bf16x8 fmh[6];
 #pragma unroll
             for (int f = 0; f < 6; ++f) {
                 fmh[f] = frag_tm(mh_s, f, lane);
-                fml[f] = frag_tm(ml_s, f, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
 
-            // O^T = (Qt S)^T + U^T M^T, so that a lane holds token 16rt + n and
-            // the four consecutive columns j0 + 4g .. +3 (one 8-byte store);
+            // O^T = (Qt S)^T + U^T M^T (U as hi + lo, M bf16), so that a lane
+            // holds token 16rt + n and the four consecutive columns j0 + 4g ..
+            // +3 (one 8-byte store);
             // S <- Diag(gamma) S + Kb^T U   (U as hi + lo)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) split_b(U[2 * s2], U[2 * s2 + 1], bh_[s2], bl_[s2]);
@@ -901,7 +902,6 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     if (tm_rt(f) != rt) continue;
                     const int s2 = tm_s2(f);
                     o = mma(o, bh_[s2], fmh[f]);
-                    o = mma(o, bh_[s2], fml[f]);
                     o = mma(o, bl_[s2], fmh[f]);
                 }
                 const int64_t tk = c0 + 16 * rt + n;
