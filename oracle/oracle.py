@@ -222,3 +222,56 @@ def step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, eps=1e-6, thre
     if gate is not None:
         o = output_gate(o, gate)
     return o, S_new, tuple(states)
+
+
+# ---------------------------------------------------------------------------
+# Backward of one recurrent step (training through the recurrence, one token
+# at a time in reverse).  The pages say only that the log-decay bound serves
+# training speed (the ai-pulse-lab summary of the technical report, KDA
+# paragraph); the gradient is derived here by reverse-mode differentiation of
+# the step's own assignments, in reverse order.
+# ---------------------------------------------------------------------------
+def step_backward(q, k, v, g, beta, scale, S_prev, d_o, dS_next, eps=1e-6):
+    """Gradients of L = sum(d_o * o) + sum(dS_next * S_new) for one step
+    S_new, o = step(q, k, v, g, beta, scale, S_prev).  Shapes as ``step``
+    (d_o like o, dS_next like S).  Returns (dq, dk, dv, dg, dbeta, dS_prev)
+    in fp64, one (b, h) at a time with plain numpy."""
+    q, k, v, g, beta, S_prev, d_o, dS_next = map(
+        _f64, (q, k, v, g, beta, S_prev, d_o, dS_next))
+    dq, dk, dv, dg = (np.zeros_like(x) for x in (q, k, v, g))
+    dbeta = np.zeros_like(beta)
+    dS_prev = np.zeros_like(S_prev)
+    B, H = q.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            # forward, keeping every intermediate
+            rq = 1.0 / np.sqrt(q[b, h] @ q[b, h] + eps)
+            rk = 1.0 / np.sqrt(k[b, h] @ k[b, h] + eps)
+            qh, kh = q[b, h] * rq, k[b, h] * rk
+            a = np.exp(g[b, h])
+            St = a[:, None] * S_prev[b, h]           # decayed state
+            p = St.T @ kh                              # prediction
+            bt = beta[b, h]
+            u = bt * (v[b, h] - p)                     # scaled error
+            Sn = St + np.outer(kh, u)                  # new state
+            # o = scale * Sn^T qh
+            G = dS_next[b, h] + scale * np.outer(qh, d_o[b, h])   # dL/dSn
+            dqh = scale * (Sn @ d_o[b, h])
+            # Sn = St + kh u^T
+            dSt = G.copy()
+            dkh = G @ u
+            du = G.T @ kh
+            # u = beta (v - p)
+            dv[b, h] = bt * du
+            dbeta[b, h] = du @ (v[b, h] - p)
+            dp = -bt * du
+            # p = St^T kh
+            dSt += np.outer(kh, dp)
+            dkh += St @ dp
+            # St = diag(exp g) S_prev
+            dS_prev[b, h] = a[:, None] * dSt
+            dg[b, h] = np.sum(St * dSt, axis=1)
+            # qh = q / sqrt(|q|^2 + eps), likewise k
+            dq[b, h] = rq * dqh - rq ** 3 * (q[b, h] @ dqh) * q[b, h]
+            dk[b, h] = rk * dkh - rk ** 3 * (k[b, h] @ dkh) * k[b, h]
+    return dq, dk, dv, dg, dbeta, dS_prev

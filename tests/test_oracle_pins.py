@@ -407,3 +407,85 @@ def test_gated_conv_forward_and_steps():
         ot, S, cs = oracle.step_conv(q[:, t], k[:, t], v[:, t], wq, wk, wv, cs, g[:, t],
                                      beta[:, t], 0.7, S, threads=1, gate=z[:, t])
         np.testing.assert_allclose(ot, og[:, t], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# backward of one recurrent step
+# ---------------------------------------------------------------------------
+def _step_loss(x, d_o, dS_next, scale):
+    o, Sn = oracle.step(x["q"], x["k"], x["v"], x["g"], x["beta"], scale, x["S"], threads=1)
+    return float(np.sum(d_o * o) + np.sum(dS_next * Sn))
+
+
+def test_step_backward_against_finite_differences():
+    """Every gradient of one step (q, k, v, g, beta and the previous state)
+    against central differences of the forward step in fp64: a dropped term,
+    a wrong sign or a transposed operand anywhere in the reverse pass fails
+    here.  Small D so that every entry is perturbed."""
+    rng = np.random.default_rng(21)
+    B, H, D, scale = 1, 2, 6, 0.8
+    x = {"q": rng.standard_normal((B, H, D)), "k": rng.standard_normal((B, H, D)),
+         "v": rng.standard_normal((B, H, D)),
+         "g": -5.0 / (1.0 + np.exp(-rng.standard_normal((B, H, D)))),
+         "beta": 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H)))),
+         "S": rng.standard_normal((B, H, D, D))}
+    d_o = rng.standard_normal((B, H, D))
+    dS_next = rng.standard_normal((B, H, D, D))
+    grads = oracle.step_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], scale, x["S"],
+                                 d_o, dS_next)
+    h = 1e-6
+    for name, gr in zip(("q", "k", "v", "g", "beta", "S"), grads):
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(*x[name].shape):
+            xp = {k_: v_.copy() for k_, v_ in x.items()}
+            xm = {k_: v_.copy() for k_, v_ in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            num[idx] = (_step_loss(xp, d_o, dS_next, scale) -
+                        _step_loss(xm, d_o, dS_next, scale)) / (2 * h)
+        np.testing.assert_allclose(gr, num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_step_backward_chains_to_the_sequence_gradient():
+    """Backpropagating token by token through stored states gives the
+    gradient of the whole T-token forward pass (checked by central
+    differences of forward), including that of the initial state."""
+    rng = np.random.default_rng(22)
+    B, T, H, D, scale = 1, 4, 1, 5, 0.9
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    g = -5.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, D))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    h0 = rng.standard_normal((B, H, D, D))
+    d_o = rng.standard_normal((B, T, H, D))
+    d_hT = rng.standard_normal((B, H, D, D))
+
+    def loss(h0_, v_):
+        o, hT = oracle.forward(q, k, v_, g, beta, scale, h0_, threads=1)
+        return float(np.sum(d_o * o) + np.sum(d_hT * hT))
+
+    states = [h0]
+    for t in range(T):
+        _, Sn = oracle.step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], scale, states[-1],
+                            threads=1)
+        states.append(Sn)
+    dS = d_hT.copy()
+    dv = np.zeros_like(v)
+    for t in reversed(range(T)):
+        _, _, dv_t, _, _, dS = oracle.step_backward(q[:, t], k[:, t], v[:, t], g[:, t],
+                                                    beta[:, t], scale, states[t], d_o[:, t], dS)
+        dv[:, t] = dv_t
+    eps = 1e-6
+    num_h0 = np.zeros_like(h0)
+    for idx in np.ndindex(*h0.shape):
+        hp, hm = h0.copy(), h0.copy()
+        hp[idx] += eps
+        hm[idx] -= eps
+        num_h0[idx] = (loss(hp, v) - loss(hm, v)) / (2 * eps)
+    np.testing.assert_allclose(dS, num_h0, rtol=1e-6, atol=1e-7)
+    num_v = np.zeros_like(v)
+    for idx in np.ndindex(*v.shape):
+        vp, vm = v.copy(), v.copy()
+        vp[idx] += eps
+        vm[idx] -= eps
+        num_v[idx] = (loss(h0, vp) - loss(h0, vm)) / (2 * eps)
+    np.testing.assert_allclose(dv, num_v, rtol=1e-6, atol=1e-7)
