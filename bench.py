@@ -44,6 +44,10 @@ CONV_STATE_BYTES = 3 * 3 * 128 * 2
 CONV_TAP_BYTES_PER_HEAD = 3 * 128 * 4 * 4
 # the output gate's bf16 logits, one per output value
 GATE_BYTES_PER_TOKEN_HEAD = 128 * 2
+# backward of one fp32 decode step per (sequence, head): the state before the
+# step and the state gradient read, the state gradient written; q, k, v, g,
+# dout read and dq, dk, dv, dg written (fp32); beta read, dbeta written
+BWD_STEP_BYTES_PER_SEQ_HEAD = 3 * STATE_BYTES + 9 * 128 * 4 + 2 * 4
 
 
 def parse():
@@ -259,6 +263,24 @@ def main():
           file=sys.stderr, flush=True)
     del dcp, xcs, zds
 
+    # ---- backward of one decode step (fp32) ---------------------------------
+    del S
+    xb = synth.decode_step_inputs(wd.B, wd.H, torch.float32, seed=wd.seed, step=0, device=dev)
+    Sp = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
+    dSb = synth.decode_state(wd.B, wd.H, seed=wd.seed + 1, h0_std=wd.h0_std, device=dev)
+    dob = torch.randn((wd.B, wd.H, 128), device=dev)
+
+    def decode_bwd():
+        libkda.recurrent_step_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
+                                  Sp, dob, dSb)
+
+    bms, bms_med, bms_min = time_op(torch, decode_bwd, dsteps, args.warmup)
+    bwd_bytes = nbh * BWD_STEP_BYTES_PER_SEQ_HEAD
+    bwd_gbps = bwd_bytes / (bms / 1e3) / 1e9
+    print(f"# decode backward step: {bms:.3f} ms/step, total {bwd_gbps:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    del xb, Sp, dSb, dob
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -355,6 +377,22 @@ def main():
                 "unit": "GB/s",
                 "frac": round(dconv_gbps / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_call": dconv_bytes,
+            },
+        },
+        "decode_bwd": {
+            "workload": "backward of one decode step at B=256 H=96, all fp32 "
+                        "(kda_recurrent_step_bwd_f32): state and state gradient read, "
+                        "state gradient written in place",
+            "ms_per_step": round(bms, 4),
+            "ms_per_step_median": round(bms_med, 4),
+            "ms_per_step_min": round(bms_min, 4),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(bwd_gbps, 1),
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes_per_call": bwd_bytes,
             },
         },
         "decode": {

@@ -216,6 +216,33 @@ KDA_API kda_status_t kda_recurrent_step_f32(const float *q, const float *k, cons
                                     float *S_inout, float *out,
                                     int B, int H, hipStream_t stream);
 
+/*
+ * kda_recurrent_step_bwd_f32 — backward of one kda_recurrent_step_f32 step,
+ * for training through the recurrence one token at a time in reverse
+ * (backpropagation through time, with the states before each step kept by
+ * the caller).  The pages say only that the log-decay bound serves training
+ * speed (ai-pulse-lab summary of the technical report, KDA paragraph); the
+ * gradients are those of the step's assignments, differentiated in reverse
+ * order.  For L = <dout, o> + <dS_next, S_new> of the step
+ * (o, S_new) = step(q, k, v, g, beta, scale, S_prev):
+ *
+ *   q, k, v, g : [B, H, 128] fp32, the step's inputs (q, k raw: the L2 norms
+ *                are differentiated too); beta [B, H] fp32; scale finite.
+ *   S_prev     : [B, H, 128, 128] fp32, the state before the step.
+ *   dout       : [B, H, 128] fp32, dL/do.
+ *   dS         : [B, H, 128, 128] fp32, in: dL/dS_new (zeros after the last
+ *                token); out: dL/dS_prev, in place, ready for the step before.
+ *   dq, dk, dv, dg : [B, H, 128] fp32 outputs; dbeta [B, H] fp32 output.
+ *
+ * Every written buffer must not overlap any other argument.  All pointers
+ * 16-byte aligned (beta, dbeta 4).  B == 0 or H == 0 is a no-op.
+ */
+KDA_API kda_status_t kda_recurrent_step_bwd_f32(const float *q, const float *k, const float *v,
+                                        const float *g, const float *beta, float scale,
+                                        const float *S_prev, const float *dout, float *dS,
+                                        float *dq, float *dk, float *dv, float *dg,
+                                        float *dbeta, int B, int H, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "lib", "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk16.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk16.hip", "kda_backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

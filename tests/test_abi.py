@@ -171,6 +171,32 @@ def test_step_conv_invalid_arguments(lib):
     assert step_conv(lib, H=0) == libkda.KDA_OK
 
 
+def step_bwd(lib, **kw):
+    args = dict(q=P[0], k=P[1], v=P[2], g=P[3], beta=P[4], scale=1.0, S_prev=P[5], dout=P[6],
+                dS=P[7], dq=P[8], dk=P[9], dv=P[10], dg=P[11], dbeta=ctypes.c_void_p(A * 13),
+                B=1, H=1)
+    args.update(kw)
+    return lib.kda_recurrent_step_bwd_f32(*args.values(), None)
+
+
+def test_step_bwd_invalid_arguments(lib):
+    INV = libkda.KDA_ERR_INVALID_ARG
+    assert step_bwd(lib, B=-1) == INV
+    assert step_bwd(lib, scale=math.inf) == INV
+    for name in ("q", "k", "v", "g", "beta", "S_prev", "dout", "dS", "dq", "dk", "dv", "dg",
+                 "dbeta"):
+        assert step_bwd(lib, **{name: NULL}) == INV, name
+    for name in ("q", "dS", "dq", "dg"):
+        assert step_bwd(lib, **{name: ctypes.c_void_p(A * 20 + 8)}) == INV, name
+    # a written buffer over an input, over the state, over another output
+    assert step_bwd(lib, dq=ctypes.c_void_p(A * 1 + 256)) == INV
+    assert step_bwd(lib, dS=ctypes.c_void_p(A * 6 - 4096)) == INV
+    assert step_bwd(lib, dv=ctypes.c_void_p(A * 9 + 256)) == INV
+    assert step_bwd(lib, dbeta=ctypes.c_void_p(A * 12 + 64)) == INV
+    assert step_bwd(lib, B=0) == libkda.KDA_OK
+    assert step_bwd(lib, H=0) == libkda.KDA_OK
+
+
 def test_binding_rejects_bad_tensors():
     import torch
     q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
