@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=None,
-                    help="timed decode steps (default: --steps)")
+                    help="timed decode steps (default: the workload's 64 consecutive "
+                         "steps, each with its own inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
@@ -223,19 +224,22 @@ def main():
     # ---- decode -------------------------------------------------------------
     wd = synth.WORKLOADS["decode_b256"]
     S = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
+    # the workload's 64 consecutive steps, each with its own inputs (drawn
+    # beforehand); warm-up steps reuse the first ones
+    dsteps = args.decode_steps or wd.T
     xs = [synth.decode_step_inputs(wd.B, wd.H, wd.io, seed=wd.seed, step=t, device=dev)
-          for t in range(4)]
+          for t in range(dsteps)]
     dout = torch.empty_like(xs[0]["v"])
     it = [0]
 
     def decode():
-        x = xs[it[0] & 3]
+        x = xs[it[0] % dsteps]
         it[0] += 1
         libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S,
                               out=dout)
 
-    dsteps = args.decode_steps or args.steps
     dms, dms_med, dms_min = time_op(torch, decode, dsteps, args.warmup)
+    del xs
     nbh = wd.B * wd.H
     state_gbps = nbh * 2 * STATE_BYTES / (dms / 1e3) / 1e9
     dec_gbps = nbh * DECODE_BYTES_PER_SEQ_HEAD / (dms / 1e3) / 1e9
@@ -396,7 +400,8 @@ def main():
             },
         },
         "decode": {
-            "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v",
+            "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v; 64 "
+                        "consecutive steps timed, fresh inputs each step",
             "ms_per_step": round(dms, 4),
             "ms_per_step_median": round(dms_med, 4),
             "ms_per_step_min": round(dms_min, 4),
