@@ -299,3 +299,18 @@ def test_gated_decode_b256():
     eo, es = rel_out(host64(out)[:, None], o_ref[:, None]), rel_state(host64(S), S_ref)
     say(f"gated decode b256: out err {eo:.2e} state err {es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_gated_conv_more_scan_workgroups_than_cus():
+    """The whole layer (filter + attention + gate) at B=3, H=96: 576 scan
+    workgroups, run in rounds; every head against the oracle."""
+    B, T, H = 3, 200, 96
+    inp = synth.conv_inputs(B, T, H, seed=730, with_state=True, device=DEV)
+    z = synth.gate_logits((B, T, H, 128), seed=731, device=DEV)
+    out, hT, cout = run(inp, gate=z)
+    o_ref, h_ref, c_ref = oracle_conv(inp, gate=z)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"gated conv B={B} T={T} H={H}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for i in range(3):
+        assert np.array_equal(host64(cout[i]), c_ref[i]), i
