@@ -243,6 +243,19 @@ KDA_API kda_status_t kda_recurrent_step_bwd_f32(const float *q, const float *k, 
                                         float *dq, float *dk, float *dv, float *dg,
                                         float *dbeta, int B, int H, hipStream_t stream);
 
+/*
+ * kda_recurrent_step_bwd — kda_recurrent_step_bwd_f32 for the bf16 decode
+ * step kda_recurrent_step: q, k, v and dout are [B, H, 128] bf16, and dq, dk,
+ * dv are written as [B, H, 128] bf16 (rounded to nearest even from fp32).
+ * g, beta, S_prev, dS, dg and dbeta, the validation and the in-place update
+ * of dS are those of kda_recurrent_step_bwd_f32.
+ */
+KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k,
+                                    const uint16_t *v, const float *g, const float *beta,
+                                    float scale, const float *S_prev, const uint16_t *dout,
+                                    float *dS, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                                    float *dg, float *dbeta, int B, int H, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);
 

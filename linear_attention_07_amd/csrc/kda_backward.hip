@@ -1,5 +1,5 @@
 // Backward of one recurrent KDA step (training through the recurrence, one
-// token at a time in reverse), and its C entry point.
+// token at a time in reverse), and its C entry points (fp32 and bf16 I/O).
 //
 // The step (Kimi-K3 深度解析 blog, section 三; 深入 Kimi-K3 thread, KDA
 // paragraph, for the in-kernel L2 norms):
@@ -33,12 +33,18 @@
 namespace kda {
 namespace {
 
+// F32: q, k, v, dout, dq, dk, dv in fp32; else in bf16 (rounded to nearest
+// even on store).  g, beta, the states and dg, dbeta are fp32 either way.
+template <bool F32>
 __global__ __launch_bounds__(256) void kda_step_bwd_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, float scale,
-    const float* __restrict__ S_prev, const float* __restrict__ d_o, float* __restrict__ dS,
-    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-    float* __restrict__ dg, float* __restrict__ dbeta) {
+    const typename Prec<F32>::io_t* __restrict__ q, const typename Prec<F32>::io_t* __restrict__ k,
+    const typename Prec<F32>::io_t* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, float scale, const float* __restrict__ S_prev,
+    const typename Prec<F32>::io_t* __restrict__ d_o, float* __restrict__ dS,
+    typename Prec<F32>::io_t* __restrict__ dq, typename Prec<F32>::io_t* __restrict__ dk,
+    typename Prec<F32>::io_t* __restrict__ dv, float* __restrict__ dg,
+    float* __restrict__ dbeta) {
+    using P = Prec<F32>;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t bh = blockIdx.x;
     const int cg = lane & 7, rg = lane >> 3;
@@ -60,9 +66,10 @@ __global__ __launch_bounds__(256) void kda_step_bwd_kernel(
     }
 
     // norms (every wave computes them; wave 0 publishes qh, kh, exp g)
-    const float* qb = q + bh * kD;
-    const float* kb = k + bh * kD;
-    const float q0 = qb[lane], q1 = qb[lane + 64], k0 = kb[lane], k1 = kb[lane + 64];
+    const auto* qb = q + bh * kD;
+    const auto* kb = k + bh * kD;
+    const float q0 = P::from_io(qb[lane]), q1 = P::from_io(qb[lane + 64]);
+    const float k0 = P::from_io(kb[lane]), k1 = P::from_io(kb[lane + 64]);
     float ssq = q0 * q0 + q1 * q1, ssk = k0 * k0 + k1 * k1, sqk = q0 * k0 + q1 * k1;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -84,8 +91,8 @@ __global__ __launch_bounds__(256) void kda_step_bwd_kernel(
     float vv[4], dov[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        vv[c] = v[bh * kD + col + c];
-        dov[c] = d_o[bh * kD + col + c];
+        vv[c] = P::from_io(v[bh * kD + col + c]);
+        dov[c] = P::from_io(d_o[bh * kD + col + c]);
     }
     __syncthreads();
 
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(256) void kda_step_bwd_kernel(
     }
     if (rg == 0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dv[bh * kD + col + c] = bt * du[c];
+        for (int c = 0; c < 4; ++c) dv[bh * kD + col + c] = P::to_io(bt * du[c]);
     }
 #pragma unroll
     for (int off = 1; off <= 4; off <<= 1) {
@@ -200,8 +207,8 @@ __global__ __launch_bounds__(256) void kda_step_bwd_kernel(
     __syncthreads();
     if (tid < kD) {
         const float qdq = dot_s[0][0] + dot_s[0][1], kdk = dot_s[1][0] + dot_s[1][1];
-        dq[bh * kD + i] = rq * (dqh - qh_s[i] * qdq);
-        dk[bh * kD + i] = rk * (dkh - kh_s[i] * kdk);
+        dq[bh * kD + i] = P::to_io(rq * (dqh - qh_s[i] * qdq));
+        dk[bh * kD + i] = P::to_io(rk * (dkh - kh_s[i] * kdk));
     }
 }
 
@@ -216,31 +223,36 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }  // namespace
 }  // namespace kda
 
-extern "C" kda_status_t kda_recurrent_step_bwd_f32(
-    const float* q, const float* k, const float* v, const float* g, const float* beta,
-    float scale, const float* S_prev, const float* dout, float* dS, float* dq, float* dk,
-    float* dv, float* dg, float* dbeta, int B, int H, hipStream_t stream) {
+namespace {
+
+template <bool F32>
+kda_status_t step_bwd(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, float scale, const float* S_prev, const void* dout,
+                      float* dS, void* dq, void* dk, void* dv, float* dg, float* dbeta, int B,
+                      int H, hipStream_t stream) {
     using kda::aligned;
     using kda::overlap;
+    using io = typename kda::Prec<F32>::io_t;
     if (B < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     if (B == 0 || H == 0) return KDA_OK;
     const void* ins[] = {q, k, v, g, S_prev, dout};
-    float* outs[] = {dq, dk, dv, dg};
+    const void* outs[] = {dq, dk, dv, dg};
     for (const void* p : ins)
         if (!p || !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
-    for (const float* p : outs)
+    for (const void* p : outs)
         if (!p || !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
     if (!dS || !aligned(dS, 16) || !beta || !aligned(beta, 4) || !dbeta || !aligned(dbeta, 4))
         return KDA_ERR_INVALID_ARG;
     if ((int64_t)B * H > ((int64_t)1 << 31) - 1) return KDA_ERR_UNSUPPORTED;
     const size_t nbh = (size_t)B * H;
-    const size_t vec = nbh * KDA_HEAD_DIM * sizeof(float);
-    const size_t sbytes = vec * KDA_HEAD_DIM;
-    const size_t ins_n[] = {vec, vec, vec, vec, sbytes, vec};
+    const size_t vec = nbh * KDA_HEAD_DIM * sizeof(io);      // q, k, v, dout, dq, dk, dv
+    const size_t vec32 = nbh * KDA_HEAD_DIM * sizeof(float);  // g, dg
+    const size_t sbytes = vec32 * KDA_HEAD_DIM;
+    const size_t ins_n[] = {vec, vec, vec, vec32, sbytes, vec};
     // every written buffer overlaps nothing else that is read or written
     const void* written[] = {dq, dk, dv, dg, dbeta, dS};
-    const size_t written_n[] = {vec, vec, vec, vec, nbh * sizeof(float), sbytes};
+    const size_t written_n[] = {vec, vec, vec, vec32, nbh * sizeof(float), sbytes};
     for (int a = 0; a < 6; ++a) {
         for (int b = 0; b < 6; ++b)
             if (overlap(written[a], written_n[a], ins[b], ins_n[b])) return KDA_ERR_INVALID_ARG;
@@ -250,7 +262,28 @@ extern "C" kda_status_t kda_recurrent_step_bwd_f32(
             if (overlap(written[a], written_n[a], written[b], written_n[b]))
                 return KDA_ERR_INVALID_ARG;
     }
-    hipLaunchKernelGGL(kda::kda_step_bwd_kernel, dim3((unsigned)nbh), dim3(256), 0, stream, q, k,
-                       v, g, beta, scale, S_prev, dout, dS, dq, dk, dv, dg, dbeta);
+    hipLaunchKernelGGL(kda::kda_step_bwd_kernel<F32>, dim3((unsigned)nbh), dim3(256), 0, stream,
+                       static_cast<const io*>(q), static_cast<const io*>(k),
+                       static_cast<const io*>(v), g, beta, scale, S_prev,
+                       static_cast<const io*>(dout), dS, static_cast<io*>(dq),
+                       static_cast<io*>(dk), static_cast<io*>(dv), dg, dbeta);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" kda_status_t kda_recurrent_step_bwd_f32(
+    const float* q, const float* k, const float* v, const float* g, const float* beta,
+    float scale, const float* S_prev, const float* dout, float* dS, float* dq, float* dk,
+    float* dv, float* dg, float* dbeta, int B, int H, hipStream_t stream) {
+    return step_bwd<true>(q, k, v, g, beta, scale, S_prev, dout, dS, dq, dk, dv, dg, dbeta, B, H,
+                          stream);
+}
+
+extern "C" kda_status_t kda_recurrent_step_bwd(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+    float scale, const float* S_prev, const uint16_t* dout, float* dS, uint16_t* dq,
+    uint16_t* dk, uint16_t* dv, float* dg, float* dbeta, int B, int H, hipStream_t stream) {
+    return step_bwd<false>(q, k, v, g, beta, scale, S_prev, dout, dS, dq, dk, dv, dg, dbeta, B,
+                           H, stream);
 }

@@ -29,6 +29,7 @@ EXPORTS = (
     "kda_chunk_fwd_f32",
     "kda_chunk_fwd_g16",
     "kda_recurrent_step",
+    "kda_recurrent_step_bwd",
     "kda_recurrent_step_bwd_f32",
     "kda_recurrent_step_conv",
     "kda_recurrent_step_f32",
@@ -67,8 +68,10 @@ def load() -> ctypes.CDLL:
     lib.kda_recurrent_step_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, i,
                                             i, vp]
     lib.kda_recurrent_step_conv.restype = ctypes.c_int
-    lib.kda_recurrent_step_bwd_f32.argtypes = [vp] * 5 + [f] + [vp] * 8 + [i, i, vp]
-    lib.kda_recurrent_step_bwd_f32.restype = ctypes.c_int
+    for name in ("kda_recurrent_step_bwd_f32", "kda_recurrent_step_bwd"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp] * 5 + [f] + [vp] * 8 + [i, i, vp]
+        fn.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -259,26 +262,35 @@ def recurrent_step_conv(q, k, v, wq, wk, wv, conv_state, g, beta, scale, S, out=
 
 
 def recurrent_step_bwd(q, k, v, g, beta, scale, S_prev, dout, dS):
-    """Backward of one fp32 recurrent step (kda_recurrent_step_bwd_f32).
-    q, k, v, g, dout: [B, H, 128] fp32; beta: [B, H] fp32; S_prev: the state
-    before the step; dS: [B, H, 128, 128] fp32 gradient of the state after
-    the step, replaced in place by the gradient of the state before it.
-    Returns (dq, dk, dv, dg, dbeta)."""
+    """Backward of one recurrent step (kda_recurrent_step_bwd_f32, or
+    kda_recurrent_step_bwd for bf16 q / k / v / dout).  q, k, v, dout:
+    [B, H, 128] fp32 or bf16 (all alike); g: [B, H, 128] fp32; beta: [B, H]
+    fp32; S_prev: the state before the step; dS: [B, H, 128, 128] fp32
+    gradient of the state after the step, replaced in place by the gradient
+    of the state before it.  Returns (dq, dk, dv in the type of q, dg, dbeta
+    fp32)."""
     if q.dim() != 3 or q.shape[-1] != HEAD_DIM:
         raise ValueError(f"q: expected [B, H, {HEAD_DIM}], got {tuple(q.shape)}")
     B, H, _ = q.shape
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("kda tensors must live on a GPU")
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("dout", dout)):
-        _check(t, name, q.shape, torch.float32, dev)
+    io = q.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q: dtype {io} not supported")
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, q.shape, io, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
     _check(beta, "beta", (B, H), torch.float32, dev)
     sshape = (B, H, HEAD_DIM, HEAD_DIM)
     _check(S_prev, "S_prev", sshape, torch.float32, dev)
     _check(dS, "dS", sshape, torch.float32, dev)
-    dq, dk, dv, dg = (torch.empty_like(q) for _ in range(4))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dg = torch.empty_like(g)
     dbeta = torch.empty_like(beta)
-    st = load().kda_recurrent_step_bwd_f32(
+    lib = load()
+    fn = lib.kda_recurrent_step_bwd_f32 if io == torch.float32 else lib.kda_recurrent_step_bwd
+    st = fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(S_prev), _ptr(dout),
         _ptr(dS), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), B, H, _stream(dev))
     if st != KDA_OK:

@@ -3,8 +3,10 @@ step) against the fp64 oracle's step_backward, which is pinned by central
 differences of the forward step; and backpropagation through a short
 sequence with the states kept, against the oracle chained the same way.
 
-fp32 arithmetic throughout: the bar is the fp32-mode one, 1e-3 normalised
-max error per gradient (the measured errors are near 1e-6)."""
+fp32 arithmetic throughout: with fp32 I/O the bar is the fp32-mode one, 1e-3
+normalised max error per gradient (the measured errors are near 1e-6); with
+bf16 q / k / v / dout the oracle reads the same bf16 values and dq, dk, dv
+are rounded to bf16, so the bar is the bf16 one, 1e-2."""
 import numpy as np
 import pytest
 import torch
@@ -25,11 +27,11 @@ def rel(x, ref):
     return float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
 
 
-def inputs(B, H, seed):
-    x = synth.decode_step_inputs(B, H, torch.float32, seed=seed, step=0, device=DEV)
+def inputs(B, H, seed, io=torch.float32):
+    x = synth.decode_step_inputs(B, H, io, seed=seed, step=0, device=DEV)
     gen = torch.Generator(device=DEV).manual_seed(seed)
     x["S"] = 0.1 * torch.randn((B, H, 128, 128), generator=gen, device=DEV)
-    x["dout"] = torch.randn((B, H, 128), generator=gen, device=DEV)
+    x["dout"] = torch.randn((B, H, 128), generator=gen, device=DEV).to(io)
     x["dS"] = 0.1 * torch.randn((B, H, 128, 128), generator=gen, device=DEV)
     return x
 
@@ -48,14 +50,17 @@ def oracle_bwd(x, sel=slice(None)):
                                 x["scale"], h(x["S"]), h(x["dout"]), h(x["dS"]))
 
 
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("B,H", [(1, 1), (3, 5), (2, 8)])
-def test_step_bwd_against_oracle(B, H):
-    x = inputs(B, H, seed=800 + 10 * B + H)
+def test_step_bwd_against_oracle(B, H, io):
+    x = inputs(B, H, seed=800 + 10 * B + H, io=io)
     got = gpu_bwd(x)
     want = oracle_bwd(x)
     errs = {n: rel(host64(a), b) for n, a, b in zip(NAMES, got, want)}
-    say(f"step bwd B={B} H={H}: " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()))
-    assert max(errs.values()) <= TOL
+    say(f"step bwd B={B} H={H} {io}: " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+    assert max(errs.values()) <= (TOL if io == torch.float32 else 1e-2)
+    if io == torch.bfloat16:   # the fp32 outputs keep fp32 accuracy
+        assert max(errs["dg"], errs["dbeta"], errs["dS_prev"]) <= TOL
 
 
 def test_step_bwd_b256_sampled():
