@@ -23,6 +23,7 @@ OUT_HEADS = (0, 47)
 @pytest.fixture(scope="module")
 def million():
     w = synth.WORKLOADS["prefill_1m"]
+    torch.cuda.empty_cache()   # blocks cached by earlier tests in this process
     free, total = torch.cuda.mem_get_info()
     if free < 170e9:
         pytest.skip(f"needs ~170 GB of device memory, {free / 1e9:.0f} GB free")
