@@ -99,14 +99,16 @@ def test_conv_chaining_matches_one_call(split):
 
 def test_conv_segmented_workspace_matches():
     """Workspace segments read the tokens before their first chunk from the
-    raw inputs: the split run equals the single-segment run exactly."""
+    raw inputs, and the gate by global token index: the split run equals the
+    single-segment run exactly."""
     B, T, H = 1, 2000, 3
     inp = synth.conv_inputs(B, T, H, seed=544, with_state=True, device=DEV)
-    out1, h1, c1 = run(inp)
+    z = synth.gate_logits((B, T, H, 128), seed=545, device=DEV)
+    out1, h1, c1 = run(inp, gate=z)
     old = os.environ.get("KDA_WORKSPACE_MB")
     os.environ["KDA_WORKSPACE_MB"] = "1"
     try:
-        out2, h2, c2 = run(inp)
+        out2, h2, c2 = run(inp, gate=z)
     finally:
         if old is None:
             del os.environ["KDA_WORKSPACE_MB"]
