@@ -13,6 +13,12 @@ the per-channel decay).  Inputs are widened to float64 from whatever exact
 values the caller holds (for GPU parity: the very bf16/fp32 bytes the GPU
 consumed), so input quantisation never counts as error.
 
+``step_backward`` is the reverse-mode derivative of one recurrent step, and
+``chunk_backward`` that of the chunkwise form over a whole sequence (the
+state entering each chunk kept from a forward pass, the chunks differentiated
+in reverse); the first is pinned to central differences, the second to the
+first chained token by token.
+
 Layouts follow the library's: q, k, v, g, o are ``[B, T, H, D]``; beta is
 ``[B, T, H]``; h0 and hT are ``[B, H, Dk, Dv]`` (key channel = row).
 """
@@ -275,3 +281,132 @@ def step_backward(q, k, v, g, beta, scale, S_prev, d_o, dS_next, eps=1e-6):
             dq[b, h] = rq * dqh - rq ** 3 * (q[b, h] @ dqh) * q[b, h]
             dk[b, h] = rk * dkh - rk ** 3 * (k[b, h] @ dkh) * k[b, h]
     return dq, dk, dv, dg, dbeta, dS_prev
+
+
+# ---------------------------------------------------------------------------
+# Backward of the chunkwise prefill.  The chunk form (derived from the
+# recurrence, not printed on the pages): for a chunk of tokens r = 0..C-1
+# entering with state S, with Gam_r = sum_{s<=r} g_s per channel and L the
+# chunk's last token,
+#   Kt_r = e^{Gam_r} kh_r, Qt_r = e^{Gam_r} qh_r, Kb_r = e^{Gam_L - Gam_r} kh_r,
+#   gamma = e^{Gam_L},
+#   P_ri = sum_c kh_rc kh_ic e^{Gam_rc - Gam_ic} (i < r),  A = diag(beta) P,
+#   N_ri = sum_c qh_rc kh_ic e^{Gam_rc - Gam_ic} (i <= r),  M = N,
+#   X = (I + A)^-1,  T = X diag(beta),  R = V - Kt S,  U = T R,
+#   O = scale (Qt S + M U),  S' = Diag(gamma) S + Kb^T U.
+# Its reverse-mode derivative, assignment by assignment in reverse order, is
+# written out below in fp64 (no factorisation of the decays is needed at
+# this precision: e^{+-320} is finite in fp64).
+# ---------------------------------------------------------------------------
+def _chunk_backward_one(qh, kh, v, g, beta, scale, S, dO, dSn):
+    """One chunk of one (b, h): qh, kh [C, Dk] normalised, v [C, Dv], g [C,
+    Dk], beta [C], S [Dk, Dv] entering state, dO [C, Dv], dSn = dL/dS'.
+    Returns (dqh, dkh, dv, dg, dbeta, dS)."""
+    C = qh.shape[0]
+    Gam = np.cumsum(g, axis=0)
+    GL = Gam[-1]
+    eG = np.exp(Gam)
+    Kt, Qt = eG * kh, eG * qh
+    eB = np.exp(GL[None, :] - Gam)
+    Kb = eB * kh
+    gam = np.exp(GL)
+    E = np.exp(Gam[:, None, :] - Gam[None, :, :])            # [r, i, c]
+    P = np.einsum("rc,ic,ric->ri", kh, kh, E)
+    N = np.einsum("rc,ic,ric->ri", qh, kh, E)
+    strict = np.tril(np.ones((C, C)), -1)
+    incl = np.tril(np.ones((C, C)))
+    A = beta[:, None] * P * strict
+    M = N * incl
+    X = np.linalg.inv(np.eye(C) + A)
+    T = X * beta[None, :]
+    R = v - Kt @ S
+    U = T @ R
+    # reverse
+    dU = scale * M.T @ dO + Kb @ dSn
+    dM = scale * (dO @ U.T) * incl
+    dQt = scale * dO @ S.T
+    dKb = U @ dSn.T
+    dgam = np.sum(dSn * S, axis=1)
+    dT = (dU @ R.T) * incl
+    dR = T.T @ dU
+    dv = dR
+    dKt = -dR @ S.T
+    dS = scale * Qt.T @ dO + gam[:, None] * dSn - Kt.T @ dR
+    dX = dT * beta[None, :]
+    dbeta = np.sum(X * dT, axis=0)
+    dA = -(X.T @ dX @ X.T) * strict
+    dbeta = dbeta + np.sum(dA * P, axis=1)
+    dP = beta[:, None] * dA
+    dN = dM
+    dkh = np.zeros_like(kh)
+    dqh = np.zeros_like(qh)
+    dGam = np.zeros_like(Gam)
+    # P_ri = sum_c kh_rc kh_ic E_ric ; N_ri = sum_c qh_rc kh_ic E_ric
+    wP = dP[:, :, None] * E                                 # [r, i, c]
+    wN = dN[:, :, None] * E
+    dkh += np.einsum("ric,ic->rc", wP, kh) + np.einsum("ric,rc->ic", wP, kh)
+    dqh += np.einsum("ric,ic->rc", wN, kh)
+    dkh += np.einsum("ric,rc->ic", wN, qh)
+    tP = wP * kh[:, None, :] * kh[None, :, :]
+    tN = wN * qh[:, None, :] * kh[None, :, :]
+    dGam += tP.sum(axis=1) - tP.sum(axis=0) + tN.sum(axis=1) - tN.sum(axis=0)
+    # Kt, Qt, Kb, gamma
+    dkh += eG * dKt
+    dGam += Kt * dKt
+    dqh += eG * dQt
+    dGam += Qt * dQt
+    dkh += eB * dKb
+    dGam -= Kb * dKb
+    dGam[-1] += np.sum(Kb * dKb, axis=0) + gam * dgam
+    # Gam_r = sum_{s <= r} g_s
+    dg = np.cumsum(dGam[::-1], axis=0)[::-1]
+    return dqh, dkh, dv, dg, dbeta, dS
+
+
+def chunk_backward(q, k, v, g, beta, scale, h0, d_o, d_hT=None, chunk=64, eps=1e-6):
+    """Gradients of L = <d_o, o> + <d_hT, hT> for (o, hT) = forward(q, k, v,
+    g, beta, scale, h0), computed the chunkwise way: a forward pass keeps the
+    state entering each chunk, then the chunks are differentiated in reverse
+    (_chunk_backward_one), the state gradient carried from one to the one
+    before.  Shapes as ``forward``; h0 may be None (zeros).  Returns (dq, dk,
+    dv, dg, dbeta, dh0) in fp64."""
+    q, k, v, g, beta, d_o = map(_f64, (q, k, v, g, beta, d_o))
+    B, T, H, D = q.shape
+    Dv = v.shape[3]
+    h0 = np.zeros((B, H, D, Dv)) if h0 is None else _f64(h0)
+    d_hT = np.zeros((B, H, D, Dv)) if d_hT is None else _f64(d_hT)
+    dq, dk, dv, dg = (np.zeros_like(x) for x in (q, k, v, g))
+    dbeta = np.zeros_like(beta)
+    dh0 = np.zeros_like(h0)
+    starts = list(range(0, T, chunk))
+    for b in range(B):
+        for h in range(H):
+            rq = 1.0 / np.sqrt(np.sum(q[b, :, h] ** 2, axis=1) + eps)
+            rk = 1.0 / np.sqrt(np.sum(k[b, :, h] ** 2, axis=1) + eps)
+            qh, kh = q[b, :, h] * rq[:, None], k[b, :, h] * rk[:, None]
+            # forward over the chunks, keeping each entering state
+            S = h0[b, h].copy()
+            states = []
+            for c0 in starts:
+                sl = slice(c0, min(T, c0 + chunk))
+                states.append(S.copy())
+                for r in range(sl.stop - sl.start):   # the recurrence within the chunk
+                    t = sl.start + r
+                    S = np.exp(g[b, t, h])[:, None] * S
+                    u = beta[b, t, h] * (v[b, t, h] - S.T @ kh[t])
+                    S = S + np.outer(kh[t], u)
+            dS = d_hT[b, h].copy()
+            dqh = np.zeros_like(qh)
+            dkh = np.zeros_like(kh)
+            for ci in reversed(range(len(starts))):
+                sl = slice(starts[ci], min(T, starts[ci] + chunk))
+                r = _chunk_backward_one(qh[sl], kh[sl], v[b, sl, h], g[b, sl, h],
+                                        beta[b, sl, h], scale, states[ci], d_o[b, sl, h], dS)
+                dqh[sl], dkh[sl] = r[0], r[1]
+                dv[b, sl, h], dg[b, sl, h], dbeta[b, sl, h] = r[2], r[3], r[4]
+                dS = r[5]
+            dh0[b, h] = dS
+            # qh = q / sqrt(|q|^2 + eps), likewise k
+            dq[b, :, h] = rq[:, None] * dqh - (rq ** 3 * np.sum(q[b, :, h] * dqh, axis=1))[:, None] * q[b, :, h]
+            dk[b, :, h] = rk[:, None] * dkh - (rk ** 3 * np.sum(k[b, :, h] * dkh, axis=1))[:, None] * k[b, :, h]
+    return dq, dk, dv, dg, dbeta, dh0

@@ -489,3 +489,44 @@ def test_step_backward_chains_to_the_sequence_gradient():
         vm[idx] -= eps
         num_v[idx] = (loss(h0, vp) - loss(h0, vm)) / (2 * eps)
     np.testing.assert_allclose(dv, num_v, rtol=1e-6, atol=1e-7)
+
+
+def _chained_step_backward(q, k, v, g, beta, scale, h0, d_o, d_hT):
+    """Reference: step_backward chained over the kept states (itself pinned
+    to central differences above)."""
+    B, T, H, D = q.shape
+    states = [h0]
+    for t in range(T):
+        _, Sn = oracle.step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], scale, states[-1],
+                            threads=1)
+        states.append(Sn)
+    dS = d_hT.copy()
+    out = [np.zeros_like(x) for x in (q, k, v, g)] + [np.zeros_like(beta)]
+    for t in reversed(range(T)):
+        r = oracle.step_backward(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], scale,
+                                 states[t], d_o[:, t], dS)
+        for j in range(4):
+            out[j][:, t] = r[j]
+        out[4][:, t] = r[4]
+        dS = r[5]
+    return (*out, dS)
+
+
+@pytest.mark.parametrize("chunk", [4, 16, 64])
+def test_chunk_backward_equals_chained_steps(chunk):
+    """The chunkwise backward (chunk algebra, differentiated in reverse) gives
+    the gradients of the token-by-token chain for every chunk size, with a
+    partial last chunk, decays down to the -5 bound and a nonzero initial
+    state: a wrong term in the chunk form's derivative fails here."""
+    rng = np.random.default_rng(31)
+    B, T, H, D, scale = 1, 37, 2, 6, 0.8
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    g = -5.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, D)) * 2.0))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    h0 = 0.3 * rng.standard_normal((B, H, D, D))
+    d_o = rng.standard_normal((B, T, H, D))
+    d_hT = rng.standard_normal((B, H, D, D))
+    got = oracle.chunk_backward(q, k, v, g, beta, scale, h0, d_o, d_hT, chunk=chunk)
+    want = _chained_step_backward(q, k, v, g, beta, scale, h0, d_o, d_hT)
+    for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, want):
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-11, err_msg=name)
