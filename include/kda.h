@@ -256,6 +256,38 @@ KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k
                                     float *dS, uint16_t *dq, uint16_t *dk, uint16_t *dv,
                                     float *dg, float *dbeta, int B, int H, hipStream_t stream);
 
+/*
+ * kda_chunk_bwd_f32 — backward of the fp32 chunked prefill kda_chunk_fwd_f32.
+ *
+ * The pages give no backward (they name training speed as the reason for the
+ * decay's lower bound: ai-pulse-lab summary of the technical report, KDA
+ * paragraph); the gradients are those of the recurrence of kda_chunk_fwd
+ * (Kimi-K3 深度解析 blog, section 三), computed through its chunk form: for
+ * L = <dout, o> + <dhT, hT> with (o, hT) = forward(q, k, v, g, beta, scale, h0),
+ *
+ *   q, k, v, g : [B, T, H, 128] fp32, the forward's inputs (q, k raw: the L2
+ *                norms are differentiated too); beta [B, T, H] fp32.
+ *   h0         : [B, H, 128, 128] fp32 initial state, or NULL for zeros.
+ *   dout       : [B, T, H, 128] fp32, dL/do.
+ *   dhT        : [B, H, 128, 128] fp32, dL/dhT, or NULL for zeros.
+ *   dq, dk, dv, dg : [B, T, H, 128] fp32 outputs; dbeta [B, T, H] fp32 output.
+ *   dh0        : [B, H, 128, 128] fp32 output dL/dh0, or NULL (not stored).
+ *
+ * Every written buffer must not overlap any other argument.  All pointers
+ * 16-byte aligned (beta, dbeta 4).  B == 0 or H == 0 is a no-op; T == 0
+ * copies dhT (or zeros) to dh0.  Workspace (the chunk records, the state
+ * entering and the state gradient leaving every chunk, and per-chunk scratch:
+ * about 385 KB per 64 tokens and head) comes from the library's stream-ordered
+ * pool; KDA_ERR_NO_MEMORY if it cannot be had.  Computed in fp32; g obeys
+ * the forward's bound (every entry in [-5, 0]), which the chunk records that
+ * the two state scans read rely on.
+ */
+KDA_API kda_status_t kda_chunk_bwd_f32(const float *q, const float *k, const float *v,
+                               const float *g, const float *beta, float scale,
+                               const float *h0, const float *dout, const float *dhT,
+                               float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                               float *dh0, int B, int T, int H, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);
 

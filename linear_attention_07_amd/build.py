@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "lib", "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk16.hip", "kda_backward.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk16.hip", "kda_backward.hip",
+           "kda_chunk_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

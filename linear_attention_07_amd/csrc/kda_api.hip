@@ -201,6 +201,62 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     return st;
 }
 
+// Backward of the fp32 chunked prefill; see kda_chunk_bwd_f32 in kda.h.
+kda_status_t chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
+                           const float* beta, float scale, const float* h0, const float* dout,
+                           const float* dhT, float* dq, float* dk, float* dv, float* dg,
+                           float* dbeta, float* dh0, int B, int T, int H, hipStream_t stream) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    const size_t sbytes = (size_t)B * H * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
+    const float* states[] = {h0, dhT, dh0};
+    for (const float* p : states)
+        if (p && !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    if (dh0 && (overlap(dh0, sbytes, h0, sbytes) || overlap(dh0, sbytes, dhT, sbytes)))
+        return KDA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    if (T == 0) {  // no tokens: the state gradient passes through
+        if (!dh0) return KDA_OK;
+        const hipError_t e = kda::launch_copy_or_zero(dhT, dh0, sbytes / sizeof(float), stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    const float* ins[] = {q, k, v, g, dout};
+    float* outs[] = {dq, dk, dv, dg};
+    for (const float* p : ins)
+        if (!p || !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    for (const float* p : outs)
+        if (!p || !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    if (!beta || !dbeta || !aligned(beta, 4) || !aligned(dbeta, 4)) return KDA_ERR_INVALID_ARG;
+    const size_t n_tok = (size_t)B * T * H;
+    const size_t vb = n_tok * KDA_HEAD_DIM * sizeof(float), bb = n_tok * sizeof(float);
+    // every written buffer overlaps no other argument
+    struct Buf {
+        const void* p;
+        size_t n;
+    };
+    const Buf all[] = {{q, vb},  {k, vb},  {v, vb},      {g, vb},     {dout, vb},
+                       {beta, bb}, {h0, sbytes}, {dhT, sbytes}, {dq, vb}, {dk, vb},
+                       {dv, vb}, {dg, vb}, {dbeta, bb}, {dh0, sbytes}};
+    const Buf written[] = {{dq, vb}, {dk, vb}, {dv, vb}, {dg, vb}, {dbeta, bb}, {dh0, sbytes}};
+    for (const Buf& w : written)
+        for (const Buf& a : all)
+            if (w.p != a.p && overlap(w.p, w.n, a.p, a.n)) return KDA_ERR_INVALID_ARG;
+    const int nch = (T + 63) / 64;
+    if ((int64_t)B * H * nch > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+
+    hipMemPool_t pool = nullptr;
+    if (pool_for_device(&pool) != hipSuccess) return KDA_ERR_HIP;
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, kda::chunk_bwd_f32_workspace_bytes(B, T, H), pool, stream) !=
+        hipSuccess)
+        return KDA_ERR_NO_MEMORY;
+    const hipError_t e = kda::launch_chunk_bwd_f32(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk,
+                                                   dv, dg, dbeta, dh0, B, T, H, ws, stream);
+    (void)hipFreeAsync(ws, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 // conv != NULL: q, k, v are raw values before the short convolution (bf16 I/O
 // only), and conv->state is advanced by one token in place.
 template <bool F32>
@@ -341,6 +397,15 @@ kda_status_t kda_recurrent_step_f32(const float* q, const float* k, const float*
                                     float* S_inout, float* out, int B, int H,
                                     hipStream_t stream) {
     return recurrent_step<true>(q, k, v, g, beta, scale, S_inout, out, B, H, stream);
+}
+
+kda_status_t kda_chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
+                               const float* beta, float scale, const float* h0,
+                               const float* dout, const float* dhT, float* dq, float* dk,
+                               float* dv, float* dg, float* dbeta, float* dh0, int B, int T,
+                               int H, hipStream_t stream) {
+    return chunk_bwd_f32(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, B,
+                         T, H, stream);
 }
 
 const char* kda_status_string(kda_status_t s) {

@@ -51,16 +51,7 @@ using P = Prec<true>;
 using F8 = P::F8;
 using F4 = P::F4;
 
-// Record of one (batch, head, chunk), fp32.
-struct RecF {
-    static constexpr size_t W = 0;                                      // [64][128] W
-    static constexpr size_t QP = W + kChunk * kD * sizeof(float);       // [64][128] Q'
-    static constexpr size_t KT = QP + kChunk * kD * sizeof(float);      // [128][64] Kb^T
-    static constexpr size_t TH = KT + kD * kChunk * sizeof(float);      // [64][64]  T
-    static constexpr size_t MH = TH + kChunk * kChunk * sizeof(float);  // [64][64]  MT
-    static constexpr size_t G = MH + kChunk * kChunk * sizeof(float);   // [128] gamma
-    static constexpr size_t BYTES = ((G + kD * sizeof(float)) + 255) / 256 * 256;
-};
+using RecF = ChunkRecF32;
 
 constexpr int kScanSlices = 2;          // value-column slices per head
 constexpr int kSliceCols = kD / kScanSlices;

@@ -1,0 +1,664 @@
+// Backward of the chunkwise prefill for fp32 I/O: the gradients of
+// L = <dO, O> + <dS_T, S_T> with respect to q, k, v, g, beta and the initial
+// state, for O, S_T computed by the Kimi Delta Attention recurrence (Kimi-K3
+// 深度解析 blog, section 三; the KDA paragraph of the 深入 Kimi-K3 thread for
+// the in-kernel L2 normalisation and the per-channel decay).  The pages give
+// no backward; this is the reverse-mode derivative of the chunk form written
+// out in kda_chunk.hip, in fp32 arithmetic throughout.
+//
+// Per 64-token chunk entering with state S and leaving with S', with R = V -
+// Kt S, U = T R and the quantities of the chunk form (Kt, Qt, Kb, gamma, the
+// pairwise-decayed products P = strict-lower(kh kh^T decayed) and N =
+// lower-incl(qh kh^T decayed), A = diag(beta) P, X = (I + A)^-1, T = X
+// diag(beta), M = N), the gradients given dO and dS' = dL/dS' are
+//   dU  = scale M^T dO + Kb dS'          dV = dR = T^T dU
+//   dS  = Diag(gamma) dS' - W^T (Kb dS') + scale Q'^T dO      (W = T Kt,
+//                                                   Q' = Qt - M W)
+//   dT  = lower-incl(dU R^T),  dX = dT diag(beta),  dbeta_i += sum_r X_ri dT_ri
+//   dA  = -strict-lower(X^T dX X^T), dbeta_r += sum_i dA_ri P_ri, dP = diag(beta) dA
+//   dM  = scale lower-incl(dO U^T)
+//   dQt = scale dO S^T,  dKt = -dR S^T,  dKb = U dS'^T,  dgamma = rowsum(dS' . S)
+// then through the decay factors into dkh, dqh and the in-chunk cumulative
+// log-decay Gam (whose reverse cumulative sum is dg), and through the L2
+// normalisation into dq, dk.  dS depends on dS' and dO column by column, as S'
+// on S in the forward, so it runs as a scan over chunks in reverse; all other
+// gradients of a chunk follow from S and dS' alone, in parallel over chunks.
+//
+// Four launches:
+//   prep  (kda_chunk.hip) writes each chunk's record (W, Q', Kb^T, T, M T,
+//         gamma);
+//   state scan    walks the chunks forward and stores the state entering each;
+//   gradient scan walks them in reverse and stores dS' of each chunk, and dS
+//         of the first as the initial state's gradient;
+//   chunk gradients, one workgroup per (batch, head, chunk), rebuilds the
+//         chunk's matrices from q, k, g, beta and writes dq, dk, dv, dg, dbeta.
+// Products run on the vector ALUs from LDS and L1/L2-resident operands, each
+// thread owning a fixed micro-tile of the result.
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+
+using RF = ChunkRecF32;
+constexpr int kThreads = 256;
+constexpr int kScanCols = 32;              // value columns per scan workgroup
+constexpr int kScanSlices = kD / kScanCols;
+constexpr size_t kStateFloats = (size_t)kD * kD;
+
+// Scratch of one chunk-gradient workgroup in global memory (floats).
+constexpr size_t kScrR = 0;                       // [64][128] R = V - Kt S
+constexpr size_t kScrU = kScrR + kChunk * kD;     // [64][128] U = T R
+constexpr size_t kScrDU = kScrU + kChunk * kD;    // [64][128] dU
+constexpr size_t kScrDX = kScrDU + kChunk * kD;   // [64][64]  dX
+constexpr size_t kScrY = kScrDX + kChunk * kChunk;  // [64][64] X^T dX
+constexpr size_t kScrFloats = kScrY + kChunk * kChunk;
+
+__device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// C[M][N] = sum_k A(i, k) B(k, j) for k < K.  Thread t owns rows
+// i0 .. i0 + TM - 1 (i0 = TM (t / (N / TN))) and columns ct + (N / TN) n,
+// n < TN (ct = t mod N / TN), so neighbouring threads read neighbouring
+// columns of B and threads of one row group share each A value.  Each result
+// goes to out(m, n, i, j, value).
+template <int M, int N, int TM, int TN, class FA, class FB, class FO>
+__device__ __forceinline__ void mm(int K, FA&& A, FB&& B, FO&& out) {
+    constexpr int CT = N / TN;
+    static_assert((M / TM) * CT == kThreads, "micro-tiles must cover the result once");
+    const int t = threadIdx.x;
+    const int i0 = (t / CT) * TM, ct = t % CT;
+    float acc[TM][TN];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
+#pragma unroll 2
+    for (int kk = 0; kk < K; ++kk) {
+        float a[TM], b[TN];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) a[m] = A(i0 + m, kk);
+#pragma unroll
+        for (int n = 0; n < TN; ++n) b[n] = B(kk, ct + CT * n);
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) acc[m][n] = fmaf(a[m], b[n], acc[m][n]);
+    }
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) out(m, n, i0 + m, ct + CT * n, acc[m][n]);
+}
+
+__device__ __forceinline__ void scan_ids(int& bh, int& slice) {
+    // all slices of one head on one XCD (workgroups are dealt round-robin to
+    // the 8 XCDs), so the records they share come from HBM once
+    const int nb = gridDim.x;
+    const int id = blockIdx.x;
+    if (nb % (8 * kScanSlices) == 0) {
+        const int xcd = id % 8, j = id / 8;
+        const int per = nb / 8;  // workgroups per XCD, a multiple of kScanSlices
+        const int w = xcd * per + j;
+        bh = w / kScanSlices;
+        slice = w % kScanSlices;
+    } else {
+        bh = id / kScanSlices;
+        slice = id % kScanSlices;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// State scan: one workgroup per (b, h, 32 value columns).  For chunk c the
+// state slice entering it is stored, then S <- Diag(gamma) S + Kb^T (T V - W S).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void kda_bwd_state_scan_kernel(
+    const uint8_t* __restrict__ rec, const float* __restrict__ v, const float* __restrict__ h0,
+    float* __restrict__ states, int T, int H, int nch) {
+    __shared__ float s_S[kD][kScanCols];
+    __shared__ float s_Z[kChunk][kScanCols];
+    int bh, slice;
+    scan_ids(bh, slice);
+    const int b = bh / H, h = bh % H;
+    const int col0 = slice * kScanCols;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < kD * kScanCols; e += kThreads) {
+        const int i = e / kScanCols, j = e % kScanCols;
+        s_S[i][j] = h0 ? h0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
+        const float* W = reinterpret_cast<const float*>(r + RF::W);
+        const float* KT = reinterpret_cast<const float*>(r + RF::KT);
+        const float* Tm = reinterpret_cast<const float*>(r + RF::TH);
+        const float* gam = reinterpret_cast<const float*>(r + RF::G);
+        float* st = states + ((size_t)bh * nch + c) * kStateFloats;
+        for (int e = tid; e < kD * kScanCols; e += kThreads) {
+            const int i = e / kScanCols, j = e % kScanCols;
+            st[(size_t)i * kD + col0 + j] = s_S[i][j];
+        }
+        const int L = min(kChunk, T - c * kChunk);
+        const float* vc = v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+        const size_t vp = (size_t)H * kD;
+        // Z = T V - W S
+        mm<kChunk, kScanCols, 2, 4>(
+            kChunk + kD,
+            [&](int i, int k) {
+                return k < kChunk ? Tm[i * kChunk + k] : -W[i * kD + (k - kChunk)];
+            },
+            [&](int k, int j) {
+                return k < kChunk ? (k < L ? vc[(size_t)k * vp + j] : 0.f) : s_S[k - kChunk][j];
+            },
+            [&](int, int, int i, int j, float a) { s_Z[i][j] = a; });
+        __syncthreads();
+        // S' = Diag(gamma) S + Kb^T Z (each thread updates only its own entries)
+        mm<kD, kScanCols, 4, 4>(
+            kChunk, [&](int i, int k) { return KT[i * kChunk + k]; },
+            [&](int k, int j) { return s_Z[k][j]; },
+            [&](int, int, int i, int j, float a) { s_S[i][j] = fmaf(gam[i], s_S[i][j], a); });
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gradient scan: chunks in reverse.  For chunk c, dS' (the gradient of the
+// state leaving it) is stored, then
+//   dS <- Diag(gamma) dS' - W^T (Kb dS') + scale Q'^T dO.
+// After chunk 0, dS is the initial state's gradient.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void kda_bwd_grad_scan_kernel(
+    const uint8_t* __restrict__ rec, const float* __restrict__ dout,
+    const float* __restrict__ dhT, float* __restrict__ dsn, float* __restrict__ dh0,
+    float scale, int T, int H, int nch) {
+    __shared__ float s_D[kD][kScanCols];
+    __shared__ float s_Y[kChunk][kScanCols];
+    int bh, slice;
+    scan_ids(bh, slice);
+    const int b = bh / H, h = bh % H;
+    const int col0 = slice * kScanCols;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < kD * kScanCols; e += kThreads) {
+        const int i = e / kScanCols, j = e % kScanCols;
+        s_D[i][j] = dhT ? dhT[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int c = nch - 1; c >= 0; --c) {
+        const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
+        const float* W = reinterpret_cast<const float*>(r + RF::W);
+        const float* QP = reinterpret_cast<const float*>(r + RF::QP);
+        const float* KT = reinterpret_cast<const float*>(r + RF::KT);
+        const float* gam = reinterpret_cast<const float*>(r + RF::G);
+        float* st = dsn + ((size_t)bh * nch + c) * kStateFloats;
+        for (int e = tid; e < kD * kScanCols; e += kThreads) {
+            const int i = e / kScanCols, j = e % kScanCols;
+            st[(size_t)i * kD + col0 + j] = s_D[i][j];
+        }
+        const int L = min(kChunk, T - c * kChunk);
+        const float* oc = dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+        const size_t op = (size_t)H * kD;
+        // Y = Kb dS'   (Kb[i][k] = Kb^T[k][i])
+        mm<kChunk, kScanCols, 2, 4>(
+            kD, [&](int i, int k) { return KT[k * kChunk + i]; },
+            [&](int k, int j) { return s_D[k][j]; },
+            [&](int, int, int i, int j, float a) { s_Y[i][j] = a; });
+        __syncthreads();
+        // dS = Diag(gamma) dS' - W^T Y + scale Q'^T dO
+        mm<kD, kScanCols, 4, 4>(
+            2 * kChunk,
+            [&](int i, int k) {
+                return k < kChunk ? -W[k * kD + i] : scale * QP[(k - kChunk) * kD + i];
+            },
+            [&](int k, int j) {
+                return k < kChunk ? s_Y[k][j]
+                                  : (k - kChunk < L ? oc[(size_t)(k - kChunk) * op + j] : 0.f);
+            },
+            [&](int, int, int i, int j, float a) { s_D[i][j] = fmaf(gam[i], s_D[i][j], a); });
+        __syncthreads();
+    }
+    if (dh0)
+        for (int e = tid; e < kD * kScanCols; e += kThreads) {
+            const int i = e / kScanCols, j = e % kScanCols;
+            dh0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] = s_D[i][j];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk gradients: one workgroup per (b, h, chunk).  Results over [64][128]
+// (token row x channel) use the micro-tile of mm<64, 128, 8, 4>: thread t owns
+// rows 8 (t / 32) + m and channels t % 32 + 32 n, and keeps its share of dkh,
+// dqh and dGam in registers from the first contribution to the last.
+// ---------------------------------------------------------------------------
+struct BwdLds {
+    float gam[kChunk][kD];  // Gam (cumulative log-decay), later dGam
+    float kh[kChunk][kD];
+    float qh[kChunk][kD];
+    float p[kChunk][kChunk];  // P, later dP
+    float n[kChunk][kChunk];  // N (= M), later dM
+    float x[kChunk][kChunk];  // X = (I + A)^-1
+    float beta[kChunk];
+    float rq[kChunk];
+    float rk[kChunk];
+    float dbeta[kChunk];
+    float dotq[kChunk];
+    float dotk[kChunk];
+    float gl[kD];    // Gam of the chunk's last row
+    float dlast[kD];  // gamma dgamma, the extra dGam of the last row besides sum_r Kb dKb
+    float red[1024];  // per-thread partial sums, reduced in a fixed order (deterministic)
+};
+
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ dout,
+    const float* __restrict__ states, const float* __restrict__ dsn, float* __restrict__ scr_all,
+    float scale, int T, int H, int nch, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
+    __shared__ BwdLds s;
+
+    const int c = blockIdx.x % nch;
+    const int bh = blockIdx.x / nch;
+    const int b = bh / H, h = bh % H;
+    const int L = min(kChunk, T - c * kChunk);
+    const int tid = threadIdx.x;
+    const size_t rp = (size_t)H * kD;  // pitch of one token row
+    const size_t base = (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD;
+    const float* S = states + ((size_t)bh * nch + c) * kStateFloats;
+    const float* dSn = dsn + ((size_t)bh * nch + c) * kStateFloats;
+    float* scr = scr_all + (size_t)blockIdx.x * kScrFloats;
+    float* R_ = scr + kScrR;
+    float* U_ = scr + kScrU;
+    float* dU_ = scr + kScrDU;
+    float* dX_ = scr + kScrDX;
+    float* Y_ = scr + kScrY;
+    auto in = [&](const float* p, int r, int col) {
+        return r < L ? p[base + (size_t)r * rp + col] : 0.f;
+    };
+
+    // ---- load: normalised q, k (4 threads per row, 32 channels each), g ---
+    {
+        const int r = tid >> 2, part = tid & 3;
+        float sq = 0.f, sk = 0.f;
+        for (int e = 0; e < 32; ++e) {
+            const int col = 32 * part + e;
+            const float qv = in(q, r, col), kv = in(k, r, col);
+            sq = fmaf(qv, qv, sq);
+            sk = fmaf(kv, kv, sk);
+            s.qh[r][col] = qv;
+            s.kh[r][col] = kv;
+            s.gam[r][col] = in(g, r, col);
+        }
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+        sk += __shfl_xor(sk, 1);
+        sk += __shfl_xor(sk, 2);
+        const float rq = 1.f / sqrtf(sq + kNormEps), rk = 1.f / sqrtf(sk + kNormEps);
+        for (int e = 0; e < 32; ++e) {
+            const int col = 32 * part + e;
+            s.qh[r][col] *= rq;
+            s.kh[r][col] *= rk;
+        }
+        if (part == 0) {
+            s.rq[r] = rq;
+            s.rk[r] = rk;
+            s.beta[r] = r < L ? beta[((size_t)b * T + (size_t)c * kChunk + r) * H + h] : 0.f;
+            s.dbeta[r] = 0.f;
+            s.dotq[r] = 0.f;
+            s.dotk[r] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (tid < kD) {  // Gam = cumulative sum of g down the chunk, per channel
+        float a = 0.f;
+        for (int r = 0; r < kChunk; ++r) {
+            a += s.gam[r][tid];
+            s.gam[r][tid] = a;
+        }
+        s.gl[tid] = a;
+    } else {  // dgamma = rowsum(dS' . S), kept times gamma for the last row of dGam
+        const int row = tid - kD;
+        float d = 0.f;
+        for (int j = 0; j < kD; ++j) d = fmaf(dSn[(size_t)row * kD + j], S[(size_t)row * kD + j], d);
+        s.dlast[row] = d;
+    }
+    __syncthreads();
+    if (tid < kD) s.dlast[tid] *= ex(s.gl[tid]);
+
+    // ---- P (strict lower) and N (lower incl) with the exact pairwise decays ---
+    {
+        constexpr int CT = 16, TM = 4, TN = 4;
+        const int i0 = (tid / CT) * TM, ct = tid % CT;
+        float ap[TM][TN] = {}, an[TM][TN] = {};
+        for (int cc = 0; cc < kD; ++cc) {
+            float kr[TM], qr[TM], gr[TM], ki[TN], gi[TN];
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+                kr[m] = s.kh[i0 + m][cc];
+                qr[m] = s.qh[i0 + m][cc];
+                gr[m] = s.gam[i0 + m][cc];
+            }
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                ki[n] = s.kh[ct + CT * n][cc];
+                gi[n] = s.gam[ct + CT * n][cc];
+            }
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int n = 0; n < TN; ++n) {
+                    const float e =
+                        ct + CT * n <= i0 + m ? ex(gr[m] - gi[n]) * ki[n] : 0.f;
+                    ap[m][n] = fmaf(kr[m], e, ap[m][n]);
+                    an[m][n] = fmaf(qr[m], e, an[m][n]);
+                }
+        }
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                const int r = i0 + m, i = ct + CT * n;
+                s.p[r][i] = i < r ? ap[m][n] : 0.f;
+                s.n[r][i] = i <= r ? an[m][n] : 0.f;
+            }
+    }
+    __syncthreads();
+    // ---- X = (I + A)^-1, A = diag(beta) P, by forward substitution per column
+    if (tid < kChunk) {
+        const int j = tid;
+        for (int r = 0; r < kChunk; ++r) {
+            float a = (r == j) ? 1.f : 0.f;
+            if (r > j) {
+                for (int i = j; i < r; ++i) a = fmaf(-s.beta[r] * s.p[r][i], s.x[i][j], a);
+            }
+            s.x[r][j] = r >= j ? a : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- R = V - Kt S --------------------------------------------------------
+    mm<kChunk, kD, 8, 4>(
+        kD, [&](int i, int kk) { return ex(s.gam[i][kk]) * s.kh[i][kk]; },
+        [&](int kk, int j) { return S[(size_t)kk * kD + j]; },
+        [&](int, int, int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
+    __syncthreads();
+    // ---- U = T R,  T = X diag(beta) ------------------------------------------
+    mm<kChunk, kD, 8, 4>(
+        kChunk, [&](int i, int kk) { return s.x[i][kk] * s.beta[kk]; },
+        [&](int kk, int j) { return R_[kk * kD + j]; },
+        [&](int, int, int i, int j, float a) { U_[i * kD + j] = a; });
+    __syncthreads();
+    // ---- dU = scale M^T dO + Kb dS' ------------------------------------------
+    mm<kChunk, kD, 8, 4>(
+        kChunk + kD,
+        [&](int i, int kk) {
+            return kk < kChunk ? scale * s.n[kk][i]
+                               : ex(s.gl[kk - kChunk] - s.gam[i][kk - kChunk]) *
+                                     s.kh[i][kk - kChunk];
+        },
+        [&](int kk, int j) {
+            return kk < kChunk ? in(dout, kk, j) : dSn[(size_t)(kk - kChunk) * kD + j];
+        },
+        [&](int, int, int i, int j, float a) { dU_[i * kD + j] = a; });
+    __syncthreads();
+    // ---- dV = dR = T^T dU ----------------------------------------------------
+    mm<kChunk, kD, 8, 4>(
+        kChunk, [&](int i, int kk) { return s.x[kk][i] * s.beta[i]; },
+        [&](int kk, int j) { return dU_[kk * kD + j]; },
+        [&](int, int, int i, int j, float a) {
+            if (i < L) dv[base + (size_t)i * rp + j] = a;
+        });
+    // ---- dX = lower-incl(dU R^T) diag(beta); dbeta_j += sum_i X_ij dT_ij ------
+    {
+        float pb[4] = {0.f, 0.f, 0.f, 0.f};
+        mm<kChunk, kChunk, 4, 4>(
+            kD, [&](int i, int kk) { return dU_[i * kD + kk]; },
+            [&](int kk, int j) { return R_[j * kD + kk]; },
+            [&](int, int n, int i, int j, float a) {
+                const float dt = j <= i ? a : 0.f;
+                dX_[i * kChunk + j] = dt * s.beta[j];
+                pb[n] = fmaf(s.x[i][j], dt, pb[n]);
+            });
+#pragma unroll
+        for (int n = 0; n < 4; ++n) s.red[(tid / 16) * kChunk + tid % 16 + 16 * n] = pb[n];
+    }
+    __syncthreads();
+    if (tid < kChunk) {
+        float a = 0.f;
+        for (int rg = 0; rg < 16; ++rg) a += s.red[rg * kChunk + tid];
+        s.dbeta[tid] = a;
+    }
+    // ---- dM = scale lower-incl(dO U^T), over N ---------------------------------
+    mm<kChunk, kChunk, 4, 4>(
+        kD, [&](int i, int kk) { return in(dout, i, kk); },
+        [&](int kk, int j) { return U_[j * kD + kk]; },
+        [&](int, int, int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
+    // ---- Y = X^T dX ------------------------------------------------------------
+    mm<kChunk, kChunk, 4, 4>(
+        kChunk, [&](int i, int kk) { return s.x[kk][i]; },
+        [&](int kk, int j) { return dX_[kk * kChunk + j]; },
+        [&](int, int, int i, int j, float a) { Y_[i * kChunk + j] = a; });
+    __syncthreads();
+    // ---- dA = -strict-lower(Y X^T); dbeta_i += sum_j dA_ij P_ij; dP over P ----
+    {
+        float pr[4] = {0.f, 0.f, 0.f, 0.f};
+        mm<kChunk, kChunk, 4, 4>(
+            kChunk, [&](int i, int kk) { return Y_[i * kChunk + kk]; },
+            [&](int kk, int j) { return s.x[j][kk]; },
+            [&](int m, int, int i, int j, float a) {
+                const float da = j < i ? -a : 0.f;
+                pr[m] = fmaf(da, s.p[i][j], pr[m]);
+                s.p[i][j] = s.beta[i] * da;
+            });
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s.red[(tid % 16) * kChunk + (tid / 16) * 4 + m] = pr[m];
+    }
+    __syncthreads();
+    if (tid < kChunk) {
+        float a = s.dbeta[tid];
+        for (int ct = 0; ct < 16; ++ct) a += s.red[ct * kChunk + tid];
+        s.dbeta[tid] = a;
+    }
+
+    // ---- per-element accumulators of dkh, dqh, dGam (micro-tile 8 x 4) -------
+    const int i0 = (tid / 32) * 8, ct = tid % 32;
+    float dkh[8][4], dqh[8][4], dgm[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dkh[m][n] = dqh[m][n] = dgm[m][n] = 0.f;
+
+    // dQt = scale dO S^T:  dqh += e^Gam dQt,  dGam += Qt dQt
+    mm<kChunk, kD, 8, 4>(
+        kD, [&](int i, int kk) { return in(dout, i, kk); },
+        [&](int kk, int j) { return S[(size_t)j * kD + kk]; },
+        [&](int m, int n, int i, int j, float a) {
+            const float d = scale * a, e = ex(s.gam[i][j]);
+            dqh[m][n] = fmaf(e, d, dqh[m][n]);
+            dgm[m][n] = fmaf(e * s.qh[i][j], d, dgm[m][n]);
+        });
+    // dKt = -dR S^T:  dkh += e^Gam dKt,  dGam += Kt dKt
+    mm<kChunk, kD, 8, 4>(
+        kD, [&](int i, int kk) { return i < L ? -dv[base + (size_t)i * rp + kk] : 0.f; },
+        [&](int kk, int j) { return S[(size_t)j * kD + kk]; },
+        [&](int m, int n, int i, int j, float a) {
+            const float e = ex(s.gam[i][j]);
+            dkh[m][n] = fmaf(e, a, dkh[m][n]);
+            dgm[m][n] = fmaf(e * s.kh[i][j], a, dgm[m][n]);
+        });
+    // dKb = U dS'^T:  dkh += e^(GL - Gam) dKb,  dGam -= Kb dKb, last row += Kb dKb
+    __syncthreads();  // the dbeta reduction has read red
+    {
+        float pl[4] = {0.f, 0.f, 0.f, 0.f};
+        mm<kChunk, kD, 8, 4>(
+            kD, [&](int i, int kk) { return U_[i * kD + kk]; },
+            [&](int kk, int j) { return dSn[(size_t)j * kD + kk]; },
+            [&](int m, int n, int i, int j, float a) {
+                const float e = ex(s.gl[j] - s.gam[i][j]);
+                const float t = e * s.kh[i][j] * a;
+                dkh[m][n] = fmaf(e, a, dkh[m][n]);
+                dgm[m][n] -= t;
+                pl[n] += t;
+            });
+#pragma unroll
+        for (int n = 0; n < 4; ++n) s.red[(tid / 32) * kD + ct + 32 * n] = pl[n];
+    }
+
+    // ---- the pairwise-decay terms of P and N ---------------------------------
+    // row side:  a_rc = sum_i dP_ri E_ric kh_ic,  b_rc = sum_i dN_ri E_ric kh_ic
+    // column side: c_ic = sum_r (dP_ri kh_rc + dN_ri qh_rc) E_ric
+    // with E_ric = exp(Gam_rc - Gam_ic) (i <= r); then dkh += a + c, dqh += b,
+    // dGam += kh a + qh b - kh c.
+    {
+        float gown[8][4];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) gown[m][n] = s.gam[i0 + m][ct + 32 * n];
+        float ta[8][4], tb[8][4];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) ta[m][n] = tb[m][n] = 0.f;
+        for (int i = 0; i < kChunk; ++i) {
+            float ki[4], gi[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                ki[n] = s.kh[i][ct + 32 * n];
+                gi[n] = s.gam[i][ct + 32 * n];
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float dp = s.p[i0 + m][i], dn = s.n[i0 + m][i];
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    const float w = i <= i0 + m ? ex(gown[m][n] - gi[n]) * ki[n] : 0.f;
+                    ta[m][n] = fmaf(dp, w, ta[m][n]);
+                    tb[m][n] = fmaf(dn, w, tb[m][n]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const float khv = s.kh[i0 + m][ct + 32 * n], qhv = s.qh[i0 + m][ct + 32 * n];
+                dkh[m][n] += ta[m][n];
+                dqh[m][n] += tb[m][n];
+                dgm[m][n] = fmaf(khv, ta[m][n], fmaf(qhv, tb[m][n], dgm[m][n]));
+                ta[m][n] = 0.f;
+            }
+        for (int r = 0; r < kChunk; ++r) {
+            float kr[4], qr[4], gr[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                kr[n] = s.kh[r][ct + 32 * n];
+                qr[n] = s.qh[r][ct + 32 * n];
+                gr[n] = s.gam[r][ct + 32 * n];
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float dp = s.p[r][i0 + m], dn = s.n[r][i0 + m];
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    const float e = r >= i0 + m ? ex(gr[n] - gown[m][n]) : 0.f;
+                    ta[m][n] = fmaf(fmaf(dp, kr[n], dn * qr[n]), e, ta[m][n]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const float khv = s.kh[i0 + m][ct + 32 * n];
+                dkh[m][n] += ta[m][n];
+                dgm[m][n] = fmaf(-khv, ta[m][n], dgm[m][n]);
+            }
+    }
+    __syncthreads();  // every read of Gam is done: its space takes dGam
+
+    // ---- dg = reverse cumulative sum of dGam; the norms' backward -------------
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) s.gam[i0 + m][ct + 32 * n] = dgm[m][n];
+    {
+        // row dots qh . dqh and kh . dkh: 32 threads of a row group share a row
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            float aq = 0.f, ak = 0.f;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                aq = fmaf(s.qh[i0 + m][ct + 32 * n], dqh[m][n], aq);
+                ak = fmaf(s.kh[i0 + m][ct + 32 * n], dkh[m][n], ak);
+            }
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                aq += __shfl_xor(aq, o);
+                ak += __shfl_xor(ak, o);
+            }
+            if (ct == 0) {
+                s.dotq[i0 + m] = aq;
+                s.dotk[i0 + m] = ak;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int r = i0 + m;
+        if (r >= L) continue;
+        const float rq = s.rq[r], rk = s.rk[r], dtq = s.dotq[r], dtk = s.dotk[r];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int j = ct + 32 * n;
+            // qh = q / sqrt(|q|^2 + eps): dq = rq (dqh - qh (qh . dqh))
+            dq[base + (size_t)r * rp + j] = rq * fmaf(-s.qh[r][j], dtq, dqh[m][n]);
+            dk[base + (size_t)r * rp + j] = rk * fmaf(-s.kh[r][j], dtk, dkh[m][n]);
+        }
+    }
+    if (tid < kD) {
+        float a = s.dlast[tid];  // Gam of the last row also enters Kb and gamma
+        for (int rg = 0; rg < 8; ++rg) a += s.red[rg * kD + tid];
+        for (int r = kChunk - 1; r >= 0; --r) {
+            a += s.gam[r][tid];
+            if (r < L) dg[base + (size_t)r * rp + tid] = a;
+        }
+    } else if (tid < kD + kChunk) {
+        const int r = tid - kD;
+        if (r < L) dbeta[((size_t)b * T + (size_t)c * kChunk + r) * H + h] = s.dbeta[r];
+    }
+}
+
+}  // namespace
+
+size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H) {
+    const size_t nch = (size_t)(T + kChunk - 1) / kChunk;
+    const size_t n = (size_t)B * H * nch;
+    return n * (RF::BYTES + 2 * kStateFloats * sizeof(float) + kScrFloats * sizeof(float));
+}
+
+hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
+                                const float* beta, float scale, const float* h0,
+                                const float* dout, const float* dhT, float* dq, float* dk,
+                                float* dv, float* dg, float* dbeta, float* dh0, int B, int T,
+                                int H, void* ws, hipStream_t stream) {
+    const int nch = (T + kChunk - 1) / kChunk;
+    const size_t n = (size_t)B * H * nch;
+    uint8_t* rec = static_cast<uint8_t*>(ws);
+    float* states = reinterpret_cast<float*>(rec + n * RF::BYTES);
+    float* dsn = states + n * kStateFloats;
+    float* scr = dsn + n * kStateFloats;
+    hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, 0, nch, rec, stream);
+    if (e != hipSuccess) return e;
+    const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
+    hipLaunchKernelGGL(kda_bwd_state_scan_kernel, dim3(nscan), dim3(kThreads), 0, stream, rec, v,
+                       h0, states, T, H, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel, dim3(nscan), dim3(kThreads), 0, stream, rec,
+                       dout, dhT, dsn, dh0, scale, T, H, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)n), dim3(kThreads), 0,
+                       stream, q, k, v, g, beta, dout, states, dsn, scr, scale, T, H, nch, dq, dk,
+                       dv, dg, dbeta);
+    return hipGetLastError();
+}
+
+}  // namespace kda

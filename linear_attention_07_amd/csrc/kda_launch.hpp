@@ -34,12 +34,34 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 // writes out and, if h_out is not NULL, the final state.
 size_t chunk_f32_record_bytes();
 int chunk_f32_slices();
+// Byte offsets inside one fp32 record (64-token chunks, 128 channels).
+struct ChunkRecF32 {
+    static constexpr size_t W = 0;                          // [64][128] W = T Kt
+    static constexpr size_t QP = W + 64 * 128 * 4;          // [64][128] Q' = Qt - M W
+    static constexpr size_t KT = QP + 64 * 128 * 4;         // [128][64] Kb^T
+    static constexpr size_t TH = KT + 128 * 64 * 4;         // [64][64]  T
+    static constexpr size_t MH = TH + 64 * 64 * 4;          // [64][64]  M T
+    static constexpr size_t G = MH + 64 * 64 * 4;           // [128] gamma
+    static constexpr size_t BYTES = ((G + 128 * 4) + 255) / 256 * 256;
+};
 hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
                                  const float* beta, int B, int T, int H, int chunk0, int nchunks,
                                  void* ws, hipStream_t stream);
 hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
                                  float* out, float scale, int B, int T, int H, int chunk0,
                                  int nchunks, hipStream_t stream);
+
+// Backward of the fp32 chunked prefill: prep records, a forward scan storing
+// the state entering each chunk, a reverse scan storing the state gradient
+// leaving each chunk (and dh0), and one gradient workgroup per chunk.  ws
+// holds chunk_bwd_f32_workspace_bytes(B, T, H) bytes.  h0, dhT: NULL = zeros;
+// dh0: NULL = not stored.
+size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H);
+hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
+                                const float* beta, float scale, const float* h0,
+                                const float* dout, const float* dhT, float* dq, float* dk,
+                                float* dv, float* dg, float* dbeta, float* dh0, int B, int T,
+                                int H, void* ws, hipStream_t stream);
 
 // Short convolution in front of the attention: depthwise 4-tap causal filter
 // per head and channel, then SiLU, on q, k and v.  wq == NULL: none.  state:

@@ -1,0 +1,126 @@
+"""GPU parity of kda_chunk_bwd_f32 (backward of the fp32 chunked prefill)
+against the fp64 oracle's chunk_backward, which is pinned to the step backward
+chained token by token (itself pinned to central differences of the forward).
+
+fp32 arithmetic throughout, fp32 I/O: the bar is the fp32-mode one, 1e-3
+normalised max error per gradient (max |gpu - oracle| / max |oracle|).  Cases
+span several chunks with a ragged last one, strong and mild decays, a nonzero
+initial state and final-state gradient, one-token and empty sequences."""
+import numpy as np
+import pytest
+import torch
+
+from kda_check import host64, say
+from linear_attention_07_amd import libkda, synth
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-3
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def rel(x, ref):
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    den = np.abs(ref).max()
+    return float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
+
+
+def inputs(B, T, H, seed, g_shift=4.0, h0_std=0.1, dhT_std=0.1):
+    x = synth.prefill_inputs(B, T, H, torch.float32, seed=seed, g_shift=g_shift, h0_std=h0_std,
+                             device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(seed + 7)
+    x["dout"] = torch.randn((B, T, H, 128), generator=gen, device=DEV)
+    x["dhT"] = (dhT_std * torch.randn((B, H, 128, 128), generator=gen, device=DEV)
+                if dhT_std > 0 else None)
+    return x
+
+
+def gpu(x):
+    r = libkda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["dout"],
+                         h0=x["h0"], dhT=x["dhT"])
+    torch.cuda.synchronize()
+    return r
+
+
+def ref(x):
+    h = lambda t: None if t is None else host64(t)
+    return oracle.chunk_backward(h(x["q"]), h(x["k"]), h(x["v"]), h(x["g"]), h(x["beta"]),
+                                 x["scale"], h(x["h0"]), h(x["dout"]), h(x["dhT"]))
+
+
+def check(x, label):
+    got = gpu(x)
+    want = ref(x)
+    errs = {n: rel(host64(a), b) for n, a, b in zip(NAMES, got, want)}
+    say(f"chunk bwd {label}: " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+    for n, a in zip(NAMES, got):
+        assert torch.isfinite(a).all(), n
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)
+
+
+@pytest.mark.parametrize("B,T,H,g_shift", [(1, 64, 1, 4.0), (1, 100, 2, 4.0), (2, 200, 3, 0.0),
+                                           (1, 1, 1, 4.0), (1, 65, 1, -2.0)])
+def test_chunk_bwd_against_oracle(B, T, H, g_shift):
+    say(f"chunk bwd case B={B} T={T} H={H} g_shift={g_shift}")
+    check(inputs(B, T, H, seed=900 + T + H, g_shift=g_shift), f"B={B} T={T} H={H} "
+          f"g_shift={g_shift}")
+
+
+def test_chunk_bwd_zero_state_and_no_final_gradient():
+    x = inputs(1, 130, 2, seed=931, h0_std=0.0, dhT_std=0.0)
+    assert x["h0"] is None and x["dhT"] is None
+    check(x, "h0 = dhT = 0")
+
+
+def test_chunk_bwd_long_sequence():
+    """4096 tokens (64 chunks) over 4 heads: the two state scans carry the
+    state and its gradient across every chunk boundary."""
+    say("chunk bwd case B=1 T=4096 H=4")
+    check(inputs(1, 4096, 4, seed=977, g_shift=2.0), "B=1 T=4096 H=4")
+
+
+def test_chunk_bwd_empty_sequence_passes_the_state_gradient():
+    x = inputs(2, 0, 3, seed=5)
+    dq, dk, dv, dg, dbeta, dh0 = gpu(x)
+    assert dq.numel() == 0 and dbeta.numel() == 0
+    assert torch.equal(dh0, x["dhT"])
+
+
+def test_chunk_bwd_matches_chained_step_backward_on_gpu():
+    """The chunkwise backward equals the GPU's own step backward chained over
+    the states of the GPU's recurrent steps (two independent kernels)."""
+    B, T, H = 1, 80, 2
+    x = inputs(B, T, H, seed=951)
+    got = gpu(x)
+    S = x["h0"].clone()
+    states = []
+    for t in range(T):
+        states.append(S.clone())
+        out = torch.empty((B, H, 128), device=DEV)
+        libkda.recurrent_step(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                              x["v"][:, t].contiguous(), x["g"][:, t].contiguous(),
+                              x["beta"][:, t].contiguous(), x["scale"], S, out=out)
+    dS = x["dhT"].clone()
+    want = [torch.empty_like(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    for t in reversed(range(T)):
+        r = libkda.recurrent_step_bwd(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                                      x["v"][:, t].contiguous(), x["g"][:, t].contiguous(),
+                                      x["beta"][:, t].contiguous(), x["scale"], states[t],
+                                      x["dout"][:, t].contiguous(), dS)
+        for j in range(5):
+            want[j][:, t] = r[j]
+    torch.cuda.synchronize()
+    for n, a, b in zip(NAMES, got, (*want, dS)):
+        e = rel(host64(a), host64(b))
+        say(f"chunk bwd vs chained steps {n}: {e:.1e}")
+        assert e <= TOL, (n, e)
+
+
+def test_chunk_bwd_deterministic():
+    x = inputs(1, 150, 2, seed=961)
+    a = gpu(x)
+    b = gpu(x)
+    for n, u, w in zip(NAMES, a, b):
+        assert torch.equal(u, w), n
