@@ -48,6 +48,18 @@ GATE_BYTES_PER_TOKEN_HEAD = 128 * 2
 # step and the state gradient read, the state gradient written; q, k, v, g,
 # dout read and dq, dk, dv, dg written (fp32); beta read, dbeta written
 BWD_STEP_BYTES_PER_SEQ_HEAD = 3 * STATE_BYTES + 9 * 128 * 4 + 2 * 4
+# backward of the fp32 chunked prefill (kda_chunk_bwd_f32), algorithmic work
+# per 64-token chunk and head, in units of one 64x64x128 product (MACs):
+# record prep 4.5 (W, the two decayed key products, M W, M T); state scan 5
+# (T V - W S, Kb^T Z); gradient scan 6 (Kb dS', W^T Y + Q'^T dO); chunk
+# gradients 22 (P and N 2, R 2, U 1, dU 3, dR 1, dT 1, dM 1, X^T dX and
+# its product with X^T 1, dQt dKt dKb 6, the pairwise-decay terms 4)
+BWD_CHUNK_FLOP_PER_CHUNK_HEAD = int(2 * 37.5 * 64 * 64 * 128)
+# its algorithmic HBM bytes per token-head: q, k, v, g, dout read and dq, dk,
+# dv, dg written (fp32), beta read and dbeta written; per head h0 and dhT
+# read, dh0 written
+BWD_CHUNK_BYTES_PER_TOKEN_HEAD = 9 * 128 * 4 + 2 * 4
+FP32_VALU_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -285,6 +297,27 @@ def main():
           file=sys.stderr, flush=True)
     del xb, Sp, dSb, dob
 
+    # ---- backward of the fp32 chunked prefill --------------------------------
+    wb = synth.WORKLOADS["prefill_bwd_8k"]
+    xb = synth.prefill_inputs(wb.B, wb.T, wb.H, torch.float32, seed=wb.seed, g_shift=wb.g_shift,
+                              h0_std=wb.h0_std, device=dev)
+    gb = torch.Generator(device=dev).manual_seed(wb.seed + 1)
+    xb["dout"] = torch.randn((wb.B, wb.T, wb.H, 128), generator=gb, device=dev)
+    xb["dhT"] = 0.1 * torch.randn((wb.B, wb.H, 128, 128), generator=gb, device=dev)
+
+    def prefill_bwd():
+        libkda.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
+                         xb["dout"], h0=xb["h0"], dhT=xb["dhT"])
+
+    pbms, pbms_med, pbms_min = time_op(torch, prefill_bwd, max(3, args.steps // 4), args.warmup)
+    pb_chunks = wb.B * wb.H * ((wb.T + 63) // 64)
+    pb_flop = pb_chunks * BWD_CHUNK_FLOP_PER_CHUNK_HEAD
+    pb_tflops = pb_flop / (pbms / 1e3) / 1e12
+    pb_bytes = wb.B * wb.T * wb.H * BWD_CHUNK_BYTES_PER_TOKEN_HEAD + 3 * wb.B * wb.H * STATE_BYTES
+    print(f"# prefill backward (fp32): {pbms:.3f} ms/call, {pb_tflops:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    del xb
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -397,6 +430,26 @@ def main():
                 "unit": "GB/s",
                 "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_call": bwd_bytes,
+            },
+        },
+        "prefill_bwd": {
+            "workload": f"prefill_bwd_8k: backward of one fp32 KDA layer prefill, B={wb.B} "
+                        f"H={wb.H} T={wb.T} d=128, h0 and dhT ~ N(0, 0.1^2), dout ~ N(0, 1) "
+                        "(kda_chunk_bwd_f32: gradients of q, k, v, g, beta and h0)",
+            "ms_per_step": round(pbms, 4),
+            "ms_per_step_median": round(pbms_med, 4),
+            "ms_per_step_min": round(pbms_min, 4),
+            "Mtok_s": round(wb.B * wb.T / (pbms / 1e3) / 1e6, 3),
+            "roofline": {
+                "bound": "alu",
+                "kernel": "kda_chunk_bwd_f32 (prep, two state scans, chunk gradients; one call)",
+                "achieved": round(pb_tflops, 2),
+                "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(pb_tflops / FP32_VALU_PEAK_TFLOPS, 4),
+                "algorithmic_flop_per_call": pb_flop,
+                "algorithmic_bytes_per_call": pb_bytes,
+                "hbm_GBps_algorithmic": round(pb_bytes / (pbms / 1e3) / 1e9, 1),
             },
         },
         "decode": {

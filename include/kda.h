@@ -277,7 +277,7 @@ KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k
  * 16-byte aligned (beta, dbeta 4).  B == 0 or H == 0 is a no-op; T == 0
  * copies dhT (or zeros) to dh0.  Workspace (the chunk records, the state
  * entering and the state gradient leaving every chunk, and per-chunk scratch:
- * about 385 KB per 64 tokens and head) comes from the library's stream-ordered
+ * about 400 KB per 64 tokens and head) comes from the library's stream-ordered
  * pool; KDA_ERR_NO_MEMORY if it cannot be had.  Computed in fp32; g obeys
  * the forward's bound (every entry in [-5, 0]), which the chunk records that
  * the two state scans read rely on.

@@ -96,7 +96,7 @@ int chunk_f32_slices() { return kScanSlices; }
 __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
-    uint8_t* __restrict__ ws) {
+    uint8_t* __restrict__ ws, float* __restrict__ x_out) {
     using st = float;
     using R = RecF;
 
@@ -342,9 +342,11 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
         }
         __syncthreads();
     }
-    // T = X diag(beta), zero above the diagonal
+    // T = X diag(beta), zero above the diagonal (and X itself, if asked for)
+    float* xg = x_out ? x_out + ((size_t)bh * nchunks + cl) * kChunk * kChunk : nullptr;
     for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
         const int rr = idx >> 6, cc = idx & 63;
+        if (xg) xg[idx] = (cc <= rr) ? x_s[rr * SP + cc] : 0.f;
         const float tv = (cc <= rr) ? x_s[rr * SP + cc] * beta_s[cc] : 0.f;
         x_s[rr * SP + cc] = tv;
         THg[idx] = tv;
@@ -588,10 +590,10 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
 
 hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
                                  const float* beta, int B, int T, int H, int chunk0, int nchunks,
-                                 void* ws, hipStream_t stream) {
+                                 void* ws, hipStream_t stream, float* x_out) {
     const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
     hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3(nblk), dim3(256), 0, stream, q, k, g, beta, T,
-                       H, chunk0, nchunks, static_cast<uint8_t*>(ws));
+                       H, chunk0, nchunks, static_cast<uint8_t*>(ws), x_out);
     return hipGetLastError();
 }
 

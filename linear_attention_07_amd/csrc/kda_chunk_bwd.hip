@@ -26,7 +26,7 @@
 //
 // Four launches:
 //   prep  (kda_chunk.hip) writes each chunk's record (W, Q', Kb^T, T, M T,
-//         gamma);
+//         gamma) and X = (I + A)^-1;
 //   state scan    walks the chunks forward and stores the state entering each;
 //   gradient scan walks them in reverse and stores dS' of each chunk, and dS
 //         of the first as the initial state's gradient;
@@ -42,8 +42,9 @@ namespace {
 
 using RF = ChunkRecF32;
 constexpr int kThreads = 256;
-constexpr int kScanCols = 32;              // value columns per scan workgroup
+constexpr int kScanCols = 64;              // value columns per scan workgroup
 constexpr int kScanSlices = kD / kScanCols;
+constexpr int kScanThreads = 512;
 constexpr size_t kStateFloats = (size_t)kD * kD;
 
 // Scratch of one chunk-gradient workgroup in global memory (floats).
@@ -61,10 +62,10 @@ __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x *
 // n < TN (ct = t mod N / TN), so neighbouring threads read neighbouring
 // columns of B and threads of one row group share each A value.  Each result
 // goes to out(m, n, i, j, value).
-template <int M, int N, int TM, int TN, class FA, class FB, class FO>
+template <int M, int N, int TM, int TN, int NT = kThreads, class FA, class FB, class FO>
 __device__ __forceinline__ void mm(int K, FA&& A, FB&& B, FO&& out) {
     constexpr int CT = N / TN;
-    static_assert((M / TM) * CT == kThreads, "micro-tiles must cover the result once");
+    static_assert((M / TM) * CT == NT, "micro-tiles must cover the result once");
     const int t = threadIdx.x;
     const int i0 = (t / CT) * TM, ct = t % CT;
     float acc[TM][TN];
@@ -90,6 +91,61 @@ __device__ __forceinline__ void mm(int K, FA&& A, FB&& B, FO&& out) {
         for (int n = 0; n < TN; ++n) out(m, n, i0 + m, ct + CT * n, acc[m][n]);
 }
 
+// mm with k taken four at a time: A4(i, k) returns A(i, k .. k + 3) and
+// B4(k, j) returns B(k .. k + 3, j) as float4, so operands stored along k
+// load as one 16-byte access.  K is a multiple of 4.
+template <int M, int N, int TM, int TN, class FA, class FB, class FO>
+__device__ __forceinline__ void mm4(int K, FA&& A4, FB&& B4, FO&& out) {
+    constexpr int CT = N / TN;
+    static_assert((M / TM) * CT == kThreads, "micro-tiles must cover the result once");
+    const int t = threadIdx.x;
+    const int i0 = (t / CT) * TM, ct = t % CT;
+    float acc[TM][TN];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
+#pragma unroll 2
+    for (int kk = 0; kk < K; kk += 4) {
+        float4 a[TM], b[TN];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) a[m] = A4(i0 + m, kk);
+#pragma unroll
+        for (int n = 0; n < TN; ++n) b[n] = B4(kk, ct + CT * n);
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                float c = acc[m][n];
+                c = fmaf(a[m].x, b[n].x, c);
+                c = fmaf(a[m].y, b[n].y, c);
+                c = fmaf(a[m].z, b[n].z, c);
+                acc[m][n] = fmaf(a[m].w, b[n].w, c);
+            }
+    }
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) out(m, n, i0 + m, ct + CT * n, acc[m][n]);
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+// four values down a column of a row-major matrix
+__device__ __forceinline__ float4 col4(const float* p, size_t pitch) {
+    return make_float4(p[0], p[pitch], p[2 * pitch], p[3 * pitch]);
+}
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) {
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ float4 exp4(float4 a) {
+    return make_float4(ex(a.x), ex(a.y), ex(a.z), ex(a.w));
+}
+__device__ __forceinline__ float4 scale4(float4 a, float c) {
+    return make_float4(a.x * c, a.y * c, a.z * c, a.w * c);
+}
+
 __device__ __forceinline__ void scan_ids(int& bh, int& slice) {
     // all slices of one head on one XCD (workgroups are dealt round-robin to
     // the 8 XCDs), so the records they share come from HBM once
@@ -107,56 +163,91 @@ __device__ __forceinline__ void scan_ids(int& bh, int& slice) {
     }
 }
 
+// Copy a rows x cols block (cols a multiple of 4, row pitch spitch floats,
+// 16-byte aligned rows) into LDS with row pitch dpitch; rows >= valid read as
+// zeros.  Every thread issues its float4 loads back to back.
+template <int NT>
+__device__ __forceinline__ void stage(const float* __restrict__ src, size_t spitch, int rows,
+                                      int cols, int valid, float* dst, int dpitch) {
+    const int q = cols / 4;
+    for (int e = threadIdx.x; e < rows * q; e += NT) {
+        const int r = e / q, c4 = 4 * (e % q);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < valid) x = *reinterpret_cast<const float4*>(src + (size_t)r * spitch + c4);
+        float* d = dst + r * dpitch + c4;
+        d[0] = x.x;
+        d[1] = x.y;
+        d[2] = x.z;
+        d[3] = x.w;
+    }
+}
+
+// LDS row pitches of the staged record parts (one float of padding per row, so
+// that the rows that a wave reads at one k fall in different banks)
+constexpr int kP64 = kChunk + 1;
+constexpr int kP128 = kD + 1;
+
 // ---------------------------------------------------------------------------
-// State scan: one workgroup per (b, h, 32 value columns).  For chunk c the
+// State scan: one workgroup per (b, h, 64 value columns).  For chunk c the
 // state slice entering it is stored, then S <- Diag(gamma) S + Kb^T (T V - W S).
+// Each chunk's record parts and V slice are first staged in LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void kda_bwd_state_scan_kernel(
+struct StateScanLds {
+    float S[kD][kScanCols];
+    float Z[kChunk][kScanCols];
+    float Tm[kChunk * kP64];
+    float W[kChunk * kP128];
+    float KT[kD * kP64];
+    float V[kChunk][kScanCols];
+    float gam[kD];
+};
+
+__global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
     const uint8_t* __restrict__ rec, const float* __restrict__ v, const float* __restrict__ h0,
     float* __restrict__ states, int T, int H, int nch) {
-    __shared__ float s_S[kD][kScanCols];
-    __shared__ float s_Z[kChunk][kScanCols];
+    __shared__ StateScanLds s;
     int bh, slice;
     scan_ids(bh, slice);
     const int b = bh / H, h = bh % H;
     const int col0 = slice * kScanCols;
     const int tid = threadIdx.x;
-    for (int e = tid; e < kD * kScanCols; e += kThreads) {
+    for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
         const int i = e / kScanCols, j = e % kScanCols;
-        s_S[i][j] = h0 ? h0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
+        s.S[i][j] = h0 ? h0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
     }
-    __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
-        const float* W = reinterpret_cast<const float*>(r + RF::W);
-        const float* KT = reinterpret_cast<const float*>(r + RF::KT);
-        const float* Tm = reinterpret_cast<const float*>(r + RF::TH);
-        const float* gam = reinterpret_cast<const float*>(r + RF::G);
-        float* st = states + ((size_t)bh * nch + c) * kStateFloats;
-        for (int e = tid; e < kD * kScanCols; e += kThreads) {
-            const int i = e / kScanCols, j = e % kScanCols;
-            st[(size_t)i * kD + col0 + j] = s_S[i][j];
-        }
         const int L = min(kChunk, T - c * kChunk);
-        const float* vc = v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
-        const size_t vp = (size_t)H * kD;
+        __syncthreads();  // the previous chunk's reads of the staged parts are done
+        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::TH), kChunk, kChunk, kChunk,
+                            kChunk, s.Tm, kP64);
+        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::W), kD, kChunk, kD, kChunk,
+                            s.W, kP128);
+        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::KT), kChunk, kD, kChunk, kD,
+                            s.KT, kP64);
+        stage<kScanThreads>(v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0,
+                            (size_t)H * kD, kChunk, kScanCols, L, &s.V[0][0], kScanCols);
+        if (tid < kD) s.gam[tid] = reinterpret_cast<const float*>(r + RF::G)[tid];
+        float* st = states + ((size_t)bh * nch + c) * kStateFloats;
+        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
+            const int i = e / kScanCols, j = e % kScanCols;
+            st[(size_t)i * kD + col0 + j] = s.S[i][j];
+        }
+        __syncthreads();
         // Z = T V - W S
-        mm<kChunk, kScanCols, 2, 4>(
+        mm<kChunk, kScanCols, 2, 4, kScanThreads>(
             kChunk + kD,
             [&](int i, int k) {
-                return k < kChunk ? Tm[i * kChunk + k] : -W[i * kD + (k - kChunk)];
+                return k < kChunk ? s.Tm[i * kP64 + k] : -s.W[i * kP128 + (k - kChunk)];
             },
-            [&](int k, int j) {
-                return k < kChunk ? (k < L ? vc[(size_t)k * vp + j] : 0.f) : s_S[k - kChunk][j];
-            },
-            [&](int, int, int i, int j, float a) { s_Z[i][j] = a; });
+            [&](int k, int j) { return k < kChunk ? s.V[k][j] : s.S[k - kChunk][j]; },
+            [&](int, int, int i, int j, float a) { s.Z[i][j] = a; });
         __syncthreads();
         // S' = Diag(gamma) S + Kb^T Z (each thread updates only its own entries)
-        mm<kD, kScanCols, 4, 4>(
-            kChunk, [&](int i, int k) { return KT[i * kChunk + k]; },
-            [&](int k, int j) { return s_Z[k][j]; },
-            [&](int, int, int i, int j, float a) { s_S[i][j] = fmaf(gam[i], s_S[i][j], a); });
-        __syncthreads();
+        mm<kD, kScanCols, 4, 4, kScanThreads>(
+            kChunk, [&](int i, int k) { return s.KT[i * kP64 + k]; },
+            [&](int k, int j) { return s.Z[k][j]; },
+            [&](int, int, int i, int j, float a) { s.S[i][j] = fmaf(s.gam[i], s.S[i][j], a); });
     }
 }
 
@@ -164,61 +255,73 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_state_scan_kernel(
 // Gradient scan: chunks in reverse.  For chunk c, dS' (the gradient of the
 // state leaving it) is stored, then
 //   dS <- Diag(gamma) dS' - W^T (Kb dS') + scale Q'^T dO.
-// After chunk 0, dS is the initial state's gradient.
+// After chunk 0, dS is the initial state's gradient.  Kb^T and then W take
+// turns in one LDS buffer.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void kda_bwd_grad_scan_kernel(
+struct GradScanLds {
+    float D[kD][kScanCols];
+    float Y[kChunk][kScanCols];
+    float KW[kD * kP64];  // Kb^T [128][64], then W [64][128] (pitch 129 fits in it)
+    float QP[kChunk * kP128];
+    float O[kChunk][kScanCols];
+    float gam[kD];
+};
+static_assert(kD * kP64 >= kChunk * kP128, "W must fit in the Kb^T buffer");
+
+__global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
     const uint8_t* __restrict__ rec, const float* __restrict__ dout,
     const float* __restrict__ dhT, float* __restrict__ dsn, float* __restrict__ dh0,
     float scale, int T, int H, int nch) {
-    __shared__ float s_D[kD][kScanCols];
-    __shared__ float s_Y[kChunk][kScanCols];
+    __shared__ GradScanLds s;
     int bh, slice;
     scan_ids(bh, slice);
     const int b = bh / H, h = bh % H;
     const int col0 = slice * kScanCols;
     const int tid = threadIdx.x;
-    for (int e = tid; e < kD * kScanCols; e += kThreads) {
+    for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
         const int i = e / kScanCols, j = e % kScanCols;
-        s_D[i][j] = dhT ? dhT[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
+        s.D[i][j] = dhT ? dhT[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
     }
-    __syncthreads();
     for (int c = nch - 1; c >= 0; --c) {
         const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
-        const float* W = reinterpret_cast<const float*>(r + RF::W);
-        const float* QP = reinterpret_cast<const float*>(r + RF::QP);
-        const float* KT = reinterpret_cast<const float*>(r + RF::KT);
-        const float* gam = reinterpret_cast<const float*>(r + RF::G);
-        float* st = dsn + ((size_t)bh * nch + c) * kStateFloats;
-        for (int e = tid; e < kD * kScanCols; e += kThreads) {
-            const int i = e / kScanCols, j = e % kScanCols;
-            st[(size_t)i * kD + col0 + j] = s_D[i][j];
-        }
         const int L = min(kChunk, T - c * kChunk);
-        const float* oc = dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
-        const size_t op = (size_t)H * kD;
+        __syncthreads();  // the previous chunk's reads of the staged parts are done
+        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::KT), kChunk, kD, kChunk, kD,
+                            s.KW, kP64);
+        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::QP), kD, kChunk, kD, kChunk,
+                            s.QP, kP128);
+        stage<kScanThreads>(dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0,
+                            (size_t)H * kD, kChunk, kScanCols, L, &s.O[0][0], kScanCols);
+        if (tid < kD) s.gam[tid] = reinterpret_cast<const float*>(r + RF::G)[tid];
+        float* st = dsn + ((size_t)bh * nch + c) * kStateFloats;
+        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
+            const int i = e / kScanCols, j = e % kScanCols;
+            st[(size_t)i * kD + col0 + j] = s.D[i][j];
+        }
+        __syncthreads();
         // Y = Kb dS'   (Kb[i][k] = Kb^T[k][i])
-        mm<kChunk, kScanCols, 2, 4>(
-            kD, [&](int i, int k) { return KT[k * kChunk + i]; },
-            [&](int k, int j) { return s_D[k][j]; },
-            [&](int, int, int i, int j, float a) { s_Y[i][j] = a; });
+        mm<kChunk, kScanCols, 2, 4, kScanThreads>(
+            kD, [&](int i, int k) { return s.KW[k * kP64 + i]; },
+            [&](int k, int j) { return s.D[k][j]; },
+            [&](int, int, int i, int j, float a) { s.Y[i][j] = a; });
+        __syncthreads();
+        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::W), kD, kChunk, kD, kChunk,
+                            s.KW, kP128);
         __syncthreads();
         // dS = Diag(gamma) dS' - W^T Y + scale Q'^T dO
-        mm<kD, kScanCols, 4, 4>(
+        mm<kD, kScanCols, 4, 4, kScanThreads>(
             2 * kChunk,
             [&](int i, int k) {
-                return k < kChunk ? -W[k * kD + i] : scale * QP[(k - kChunk) * kD + i];
+                return k < kChunk ? -s.KW[k * kP128 + i] : scale * s.QP[(k - kChunk) * kP128 + i];
             },
-            [&](int k, int j) {
-                return k < kChunk ? s_Y[k][j]
-                                  : (k - kChunk < L ? oc[(size_t)(k - kChunk) * op + j] : 0.f);
-            },
-            [&](int, int, int i, int j, float a) { s_D[i][j] = fmaf(gam[i], s_D[i][j], a); });
-        __syncthreads();
+            [&](int k, int j) { return k < kChunk ? s.Y[k][j] : s.O[k - kChunk][j]; },
+            [&](int, int, int i, int j, float a) { s.D[i][j] = fmaf(s.gam[i], s.D[i][j], a); });
     }
+    __syncthreads();
     if (dh0)
-        for (int e = tid; e < kD * kScanCols; e += kThreads) {
+        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
             const int i = e / kScanCols, j = e % kScanCols;
-            dh0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] = s_D[i][j];
+            dh0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] = s.D[i][j];
         }
 }
 
@@ -228,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_scan_kernel(
 // rows 8 (t / 32) + m and channels t % 32 + 32 n, and keeps its share of dkh,
 // dqh and dGam in registers from the first contribution to the last.
 // ---------------------------------------------------------------------------
-struct BwdLds {
+struct __align__(16) BwdLds {
     float gam[kChunk][kD];  // Gam (cumulative log-decay), later dGam
     float kh[kChunk][kD];
     float qh[kChunk][kD];
@@ -249,7 +352,8 @@ struct BwdLds {
 __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ dout,
-    const float* __restrict__ states, const float* __restrict__ dsn, float* __restrict__ scr_all,
+    const float* __restrict__ states, const float* __restrict__ dsn,
+    const float* __restrict__ xs, float* __restrict__ scr_all,
     float scale, int T, int H, int nch, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
     __shared__ BwdLds s;
@@ -321,6 +425,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     }
     __syncthreads();
     if (tid < kD) s.dlast[tid] *= ex(s.gl[tid]);
+    // X = (I + A)^-1 of this chunk, as the record prep formed it
+    stage<kThreads>(xs + (size_t)blockIdx.x * kChunk * kChunk, kChunk, kChunk, kChunk, kChunk,
+                    &s.x[0][0], kChunk);
 
     // ---- P (strict lower) and N (lower incl) with the exact pairwise decays ---
     {
@@ -360,57 +467,58 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
             }
     }
     __syncthreads();
-    // ---- X = (I + A)^-1, A = diag(beta) P, by forward substitution per column
-    if (tid < kChunk) {
-        const int j = tid;
-        for (int r = 0; r < kChunk; ++r) {
-            float a = (r == j) ? 1.f : 0.f;
-            if (r > j) {
-                for (int i = j; i < r; ++i) a = fmaf(-s.beta[r] * s.p[r][i], s.x[i][j], a);
-            }
-            s.x[r][j] = r >= j ? a : 0.f;
-        }
-    }
     __syncthreads();
 
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // q / k / v / dout row r from channel col on, four values (zeros past the sequence)
+    auto in4 = [&](const float* p, int r, int col) {
+        return r < L ? ld4(p + base + (size_t)r * rp + col) : z4;
+    };
     // ---- R = V - Kt S --------------------------------------------------------
-    mm<kChunk, kD, 8, 4>(
-        kD, [&](int i, int kk) { return ex(s.gam[i][kk]) * s.kh[i][kk]; },
-        [&](int kk, int j) { return S[(size_t)kk * kD + j]; },
+    mm4<kChunk, kD, 8, 4>(
+        kD, [&](int i, int kk) { return mul4(exp4(ld4(&s.gam[i][kk])), ld4(&s.kh[i][kk])); },
+        [&](int kk, int j) { return col4(S + (size_t)kk * kD + j, kD); },
         [&](int, int, int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
     __syncthreads();
     // ---- U = T R,  T = X diag(beta) ------------------------------------------
-    mm<kChunk, kD, 8, 4>(
-        kChunk, [&](int i, int kk) { return s.x[i][kk] * s.beta[kk]; },
-        [&](int kk, int j) { return R_[kk * kD + j]; },
+    mm4<kChunk, kD, 8, 4>(
+        kChunk, [&](int i, int kk) { return mul4(ld4(&s.x[i][kk]), ld4(&s.beta[kk])); },
+        [&](int kk, int j) { return col4(R_ + kk * kD + j, kD); },
         [&](int, int, int i, int j, float a) { U_[i * kD + j] = a; });
     __syncthreads();
     // ---- dU = scale M^T dO + Kb dS' ------------------------------------------
-    mm<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 8, 4>(
         kChunk + kD,
         [&](int i, int kk) {
-            return kk < kChunk ? scale * s.n[kk][i]
-                               : ex(s.gl[kk - kChunk] - s.gam[i][kk - kChunk]) *
-                                     s.kh[i][kk - kChunk];
+            if (kk < kChunk) return scale4(col4(&s.n[kk][i], kChunk), scale);
+            const int c4 = kk - kChunk;
+            float4 e = ld4(&s.gam[i][c4]);
+            const float4 gl = ld4(&s.gl[c4]);
+            e = exp4(make_float4(gl.x - e.x, gl.y - e.y, gl.z - e.z, gl.w - e.w));
+            return mul4(e, ld4(&s.kh[i][c4]));
         },
         [&](int kk, int j) {
-            return kk < kChunk ? in(dout, kk, j) : dSn[(size_t)(kk - kChunk) * kD + j];
+            if (kk < kChunk) {
+                return make_float4(in(dout, kk, j), in(dout, kk + 1, j), in(dout, kk + 2, j),
+                                   in(dout, kk + 3, j));
+            }
+            return col4(dSn + (size_t)(kk - kChunk) * kD + j, kD);
         },
         [&](int, int, int i, int j, float a) { dU_[i * kD + j] = a; });
     __syncthreads();
     // ---- dV = dR = T^T dU ----------------------------------------------------
-    mm<kChunk, kD, 8, 4>(
-        kChunk, [&](int i, int kk) { return s.x[kk][i] * s.beta[i]; },
-        [&](int kk, int j) { return dU_[kk * kD + j]; },
+    mm4<kChunk, kD, 8, 4>(
+        kChunk, [&](int i, int kk) { return scale4(col4(&s.x[kk][i], kChunk), s.beta[i]); },
+        [&](int kk, int j) { return col4(dU_ + kk * kD + j, kD); },
         [&](int, int, int i, int j, float a) {
             if (i < L) dv[base + (size_t)i * rp + j] = a;
         });
     // ---- dX = lower-incl(dU R^T) diag(beta); dbeta_j += sum_i X_ij dT_ij ------
     {
         float pb[4] = {0.f, 0.f, 0.f, 0.f};
-        mm<kChunk, kChunk, 4, 4>(
-            kD, [&](int i, int kk) { return dU_[i * kD + kk]; },
-            [&](int kk, int j) { return R_[j * kD + kk]; },
+        mm4<kChunk, kChunk, 4, 4>(
+            kD, [&](int i, int kk) { return ld4(dU_ + i * kD + kk); },
+            [&](int kk, int j) { return ld4(R_ + j * kD + kk); },
             [&](int, int n, int i, int j, float a) {
                 const float dt = j <= i ? a : 0.f;
                 dX_[i * kChunk + j] = dt * s.beta[j];
@@ -426,22 +534,22 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
         s.dbeta[tid] = a;
     }
     // ---- dM = scale lower-incl(dO U^T), over N ---------------------------------
-    mm<kChunk, kChunk, 4, 4>(
-        kD, [&](int i, int kk) { return in(dout, i, kk); },
-        [&](int kk, int j) { return U_[j * kD + kk]; },
+    mm4<kChunk, kChunk, 4, 4>(
+        kD, [&](int i, int kk) { return in4(dout, i, kk); },
+        [&](int kk, int j) { return ld4(U_ + j * kD + kk); },
         [&](int, int, int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
     // ---- Y = X^T dX ------------------------------------------------------------
-    mm<kChunk, kChunk, 4, 4>(
-        kChunk, [&](int i, int kk) { return s.x[kk][i]; },
-        [&](int kk, int j) { return dX_[kk * kChunk + j]; },
+    mm4<kChunk, kChunk, 4, 4>(
+        kChunk, [&](int i, int kk) { return col4(&s.x[kk][i], kChunk); },
+        [&](int kk, int j) { return col4(dX_ + kk * kChunk + j, kChunk); },
         [&](int, int, int i, int j, float a) { Y_[i * kChunk + j] = a; });
     __syncthreads();
     // ---- dA = -strict-lower(Y X^T); dbeta_i += sum_j dA_ij P_ij; dP over P ----
     {
         float pr[4] = {0.f, 0.f, 0.f, 0.f};
-        mm<kChunk, kChunk, 4, 4>(
-            kChunk, [&](int i, int kk) { return Y_[i * kChunk + kk]; },
-            [&](int kk, int j) { return s.x[j][kk]; },
+        mm4<kChunk, kChunk, 4, 4>(
+            kChunk, [&](int i, int kk) { return ld4(Y_ + i * kChunk + kk); },
+            [&](int kk, int j) { return ld4(&s.x[j][kk]); },
             [&](int m, int, int i, int j, float a) {
                 const float da = j < i ? -a : 0.f;
                 pr[m] = fmaf(da, s.p[i][j], pr[m]);
@@ -466,18 +574,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
         for (int n = 0; n < 4; ++n) dkh[m][n] = dqh[m][n] = dgm[m][n] = 0.f;
 
     // dQt = scale dO S^T:  dqh += e^Gam dQt,  dGam += Qt dQt
-    mm<kChunk, kD, 8, 4>(
-        kD, [&](int i, int kk) { return in(dout, i, kk); },
-        [&](int kk, int j) { return S[(size_t)j * kD + kk]; },
+    mm4<kChunk, kD, 8, 4>(
+        kD, [&](int i, int kk) { return in4(dout, i, kk); },
+        [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
         [&](int m, int n, int i, int j, float a) {
             const float d = scale * a, e = ex(s.gam[i][j]);
             dqh[m][n] = fmaf(e, d, dqh[m][n]);
             dgm[m][n] = fmaf(e * s.qh[i][j], d, dgm[m][n]);
         });
     // dKt = -dR S^T:  dkh += e^Gam dKt,  dGam += Kt dKt
-    mm<kChunk, kD, 8, 4>(
-        kD, [&](int i, int kk) { return i < L ? -dv[base + (size_t)i * rp + kk] : 0.f; },
-        [&](int kk, int j) { return S[(size_t)j * kD + kk]; },
+    mm4<kChunk, kD, 8, 4>(
+        kD, [&](int i, int kk) { return scale4(in4(dv, i, kk), -1.f); },
+        [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
         [&](int m, int n, int i, int j, float a) {
             const float e = ex(s.gam[i][j]);
             dkh[m][n] = fmaf(e, a, dkh[m][n]);
@@ -487,9 +595,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     __syncthreads();  // the dbeta reduction has read red
     {
         float pl[4] = {0.f, 0.f, 0.f, 0.f};
-        mm<kChunk, kD, 8, 4>(
-            kD, [&](int i, int kk) { return U_[i * kD + kk]; },
-            [&](int kk, int j) { return dSn[(size_t)j * kD + kk]; },
+        mm4<kChunk, kD, 8, 4>(
+            kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
+            [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
             [&](int m, int n, int i, int j, float a) {
                 const float e = ex(s.gl[j] - s.gam[i][j]);
                 const float t = e * s.kh[i][j] * a;
@@ -632,7 +740,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
 size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H) {
     const size_t nch = (size_t)(T + kChunk - 1) / kChunk;
     const size_t n = (size_t)B * H * nch;
-    return n * (RF::BYTES + 2 * kStateFloats * sizeof(float) + kScrFloats * sizeof(float));
+    return n * (RF::BYTES +
+                (2 * kStateFloats + (size_t)kChunk * kChunk + kScrFloats) * sizeof(float));
 }
 
 hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
@@ -645,18 +754,19 @@ hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, 
     uint8_t* rec = static_cast<uint8_t*>(ws);
     float* states = reinterpret_cast<float*>(rec + n * RF::BYTES);
     float* dsn = states + n * kStateFloats;
-    float* scr = dsn + n * kStateFloats;
-    hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, 0, nch, rec, stream);
+    float* xs = dsn + n * kStateFloats;
+    float* scr = xs + n * kChunk * kChunk;
+    hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, 0, nch, rec, stream, xs);
     if (e != hipSuccess) return e;
     const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
-    hipLaunchKernelGGL(kda_bwd_state_scan_kernel, dim3(nscan), dim3(kThreads), 0, stream, rec, v,
+    hipLaunchKernelGGL(kda_bwd_state_scan_kernel, dim3(nscan), dim3(kScanThreads), 0, stream, rec, v,
                        h0, states, T, H, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel, dim3(nscan), dim3(kThreads), 0, stream, rec,
+    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel, dim3(nscan), dim3(kScanThreads), 0, stream, rec,
                        dout, dhT, dsn, dh0, scale, T, H, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)n), dim3(kThreads), 0,
-                       stream, q, k, v, g, beta, dout, states, dsn, scr, scale, T, H, nch, dq, dk,
+                       stream, q, k, v, g, beta, dout, states, dsn, xs, scr, scale, T, H, nch, dq, dk,
                        dv, dg, dbeta);
     return hipGetLastError();
 }

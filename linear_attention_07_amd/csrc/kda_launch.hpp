@@ -31,7 +31,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 // prep writes one record (W, Q', Kb^T, T, MT, gamma) per (batch, head, chunk)
 // of chunks [chunk0, chunk0 + nchunks) into ws, from q, k, g, beta; scan walks
 // them in order, reading v, the records and h_in (NULL = zero state), and
-// writes out and, if h_out is not NULL, the final state.
+// writes out and, if h_out is not NULL, the final state.  x_out (or NULL)
+// receives X = (I + A)^-1 of every chunk, [64][64] fp32 each, zero above the
+// diagonal, in record order.
 size_t chunk_f32_record_bytes();
 int chunk_f32_slices();
 // Byte offsets inside one fp32 record (64-token chunks, 128 channels).
@@ -46,7 +48,7 @@ struct ChunkRecF32 {
 };
 hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
                                  const float* beta, int B, int T, int H, int chunk0, int nchunks,
-                                 void* ws, hipStream_t stream);
+                                 void* ws, hipStream_t stream, float* x_out = nullptr);
 hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
                                  float* out, float scale, int B, int T, int H, int chunk0,
                                  int nchunks, hipStream_t stream);

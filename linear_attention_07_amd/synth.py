@@ -38,7 +38,7 @@ HEAD_DIM = 128
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "prefill" or "decode"
+    kind: str            # "prefill", "decode" or "prefill_bwd"
     B: int
     H: int
     T: int               # tokens (prefill) or decode steps
@@ -63,6 +63,10 @@ WORKLOADS = {
     # 256 sequences x 96 heads, 64 decode steps, random initial state
     "decode_b256": Workload("decode_b256", "decode", 256, 96, 64, torch.bfloat16, 3,
                             h0_std=0.1),
+    # backward of one fp32 layer prefill at a training length: 8K tokens, 96
+    # heads, random initial state (dout and dhT drawn beside it)
+    "prefill_bwd_8k": Workload("prefill_bwd_8k", "prefill_bwd", 1, 96, 8192, torch.float32, 5,
+                               h0_std=0.1),
     # million-token prefill with slow decay, zero state
     "prefill_1m": Workload("prefill_1m", "prefill", 1, 96, 1 << 20, torch.bfloat16, 4,
                            g_shift=6.0),

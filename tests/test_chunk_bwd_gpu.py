@@ -124,3 +124,26 @@ def test_chunk_bwd_deterministic():
     b = gpu(x)
     for n, u, w in zip(NAMES, a, b):
         assert torch.equal(u, w), n
+
+
+def test_chunk_bwd_bench_workload_sampled_heads():
+    """The timed workload (B=1, H=96, T=8192, as launched by the benchmark):
+    heads are independent, so the oracle runs on three sampled heads."""
+    w = synth.WORKLOADS["prefill_bwd_8k"]
+    say(f"chunk bwd case {w.name} B={w.B} T={w.T} H={w.H}")
+    x = synth.prefill_inputs(w.B, w.T, w.H, torch.float32, seed=w.seed, g_shift=w.g_shift,
+                             h0_std=w.h0_std, device=DEV)
+    gb = torch.Generator(device=DEV).manual_seed(w.seed + 1)
+    x["dout"] = torch.randn((w.B, w.T, w.H, 128), generator=gb, device=DEV)
+    x["dhT"] = 0.1 * torch.randn((w.B, w.H, 128, 128), generator=gb, device=DEV)
+    got = gpu(x)
+    heads = [0, 47, w.H - 1]
+    h = lambda t, ax: host64(t.index_select(ax, torch.tensor(heads, device=DEV)))
+    want = oracle.chunk_backward(h(x["q"], 2), h(x["k"], 2), h(x["v"], 2), h(x["g"], 2),
+                                 h(x["beta"], 2), x["scale"], h(x["h0"], 1), h(x["dout"], 2),
+                                 h(x["dhT"], 1))
+    axes = (2, 2, 2, 2, 2, 1)
+    for n, a, b, ax in zip(NAMES, got, want, axes):
+        e = rel(h(a, ax), b)
+        say(f"chunk bwd {w.name} heads {heads} {n}: {e:.1e}")
+        assert e <= TOL, (n, e)
