@@ -94,10 +94,10 @@ __device__ __forceinline__ void mm(int K, FA&& A, FB&& B, FO&& out) {
 // mm with k taken four at a time: A4(i, k) returns A(i, k .. k + 3) and
 // B4(k, j) returns B(k .. k + 3, j) as float4, so operands stored along k
 // load as one 16-byte access.  K is a multiple of 4.
-template <int M, int N, int TM, int TN, class FA, class FB, class FO>
+template <int M, int N, int TM, int TN, int NT = kThreads, class FA, class FB, class FO>
 __device__ __forceinline__ void mm4(int K, FA&& A4, FB&& B4, FO&& out) {
     constexpr int CT = N / TN;
-    static_assert((M / TM) * CT == kThreads, "micro-tiles must cover the result once");
+    static_assert((M / TM) * CT == NT, "micro-tiles must cover the result once");
     const int t = threadIdx.x;
     const int i0 = (t / CT) * TM, ct = t % CT;
     float acc[TM][TN];
@@ -326,15 +326,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Chunk gradients: one workgroup per (b, h, chunk).  Results over [64][128]
-// (token row x channel) use the micro-tile of mm<64, 128, 8, 4>: thread t owns
-// rows 8 (t / 32) + m and channels t % 32 + 32 n, and keeps its share of dkh,
-// dqh and dGam in registers from the first contribution to the last.
+// Chunk gradients: one 512-thread workgroup per (b, h, chunk) (two waves per
+// SIMD).  Results over [64][128] (token row x channel) use the micro-tile of
+// mm4<64, 128, 4, 4>: thread t owns rows 4 (t / 32) + m and channels t % 32 +
+// 32 n, and keeps its share of dkh, dqh and dGam in registers from the first
+// contribution to the last.
 // ---------------------------------------------------------------------------
+constexpr int kCT = 512;
+constexpr int kPK = kD + 4;  // row pitch of the per-channel arrays: rows 16 B apart in bank
 struct __align__(16) BwdLds {
-    float gam[kChunk][kD];  // Gam (cumulative log-decay), later dGam
-    float kh[kChunk][kD];
-    float qh[kChunk][kD];
+    float gam[kChunk][kPK];  // Gam (cumulative log-decay), later dGam
+    float kh[kChunk][kPK];
+    float qh[kChunk][kPK];
     float p[kChunk][kChunk];  // P, later dP
     float n[kChunk][kChunk];  // N (= M), later dM
     float x[kChunk][kChunk];  // X = (I + A)^-1
@@ -346,10 +349,10 @@ struct __align__(16) BwdLds {
     float dotk[kChunk];
     float gl[kD];    // Gam of the chunk's last row
     float dlast[kD];  // gamma dgamma, the extra dGam of the last row besides sum_r Kb dKb
-    float red[1024];  // per-thread partial sums, reduced in a fixed order (deterministic)
+    float red[2048];  // per-thread partial sums, reduced in a fixed order (deterministic)
 };
 
-__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
+__global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ dout,
     const float* __restrict__ states, const float* __restrict__ dsn,
@@ -377,28 +380,33 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
         return r < L ? p[base + (size_t)r * rp + col] : 0.f;
     };
 
-    // ---- load: normalised q, k (4 threads per row, 32 channels each), g ---
+    // ---- load: normalised q, k (8 threads per row, 16 channels each), g ---
     {
-        const int r = tid >> 2, part = tid & 3;
+        const int r = tid >> 3, part = tid & 7;
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
         float sq = 0.f, sk = 0.f;
-        for (int e = 0; e < 32; ++e) {
-            const int col = 32 * part + e;
-            const float qv = in(q, r, col), kv = in(k, r, col);
-            sq = fmaf(qv, qv, sq);
-            sk = fmaf(kv, kv, sk);
-            s.qh[r][col] = qv;
-            s.kh[r][col] = kv;
-            s.gam[r][col] = in(g, r, col);
+        float4 qv[4], kv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int col = 16 * part + 4 * e;
+            const size_t off = base + (size_t)r * rp + col;
+            qv[e] = r < L ? ld4(q + off) : z;
+            kv[e] = r < L ? ld4(k + off) : z;
+            *reinterpret_cast<float4*>(&s.gam[r][col]) = r < L ? ld4(g + off) : z;
+            sq += qv[e].x * qv[e].x + qv[e].y * qv[e].y + qv[e].z * qv[e].z + qv[e].w * qv[e].w;
+            sk += kv[e].x * kv[e].x + kv[e].y * kv[e].y + kv[e].z * kv[e].z + kv[e].w * kv[e].w;
         }
-        sq += __shfl_xor(sq, 1);
-        sq += __shfl_xor(sq, 2);
-        sk += __shfl_xor(sk, 1);
-        sk += __shfl_xor(sk, 2);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            sq += __shfl_xor(sq, o);
+            sk += __shfl_xor(sk, o);
+        }
         const float rq = 1.f / sqrtf(sq + kNormEps), rk = 1.f / sqrtf(sk + kNormEps);
-        for (int e = 0; e < 32; ++e) {
-            const int col = 32 * part + e;
-            s.qh[r][col] *= rq;
-            s.kh[r][col] *= rk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int col = 16 * part + 4 * e;
+            *reinterpret_cast<float4*>(&s.qh[r][col]) = scale4(qv[e], rq);
+            *reinterpret_cast<float4*>(&s.kh[r][col]) = scale4(kv[e], rk);
         }
         if (part == 0) {
             s.rq[r] = rq;
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
             s.gam[r][tid] = a;
         }
         s.gl[tid] = a;
-    } else {  // dgamma = rowsum(dS' . S), kept times gamma for the last row of dGam
+    } else if (tid < 2 * kD) {  // dgamma = rowsum(dS' . S), times gamma for the last row of dGam
         const int row = tid - kD;
         float d = 0.f;
         for (int j = 0; j < kD; ++j) d = fmaf(dSn[(size_t)row * kD + j], S[(size_t)row * kD + j], d);
@@ -426,35 +434,38 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     __syncthreads();
     if (tid < kD) s.dlast[tid] *= ex(s.gl[tid]);
     // X = (I + A)^-1 of this chunk, as the record prep formed it
-    stage<kThreads>(xs + (size_t)blockIdx.x * kChunk * kChunk, kChunk, kChunk, kChunk, kChunk,
+    stage<kCT>(xs + (size_t)blockIdx.x * kChunk * kChunk, kChunk, kChunk, kChunk, kChunk,
                     &s.x[0][0], kChunk);
 
     // ---- P (strict lower) and N (lower incl) with the exact pairwise decays ---
     {
-        constexpr int CT = 16, TM = 4, TN = 4;
+        constexpr int CT = 16, TM = 2, TN = 4;
         const int i0 = (tid / CT) * TM, ct = tid % CT;
         float ap[TM][TN] = {}, an[TM][TN] = {};
-        for (int cc = 0; cc < kD; ++cc) {
-            float kr[TM], qr[TM], gr[TM], ki[TN], gi[TN];
+        for (int cc = 0; cc < kD; cc += 4) {
+            float4 kr[TM], qr[TM], gr[TM], ki[TN], gi[TN];
 #pragma unroll
             for (int m = 0; m < TM; ++m) {
-                kr[m] = s.kh[i0 + m][cc];
-                qr[m] = s.qh[i0 + m][cc];
-                gr[m] = s.gam[i0 + m][cc];
+                kr[m] = ld4(&s.kh[i0 + m][cc]);
+                qr[m] = ld4(&s.qh[i0 + m][cc]);
+                gr[m] = ld4(&s.gam[i0 + m][cc]);
             }
 #pragma unroll
             for (int n = 0; n < TN; ++n) {
-                ki[n] = s.kh[ct + CT * n][cc];
-                gi[n] = s.gam[ct + CT * n][cc];
+                ki[n] = ld4(&s.kh[ct + CT * n][cc]);
+                gi[n] = ld4(&s.gam[ct + CT * n][cc]);
             }
 #pragma unroll
             for (int m = 0; m < TM; ++m)
 #pragma unroll
                 for (int n = 0; n < TN; ++n) {
-                    const float e =
-                        ct + CT * n <= i0 + m ? ex(gr[m] - gi[n]) * ki[n] : 0.f;
-                    ap[m][n] = fmaf(kr[m], e, ap[m][n]);
-                    an[m][n] = fmaf(qr[m], e, an[m][n]);
+                    if (ct + CT * n > i0 + m) continue;
+                    const float ex0 = ex(gr[m].x - gi[n].x) * ki[n].x;
+                    const float ex1 = ex(gr[m].y - gi[n].y) * ki[n].y;
+                    const float ex2 = ex(gr[m].z - gi[n].z) * ki[n].z;
+                    const float ex3 = ex(gr[m].w - gi[n].w) * ki[n].w;
+                    ap[m][n] += kr[m].x * ex0 + kr[m].y * ex1 + kr[m].z * ex2 + kr[m].w * ex3;
+                    an[m][n] += qr[m].x * ex0 + qr[m].y * ex1 + qr[m].z * ex2 + qr[m].w * ex3;
                 }
         }
 #pragma unroll
@@ -475,19 +486,19 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
         return r < L ? ld4(p + base + (size_t)r * rp + col) : z4;
     };
     // ---- R = V - Kt S --------------------------------------------------------
-    mm4<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 4, 4, kCT>(
         kD, [&](int i, int kk) { return mul4(exp4(ld4(&s.gam[i][kk])), ld4(&s.kh[i][kk])); },
         [&](int kk, int j) { return col4(S + (size_t)kk * kD + j, kD); },
         [&](int, int, int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
     __syncthreads();
     // ---- U = T R,  T = X diag(beta) ------------------------------------------
-    mm4<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 4, 4, kCT>(
         kChunk, [&](int i, int kk) { return mul4(ld4(&s.x[i][kk]), ld4(&s.beta[kk])); },
         [&](int kk, int j) { return col4(R_ + kk * kD + j, kD); },
         [&](int, int, int i, int j, float a) { U_[i * kD + j] = a; });
     __syncthreads();
     // ---- dU = scale M^T dO + Kb dS' ------------------------------------------
-    mm4<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 4, 4, kCT>(
         kChunk + kD,
         [&](int i, int kk) {
             if (kk < kChunk) return scale4(col4(&s.n[kk][i], kChunk), scale);
@@ -507,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
         [&](int, int, int i, int j, float a) { dU_[i * kD + j] = a; });
     __syncthreads();
     // ---- dV = dR = T^T dU ----------------------------------------------------
-    mm4<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 4, 4, kCT>(
         kChunk, [&](int i, int kk) { return scale4(col4(&s.x[kk][i], kChunk), s.beta[i]); },
         [&](int kk, int j) { return col4(dU_ + kk * kD + j, kD); },
         [&](int, int, int i, int j, float a) {
@@ -516,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     // ---- dX = lower-incl(dU R^T) diag(beta); dbeta_j += sum_i X_ij dT_ij ------
     {
         float pb[4] = {0.f, 0.f, 0.f, 0.f};
-        mm4<kChunk, kChunk, 4, 4>(
+        mm4<kChunk, kChunk, 2, 4, kCT>(
             kD, [&](int i, int kk) { return ld4(dU_ + i * kD + kk); },
             [&](int kk, int j) { return ld4(R_ + j * kD + kk); },
             [&](int, int n, int i, int j, float a) {
@@ -530,16 +541,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     __syncthreads();
     if (tid < kChunk) {
         float a = 0.f;
-        for (int rg = 0; rg < 16; ++rg) a += s.red[rg * kChunk + tid];
+        for (int rg = 0; rg < 32; ++rg) a += s.red[rg * kChunk + tid];
         s.dbeta[tid] = a;
     }
     // ---- dM = scale lower-incl(dO U^T), over N ---------------------------------
-    mm4<kChunk, kChunk, 4, 4>(
+    mm4<kChunk, kChunk, 2, 4, kCT>(
         kD, [&](int i, int kk) { return in4(dout, i, kk); },
         [&](int kk, int j) { return ld4(U_ + j * kD + kk); },
         [&](int, int, int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
     // ---- Y = X^T dX ------------------------------------------------------------
-    mm4<kChunk, kChunk, 4, 4>(
+    mm4<kChunk, kChunk, 2, 4, kCT>(
         kChunk, [&](int i, int kk) { return col4(&s.x[kk][i], kChunk); },
         [&](int kk, int j) { return col4(dX_ + kk * kChunk + j, kChunk); },
         [&](int, int, int i, int j, float a) { Y_[i * kChunk + j] = a; });
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     // ---- dA = -strict-lower(Y X^T); dbeta_i += sum_j dA_ij P_ij; dP over P ----
     {
         float pr[4] = {0.f, 0.f, 0.f, 0.f};
-        mm4<kChunk, kChunk, 4, 4>(
+        mm4<kChunk, kChunk, 2, 4, kCT>(
             kChunk, [&](int i, int kk) { return ld4(Y_ + i * kChunk + kk); },
             [&](int kk, int j) { return ld4(&s.x[j][kk]); },
             [&](int m, int, int i, int j, float a) {
@@ -556,7 +567,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
                 s.p[i][j] = s.beta[i] * da;
             });
 #pragma unroll
-        for (int m = 0; m < 4; ++m) s.red[(tid % 16) * kChunk + (tid / 16) * 4 + m] = pr[m];
+        for (int m = 0; m < 2; ++m) s.red[(tid % 16) * kChunk + (tid / 16) * 2 + m] = pr[m];
     }
     __syncthreads();
     if (tid < kChunk) {
@@ -566,15 +577,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     }
 
     // ---- per-element accumulators of dkh, dqh, dGam (micro-tile 8 x 4) -------
-    const int i0 = (tid / 32) * 8, ct = tid % 32;
-    float dkh[8][4], dqh[8][4], dgm[8][4];
+    const int i0 = (tid / 32) * 4, ct = tid % 32;
+    float dkh[4][4], dqh[4][4], dgm[4][4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) dkh[m][n] = dqh[m][n] = dgm[m][n] = 0.f;
 
     // dQt = scale dO S^T:  dqh += e^Gam dQt,  dGam += Qt dQt
-    mm4<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 4, 4, kCT>(
         kD, [&](int i, int kk) { return in4(dout, i, kk); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
         [&](int m, int n, int i, int j, float a) {
@@ -583,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
             dgm[m][n] = fmaf(e * s.qh[i][j], d, dgm[m][n]);
         });
     // dKt = -dR S^T:  dkh += e^Gam dKt,  dGam += Kt dKt
-    mm4<kChunk, kD, 8, 4>(
+    mm4<kChunk, kD, 4, 4, kCT>(
         kD, [&](int i, int kk) { return scale4(in4(dv, i, kk), -1.f); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
         [&](int m, int n, int i, int j, float a) {
@@ -595,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     __syncthreads();  // the dbeta reduction has read red
     {
         float pl[4] = {0.f, 0.f, 0.f, 0.f};
-        mm4<kChunk, kD, 8, 4>(
+        mm4<kChunk, kD, 4, 4, kCT>(
             kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
             [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
             [&](int m, int n, int i, int j, float a) {
@@ -615,14 +626,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     // with E_ric = exp(Gam_rc - Gam_ic) (i <= r); then dkh += a + c, dqh += b,
     // dGam += kh a + qh b - kh c.
     {
-        float gown[8][4];
+        float gown[4][4];
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int n = 0; n < 4; ++n) gown[m][n] = s.gam[i0 + m][ct + 32 * n];
-        float ta[8][4], tb[8][4];
+        float ta[4][4], tb[4][4];
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int n = 0; n < 4; ++n) ta[m][n] = tb[m][n] = 0.f;
         for (int i = 0; i < kChunk; ++i) {
@@ -633,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
                 gi[n] = s.gam[i][ct + 32 * n];
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 const float dp = s.p[i0 + m][i], dn = s.n[i0 + m][i];
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
             }
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
                 const float khv = s.kh[i0 + m][ct + 32 * n], qhv = s.qh[i0 + m][ct + 32 * n];
@@ -662,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
                 gr[n] = s.gam[r][ct + 32 * n];
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 const float dp = s.p[r][i0 + m], dn = s.n[r][i0 + m];
 #pragma unroll
                 for (int n = 0; n < 4; ++n) {
@@ -672,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
             }
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
                 const float khv = s.kh[i0 + m][ct + 32 * n];
@@ -684,13 +695,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
 
     // ---- dg = reverse cumulative sum of dGam; the norms' backward -------------
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) s.gam[i0 + m][ct + 32 * n] = dgm[m][n];
     {
         // row dots qh . dqh and kh . dkh: 32 threads of a row group share a row
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 4; ++m) {
             float aq = 0.f, ak = 0.f;
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
@@ -710,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
         const int r = i0 + m;
         if (r >= L) continue;
         const float rq = s.rq[r], rk = s.rk[r], dtq = s.dotq[r], dtk = s.dotk[r];
@@ -724,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     }
     if (tid < kD) {
         float a = s.dlast[tid];  // Gam of the last row also enters Kb and gamma
-        for (int rg = 0; rg < 8; ++rg) a += s.red[rg * kD + tid];
+        for (int rg = 0; rg < 16; ++rg) a += s.red[rg * kD + tid];
         for (int r = kChunk - 1; r >= 0; --r) {
             a += s.gam[r][tid];
             if (r < L) dg[base + (size_t)r * rp + tid] = a;
@@ -765,7 +776,7 @@ hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, 
     hipLaunchKernelGGL(kda_bwd_grad_scan_kernel, dim3(nscan), dim3(kScanThreads), 0, stream, rec,
                        dout, dhT, dsn, dh0, scale, T, H, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)n), dim3(kThreads), 0,
+    hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)n), dim3(kCT), 0,
                        stream, q, k, v, g, beta, dout, states, dsn, xs, scr, scale, T, H, nch, dq, dk,
                        dv, dg, dbeta);
     return hipGetLastError();

@@ -234,3 +234,47 @@ def test_oracle_is_not_reachable_from_the_product():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "_kda_oracle" not in text and "kda_oracle_run" not in text, f
+
+
+# Fake addresses for the prefill backward: 15 buffers, 1 MiB apart (or 1 TiB
+# apart for sizes that would otherwise overlap).
+def chunk_bwd(lib, spacing=A, **kw):
+    names = ("q", "k", "v", "g", "beta", "h0", "dout", "dhT", "dq", "dk", "dv", "dg", "dbeta",
+             "dh0")
+    args = {n: ctypes.c_void_p(spacing * (i + 1)) for i, n in enumerate(names)}
+    args.update(scale=1.0, B=1, T=4, H=1)
+    args.update(kw)
+    return lib.kda_chunk_bwd_f32(
+        args["q"], args["k"], args["v"], args["g"], args["beta"], args["scale"], args["h0"],
+        args["dout"], args["dhT"], args["dq"], args["dk"], args["dv"], args["dg"], args["dbeta"],
+        args["dh0"], args["B"], args["T"], args["H"], None)
+
+
+def test_chunk_bwd_invalid_arguments(lib):
+    INV = libkda.KDA_ERR_INVALID_ARG
+    for bad in (dict(B=-1), dict(T=-1), dict(H=-1), dict(scale=math.inf), dict(scale=math.nan)):
+        assert chunk_bwd(lib, **bad) == INV, bad
+    for name in ("q", "k", "v", "g", "beta", "dout", "dq", "dk", "dv", "dg", "dbeta"):
+        assert chunk_bwd(lib, **{name: NULL}) == INV, name
+    for name in ("q", "g", "dout", "h0", "dhT", "dq", "dg", "dh0"):
+        assert chunk_bwd(lib, **{name: ctypes.c_void_p(A * 20 + 8)}) == INV, name
+    for name in ("beta", "dbeta"):
+        assert chunk_bwd(lib, **{name: ctypes.c_void_p(A * 20 + 2)}) == INV, name
+    # a written buffer over an input, over the states, over another output
+    assert chunk_bwd(lib, dq=ctypes.c_void_p(A * 2 + 128)) == INV       # over k
+    assert chunk_bwd(lib, dg=ctypes.c_void_p(A * 7 + 1024)) == INV      # over dout
+    assert chunk_bwd(lib, dv=ctypes.c_void_p(A * 12 - 1024)) == INV     # over dg
+    assert chunk_bwd(lib, dbeta=ctypes.c_void_p(A * 5 + 8)) == INV      # over beta
+    assert chunk_bwd(lib, dh0=ctypes.c_void_p(A * 6 + 4096)) == INV     # over h0
+    assert chunk_bwd(lib, dh0=ctypes.c_void_p(A * 8 - 4096)) == INV     # over dhT
+    assert chunk_bwd(lib, dk=ctypes.c_void_p(A * 14 + 512)) == INV      # over dh0
+    # no batch or no heads: nothing to do
+    assert chunk_bwd(lib, B=0) == libkda.KDA_OK
+    assert chunk_bwd(lib, H=0) == libkda.KDA_OK
+    # no tokens and no initial-state gradient asked for: nothing to do
+    assert chunk_bwd(lib, T=0, dh0=NULL) == libkda.KDA_OK
+
+
+def test_chunk_bwd_grid_limit(lib):
+    # 4096 heads x 2049 chunks of workgroups exceed the launch limit
+    assert chunk_bwd(lib, spacing=1 << 40, H=4096, T=64 * 2048 + 1) == libkda.KDA_ERR_UNSUPPORTED
