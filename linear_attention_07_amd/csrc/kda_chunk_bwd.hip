@@ -624,72 +624,101 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     // row side:  a_rc = sum_i dP_ri E_ric kh_ic,  b_rc = sum_i dN_ri E_ric kh_ic
     // column side: c_ic = sum_r (dP_ri kh_rc + dN_ri qh_rc) E_ric
     // with E_ric = exp(Gam_rc - Gam_ic) (i <= r); then dkh += a + c, dqh += b,
-    // dGam += kh a + qh b - kh c.
+    // dGam += kh a + qh b - kh c.  E is split about a reference row per
+    // 16-row block, as in the forward: with g >= -5 each factor stays within
+    // exp(+-75), finite in fp32.
+    //   row side, i in block b, reference e = 16 b + 15:
+    //     E = exp(Gam_r - Gam_e) exp(Gam_e - Gam_i), rows r >= 16 b;
+    //   column side, r in block a, reference s0 = 16 a:
+    //     E = exp(Gam_r - Gam_s0) exp(Gam_s0 - Gam_i), rows i <= 16 a + 15.
+    // The per-block factor matrices (16 x 128) take the space of X.
     {
-        float gown[4][4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) gown[m][n] = s.gam[i0 + m][ct + 32 * n];
-        float ta[4][4], tb[4][4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) ta[m][n] = tb[m][n] = 0.f;
-        for (int i = 0; i < kChunk; ++i) {
-            float ki[4], gi[4];
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                ki[n] = s.kh[i][ct + 32 * n];
-                gi[n] = s.gam[i][ct + 32 * n];
+        float (*f1)[kD] = reinterpret_cast<float (*)[kD]>(&s.x[0][0]);       // [16][128]
+        float (*f2)[kD] = reinterpret_cast<float (*)[kD]>(&s.x[0][0] + kSub * kD);
+        __syncthreads();  // X is dead
+        for (int blk = 0; blk < kChunk / kSub; ++blk) {
+            const int r0 = kSub * blk, e = r0 + kSub - 1;
+            // kh_i exp(Gam_e - Gam_i) for i in block blk
+            for (int idx = tid; idx < kSub * kD; idx += kCT) {
+                const int kk = idx / kD, cc = idx % kD;
+                f1[kk][cc] = s.kh[r0 + kk][cc] * ex(s.gam[e][cc] - s.gam[r0 + kk][cc]);
             }
+            __syncthreads();
+            if (i0 + 3 >= r0) {
+                float pa[4][4] = {}, pb[4][4] = {};
+#pragma unroll 2
+                for (int kk = 0; kk < kSub; ++kk) {
+                    float fv[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float dp = s.p[i0 + m][i], dn = s.n[i0 + m][i];
+                    for (int n = 0; n < 4; ++n) fv[n] = f1[kk][ct + 32 * n];
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const float w = i <= i0 + m ? ex(gown[m][n] - gi[n]) * ki[n] : 0.f;
-                    ta[m][n] = fmaf(dp, w, ta[m][n]);
-                    tb[m][n] = fmaf(dn, w, tb[m][n]);
+                    for (int m = 0; m < 4; ++m) {
+                        const float dp = s.p[i0 + m][r0 + kk], dn = s.n[i0 + m][r0 + kk];
+#pragma unroll
+                        for (int n = 0; n < 4; ++n) {
+                            pa[m][n] = fmaf(dp, fv[n], pa[m][n]);
+                            pb[m][n] = fmaf(dn, fv[n], pb[m][n]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (i0 + m < r0) continue;
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        const int cc = ct + 32 * n;
+                        const float f = ex(s.gam[i0 + m][cc] - s.gam[e][cc]);
+                        const float ta = f * pa[m][n], tb = f * pb[m][n];
+                        dkh[m][n] += ta;
+                        dqh[m][n] += tb;
+                        dgm[m][n] = fmaf(s.kh[i0 + m][cc], ta, fmaf(s.qh[i0 + m][cc], tb, dgm[m][n]));
+                    }
                 }
             }
+            __syncthreads();
         }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const float khv = s.kh[i0 + m][ct + 32 * n], qhv = s.qh[i0 + m][ct + 32 * n];
-                dkh[m][n] += ta[m][n];
-                dqh[m][n] += tb[m][n];
-                dgm[m][n] = fmaf(khv, ta[m][n], fmaf(qhv, tb[m][n], dgm[m][n]));
-                ta[m][n] = 0.f;
+        for (int blk = 0; blk < kChunk / kSub; ++blk) {
+            const int r0 = kSub * blk;
+            // kh_r exp(Gam_r - Gam_s0) and qh_r exp(Gam_r - Gam_s0) for r in block blk
+            for (int idx = tid; idx < kSub * kD; idx += kCT) {
+                const int kk = idx / kD, cc = idx % kD;
+                const float f = ex(s.gam[r0 + kk][cc] - s.gam[r0][cc]);
+                f1[kk][cc] = s.kh[r0 + kk][cc] * f;
+                f2[kk][cc] = s.qh[r0 + kk][cc] * f;
             }
-        for (int r = 0; r < kChunk; ++r) {
-            float kr[4], qr[4], gr[4];
+            __syncthreads();
+            if (i0 <= r0 + kSub - 1) {
+                float pc[4][4] = {};
+#pragma unroll 2
+                for (int kk = 0; kk < kSub; ++kk) {
+                    float fk[4], fq[4];
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                kr[n] = s.kh[r][ct + 32 * n];
-                qr[n] = s.qh[r][ct + 32 * n];
-                gr[n] = s.gam[r][ct + 32 * n];
-            }
+                    for (int n = 0; n < 4; ++n) {
+                        fk[n] = f1[kk][ct + 32 * n];
+                        fq[n] = f2[kk][ct + 32 * n];
+                    }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float dp = s.p[r][i0 + m], dn = s.n[r][i0 + m];
+                    for (int m = 0; m < 4; ++m) {
+                        const float dp = s.p[r0 + kk][i0 + m], dn = s.n[r0 + kk][i0 + m];
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const float e = r >= i0 + m ? ex(gr[n] - gown[m][n]) : 0.f;
-                    ta[m][n] = fmaf(fmaf(dp, kr[n], dn * qr[n]), e, ta[m][n]);
+                        for (int n = 0; n < 4; ++n)
+                            pc[m][n] = fmaf(dp, fk[n], fmaf(dn, fq[n], pc[m][n]));
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (i0 + m > r0 + kSub - 1) continue;
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        const int cc = ct + 32 * n;
+                        const float tc = ex(s.gam[r0][cc] - s.gam[i0 + m][cc]) * pc[m][n];
+                        dkh[m][n] += tc;
+                        dgm[m][n] = fmaf(-s.kh[i0 + m][cc], tc, dgm[m][n]);
+                    }
                 }
             }
+            __syncthreads();
         }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const float khv = s.kh[i0 + m][ct + 32 * n];
-                dkh[m][n] += ta[m][n];
-                dgm[m][n] = fmaf(-khv, ta[m][n], dgm[m][n]);
-            }
     }
     __syncthreads();  // every read of Gam is done: its space takes dGam
 
