@@ -79,9 +79,9 @@ def parse():
     return ap.parse_args()
 
 
-# the sources the measured forward kernels and their launches are built from
-MEASURED_SOURCES = ("kda_api.hip", "kda_bf16.hpp", "kda_chunk16.hip", "kda_common.hpp",
-                    "kda_decode.hip", "kda_launch.hpp")
+# the sources the measured kernels and their launches are built from
+MEASURED_SOURCES = ("kda_api.hip", "kda_bf16.hpp", "kda_chunk.hip", "kda_chunk16.hip",
+                    "kda_chunk_bwd.hip", "kda_common.hpp", "kda_decode.hip", "kda_launch.hpp")
 
 
 def kernel_sources_digest():
@@ -448,6 +448,7 @@ def main():
                 "unit": "TFLOP/s",
                 "frac": round(pb_tflops / FP32_VALU_PEAK_TFLOPS, 4),
                 "algorithmic_flop_per_call": pb_flop,
+                "traffic": measured_traffic("prefill_bwd_8k"),
                 "algorithmic_bytes_per_call": pb_bytes,
                 "hbm_GBps_algorithmic": round(pb_bytes / (pbms / 1e3) / 1e9, 1),
             },
