@@ -129,6 +129,37 @@ __device__ __forceinline__ void mm4(int K, FA&& A4, FB&& B4, FO&& out) {
         for (int n = 0; n < TN; ++n) out(m, n, i0 + m, ct + CT * n, acc[m][n]);
 }
 
+// C[M][N] = sum_k A(i, k) B(k, j) on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32), with the operand functors of mm4.  The result is
+// cut into 16 x 16 tiles dealt round-robin to the NT / 64 waves.  For a tile
+// at (i0, j0), lane (n = lane % 16, g = lane / 16) loads A(i0 + n, k0 + 4g ..
+// + 3) and B(k0 + 4g .. + 3, j0 + n); MFMA e of a 16-wide k block takes value
+// e of each, so lane (n, g) stands for k = k0 + 4g + e in both operands.  The
+// accumulator holds C[i0 + 4g + e][j0 + n], handed to out(i, j, value).  K is a
+// multiple of 16.
+template <int M, int N, int NT, class FA, class FB, class FO>
+__device__ __forceinline__ void mmf(int K, FA&& A4, FB&& B4, FO&& out) {
+    constexpr int TR = M / 16, TC = N / 16, W = NT / 64;
+    static_assert(M % 16 == 0 && N % 16 == 0 && NT % 64 == 0, "16 x 16 tiles, whole waves");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    for (int t = w; t < TR * TC; t += W) {
+        const int i0 = 16 * (t / TC), j0 = 16 * (t % TC);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            const float4 a = A4(i0 + n, k0 + 4 * g);
+            const float4 b = B4(k0 + 4 * g, j0 + n);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out(i0 + 4 * g + e, j0 + n, acc[e]);
+    }
+}
+
 __device__ __forceinline__ float4 ld4(const float* p) {
     return *reinterpret_cast<const float4*>(p);
 }
@@ -327,10 +358,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
 
 // ---------------------------------------------------------------------------
 // Chunk gradients: one 512-thread workgroup per (b, h, chunk) (two waves per
-// SIMD).  Results over [64][128] (token row x channel) use the micro-tile of
-// mm4<64, 128, 4, 4>: thread t owns rows 4 (t / 32) + m and channels t % 32 +
-// 32 n, and keeps its share of dkh, dqh and dGam in registers from the first
-// contribution to the last.
+// SIMD).  The products run on the fp32 matrix cores (mmf); for the element-wise
+// part over [64][128] (token row x channel) thread t owns rows 4 (t / 32) + m
+// and channels t % 32 + 32 n, and keeps its share of dkh, dqh and dGam in
+// registers from the first contribution to the last.
 // ---------------------------------------------------------------------------
 constexpr int kCT = 512;
 constexpr int kPK = kD + 4;  // row pitch of the per-channel arrays: rows 16 B apart in bank
@@ -486,19 +517,19 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         return r < L ? ld4(p + base + (size_t)r * rp + col) : z4;
     };
     // ---- R = V - Kt S --------------------------------------------------------
-    mm4<kChunk, kD, 4, 4, kCT>(
+    mmf<kChunk, kD, kCT>(
         kD, [&](int i, int kk) { return mul4(exp4(ld4(&s.gam[i][kk])), ld4(&s.kh[i][kk])); },
         [&](int kk, int j) { return col4(S + (size_t)kk * kD + j, kD); },
-        [&](int, int, int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
+        [&](int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
     __syncthreads();
     // ---- U = T R,  T = X diag(beta) ------------------------------------------
-    mm4<kChunk, kD, 4, 4, kCT>(
+    mmf<kChunk, kD, kCT>(
         kChunk, [&](int i, int kk) { return mul4(ld4(&s.x[i][kk]), ld4(&s.beta[kk])); },
         [&](int kk, int j) { return col4(R_ + kk * kD + j, kD); },
-        [&](int, int, int i, int j, float a) { U_[i * kD + j] = a; });
+        [&](int i, int j, float a) { U_[i * kD + j] = a; });
     __syncthreads();
     // ---- dU = scale M^T dO + Kb dS' ------------------------------------------
-    mm4<kChunk, kD, 4, 4, kCT>(
+    mmf<kChunk, kD, kCT>(
         kChunk + kD,
         [&](int i, int kk) {
             if (kk < kChunk) return scale4(col4(&s.n[kk][i], kChunk), scale);
@@ -515,107 +546,103 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             }
             return col4(dSn + (size_t)(kk - kChunk) * kD + j, kD);
         },
-        [&](int, int, int i, int j, float a) { dU_[i * kD + j] = a; });
+        [&](int i, int j, float a) { dU_[i * kD + j] = a; });
     __syncthreads();
     // ---- dV = dR = T^T dU ----------------------------------------------------
-    mm4<kChunk, kD, 4, 4, kCT>(
+    mmf<kChunk, kD, kCT>(
         kChunk, [&](int i, int kk) { return scale4(col4(&s.x[kk][i], kChunk), s.beta[i]); },
         [&](int kk, int j) { return col4(dU_ + kk * kD + j, kD); },
-        [&](int, int, int i, int j, float a) {
+        [&](int i, int j, float a) {
             if (i < L) dv[base + (size_t)i * rp + j] = a;
         });
-    // ---- dX = lower-incl(dU R^T) diag(beta); dbeta_j += sum_i X_ij dT_ij ------
-    {
-        float pb[4] = {0.f, 0.f, 0.f, 0.f};
-        mm4<kChunk, kChunk, 2, 4, kCT>(
-            kD, [&](int i, int kk) { return ld4(dU_ + i * kD + kk); },
-            [&](int kk, int j) { return ld4(R_ + j * kD + kk); },
-            [&](int, int n, int i, int j, float a) {
-                const float dt = j <= i ? a : 0.f;
-                dX_[i * kChunk + j] = dt * s.beta[j];
-                pb[n] = fmaf(s.x[i][j], dt, pb[n]);
-            });
-#pragma unroll
-        for (int n = 0; n < 4; ++n) s.red[(tid / 16) * kChunk + tid % 16 + 16 * n] = pb[n];
-    }
-    __syncthreads();
-    if (tid < kChunk) {
-        float a = 0.f;
-        for (int rg = 0; rg < 32; ++rg) a += s.red[rg * kChunk + tid];
-        s.dbeta[tid] = a;
-    }
+    // ---- dT = lower-incl(dU R^T), into dX's space -----------------------------
+    mmf<kChunk, kChunk, kCT>(
+        kD, [&](int i, int kk) { return ld4(dU_ + i * kD + kk); },
+        [&](int kk, int j) { return ld4(R_ + j * kD + kk); },
+        [&](int i, int j, float a) { dX_[i * kChunk + j] = j <= i ? a : 0.f; });
     // ---- dM = scale lower-incl(dO U^T), over N ---------------------------------
-    mm4<kChunk, kChunk, 2, 4, kCT>(
+    mmf<kChunk, kChunk, kCT>(
         kD, [&](int i, int kk) { return in4(dout, i, kk); },
         [&](int kk, int j) { return ld4(U_ + j * kD + kk); },
-        [&](int, int, int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
-    // ---- Y = X^T dX ------------------------------------------------------------
-    mm4<kChunk, kChunk, 2, 4, kCT>(
-        kChunk, [&](int i, int kk) { return col4(&s.x[kk][i], kChunk); },
-        [&](int kk, int j) { return col4(dX_ + kk * kChunk + j, kChunk); },
-        [&](int, int, int i, int j, float a) { Y_[i * kChunk + j] = a; });
+        [&](int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
     __syncthreads();
-    // ---- dA = -strict-lower(Y X^T); dbeta_i += sum_j dA_ij P_ij; dP over P ----
-    {
-        float pr[4] = {0.f, 0.f, 0.f, 0.f};
-        mm4<kChunk, kChunk, 2, 4, kCT>(
-            kChunk, [&](int i, int kk) { return ld4(Y_ + i * kChunk + kk); },
-            [&](int kk, int j) { return ld4(&s.x[j][kk]); },
-            [&](int m, int, int i, int j, float a) {
-                const float da = j < i ? -a : 0.f;
-                pr[m] = fmaf(da, s.p[i][j], pr[m]);
-                s.p[i][j] = s.beta[i] * da;
-            });
-#pragma unroll
-        for (int m = 0; m < 2; ++m) s.red[(tid % 16) * kChunk + (tid / 16) * 2 + m] = pr[m];
-    }
-    __syncthreads();
+    // dbeta_j = sum_i X_ij dT_ij (one thread per column, rows in order), then
+    // dX = dT diag(beta) in place
     if (tid < kChunk) {
-        float a = s.dbeta[tid];
-        for (int ct = 0; ct < 16; ++ct) a += s.red[ct * kChunk + tid];
+        float a = 0.f;
+        for (int i = tid; i < kChunk; ++i) a = fmaf(s.x[i][tid], dX_[i * kChunk + tid], a);
         s.dbeta[tid] = a;
     }
+    __syncthreads();
+    for (int idx = tid; idx < kChunk * kChunk; idx += kCT)
+        dX_[idx] *= s.beta[idx % kChunk];
+    __syncthreads();
+    // ---- Y = X^T dX ------------------------------------------------------------
+    mmf<kChunk, kChunk, kCT>(
+        kChunk, [&](int i, int kk) { return col4(&s.x[kk][i], kChunk); },
+        [&](int kk, int j) { return col4(dX_ + kk * kChunk + j, kChunk); },
+        [&](int i, int j, float a) { Y_[i * kChunk + j] = a; });
+    __syncthreads();
+    // ---- dA = -strict-lower(Y X^T), into dX's space ----------------------------
+    mmf<kChunk, kChunk, kCT>(
+        kChunk, [&](int i, int kk) { return ld4(Y_ + i * kChunk + kk); },
+        [&](int kk, int j) { return ld4(&s.x[j][kk]); },
+        [&](int i, int j, float a) { dX_[i * kChunk + j] = j < i ? -a : 0.f; });
+    __syncthreads();
+    // dbeta_i += sum_j dA_ij P_ij (one thread per row, columns in order), then
+    // dP = diag(beta) dA over P
+    if (tid < kChunk) {
+        float a = s.dbeta[tid];
+        for (int j = 0; j < tid; ++j) a = fmaf(dX_[tid * kChunk + j], s.p[tid][j], a);
+        s.dbeta[tid] = a;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kChunk * kChunk; idx += kCT) {
+        const int i = idx / kChunk, j = idx % kChunk;
+        s.p[i][j] = s.beta[i] * dX_[idx];
+    }
 
-    // ---- per-element accumulators of dkh, dqh, dGam (micro-tile 8 x 4) -------
-    const int i0 = (tid / 32) * 4, ct = tid % 32;
-    float dkh[4][4], dqh[4][4], dgm[4][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) dkh[m][n] = dqh[m][n] = dgm[m][n] = 0.f;
-
-    // dQt = scale dO S^T:  dqh += e^Gam dQt,  dGam += Qt dQt
-    mm4<kChunk, kD, 4, 4, kCT>(
+    // ---- dQt = scale dO S^T, dKt = -dR S^T, dKb = U dS'^T into the scratch ---
+    float* dQt_ = R_;   // R is dead
+    float* dKt_ = dU_;  // dU is dead
+    float* dKb_ = dX_;  // dA is in P now; dX and X^T dX are dead (64 x 128 over both)
+    __syncthreads();
+    mmf<kChunk, kD, kCT>(
         kD, [&](int i, int kk) { return in4(dout, i, kk); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
-        [&](int m, int n, int i, int j, float a) {
-            const float d = scale * a, e = ex(s.gam[i][j]);
-            dqh[m][n] = fmaf(e, d, dqh[m][n]);
-            dgm[m][n] = fmaf(e * s.qh[i][j], d, dgm[m][n]);
-        });
-    // dKt = -dR S^T:  dkh += e^Gam dKt,  dGam += Kt dKt
-    mm4<kChunk, kD, 4, 4, kCT>(
+        [&](int i, int j, float a) { dQt_[i * kD + j] = scale * a; });
+    mmf<kChunk, kD, kCT>(
         kD, [&](int i, int kk) { return scale4(in4(dv, i, kk), -1.f); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
-        [&](int m, int n, int i, int j, float a) {
-            const float e = ex(s.gam[i][j]);
-            dkh[m][n] = fmaf(e, a, dkh[m][n]);
-            dgm[m][n] = fmaf(e * s.kh[i][j], a, dgm[m][n]);
-        });
-    // dKb = U dS'^T:  dkh += e^(GL - Gam) dKb,  dGam -= Kb dKb, last row += Kb dKb
-    __syncthreads();  // the dbeta reduction has read red
+        [&](int i, int j, float a) { dKt_[i * kD + j] = a; });
+    mmf<kChunk, kD, kCT>(
+        kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
+        [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
+        [&](int i, int j, float a) { dKb_[i * kD + j] = a; });
+    __syncthreads();
+
+    // ---- per-element accumulators of dkh, dqh, dGam (thread t: rows
+    // 4 (t / 32) + m, channels t % 32 + 32 n) --------------------------------
+    const int i0 = (tid / 32) * 4, ct = tid % 32;
+    float dkh[4][4], dqh[4][4], dgm[4][4];
     {
         float pl[4] = {0.f, 0.f, 0.f, 0.f};
-        mm4<kChunk, kD, 4, 4, kCT>(
-            kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
-            [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
-            [&](int m, int n, int i, int j, float a) {
-                const float e = ex(s.gl[j] - s.gam[i][j]);
-                const float t = e * s.kh[i][j] * a;
-                dkh[m][n] = fmaf(e, a, dkh[m][n]);
-                dgm[m][n] -= t;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int i = i0 + m, j = ct + 32 * n;
+                const float e = ex(s.gam[i][j]), eb = ex(s.gl[j] - s.gam[i][j]);
+                const float dqt = dQt_[i * kD + j], dkt = dKt_[i * kD + j];
+                const float dkb = dKb_[i * kD + j];
+                const float t = eb * s.kh[i][j] * dkb;
+                // dqh = e^Gam dQt; dkh = e^Gam dKt + e^(GL - Gam) dKb;
+                // dGam = Qt dQt + Kt dKt - Kb dKb; the last row also gets Kb dKb
+                dqh[m][n] = e * dqt;
+                dkh[m][n] = fmaf(e, dkt, eb * dkb);
+                dgm[m][n] = fmaf(e * s.qh[i][j], dqt, fmaf(e * s.kh[i][j], dkt, -t));
                 pl[n] += t;
-            });
+            }
 #pragma unroll
         for (int n = 0; n < 4; ++n) s.red[(tid / 32) * kD + ct + 32 * n] = pl[n];
     }
