@@ -167,6 +167,10 @@ __device__ __forceinline__ float4 ld4(const float* p) {
 __device__ __forceinline__ float4 col4(const float* p, size_t pitch) {
     return make_float4(p[0], p[pitch], p[2 * pitch], p[3 * pitch]);
 }
+// four consecutive values at any 4-byte alignment
+__device__ __forceinline__ float4 lc4(const float* p) {
+    return make_float4(p[0], p[1], p[2], p[3]);
+}
 __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
     return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
 }
@@ -266,19 +270,22 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
         }
         __syncthreads();
         // Z = T V - W S
-        mm<kChunk, kScanCols, 2, 4, kScanThreads>(
+        mmf<kChunk, kScanCols, kScanThreads>(
             kChunk + kD,
             [&](int i, int k) {
-                return k < kChunk ? s.Tm[i * kP64 + k] : -s.W[i * kP128 + (k - kChunk)];
+                return k < kChunk ? lc4(&s.Tm[i * kP64 + k])
+                                  : scale4(lc4(&s.W[i * kP128 + (k - kChunk)]), -1.f);
             },
-            [&](int k, int j) { return k < kChunk ? s.V[k][j] : s.S[k - kChunk][j]; },
-            [&](int, int, int i, int j, float a) { s.Z[i][j] = a; });
+            [&](int k, int j) {
+                return k < kChunk ? col4(&s.V[k][j], kScanCols) : col4(&s.S[k - kChunk][j], kScanCols);
+            },
+            [&](int i, int j, float a) { s.Z[i][j] = a; });
         __syncthreads();
-        // S' = Diag(gamma) S + Kb^T Z (each thread updates only its own entries)
-        mm<kD, kScanCols, 4, 4, kScanThreads>(
-            kChunk, [&](int i, int k) { return s.KT[i * kP64 + k]; },
-            [&](int k, int j) { return s.Z[k][j]; },
-            [&](int, int, int i, int j, float a) { s.S[i][j] = fmaf(s.gam[i], s.S[i][j], a); });
+        // S' = Diag(gamma) S + Kb^T Z (each lane updates only its own entries)
+        mmf<kD, kScanCols, kScanThreads>(
+            kChunk, [&](int i, int k) { return lc4(&s.KT[i * kP64 + k]); },
+            [&](int k, int j) { return col4(&s.Z[k][j], kScanCols); },
+            [&](int i, int j, float a) { s.S[i][j] = fmaf(s.gam[i], s.S[i][j], a); });
     }
 }
 
@@ -331,22 +338,25 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
         }
         __syncthreads();
         // Y = Kb dS'   (Kb[i][k] = Kb^T[k][i])
-        mm<kChunk, kScanCols, 2, 4, kScanThreads>(
-            kD, [&](int i, int k) { return s.KW[k * kP64 + i]; },
-            [&](int k, int j) { return s.D[k][j]; },
-            [&](int, int, int i, int j, float a) { s.Y[i][j] = a; });
+        mmf<kChunk, kScanCols, kScanThreads>(
+            kD, [&](int i, int k) { return col4(&s.KW[k * kP64 + i], kP64); },
+            [&](int k, int j) { return col4(&s.D[k][j], kScanCols); },
+            [&](int i, int j, float a) { s.Y[i][j] = a; });
         __syncthreads();
         stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::W), kD, kChunk, kD, kChunk,
                             s.KW, kP128);
         __syncthreads();
         // dS = Diag(gamma) dS' - W^T Y + scale Q'^T dO
-        mm<kD, kScanCols, 4, 4, kScanThreads>(
+        mmf<kD, kScanCols, kScanThreads>(
             2 * kChunk,
             [&](int i, int k) {
-                return k < kChunk ? -s.KW[k * kP128 + i] : scale * s.QP[(k - kChunk) * kP128 + i];
+                return k < kChunk ? scale4(col4(&s.KW[k * kP128 + i], kP128), -1.f)
+                                  : scale4(col4(&s.QP[(k - kChunk) * kP128 + i], kP128), scale);
             },
-            [&](int k, int j) { return k < kChunk ? s.Y[k][j] : s.O[k - kChunk][j]; },
-            [&](int, int, int i, int j, float a) { s.D[i][j] = fmaf(s.gam[i], s.D[i][j], a); });
+            [&](int k, int j) {
+                return k < kChunk ? col4(&s.Y[k][j], kScanCols) : col4(&s.O[k - kChunk][j], kScanCols);
+            },
+            [&](int i, int j, float a) { s.D[i][j] = fmaf(s.gam[i], s.D[i][j], a); });
     }
     __syncthreads();
     if (dh0)
