@@ -466,14 +466,21 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             s.gam[r][tid] = a;
         }
         s.gl[tid] = a;
-    } else if (tid < 2 * kD) {  // dgamma = rowsum(dS' . S), times gamma for the last row of dGam
-        const int row = tid - kD;
-        float d = 0.f;
-        for (int j = 0; j < kD; ++j) d = fmaf(dSn[(size_t)row * kD + j], S[(size_t)row * kD + j], d);
-        s.dlast[row] = d;
     }
-    __syncthreads();
-    if (tid < kD) s.dlast[tid] *= ex(s.gl[tid]);
+    {  // dgamma = rowsum(dS' . S), times gamma for the last row of dGam: 4 threads a row
+        const int row = tid >> 2, part = tid & 3;
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = 32 * part + 4 * e;
+            const float4 a = ld4(dSn + (size_t)row * kD + col), b = ld4(S + (size_t)row * kD + col);
+            d += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+        }
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        __syncthreads();  // Gam's last row is complete
+        if (part == 0) s.dlast[row] = d * ex(s.gl[row]);
+    }
     // X = (I + A)^-1 of this chunk, as the record prep formed it
     stage<kCT>(xs + (size_t)blockIdx.x * kChunk * kChunk, kChunk, kChunk, kChunk, kChunk,
                     &s.x[0][0], kChunk);
@@ -576,14 +583,24 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         [&](int kk, int j) { return ld4(U_ + j * kD + kk); },
         [&](int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
     __syncthreads();
-    // dbeta_j = sum_i X_ij dT_ij (one thread per column, rows in order), then
-    // dX = dT diag(beta) in place
-    if (tid < kChunk) {
+    // dbeta_j = sum_i X_ij dT_ij (eight partial sums over 8 rows each, added in
+    // order), then dX = dT diag(beta) in place
+    {
+        const int j = tid % kChunk, part = tid / kChunk;
         float a = 0.f;
-        for (int i = tid; i < kChunk; ++i) a = fmaf(s.x[i][tid], dX_[i * kChunk + tid], a);
-        s.dbeta[tid] = a;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = 8 * part + u;
+            a = fmaf(s.x[i][j], dX_[i * kChunk + j], a);
+        }
+        s.red[part * kChunk + j] = a;
     }
     __syncthreads();
+    if (tid < kChunk) {
+        float a = 0.f;
+        for (int part = 0; part < kCT / kChunk; ++part) a += s.red[part * kChunk + tid];
+        s.dbeta[tid] = a;
+    }
     for (int idx = tid; idx < kChunk * kChunk; idx += kCT)
         dX_[idx] *= s.beta[idx % kChunk];
     __syncthreads();
@@ -599,11 +616,22 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         [&](int kk, int j) { return ld4(&s.x[j][kk]); },
         [&](int i, int j, float a) { dX_[i * kChunk + j] = j < i ? -a : 0.f; });
     __syncthreads();
-    // dbeta_i += sum_j dA_ij P_ij (one thread per row, columns in order), then
-    // dP = diag(beta) dA over P
+    // dbeta_i += sum_j dA_ij P_ij (eight partial sums over 8 columns each, added
+    // in order), then dP = diag(beta) dA over P
+    {
+        const int i = tid % kChunk, part = tid / kChunk;
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = 8 * part + u;
+            a = fmaf(dX_[i * kChunk + j], s.p[i][j], a);
+        }
+        s.red[part * kChunk + i] = a;
+    }
+    __syncthreads();
     if (tid < kChunk) {
         float a = s.dbeta[tid];
-        for (int j = 0; j < tid; ++j) a = fmaf(dX_[tid * kChunk + j], s.p[tid][j], a);
+        for (int part = 0; part < kCT / kChunk; ++part) a += s.red[part * kChunk + tid];
         s.dbeta[tid] = a;
     }
     __syncthreads();
