@@ -131,33 +131,45 @@ __device__ __forceinline__ void mm4(int K, FA&& A4, FB&& B4, FO&& out) {
 
 // C[M][N] = sum_k A(i, k) B(k, j) on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32), with the operand functors of mm4.  The result is
-// cut into 16 x 16 tiles dealt round-robin to the NT / 64 waves.  For a tile
-// at (i0, j0), lane (n = lane % 16, g = lane / 16) loads A(i0 + n, k0 + 4g ..
-// + 3) and B(k0 + 4g .. + 3, j0 + n); MFMA e of a 16-wide k block takes value
-// e of each, so lane (n, g) stands for k = k0 + 4g + e in both operands.  The
-// accumulator holds C[i0 + 4g + e][j0 + n], handed to out(i, j, value).  K is a
-// multiple of 16.
+// cut into 16 x 16 tiles; wave w takes column tile w mod (N / 16) and every
+// (NT / 64) / (N / 16)-th row tile from w / (N / 16) on, so the B operand it
+// loads serves all its tiles and their loads are in flight together.  For a
+// tile at (i0, j0), lane (n = lane % 16, g = lane / 16) loads A(i0 + n, k0 +
+// 4g .. + 3) and B(k0 + 4g .. + 3, j0 + n); MFMA e of a 16-wide k block takes
+// value e of each, so lane (n, g) stands for k = k0 + 4g + e in both operands.
+// The accumulator holds C[i0 + 4g + e][j0 + n], handed to out(i, j, value).
+// K is a multiple of 16.
 template <int M, int N, int NT, class FA, class FB, class FO>
 __device__ __forceinline__ void mmf(int K, FA&& A4, FB&& B4, FO&& out) {
     constexpr int TR = M / 16, TC = N / 16, W = NT / 64;
     static_assert(M % 16 == 0 && N % 16 == 0 && NT % 64 == 0, "16 x 16 tiles, whole waves");
+    static_assert(W % TC == 0 && (TR * TC) % W == 0, "each wave keeps one column tile");
+    constexpr int RPW = TR * TC / W;  // row tiles per wave
+    constexpr int RSTEP = W / TC;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
-    for (int t = w; t < TR * TC; t += W) {
-        const int i0 = 16 * (t / TC), j0 = 16 * (t % TC);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            const float4 a = A4(i0 + n, k0 + 4 * g);
-            const float4 b = B4(k0 + 4 * g, j0 + n);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
-        }
+    const int j0 = 16 * (w % TC), r0 = w / TC;
+    f32x4 acc[RPW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out(i0 + 4 * g + e, j0 + n, acc[e]);
+    for (int u = 0; u < RPW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const float4 b = B4(k0 + 4 * g, j0 + n);
+        float4 a[RPW];
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) a[u] = A4(16 * (r0 + RSTEP * u) + n, k0 + 4 * g);
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) {
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].x, b.x, acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].y, b.y, acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].z, b.z, acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].w, b.w, acc[u], 0, 0, 0);
+        }
     }
+#pragma unroll
+    for (int u = 0; u < RPW; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out(16 * (r0 + RSTEP * u) + 4 * g + e, j0 + n, acc[u][e]);
 }
 
 __device__ __forceinline__ float4 ld4(const float* p) {
