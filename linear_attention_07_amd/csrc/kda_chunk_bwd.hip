@@ -262,25 +262,73 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
         const int i = e / kScanCols, j = e % kScanCols;
         s.S[i][j] = h0 ? h0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
     }
-    for (int c = 0; c < nch; ++c) {
+    // The next chunk's record parts and V slice are loaded into registers while
+    // the current chunk computes: float4 number tid + 512 u of T (u < 2), W
+    // (u < 6), Kb^T (u < 10) and V (u < 12).
+    static_assert(kScanThreads == 512 && kScanCols == 64, "prefetch layout");
+    float4 pf[12];
+    float gpf = 0.f;
+    auto fetch = [&](int c) {
         const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
         const int L = min(kChunk, T - c * kChunk);
+        const float* Tg = reinterpret_cast<const float*>(r + RF::TH);
+        const float* Wg = reinterpret_cast<const float*>(r + RF::W);
+        const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
+        const float* Vg = v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+#pragma unroll
+        for (int u = 0; u < 12; ++u) {
+            if (u < 2) {
+                const int e = tid + 512 * u;
+                pf[u] = ld4(Tg + (e >> 4) * kChunk + 4 * (e & 15));
+            } else if (u < 6) {
+                const int e = tid + 512 * (u - 2);
+                pf[u] = ld4(Wg + (e >> 5) * kD + 4 * (e & 31));
+            } else if (u < 10) {
+                const int e = tid + 512 * (u - 6);
+                pf[u] = ld4(Kg + (e >> 4) * kChunk + 4 * (e & 15));
+            } else {
+                const int e = tid + 512 * (u - 10), row = e >> 4;
+                pf[u] = row < L ? ld4(Vg + (size_t)row * H * kD + 4 * (e & 15))
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        if (tid < kD) gpf = reinterpret_cast<const float*>(r + RF::G)[tid];
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int u = 0; u < 12; ++u) {
+            float* d;
+            if (u < 2) {
+                const int e = tid + 512 * u;
+                d = &s.Tm[(e >> 4) * kP64 + 4 * (e & 15)];
+            } else if (u < 6) {
+                const int e = tid + 512 * (u - 2);
+                d = &s.W[(e >> 5) * kP128 + 4 * (e & 31)];
+            } else if (u < 10) {
+                const int e = tid + 512 * (u - 6);
+                d = &s.KT[(e >> 4) * kP64 + 4 * (e & 15)];
+            } else {
+                const int e = tid + 512 * (u - 10);
+                d = &s.V[e >> 4][4 * (e & 15)];
+            }
+            d[0] = pf[u].x;
+            d[1] = pf[u].y;
+            d[2] = pf[u].z;
+            d[3] = pf[u].w;
+        }
+        if (tid < kD) s.gam[tid] = gpf;
+    };
+    fetch(0);
+    for (int c = 0; c < nch; ++c) {
         __syncthreads();  // the previous chunk's reads of the staged parts are done
-        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::TH), kChunk, kChunk, kChunk,
-                            kChunk, s.Tm, kP64);
-        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::W), kD, kChunk, kD, kChunk,
-                            s.W, kP128);
-        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::KT), kChunk, kD, kChunk, kD,
-                            s.KT, kP64);
-        stage<kScanThreads>(v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0,
-                            (size_t)H * kD, kChunk, kScanCols, L, &s.V[0][0], kScanCols);
-        if (tid < kD) s.gam[tid] = reinterpret_cast<const float*>(r + RF::G)[tid];
+        put();
         float* st = states + ((size_t)bh * nch + c) * kStateFloats;
         for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
             const int i = e / kScanCols, j = e % kScanCols;
             st[(size_t)i * kD + col0 + j] = s.S[i][j];
         }
         __syncthreads();
+        if (c + 1 < nch) fetch(c + 1);
         // Z = T V - W S
         mmf<kChunk, kScanCols, kScanThreads>(
             kChunk + kD,
@@ -332,17 +380,71 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
         const int i = e / kScanCols, j = e % kScanCols;
         s.D[i][j] = dhT ? dhT[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
     }
-    for (int c = nch - 1; c >= 0; --c) {
+    // The next chunk's record parts and dO slice are loaded into registers while
+    // the current chunk computes: float4 number tid + 512 u of Kb^T (u < 4),
+    // Q' (u < 8), dO (u < 10) and W (u < 14).
+    static_assert(kScanThreads == 512 && kScanCols == 64, "prefetch layout");
+    float4 pf[14];
+    float gpf = 0.f;
+    auto fetch = [&](int c) {
         const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
         const int L = min(kChunk, T - c * kChunk);
+        const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
+        const float* Qg = reinterpret_cast<const float*>(r + RF::QP);
+        const float* Wg = reinterpret_cast<const float*>(r + RF::W);
+        const float* Og = dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+#pragma unroll
+        for (int u = 0; u < 14; ++u) {
+            if (u < 4) {
+                const int e = tid + 512 * u;
+                pf[u] = ld4(Kg + (e >> 4) * kChunk + 4 * (e & 15));
+            } else if (u < 8) {
+                const int e = tid + 512 * (u - 4);
+                pf[u] = ld4(Qg + (e >> 5) * kD + 4 * (e & 31));
+            } else if (u < 10) {
+                const int e = tid + 512 * (u - 8), row = e >> 4;
+                pf[u] = row < L ? ld4(Og + (size_t)row * H * kD + 4 * (e & 15))
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                const int e = tid + 512 * (u - 10);
+                pf[u] = ld4(Wg + (e >> 5) * kD + 4 * (e & 31));
+            }
+        }
+        if (tid < kD) gpf = reinterpret_cast<const float*>(r + RF::G)[tid];
+    };
+    auto put4 = [&](float* d, float4 x) {
+        d[0] = x.x;
+        d[1] = x.y;
+        d[2] = x.z;
+        d[3] = x.w;
+    };
+    auto put = [&]() {  // Kb^T, Q', dO and gamma
+#pragma unroll
+        for (int u = 0; u < 10; ++u) {
+            if (u < 4) {
+                const int e = tid + 512 * u;
+                put4(&s.KW[(e >> 4) * kP64 + 4 * (e & 15)], pf[u]);
+            } else if (u < 8) {
+                const int e = tid + 512 * (u - 4);
+                put4(&s.QP[(e >> 5) * kP128 + 4 * (e & 31)], pf[u]);
+            } else {
+                const int e = tid + 512 * (u - 8);
+                put4(&s.O[e >> 4][4 * (e & 15)], pf[u]);
+            }
+        }
+        if (tid < kD) s.gam[tid] = gpf;
+    };
+    auto put_w = [&]() {  // W, over Kb^T
+#pragma unroll
+        for (int u = 10; u < 14; ++u) {
+            const int e = tid + 512 * (u - 10);
+            put4(&s.KW[(e >> 5) * kP128 + 4 * (e & 31)], pf[u]);
+        }
+    };
+    fetch(nch - 1);
+    for (int c = nch - 1; c >= 0; --c) {
         __syncthreads();  // the previous chunk's reads of the staged parts are done
-        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::KT), kChunk, kD, kChunk, kD,
-                            s.KW, kP64);
-        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::QP), kD, kChunk, kD, kChunk,
-                            s.QP, kP128);
-        stage<kScanThreads>(dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0,
-                            (size_t)H * kD, kChunk, kScanCols, L, &s.O[0][0], kScanCols);
-        if (tid < kD) s.gam[tid] = reinterpret_cast<const float*>(r + RF::G)[tid];
+        put();
         float* st = dsn + ((size_t)bh * nch + c) * kStateFloats;
         for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
             const int i = e / kScanCols, j = e % kScanCols;
@@ -355,9 +457,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
             [&](int k, int j) { return col4(&s.D[k][j], kScanCols); },
             [&](int i, int j, float a) { s.Y[i][j] = a; });
         __syncthreads();
-        stage<kScanThreads>(reinterpret_cast<const float*>(r + RF::W), kD, kChunk, kD, kChunk,
-                            s.KW, kP128);
+        put_w();
         __syncthreads();
+        if (c > 0) fetch(c - 1);
         // dS = Diag(gamma) dS' - W^T Y + scale Q'^T dO
         mmf<kD, kScanCols, kScanThreads>(
             2 * kChunk,
