@@ -599,45 +599,52 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     stage<kCT>(xs + (size_t)blockIdx.x * kChunk * kChunk, kChunk, kChunk, kChunk, kChunk,
                     &s.x[0][0], kChunk);
 
-    // ---- P (strict lower) and N (lower incl) with the exact pairwise decays ---
+    // ---- P (strict lower) and N (lower incl) on the matrix cores -------------
+    // For column block cb (i in 16 cb .. 16 cb + 15, reference row e = 16 cb +
+    // 15) and rows r >= 16 cb: exp(Gam_r - Gam_i) = exp(Gam_r - Gam_e) exp(Gam_e -
+    // Gam_i), both factors within exp(+-75) for g >= -5, so
+    //   P_ri = sum_c (kh_rc exp(Gam_rc - Gam_ec)) (kh_ic exp(Gam_ec - Gam_ic)),
+    // N likewise with qh_r; tiles above the diagonal blocks stay zero.
+    for (int idx = tid; idx < kChunk * kChunk; idx += kCT) {
+        (&s.p[0][0])[idx] = 0.f;
+        (&s.n[0][0])[idx] = 0.f;
+    }
+    __syncthreads();
     {
-        constexpr int CT = 16, TM = 2, TN = 4;
-        const int i0 = (tid / CT) * TM, ct = tid % CT;
-        float ap[TM][TN] = {}, an[TM][TN] = {};
-        for (int cc = 0; cc < kD; cc += 4) {
-            float4 kr[TM], qr[TM], gr[TM], ki[TN], gi[TN];
-#pragma unroll
-            for (int m = 0; m < TM; ++m) {
-                kr[m] = ld4(&s.kh[i0 + m][cc]);
-                qr[m] = ld4(&s.qh[i0 + m][cc]);
-                gr[m] = ld4(&s.gam[i0 + m][cc]);
+        const int lane = tid & 63, w = tid >> 6, n = lane & 15, g = lane >> 4;
+        for (int t = w; t < 10; t += kCT / 64) {  // the 10 tiles (rt, cb), rt >= cb
+            int cb = 0, rem = t;
+            while (rem >= 4 - cb) {
+                rem -= 4 - cb;
+                ++cb;
+            }
+            const int rt = cb + rem;
+            const int r = 16 * rt + n, i = 16 * cb + n, e = 16 * cb + 15;
+            f32x4 accp = {0.f, 0.f, 0.f, 0.f}, accn = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < kD; k0 += 16) {
+                const int c = k0 + 4 * g;
+                const float4 gr = ld4(&s.gam[r][c]), ge = ld4(&s.gam[e][c]);
+                const float4 gi = ld4(&s.gam[i][c]);
+                const float4 f = exp4(make_float4(gr.x - ge.x, gr.y - ge.y, gr.z - ge.z, gr.w - ge.w));
+                const float4 hh = exp4(make_float4(ge.x - gi.x, ge.y - gi.y, ge.z - gi.z, ge.w - gi.w));
+                const float4 ak = mul4(ld4(&s.kh[r][c]), f), aq = mul4(ld4(&s.qh[r][c]), f);
+                const float4 bk = mul4(ld4(&s.kh[i][c]), hh);
+                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bk.x, accp, 0, 0, 0);
+                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bk.y, accp, 0, 0, 0);
+                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bk.z, accp, 0, 0, 0);
+                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bk.w, accp, 0, 0, 0);
+                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bk.x, accn, 0, 0, 0);
+                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bk.y, accn, 0, 0, 0);
+                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.z, bk.z, accn, 0, 0, 0);
+                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.w, bk.w, accn, 0, 0, 0);
             }
 #pragma unroll
-            for (int n = 0; n < TN; ++n) {
-                ki[n] = ld4(&s.kh[ct + CT * n][cc]);
-                gi[n] = ld4(&s.gam[ct + CT * n][cc]);
+            for (int u = 0; u < 4; ++u) {
+                const int row = 16 * rt + 4 * g + u, col = 16 * cb + n;
+                s.p[row][col] = col < row ? accp[u] : 0.f;
+                s.n[row][col] = col <= row ? accn[u] : 0.f;
             }
-#pragma unroll
-            for (int m = 0; m < TM; ++m)
-#pragma unroll
-                for (int n = 0; n < TN; ++n) {
-                    if (ct + CT * n > i0 + m) continue;
-                    const float ex0 = ex(gr[m].x - gi[n].x) * ki[n].x;
-                    const float ex1 = ex(gr[m].y - gi[n].y) * ki[n].y;
-                    const float ex2 = ex(gr[m].z - gi[n].z) * ki[n].z;
-                    const float ex3 = ex(gr[m].w - gi[n].w) * ki[n].w;
-                    ap[m][n] += kr[m].x * ex0 + kr[m].y * ex1 + kr[m].z * ex2 + kr[m].w * ex3;
-                    an[m][n] += qr[m].x * ex0 + qr[m].y * ex1 + qr[m].z * ex2 + qr[m].w * ex3;
-                }
         }
-#pragma unroll
-        for (int m = 0; m < TM; ++m)
-#pragma unroll
-            for (int n = 0; n < TN; ++n) {
-                const int r = i0 + m, i = ct + CT * n;
-                s.p[r][i] = i < r ? ap[m][n] : 0.f;
-                s.n[r][i] = i <= r ? an[m][n] : 0.f;
-            }
     }
     __syncthreads();
     __syncthreads();
