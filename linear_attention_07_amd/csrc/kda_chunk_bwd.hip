@@ -32,8 +32,8 @@
 //         of the first as the initial state's gradient;
 //   chunk gradients, one workgroup per (batch, head, chunk), rebuilds the
 //         chunk's matrices from q, k, g, beta and writes dq, dk, dv, dg, dbeta.
-// Products run on the vector ALUs from LDS and L1/L2-resident operands, each
-// thread owning a fixed micro-tile of the result.
+// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) from
+// LDS and L1/L2-resident operands.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -41,7 +41,6 @@ namespace kda {
 namespace {
 
 using RF = ChunkRecF32;
-constexpr int kThreads = 256;
 constexpr int kScanCols = 64;              // value columns per scan workgroup
 constexpr int kScanSlices = kD / kScanCols;
 constexpr int kScanThreads = 512;
@@ -57,80 +56,9 @@ constexpr size_t kScrFloats = kScrY + kChunk * kChunk;
 
 __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// C[M][N] = sum_k A(i, k) B(k, j) for k < K.  Thread t owns rows
-// i0 .. i0 + TM - 1 (i0 = TM (t / (N / TN))) and columns ct + (N / TN) n,
-// n < TN (ct = t mod N / TN), so neighbouring threads read neighbouring
-// columns of B and threads of one row group share each A value.  Each result
-// goes to out(m, n, i, j, value).
-template <int M, int N, int TM, int TN, int NT = kThreads, class FA, class FB, class FO>
-__device__ __forceinline__ void mm(int K, FA&& A, FB&& B, FO&& out) {
-    constexpr int CT = N / TN;
-    static_assert((M / TM) * CT == NT, "micro-tiles must cover the result once");
-    const int t = threadIdx.x;
-    const int i0 = (t / CT) * TM, ct = t % CT;
-    float acc[TM][TN];
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
-#pragma unroll 2
-    for (int kk = 0; kk < K; ++kk) {
-        float a[TM], b[TN];
-#pragma unroll
-        for (int m = 0; m < TM; ++m) a[m] = A(i0 + m, kk);
-#pragma unroll
-        for (int n = 0; n < TN; ++n) b[n] = B(kk, ct + CT * n);
-#pragma unroll
-        for (int m = 0; m < TM; ++m)
-#pragma unroll
-            for (int n = 0; n < TN; ++n) acc[m][n] = fmaf(a[m], b[n], acc[m][n]);
-    }
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n) out(m, n, i0 + m, ct + CT * n, acc[m][n]);
-}
-
-// mm with k taken four at a time: A4(i, k) returns A(i, k .. k + 3) and
-// B4(k, j) returns B(k .. k + 3, j) as float4, so operands stored along k
-// load as one 16-byte access.  K is a multiple of 4.
-template <int M, int N, int TM, int TN, int NT = kThreads, class FA, class FB, class FO>
-__device__ __forceinline__ void mm4(int K, FA&& A4, FB&& B4, FO&& out) {
-    constexpr int CT = N / TN;
-    static_assert((M / TM) * CT == NT, "micro-tiles must cover the result once");
-    const int t = threadIdx.x;
-    const int i0 = (t / CT) * TM, ct = t % CT;
-    float acc[TM][TN];
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
-#pragma unroll 2
-    for (int kk = 0; kk < K; kk += 4) {
-        float4 a[TM], b[TN];
-#pragma unroll
-        for (int m = 0; m < TM; ++m) a[m] = A4(i0 + m, kk);
-#pragma unroll
-        for (int n = 0; n < TN; ++n) b[n] = B4(kk, ct + CT * n);
-#pragma unroll
-        for (int m = 0; m < TM; ++m)
-#pragma unroll
-            for (int n = 0; n < TN; ++n) {
-                float c = acc[m][n];
-                c = fmaf(a[m].x, b[n].x, c);
-                c = fmaf(a[m].y, b[n].y, c);
-                c = fmaf(a[m].z, b[n].z, c);
-                acc[m][n] = fmaf(a[m].w, b[n].w, c);
-            }
-    }
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n) out(m, n, i0 + m, ct + CT * n, acc[m][n]);
-}
-
 // C[M][N] = sum_k A(i, k) B(k, j) on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32), with the operand functors of mm4.  The result is
+// (v_mfma_f32_16x16x4_f32).  The operand functors return four values along k:
+// A4(i, k) = A(i, k .. k + 3), B4(k, j) = B(k .. k + 3, j).  The result is
 // cut into 16 x 16 tiles; wave w takes column tile w mod (N / 16) and every
 // (NT / 64) / (N / 16)-th row tile from w / (N / 16) on, so the B operand it
 // loads serves all its tiles and their loads are in flight together.  For a
