@@ -34,6 +34,8 @@
 //         chunk's matrices from q, k, g, beta and writes dq, dk, dv, dg, dbeta.
 // Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) from
 // LDS and L1/L2-resident operands.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -97,7 +99,14 @@ __device__ __forceinline__ void mmf(int K, FA&& A4, FB&& B4, FO&& out) {
 #pragma unroll
     for (int u = 0; u < RPW; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out(16 * (r0 + RSTEP * u) + 4 * g + e, j0 + n, acc[u][e]);
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * (r0 + RSTEP * u) + 4 * g + e;
+            // out(m, i, j, v) also gets the element's slot m = 4 u + e in the lane
+            if constexpr (std::is_invocable_v<FO, int, int, int, float>)
+                out(4 * u + e, i, j0 + n, acc[u][e]);
+            else
+                out(i, j0 + n, acc[u][e]);
+        }
 }
 
 __device__ __forceinline__ float4 ld4(const float* p) {
@@ -689,49 +698,49 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         s.p[i][j] = s.beta[i] * dX_[idx];
     }
 
-    // ---- dQt = scale dO S^T, dKt = -dR S^T, dKb = U dS'^T into the scratch ---
-    float* dQt_ = R_;   // R is dead
-    float* dKt_ = dU_;  // dU is dead
-    float* dKb_ = dX_;  // dA is in P now; dX and X^T dX are dead (64 x 128 over both)
-    __syncthreads();
+    // ---- element-wise part over [64][128] ------------------------------------
+    // Lane (n, g) of wave w owns channel cc = 16 w + n and rows 16 u + 4 g + e
+    // (u, e < 4; slot m = 4 u + e): the accumulator layout of column tile w in
+    // mmf<64, 128>, so the products below hand their results straight to it.
+    const int lane = tid & 63, wv = tid >> 6, g4 = 4 * (lane >> 4);
+    const int cc = 16 * wv + (lane & 15);
+    float dkh[16], dqh[16], dgm[16];
+    __syncthreads();  // dP is in P
+    // dQt = scale dO S^T:  dqh = e^Gam dQt,  dGam = Qt dQt
     mmf<kChunk, kD, kCT>(
         kD, [&](int i, int kk) { return in4(dout, i, kk); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
-        [&](int i, int j, float a) { dQt_[i * kD + j] = scale * a; });
+        [&](int m, int i, int j, float a) {
+            const float d = scale * a, e = ex(s.gam[i][j]);
+            dqh[m] = e * d;
+            dgm[m] = e * s.qh[i][j] * d;
+        });
+    // dKt = -dR S^T:  dkh = e^Gam dKt,  dGam += Kt dKt
     mmf<kChunk, kD, kCT>(
         kD, [&](int i, int kk) { return scale4(in4(dv, i, kk), -1.f); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
-        [&](int i, int j, float a) { dKt_[i * kD + j] = a; });
-    mmf<kChunk, kD, kCT>(
-        kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
-        [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
-        [&](int i, int j, float a) { dKb_[i * kD + j] = a; });
-    __syncthreads();
-
-    // ---- per-element accumulators of dkh, dqh, dGam (thread t: rows
-    // 4 (t / 32) + m, channels t % 32 + 32 n) --------------------------------
-    const int i0 = (tid / 32) * 4, ct = tid % 32;
-    float dkh[4][4], dqh[4][4], dgm[4][4];
+        [&](int m, int i, int j, float a) {
+            const float e = ex(s.gam[i][j]);
+            dkh[m] = e * a;
+            dgm[m] = fmaf(e * s.kh[i][j], a, dgm[m]);
+        });
+    // dKb = U dS'^T:  dkh += e^(GL - Gam) dKb,  dGam -= Kb dKb; the last row of
+    // dGam also gets sum_r Kb dKb (per channel, into red[0 .. 127])
     {
-        float pl[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int i = i0 + m, j = ct + 32 * n;
-                const float e = ex(s.gam[i][j]), eb = ex(s.gl[j] - s.gam[i][j]);
-                const float dqt = dQt_[i * kD + j], dkt = dKt_[i * kD + j];
-                const float dkb = dKb_[i * kD + j];
-                const float t = eb * s.kh[i][j] * dkb;
-                // dqh = e^Gam dQt; dkh = e^Gam dKt + e^(GL - Gam) dKb;
-                // dGam = Qt dQt + Kt dKt - Kb dKb; the last row also gets Kb dKb
-                dqh[m][n] = e * dqt;
-                dkh[m][n] = fmaf(e, dkt, eb * dkb);
-                dgm[m][n] = fmaf(e * s.qh[i][j], dqt, fmaf(e * s.kh[i][j], dkt, -t));
-                pl[n] += t;
-            }
-#pragma unroll
-        for (int n = 0; n < 4; ++n) s.red[(tid / 32) * kD + ct + 32 * n] = pl[n];
+        float pl = 0.f;
+        mmf<kChunk, kD, kCT>(
+            kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
+            [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
+            [&](int m, int i, int j, float a) {
+                const float e = ex(s.gl[j] - s.gam[i][j]);
+                const float t = e * s.kh[i][j] * a;
+                dkh[m] = fmaf(e, a, dkh[m]);
+                dgm[m] -= t;
+                pl += t;
+            });
+        pl += __shfl_xor(pl, 16);
+        pl += __shfl_xor(pl, 32);
+        if (lane < 16) s.red[cc] = pl;
     }
 
     // ---- the pairwise-decay terms of P and N ---------------------------------
@@ -745,140 +754,114 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     //     E = exp(Gam_r - Gam_e) exp(Gam_e - Gam_i), rows r >= 16 b;
     //   column side, r in block a, reference s0 = 16 a:
     //     E = exp(Gam_r - Gam_s0) exp(Gam_s0 - Gam_i), rows i <= 16 a + 15.
-    // The per-block factor matrices (16 x 128) take the space of X.
+    // Each block's sums are a 16-deep product on the matrix cores; the factor
+    // matrices (16 x 128) take the space of X.
     {
         float (*f1)[kD] = reinterpret_cast<float (*)[kD]>(&s.x[0][0]);       // [16][128]
         float (*f2)[kD] = reinterpret_cast<float (*)[kD]>(&s.x[0][0] + kSub * kD);
-        __syncthreads();  // X is dead
         for (int blk = 0; blk < kChunk / kSub; ++blk) {
             const int r0 = kSub * blk, e = r0 + kSub - 1;
+            __syncthreads();  // X, or the previous block's factors, are no longer read
             // kh_i exp(Gam_e - Gam_i) for i in block blk
             for (int idx = tid; idx < kSub * kD; idx += kCT) {
-                const int kk = idx / kD, cc = idx % kD;
-                f1[kk][cc] = s.kh[r0 + kk][cc] * ex(s.gam[e][cc] - s.gam[r0 + kk][cc]);
+                const int kk = idx / kD, c = idx % kD;
+                f1[kk][c] = s.kh[r0 + kk][c] * ex(s.gam[e][c] - s.gam[r0 + kk][c]);
             }
             __syncthreads();
-            if (i0 + 3 >= r0) {
-                float pa[4][4] = {}, pb[4][4] = {};
-#pragma unroll 2
-                for (int kk = 0; kk < kSub; ++kk) {
-                    float fv[4];
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) fv[n] = f1[kk][ct + 32 * n];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const float dp = s.p[i0 + m][r0 + kk], dn = s.n[i0 + m][r0 + kk];
-#pragma unroll
-                        for (int n = 0; n < 4; ++n) {
-                            pa[m][n] = fmaf(dp, fv[n], pa[m][n]);
-                            pb[m][n] = fmaf(dn, fv[n], pb[m][n]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if (i0 + m < r0) continue;
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) {
-                        const int cc = ct + 32 * n;
-                        const float f = ex(s.gam[i0 + m][cc] - s.gam[e][cc]);
-                        const float ta = f * pa[m][n], tb = f * pb[m][n];
-                        dkh[m][n] += ta;
-                        dqh[m][n] += tb;
-                        dgm[m][n] = fmaf(s.kh[i0 + m][cc], ta, fmaf(s.qh[i0 + m][cc], tb, dgm[m][n]));
-                    }
-                }
-            }
-            __syncthreads();
+            // a = F (dP[:, block] KG), b = F (dN[:, block] KG), F = exp(Gam_r - Gam_e)
+            mmf<kChunk, kD, kCT>(
+                kSub, [&](int i, int kk) { return ld4(&s.p[i][r0 + kk]); },
+                [&](int kk, int j) { return col4(&f1[kk][j], kD); },
+                [&](int m, int i, int j, float a) {
+                    if (i < r0) return;
+                    const float ta = ex(s.gam[i][j] - s.gam[e][j]) * a;
+                    dkh[m] += ta;
+                    dgm[m] = fmaf(s.kh[i][j], ta, dgm[m]);
+                });
+            mmf<kChunk, kD, kCT>(
+                kSub, [&](int i, int kk) { return ld4(&s.n[i][r0 + kk]); },
+                [&](int kk, int j) { return col4(&f1[kk][j], kD); },
+                [&](int m, int i, int j, float a) {
+                    if (i < r0) return;
+                    const float tb = ex(s.gam[i][j] - s.gam[e][j]) * a;
+                    dqh[m] += tb;
+                    dgm[m] = fmaf(s.qh[i][j], tb, dgm[m]);
+                });
         }
         for (int blk = 0; blk < kChunk / kSub; ++blk) {
             const int r0 = kSub * blk;
+            __syncthreads();
             // kh_r exp(Gam_r - Gam_s0) and qh_r exp(Gam_r - Gam_s0) for r in block blk
             for (int idx = tid; idx < kSub * kD; idx += kCT) {
-                const int kk = idx / kD, cc = idx % kD;
-                const float f = ex(s.gam[r0 + kk][cc] - s.gam[r0][cc]);
-                f1[kk][cc] = s.kh[r0 + kk][cc] * f;
-                f2[kk][cc] = s.qh[r0 + kk][cc] * f;
+                const int kk = idx / kD, c = idx % kD;
+                const float f = ex(s.gam[r0 + kk][c] - s.gam[r0][c]);
+                f1[kk][c] = s.kh[r0 + kk][c] * f;
+                f2[kk][c] = s.qh[r0 + kk][c] * f;
             }
             __syncthreads();
-            if (i0 <= r0 + kSub - 1) {
-                float pc[4][4] = {};
-#pragma unroll 2
-                for (int kk = 0; kk < kSub; ++kk) {
-                    float fk[4], fq[4];
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) {
-                        fk[n] = f1[kk][ct + 32 * n];
-                        fq[n] = f2[kk][ct + 32 * n];
-                    }
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const float dp = s.p[r0 + kk][i0 + m], dn = s.n[r0 + kk][i0 + m];
-#pragma unroll
-                        for (int n = 0; n < 4; ++n)
-                            pc[m][n] = fmaf(dp, fk[n], fmaf(dn, fq[n], pc[m][n]));
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if (i0 + m > r0 + kSub - 1) continue;
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) {
-                        const int cc = ct + 32 * n;
-                        const float tc = ex(s.gam[r0][cc] - s.gam[i0 + m][cc]) * pc[m][n];
-                        dkh[m][n] += tc;
-                        dgm[m][n] = fmaf(-s.kh[i0 + m][cc], tc, dgm[m][n]);
-                    }
-                }
-            }
-            __syncthreads();
+            // c = H (dP[block, :]^T KR + dN[block, :]^T QR), H = exp(Gam_s0 - Gam_i)
+            mmf<kChunk, kD, kCT>(
+                2 * kSub,
+                [&](int i, int kk) {
+                    return kk < kSub ? col4(&s.p[r0 + kk][i], kChunk)
+                                     : col4(&s.n[r0 + kk - kSub][i], kChunk);
+                },
+                [&](int kk, int j) {
+                    return kk < kSub ? col4(&f1[kk][j], kD) : col4(&f2[kk - kSub][j], kD);
+                },
+                [&](int m, int i, int j, float a) {
+                    if (i > r0 + kSub - 1) return;
+                    const float tc = ex(s.gam[r0][j] - s.gam[i][j]) * a;
+                    dkh[m] += tc;
+                    dgm[m] = fmaf(-s.kh[i][j], tc, dgm[m]);
+                });
         }
     }
-    __syncthreads();  // every read of Gam is done: its space takes dGam
 
     // ---- dg = reverse cumulative sum of dGam; the norms' backward -------------
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) s.gam[i0 + m][ct + 32 * n] = dgm[m][n];
+    // row dots qh . dqh and kh . dkh: over the 16 channels of the lane's column
+    // tile by shuffles, then over the 8 tiles in a fixed order
     {
-        // row dots qh . dqh and kh . dkh: 32 threads of a row group share a row
+        float* dq_part = s.red + kD;             // [8][64]
+        float* dk_part = s.red + kD + 8 * kChunk;  // [8][64]
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            float aq = 0.f, ak = 0.f;
+        for (int m = 0; m < 16; ++m) {
+            const int r = 16 * (m >> 2) + g4 + (m & 3);
+            float aq = s.qh[r][cc] * dqh[m], ak = s.kh[r][cc] * dkh[m];
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                aq = fmaf(s.qh[i0 + m][ct + 32 * n], dqh[m][n], aq);
-                ak = fmaf(s.kh[i0 + m][ct + 32 * n], dkh[m][n], ak);
-            }
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) {
+            for (int o = 1; o < 16; o <<= 1) {
                 aq += __shfl_xor(aq, o);
                 ak += __shfl_xor(ak, o);
             }
-            if (ct == 0) {
-                s.dotq[i0 + m] = aq;
-                s.dotk[i0 + m] = ak;
+            if ((lane & 15) == 0) {
+                dq_part[wv * kChunk + r] = aq;
+                dk_part[wv * kChunk + r] = ak;
             }
         }
+        __syncthreads();  // every read of Gam is done: its space takes dGam
+        if (tid < kChunk) {
+            float aq = 0.f, ak = 0.f;
+            for (int w = 0; w < kCT / 64; ++w) {
+                aq += dq_part[w * kChunk + tid];
+                ak += dk_part[w * kChunk + tid];
+            }
+            s.dotq[tid] = aq;
+            s.dotk[tid] = ak;
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s.gam[16 * (m >> 2) + g4 + (m & 3)][cc] = dgm[m];
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = i0 + m;
+    for (int m = 0; m < 16; ++m) {
+        const int r = 16 * (m >> 2) + g4 + (m & 3);
         if (r >= L) continue;
-        const float rq = s.rq[r], rk = s.rk[r], dtq = s.dotq[r], dtk = s.dotk[r];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int j = ct + 32 * n;
-            // qh = q / sqrt(|q|^2 + eps): dq = rq (dqh - qh (qh . dqh))
-            dq[base + (size_t)r * rp + j] = rq * fmaf(-s.qh[r][j], dtq, dqh[m][n]);
-            dk[base + (size_t)r * rp + j] = rk * fmaf(-s.kh[r][j], dtk, dkh[m][n]);
-        }
+        // qh = q / sqrt(|q|^2 + eps): dq = rq (dqh - qh (qh . dqh))
+        dq[base + (size_t)r * rp + cc] = s.rq[r] * fmaf(-s.qh[r][cc], s.dotq[r], dqh[m]);
+        dk[base + (size_t)r * rp + cc] = s.rk[r] * fmaf(-s.kh[r][cc], s.dotk[r], dkh[m]);
     }
     if (tid < kD) {
-        float a = s.dlast[tid];  // Gam of the last row also enters Kb and gamma
-        for (int rg = 0; rg < 16; ++rg) a += s.red[rg * kD + tid];
+        float a = s.dlast[tid] + s.red[tid];  // Gam of the last row also enters Kb and gamma
         for (int r = kChunk - 1; r >= 0; --r) {
             a += s.gam[r][tid];
             if (r < L) dg[base + (size_t)r * rp + tid] = a;
