@@ -277,7 +277,7 @@ KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k
  * 16-byte aligned (beta, dbeta 4).  B == 0 or H == 0 is a no-op; T == 0
  * copies dhT (or zeros) to dh0.  Workspace (the chunk records, the state
  * entering and the state gradient leaving every chunk, and per-chunk scratch:
- * about 400 KB per 64 tokens and head) comes from the library's stream-ordered
+ * about 430 KB per 64 tokens and head) comes from the library's stream-ordered
  * pool; KDA_ERR_NO_MEMORY if it cannot be had.  Computed in fp32; g obeys
  * the forward's bound (every entry in [-5, 0]), which the chunk records that
  * the two state scans read rely on.
@@ -287,6 +287,21 @@ KDA_API kda_status_t kda_chunk_bwd_f32(const float *q, const float *k, const flo
                                const float *h0, const float *dout, const float *dhT,
                                float *dq, float *dk, float *dv, float *dg, float *dbeta,
                                float *dh0, int B, int T, int H, hipStream_t stream);
+
+/*
+ * kda_chunk_bwd — kda_chunk_bwd_f32 for bf16 q, k, v and dout (the inputs of
+ * kda_chunk_fwd): q, k, v, dout are [B, T, H, 128] bf16, and dq, dk, dv are
+ * written as [B, T, H, 128] bf16 (rounded to nearest even from fp32).  g,
+ * beta, the states, dg, dbeta and dh0 are fp32; all arithmetic is fp32.  The
+ * gradients are those of the recurrence on the given bf16 values, not of the
+ * bf16 forward kernel's own roundings.  Validation, workspace and the T == 0
+ * case are those of kda_chunk_bwd_f32.
+ */
+KDA_API kda_status_t kda_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const float *g, const float *beta, float scale, const float *h0,
+                           const uint16_t *dout, const float *dhT, uint16_t *dq,
+                           uint16_t *dk, uint16_t *dv, float *dg, float *dbeta, float *dh0,
+                           int B, int T, int H, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);

@@ -201,11 +201,13 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     return st;
 }
 
-// Backward of the fp32 chunked prefill; see kda_chunk_bwd_f32 in kda.h.
-kda_status_t chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
-                           const float* beta, float scale, const float* h0, const float* dout,
-                           const float* dhT, float* dq, float* dk, float* dv, float* dg,
-                           float* dbeta, float* dh0, int B, int T, int H, hipStream_t stream) {
+// Backward of the chunked prefill; see kda_chunk_bwd_f32 and kda_chunk_bwd in
+// kda.h.  IO: float, or uint16_t for bf16 q / k / v / dout / dq / dk / dv.
+template <typename IO>
+kda_status_t chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g, const float* beta,
+                       float scale, const float* h0, const IO* dout, const float* dhT, IO* dq,
+                       IO* dk, IO* dv, float* dg, float* dbeta, float* dh0, int B, int T, int H,
+                       hipStream_t stream) {
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     if (B == 0 || H == 0) return KDA_OK;
@@ -221,24 +223,23 @@ kda_status_t chunk_bwd_f32(const float* q, const float* k, const float* v, const
         const hipError_t e = kda::launch_copy_or_zero(dhT, dh0, sbytes / sizeof(float), stream);
         return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
-    const float* ins[] = {q, k, v, g, dout};
-    float* outs[] = {dq, dk, dv, dg};
-    for (const float* p : ins)
-        if (!p || !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
-    for (const float* p : outs)
+    const void* ptrs[] = {q, k, v, g, dout, dq, dk, dv, dg};
+    for (const void* p : ptrs)
         if (!p || !aligned(p, 16)) return KDA_ERR_INVALID_ARG;
     if (!beta || !dbeta || !aligned(beta, 4) || !aligned(dbeta, 4)) return KDA_ERR_INVALID_ARG;
     const size_t n_tok = (size_t)B * T * H;
-    const size_t vb = n_tok * KDA_HEAD_DIM * sizeof(float), bb = n_tok * sizeof(float);
+    // IO arrays (q, k, v, dout, dq, dk, dv) and fp32 ones (g, dg)
+    const size_t vb = n_tok * KDA_HEAD_DIM * sizeof(IO), fb = n_tok * KDA_HEAD_DIM * sizeof(float);
+    const size_t bb = n_tok * sizeof(float);
     // every written buffer overlaps no other argument
     struct Buf {
         const void* p;
         size_t n;
     };
-    const Buf all[] = {{q, vb},  {k, vb},  {v, vb},      {g, vb},     {dout, vb},
+    const Buf all[] = {{q, vb},  {k, vb},  {v, vb},      {g, fb},     {dout, vb},
                        {beta, bb}, {h0, sbytes}, {dhT, sbytes}, {dq, vb}, {dk, vb},
-                       {dv, vb}, {dg, vb}, {dbeta, bb}, {dh0, sbytes}};
-    const Buf written[] = {{dq, vb}, {dk, vb}, {dv, vb}, {dg, vb}, {dbeta, bb}, {dh0, sbytes}};
+                       {dv, vb}, {dg, fb}, {dbeta, bb}, {dh0, sbytes}};
+    const Buf written[] = {{dq, vb}, {dk, vb}, {dv, vb}, {dg, fb}, {dbeta, bb}, {dh0, sbytes}};
     for (const Buf& w : written)
         for (const Buf& a : all)
             if (w.p != a.p && overlap(w.p, w.n, a.p, a.n)) return KDA_ERR_INVALID_ARG;
@@ -251,7 +252,7 @@ kda_status_t chunk_bwd_f32(const float* q, const float* k, const float* v, const
     if (hipMallocFromPoolAsync(&ws, kda::chunk_bwd_f32_workspace_bytes(B, T, H), pool, stream) !=
         hipSuccess)
         return KDA_ERR_NO_MEMORY;
-    const hipError_t e = kda::launch_chunk_bwd_f32(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk,
+    const hipError_t e = kda::launch_chunk_bwd<IO>(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk,
                                                    dv, dg, dbeta, dh0, B, T, H, ws, stream);
     (void)hipFreeAsync(ws, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -404,8 +405,17 @@ kda_status_t kda_chunk_bwd_f32(const float* q, const float* k, const float* v, c
                                const float* dout, const float* dhT, float* dq, float* dk,
                                float* dv, float* dg, float* dbeta, float* dh0, int B, int T,
                                int H, hipStream_t stream) {
-    return chunk_bwd_f32(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0, B,
-                         T, H, stream);
+    return chunk_bwd<float>(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0,
+                            B, T, H, stream);
+}
+
+kda_status_t kda_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* g, const float* beta, float scale, const float* h0,
+                           const uint16_t* dout, const float* dhT, uint16_t* dq, uint16_t* dk,
+                           uint16_t* dv, float* dg, float* dbeta, float* dh0, int B, int T, int H,
+                           hipStream_t stream) {
+    return chunk_bwd<uint16_t>(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk, dv, dg, dbeta,
+                               dh0, B, T, H, stream);
 }
 
 const char* kda_status_string(kda_status_t s) {

@@ -93,8 +93,10 @@ int chunk_f32_slices() { return kScanSlices; }
 // channels 32s + 8g + e (s, e = 0..3, 0..7), i.e. exactly the A-operand
 // fragment of that row for the four k32 steps over the 128 channels.
 // ---------------------------------------------------------------------------
+// IO: float, or uint16_t for bf16 q and k (the backward of the bf16 prefill)
+template <typename IO>
 __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
+    const IO* __restrict__ q, const IO* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
     uint8_t* __restrict__ ws, float* __restrict__ x_out) {
     using st = float;
@@ -592,8 +594,17 @@ hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
                                  const float* beta, int B, int T, int H, int chunk0, int nchunks,
                                  void* ws, hipStream_t stream, float* x_out) {
     const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
-    hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3(nblk), dim3(256), 0, stream, q, k, g, beta, T,
-                       H, chunk0, nchunks, static_cast<uint8_t*>(ws), x_out);
+    hipLaunchKernelGGL(kda_chunk_prep_kernel<float>, dim3(nblk), dim3(256), 0, stream, q, k, g,
+                       beta, T, H, chunk0, nchunks, static_cast<uint8_t*>(ws), x_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_prep_f32(const uint16_t* q, const uint16_t* k, const float* g,
+                                 const float* beta, int B, int T, int H, int chunk0, int nchunks,
+                                 void* ws, hipStream_t stream, float* x_out) {
+    const unsigned nblk = (unsigned)((int64_t)B * H * nchunks);
+    hipLaunchKernelGGL(kda_chunk_prep_kernel<uint16_t>, dim3(nblk), dim3(256), 0, stream, q, k,
+                       g, beta, T, H, chunk0, nchunks, static_cast<uint8_t*>(ws), x_out);
     return hipGetLastError();
 }
 

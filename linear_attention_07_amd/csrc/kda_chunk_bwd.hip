@@ -54,7 +54,8 @@ constexpr size_t kScrU = kScrR + kChunk * kD;     // [64][128] U = T R
 constexpr size_t kScrDU = kScrU + kChunk * kD;    // [64][128] dU
 constexpr size_t kScrDX = kScrDU + kChunk * kD;   // [64][64]  dX
 constexpr size_t kScrY = kScrDX + kChunk * kChunk;  // [64][64] X^T dX
-constexpr size_t kScrFloats = kScrY + kChunk * kChunk;
+constexpr size_t kScrDR = kScrY + kChunk * kChunk;  // [64][128] dR (= dV in fp32)
+constexpr size_t kScrFloats = kScrDR + kChunk * kD;
 
 __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -116,6 +117,21 @@ __device__ __forceinline__ float4 ld4(const float* p) {
 __device__ __forceinline__ float4 col4(const float* p, size_t pitch) {
     return make_float4(p[0], p[pitch], p[2 * pitch], p[3 * pitch]);
 }
+// q / k / v / dout in and dq / dk / dv out: fp32, or bf16 widened on load and
+// rounded to nearest even on store (8-byte aligned groups of four)
+__device__ __forceinline__ float io1(const float* p) { return *p; }
+__device__ __forceinline__ float io1(const uint16_t* p) { return bf2f(*p); }
+__device__ __forceinline__ float4 io4(const float* p) { return ld4(p); }
+__device__ __forceinline__ float4 io4(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__builtin_bit_cast(float, u.x << 16),
+                       __builtin_bit_cast(float, u.x & 0xffff0000u),
+                       __builtin_bit_cast(float, u.y << 16),
+                       __builtin_bit_cast(float, u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void io_st(float* p, float x) { *p = x; }
+__device__ __forceinline__ void io_st(uint16_t* p, float x) { *p = f2bf(x); }
+
 // four consecutive values at any 4-byte alignment
 __device__ __forceinline__ float4 lc4(const float* p) {
     return make_float4(p[0], p[1], p[2], p[3]);
@@ -186,8 +202,9 @@ struct StateScanLds {
     float gam[kD];
 };
 
+template <typename IO>
 __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
-    const uint8_t* __restrict__ rec, const float* __restrict__ v, const float* __restrict__ h0,
+    const uint8_t* __restrict__ rec, const IO* __restrict__ v, const float* __restrict__ h0,
     float* __restrict__ states, int T, int H, int nch) {
     __shared__ StateScanLds s;
     int bh, slice;
@@ -211,7 +228,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
         const float* Tg = reinterpret_cast<const float*>(r + RF::TH);
         const float* Wg = reinterpret_cast<const float*>(r + RF::W);
         const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
-        const float* Vg = v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+        const IO* Vg = v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
 #pragma unroll
         for (int u = 0; u < 12; ++u) {
             if (u < 2) {
@@ -225,7 +242,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
                 pf[u] = ld4(Kg + (e >> 4) * kChunk + 4 * (e & 15));
             } else {
                 const int e = tid + 512 * (u - 10), row = e >> 4;
-                pf[u] = row < L ? ld4(Vg + (size_t)row * H * kD + 4 * (e & 15))
+                pf[u] = row < L ? io4(Vg + (size_t)row * H * kD + 4 * (e & 15))
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
@@ -303,8 +320,9 @@ struct GradScanLds {
 };
 static_assert(kD * kP64 >= kChunk * kP128, "W must fit in the Kb^T buffer");
 
+template <typename IO>
 __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
-    const uint8_t* __restrict__ rec, const float* __restrict__ dout,
+    const uint8_t* __restrict__ rec, const IO* __restrict__ dout,
     const float* __restrict__ dhT, float* __restrict__ dsn, float* __restrict__ dh0,
     float scale, int T, int H, int nch) {
     __shared__ GradScanLds s;
@@ -329,7 +347,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
         const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
         const float* Qg = reinterpret_cast<const float*>(r + RF::QP);
         const float* Wg = reinterpret_cast<const float*>(r + RF::W);
-        const float* Og = dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+        const IO* Og = dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
 #pragma unroll
         for (int u = 0; u < 14; ++u) {
             if (u < 4) {
@@ -340,7 +358,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
                 pf[u] = ld4(Qg + (e >> 5) * kD + 4 * (e & 31));
             } else if (u < 10) {
                 const int e = tid + 512 * (u - 8), row = e >> 4;
-                pf[u] = row < L ? ld4(Og + (size_t)row * H * kD + 4 * (e & 15))
+                pf[u] = row < L ? io4(Og + (size_t)row * H * kD + 4 * (e & 15))
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
             } else {
                 const int e = tid + 512 * (u - 10);
@@ -444,13 +462,14 @@ struct __align__(16) BwdLds {
     float red[2048];  // per-thread partial sums, reduced in a fixed order (deterministic)
 };
 
+template <typename IO>
 __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ dout,
+    const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const IO* __restrict__ dout,
     const float* __restrict__ states, const float* __restrict__ dsn,
     const float* __restrict__ xs, float* __restrict__ scr_all,
-    float scale, int T, int H, int nch, float* __restrict__ dq, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
+    float scale, int T, int H, int nch, IO* __restrict__ dq, IO* __restrict__ dk,
+    IO* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
     __shared__ BwdLds s;
 
     const int c = blockIdx.x % nch;
@@ -468,8 +487,9 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     float* dU_ = scr + kScrDU;
     float* dX_ = scr + kScrDX;
     float* Y_ = scr + kScrY;
-    auto in = [&](const float* p, int r, int col) {
-        return r < L ? p[base + (size_t)r * rp + col] : 0.f;
+    float* dR_ = scr + kScrDR;
+    auto in = [&](const IO* p, int r, int col) {
+        return r < L ? io1(p + base + (size_t)r * rp + col) : 0.f;
     };
 
     // ---- load: normalised q, k (8 threads per row, 16 channels each), g ---
@@ -482,8 +502,8 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         for (int e = 0; e < 4; ++e) {
             const int col = 16 * part + 4 * e;
             const size_t off = base + (size_t)r * rp + col;
-            qv[e] = r < L ? ld4(q + off) : z;
-            kv[e] = r < L ? ld4(k + off) : z;
+            qv[e] = r < L ? io4(q + off) : z;
+            kv[e] = r < L ? io4(k + off) : z;
             *reinterpret_cast<float4*>(&s.gam[r][col]) = r < L ? ld4(g + off) : z;
             sq += qv[e].x * qv[e].x + qv[e].y * qv[e].y + qv[e].z * qv[e].z + qv[e].w * qv[e].w;
             sk += kv[e].x * kv[e].x + kv[e].y * kv[e].y + kv[e].z * kv[e].z + kv[e].w * kv[e].w;
@@ -588,8 +608,8 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
 
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     // q / k / v / dout row r from channel col on, four values (zeros past the sequence)
-    auto in4 = [&](const float* p, int r, int col) {
-        return r < L ? ld4(p + base + (size_t)r * rp + col) : z4;
+    auto in4 = [&](const IO* p, int r, int col) {
+        return r < L ? io4(p + base + (size_t)r * rp + col) : z4;
     };
     // ---- R = V - Kt S --------------------------------------------------------
     mmf<kChunk, kD, kCT>(
@@ -628,7 +648,8 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         kChunk, [&](int i, int kk) { return scale4(col4(&s.x[kk][i], kChunk), s.beta[i]); },
         [&](int kk, int j) { return col4(dU_ + kk * kD + j, kD); },
         [&](int i, int j, float a) {
-            if (i < L) dv[base + (size_t)i * rp + j] = a;
+            dR_[i * kD + j] = a;
+            if (i < L) io_st(dv + base + (size_t)i * rp + j, a);
         });
     // ---- dT = lower-incl(dU R^T), into dX's space -----------------------------
     mmf<kChunk, kChunk, kCT>(
@@ -717,7 +738,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         });
     // dKt = -dR S^T:  dkh = e^Gam dKt,  dGam += Kt dKt
     mmf<kChunk, kD, kCT>(
-        kD, [&](int i, int kk) { return scale4(in4(dv, i, kk), -1.f); },
+        kD, [&](int i, int kk) { return scale4(ld4(dR_ + i * kD + kk), -1.f); },
         [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
         [&](int m, int i, int j, float a) {
             const float e = ex(s.gam[i][j]);
@@ -857,8 +878,8 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         const int r = 16 * (m >> 2) + g4 + (m & 3);
         if (r >= L) continue;
         // qh = q / sqrt(|q|^2 + eps): dq = rq (dqh - qh (qh . dqh))
-        dq[base + (size_t)r * rp + cc] = s.rq[r] * fmaf(-s.qh[r][cc], s.dotq[r], dqh[m]);
-        dk[base + (size_t)r * rp + cc] = s.rk[r] * fmaf(-s.kh[r][cc], s.dotk[r], dkh[m]);
+        io_st(dq + base + (size_t)r * rp + cc, s.rq[r] * fmaf(-s.qh[r][cc], s.dotq[r], dqh[m]));
+        io_st(dk + base + (size_t)r * rp + cc, s.rk[r] * fmaf(-s.kh[r][cc], s.dotk[r], dkh[m]));
     }
     if (tid < kD) {
         float a = s.dlast[tid] + s.red[tid];  // Gam of the last row also enters Kb and gamma
@@ -881,11 +902,11 @@ size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H) {
                 (2 * kStateFloats + (size_t)kChunk * kChunk + kScrFloats) * sizeof(float));
 }
 
-hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
-                                const float* beta, float scale, const float* h0,
-                                const float* dout, const float* dhT, float* dq, float* dk,
-                                float* dv, float* dg, float* dbeta, float* dh0, int B, int T,
-                                int H, void* ws, hipStream_t stream) {
+template <typename IO>
+hipError_t launch_chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g,
+                            const float* beta, float scale, const float* h0, const IO* dout,
+                            const float* dhT, IO* dq, IO* dk, IO* dv, float* dg, float* dbeta,
+                            float* dh0, int B, int T, int H, void* ws, hipStream_t stream) {
     const int nch = (T + kChunk - 1) / kChunk;
     const size_t n = (size_t)B * H * nch;
     uint8_t* rec = static_cast<uint8_t*>(ws);
@@ -896,16 +917,27 @@ hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, 
     hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, 0, nch, rec, stream, xs);
     if (e != hipSuccess) return e;
     const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
-    hipLaunchKernelGGL(kda_bwd_state_scan_kernel, dim3(nscan), dim3(kScanThreads), 0, stream, rec, v,
-                       h0, states, T, H, nch);
+    hipLaunchKernelGGL(kda_bwd_state_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
+                       rec, v, h0, states, T, H, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel, dim3(nscan), dim3(kScanThreads), 0, stream, rec,
-                       dout, dhT, dsn, dh0, scale, T, H, nch);
+    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
+                       rec, dout, dhT, dsn, dh0, scale, T, H, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)n), dim3(kCT), 0,
-                       stream, q, k, v, g, beta, dout, states, dsn, xs, scr, scale, T, H, nch, dq, dk,
-                       dv, dg, dbeta);
+    hipLaunchKernelGGL(kda_bwd_chunk_kernel<IO>, dim3((unsigned)n), dim3(kCT), 0, stream, q, k, v,
+                       g, beta, dout, states, dsn, xs, scr, scale, T, H, nch, dq, dk, dv, dg,
+                       dbeta);
     return hipGetLastError();
 }
+
+template hipError_t launch_chunk_bwd<float>(const float*, const float*, const float*,
+                                            const float*, const float*, float, const float*,
+                                            const float*, const float*, float*, float*, float*,
+                                            float*, float*, float*, int, int, int, void*,
+                                            hipStream_t);
+template hipError_t launch_chunk_bwd<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*,
+                                               const float*, const float*, float, const float*,
+                                               const uint16_t*, const float*, uint16_t*,
+                                               uint16_t*, uint16_t*, float*, float*, float*, int,
+                                               int, int, void*, hipStream_t);
 
 }  // namespace kda

@@ -49,6 +49,10 @@ struct ChunkRecF32 {
 hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
                                  const float* beta, int B, int T, int H, int chunk0, int nchunks,
                                  void* ws, hipStream_t stream, float* x_out = nullptr);
+// the same records (fp32) from bf16 q and k
+hipError_t launch_chunk_prep_f32(const uint16_t* q, const uint16_t* k, const float* g,
+                                 const float* beta, int B, int T, int H, int chunk0, int nchunks,
+                                 void* ws, hipStream_t stream, float* x_out = nullptr);
 hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
                                  float* out, float scale, int B, int T, int H, int chunk0,
                                  int nchunks, hipStream_t stream);
@@ -58,12 +62,14 @@ hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_
 // leaving each chunk (and dh0), and one gradient workgroup per chunk.  ws
 // holds chunk_bwd_f32_workspace_bytes(B, T, H) bytes.  h0, dhT: NULL = zeros;
 // dh0: NULL = not stored.
+// IO = float or uint16_t (bf16 q, k, v, dout in and dq, dk, dv out; all
+// arithmetic fp32).
 size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H);
-hipError_t launch_chunk_bwd_f32(const float* q, const float* k, const float* v, const float* g,
-                                const float* beta, float scale, const float* h0,
-                                const float* dout, const float* dhT, float* dq, float* dk,
-                                float* dv, float* dg, float* dbeta, float* dh0, int B, int T,
-                                int H, void* ws, hipStream_t stream);
+template <typename IO>
+hipError_t launch_chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g,
+                            const float* beta, float scale, const float* h0, const IO* dout,
+                            const float* dhT, IO* dq, IO* dk, IO* dv, float* dg, float* dbeta,
+                            float* dh0, int B, int T, int H, void* ws, hipStream_t stream);
 
 // Short convolution in front of the attention: depthwise 4-tap causal filter
 // per head and channel, then SiLU, on q, k and v.  wq == NULL: none.  state:

@@ -24,6 +24,7 @@ KDA_ERR_HIP = 3
 KDA_ERR_NO_MEMORY = 4
 
 EXPORTS = (
+    "kda_chunk_bwd",
     "kda_chunk_bwd_f32",
     "kda_chunk_fwd",
     "kda_chunk_fwd_conv",
@@ -73,8 +74,10 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp] * 5 + [f] + [vp] * 8 + [i, i, vp]
         fn.restype = ctypes.c_int
-    lib.kda_chunk_bwd_f32.argtypes = [vp] * 5 + [f] + [vp] * 9 + [i, i, i, vp]
-    lib.kda_chunk_bwd_f32.restype = ctypes.c_int
+    for name in ("kda_chunk_bwd_f32", "kda_chunk_bwd"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp] * 5 + [f] + [vp] * 9 + [i, i, i, vp]
+        fn.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -302,31 +305,40 @@ def recurrent_step_bwd(q, k, v, g, beta, scale, S_prev, dout, dS):
 
 
 def chunk_bwd(q, k, v, g, beta, scale, dout, h0=None, dhT=None):
-    """Backward of the fp32 chunked prefill (kda_chunk_bwd_f32): gradients of
-    <dout, o> + <dhT, hT> for (o, hT) = chunk_fwd(q, k, v, g, beta, scale, h0).
-    q, k, v, g, dout: [B, T, H, 128] fp32; beta: [B, T, H] fp32; h0, dhT:
-    optional [B, H, 128, 128] fp32.  Returns (dq, dk, dv, dg, dbeta, dh0)."""
+    """Backward of the chunked prefill (kda_chunk_bwd_f32, or kda_chunk_bwd for
+    bf16 q / k / v / dout): gradients of <dout, o> + <dhT, hT> for (o, hT) =
+    chunk_fwd(q, k, v, g, beta, scale, h0).  q, k, v, dout: [B, T, H, 128]
+    fp32 or bf16 (all alike); g: [B, T, H, 128] fp32; beta: [B, T, H] fp32;
+    h0, dhT: optional [B, H, 128, 128] fp32.  Returns (dq, dk, dv in the type
+    of q, dg, dbeta, dh0 fp32)."""
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM:
         raise ValueError(f"q: expected [B, T, H, {HEAD_DIM}], got {tuple(q.shape)}")
     B, T, H, _ = q.shape
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("kda tensors must live on a GPU")
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("dout", dout)):
-        _check(t, name, q.shape, torch.float32, dev)
+    io = q.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q: dtype {io} not supported")
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, q.shape, io, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
     _check(beta, "beta", (B, T, H), torch.float32, dev)
     sshape = (B, H, HEAD_DIM, HEAD_DIM)
     if h0 is not None:
         _check(h0, "h0", sshape, torch.float32, dev)
     if dhT is not None:
         _check(dhT, "dhT", sshape, torch.float32, dev)
-    dq, dk, dv, dg = (torch.empty_like(q) for _ in range(4))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dg = torch.empty_like(g)
     dbeta = torch.empty_like(beta)
     dh0 = torch.empty(sshape, dtype=torch.float32, device=dev)
-    st = load().kda_chunk_bwd_f32(
+    lib = load()
+    name = "kda_chunk_bwd_f32" if io == torch.float32 else "kda_chunk_bwd"
+    st = getattr(lib, name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(h0), _ptr(dout),
         _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H,
         _stream(dev))
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_bwd_f32")
+        raise KDAError(st, name)
     return dq, dk, dv, dg, dbeta, dh0

@@ -278,3 +278,25 @@ def test_chunk_bwd_invalid_arguments(lib):
 def test_chunk_bwd_grid_limit(lib):
     # 4096 heads x 2049 chunks of workgroups exceed the launch limit
     assert chunk_bwd(lib, spacing=1 << 40, H=4096, T=64 * 2048 + 1) == libkda.KDA_ERR_UNSUPPORTED
+
+
+def test_chunk_bwd_bf16_invalid_arguments(lib):
+    INV = libkda.KDA_ERR_INVALID_ARG
+    # the bf16 entry point shares the validation; the bf16 arrays are half the size
+    def call(**kw):
+        names = ("q", "k", "v", "g", "beta", "h0", "dout", "dhT", "dq", "dk", "dv", "dg",
+                 "dbeta", "dh0")
+        args = {n: ctypes.c_void_p(A * (i + 1)) for i, n in enumerate(names)}
+        args.update(scale=1.0, B=1, T=4, H=1)
+        args.update(kw)
+        return lib.kda_chunk_bwd(
+            args["q"], args["k"], args["v"], args["g"], args["beta"], args["scale"],
+            args["h0"], args["dout"], args["dhT"], args["dq"], args["dk"], args["dv"],
+            args["dg"], args["dbeta"], args["dh0"], args["B"], args["T"], args["H"], None)
+    assert call(B=-1) == INV
+    assert call(q=NULL) == INV
+    assert call(dv=ctypes.c_void_p(A * 20 + 8)) == INV
+    assert call(dq=ctypes.c_void_p(A * 2 + 512)) == INV     # inside k's 1 KiB of bf16
+    assert call(dg=ctypes.c_void_p(A * 4 + 1024)) == INV    # inside g's 2 KiB of fp32
+    assert call(B=0) == libkda.KDA_OK
+    assert call(T=0, dh0=NULL) == libkda.KDA_OK
