@@ -60,6 +60,8 @@ BWD_CHUNK_FLOP_PER_CHUNK_HEAD = int(2 * 37.5 * 64 * 64 * 128)
 # read, dh0 written
 BWD_CHUNK_BYTES_PER_TOKEN_HEAD = 9 * 128 * 4 + 2 * 4
 FP32_VALU_PEAK_TFLOPS = 157.3
+# the same with bf16 q, k, v, dout in and dq, dk, dv out (g, dg fp32)
+BWD_CHUNK_BF16_BYTES_PER_TOKEN_HEAD = 7 * 128 * 2 + 2 * 128 * 4 + 2 * 4
 
 
 def parse():
@@ -316,6 +318,20 @@ def main():
     pb_bytes = wb.B * wb.T * wb.H * BWD_CHUNK_BYTES_PER_TOKEN_HEAD + 3 * wb.B * wb.H * STATE_BYTES
     print(f"# prefill backward (fp32): {pbms:.3f} ms/call, {pb_tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
+    for key in ("q", "k", "v", "dout"):
+        xb[key] = xb[key].to(torch.bfloat16)
+
+    def prefill_bwd16():
+        libkda.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
+                         xb["dout"], h0=xb["h0"], dhT=xb["dhT"])
+
+    p16ms, p16ms_med, p16ms_min = time_op(torch, prefill_bwd16, max(3, args.steps // 4),
+                                          args.warmup)
+    p16_tflops = pb_flop / (p16ms / 1e3) / 1e12
+    p16_bytes = (wb.B * wb.T * wb.H * BWD_CHUNK_BF16_BYTES_PER_TOKEN_HEAD +
+                 3 * wb.B * wb.H * STATE_BYTES)
+    print(f"# prefill backward (bf16 I/O): {p16ms:.3f} ms/call, {p16_tflops:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
     del xb
 
     if args.calibrate_copy:
@@ -451,6 +467,23 @@ def main():
                 "traffic": measured_traffic("prefill_bwd_8k"),
                 "algorithmic_bytes_per_call": pb_bytes,
                 "hbm_GBps_algorithmic": round(pb_bytes / (pbms / 1e3) / 1e9, 1),
+            },
+        },
+        "prefill_bwd_bf16": {
+            "workload": "prefill_bwd_8k with bf16 q, k, v, dout in and bf16 dq, dk, dv out "
+                        "(kda_chunk_bwd), fp32 arithmetic",
+            "ms_per_step": round(p16ms, 4),
+            "ms_per_step_median": round(p16ms_med, 4),
+            "ms_per_step_min": round(p16ms_min, 4),
+            "Mtok_s": round(wb.B * wb.T / (p16ms / 1e3) / 1e6, 3),
+            "roofline": {
+                "bound": "alu",
+                "achieved": round(p16_tflops, 2),
+                "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(p16_tflops / FP32_VALU_PEAK_TFLOPS, 4),
+                "algorithmic_flop_per_call": pb_flop,
+                "algorithmic_bytes_per_call": p16_bytes,
             },
         },
         "decode": {
