@@ -1,10 +1,11 @@
-// Backward of the chunkwise prefill for fp32 I/O: the gradients of
+// Backward of the chunkwise prefill, for fp32 or bf16 q / k / v / dout (and
+// dq / dk / dv in the same type; all arithmetic fp32): the gradients of
 // L = <dO, O> + <dS_T, S_T> with respect to q, k, v, g, beta and the initial
 // state, for O, S_T computed by the Kimi Delta Attention recurrence (Kimi-K3
 // 深度解析 blog, section 三; the KDA paragraph of the 深入 Kimi-K3 thread for
 // the in-kernel L2 normalisation and the per-channel decay).  The pages give
 // no backward; this is the reverse-mode derivative of the chunk form written
-// out in kda_chunk.hip, in fp32 arithmetic throughout.
+// out in kda_chunk.hip.
 //
 // Per 64-token chunk entering with state S and leaving with S', with R = V -
 // Kt S, U = T R and the quantities of the chunk form (Kt, Qt, Kb, gamma, the
