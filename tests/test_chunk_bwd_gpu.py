@@ -155,16 +155,20 @@ def test_chunk_bwd_deterministic():
         assert torch.equal(u, w), n
 
 
-def test_chunk_bwd_bench_workload_sampled_heads():
-    """The timed workload (B=1, H=96, T=8192, as launched by the benchmark):
-    heads are independent, so the oracle runs on three sampled heads."""
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_chunk_bwd_bench_workload_sampled_heads(io):
+    """The timed workload (B=1, H=96, T=8192, as launched by the benchmark, with
+    fp32 and with bf16 I/O): heads are independent, so the oracle runs on three
+    sampled heads."""
     w = synth.WORKLOADS["prefill_bwd_8k"]
-    say(f"chunk bwd case {w.name} B={w.B} T={w.T} H={w.H}")
+    say(f"chunk bwd case {w.name} B={w.B} T={w.T} H={w.H} {io}")
     x = synth.prefill_inputs(w.B, w.T, w.H, torch.float32, seed=w.seed, g_shift=w.g_shift,
                              h0_std=w.h0_std, device=DEV)
     gb = torch.Generator(device=DEV).manual_seed(w.seed + 1)
     x["dout"] = torch.randn((w.B, w.T, w.H, 128), generator=gb, device=DEV)
     x["dhT"] = 0.1 * torch.randn((w.B, w.H, 128, 128), generator=gb, device=DEV)
+    for key in ("q", "k", "v", "dout"):
+        x[key] = x[key].to(io)
     got = gpu(x)
     heads = [0, 47, w.H - 1]
     h = lambda t, ax: host64(t.index_select(ax, torch.tensor(heads, device=DEV)))
@@ -174,5 +178,5 @@ def test_chunk_bwd_bench_workload_sampled_heads():
     axes = (2, 2, 2, 2, 2, 1)
     for n, a, b, ax in zip(NAMES, got, want, axes):
         e = rel(h(a, ax), b)
-        say(f"chunk bwd {w.name} heads {heads} {n}: {e:.1e}")
-        assert e <= TOL, (n, e)
+        say(f"chunk bwd {w.name} {io} heads {heads} {n}: {e:.1e}")
+        assert e <= tol(n, io), (n, e)
