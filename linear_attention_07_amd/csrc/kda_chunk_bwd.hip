@@ -605,25 +605,19 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         }
     }
     __syncthreads();
-    __syncthreads();
 
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     // q / k / v / dout row r from channel col on, four values (zeros past the sequence)
     auto in4 = [&](const IO* p, int r, int col) {
         return r < L ? io4(p + base + (size_t)r * rp + col) : z4;
     };
+    // Products in three phases, each needing only the ones before it:
+    // (R, dU), then (U, dR, dT), then dM.
     // ---- R = V - Kt S --------------------------------------------------------
     mmf<kChunk, kD, kCT>(
         kD, [&](int i, int kk) { return mul4(exp4(ld4(&s.gam[i][kk])), ld4(&s.kh[i][kk])); },
         [&](int kk, int j) { return col4(S + (size_t)kk * kD + j, kD); },
         [&](int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
-    __syncthreads();
-    // ---- U = T R,  T = X diag(beta) ------------------------------------------
-    mmf<kChunk, kD, kCT>(
-        kChunk, [&](int i, int kk) { return mul4(ld4(&s.x[i][kk]), ld4(&s.beta[kk])); },
-        [&](int kk, int j) { return col4(R_ + kk * kD + j, kD); },
-        [&](int i, int j, float a) { U_[i * kD + j] = a; });
-    __syncthreads();
     // ---- dU = scale M^T dO + Kb dS' ------------------------------------------
     mmf<kChunk, kD, kCT>(
         kChunk + kD,
@@ -644,6 +638,11 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         },
         [&](int i, int j, float a) { dU_[i * kD + j] = a; });
     __syncthreads();
+    // ---- U = T R,  T = X diag(beta) ------------------------------------------
+    mmf<kChunk, kD, kCT>(
+        kChunk, [&](int i, int kk) { return mul4(ld4(&s.x[i][kk]), ld4(&s.beta[kk])); },
+        [&](int kk, int j) { return col4(R_ + kk * kD + j, kD); },
+        [&](int i, int j, float a) { U_[i * kD + j] = a; });
     // ---- dV = dR = T^T dU ----------------------------------------------------
     mmf<kChunk, kD, kCT>(
         kChunk, [&](int i, int kk) { return scale4(col4(&s.x[kk][i], kChunk), s.beta[i]); },
@@ -657,6 +656,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         kD, [&](int i, int kk) { return ld4(dU_ + i * kD + kk); },
         [&](int kk, int j) { return ld4(R_ + j * kD + kk); },
         [&](int i, int j, float a) { dX_[i * kChunk + j] = j <= i ? a : 0.f; });
+    __syncthreads();
     // ---- dM = scale lower-incl(dO U^T), over N ---------------------------------
     mmf<kChunk, kChunk, kCT>(
         kD, [&](int i, int kk) { return in4(dout, i, kk); },
