@@ -133,10 +133,6 @@ __device__ __forceinline__ float4 io4(const uint16_t* p) {
 __device__ __forceinline__ void io_st(float* p, float x) { *p = x; }
 __device__ __forceinline__ void io_st(uint16_t* p, float x) { *p = f2bf(x); }
 
-// four consecutive values at any 4-byte alignment
-__device__ __forceinline__ float4 lc4(const float* p) {
-    return make_float4(p[0], p[1], p[2], p[3]);
-}
 __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
     return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
 }
@@ -183,17 +179,18 @@ __device__ __forceinline__ void stage(const float* __restrict__ src, size_t spit
     }
 }
 
-// LDS row pitches of the staged record parts (one float of padding per row, so
-// that the rows that a wave reads at one k fall in different banks)
-constexpr int kP64 = kChunk + 1;
-constexpr int kP128 = kD + 1;
+// LDS row pitches of the staged record parts: four floats of padding per row,
+// so rows stay 16-byte aligned (float4 reads and writes) while the rows that a
+// wave reads at one k fall in different banks
+constexpr int kP64 = kChunk + 4;
+constexpr int kP128 = kD + 4;
 
 // ---------------------------------------------------------------------------
 // State scan: one workgroup per (b, h, 64 value columns).  For chunk c the
 // state slice entering it is stored, then S <- Diag(gamma) S + Kb^T (T V - W S).
 // Each chunk's record parts and V slice are first staged in LDS.
 // ---------------------------------------------------------------------------
-struct StateScanLds {
+struct __align__(16) StateScanLds {
     float S[kD][kScanCols];
     float Z[kChunk][kScanCols];
     float Tm[kChunk * kP64];
@@ -266,10 +263,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
                 const int e = tid + 512 * (u - 10);
                 d = &s.V[e >> 4][4 * (e & 15)];
             }
-            d[0] = pf[u].x;
-            d[1] = pf[u].y;
-            d[2] = pf[u].z;
-            d[3] = pf[u].w;
+            *reinterpret_cast<float4*>(d) = pf[u];
         }
         if (tid < kD) s.gam[tid] = gpf;
     };
@@ -288,8 +282,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
         mmf<kChunk, kScanCols, kScanThreads>(
             kChunk + kD,
             [&](int i, int k) {
-                return k < kChunk ? lc4(&s.Tm[i * kP64 + k])
-                                  : scale4(lc4(&s.W[i * kP128 + (k - kChunk)]), -1.f);
+                return k < kChunk ? ld4(&s.Tm[i * kP64 + k])
+                                  : scale4(ld4(&s.W[i * kP128 + (k - kChunk)]), -1.f);
             },
             [&](int k, int j) {
                 return k < kChunk ? col4(&s.V[k][j], kScanCols) : col4(&s.S[k - kChunk][j], kScanCols);
@@ -298,7 +292,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
         __syncthreads();
         // S' = Diag(gamma) S + Kb^T Z (each lane updates only its own entries)
         mmf<kD, kScanCols, kScanThreads>(
-            kChunk, [&](int i, int k) { return lc4(&s.KT[i * kP64 + k]); },
+            kChunk, [&](int i, int k) { return ld4(&s.KT[i * kP64 + k]); },
             [&](int k, int j) { return col4(&s.Z[k][j], kScanCols); },
             [&](int i, int j, float a) { s.S[i][j] = fmaf(s.gam[i], s.S[i][j], a); });
     }
@@ -311,10 +305,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
 // After chunk 0, dS is the initial state's gradient.  Kb^T and then W take
 // turns in one LDS buffer.
 // ---------------------------------------------------------------------------
-struct GradScanLds {
+struct __align__(16) GradScanLds {
     float D[kD][kScanCols];
     float Y[kChunk][kScanCols];
-    float KW[kD * kP64];  // Kb^T [128][64], then W [64][128] (pitch 129 fits in it)
+    float KW[kD * kP64];  // Kb^T [128][64], then W [64][128] (at pitch kP128 it fits)
     float QP[kChunk * kP128];
     float O[kChunk][kScanCols];
     float gam[kD];
@@ -368,12 +362,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
         }
         if (tid < kD) gpf = reinterpret_cast<const float*>(r + RF::G)[tid];
     };
-    auto put4 = [&](float* d, float4 x) {
-        d[0] = x.x;
-        d[1] = x.y;
-        d[2] = x.z;
-        d[3] = x.w;
-    };
+    auto put4 = [&](float* d, float4 x) { *reinterpret_cast<float4*>(d) = x; };
     auto put = [&]() {  // Kb^T, Q', dO and gamma
 #pragma unroll
         for (int u = 0; u < 10; ++u) {
