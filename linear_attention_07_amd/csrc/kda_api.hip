@@ -236,13 +236,16 @@ kda_status_t chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g, co
         const void* p;
         size_t n;
     };
+    // argument slots; the written ones come last.  Two different slots may
+    // never overlap when either is written, even at the same address.
     const Buf all[] = {{q, vb},  {k, vb},  {v, vb},      {g, fb},     {dout, vb},
                        {beta, bb}, {h0, sbytes}, {dhT, sbytes}, {dq, vb}, {dk, vb},
                        {dv, vb}, {dg, fb}, {dbeta, bb}, {dh0, sbytes}};
-    const Buf written[] = {{dq, vb}, {dk, vb}, {dv, vb}, {dg, fb}, {dbeta, bb}, {dh0, sbytes}};
-    for (const Buf& w : written)
-        for (const Buf& a : all)
-            if (w.p != a.p && overlap(w.p, w.n, a.p, a.n)) return KDA_ERR_INVALID_ARG;
+    constexpr int kSlots = sizeof(all) / sizeof(all[0]), kFirstWritten = 8;
+    for (int w = kFirstWritten; w < kSlots; ++w)
+        for (int a = 0; a < kSlots; ++a)
+            if (a != w && overlap(all[w].p, all[w].n, all[a].p, all[a].n))
+                return KDA_ERR_INVALID_ARG;
     const int nch = (T + 63) / 64;
     if ((int64_t)B * H * nch > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
 

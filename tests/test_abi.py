@@ -300,3 +300,21 @@ def test_chunk_bwd_bf16_invalid_arguments(lib):
     assert call(dg=ctypes.c_void_p(A * 4 + 1024)) == INV    # inside g's 2 KiB of fp32
     assert call(B=0) == libkda.KDA_OK
     assert call(T=0, dh0=NULL) == libkda.KDA_OK
+
+
+@pytest.mark.parametrize("fn", ["kda_chunk_bwd_f32", "kda_chunk_bwd"])
+@pytest.mark.parametrize("pair", [("dq", "dk"), ("dv", "dout"), ("dq", "q"), ("dg", "g"),
+                                  ("dbeta", "beta"), ("dh0", "dhT"), ("dh0", "h0")])
+def test_chunk_bwd_rejects_a_buffer_passed_twice(lib, fn, pair):
+    """A written buffer given at the very address of another argument is an
+    overlap like any other (kda.h: every written buffer overlaps no other
+    argument)."""
+    names = ("q", "k", "v", "g", "beta", "h0", "dout", "dhT", "dq", "dk", "dv", "dg", "dbeta",
+             "dh0")
+    args = {n: ctypes.c_void_p(A * (i + 1)) for i, n in enumerate(names)}
+    args[pair[0]] = args[pair[1]]
+    rc = getattr(lib, fn)(
+        args["q"], args["k"], args["v"], args["g"], args["beta"], 1.0, args["h0"], args["dout"],
+        args["dhT"], args["dq"], args["dk"], args["dv"], args["dg"], args["dbeta"], args["dh0"],
+        1, 4, 1, None)
+    assert rc == libkda.KDA_ERR_INVALID_ARG, pair
