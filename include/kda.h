@@ -28,12 +28,26 @@
  *   - Work is enqueued on `stream` and the call returns without
  *     synchronising.  A device fault surfaces at the caller's next sync.
  *   - Offsets are 64-bit: B*T*H*128 may exceed 2^31.
- *   - Precondition (documented, not checked): g lies in [-5, 0].  The chunked
- *     path relies on the lower bound to keep its factorised decay in range;
- *     it is the bound the pages give for the decay gate.
+ *   - Precondition: g lies in [-5, 0].  The chunked path relies on the lower
+ *     bound to keep its factorised decay in range; it is the bound the pages
+ *     give for the decay gate.  It is not checked by default (the check reads
+ *     every g); see KDA_DEBUG_CHECKS below.
  *   - Arguments are validated before any HIP call, so every
  *     KDA_ERR_INVALID_ARG case is reported without touching a GPU.
  *   - No exceptions cross the ABI; nothing is printed; nothing aborts.
+ *
+ * Environment (read on every call)
+ *   - KDA_WORKSPACE_MB: workspace budget per segment of the chunked paths
+ *     (default 4096 for the prefill, 8192 for its backward).  Long sequences
+ *     are split into segments of as many 64-token chunks as fit.
+ *   - KDA_DEBUG_CHECKS=1: before launching, every entry point scans its
+ *     inputs on the device (g within [-5, 0]; q, k, v, beta, states, output
+ *     gradients, taps, conv states and gate logits finite), synchronises its
+ *     stream and returns KDA_ERR_PRECONDITION if one fails; after its work it
+ *     synchronises again and returns KDA_ERR_DEVICE if a bounded device wait
+ *     gave up.  The mode synchronises: it is not for graph capture.
+ *   - KDA_DEBUG_SPIN_LIMIT=n (only with KDA_DEBUG_CHECKS): the polls a bounded
+ *     wait makes before it gives up, to exercise the KDA_ERR_DEVICE path.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -58,7 +72,11 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad scale */
     KDA_ERR_UNSUPPORTED = 2, /* a size the library cannot index (e.g. T > 2^31-1) */
     KDA_ERR_HIP = 3,         /* a HIP runtime call or launch failed */
-    KDA_ERR_NO_MEMORY = 4    /* internal workspace could not be allocated */
+    KDA_ERR_NO_MEMORY = 4,   /* internal workspace could not be allocated */
+    KDA_ERR_PRECONDITION = 5, /* KDA_DEBUG_CHECKS: g outside [-5, 0] or a value not finite;
+                                 nothing was launched */
+    KDA_ERR_DEVICE = 6       /* KDA_DEBUG_CHECKS: a bounded device wait gave up; the outputs
+                                are invalid */
 } kda_status_t;
 
 /*
@@ -275,12 +293,16 @@ KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k
  *
  * Every written buffer must not overlap any other argument.  All pointers
  * 16-byte aligned (beta, dbeta 4).  B == 0 or H == 0 is a no-op; T == 0
- * copies dhT (or zeros) to dh0.  Workspace (the chunk records, the state
- * entering and the state gradient leaving every chunk, and per-chunk scratch:
- * about 430 KB per 64 tokens and head) comes from the library's stream-ordered
- * pool; KDA_ERR_NO_MEMORY if it cannot be had.  Computed in fp32; g obeys
- * the forward's bound (every entry in [-5, 0]), which the chunk records that
- * the two state scans read rely on.
+ * copies dhT (or zeros) to dh0.  Workspace comes from the library's
+ * stream-ordered pool (KDA_ERR_NO_MEMORY if it cannot be had) and is bounded
+ * by the budget, not by T: the chunk records, the state entering and the
+ * state gradient leaving every chunk and per-chunk scratch (about 430 KB per
+ * 64 tokens and head) are held for one segment of chunks at a time.  With more
+ * than one segment, a forward pass first keeps the state entering each
+ * segment (64 KB per segment and head), and the segments are then
+ * differentiated last to first, each recomputing its states from its
+ * checkpoint.  Computed in fp32; g obeys the forward's bound (every entry in
+ * [-5, 0]), which the chunk records that the two state scans read rely on.
  */
 KDA_API kda_status_t kda_chunk_bwd_f32(const float *q, const float *k, const float *v,
                                const float *g, const float *beta, float scale,
@@ -302,6 +324,16 @@ KDA_API kda_status_t kda_chunk_bwd(const uint16_t *q, const uint16_t *k, const u
                            const uint16_t *dout, const float *dhT, uint16_t *dq,
                            uint16_t *dk, uint16_t *dv, float *dg, float *dbeta, float *dh0,
                            int B, int T, int H, hipStream_t stream);
+
+/*
+ * kda_trim_workspace — hands back to the driver the device memory that the
+ * library's workspace pools keep cached between calls (one pool per device;
+ * a 64K-token prefill keeps about 4 GB, an 8K-token backward about 5 GB).
+ * Call it when no work of this library is in flight (after synchronising the
+ * streams it ran on); memory still in use is not touched.  Returns KDA_OK, or
+ * KDA_ERR_HIP.  Not needed before exit.
+ */
+KDA_API kda_status_t kda_trim_workspace(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 KDA_API const char *kda_status_string(kda_status_t status);

@@ -9,6 +9,8 @@
 #include <mutex>
 
 #include "../../include/kda.h"
+#include "kda_common.hpp"
+#include "kda_debug.hpp"
 #include "kda_launch.hpp"
 
 namespace {
@@ -23,12 +25,13 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Workspace budget for one segment of the chunked path: 4 GB by default (a
-// 64K-token, 96-head layer in one segment; longer sequences are split).  The
-// environment variable KDA_WORKSPACE_MB overrides it; it is read on every
-// call, so a caller can force small segments.
-size_t workspace_budget() {
-    size_t mb = 4096;
+// Workspace budget for one segment of the chunked paths: default_mb (4 GB for
+// the prefill, a 64K-token 96-head layer in one segment; 8 GB for the
+// backward, an 8K-token 96-head layer in one segment); longer sequences are
+// split.  The environment variable KDA_WORKSPACE_MB overrides both; it is read
+// on every call, so a caller can force small segments.
+size_t workspace_budget(size_t default_mb = 4096) {
+    size_t mb = default_mb;
     if (const char* s = getenv("KDA_WORKSPACE_MB")) {
         const long v = strtol(s, nullptr, 10);
         if (v > 0) mb = (size_t)v;
@@ -36,15 +39,29 @@ size_t workspace_budget() {
     return mb << 20;
 }
 
+long env_long(const char* name, long dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    char* end = nullptr;
+    const long v = strtol(s, &end, 10);
+    return end && *end == '\0' ? v : dflt;
+}
+
 // One memory pool per device, created on first use, that keeps freed blocks
-// cached so repeated calls do not go back to the driver.
+// cached so repeated calls do not go back to the driver (kda_trim_workspace
+// hands them back).  Plain arrays and a mutex with trivial destructors: nothing
+// here runs at process exit.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
 hipError_t pool_for_device(hipMemPool_t* pool) {
-    static std::mutex mu;
-    static hipMemPool_t pools[64] = {};
+    std::mutex& mu = g_pool_mu;
+    hipMemPool_t* pools = g_pools;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
     if (!pools[dev]) {
         hipMemPoolProps props = {};
@@ -150,6 +167,40 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     if (seg < 1) return KDA_ERR_UNSUPPORTED;
     const bool multi = seg < nch;
 
+    kda::DebugScope dbg(stream);
+    if (dbg.on()) {
+        if (dbg.setup_status() != KDA_OK) return dbg.setup_status();
+        const size_t nel = n_tok * KDA_HEAD_DIM;
+        if constexpr (F32) {
+            dbg.finite(static_cast<const float*>(q), nel);
+            dbg.finite(static_cast<const float*>(k), nel);
+            dbg.finite(static_cast<const float*>(v), nel);
+        } else {
+            dbg.finite(static_cast<const uint16_t*>(q), nel);
+            dbg.finite(static_cast<const uint16_t*>(k), nel);
+            dbg.finite(static_cast<const uint16_t*>(v), nel);
+        }
+        if constexpr (G16)
+            dbg.decay(static_cast<const uint16_t*>(g), nel);
+        else
+            dbg.decay(static_cast<const float*>(g), nel);
+        dbg.finite(beta, n_tok);
+        dbg.finite(h0, state_bytes / sizeof(float));
+        if (cv) {
+            const size_t nw = wbytes / sizeof(float);
+            dbg.finite(conv.wq, nw);
+            dbg.finite(conv.wk, nw);
+            dbg.finite(conv.wv, nw);
+            dbg.finite(conv.state, cbytes / sizeof(uint16_t));
+            dbg.finite(conv.gate, nel);
+        }
+        const kda_status_t st = dbg.inputs_status();
+        if (st != KDA_OK) return st;
+    }
+    kda::WaitCtl wait;
+    wait.abort_out = dbg.abort_word();
+    wait.spin_limit = dbg.spin_limit();
+
     hipMemPool_t pool = nullptr;
     if (pool_for_device(&pool) != hipSuccess) return KDA_ERR_HIP;
     void* ws = nullptr;
@@ -173,7 +224,7 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
         if constexpr (v16) {
             e1 = kda::launch_prep16(q, k, g, G16, beta, B, T, H, c0, n, ws, conv, stream);
             e2 = e1 == hipSuccess ? kda::launch_scan16(ws, v, h_in, h_out, out, scale, B, T, H, c0,
-                                                       n, conv, stream)
+                                                       n, conv, wait, stream)
                                   : e1;
         } else {
             e1 = kda::launch_chunk_prep_f32(static_cast<const float*>(q),
@@ -198,6 +249,7 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
         st = KDA_ERR_HIP;
     if (carry) (void)hipFreeAsync(carry, stream);
     (void)hipFreeAsync(ws, stream);
+    if (st == KDA_OK && dbg.on()) st = dbg.device_status();
     return st;
 }
 
@@ -246,19 +298,67 @@ kda_status_t chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g, co
         for (int a = 0; a < kSlots; ++a)
             if (a != w && overlap(all[w].p, all[w].n, all[a].p, all[a].n))
                 return KDA_ERR_INVALID_ARG;
+    if ((int64_t)B * H * 2 > kMaxBlocks) return KDA_ERR_UNSUPPORTED;  // two scan slices a head
+
+    // Segments of seg chunks within the workspace budget (8 GB by default).
+    // Segment s needs the state entering it: a forward pass over the segments
+    // before the last keeps those states (checkpoints, one per segment), then
+    // the segments are differentiated last to first, each recomputing its
+    // records and states from its checkpoint, the state gradient carried from
+    // one to the one before.  One segment (the whole sequence) needs neither.
     const int nch = (T + 63) / 64;
-    if ((int64_t)B * H * nch > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const size_t per_chunk = kda::chunk_bwd_segment_bytes_per_chunk(B, H);
+    int seg = (int)(workspace_budget(8192) / per_chunk);
+    if (seg < 1) seg = 1;
+    if (seg > nch) seg = nch;
+    if ((int64_t)B * H * seg > kMaxBlocks) seg = (int)(kMaxBlocks / ((int64_t)B * H));
+    if (seg < 1) return KDA_ERR_UNSUPPORTED;
+    const int nseg = (nch + seg - 1) / seg;
+    const size_t sfloats = sbytes / sizeof(float);
+
+    kda::DebugScope dbg(stream);
+    if (dbg.on()) {
+        if (dbg.setup_status() != KDA_OK) return dbg.setup_status();
+        const size_t nel = n_tok * KDA_HEAD_DIM;
+        dbg.finite(q, nel);
+        dbg.finite(k, nel);
+        dbg.finite(v, nel);
+        dbg.decay(g, nel);
+        dbg.finite(beta, n_tok);
+        dbg.finite(dout, nel);
+        dbg.finite(h0, sfloats);
+        dbg.finite(dhT, sfloats);
+        const kda_status_t st = dbg.inputs_status();
+        if (st != KDA_OK) return st;
+    }
 
     hipMemPool_t pool = nullptr;
     if (pool_for_device(&pool) != hipSuccess) return KDA_ERR_HIP;
+    // the segment's workspace, then the checkpoints of segments 1 .. nseg - 1
+    // and the carried state gradient
+    const size_t seg_bytes = per_chunk * seg;
+    const size_t extra = nseg > 1 ? (size_t)nseg * sbytes : 0;
     void* ws = nullptr;
-    if (hipMallocFromPoolAsync(&ws, kda::chunk_bwd_f32_workspace_bytes(B, T, H), pool, stream) !=
-        hipSuccess)
+    if (hipMallocFromPoolAsync(&ws, seg_bytes + extra, pool, stream) != hipSuccess)
         return KDA_ERR_NO_MEMORY;
-    const hipError_t e = kda::launch_chunk_bwd<IO>(q, k, v, g, beta, scale, h0, dout, dhT, dq, dk,
-                                                   dv, dg, dbeta, dh0, B, T, H, ws, stream);
+    float* ckpt = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + seg_bytes);
+    float* dcarry = ckpt + (size_t)(nseg - 1) * sfloats;
+    hipError_t e = hipSuccess;
+    for (int sg = 0; sg + 1 < nseg && e == hipSuccess; ++sg)
+        e = kda::launch_chunk_fwd_state<IO>(q, k, v, g, beta,
+                                            sg == 0 ? h0 : ckpt + (size_t)(sg - 1) * sfloats,
+                                            ckpt + (size_t)sg * sfloats, B, T, H, sg * seg, seg,
+                                            ws, stream);
+    for (int sg = nseg - 1; sg >= 0 && e == hipSuccess; --sg) {
+        const int c0 = sg * seg, n = nch - c0 < seg ? nch - c0 : seg;
+        e = kda::launch_chunk_bwd_segment<IO>(
+            q, k, v, g, beta, scale, sg == 0 ? h0 : ckpt + (size_t)(sg - 1) * sfloats, dout,
+            sg == nseg - 1 ? dhT : dcarry, dq, dk, dv, dg, dbeta, sg == 0 ? dh0 : dcarry, B, T, H,
+            c0, n, ws, stream);
+    }
     (void)hipFreeAsync(ws, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    return dbg.on() ? dbg.device_status() : KDA_OK;
 }
 
 // conv != NULL: q, k, v are raw values before the short convolution (bf16 I/O
@@ -312,14 +412,132 @@ kda_status_t recurrent_step(const void* q, const void* k, const void* v, const f
         conv->B = B;
         conv->H = H;
     }
+    kda::DebugScope dbg(stream);
+    if (dbg.on()) {
+        if (dbg.setup_status() != KDA_OK) return dbg.setup_status();
+        const size_t nel = nbh * KDA_HEAD_DIM;
+        if constexpr (F32) {
+            dbg.finite(static_cast<const float*>(q), nel);
+            dbg.finite(static_cast<const float*>(k), nel);
+            dbg.finite(static_cast<const float*>(v), nel);
+        } else {
+            dbg.finite(static_cast<const uint16_t*>(q), nel);
+            dbg.finite(static_cast<const uint16_t*>(k), nel);
+            dbg.finite(static_cast<const uint16_t*>(v), nel);
+        }
+        dbg.decay(g, nel);
+        dbg.finite(beta, nbh);
+        dbg.finite(S, nbh * KDA_HEAD_DIM * KDA_HEAD_DIM);
+        if (conv) {
+            const size_t nw = (size_t)H * KDA_HEAD_DIM * 4;
+            dbg.finite(conv->wq, nw);
+            dbg.finite(conv->wk, nw);
+            dbg.finite(conv->wv, nw);
+            dbg.finite(static_cast<const uint16_t*>(conv->state), (size_t)9 * nbh * KDA_HEAD_DIM);
+            dbg.finite(conv->gate, nel);
+        }
+        const kda_status_t st = dbg.inputs_status();
+        if (st != KDA_OK) return st;
+    }
     const hipError_t e =
         kda::launch_decode<F32>(q, k, v, g, beta, scale, S, out, B, H, conv, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    return dbg.on() ? dbg.device_status() : KDA_OK;
 }
 
 }  // namespace
 
 namespace kda {
+
+// The status words of the KDA_DEBUG_CHECKS mode, one array per GPU (each device
+// holds its own copy at its own address): [0] a value outside its range, [1]
+// a value not finite, [2] a bounded device wait gave up.
+__device__ __align__(256) unsigned kda_debug_words[4];
+
+namespace {
+std::mutex g_words_mu;
+unsigned* g_words[kMaxDevices] = {};
+
+// the current device's status words (device address), looked up once per device
+hipError_t debug_words(unsigned** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_words_mu);
+    if (!g_words[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(kda_debug_words));
+        if (e != hipSuccess) return e;
+        g_words[dev] = static_cast<unsigned*>(p);
+    }
+    *out = g_words[dev];
+    return hipSuccess;
+}
+
+template <bool BF16>
+__global__ void kda_check_kernel(const void* __restrict__ p, size_t n, float lo, float hi,
+                                 unsigned* __restrict__ flags) {
+    bool out_of_range = false, not_finite = false;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = BF16 ? bf2f(static_cast<const uint16_t*>(p)[i])
+                             : static_cast<const float*>(p)[i];
+        if (lo <= hi && !(x >= lo && x <= hi)) out_of_range = true;
+        if (!isfinite(x)) not_finite = true;
+    }
+    if (out_of_range) flags[0] = 1u;
+    if (not_finite) flags[1] = 1u;
+}
+}  // namespace
+
+hipError_t launch_check(const void* p, size_t n, bool bf16, float lo, float hi,
+                        unsigned* flags, hipStream_t stream) {
+    if (!p || n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (bf16)
+        hipLaunchKernelGGL(kda_check_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           p, n, lo, hi, flags);
+    else
+        hipLaunchKernelGGL(kda_check_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           p, n, lo, hi, flags);
+    return hipGetLastError();
+}
+
+DebugScope::DebugScope(hipStream_t stream) : stream_(stream) {
+    on_ = env_long("KDA_DEBUG_CHECKS", 0) != 0;
+    if (!on_) return;
+    const long lim = env_long("KDA_DEBUG_SPIN_LIMIT", 0);
+    if (lim > 0) spin_ = (unsigned)(lim < (long)kDefaultSpinLimit ? lim : kDefaultSpinLimit);
+    if (debug_words(&flags_) != hipSuccess ||
+        launch_copy_or_zero(nullptr, reinterpret_cast<float*>(flags_), 4, stream_) != hipSuccess)
+        setup_ = KDA_ERR_HIP;
+}
+
+void DebugScope::check(const void* p, size_t n, bool bf16, float lo, float hi) {
+    if (!on_ || setup_ != KDA_OK || !p) return;
+    if (launch_check(p, n, bf16, lo, hi, flags_, stream_) != hipSuccess) launch_failed_ = true;
+}
+
+kda_status_t DebugScope::inputs_status() {
+    if (!on_) return KDA_OK;
+    if (setup_ != KDA_OK || launch_failed_) return KDA_ERR_HIP;
+    unsigned w[4] = {0u, 0u, 0u, 0u};
+    if (hipMemcpyAsync(w, flags_, sizeof(w), hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+        return KDA_ERR_HIP;
+    return (w[0] | w[1]) ? KDA_ERR_PRECONDITION : KDA_OK;
+}
+
+kda_status_t DebugScope::device_status() {
+    if (!on_) return KDA_OK;
+    unsigned w[4] = {0u, 0u, 0u, 0u};
+    if (hipMemcpyAsync(w, flags_, sizeof(w), hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+        return KDA_ERR_HIP;
+    return w[2] ? KDA_ERR_DEVICE : KDA_OK;
+}
 
 __global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                     size_t n) {
@@ -421,6 +639,13 @@ kda_status_t kda_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                                dh0, B, T, H, stream);
 }
 
+kda_status_t kda_trim_workspace(void) {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    for (int d = 0; d < kMaxDevices; ++d)
+        if (g_pools[d] && hipMemPoolTrimTo(g_pools[d], 0) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
 const char* kda_status_string(kda_status_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK: success";
@@ -428,6 +653,12 @@ const char* kda_status_string(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: size not supported";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime or launch error";
         case KDA_ERR_NO_MEMORY: return "KDA_ERR_NO_MEMORY: workspace allocation failed";
+        case KDA_ERR_PRECONDITION:
+            return "KDA_ERR_PRECONDITION: an input breaks a precondition (g outside [-5, 0] or a "
+                   "value not finite; KDA_DEBUG_CHECKS)";
+        case KDA_ERR_DEVICE:
+            return "KDA_ERR_DEVICE: a device wait gave up; the outputs are invalid "
+                   "(KDA_DEBUG_CHECKS)";
     }
     return "KDA: unknown status";
 }

@@ -29,6 +29,7 @@
 
 #include "../../include/kda.h"
 #include "kda_common.hpp"
+#include "kda_debug.hpp"
 
 namespace kda {
 namespace {
@@ -262,12 +263,28 @@ kda_status_t step_bwd(const void* q, const void* k, const void* v, const float* 
             if (overlap(written[a], written_n[a], written[b], written_n[b]))
                 return KDA_ERR_INVALID_ARG;
     }
+    kda::DebugScope dbg(stream);
+    if (dbg.on()) {
+        if (dbg.setup_status() != KDA_OK) return dbg.setup_status();
+        const size_t nel = nbh * KDA_HEAD_DIM;
+        dbg.finite(static_cast<const io*>(q), nel);
+        dbg.finite(static_cast<const io*>(k), nel);
+        dbg.finite(static_cast<const io*>(v), nel);
+        dbg.finite(static_cast<const io*>(dout), nel);
+        dbg.decay(g, nel);
+        dbg.finite(beta, nbh);
+        dbg.finite(S_prev, nel * KDA_HEAD_DIM);
+        dbg.finite(dS, nel * KDA_HEAD_DIM);
+        const kda_status_t st = dbg.inputs_status();
+        if (st != KDA_OK) return st;
+    }
     hipLaunchKernelGGL(kda::kda_step_bwd_kernel<F32>, dim3((unsigned)nbh), dim3(256), 0, stream,
                        static_cast<const io*>(q), static_cast<const io*>(k),
                        static_cast<const io*>(v), g, beta, scale, S_prev,
                        static_cast<const io*>(dout), dS, static_cast<io*>(dq),
                        static_cast<io*>(dk), static_cast<io*>(dv), dg, dbeta);
-    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    return dbg.on() ? dbg.device_status() : KDA_OK;
 }
 
 }  // namespace

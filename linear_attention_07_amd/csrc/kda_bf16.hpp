@@ -9,24 +9,25 @@
 namespace kda {
 namespace b16 {
 
-constexpr unsigned kSpinLimit = 1u << 23;
-
 __device__ __forceinline__ void signal(unsigned* c, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Waits until *c >= target.  The wait is bounded: a wait that runs out sets the
-// workgroup's abort word, after which every wait returns at once, so the
-// kernel always ends (with meaningless results in that case).  All waves of a
-// workgroup are resident together, so the bound is never reached in practice.
-__device__ __forceinline__ void wait_for(unsigned* c, unsigned target, unsigned* abort_word) {
+// Waits until *c >= target.  The wait is bounded by spin_limit polls: a wait
+// that runs out sets the workgroup's abort word, after which every wait
+// returns at once, so the kernel always ends (with meaningless results in that
+// case, which the kernel reports to the host through its WaitCtl).  All waves
+// of a workgroup are resident together, so the default bound is never reached
+// in practice.
+__device__ __forceinline__ void wait_for(unsigned* c, unsigned target, unsigned* abort_word,
+                                         unsigned spin_limit) {
     unsigned spins = 0;
     while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
         if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u)
             break;
         __builtin_amdgcn_s_sleep(1);
-        if (++spins == kSpinLimit) {
+        if (++spins >= spin_limit) {
             __hip_atomic_store(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             break;
         }

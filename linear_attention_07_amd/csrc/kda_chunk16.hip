@@ -562,7 +562,7 @@ template <bool CONV>
 __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, float scale,
     const float* h_in, float* h_out, uint16_t* __restrict__ out, int T, int H, int chunk0,
-    int nchunks, ConvArgs conv) {
+    int nchunks, ConvArgs conv, WaitCtl wait) {
     // The record, verbatim: Kt / Qt once, the rest (Kb^T, T / M, gamma) in two
     // buffers by chunk parity, so that the rest of chunk i + 1 is in place
     // while chunk i is scanned.
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // beside the output stores hold those up).
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
-            if (i >= 2) wait_for(&sync_s[3], 4u * (i - 1), &sync_s[4]);
+            if (i >= 2) wait_for(&sync_s[3], 4u * (i - 1), &sync_s[4], wait.spin_limit);
             u32x4* rs = rest_s[i & 1];
 #pragma unroll
             for (int m = 0; m < kRestFull; ++m) rs[tid + 256 * m] = rb[m];
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             }
             // Kt, Qt (pieces 0..2047) and V, once the scan waves are done
             // with the previous ones
-            wait_for(&sync_s[1], 4u * i, &sync_s[4]);
+            wait_for(&sync_s[1], 4u * i, &sync_s[4], wait.spin_limit);
 #pragma unroll
             for (int m = 0; m < 8; ++m) kq_s[tid + 256 * m] = ra[m];
 #pragma unroll
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             }
             signal(&sync_s[0], lane);
             if (i + 1 < nchunks) {
-                wait_for(&sync_s[5], 4u * i, &sync_s[4]);
+                wait_for(&sync_s[5], 4u * i, &sync_s[4], wait.spin_limit);
                 KDA_LOAD_ISSUE(i + 1);
             }
         }
@@ -801,7 +801,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         }
         for (int i = 0; i < nchunks; ++i) {
             const int64_t c0 = (int64_t)(chunk0 + i) * kChunk;
-            wait_for(&sync_s[0], 4u * (i + 1), &sync_s[4]);
+            wait_for(&sync_s[0], 4u * (i + 1), &sync_s[4], wait.spin_limit);
 
             // Pk = Kt S (rows token 4g + e, column n) and Pq = (Qt S)^T (rows
             // column 4g + e, column token n): the S slice serves as the B
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 }
             }
             signal(&sync_s[1], lane);  // Kt, Qt, V consumed
-            wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4]);
+            wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4], wait.spin_limit);
             const u32x4* rs = rest_s[i & 1];
             const u32x4* kb_s = rs;
             const u32x4* th_s = rs + (Rec16::TM - Rec16::KB + 0 * Rec16::kTM) / 16;
@@ -950,6 +950,10 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
         }
     }
+    // a wait of this wave (or of one that ended before) gave up: tell the host
+    if (wait.abort_out && lane == 0 &&
+        __hip_atomic_load(&sync_s[4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u)
+        wait.abort_out[0] = 1u;
 }
 
 hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
@@ -977,16 +981,18 @@ hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf1
 
 hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
                          void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
-                         const ConvArgs& conv, hipStream_t stream) {
+                         const ConvArgs& conv, const WaitCtl& wait, hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * kSlices);
     if (conv.wq)
         hipLaunchKernelGGL(kda_scan16_kernel<true>, dim3(nblk), dim3(512), 0, stream,
                            static_cast<const uint8_t*>(ws), static_cast<const uint16_t*>(v), scale,
-                           h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks, conv);
+                           h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks, conv,
+                           wait);
     else
         hipLaunchKernelGGL(kda_scan16_kernel<false>, dim3(nblk), dim3(512), 0, stream,
                            static_cast<const uint8_t*>(ws), static_cast<const uint16_t*>(v), scale,
-                           h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks, conv);
+                           h_in, h_out, static_cast<uint16_t*>(out), T, H, chunk0, nchunks, conv,
+                           wait);
     return hipGetLastError();
 }
 

@@ -200,10 +200,12 @@ struct __align__(16) StateScanLds {
     float gam[kD];
 };
 
+// Chunks chunk0 .. chunk0 + nch - 1 of the sequence (records, states local to
+// the segment); h_out (or NULL) receives the state leaving the last one.
 template <typename IO>
 __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
     const uint8_t* __restrict__ rec, const IO* __restrict__ v, const float* __restrict__ h0,
-    float* __restrict__ states, int T, int H, int nch) {
+    float* __restrict__ states, float* __restrict__ h_out, int T, int H, int chunk0, int nch) {
     __shared__ StateScanLds s;
     int bh, slice;
     scan_ids(bh, slice);
@@ -222,11 +224,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
     float gpf = 0.f;
     auto fetch = [&](int c) {
         const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
-        const int L = min(kChunk, T - c * kChunk);
+        const int cg = chunk0 + c;
+        const int L = min(kChunk, T - cg * kChunk);
         const float* Tg = reinterpret_cast<const float*>(r + RF::TH);
         const float* Wg = reinterpret_cast<const float*>(r + RF::W);
         const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
-        const IO* Vg = v + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+        const IO* Vg = v + (((size_t)b * T + (size_t)cg * kChunk) * H + h) * kD + col0;
 #pragma unroll
         for (int u = 0; u < 12; ++u) {
             if (u < 2) {
@@ -296,6 +299,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
             [&](int k, int j) { return col4(&s.Z[k][j], kScanCols); },
             [&](int i, int j, float a) { s.S[i][j] = fmaf(s.gam[i], s.S[i][j], a); });
     }
+    if (h_out) {
+        __syncthreads();
+        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
+            const int i = e / kScanCols, j = e % kScanCols;
+            h_out[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] = s.S[i][j];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -315,11 +325,14 @@ struct __align__(16) GradScanLds {
 };
 static_assert(kD * kP64 >= kChunk * kP128, "W must fit in the Kb^T buffer");
 
+// Chunks chunk0 .. chunk0 + nch - 1 (records and dS' local to the segment):
+// dhT is the gradient of the state leaving the last of them, dh0 receives that
+// of the state entering the first.  dh0 may equal dhT (each workgroup reads its
+// slice before it writes it).
 template <typename IO>
 __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
-    const uint8_t* __restrict__ rec, const IO* __restrict__ dout,
-    const float* __restrict__ dhT, float* __restrict__ dsn, float* __restrict__ dh0,
-    float scale, int T, int H, int nch) {
+    const uint8_t* __restrict__ rec, const IO* __restrict__ dout, const float* dhT,
+    float* __restrict__ dsn, float* dh0, float scale, int T, int H, int chunk0, int nch) {
     __shared__ GradScanLds s;
     int bh, slice;
     scan_ids(bh, slice);
@@ -338,11 +351,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
     float gpf = 0.f;
     auto fetch = [&](int c) {
         const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
-        const int L = min(kChunk, T - c * kChunk);
+        const int cg = chunk0 + c;
+        const int L = min(kChunk, T - cg * kChunk);
         const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
         const float* Qg = reinterpret_cast<const float*>(r + RF::QP);
         const float* Wg = reinterpret_cast<const float*>(r + RF::W);
-        const IO* Og = dout + (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD + col0;
+        const IO* Og = dout + (((size_t)b * T + (size_t)cg * kChunk) * H + h) * kD + col0;
 #pragma unroll
         for (int u = 0; u < 14; ++u) {
             if (u < 4) {
@@ -458,17 +472,19 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const IO* __restrict__ dout,
     const float* __restrict__ states, const float* __restrict__ dsn,
     const float* __restrict__ xs, float* __restrict__ scr_all,
-    float scale, int T, int H, int nch, IO* __restrict__ dq, IO* __restrict__ dk,
+    float scale, int T, int H, int chunk0, int nch, IO* __restrict__ dq, IO* __restrict__ dk,
     IO* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
     __shared__ BwdLds s;
 
+    // chunk c of the segment (states, dS', X, scratch) is chunk cg of the sequence
     const int c = blockIdx.x % nch;
     const int bh = blockIdx.x / nch;
     const int b = bh / H, h = bh % H;
-    const int L = min(kChunk, T - c * kChunk);
+    const int cg = chunk0 + c;
+    const int L = min(kChunk, T - cg * kChunk);
     const int tid = threadIdx.x;
     const size_t rp = (size_t)H * kD;  // pitch of one token row
-    const size_t base = (((size_t)b * T + (size_t)c * kChunk) * H + h) * kD;
+    const size_t base = (((size_t)b * T + (size_t)cg * kChunk) * H + h) * kD;
     const float* S = states + ((size_t)bh * nch + c) * kStateFloats;
     const float* dSn = dsn + ((size_t)bh * nch + c) * kStateFloats;
     float* scr = scr_all + (size_t)blockIdx.x * kScrFloats;
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         if (part == 0) {
             s.rq[r] = rq;
             s.rk[r] = rk;
-            s.beta[r] = r < L ? beta[((size_t)b * T + (size_t)c * kChunk + r) * H + h] : 0.f;
+            s.beta[r] = r < L ? beta[((size_t)b * T + (size_t)cg * kChunk + r) * H + h] : 0.f;
             s.dbeta[r] = 0.f;
             s.dotq[r] = 0.f;
             s.dotk[r] = 0.f;
@@ -879,55 +895,83 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         }
     } else if (tid < kD + kChunk) {
         const int r = tid - kD;
-        if (r < L) dbeta[((size_t)b * T + (size_t)c * kChunk + r) * H + h] = s.dbeta[r];
+        if (r < L) dbeta[((size_t)b * T + (size_t)cg * kChunk + r) * H + h] = s.dbeta[r];
     }
 }
 
 }  // namespace
 
-size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H) {
-    const size_t nch = (size_t)(T + kChunk - 1) / kChunk;
-    const size_t n = (size_t)B * H * nch;
-    return n * (RF::BYTES +
-                (2 * kStateFloats + (size_t)kChunk * kChunk + kScrFloats) * sizeof(float));
+size_t chunk_bwd_segment_bytes_per_chunk(int B, int H) {
+    return (size_t)B * H *
+           (RF::BYTES + (2 * kStateFloats + (size_t)kChunk * kChunk + kScrFloats) * sizeof(float));
 }
 
+namespace {
+// Workspace of a segment of nch chunks: records, then the states entering the
+// chunks, the state gradients leaving them, X and the chunk kernels' scratch.
+struct SegWs {
+    uint8_t* rec;
+    float *states, *dsn, *xs, *scr;
+    SegWs(void* ws, int B, int H, int nch) {
+        const size_t n = (size_t)B * H * nch;
+        rec = static_cast<uint8_t*>(ws);
+        states = reinterpret_cast<float*>(rec + n * RF::BYTES);
+        dsn = states + n * kStateFloats;
+        xs = dsn + n * kStateFloats;
+        scr = xs + n * kChunk * kChunk;
+    }
+};
+}  // namespace
+
 template <typename IO>
-hipError_t launch_chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g,
-                            const float* beta, float scale, const float* h0, const IO* dout,
-                            const float* dhT, IO* dq, IO* dk, IO* dv, float* dg, float* dbeta,
-                            float* dh0, int B, int T, int H, void* ws, hipStream_t stream) {
-    const int nch = (T + kChunk - 1) / kChunk;
-    const size_t n = (size_t)B * H * nch;
-    uint8_t* rec = static_cast<uint8_t*>(ws);
-    float* states = reinterpret_cast<float*>(rec + n * RF::BYTES);
-    float* dsn = states + n * kStateFloats;
-    float* xs = dsn + n * kStateFloats;
-    float* scr = xs + n * kChunk * kChunk;
-    hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, 0, nch, rec, stream, xs);
+hipError_t launch_chunk_fwd_state(const IO* q, const IO* k, const IO* v, const float* g,
+                                  const float* beta, const float* h_in, float* h_out, int B,
+                                  int T, int H, int chunk0, int nch, void* ws,
+                                  hipStream_t stream) {
+    const SegWs w(ws, B, H, nch);
+    hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, chunk0, nch, w.rec, stream);
     if (e != hipSuccess) return e;
     const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
     hipLaunchKernelGGL(kda_bwd_state_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
-                       rec, v, h0, states, T, H, nch);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
-                       rec, dout, dhT, dsn, dh0, scale, T, H, nch);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_bwd_chunk_kernel<IO>, dim3((unsigned)n), dim3(kCT), 0, stream, q, k, v,
-                       g, beta, dout, states, dsn, xs, scr, scale, T, H, nch, dq, dk, dv, dg,
-                       dbeta);
+                       w.rec, v, h_in, w.states, h_out, T, H, chunk0, nch);
     return hipGetLastError();
 }
 
-template hipError_t launch_chunk_bwd<float>(const float*, const float*, const float*,
-                                            const float*, const float*, float, const float*,
-                                            const float*, const float*, float*, float*, float*,
-                                            float*, float*, float*, int, int, int, void*,
-                                            hipStream_t);
-template hipError_t launch_chunk_bwd<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*,
-                                               const float*, const float*, float, const float*,
-                                               const uint16_t*, const float*, uint16_t*,
-                                               uint16_t*, uint16_t*, float*, float*, float*, int,
-                                               int, int, void*, hipStream_t);
+template <typename IO>
+hipError_t launch_chunk_bwd_segment(const IO* q, const IO* k, const IO* v, const float* g,
+                                    const float* beta, float scale, const float* h_in,
+                                    const IO* dout, const float* dS_in, IO* dq, IO* dk, IO* dv,
+                                    float* dg, float* dbeta, float* dS_out, int B, int T, int H,
+                                    int chunk0, int nch, void* ws, hipStream_t stream) {
+    const SegWs w(ws, B, H, nch);
+    hipError_t e =
+        launch_chunk_prep_f32(q, k, g, beta, B, T, H, chunk0, nch, w.rec, stream, w.xs);
+    if (e != hipSuccess) return e;
+    const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
+    hipLaunchKernelGGL(kda_bwd_state_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
+                       w.rec, v, h_in, w.states, nullptr, T, H, chunk0, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_bwd_grad_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
+                       w.rec, dout, dS_in, w.dsn, dS_out, scale, T, H, chunk0, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t n = (size_t)B * H * nch;
+    hipLaunchKernelGGL(kda_bwd_chunk_kernel<IO>, dim3((unsigned)n), dim3(kCT), 0, stream, q, k, v,
+                       g, beta, dout, w.states, w.dsn, w.xs, w.scr, scale, T, H, chunk0, nch, dq,
+                       dk, dv, dg, dbeta);
+    return hipGetLastError();
+}
+
+#define KDA_INST_BWD(IO)                                                                        \
+    template hipError_t launch_chunk_fwd_state<IO>(const IO*, const IO*, const IO*,              \
+                                                   const float*, const float*, const float*,     \
+                                                   float*, int, int, int, int, int, void*,       \
+                                                   hipStream_t);                                 \
+    template hipError_t launch_chunk_bwd_segment<IO>(                                            \
+        const IO*, const IO*, const IO*, const float*, const float*, float, const float*,        \
+        const IO*, const float*, IO*, IO*, IO*, float*, float*, float*, int, int, int, int, int, \
+        void*, hipStream_t);
+KDA_INST_BWD(float)
+KDA_INST_BWD(uint16_t)
+#undef KDA_INST_BWD
 
 }  // namespace kda

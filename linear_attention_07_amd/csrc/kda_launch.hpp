@@ -57,19 +57,29 @@ hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_
                                  float* out, float scale, int B, int T, int H, int chunk0,
                                  int nchunks, hipStream_t stream);
 
-// Backward of the fp32 chunked prefill: prep records, a forward scan storing
-// the state entering each chunk, a reverse scan storing the state gradient
-// leaving each chunk (and dh0), and one gradient workgroup per chunk.  ws
-// holds chunk_bwd_f32_workspace_bytes(B, T, H) bytes.  h0, dhT: NULL = zeros;
-// dh0: NULL = not stored.
+// Backward of the chunked prefill over one segment of chunks [chunk0, chunk0 +
+// nch): prep records, a forward scan storing the state entering each chunk
+// (from h_in, the state entering chunk0; NULL = zeros), a reverse scan storing
+// the state gradient leaving each chunk (from dS_in, the gradient of the state
+// leaving the segment; NULL = zeros) and writing that of the state entering it
+// to dS_out (NULL = not stored; may equal dS_in), and one gradient workgroup
+// per chunk.  ws holds chunk_bwd_segment_bytes_per_chunk(B, H) * nch bytes.
+// launch_chunk_fwd_state runs only the first two launches, and writes the
+// state leaving the segment to h_out (the checkpoints of a segmented call).
 // IO = float or uint16_t (bf16 q, k, v, dout in and dq, dk, dv out; all
 // arithmetic fp32).
-size_t chunk_bwd_f32_workspace_bytes(int B, int T, int H);
+size_t chunk_bwd_segment_bytes_per_chunk(int B, int H);
 template <typename IO>
-hipError_t launch_chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g,
-                            const float* beta, float scale, const float* h0, const IO* dout,
-                            const float* dhT, IO* dq, IO* dk, IO* dv, float* dg, float* dbeta,
-                            float* dh0, int B, int T, int H, void* ws, hipStream_t stream);
+hipError_t launch_chunk_fwd_state(const IO* q, const IO* k, const IO* v, const float* g,
+                                  const float* beta, const float* h_in, float* h_out, int B,
+                                  int T, int H, int chunk0, int nch, void* ws,
+                                  hipStream_t stream);
+template <typename IO>
+hipError_t launch_chunk_bwd_segment(const IO* q, const IO* k, const IO* v, const float* g,
+                                    const float* beta, float scale, const float* h_in,
+                                    const IO* dout, const float* dS_in, IO* dq, IO* dk, IO* dv,
+                                    float* dg, float* dbeta, float* dS_out, int B, int T, int H,
+                                    int chunk0, int nch, void* ws, hipStream_t stream);
 
 // Short convolution in front of the attention: depthwise 4-tap causal filter
 // per head and channel, then SiLU, on q, k and v.  wq == NULL: none.  state:
@@ -92,12 +102,18 @@ struct ConvArgs {
 // h_out NULL = final state not stored).
 size_t chunk16_record_bytes();
 int chunk16_slices();
+// The scan's bounded LDS waits: their spin limit, and where a wait that gives
+// up records it (NULL: nowhere).
+struct WaitCtl {
+    unsigned* abort_out = nullptr;
+    unsigned spin_limit = 1u << 23;
+};
 hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
                          const float* beta, int B, int T, int H, int chunk0, int nchunks, void* ws,
                          const ConvArgs& conv, hipStream_t stream);
 hipError_t launch_scan16(const void* ws, const void* v, const float* h_in, float* h_out,
                          void* out, float scale, int B, int T, int H, int chunk0, int nchunks,
-                         const ConvArgs& conv, hipStream_t stream);
+                         const ConvArgs& conv, const WaitCtl& wait, hipStream_t stream);
 // the conv state after the sequence: the last 3 raw tokens of q, k, v (from
 // the inputs, or from conv.state where T < 3), [3][B][3][H][128]; safe in
 // place (st_out == conv.state)

@@ -22,6 +22,8 @@ KDA_ERR_INVALID_ARG = 1
 KDA_ERR_UNSUPPORTED = 2
 KDA_ERR_HIP = 3
 KDA_ERR_NO_MEMORY = 4
+KDA_ERR_PRECONDITION = 5
+KDA_ERR_DEVICE = 6
 
 EXPORTS = (
     "kda_chunk_bwd",
@@ -36,6 +38,7 @@ EXPORTS = (
     "kda_recurrent_step_conv",
     "kda_recurrent_step_f32",
     "kda_status_string",
+    "kda_trim_workspace",
 )
 
 _lib = None
@@ -80,12 +83,22 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_trim_workspace.argtypes = []
+    lib.kda_trim_workspace.restype = ctypes.c_int
     _lib = lib
     return lib
 
 
 def status_string(status: int) -> str:
     return load().kda_status_string(int(status)).decode()
+
+
+def trim_workspace() -> None:
+    """Hand the library's cached workspace memory back to the driver (call
+    when none of its work is in flight)."""
+    st = load().kda_trim_workspace()
+    if st != KDA_OK:
+        raise KDAError(st, "kda_trim_workspace")
 
 
 def _ptr(t):

@@ -13,11 +13,12 @@ the per-channel decay).  Inputs are widened to float64 from whatever exact
 values the caller holds (for GPU parity: the very bf16/fp32 bytes the GPU
 consumed), so input quantisation never counts as error.
 
-``step_backward`` is the reverse-mode derivative of one recurrent step, and
-``chunk_backward`` that of the chunkwise form over a whole sequence (the
-state entering each chunk kept from a forward pass, the chunks differentiated
-in reverse); the first is pinned to central differences, the second to the
-first chained token by token.
+``step_backward`` is the reverse-mode derivative of one recurrent step and
+``sequence_backward`` that of the whole recurrence, token by token in reverse
+over the kept states (in ``kda_oracle.c``); both are pinned to central
+differences of ``forward``.  ``chunk_backward`` differentiates the chunkwise
+form instead; it is kept as a CPU cross-check of that algebra, pinned to the
+token-by-token backward, and is not the reference of any GPU comparison.
 
 Layouts follow the library's: q, k, v, g, o are ``[B, T, H, D]``; beta is
 ``[B, T, H]``; h0 and hT are ``[B, H, Dk, Dv]`` (key channel = row).
@@ -59,6 +60,11 @@ def _load():
         dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_double, dp, dp, dp,
         ctypes.c_int]
     lib.kda_oracle_run.restype = ctypes.c_int
+    lib.kda_oracle_seq_backward.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_double, dp, dp, dp,
+        dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.kda_oracle_seq_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -281,6 +287,41 @@ def step_backward(q, k, v, g, beta, scale, S_prev, d_o, dS_next, eps=1e-6):
             dq[b, h] = rq * dqh - rq ** 3 * (q[b, h] @ dqh) * q[b, h]
             dk[b, h] = rk * dkh - rk ** 3 * (k[b, h] @ dkh) * k[b, h]
     return dq, dk, dv, dg, dbeta, dS_prev
+
+
+def sequence_backward(q, k, v, g, beta, scale, h0, d_o, d_hT=None, eps=1e-6, threads=None):
+    """Gradients of L = <d_o, o> + <d_hT, hT> for (o, hT) = forward(q, k, v,
+    g, beta, scale, h0): the recurrence run forward keeping the state before
+    every token, then every token's assignments differentiated in reverse
+    order (kda_oracle_seq_backward in kda_oracle.c), exactly the chain of
+    ``step_backward`` over the sequence.  Library layout as ``forward``; h0
+    and d_hT may be None (zeros).  Returns (dq, dk, dv, dg, dbeta, dh0) in
+    fp64.  Each thread keeps T + 1 states of one sequence: (T + 1) * Dk * Dv
+    doubles."""
+    q, k, v, g, beta, h0, d_o, d_hT = map(_f64, (q, k, v, g, beta, h0, d_o, d_hT))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+
+    def seq(x):  # [B, T, H, D] -> [B*H, T, D]
+        return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(B * H, T, x.shape[3]))
+
+    def unseq(x):  # [B*H, T, D] -> [B, T, H, D]
+        return np.ascontiguousarray(x.reshape(B, H, T, x.shape[2]).transpose(0, 2, 1, 3))
+
+    n = B * H
+    gq, gk, gv, gg = (np.zeros((n, T, d)) for d in (dk, dk, dv, dk))
+    gb = np.zeros((n, T))
+    dh0 = np.zeros((n, dk, dv))
+    st = lambda x: None if x is None else np.ascontiguousarray(x.reshape(n, dk, dv))
+    rc = _load().kda_oracle_seq_backward(
+        n, T, dk, dv, _ptr(seq(q)), _ptr(seq(k)), _ptr(seq(v)), _ptr(seq(g)),
+        _ptr(np.ascontiguousarray(beta.transpose(0, 2, 1).reshape(n, T))), float(scale),
+        float(eps), _ptr(st(h0)), _ptr(seq(d_o)), _ptr(st(d_hT)), _ptr(gq), _ptr(gk), _ptr(gv),
+        _ptr(gg), _ptr(gb), _ptr(dh0), int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_seq_backward failed with {rc}")
+    dbeta = np.ascontiguousarray(gb.reshape(B, H, T).transpose(0, 2, 1))
+    return unseq(gq), unseq(gk), unseq(gv), unseq(gg), dbeta, dh0.reshape(B, H, dk, dv)
 
 
 # ---------------------------------------------------------------------------

@@ -43,10 +43,20 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    names = ("KDA_OK", "KDA_ERR_INVALID_ARG", "KDA_ERR_UNSUPPORTED", "KDA_ERR_HIP",
+             "KDA_ERR_NO_MEMORY", "KDA_ERR_PRECONDITION", "KDA_ERR_DEVICE")
+    header = open(HEADER).read()
+    for code, name in enumerate(names):
         s = libkda.status_string(code)
-        assert s.startswith("KDA_")
+        assert s.startswith(name + ":"), (code, s)
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", header), name   # the header's value
+        assert getattr(libkda, name) == code
     assert "unknown" in libkda.status_string(99)
+
+
+def test_trim_without_pools_is_a_no_op(lib):
+    # no pool was ever created on this GPU-less host: nothing to hand back
+    assert lib.kda_trim_workspace() == libkda.KDA_OK
 
 
 # Fake but 16-byte aligned, non-null device addresses: validation must fail
@@ -275,9 +285,14 @@ def test_chunk_bwd_invalid_arguments(lib):
     assert chunk_bwd(lib, T=0, dh0=NULL) == libkda.KDA_OK
 
 
-def test_chunk_bwd_grid_limit(lib):
-    # 4096 heads x 2049 chunks of workgroups exceed the launch limit
-    assert chunk_bwd(lib, spacing=1 << 40, H=4096, T=64 * 2048 + 1) == libkda.KDA_ERR_UNSUPPORTED
+def test_chunk_bwd_segments_any_length(lib):
+    # 4096 heads x 2049 chunks of workgroups would exceed the launch limit in
+    # one segment; the call is split into segments instead, so validation
+    # passes it on to the device (the first HIP call fails on this host)
+    assert chunk_bwd(lib, spacing=1 << 40, H=4096, T=64 * 2048 + 1) == libkda.KDA_ERR_HIP
+    # a head count past the scan's grid is still refused before any HIP call
+    assert chunk_bwd(lib, spacing=1 << 46, B=2, H=(1 << 21) + 1, T=64) == \
+        libkda.KDA_ERR_UNSUPPORTED
 
 
 def test_chunk_bwd_bf16_invalid_arguments(lib):

@@ -1,6 +1,8 @@
-"""GPU parity of kda_chunk_bwd_f32 (backward of the fp32 chunked prefill)
-against the fp64 oracle's chunk_backward, which is pinned to the step backward
-chained token by token (itself pinned to central differences of the forward).
+"""GPU parity of kda_chunk_bwd_f32 / kda_chunk_bwd (backward of the chunked
+prefill) against the fp64 oracle's sequence_backward: the recurrence run
+forward keeping every state, then differentiated token by token in reverse
+(the plain definition of the gradient, pinned to central differences of the
+oracle's forward).  Nothing chunk-shaped sits in the reference.
 
 fp32 arithmetic throughout.  fp32 I/O: the bar is the fp32-mode one, 1e-3
 normalised max error per gradient (max |gpu - oracle| / max |oracle|).  bf16
@@ -13,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from kda_check import host64, say
+from kda_check import host64, oracle_threads, say
 from linear_attention_07_amd import libkda, synth
 from oracle import oracle
 
@@ -48,8 +50,9 @@ def gpu(x):
 
 def ref(x):
     h = lambda t: None if t is None else host64(t)
-    return oracle.chunk_backward(h(x["q"]), h(x["k"]), h(x["v"]), h(x["g"]), h(x["beta"]),
-                                 x["scale"], h(x["h0"]), h(x["dout"]), h(x["dhT"]))
+    return oracle.sequence_backward(h(x["q"]), h(x["k"]), h(x["v"]), h(x["g"]), h(x["beta"]),
+                                    x["scale"], h(x["h0"]), h(x["dout"]), h(x["dhT"]),
+                                    threads=oracle_threads())
 
 
 def tol(name, io):
@@ -172,11 +175,57 @@ def test_chunk_bwd_bench_workload_sampled_heads(io):
     got = gpu(x)
     heads = [0, 47, w.H - 1]
     h = lambda t, ax: host64(t.index_select(ax, torch.tensor(heads, device=DEV)))
-    want = oracle.chunk_backward(h(x["q"], 2), h(x["k"], 2), h(x["v"], 2), h(x["g"], 2),
-                                 h(x["beta"], 2), x["scale"], h(x["h0"], 1), h(x["dout"], 2),
-                                 h(x["dhT"], 1))
+    want = oracle.sequence_backward(h(x["q"], 2), h(x["k"], 2), h(x["v"], 2), h(x["g"], 2),
+                                    h(x["beta"], 2), x["scale"], h(x["h0"], 1),
+                                    h(x["dout"], 2), h(x["dhT"], 1), threads=len(heads))
     axes = (2, 2, 2, 2, 2, 1)
     for n, a, b, ax in zip(NAMES, got, want, axes):
         e = rel(h(a, ax), b)
         say(f"chunk bwd {w.name} {io} heads {heads} {n}: {e:.1e}")
         assert e <= tol(n, io), (n, e)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_chunk_bwd_segmented_workspace(io, monkeypatch):
+    """A 1 MB workspace budget splits the call into one segment per chunk (a
+    forward pass keeping each segment's entering state, then the segments
+    differentiated last to first from their checkpoints, the state gradient
+    carried between them): bitwise the one-segment result, and the oracle's."""
+    x = inputs(2, 300, 2, seed=991, io=io)
+    one = gpu(x)
+    monkeypatch.setenv("KDA_WORKSPACE_MB", "1")
+    many = gpu(x)
+    for n, u, w in zip(NAMES, one, many):
+        assert torch.equal(u, w), n
+    check(x, f"{io} B=2 T=300 H=2 in 5 segments")
+    x["dhT"] = None            # no final gradient, no initial state wanted
+    r = libkda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], x["dout"],
+                         h0=x["h0"], dhT=None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(r[5]).all()
+
+
+def test_chunk_bwd_64k_in_a_fixed_budget():
+    """64K tokens x 96 heads (1024 chunks; about 43 GB of workspace in one
+    segment) inside the default 8 GB budget: six segments.  Two heads checked
+    in full against the token-by-token oracle."""
+    B, T, H = 1, 65536, 96
+    say(f"chunk bwd case B={B} T={T} H={H} fp32, default budget")
+    x = synth.prefill_inputs(B, T, H, torch.float32, seed=993, g_shift=4.0, h0_std=0.1,
+                             device=DEV)
+    gb = torch.Generator(device=DEV).manual_seed(994)
+    x["dout"] = torch.randn((B, T, H, 128), generator=gb, device=DEV)
+    x["dhT"] = 0.1 * torch.randn((B, H, 128, 128), generator=gb, device=DEV)
+    got = gpu(x)
+    for n, a in zip(NAMES, got):
+        assert torch.isfinite(a).all(), n
+    heads = [0, H - 1]
+    h = lambda t, ax: host64(t.index_select(ax, torch.tensor(heads, device=DEV)))
+    want = oracle.sequence_backward(h(x["q"], 2), h(x["k"], 2), h(x["v"], 2), h(x["g"], 2),
+                                    h(x["beta"], 2), x["scale"], h(x["h0"], 1),
+                                    h(x["dout"], 2), h(x["dhT"], 1), threads=len(heads))
+    for n, a, b, ax in zip(NAMES, got, want, (2, 2, 2, 2, 2, 1)):
+        e = rel(h(a, ax), b)
+        say(f"chunk bwd 64K heads {heads} {n}: {e:.1e}")
+        assert e <= TOL, (n, e)
+    libkda.trim_workspace()

@@ -4,11 +4,14 @@ and the decode step's loads) against the fp64 oracle, through the C-ABI; plus
 the conv state hand-over from prefill to decode, and edge cases.
 
 The library rounds the filtered q, k, v to bf16 before the attention (its
-documented input type); the oracle does the same rounding (round_bf16_inputs),
-so the comparison measures the kernels, as with plain bf16 inputs.  Where the
-fp32 filter of the library and the fp64 filter of the oracle fall on either
-side of a bf16 rounding boundary the two inputs differ by one bf16 ulp, on a
-few entries in 10^4.
+documented input type).  Most comparisons give the oracle the same rounding
+(round_bf16_inputs), so that they measure the kernels, as with plain bf16
+inputs; where the fp32 filter of the library and the fp64 filter of the
+oracle fall on either side of a bf16 rounding boundary the two inputs differ
+by one bf16 ulp, on a few entries in 10^4.  The *_unrounded tests compare the
+whole layer with the oracle's plain fp64 filter, no rounding anywhere, at the
+same 1e-2 bar: the bf16 rounding of the filtered values is then counted as
+error too.
 """
 import os
 
@@ -34,7 +37,7 @@ def run(inp, conv_in="inp", h0="inp", **kw):
     return out, hT, cout
 
 
-def oracle_conv(inp, gate=None):
+def oracle_conv(inp, gate=None, rounded=True):
     ci = inp["conv_in"]
     cs = None if ci is None else tuple(host64(ci[i]) for i in range(3))
     h0 = inp["h0"]
@@ -42,7 +45,7 @@ def oracle_conv(inp, gate=None):
                                host64(inp["wq"]), host64(inp["wk"]), host64(inp["wv"]),
                                host64(inp["g"]), host64(inp["beta"]), inp["scale"],
                                None if h0 is None else host64(h0), cs, threads=oracle_threads(),
-                               round_bf16_inputs=True,
+                               round_bf16_inputs=rounded,
                                gate=None if gate is None else host64(gate))
 
 
@@ -75,6 +78,59 @@ def test_conv_layer_4k_all_heads():
     eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
     say(f"conv layer_4k: out err {eo:.2e} state err {es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("B,T,H,state", [(2, 1, 3, True), (2, 65, 3, True), (2, 1000, 3, False),
+                                         (1, 700, 8, True)])
+def test_conv_against_unrounded_oracle(B, T, H, state):
+    """The layer against the oracle's plain fp64 filter (no bf16 rounding of
+    the filtered q, k, v on the oracle's side): ragged lengths, with and
+    without a carried conv state."""
+    inp = synth.conv_inputs(B, T, H, seed=560 + T + H, with_state=state, device=DEV)
+    out, hT, cout = run(inp)
+    o_ref, h_ref, c_ref = oracle_conv(inp, rounded=False)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"conv unrounded B={B} T={T} H={H} state={state}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for i in range(3):
+        assert np.array_equal(host64(cout[i]), c_ref[i]), i
+
+
+def test_gated_conv_layer_4k_all_heads_unrounded():
+    """The whole layer (filter + attention + output gate), one 96-head layer
+    at T = 4096 with a carried conv state, every head against the unrounded
+    fp64 oracle."""
+    B, T, H = 1, 4096, 96
+    inp = synth.conv_inputs(B, T, H, seed=561, with_state=True, h0_std=0.1, device=DEV)
+    z = synth.gate_logits((B, T, H, 128), seed=562, device=DEV)
+    out, hT, _ = run(inp, gate=z)
+    o_ref, h_ref, _ = oracle_conv(inp, gate=z, rounded=False)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"gated conv layer_4k unrounded: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_gated_decode_b256_unrounded():
+    """The batched decode shape behind the filter and the gate, four steps,
+    every output and state against the unrounded fp64 oracle."""
+    B, H = 256, 96
+    p = synth.conv_params(B, H, seed=630, device=DEV)
+    S = synth.decode_state(B, H, seed=631, h0_std=0.1, device=DEV)
+    S_ref = host64(S)
+    for step in range(4):
+        x = synth.decode_conv_inputs(B, H, seed=632, step=step, device=DEV)
+        z = synth.gate_logits((B, H, 128), seed=633 + step, device=DEV)
+        o_ref, S_ref, _ = decode_conv_oracle(x, p, S_ref, gate=z, rounded=False)
+        out = libkda.recurrent_step_conv(x["q"], x["k"], x["v"], p["wq"], p["wk"], p["wv"],
+                                         p["conv_state"], x["g"], x["beta"], x["scale"], S,
+                                         gate=z)
+        torch.cuda.synchronize()
+        eo = rel_out(host64(out)[:, None], o_ref[:, None])
+        say(f"gated decode b256 unrounded step {step}: out err {eo:.2e}")
+        assert eo <= TOL_BF16
+    es = rel_state(host64(S), S_ref)
+    say(f"  state err {es:.2e}")
+    assert es <= TOL_BF16
 
 
 @pytest.mark.parametrize("split", [320, 100, 2])
@@ -165,12 +221,13 @@ def test_conv_filtered_values_match_oracle_closely():
     assert err <= TOL_BF16
 
 
-def decode_conv_oracle(x, p, S, gate=None):
+def decode_conv_oracle(x, p, S, gate=None, rounded=True):
     cs = tuple(host64(p["conv_state"][i]) for i in range(3))
     return oracle.step_conv(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(p["wq"]),
                             host64(p["wk"]), host64(p["wv"]), cs, host64(x["g"]),
                             host64(x["beta"]), x["scale"], S, threads=oracle_threads(),
-                            round_bf16_inputs=True, gate=None if gate is None else host64(gate))
+                            round_bf16_inputs=rounded,
+                            gate=None if gate is None else host64(gate))
 
 
 @pytest.mark.parametrize("B,H", [(3, 5), (2, 8)])

@@ -62,10 +62,15 @@ def test_beta_zero_pure_decay():
     assert not out0.any().item() and not hT0.any().item()
 
 
-@pytest.mark.parametrize("split", [64, 100, 1])
+@pytest.mark.parametrize("split", [64, 100, 1, 16, 32, 48])
 def test_chaining_matches_one_call(split):
     """Running T1 tokens and then T2 tokens from the returned state equals one
-    call over T1 + T2 tokens (state carry = resume)."""
+    call over T1 + T2 tokens (state carry = resume).  A split that is not a
+    multiple of 64 also moves every chunk boundary of the second call by
+    split mod 64 tokens (by 16, 32, 48 sub-blocks, or off the sub-block grid)
+    against the single call: the same tokens grouped into different chunks
+    and sub-blocks give the same result up to rounding, the chunk-partition
+    invariance of the chunk form."""
     B, T, H = 1, 640, 4
     inp = synth.prefill_inputs(B, T, H, torch.bfloat16, seed=33, h0_std=0.1, device=DEV)
     out, hT = chunk(inp)
@@ -214,3 +219,78 @@ def test_state_size_independent_of_context():
         _, hT = chunk(inp)
         assert hT.numel() * hT.element_size() == 6_291_456
     assert 69 * 6_291_456 == 434_110_464
+
+
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_norm_invariance(io):
+    """q and k are L2-normalised inside the kernel (深入 Kimi-K3 thread, KDA
+    paragraph): positive per-token rescaling of q and of k leaves o and the
+    final state unchanged up to the eps under the square root.  The factors
+    are powers of two from 2^-4 to 2^4, exact in bf16 and fp32, so the inputs
+    the kernels see differ by nothing but their scale."""
+    B, T, H = 2, 300, 3
+    inp = synth.prefill_inputs(B, T, H, io, seed=45, h0_std=0.1, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(46)
+    cq = torch.pow(2.0, torch.randint(-4, 5, (B, T, H, 1), generator=gen, device=DEV).float())
+    ck = torch.pow(2.0, torch.randint(-4, 5, (B, T, H, 1), generator=gen, device=DEV).float())
+    scaled = dict(inp)
+    scaled["q"] = (inp["q"].float() * cq).to(io)
+    scaled["k"] = (inp["k"].float() * ck).to(io)
+    assert torch.equal(scaled["q"].float() / cq, inp["q"].float())   # exact rescaling
+    out, hT = chunk(inp)
+    out2, hT2 = chunk(scaled)
+    eo, es = rel_out(host64(out2), host64(out)), rel_state(host64(hT2), host64(hT))
+    o_ref, h_ref = oracle_prefill(inp)           # the oracle on the unscaled inputs
+    eo_ref, es_ref = rel_out(host64(out2), o_ref), rel_state(host64(hT2), h_ref)
+    say(f"norm invariance {io}: vs unscaled run out {eo:.2e} state {es:.2e}; "
+        f"vs oracle out {eo_ref:.2e} state {es_ref:.2e}")
+    # |x|^2 >= 2^-8 after scaling: eps = 1e-6 moves the norm by < 2e-4 relative
+    assert eo <= 1e-3 and es <= 1e-3
+    tol = TOL_BF16 if io == torch.bfloat16 else TOL_F32
+    assert eo_ref <= tol and es_ref <= tol
+    # the decode step too
+    x = synth.decode_step_inputs(B, H, io, seed=47, device=DEV)
+    c = torch.pow(2.0, torch.randint(-4, 5, (B, H, 1), generator=gen, device=DEV).float())
+    S1, S2 = inp["h0"].clone(), inp["h0"].clone()
+    d1 = libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S1)
+    d2 = libkda.recurrent_step((x["q"].float() * c).to(io), (x["k"].float() / c).to(io), x["v"],
+                               x["g"], x["beta"], x["scale"], S2)
+    torch.cuda.synchronize()
+    ed = rel_out(host64(d2)[:, None], host64(d1)[:, None])
+    eds = rel_state(host64(S2), host64(S1))
+    say(f"norm invariance decode {io}: out {ed:.2e} state {eds:.2e}")
+    assert ed <= 1e-3 and eds <= 1e-3
+
+
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_no_decay_no_write_reads_the_initial_state(io):
+    """g = 0 and beta = 0: nothing decays and nothing is written, so the state
+    stays h0 and every output is the plain product scale * h0^T qh_t, checked
+    against a numpy matrix product of the same bytes (no oracle involved)."""
+    B, T, H = 2, 200, 3
+    inp = synth.prefill_inputs(B, T, H, io, seed=48, h0_std=0.1, device=DEV)
+    inp["g"] = torch.zeros_like(inp["g"])
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    out, hT = chunk(inp)
+    q = host64(inp["q"])
+    qh = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + 1e-6)
+    h0 = host64(inp["h0"])
+    want = inp["scale"] * np.einsum("bthi,bhij->bthj", qh, h0)
+    eo = rel_out(host64(out), want)
+    es = rel_state(host64(hT), h0)
+    say(f"g = 0, beta = 0 {io}: out {eo:.2e} state {es:.2e}")
+    assert eo <= (TOL_BF16 if io == torch.bfloat16 else TOL_F32)
+    assert es <= 1e-6
+    # the decode step: the state is left exactly as it was
+    x = synth.decode_step_inputs(B, H, io, seed=49, device=DEV)
+    S = inp["h0"].clone()
+    o1 = libkda.recurrent_step(x["q"], x["k"], x["v"], torch.zeros_like(x["g"]),
+                               torch.zeros_like(x["beta"]), x["scale"], S)
+    torch.cuda.synchronize()
+    q1 = host64(x["q"])
+    q1h = q1 / np.sqrt(np.sum(q1 * q1, axis=-1, keepdims=True) + 1e-6)
+    want1 = x["scale"] * np.einsum("bhi,bhij->bhj", q1h, h0)
+    ed = rel_out(host64(o1)[:, None], want1[:, None])
+    say(f"g = 0, beta = 0 decode {io}: out {ed:.2e}")
+    assert ed <= (TOL_BF16 if io == torch.bfloat16 else TOL_F32)
+    assert torch.equal(S, inp["h0"])

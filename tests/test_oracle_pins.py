@@ -530,3 +530,75 @@ def test_chunk_backward_equals_chained_steps(chunk):
     want = _chained_step_backward(q, k, v, g, beta, scale, h0, d_o, d_hT)
     for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, want):
         np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+# ---------------------------------------------------------------------------
+# backward of the whole recurrence, token by token (the reference of every GPU
+# backward comparison)
+# ---------------------------------------------------------------------------
+def test_sequence_backward_against_finite_differences():
+    """Every gradient of the T-token forward (q, k, v, g, beta, the initial
+    state) against central differences of ``forward`` itself, in fp64, with a
+    final-state gradient and decays down to the -5 bound: a dropped term, a
+    wrong sign, a token off by one or a transposed operand in the C reverse
+    pass fails here.  Two sequences (B = 1, H = 2) so the sequence indexing of
+    the layout is exercised too."""
+    rng = np.random.default_rng(41)
+    B, T, H, D, scale = 1, 9, 2, 5, 0.85
+    x = {"q": rng.standard_normal((B, T, H, D)), "k": rng.standard_normal((B, T, H, D)),
+         "v": rng.standard_normal((B, T, H, D)),
+         "g": -5.0 / (1.0 + np.exp(-2.0 * rng.standard_normal((B, T, H, D)))),
+         "beta": 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H)))),
+         "h0": rng.standard_normal((B, H, D, D))}
+    d_o = rng.standard_normal((B, T, H, D))
+    d_hT = rng.standard_normal((B, H, D, D))
+
+    def loss(y):
+        o, hT = oracle.forward(y["q"], y["k"], y["v"], y["g"], y["beta"], scale, y["h0"],
+                               threads=1)
+        return float(np.sum(d_o * o) + np.sum(d_hT * hT))
+
+    grads = oracle.sequence_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], scale,
+                                     x["h0"], d_o, d_hT, threads=2)
+    h = 1e-6
+    for name, gr in zip(("q", "k", "v", "g", "beta", "h0"), grads):
+        assert gr.shape == x[name].shape, name
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(*x[name].shape):
+            xp = {k_: v_.copy() for k_, v_ in x.items()}
+            xm = {k_: v_.copy() for k_, v_ in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            num[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        np.testing.assert_allclose(gr, num, rtol=2e-6, atol=2e-7, err_msg=name)
+
+
+def test_sequence_backward_equals_chained_step_backward():
+    """The C sequence backward is the chain of the (separately pinned) Python
+    step backward over the kept states, to rounding, with B = 2 and zero or
+    absent initial state and final gradient."""
+    rng = np.random.default_rng(42)
+    B, T, H, D, scale = 2, 23, 3, 7, 0.6
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    g = -5.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, D))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    d_o = rng.standard_normal((B, T, H, D))
+    for h0, d_hT in ((0.3 * rng.standard_normal((B, H, D, D)), rng.standard_normal((B, H, D, D))),
+                     (None, None)):
+        got = oracle.sequence_backward(q, k, v, g, beta, scale, h0, d_o, d_hT, threads=3)
+        z = np.zeros((B, H, D, D))
+        want = _chained_step_backward(q, k, v, g, beta, scale, z if h0 is None else h0, d_o,
+                                      z if d_hT is None else d_hT)
+        for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, want):
+            np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12, err_msg=name)
+
+
+def test_sequence_backward_empty_sequence():
+    """No tokens: the final-state gradient passes through to the initial one."""
+    rng = np.random.default_rng(43)
+    B, H, D = 2, 2, 4
+    e = np.zeros((B, 0, H, D))
+    d_hT = rng.standard_normal((B, H, D, D))
+    r = oracle.sequence_backward(e, e, e, e, np.zeros((B, 0, H)), 1.0, None, e, d_hT)
+    np.testing.assert_array_equal(r[5], d_hT)
+    assert r[0].shape == (B, 0, H, D) and r[4].shape == (B, 0, H)
