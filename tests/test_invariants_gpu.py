@@ -244,9 +244,12 @@ def test_norm_invariance(io):
     eo_ref, es_ref = rel_out(host64(out2), o_ref), rel_state(host64(hT2), h_ref)
     say(f"norm invariance {io}: vs unscaled run out {eo:.2e} state {es:.2e}; "
         f"vs oracle out {eo_ref:.2e} state {es_ref:.2e}")
-    # |x|^2 >= 2^-8 after scaling: eps = 1e-6 moves the norm by < 2e-4 relative
-    assert eo <= 1e-3 and es <= 1e-3
+    # |x|^2 >= 2^-8 after scaling: eps = 1e-6 moves the norm by < 2e-4 relative.
+    # In bf16 the two runs round the normalised operands (last bits of an
+    # approximate reciprocal square root) independently, so they differ by the
+    # kernels' own rounding error, which the bf16 bar bounds.
     tol = TOL_BF16 if io == torch.bfloat16 else TOL_F32
+    assert eo <= tol and es <= tol
     assert eo_ref <= tol and es_ref <= tol
     # the decode step too
     x = synth.decode_step_inputs(B, H, io, seed=47, device=DEV)
@@ -259,7 +262,7 @@ def test_norm_invariance(io):
     ed = rel_out(host64(d2)[:, None], host64(d1)[:, None])
     eds = rel_state(host64(S2), host64(S1))
     say(f"norm invariance decode {io}: out {ed:.2e} state {eds:.2e}")
-    assert ed <= 1e-3 and eds <= 1e-3
+    assert ed <= tol and eds <= tol
 
 
 @pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
