@@ -107,6 +107,28 @@ KDA_API kda_status_t kda_chunk_fwd(const uint16_t *q, const uint16_t *k, const u
                            int B, int T, int H, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_noalloc — kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture that must not add allocation
+ * nodes, tight serving loops, harnesses that forbid hipMalloc).  Arguments,
+ * layouts, validation and results are those of kda_chunk_fwd, and the results
+ * are bitwise the same.  Nothing is allocated: the per-chunk records and the
+ * state carried between segments live in a fixed 64 MiB device array of the
+ * library, one per GPU, held from its first use until the process ends; T is
+ * split into as many segments as that array needs (about 9 chunks of 64
+ * tokens per segment at B * H = 96), so long sequences take more launches.
+ * Returns KDA_ERR_UNSUPPORTED, before any HIP call, when B * H is too large
+ * for one chunk and the carried state to fit (B * H > 500 or so).  Calls on
+ * one GPU share that GPU's array, so calls that overlap in time on one GPU
+ * (on different streams, or from several host threads) race and give wrong
+ * results; calls on one stream are ordered and safe.  Not with
+ * KDA_DEBUG_CHECKS under graph capture (the mode synchronises).
+ */
+KDA_API kda_status_t kda_chunk_fwd_noalloc(const uint16_t *q, const uint16_t *k,
+                                   const uint16_t *v, const float *g, const float *beta,
+                                   float scale, const float *h0, uint16_t *out, float *hT,
+                                   int B, int T, int H, hipStream_t stream);
+
+/*
  * kda_chunk_fwd_g16 — as kda_chunk_fwd, with the log-decay in bf16:
  *
  *   g       : [B, T, H, 128] bf16 log-decay per key channel, in [-5, 0].

@@ -81,14 +81,49 @@ hipError_t pool_for_device(hipMemPool_t* pool) {
     return hipSuccess;
 }
 
+// The workspace of kda_chunk_fwd_noalloc: a device array of fixed size per GPU
+// instead of the pool.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+// The scratch of kda_chunk_fwd_noalloc: 64 MiB per GPU, part of the library's
+// code object, so each device that runs the library holds its own copy from
+// the first use until the process ends.  Host code never uses its name as an
+// address: the device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) uint8_t kda_noalloc_scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// the current device's copy of the scratch (device address)
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(kda_noalloc_scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
 // F32: fp32 q / k / v / out (else bf16); G16: bf16 g (else fp32; bf16 I/O only).
 // conv.wq != NULL: q, k, v are raw values before the short convolution (bf16
 // I/O only); conv_out (or NULL) receives the conv state after the sequence.
+// no_alloc: the records and the carried state live in the fixed per-GPU
+// scratch array (segments as long as it allows) and nothing is allocated.
 template <bool F32, bool G16 = false>
 kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                        const float* beta, float scale, const float* h0, void* out, float* hT,
                        int B, int T, int H, hipStream_t stream, kda::ConvArgs conv = {},
-                       void* conv_out = nullptr) {
+                       void* conv_out = nullptr, bool no_alloc = false) {
     static_assert(!(F32 && G16), "bf16 g is offered with bf16 q / k / v only");
     const bool cv = conv.wq != nullptr;
     constexpr size_t es = F32 ? 4 : 2;
@@ -160,8 +195,19 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     const int nch = (T + 63) / 64;
     const size_t rec = v16 ? kda::chunk16_record_bytes() : kda::chunk_f32_record_bytes();
     const size_t per_chunk = (size_t)B * H * rec;
-    int seg = (int)(workspace_budget() / per_chunk);
-    if (seg < 1) seg = 1;
+    int seg;
+    if (!no_alloc) {
+        seg = (int)(workspace_budget() / per_chunk);
+        if (seg < 1) seg = 1;
+    } else if (per_chunk * (size_t)nch <= kNoAllocScratchBytes) {
+        seg = nch;  // one segment, no carried state
+    } else {
+        // records of seg chunks, then the state carried between segments
+        seg = kNoAllocScratchBytes < state_bytes
+                  ? 0
+                  : (int)((kNoAllocScratchBytes - state_bytes) / per_chunk);
+        if (seg < 1) return KDA_ERR_UNSUPPORTED;  // B * H too large for the scratch
+    }
     if (seg > nch) seg = nch;
     if ((int64_t)B * H * seg > kMaxBlocks) seg = (int)(kMaxBlocks / ((int64_t)B * H));
     if (seg < 1) return KDA_ERR_UNSUPPORTED;
@@ -201,16 +247,21 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     wait.abort_out = dbg.abort_word();
     wait.spin_limit = dbg.spin_limit();
 
-    hipMemPool_t pool = nullptr;
-    if (pool_for_device(&pool) != hipSuccess) return KDA_ERR_HIP;
     void* ws = nullptr;
-    if (hipMallocFromPoolAsync(&ws, per_chunk * seg, pool, stream) != hipSuccess)
-        return KDA_ERR_NO_MEMORY;
     float* carry = nullptr;
-    if (multi) {
-        if (hipMallocFromPoolAsync((void**)&carry, state_bytes, pool, stream) != hipSuccess) {
-            (void)hipFreeAsync(ws, stream);
+    if (no_alloc) {
+        if (noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+        if (multi) carry = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + per_chunk * seg);
+    } else {
+        hipMemPool_t pool = nullptr;
+        if (pool_for_device(&pool) != hipSuccess) return KDA_ERR_HIP;
+        if (hipMallocFromPoolAsync(&ws, per_chunk * seg, pool, stream) != hipSuccess)
             return KDA_ERR_NO_MEMORY;
+        if (multi) {
+            if (hipMallocFromPoolAsync((void**)&carry, state_bytes, pool, stream) != hipSuccess) {
+                (void)hipFreeAsync(ws, stream);
+                return KDA_ERR_NO_MEMORY;
+            }
         }
     }
 
@@ -247,8 +298,10 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
     if (st == KDA_OK && cv && conv_out &&
         kda::launch_conv_state_out(q, k, v, B, T, H, conv, conv_out, stream) != hipSuccess)
         st = KDA_ERR_HIP;
-    if (carry) (void)hipFreeAsync(carry, stream);
-    (void)hipFreeAsync(ws, stream);
+    if (!no_alloc) {
+        if (carry) (void)hipFreeAsync(carry, stream);
+        (void)hipFreeAsync(ws, stream);
+    }
     if (st == KDA_OK && dbg.on()) st = dbg.device_status();
     return st;
 }
@@ -563,6 +616,14 @@ kda_status_t kda_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const float* g, const float* beta, float scale, const float* h0,
                            uint16_t* out, float* hT, int B, int T, int H, hipStream_t stream) {
     return chunk_fwd<false>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const float* g, const float* beta, float scale,
+                                   const float* h0, uint16_t* out, float* hT, int B, int T, int H,
+                                   hipStream_t stream) {
+    return chunk_fwd<false>(q, k, v, g, beta, scale, h0, out, hT, B, T, H, stream, {}, nullptr,
+                            true);
 }
 
 kda_status_t kda_chunk_fwd_g16(const uint16_t* q, const uint16_t* k, const uint16_t* v,

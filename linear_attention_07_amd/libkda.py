@@ -32,6 +32,7 @@ EXPORTS = (
     "kda_chunk_fwd_conv",
     "kda_chunk_fwd_f32",
     "kda_chunk_fwd_g16",
+    "kda_chunk_fwd_noalloc",
     "kda_recurrent_step",
     "kda_recurrent_step_bwd",
     "kda_recurrent_step_bwd_f32",
@@ -65,7 +66,8 @@ def load() -> ctypes.CDLL:
     step_args = [vp, vp, vp, vp, vp, f, vp, vp, i, i, vp]
     conv_args = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, vp]
     for name, args in (("kda_chunk_fwd", chunk_args), ("kda_chunk_fwd_f32", chunk_args),
-                       ("kda_chunk_fwd_g16", chunk_args), ("kda_chunk_fwd_conv", conv_args),
+                       ("kda_chunk_fwd_g16", chunk_args), ("kda_chunk_fwd_noalloc", chunk_args),
+                       ("kda_chunk_fwd_conv", conv_args),
                        ("kda_recurrent_step", step_args), ("kda_recurrent_step_f32", step_args)):
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -159,6 +161,29 @@ def chunk_fwd(q, k, v, g, beta, scale, h0=None, out=None, hT=None, final_state=T
             _ptr(out), _ptr(hT), B, T, H, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
+    return out, hT
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, scale, h0, out, hT=None):
+    """kda_chunk_fwd_noalloc: the bf16 prefill with its workspace in the
+    library's fixed per-GPU scratch, for callers that cannot allocate.  Every
+    buffer is the caller's: q, k, v [B, T, H, 128] bf16, g [B, T, H, 128] fp32,
+    beta [B, T, H] fp32, h0 and hT [B, H, 128, 128] fp32 or None, out like v.
+    Returns (out, hT)."""
+    B, T, H, _ = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check(t, name, q.shape, torch.bfloat16, dev)
+    _check(g, "g", q.shape, torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    for name, t in (("h0", h0), ("hT", hT)):
+        if t is not None:
+            _check(t, name, (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
+    st = load().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      float(scale), _ptr(h0), _ptr(out), _ptr(hT), B, T, H,
+                                      _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
     return out, hT
 
 

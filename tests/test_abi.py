@@ -333,3 +333,18 @@ def test_chunk_bwd_rejects_a_buffer_passed_twice(lib, fn, pair):
         args["dhT"], args["dq"], args["dk"], args["dv"], args["dg"], args["dbeta"], args["dh0"],
         1, 4, 1, None)
     assert rc == libkda.KDA_ERR_INVALID_ARG, pair
+
+
+def test_noalloc_validation_and_size_limit(lib):
+    """kda_chunk_fwd_noalloc validates like kda_chunk_fwd, and refuses, before
+    any HIP call, a B * H whose chunk records and carried state do not fit its
+    64 MiB scratch (one chunk record and one state per head)."""
+    INV = libkda.KDA_ERR_INVALID_ARG
+    for bad in (dict(B=-1), dict(scale=math.nan), dict(q=NULL), dict(out=P[0]),
+                dict(g=ctypes.c_void_p(A * 20 + 8))):
+        assert chunk(lib, fn="kda_chunk_fwd_noalloc", **bad) == INV, bad
+    assert chunk(lib, fn="kda_chunk_fwd_noalloc", B=0) == libkda.KDA_OK
+    big = dict(fn="kda_chunk_fwd_noalloc", T=640, H=1024)
+    sp = [ctypes.c_void_p((i + 1) << 36) for i in range(6)]
+    assert chunk(lib, q=sp[0], k=sp[1], v=sp[2], g=sp[3], beta=sp[4], out=sp[5], **big) == \
+        libkda.KDA_ERR_UNSUPPORTED
