@@ -55,7 +55,8 @@ def test_noalloc_two_calls_match_the_allocating_entry_point():
 
 
 def test_noalloc_rejects_what_does_not_fit():
-    inp = synth.prefill_inputs(1, 64, 1100, torch.bfloat16, seed=84, device=DEV)
+    # 4200 heads: one chunk's records (16 KB per head) exceed the 64 MiB scratch
+    inp = synth.prefill_inputs(1, 64, 4200, torch.bfloat16, seed=84, device=DEV)
     out = torch.empty_like(inp["v"])
     with pytest.raises(libkda.KDAError) as e:
         libkda.chunk_fwd_noalloc(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
