@@ -9,7 +9,12 @@ the same prefill with g in bf16 (kda_chunk_fwd_g16) and with the short
 convolution in front and the output gate behind (kda_chunk_fwd_conv), the
 batched decode step (B=256, H=96, fp32 state streamed in place; also with the
 short convolution and the gate, kda_recurrent_step_conv) and reports its state bandwidth, and times the fp64
-CPU oracle on a bounded sample of the prefill workload as a baseline.
+CPU oracle on a bounded sample of the prefill workload as a baseline.  It also
+reports the other prefill workloads of the path: the latency in microseconds of
+the small fp32 case (B=1, H=2, T=256) through both paths (one chunked call, and
+256 decode steps), one 96-head layer at T=4096, and the million-token prefill
+(B=1, H=96, T=1,048,576, about 155 GB resident), each with its HBM fraction
+and the oracle timed on a labelled sample of it.
 
 Roofline (per call of the timed op, algorithmic bytes only):
   prefill: 1540 B per token-head (q, k, v, o in bf16 = 4 x 256 B; g 512 B;
@@ -75,6 +80,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--only", default="all",
+                    help="comma-separated workloads to run (prefill, prefill_g16, prefill_conv, "
+                         "decode, decode_conv, decode_bwd, prefill_bwd, small_f32, layer_4k, "
+                         "prefill_1m), for profiler passes; the default runs all; the headline "
+                         "prefill always runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, copy 1 GiB once (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -129,6 +139,28 @@ def time_op(torch, fn, steps, warmup):
     return ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2], per[0]
 
 
+def oracle_sample(inp, heads, n_tokens):
+    """Seconds of fp64 oracle time on the first n_tokens tokens of the given
+    heads (all host threads)."""
+    from oracle import oracle
+    sel = torch_index(heads)
+
+    def host(x):
+        return x[:, :n_tokens][:, :, sel].detach().to("cpu").double().numpy()
+
+    args = [host(inp[k]) for k in ("q", "k", "v", "g", "beta")]
+    s0 = inp.get("h0")
+    s0 = None if s0 is None else s0[:, sel].detach().to("cpu").double().numpy()
+    t0 = time.perf_counter()
+    oracle.forward(*args, inp["scale"], s0, threads=oracle.default_threads())
+    return time.perf_counter() - t0
+
+
+def torch_index(heads):
+    import torch
+    return torch.tensor(list(heads), dtype=torch.long)
+
+
 def cpu_baseline(inp, n_tokens):
     """fp64 oracle on the same prefill input (first n_tokens tokens, every
     head), in groups of heads so that host memory stays bounded; all host
@@ -175,11 +207,28 @@ def main():
     import torch
     from linear_attention_07_amd import libkda, synth
 
+    only = set(args.only.split(","))
+
+    def want(name):
+        return "all" in only or name in only
+
     libkda.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    res = {}
 
-    # ---- prefill ------------------------------------------------------------
+    def hbm(gbps, nbytes, **extra):
+        r = {"bound": "hbm"}
+        r.update(extra)
+        r.update({"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_call": nbytes})
+        return r
+
+    def times(ms, ms_med, ms_min, nd=4):
+        return {"ms_per_step": round(ms, nd), "ms_per_step_median": round(ms_med, nd),
+                "ms_per_step_min": round(ms_min, nd)}
+
+    # ---- prefill (the headline) -----------------------------------------------
     w = synth.WORKLOADS["prefill_64k"]
     inp = synth.workload_inputs(w, dev)
     out = torch.empty_like(inp["v"])
@@ -203,136 +252,289 @@ def main():
           f"(wall {t_wall:.2f} s)", file=sys.stderr, flush=True)
 
     # ---- prefill with g in bf16 ---------------------------------------------
-    g16 = inp["g"].to(torch.bfloat16)
+    if want("prefill_g16"):
+        g16 = inp["g"].to(torch.bfloat16)
 
-    def prefill_g16():
-        libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], g16, inp["beta"], inp["scale"],
-                         inp["h0"], out=out, hT=hT)
+        def prefill_g16():
+            libkda.chunk_fwd(inp["q"], inp["k"], inp["v"], g16, inp["beta"], inp["scale"],
+                             inp["h0"], out=out, hT=hT)
 
-    gms, gms_med, gms_min = time_op(torch, prefill_g16, args.steps, args.warmup)
-    g16_bytes = token_heads * PREFILL_G16_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * STATE_BYTES
-    g16_gbps = g16_bytes / (gms / 1e3) / 1e9
-    print(f"# prefill, bf16 g: {gms:.3f} ms/step, {tokens / (gms / 1e3) / 1e6:.2f} Mtok/s, "
-          f"{g16_gbps:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
-    del g16
+        t = time_op(torch, prefill_g16, args.steps, args.warmup)
+        nb = token_heads * PREFILL_G16_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * STATE_BYTES
+        gb = nb / (t[0] / 1e3) / 1e9
+        print(f"# prefill, bf16 g: {t[0]:.3f} ms/step, {tokens / (t[0] / 1e3) / 1e6:.2f} Mtok/s, "
+              f"{gb:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+        res["prefill_g16"] = {
+            "workload": "prefill_64k with g in bf16 (kda_chunk_fwd_g16): 1,284 B per token-head",
+            **times(*t), "Mtok_s": round(tokens / (t[0] / 1e3) / 1e6, 3), "roofline": hbm(gb, nb)}
+        del g16
 
     # ---- prefill with the short convolution ---------------------------------
-    cp = synth.conv_params(w.B, w.H, seed=w.seed, device=dev)
-    cout = torch.empty_like(cp["conv_state"])
+    if want("prefill_conv"):
+        cp = synth.conv_params(w.B, w.H, seed=w.seed, device=dev)
+        cout = torch.empty_like(cp["conv_state"])
+        zg = synth.gate_logits(inp["v"].shape, seed=w.seed, device=dev)
 
-    zg = synth.gate_logits(inp["v"].shape, seed=w.seed, device=dev)
+        def prefill_conv():
+            libkda.chunk_fwd_conv(inp["q"], inp["k"], inp["v"], cp["wq"], cp["wk"], cp["wv"],
+                                  inp["g"], inp["beta"], inp["scale"], inp["h0"],
+                                  conv_in=cp["conv_state"], conv_out=cout, out=out, hT=hT,
+                                  gate=zg)
 
-    def prefill_conv():
-        libkda.chunk_fwd_conv(inp["q"], inp["k"], inp["v"], cp["wq"], cp["wk"], cp["wv"],
-                              inp["g"], inp["beta"], inp["scale"], inp["h0"],
-                              conv_in=cp["conv_state"], conv_out=cout, out=out, hT=hT, gate=zg)
-
-    cms, cms_med, cms_min = time_op(torch, prefill_conv, args.steps, args.warmup)
-    conv_bytes = pre_bytes + token_heads * GATE_BYTES_PER_TOKEN_HEAD + \
-        w.B * w.H * 2 * CONV_STATE_BYTES + w.H * CONV_TAP_BYTES_PER_HEAD
-    conv_gbps = conv_bytes / (cms / 1e3) / 1e9
-    print(f"# prefill, short conv + gate: {cms:.3f} ms/step, {tokens / (cms / 1e3) / 1e6:.2f} Mtok/s, "
-          f"{conv_gbps:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
-    del cp, cout, zg
+        t = time_op(torch, prefill_conv, args.steps, args.warmup)
+        nb = pre_bytes + token_heads * GATE_BYTES_PER_TOKEN_HEAD + \
+            w.B * w.H * 2 * CONV_STATE_BYTES + w.H * CONV_TAP_BYTES_PER_HEAD
+        gb = nb / (t[0] / 1e3) / 1e9
+        print(f"# prefill, short conv + gate: {t[0]:.3f} ms/step, "
+              f"{tokens / (t[0] / 1e3) / 1e6:.2f} Mtok/s, {gb:.0f} GB/s algorithmic",
+              file=sys.stderr, flush=True)
+        res["prefill_conv"] = {
+            "workload": "prefill_64k as one KDA layer: the 4-tap short convolution + SiLU on "
+                        "q, k, v in front, the sigmoid output gate behind (kda_chunk_fwd_conv), "
+                        "conv state in and out",
+            **times(*t), "Mtok_s": round(tokens / (t[0] / 1e3) / 1e6, 3), "roofline": hbm(gb, nb)}
+        del cp, cout, zg
 
     # ---- decode -------------------------------------------------------------
     wd = synth.WORKLOADS["decode_b256"]
-    S = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
-    # the workload's 64 consecutive steps, each with its own inputs (drawn
-    # beforehand); warm-up steps reuse the first ones
-    dsteps = args.decode_steps or wd.T
-    xs = [synth.decode_step_inputs(wd.B, wd.H, wd.io, seed=wd.seed, step=t, device=dev)
-          for t in range(dsteps)]
-    dout = torch.empty_like(xs[0]["v"])
-    it = [0]
-
-    def decode():
-        x = xs[it[0] % dsteps]
-        it[0] += 1
-        libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S,
-                              out=dout)
-
-    dms, dms_med, dms_min = time_op(torch, decode, dsteps, args.warmup)
-    del xs
     nbh = wd.B * wd.H
-    state_gbps = nbh * 2 * STATE_BYTES / (dms / 1e3) / 1e9
-    dec_gbps = nbh * DECODE_BYTES_PER_SEQ_HEAD / (dms / 1e3) / 1e9
-    print(f"# decode: {dms:.3f} ms/step, state {state_gbps:.0f} GB/s, "
-          f"total {dec_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+    dsteps = args.decode_steps or wd.T
+    S = None
+    if want("decode") or want("decode_conv"):
+        S = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
+    it = [0]
+    if want("decode"):
+        # the workload's 64 consecutive steps, each with its own inputs (drawn
+        # beforehand); warm-up steps reuse the first ones
+        xs = [synth.decode_step_inputs(wd.B, wd.H, wd.io, seed=wd.seed, step=t, device=dev)
+              for t in range(dsteps)]
+        dout = torch.empty_like(xs[0]["v"])
+
+        def decode():
+            x = xs[it[0] % dsteps]
+            it[0] += 1
+            libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], S,
+                                  out=dout)
+
+        t = time_op(torch, decode, dsteps, args.warmup)
+        del xs
+        state_gbps = nbh * 2 * STATE_BYTES / (t[0] / 1e3) / 1e9
+        dec_gbps = nbh * DECODE_BYTES_PER_SEQ_HEAD / (t[0] / 1e3) / 1e9
+        print(f"# decode: {t[0]:.3f} ms/step, state {state_gbps:.0f} GB/s, "
+              f"total {dec_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        res["decode"] = {
+            "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v; 64 "
+                        "consecutive steps timed, fresh inputs each step",
+            **times(*t), "state_GBps": round(state_gbps, 1),
+            "roofline": hbm(dec_gbps, nbh * DECODE_BYTES_PER_SEQ_HEAD, kernel="kda_decode_kernel",
+                            traffic=measured_traffic("decode_b256"))}
 
     # ---- decode with the short convolution ----------------------------------
-    dcp = synth.conv_params(wd.B, wd.H, seed=wd.seed, device=dev)
-    xcs = [synth.decode_conv_inputs(wd.B, wd.H, seed=wd.seed, step=t, device=dev)
-           for t in range(4)]
-    zds = [synth.gate_logits((wd.B, wd.H, 128), seed=wd.seed + t, device=dev) for t in range(4)]
+    if want("decode_conv"):
+        dcp = synth.conv_params(wd.B, wd.H, seed=wd.seed, device=dev)
+        xcs = [synth.decode_conv_inputs(wd.B, wd.H, seed=wd.seed, step=t, device=dev)
+               for t in range(4)]
+        zds = [synth.gate_logits((wd.B, wd.H, 128), seed=wd.seed + t, device=dev)
+               for t in range(4)]
+        dout = torch.empty((wd.B, wd.H, 128), dtype=torch.bfloat16, device=dev)
 
-    def decode_conv():
-        x, z = xcs[it[0] & 3], zds[it[0] & 3]
-        it[0] += 1
-        libkda.recurrent_step_conv(x["q"], x["k"], x["v"], dcp["wq"], dcp["wk"], dcp["wv"],
-                                   dcp["conv_state"], x["g"], x["beta"], x["scale"], S,
-                                   out=dout, gate=z)
+        def decode_conv():
+            x, z = xcs[it[0] & 3], zds[it[0] & 3]
+            it[0] += 1
+            libkda.recurrent_step_conv(x["q"], x["k"], x["v"], dcp["wq"], dcp["wk"], dcp["wv"],
+                                       dcp["conv_state"], x["g"], x["beta"], x["scale"], S,
+                                       out=dout, gate=z)
 
-    cdms, cdms_med, cdms_min = time_op(torch, decode_conv, dsteps, args.warmup)
-    dconv_bytes = nbh * (DECODE_BYTES_PER_SEQ_HEAD + 2 * CONV_STATE_BYTES +
-                         GATE_BYTES_PER_TOKEN_HEAD) + wd.H * CONV_TAP_BYTES_PER_HEAD
-    dconv_gbps = dconv_bytes / (cdms / 1e3) / 1e9
-    print(f"# decode, short conv + gate: {cdms:.3f} ms/step, total {dconv_gbps:.0f} GB/s",
-          file=sys.stderr, flush=True)
-    del dcp, xcs, zds
+        t = time_op(torch, decode_conv, dsteps, args.warmup)
+        nb = nbh * (DECODE_BYTES_PER_SEQ_HEAD + 2 * CONV_STATE_BYTES +
+                    GATE_BYTES_PER_TOKEN_HEAD) + wd.H * CONV_TAP_BYTES_PER_HEAD
+        gb = nb / (t[0] / 1e3) / 1e9
+        print(f"# decode, short conv + gate: {t[0]:.3f} ms/step, total {gb:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        res["decode_conv"] = {
+            "workload": "decode_b256 as one KDA layer: short convolution in front, output "
+                        "gate behind (kda_recurrent_step_conv), conv state advanced in place",
+            **times(*t), "roofline": hbm(gb, nb)}
+        del dcp, xcs, zds
+    del S
 
     # ---- backward of one decode step (fp32) ---------------------------------
-    del S
-    xb = synth.decode_step_inputs(wd.B, wd.H, torch.float32, seed=wd.seed, step=0, device=dev)
-    Sp = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
-    dSb = synth.decode_state(wd.B, wd.H, seed=wd.seed + 1, h0_std=wd.h0_std, device=dev)
-    dob = torch.randn((wd.B, wd.H, 128), device=dev)
+    if want("decode_bwd"):
+        xb = synth.decode_step_inputs(wd.B, wd.H, torch.float32, seed=wd.seed, step=0,
+                                      device=dev)
+        Sp = synth.decode_state(wd.B, wd.H, seed=wd.seed, h0_std=wd.h0_std, device=dev)
+        dSb = synth.decode_state(wd.B, wd.H, seed=wd.seed + 1, h0_std=wd.h0_std, device=dev)
+        dob = torch.randn((wd.B, wd.H, 128), device=dev)
 
-    def decode_bwd():
-        libkda.recurrent_step_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
-                                  Sp, dob, dSb)
+        def decode_bwd():
+            libkda.recurrent_step_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"],
+                                      xb["scale"], Sp, dob, dSb)
 
-    bms, bms_med, bms_min = time_op(torch, decode_bwd, dsteps, args.warmup)
-    bwd_bytes = nbh * BWD_STEP_BYTES_PER_SEQ_HEAD
-    bwd_gbps = bwd_bytes / (bms / 1e3) / 1e9
-    print(f"# decode backward step: {bms:.3f} ms/step, total {bwd_gbps:.0f} GB/s",
-          file=sys.stderr, flush=True)
-    del xb, Sp, dSb, dob
+        t = time_op(torch, decode_bwd, dsteps, args.warmup)
+        nb = nbh * BWD_STEP_BYTES_PER_SEQ_HEAD
+        gb = nb / (t[0] / 1e3) / 1e9
+        print(f"# decode backward step: {t[0]:.3f} ms/step, total {gb:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        res["decode_bwd"] = {
+            "workload": "backward of one decode step at B=256 H=96, all fp32 "
+                        "(kda_recurrent_step_bwd_f32): state and state gradient read, "
+                        "state gradient written in place",
+            **times(*t), "roofline": hbm(gb, nb)}
+        del xb, Sp, dSb, dob
 
-    # ---- backward of the fp32 chunked prefill --------------------------------
-    wb = synth.WORKLOADS["prefill_bwd_8k"]
-    xb = synth.prefill_inputs(wb.B, wb.T, wb.H, torch.float32, seed=wb.seed, g_shift=wb.g_shift,
-                              h0_std=wb.h0_std, device=dev)
-    gb = torch.Generator(device=dev).manual_seed(wb.seed + 1)
-    xb["dout"] = torch.randn((wb.B, wb.T, wb.H, 128), generator=gb, device=dev)
-    xb["dhT"] = 0.1 * torch.randn((wb.B, wb.H, 128, 128), generator=gb, device=dev)
+    # ---- backward of the chunked prefill (fp32, then bf16 I/O) ------------------
+    if want("prefill_bwd"):
+        wb = synth.WORKLOADS["prefill_bwd_8k"]
+        xb = synth.prefill_inputs(wb.B, wb.T, wb.H, torch.float32, seed=wb.seed,
+                                  g_shift=wb.g_shift, h0_std=wb.h0_std, device=dev)
+        gbn = torch.Generator(device=dev).manual_seed(wb.seed + 1)
+        xb["dout"] = torch.randn((wb.B, wb.T, wb.H, 128), generator=gbn, device=dev)
+        xb["dhT"] = 0.1 * torch.randn((wb.B, wb.H, 128, 128), generator=gbn, device=dev)
 
-    def prefill_bwd():
-        libkda.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
-                         xb["dout"], h0=xb["h0"], dhT=xb["dhT"])
+        def prefill_bwd():
+            libkda.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
+                             xb["dout"], h0=xb["h0"], dhT=xb["dhT"])
 
-    pbms, pbms_med, pbms_min = time_op(torch, prefill_bwd, max(3, args.steps // 4), args.warmup)
-    pb_chunks = wb.B * wb.H * ((wb.T + 63) // 64)
-    pb_flop = pb_chunks * BWD_CHUNK_FLOP_PER_CHUNK_HEAD
-    pb_tflops = pb_flop / (pbms / 1e3) / 1e12
-    pb_bytes = wb.B * wb.T * wb.H * BWD_CHUNK_BYTES_PER_TOKEN_HEAD + 3 * wb.B * wb.H * STATE_BYTES
-    print(f"# prefill backward (fp32): {pbms:.3f} ms/call, {pb_tflops:.1f} TFLOP/s",
-          file=sys.stderr, flush=True)
-    for key in ("q", "k", "v", "dout"):
-        xb[key] = xb[key].to(torch.bfloat16)
+        nsteps = max(3, args.steps // 4)
+        t = time_op(torch, prefill_bwd, nsteps, args.warmup)
+        pb_chunks = wb.B * wb.H * ((wb.T + 63) // 64)
+        pb_flop = pb_chunks * BWD_CHUNK_FLOP_PER_CHUNK_HEAD
+        tf = pb_flop / (t[0] / 1e3) / 1e12
+        nb = wb.B * wb.T * wb.H * BWD_CHUNK_BYTES_PER_TOKEN_HEAD + 3 * wb.B * wb.H * STATE_BYTES
+        print(f"# prefill backward (fp32): {t[0]:.3f} ms/call, {tf:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        res["prefill_bwd"] = {
+            "workload": f"prefill_bwd_8k: backward of one fp32 KDA layer prefill, B={wb.B} "
+                        f"H={wb.H} T={wb.T} d=128, h0 and dhT ~ N(0, 0.1^2), dout ~ N(0, 1) "
+                        "(kda_chunk_bwd_f32: gradients of q, k, v, g, beta and h0)",
+            **times(*t), "Mtok_s": round(wb.B * wb.T / (t[0] / 1e3) / 1e6, 3),
+            "roofline": {
+                "bound": "alu",
+                "kernel": "kda_chunk_bwd_f32 (prep, two state scans, chunk gradients; one call)",
+                "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "algorithmic_flop_per_call": pb_flop,
+                "traffic": measured_traffic("prefill_bwd_8k"), "algorithmic_bytes_per_call": nb,
+                "hbm_GBps_algorithmic": round(nb / (t[0] / 1e3) / 1e9, 1)}}
+        for key in ("q", "k", "v", "dout"):
+            xb[key] = xb[key].to(torch.bfloat16)
+        t = time_op(torch, prefill_bwd, nsteps, args.warmup)
+        tf = pb_flop / (t[0] / 1e3) / 1e12
+        nb = wb.B * wb.T * wb.H * BWD_CHUNK_BF16_BYTES_PER_TOKEN_HEAD + \
+            3 * wb.B * wb.H * STATE_BYTES
+        print(f"# prefill backward (bf16 I/O): {t[0]:.3f} ms/call, {tf:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        res["prefill_bwd_bf16"] = {
+            "workload": "prefill_bwd_8k with bf16 q, k, v, dout in and bf16 dq, dk, dv out "
+                        "(kda_chunk_bwd), fp32 arithmetic",
+            **times(*t), "Mtok_s": round(wb.B * wb.T / (t[0] / 1e3) / 1e6, 3),
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+                         "algorithmic_flop_per_call": pb_flop, "algorithmic_bytes_per_call": nb}}
+        del xb
 
-    def prefill_bwd16():
-        libkda.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["scale"],
-                         xb["dout"], h0=xb["h0"], dhT=xb["dhT"])
+    # ---- the small fp32 case through both paths (latency) ---------------------
+    if want("small_f32"):
+        ws_ = synth.WORKLOADS["small_f32"]
+        xs_ = synth.workload_inputs(ws_, dev)
+        o_s = torch.empty_like(xs_["v"])
+        h_s = torch.empty((ws_.B, ws_.H, 128, 128), device=dev)
 
-    p16ms, p16ms_med, p16ms_min = time_op(torch, prefill_bwd16, max(3, args.steps // 4),
-                                          args.warmup)
-    p16_tflops = pb_flop / (p16ms / 1e3) / 1e12
-    p16_bytes = (wb.B * wb.T * wb.H * BWD_CHUNK_BF16_BYTES_PER_TOKEN_HEAD +
-                 3 * wb.B * wb.H * STATE_BYTES)
-    print(f"# prefill backward (bf16 I/O): {p16ms:.3f} ms/call, {p16_tflops:.1f} TFLOP/s",
-          file=sys.stderr, flush=True)
-    del xb
+        def small_chunk():
+            libkda.chunk_fwd(xs_["q"], xs_["k"], xs_["v"], xs_["g"], xs_["beta"], xs_["scale"],
+                             None, out=o_s, hT=h_s)
+
+        tc = time_op(torch, small_chunk, 50, args.warmup)
+        steps_s = [{kk: xs_[kk][:, t].contiguous() for kk in ("q", "k", "v", "g", "beta")}
+                   for t in range(ws_.T)]
+        S_s = torch.zeros((ws_.B, ws_.H, 128, 128), device=dev)
+        o_r = torch.empty((ws_.B, ws_.H, 128), device=dev)
+
+        def small_recurrent():  # the whole sequence: 256 decode steps
+            S_s.zero_()
+            for x in steps_s:
+                libkda.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], xs_["scale"],
+                                      S_s, out=o_r)
+
+        tr = time_op(torch, small_recurrent, 5, 1)
+        t_or = None if args.no_cpu_baseline else oracle_sample(xs_, range(ws_.H), ws_.T)
+        print(f"# small fp32 (B=1 H=2 T=256): chunked {tc[0] * 1e3:.1f} us/call, recurrent "
+              f"{tr[0] * 1e3:.1f} us for 256 steps ({tr[0] * 1e3 / ws_.T:.2f} us/step)",
+              file=sys.stderr, flush=True)
+        res["small_f32"] = {
+            "workload": "small_f32: B=1 H=2 T=256 d=128, fp32 q/k/v/o, zero initial state, "
+                        "seed 0",
+            "chunked_us_per_call": round(tc[0] * 1e3, 2),
+            "chunked_us_median": round(tc[1] * 1e3, 2),
+            "chunked_us_min": round(tc[2] * 1e3, 2),
+            "recurrent_us_for_256_steps": round(tr[0] * 1e3, 2),
+            "recurrent_us_per_step": round(tr[0] * 1e3 / ws_.T, 3),
+            "note": "latency-bound (1.44 MB of algorithmic bytes, 0.18 us at 8 TB/s); the "
+                    "chunked path is one kda_chunk_fwd_f32, the recurrent path 256 "
+                    "kda_recurrent_step_f32 calls launched from Python",
+            "cpu_baseline": None if t_or is None else {
+                "us": round(t_or * 1e6, 1), "kind": "oracle", "sample": "the whole workload"}}
+        del xs_, o_s, h_s, steps_s, S_s, o_r
+
+    # ---- one 96-head layer at T = 4096 ------------------------------------------
+    if want("layer_4k"):
+        wl = synth.WORKLOADS["layer_4k"]
+        xl = synth.workload_inputs(wl, dev)
+        o_l = torch.empty_like(xl["v"])
+        h_l = torch.empty((wl.B, wl.H, 128, 128), device=dev)
+
+        def layer():
+            libkda.chunk_fwd(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"], xl["scale"], None,
+                             out=o_l, hT=h_l)
+
+        t = time_op(torch, layer, args.steps, args.warmup)
+        nb = wl.B * wl.T * wl.H * PREFILL_BYTES_PER_TOKEN_HEAD + wl.B * wl.H * STATE_BYTES
+        gb = nb / (t[0] / 1e3) / 1e9
+        t_ol = None if args.no_cpu_baseline else oracle_sample(xl, range(wl.H), wl.T)
+        print(f"# layer_4k: {t[0]:.3f} ms/call, {wl.B * wl.T / (t[0] / 1e3) / 1e6:.2f} Mtok/s, "
+              f"{gb:.0f} GB/s", file=sys.stderr, flush=True)
+        res["layer_4k"] = {
+            "workload": "layer_4k: B=1 H=96 T=4096 d=128, bf16 q/k/v, fp32 g/beta, zero "
+                        "initial state (no h0 read), seed 1",
+            **times(*t), "Mtok_s": round(wl.B * wl.T / (t[0] / 1e3) / 1e6, 3),
+            "roofline": hbm(gb, nb),
+            "cpu_baseline": None if t_ol is None else {
+                "value": round(wl.B * wl.T / t_ol / 1e6, 5), "unit": "Mtok/s", "kind": "oracle",
+                "sample": f"the whole workload, {t_ol:.2f} s of oracle time"}}
+        del xl, o_l, h_l
+
+    # ---- the million-token prefill ----------------------------------------------
+    if want("prefill_1m"):
+        torch.cuda.empty_cache()
+        wm = synth.WORKLOADS["prefill_1m"]
+        xm = synth.workload_inputs(wm, dev)
+        o_m = torch.empty_like(xm["v"])
+        h_m = torch.empty((wm.B, wm.H, 128, 128), device=dev)
+
+        def prefill_1m():
+            libkda.chunk_fwd(xm["q"], xm["k"], xm["v"], xm["g"], xm["beta"], xm["scale"], None,
+                             out=o_m, hT=h_m)
+
+        t = time_op(torch, prefill_1m, max(2, args.steps // 5), 1)
+        nb = wm.B * wm.T * wm.H * PREFILL_BYTES_PER_TOKEN_HEAD + wm.B * wm.H * STATE_BYTES
+        gb = nb / (t[0] / 1e3) / 1e9
+        m_heads, m_tokens = range(0, wm.H, wm.H // 16), 32768
+        t_om = None if args.no_cpu_baseline else oracle_sample(xm, m_heads, m_tokens)
+        print(f"# prefill_1m: {t[0]:.2f} ms/call, {wm.B * wm.T / (t[0] / 1e3) / 1e6:.2f} Mtok/s, "
+              f"{gb:.0f} GB/s", file=sys.stderr, flush=True)
+        res["prefill_1m"] = {
+            "workload": "prefill_1m: B=1 H=96 T=1048576 d=128, bf16 q/k/v, fp32 g = -5 "
+                        "sigmoid(x - 6) and beta, zero initial state (no h0 read), seed 4 "
+                        "(155 GB resident)",
+            **times(*t, nd=3), "Mtok_s": round(wm.B * wm.T / (t[0] / 1e3) / 1e6, 3),
+            "roofline": hbm(gb, nb),
+            "cpu_baseline": None if t_om is None else {
+                "value": round(len(m_heads) * m_tokens / wm.H / t_om / 1e6, 6),
+                "unit": "Mtok/s", "kind": "oracle",
+                "sample": f"heads {list(m_heads)} x the first {m_tokens} tokens ({t_om:.2f} s "
+                          "of oracle time), scaled to all 96 heads: Mtok/s = sampled "
+                          "token-heads / 96 / seconds"}}
+        del xm, o_m, h_m
+        torch.cuda.empty_cache()
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -368,16 +570,9 @@ def main():
             "B": w.B, "H": w.H, "T": w.T, "head_dim": 128, "chunk": 64,
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "kda_chunk_fwd (kda_prep16_kernel + kda_scan16_kernel, one call)",
-            "achieved": round(pre_gbps, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic("prefill_64k"),
-            "algorithmic_bytes_per_call": pre_bytes,
-        },
+        "roofline": hbm(pre_gbps, pre_bytes,
+                        kernel="kda_chunk_fwd (kda_prep16_kernel + kda_scan16_kernel, one call)",
+                        traffic=measured_traffic("prefill_64k")),
         "mfma": {
             "algorithmic_flop_per_call": token_heads * PREFILL_FLOP_PER_TOKEN_HEAD,
             "achieved_TFLOPs": round(pre_tflops, 1),
@@ -385,127 +580,11 @@ def main():
             "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "note": "algorithmic flops at a fixed 64-token chunk; the binding roofline is HBM",
         },
-        "prefill_g16": {
-            "workload": "prefill_64k with g in bf16 (kda_chunk_fwd_g16): 1,284 B per token-head",
-            "ms_per_step": round(gms, 4),
-            "ms_per_step_median": round(gms_med, 4),
-            "ms_per_step_min": round(gms_min, 4),
-            "Mtok_s": round(tokens / (gms / 1e3) / 1e6, 3),
-            "roofline": {
-                "bound": "hbm",
-                "achieved": round(g16_gbps, 1),
-                "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s",
-                "frac": round(g16_gbps / HBM_PEAK_GBPS, 4),
-                "algorithmic_bytes_per_call": g16_bytes,
-            },
-        },
-        "prefill_conv": {
-            "workload": "prefill_64k as one KDA layer: the 4-tap short convolution + SiLU on "
-                        "q, k, v in front, the sigmoid output gate behind (kda_chunk_fwd_conv), "
-                        "conv state in and out",
-            "ms_per_step": round(cms, 4),
-            "ms_per_step_median": round(cms_med, 4),
-            "ms_per_step_min": round(cms_min, 4),
-            "Mtok_s": round(tokens / (cms / 1e3) / 1e6, 3),
-            "roofline": {
-                "bound": "hbm",
-                "achieved": round(conv_gbps, 1),
-                "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s",
-                "frac": round(conv_gbps / HBM_PEAK_GBPS, 4),
-                "algorithmic_bytes_per_call": conv_bytes,
-            },
-        },
-        "decode_conv": {
-            "workload": "decode_b256 as one KDA layer: short convolution in front, output "
-                        "gate behind (kda_recurrent_step_conv), conv state advanced in place",
-            "ms_per_step": round(cdms, 4),
-            "ms_per_step_median": round(cdms_med, 4),
-            "ms_per_step_min": round(cdms_min, 4),
-            "roofline": {
-                "bound": "hbm",
-                "achieved": round(dconv_gbps, 1),
-                "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s",
-                "frac": round(dconv_gbps / HBM_PEAK_GBPS, 4),
-                "algorithmic_bytes_per_call": dconv_bytes,
-            },
-        },
-        "decode_bwd": {
-            "workload": "backward of one decode step at B=256 H=96, all fp32 "
-                        "(kda_recurrent_step_bwd_f32): state and state gradient read, "
-                        "state gradient written in place",
-            "ms_per_step": round(bms, 4),
-            "ms_per_step_median": round(bms_med, 4),
-            "ms_per_step_min": round(bms_min, 4),
-            "roofline": {
-                "bound": "hbm",
-                "achieved": round(bwd_gbps, 1),
-                "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s",
-                "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
-                "algorithmic_bytes_per_call": bwd_bytes,
-            },
-        },
-        "prefill_bwd": {
-            "workload": f"prefill_bwd_8k: backward of one fp32 KDA layer prefill, B={wb.B} "
-                        f"H={wb.H} T={wb.T} d=128, h0 and dhT ~ N(0, 0.1^2), dout ~ N(0, 1) "
-                        "(kda_chunk_bwd_f32: gradients of q, k, v, g, beta and h0)",
-            "ms_per_step": round(pbms, 4),
-            "ms_per_step_median": round(pbms_med, 4),
-            "ms_per_step_min": round(pbms_min, 4),
-            "Mtok_s": round(wb.B * wb.T / (pbms / 1e3) / 1e6, 3),
-            "roofline": {
-                "bound": "alu",
-                "kernel": "kda_chunk_bwd_f32 (prep, two state scans, chunk gradients; one call)",
-                "achieved": round(pb_tflops, 2),
-                "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s",
-                "frac": round(pb_tflops / FP32_VALU_PEAK_TFLOPS, 4),
-                "algorithmic_flop_per_call": pb_flop,
-                "traffic": measured_traffic("prefill_bwd_8k"),
-                "algorithmic_bytes_per_call": pb_bytes,
-                "hbm_GBps_algorithmic": round(pb_bytes / (pbms / 1e3) / 1e9, 1),
-            },
-        },
-        "prefill_bwd_bf16": {
-            "workload": "prefill_bwd_8k with bf16 q, k, v, dout in and bf16 dq, dk, dv out "
-                        "(kda_chunk_bwd), fp32 arithmetic",
-            "ms_per_step": round(p16ms, 4),
-            "ms_per_step_median": round(p16ms_med, 4),
-            "ms_per_step_min": round(p16ms_min, 4),
-            "Mtok_s": round(wb.B * wb.T / (p16ms / 1e3) / 1e6, 3),
-            "roofline": {
-                "bound": "alu",
-                "achieved": round(p16_tflops, 2),
-                "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s",
-                "frac": round(p16_tflops / FP32_VALU_PEAK_TFLOPS, 4),
-                "algorithmic_flop_per_call": pb_flop,
-                "algorithmic_bytes_per_call": p16_bytes,
-            },
-        },
-        "decode": {
-            "workload": "decode_b256: B=256 H=96, fp32 state in place, bf16 q/k/v; 64 "
-                        "consecutive steps timed, fresh inputs each step",
-            "ms_per_step": round(dms, 4),
-            "ms_per_step_median": round(dms_med, 4),
-            "ms_per_step_min": round(dms_min, 4),
-            "state_GBps": round(state_gbps, 1),
-            "roofline": {
-                "bound": "hbm",
-                "kernel": "kda_decode_kernel",
-                "achieved": round(dec_gbps, 1),
-                "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s",
-                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic("decode_b256"),
-                "algorithmic_bytes_per_call": nbh * DECODE_BYTES_PER_SEQ_HEAD,
-            },
-        },
-        "cpu_baseline": cpu,
     }
+    for key in ("prefill_g16", "prefill_conv", "decode_conv", "decode_bwd", "prefill_bwd",
+                "prefill_bwd_bf16", "decode", "small_f32", "layer_4k", "prefill_1m"):
+        line[key] = res.get(key)
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
