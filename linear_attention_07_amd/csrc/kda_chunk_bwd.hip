@@ -33,8 +33,8 @@
 //         of the first as the initial state's gradient;
 //   chunk gradients, one workgroup per (batch, head, chunk), rebuilds the
 //         chunk's matrices from q, k, g, beta and writes dq, dk, dv, dg, dbeta.
-// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) from
-// LDS and L1/L2-resident operands.
+// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
+// its operands in LDS or registers.
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -49,14 +49,6 @@ constexpr int kScanSlices = kD / kScanCols;
 constexpr int kScanThreads = 512;
 constexpr size_t kStateFloats = (size_t)kD * kD;
 
-// Scratch of one chunk-gradient workgroup in global memory (floats).
-constexpr size_t kScrR = 0;                       // [64][128] R = V - Kt S
-constexpr size_t kScrU = kScrR + kChunk * kD;     // [64][128] U = T R
-constexpr size_t kScrDU = kScrU + kChunk * kD;    // [64][128] dU
-constexpr size_t kScrDX = kScrDU + kChunk * kD;   // [64][64]  dX
-constexpr size_t kScrY = kScrDX + kChunk * kChunk;  // [64][64] X^T dX
-constexpr size_t kScrDR = kScrY + kChunk * kChunk;  // [64][128] dR (= dV in fp32)
-constexpr size_t kScrFloats = kScrDR + kChunk * kD;
 
 __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -157,25 +149,6 @@ __device__ __forceinline__ void scan_ids(int& bh, int& slice) {
     } else {
         bh = id / kScanSlices;
         slice = id % kScanSlices;
-    }
-}
-
-// Copy a rows x cols block (cols a multiple of 4, row pitch spitch floats,
-// 16-byte aligned rows) into LDS with row pitch dpitch; rows >= valid read as
-// zeros.  Every thread issues its float4 loads back to back.
-template <int NT>
-__device__ __forceinline__ void stage(const float* __restrict__ src, size_t spitch, int rows,
-                                      int cols, int valid, float* dst, int dpitch) {
-    const int q = cols / 4;
-    for (int e = threadIdx.x; e < rows * q; e += NT) {
-        const int r = e / q, c4 = 4 * (e % q);
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < valid) x = *reinterpret_cast<const float4*>(src + (size_t)r * spitch + c4);
-        float* d = dst + r * dpitch + c4;
-        d[0] = x.x;
-        d[1] = x.y;
-        d[2] = x.z;
-        d[3] = x.w;
     }
 }
 
@@ -440,77 +413,168 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Chunk gradients: one 512-thread workgroup per (b, h, chunk) (two waves per
-// SIMD).  The products run on the fp32 matrix cores (mmf); for the element-wise
-// part over [64][128] (token row x channel) thread t owns rows 4 (t / 32) + m
-// and channels t % 32 + 32 n, and keeps its share of dkh, dqh and dGam in
-// registers from the first contribution to the last.
+// Chunk gradients: one 512-thread workgroup per (b, h, chunk), two waves per
+// SIMD; every intermediate stays in registers or LDS.
+//
+// Lane (n, gq) of wave w owns channel cc = 16 w + n of the rows 16 u + 4 gq + e
+// (u, e < 4; slot m = 4 u + e): the accumulator layout of column tile w of a
+// 64 x 128 product in which wave w computes all four row tiles.  A 16-token
+// block kb of a contraction over tokens takes its B operand straight from the
+// owned slots 4 kb .. 4 kb + 3 of a [64][128] result, so U = T R and dR =
+// T^T dU run from registers.  The products that contract over channels read
+// their operands as 16-byte rows from LDS, where each such result is staged
+// once.  The B operands that come from the state and its gradient (a wave's
+// 16 columns, or its 16 rows, of S and dS') are loaded into registers one
+// phase before they are used.
+//
+// LDS: three [64][132] arrays (kh, qh and Gam while P and N are formed, then
+// Kt and Kb for R and dU, then R, dU and U, then scale dO, dX / Y and dR), P,
+// N and X at a pitch of 68 (16-byte rows that a wave reads in 8 distinct bank
+// groups), and a few vectors.  Partial sums are reduced in a fixed order, so
+// results are bitwise reproducible.
 // ---------------------------------------------------------------------------
 constexpr int kCT = 512;
-constexpr int kPK = kD + 4;  // row pitch of the per-channel arrays: rows 16 B apart in bank
+constexpr int kPB = kD + 4;      // pitch of the [64][128] arrays
+constexpr int kPS = kChunk + 4;  // pitch of the [64][64] arrays
 struct __align__(16) BwdLds {
-    float gam[kChunk][kPK];  // Gam (cumulative log-decay), later dGam
-    float kh[kChunk][kPK];
-    float qh[kChunk][kPK];
-    float p[kChunk][kChunk];  // P, later dP
-    float n[kChunk][kChunk];  // N (= M), later dM
-    float x[kChunk][kChunk];  // X = (I + A)^-1
+    float big[3][kChunk][kPB];
+    float p[kChunk][kPS];  // P, later dP
+    float n[kChunk][kPS];  // N (= M), later dM
+    float x[kChunk][kPS];  // X = (I + A)^-1
     float beta[kChunk];
     float rq[kChunk];
     float rk[kChunk];
     float dbeta[kChunk];
     float dotq[kChunk];
     float dotk[kChunk];
-    float gl[kD];    // Gam of the chunk's last row
-    float dlast[kD];  // gamma dgamma, the extra dGam of the last row besides sum_r Kb dKb
-    float red[2048];  // per-thread partial sums, reduced in a fixed order (deterministic)
+    float gl[kD];     // Gam of the chunk's last row
+    float red[8 * kD];  // partial sums
 };
+static_assert(kPS <= kPB, "dX, then Y, fit in one [64][128] array");
+
+// Raw q / k / v / dout values, held in registers until they are used (widening
+// a bf16 value is an instruction, which would make the wave wait for the load
+// where it is placed).
+template <typename IO> struct RawIO;
+template <> struct RawIO<float> {
+    using one = float;
+    using four = float4;
+    static __device__ __forceinline__ float wid(float x) { return x; }
+    static __device__ __forceinline__ float4 wid(float4 x) { return x; }
+};
+template <> struct RawIO<uint16_t> {
+    using one = uint16_t;
+    using four = uint2;
+    static __device__ __forceinline__ float wid(uint16_t x) { return bf2f(x); }
+    static __device__ __forceinline__ float4 wid(uint2 u) {
+        return make_float4(__builtin_bit_cast(float, u.x << 16),
+                           __builtin_bit_cast(float, u.x & 0xffff0000u),
+                           __builtin_bit_cast(float, u.y << 16),
+                           __builtin_bit_cast(float, u.y & 0xffff0000u));
+    }
+};
+
+// acc += A B over one 4-deep step per component: four fp32 MFMAs
+__device__ __forceinline__ void mfma4(f32x4& acc, float4 a, float4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+}
+
+// Sums each of V values (V a power of two) over the 16 lanes n of a row by
+// halving exchanges.  On return x[j] of lane n holds the sum of value
+// (V / 16) n + j (j < V / 16) for V >= 16, or of value n / (16 / V) for V < 16.
+template <int LEN, int MASK, int V>
+__device__ __forceinline__ void rsum_step(float (&x)[V], int n) {
+    if constexpr (MASK >= 1) {
+        if constexpr (LEN > 1) {
+            constexpr int HALF = LEN / 2;
+            const bool hi = (n & MASK) != 0;
+#pragma unroll
+            for (int i = 0; i < HALF; ++i) {
+                const float keep = hi ? x[HALF + i] : x[i];
+                const float send = hi ? x[i] : x[HALF + i];
+                x[i] = keep + __shfl_xor(send, MASK);
+            }
+            rsum_step<HALF, MASK / 2>(x, n);
+        } else {
+            x[0] += __shfl_xor(x[0], MASK);
+            rsum_step<1, MASK / 2>(x, n);
+        }
+    }
+}
+template <int V>
+__device__ __forceinline__ void row_sums(float (&x)[V], int n) {
+    rsum_step<V, 8>(x, n);
+}
 
 template <typename IO>
 __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const IO* __restrict__ dout,
     const float* __restrict__ states, const float* __restrict__ dsn,
-    const float* __restrict__ xs, float* __restrict__ scr_all,
-    float scale, int T, int H, int chunk0, int nch, IO* __restrict__ dq, IO* __restrict__ dk,
-    IO* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
+    const float* __restrict__ xs, float scale, int T, int H, int chunk0, int nch,
+    IO* __restrict__ dq, IO* __restrict__ dk, IO* __restrict__ dv, float* __restrict__ dg,
+    float* __restrict__ dbeta) {
+    using RW = RawIO<IO>;
     __shared__ BwdLds s;
+    float(*const A0)[kPB] = s.big[0];  // kh, Kt, R, then dR
+    float(*const A1)[kPB] = s.big[1];  // qh, Kb, dU, then scale dO
+    float(*const A2)[kPB] = s.big[2];  // Gam, then U
+    float(*const DX)[kPS] = reinterpret_cast<float(*)[kPS]>(&s.big[0][0][0]);  // dX, then Y
 
-    // chunk c of the segment (states, dS', X, scratch) is chunk cg of the sequence
+    // chunk c of the segment (states, dS', X) is chunk cg of the sequence
     const int c = blockIdx.x % nch;
     const int bh = blockIdx.x / nch;
     const int b = bh / H, h = bh % H;
     const int cg = chunk0 + c;
     const int L = min(kChunk, T - cg * kChunk);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    const int cc = 16 * wv + n;
     const size_t rp = (size_t)H * kD;  // pitch of one token row
     const size_t base = (((size_t)b * T + (size_t)cg * kChunk) * H + h) * kD;
-    const float* S = states + ((size_t)bh * nch + c) * kStateFloats;
-    const float* dSn = dsn + ((size_t)bh * nch + c) * kStateFloats;
-    float* scr = scr_all + (size_t)blockIdx.x * kScrFloats;
-    float* R_ = scr + kScrR;
-    float* U_ = scr + kScrU;
-    float* dU_ = scr + kScrDU;
-    float* dX_ = scr + kScrDX;
-    float* Y_ = scr + kScrY;
-    float* dR_ = scr + kScrDR;
-    auto in = [&](const IO* p, int r, int col) {
-        return r < L ? io1(p + base + (size_t)r * rp + col) : 0.f;
-    };
+    const float* S = states + (size_t)blockIdx.x * kStateFloats;
+    const float* dSn = dsn + (size_t)blockIdx.x * kStateFloats;
+    // row of owned slot m; rows past the sequence read row L - 1 and are zeroed on use
+    auto orow = [&](int m) { return 16 * (m >> 2) + 4 * gq + (m & 3); };
+    auto crow = [&](int r) { return min(r, L - 1); };
 
-    // ---- load: normalised q, k (8 threads per row, 16 channels each), g ---
+    // ---- loads: q, k, g (8 threads per row, 16 channels each), then X and the
+    // column strips of S and dS' (B operands of R and dU), v and dout
+    float scol[32], dcol[32];  // S, dS' at [16 kb + 4 gq + e][cc], slot 4 kb + e
+    typename RW::one vraw[16], oraw[16];
+    float4 xpf[2];
     {
         const int r = tid >> 3, part = tid & 7;
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        float sq = 0.f, sk = 0.f;
-        float4 qv[4], kv[4];
+        typename RW::four qr[4], kr[4];
+        float4 gv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int col = 16 * part + 4 * e;
-            const size_t off = base + (size_t)r * rp + col;
-            qv[e] = r < L ? io4(q + off) : z;
-            kv[e] = r < L ? io4(k + off) : z;
-            *reinterpret_cast<float4*>(&s.gam[r][col]) = r < L ? ld4(g + off) : z;
+            const size_t off = base + (size_t)crow(r) * rp + 16 * part + 4 * e;
+            qr[e] = *reinterpret_cast<const typename RW::four*>(q + off);
+            kr[e] = *reinterpret_cast<const typename RW::four*>(k + off);
+            gv[e] = ld4(g + off);
+        }
+        const float bt = beta[((size_t)b * T + (size_t)cg * kChunk + crow(r)) * H + h];
+        const float* Xg = xs + (size_t)blockIdx.x * kChunk * kChunk;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + kCT * j;
+            xpf[j] = ld4(Xg + (e >> 4) * kChunk + 4 * (e & 15));
+        }
+#pragma unroll
+        for (int t = 0; t < 32; ++t)
+            scol[t] = S[(size_t)(16 * (t >> 2) + 4 * gq + (t & 3)) * kD + cc];
+        __builtin_amdgcn_sched_barrier(0);
+        const bool ok = r < L;
+        float4 qv[4], kv[4];
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qv[e] = RW::wid(qr[e]);
+            kv[e] = RW::wid(kr[e]);
             sq += qv[e].x * qv[e].x + qv[e].y * qv[e].y + qv[e].z * qv[e].z + qv[e].w * qv[e].w;
             sk += kv[e].x * kv[e].x + kv[e].y * kv[e].y + kv[e].z * kv[e].z + kv[e].w * kv[e].w;
         }
@@ -519,255 +583,401 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             sq += __shfl_xor(sq, o);
             sk += __shfl_xor(sk, o);
         }
-        const float rq = 1.f / sqrtf(sq + kNormEps), rk = 1.f / sqrtf(sk + kNormEps);
+        // rows past the sequence: qh = kh = 0 and g = 0 (Gam stays at its last value)
+        const float rq = ok ? 1.f / sqrtf(sq + kNormEps) : 0.f;
+        const float rk = ok ? 1.f / sqrtf(sk + kNormEps) : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int col = 16 * part + 4 * e;
-            *reinterpret_cast<float4*>(&s.qh[r][col]) = scale4(qv[e], rq);
-            *reinterpret_cast<float4*>(&s.kh[r][col]) = scale4(kv[e], rk);
+            *reinterpret_cast<float4*>(&A0[r][col]) = scale4(kv[e], rk);
+            *reinterpret_cast<float4*>(&A1[r][col]) = scale4(qv[e], rq);
+            *reinterpret_cast<float4*>(&A2[r][col]) = ok ? gv[e] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         if (part == 0) {
             s.rq[r] = rq;
             s.rk[r] = rk;
-            s.beta[r] = r < L ? beta[((size_t)b * T + (size_t)cg * kChunk + r) * H + h] : 0.f;
-            s.dbeta[r] = 0.f;
-            s.dotq[r] = 0.f;
-            s.dotk[r] = 0.f;
+            s.beta[r] = ok ? bt : 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 32; ++t)
+            dcol[t] = dSn[(size_t)(16 * (t >> 2) + 4 * gq + (t & 3)) * kD + cc];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const size_t off = base + (size_t)crow(orow(m)) * rp + cc;
+            vraw[m] = v[off];
+            oraw[m] = dout[off];
         }
     }
     __syncthreads();
-    if (tid < kD) {  // Gam = cumulative sum of g down the chunk, per channel
+    // ---- Gam = cumulative sum of g down the chunk: four threads per channel,
+    // 16 rows each, then the totals of the earlier quarters
+    {
+        const int ch = tid & (kD - 1), qq = tid >> 7;
         float a = 0.f;
-        for (int r = 0; r < kChunk; ++r) {
-            a += s.gam[r][tid];
-            s.gam[r][tid] = a;
-        }
-        s.gl[tid] = a;
-    }
-    {  // dgamma = rowsum(dS' . S), times gamma for the last row of dGam: 4 threads a row
-        const int row = tid >> 2, part = tid & 3;
-        float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = 32 * part + 4 * e;
-            const float4 a = ld4(dSn + (size_t)row * kD + col), b = ld4(S + (size_t)row * kD + col);
-            d += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+        for (int r = 0; r < 16; ++r) a += A2[16 * qq + r][ch];
+        s.red[qq * kD + ch] = a;
+        __syncthreads();
+        float pre = 0.f;
+        for (int j = 0; j < qq; ++j) pre += s.red[j * kD + ch];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pre += A2[16 * qq + r][ch];
+            A2[16 * qq + r][ch] = pre;
         }
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        __syncthreads();  // Gam's last row is complete
-        if (part == 0) s.dlast[row] = d * ex(s.gl[row]);
+        if (qq == 3) s.gl[ch] = pre;
+        // the tiles of P and N above the diagonal blocks are zero
+        for (int idx = tid; idx < kChunk * kChunk; idx += kCT) {
+            const int i = idx >> 6, j = idx & 63;
+            if (j >= 16 * ((i >> 4) + 1)) {
+                s.p[i][j] = 0.f;
+                s.n[i][j] = 0.f;
+            }
+        }
     }
-    // X = (I + A)^-1 of this chunk, as the record prep formed it
-    stage<kCT>(xs + (size_t)blockIdx.x * kChunk * kChunk, kChunk, kChunk, kChunk, kChunk,
-                    &s.x[0][0], kChunk);
+    __syncthreads();
 
     // ---- P (strict lower) and N (lower incl) on the matrix cores -------------
     // For column block cb (i in 16 cb .. 16 cb + 15, reference row e = 16 cb +
     // 15) and rows r >= 16 cb: exp(Gam_r - Gam_i) = exp(Gam_r - Gam_e) exp(Gam_e -
     // Gam_i), both factors within exp(+-75) for g >= -5, so
     //   P_ri = sum_c (kh_rc exp(Gam_rc - Gam_ec)) (kh_ic exp(Gam_ec - Gam_ic)),
-    // N likewise with qh_r; tiles above the diagonal blocks stay zero.
-    for (int idx = tid; idx < kChunk * kChunk; idx += kCT) {
-        (&s.p[0][0])[idx] = 0.f;
-        (&s.n[0][0])[idx] = 0.f;
+    // N likewise with qh_r.
+    for (int t = wv; t < 10; t += kCT / 64) {  // the 10 tiles (rt, cb), rt >= cb
+        int cb = 0, rem = t;
+        while (rem >= 4 - cb) {
+            rem -= 4 - cb;
+            ++cb;
+        }
+        const int rt = cb + rem;
+        const int r = 16 * rt + n, i = 16 * cb + n, e = 16 * cb + 15;
+        f32x4 accp = {0.f, 0.f, 0.f, 0.f}, accn = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < kD; k0 += 16) {
+            const int col = k0 + 4 * gq;
+            const float4 gr = ld4(&A2[r][col]), ge = ld4(&A2[e][col]), gi = ld4(&A2[i][col]);
+            const float4 f = exp4(make_float4(gr.x - ge.x, gr.y - ge.y, gr.z - ge.z, gr.w - ge.w));
+            const float4 hh = exp4(make_float4(ge.x - gi.x, ge.y - gi.y, ge.z - gi.z, ge.w - gi.w));
+            const float4 bk = mul4(ld4(&A0[i][col]), hh);
+            mfma4(accp, mul4(ld4(&A0[r][col]), f), bk);
+            mfma4(accn, mul4(ld4(&A1[r][col]), f), bk);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 16 * rt + 4 * gq + u, col = 16 * cb + n;
+            s.p[row][col] = col < row ? accp[u] : 0.f;
+            s.n[row][col] = col <= row ? accn[u] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = tid + kCT * j;
+        *reinterpret_cast<float4*>(&s.x[e >> 4][4 * (e & 15)]) = xpf[j];
+    }
+    __syncthreads();  // P and N are done with kh, qh and Gam
+    // -Kt = -e^Gam kh over kh and Kb = e^(GL - Gam) kh over qh, in 16-byte pieces
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + kCT * j, r = e >> 5, c4 = 4 * (e & 31);
+        const float4 kh = ld4(&A0[r][c4]), gm = ld4(&A2[r][c4]), gl = ld4(&s.gl[c4]);
+        const float4 et = exp4(gm);
+        const float4 eb = exp4(make_float4(gl.x - gm.x, gl.y - gm.y, gl.z - gm.z, gl.w - gm.w));
+        *reinterpret_cast<float4*>(&A0[r][c4]) = scale4(mul4(et, kh), -1.f);
+        *reinterpret_cast<float4*>(&A1[r][c4]) = mul4(eb, kh);
     }
     __syncthreads();
+
+    // ---- R = V - Kt S and dU = scale M^T dO + Kb dS' -------------------------
+    // R starts from V, and the products add -Kt S
+    float Ro[16], dUo[16], gmo[16];
     {
-        const int lane = tid & 63, w = tid >> 6, n = lane & 15, g = lane >> 4;
-        for (int t = w; t < 10; t += kCT / 64) {  // the 10 tiles (rt, cb), rt >= cb
-            int cb = 0, rem = t;
-            while (rem >= 4 - cb) {
-                rem -= 4 - cb;
-                ++cb;
-            }
-            const int rt = cb + rem;
-            const int r = 16 * rt + n, i = 16 * cb + n, e = 16 * cb + 15;
-            f32x4 accp = {0.f, 0.f, 0.f, 0.f}, accn = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < kD; k0 += 16) {
-                const int c = k0 + 4 * g;
-                const float4 gr = ld4(&s.gam[r][c]), ge = ld4(&s.gam[e][c]);
-                const float4 gi = ld4(&s.gam[i][c]);
-                const float4 f = exp4(make_float4(gr.x - ge.x, gr.y - ge.y, gr.z - ge.z, gr.w - ge.w));
-                const float4 hh = exp4(make_float4(ge.x - gi.x, ge.y - gi.y, ge.z - gi.z, ge.w - gi.w));
-                const float4 ak = mul4(ld4(&s.kh[r][c]), f), aq = mul4(ld4(&s.qh[r][c]), f);
-                const float4 bk = mul4(ld4(&s.kh[i][c]), hh);
-                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bk.x, accp, 0, 0, 0);
-                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bk.y, accp, 0, 0, 0);
-                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bk.z, accp, 0, 0, 0);
-                accp = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bk.w, accp, 0, 0, 0);
-                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bk.x, accn, 0, 0, 0);
-                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bk.y, accn, 0, 0, 0);
-                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.z, bk.z, accn, 0, 0, 0);
-                accn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.w, bk.w, accn, 0, 0, 0);
-            }
+        f32x4 aR[4], aU[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            aU[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                aR[u][e] = orow(4 * u + e) < L ? RW::wid(vraw[4 * u + e]) : 0.f;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const float4 bs = make_float4(scol[4 * kb], scol[4 * kb + 1], scol[4 * kb + 2],
+                                          scol[4 * kb + 3]);
+            const float4 bd = make_float4(dcol[4 * kb], dcol[4 * kb + 1], dcol[4 * kb + 2],
+                                          dcol[4 * kb + 3]);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int row = 16 * rt + 4 * g + u, col = 16 * cb + n;
-                s.p[row][col] = col < row ? accp[u] : 0.f;
-                s.n[row][col] = col <= row ? accn[u] : 0.f;
+                mfma4(aR[u], ld4(&A0[16 * u + n][16 * kb + 4 * gq]), bs);
+                mfma4(aU[u], ld4(&A1[16 * u + n][16 * kb + 4 * gq]), bd);
             }
         }
+        // M^T: A(i, kk) = N[kk][i], zero for kk < i, so row tile u takes blocks kb >= u
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float o4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o4[e] = orow(4 * kb + e) < L ? scale * RW::wid(oraw[4 * kb + e]) : 0.f;
+            const float4 bo = make_float4(o4[0], o4[1], o4[2], o4[3]);
+            const int kr = 16 * kb + 4 * gq;
+#pragma unroll
+            for (int u = 0; u <= kb; ++u)
+                mfma4(aU[u], make_float4(s.n[kr][16 * u + n], s.n[kr + 1][16 * u + n],
+                                         s.n[kr + 2][16 * u + n], s.n[kr + 3][16 * u + n]),
+                      bo);
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            Ro[m] = aR[m >> 2][m & 3];
+            dUo[m] = aU[m >> 2][m & 3];
+            gmo[m] = A2[orow(m)][cc];  // the lane's own Gam, kept to the end
+        }
     }
-    __syncthreads();
+    __syncthreads();  // every read of Kt, Kb and Gam is done
 
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    // q / k / v / dout row r from channel col on, four values (zeros past the sequence)
-    auto in4 = [&](const IO* p, int r, int col) {
-        return r < L ? io4(p + base + (size_t)r * rp + col) : z4;
-    };
-    // Products in three phases, each needing only the ones before it:
-    // (R, dU), then (U, dR, dT), then dM.
-    // ---- R = V - Kt S --------------------------------------------------------
-    mmf<kChunk, kD, kCT>(
-        kD, [&](int i, int kk) { return mul4(exp4(ld4(&s.gam[i][kk])), ld4(&s.kh[i][kk])); },
-        [&](int kk, int j) { return col4(S + (size_t)kk * kD + j, kD); },
-        [&](int i, int j, float a) { R_[i * kD + j] = in(v, i, j) - a; });
-    // ---- dU = scale M^T dO + Kb dS' ------------------------------------------
-    mmf<kChunk, kD, kCT>(
-        kChunk + kD,
-        [&](int i, int kk) {
-            if (kk < kChunk) return scale4(col4(&s.n[kk][i], kChunk), scale);
-            const int c4 = kk - kChunk;
-            float4 e = ld4(&s.gam[i][c4]);
-            const float4 gl = ld4(&s.gl[c4]);
-            e = exp4(make_float4(gl.x - e.x, gl.y - e.y, gl.z - e.z, gl.w - e.w));
-            return mul4(e, ld4(&s.kh[i][c4]));
-        },
-        [&](int kk, int j) {
-            if (kk < kChunk) {
-                return make_float4(in(dout, kk, j), in(dout, kk + 1, j), in(dout, kk + 2, j),
-                                   in(dout, kk + 3, j));
+    // ---- U = T R and dV = dR = T^T dU, T = X diag(beta), from registers ------
+    float dRo[16];
+    {
+        f32x4 aX[4], aD[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) aX[u] = aD[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const float4 br = make_float4(Ro[4 * kb], Ro[4 * kb + 1], Ro[4 * kb + 2], Ro[4 * kb + 3]);
+            const float4 bd =
+                make_float4(dUo[4 * kb], dUo[4 * kb + 1], dUo[4 * kb + 2], dUo[4 * kb + 3]);
+            const int kr = 16 * kb + 4 * gq;
+            const float4 bb = ld4(&s.beta[kr]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // X is lower triangular: U's row tile u takes blocks kb <= u, dR's kb >= u
+                if (u >= kb) mfma4(aX[u], mul4(ld4(&s.x[16 * u + n][kr]), bb), br);
+                if (u <= kb)
+                    mfma4(aD[u], make_float4(s.x[kr][16 * u + n], s.x[kr + 1][16 * u + n],
+                                             s.x[kr + 2][16 * u + n], s.x[kr + 3][16 * u + n]),
+                          bd);
             }
-            return col4(dSn + (size_t)(kk - kChunk) * kD + j, kD);
-        },
-        [&](int i, int j, float a) { dU_[i * kD + j] = a; });
-    __syncthreads();
-    // ---- U = T R,  T = X diag(beta) ------------------------------------------
-    mmf<kChunk, kD, kCT>(
-        kChunk, [&](int i, int kk) { return mul4(ld4(&s.x[i][kk]), ld4(&s.beta[kk])); },
-        [&](int kk, int j) { return col4(R_ + kk * kD + j, kD); },
-        [&](int i, int j, float a) { U_[i * kD + j] = a; });
-    // ---- dV = dR = T^T dU ----------------------------------------------------
-    mmf<kChunk, kD, kCT>(
-        kChunk, [&](int i, int kk) { return scale4(col4(&s.x[kk][i], kChunk), s.beta[i]); },
-        [&](int kk, int j) { return col4(dU_ + kk * kD + j, kD); },
-        [&](int i, int j, float a) {
-            dR_[i * kD + j] = a;
-            if (i < L) io_st(dv + base + (size_t)i * rp + j, a);
-        });
-    // ---- dT = lower-incl(dU R^T), into dX's space -----------------------------
-    mmf<kChunk, kChunk, kCT>(
-        kD, [&](int i, int kk) { return ld4(dU_ + i * kD + kk); },
-        [&](int kk, int j) { return ld4(R_ + j * kD + kk); },
-        [&](int i, int j, float a) { dX_[i * kChunk + j] = j <= i ? a : 0.f; });
-    __syncthreads();
-    // ---- dM = scale lower-incl(dO U^T), over N ---------------------------------
-    mmf<kChunk, kChunk, kCT>(
-        kD, [&](int i, int kk) { return in4(dout, i, kk); },
-        [&](int kk, int j) { return ld4(U_ + j * kD + kk); },
-        [&](int i, int j, float a) { s.n[i][j] = j <= i ? scale * a : 0.f; });
-    __syncthreads();
-    // dbeta_j = sum_i X_ij dT_ij (eight partial sums over 8 rows each, added in
-    // order), then dX = dT diag(beta) in place
-    {
-        const int j = tid % kChunk, part = tid / kChunk;
-        float a = 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = 8 * part + u;
-            a = fmaf(s.x[i][j], dX_[i * kChunk + j], a);
         }
-        s.red[part * kChunk + j] = a;
-    }
-    __syncthreads();
-    if (tid < kChunk) {
-        float a = 0.f;
-        for (int part = 0; part < kCT / kChunk; ++part) a += s.red[part * kChunk + tid];
-        s.dbeta[tid] = a;
-    }
-    for (int idx = tid; idx < kChunk * kChunk; idx += kCT)
-        dX_[idx] *= s.beta[idx % kChunk];
-    __syncthreads();
-    // ---- Y = X^T dX ------------------------------------------------------------
-    mmf<kChunk, kChunk, kCT>(
-        kChunk, [&](int i, int kk) { return col4(&s.x[kk][i], kChunk); },
-        [&](int kk, int j) { return col4(dX_ + kk * kChunk + j, kChunk); },
-        [&](int i, int j, float a) { Y_[i * kChunk + j] = a; });
-    __syncthreads();
-    // ---- dA = -strict-lower(Y X^T), into dX's space ----------------------------
-    mmf<kChunk, kChunk, kCT>(
-        kChunk, [&](int i, int kk) { return ld4(Y_ + i * kChunk + kk); },
-        [&](int kk, int j) { return ld4(&s.x[j][kk]); },
-        [&](int i, int j, float a) { dX_[i * kChunk + j] = j < i ? -a : 0.f; });
-    __syncthreads();
-    // dbeta_i += sum_j dA_ij P_ij (eight partial sums over 8 columns each, added
-    // in order), then dP = diag(beta) dA over P
-    {
-        const int i = tid % kChunk, part = tid / kChunk;
-        float a = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = 8 * part + u;
-            a = fmaf(dX_[i * kChunk + j], s.p[i][j], a);
+        for (int m = 0; m < 16; ++m) {
+            const int r = orow(m);
+            dRo[m] = s.beta[r] * aD[m >> 2][m & 3];
+            if (r < L) io_st(dv + base + (size_t)r * rp + cc, dRo[m]);
+            A0[r][cc] = Ro[m];
+            A1[r][cc] = dUo[m];
+            A2[r][cc] = aX[m >> 2][m & 3];
         }
-        s.red[part * kChunk + i] = a;
     }
-    __syncthreads();
+    // later B operands: the row strips S[cc][*] and dS'[cc][*]; and dO for staging
+    float4 srow[8], drow[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        srow[kb] = ld4(S + (size_t)cc * kD + 16 * kb + 4 * gq);
+        drow[kb] = ld4(dSn + (size_t)cc * kD + 16 * kb + 4 * gq);
+    }
+    typename RW::four opf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + kCT * j;
+        opf[j] = *reinterpret_cast<const typename RW::four*>(
+            dout + base + (size_t)crow(e >> 5) * rp + 4 * (e & 31));
+    }
+    // q and k at the lane's own slots, for its kh and qh in the element-wise part
+    typename RW::one kraw[16], qraw[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const size_t off = base + (size_t)crow(orow(m)) * rp + cc;
+        kraw[m] = k[off];
+        qraw[m] = q[off];
+    }
+    __syncthreads();  // R, dU and U are in LDS
+
+    // ---- the 64 x 64 products: wave w computes tiles (rt0, ct) and (rt0 + 2, ct)
+    const int ct = wv & 3, rt0 = wv >> 2;
+    // dT = lower-incl(dU R^T); dbeta_j = sum_i X_ij dT_ij; dX = dT diag(beta)
+    float dXo[8];
+    {
+        f32x4 aT[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const float4 bR = ld4(&A0[16 * ct + n][16 * kb + 4 * gq]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (rt0 + 2 * t >= ct) mfma4(aT[t], ld4(&A1[16 * (rt0 + 2 * t) + n][16 * kb + 4 * gq]), bR);
+        }
+        const int j = 16 * ct + n;
+        float pb = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * (rt0 + 2 * t) + 4 * gq + e;
+                const float d = j <= i ? aT[t][e] : 0.f;
+                pb = fmaf(s.x[i][j], d, pb);
+                dXo[4 * t + e] = d * s.beta[j];
+            }
+        pb += __shfl_xor(pb, 16);
+        pb += __shfl_xor(pb, 32);
+        if (gq == 0) s.red[rt0 * kChunk + j] = pb;
+    }
+    __syncthreads();  // dT's reads of R and dU are done
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) DX[16 * (rt0 + 2 * t) + 4 * gq + e][16 * ct + n] = dXo[4 * t + e];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + kCT * j;
+        const int r = e >> 5;
+        *reinterpret_cast<float4*>(&A1[r][4 * (e & 31)]) =
+            r < L ? scale4(RW::wid(opf[j]), scale) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < kChunk) s.dbeta[tid] = s.red[tid] + s.red[kChunk + tid];
+    __syncthreads();  // dX and scale dO are in LDS
+    // Y = X^T dX (Y_ij = sum_k X_ki dX_kj, k >= max(i, j)); dM = lower-incl(scale dO U^T)
+    f32x4 aY[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+        f32x4 aM[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int kr = 16 * kb + 4 * gq;
+            if (kb >= ct) {
+                const float4 bX = make_float4(DX[kr][16 * ct + n], DX[kr + 1][16 * ct + n],
+                                              DX[kr + 2][16 * ct + n], DX[kr + 3][16 * ct + n]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int rt = rt0 + 2 * t;
+                    if (kb >= rt)
+                        mfma4(aY[t], make_float4(s.x[kr][16 * rt + n], s.x[kr + 1][16 * rt + n],
+                                                 s.x[kr + 2][16 * rt + n], s.x[kr + 3][16 * rt + n]),
+                              bX);
+                }
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const float4 bU = ld4(&A2[16 * ct + n][16 * kb + 4 * gq]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (rt0 + 2 * t >= ct) mfma4(aM[t], ld4(&A1[16 * (rt0 + 2 * t) + n][16 * kb + 4 * gq]), bU);
+        }
+        // over N, whose last read was in dU
+        const int j = 16 * ct + n;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * (rt0 + 2 * t) + 4 * gq + e;
+                s.n[i][j] = j <= i ? aM[t][e] : 0.f;
+            }
+    }
+    __syncthreads();  // Y's reads of dX are done
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) DX[16 * (rt0 + 2 * t) + 4 * gq + e][16 * ct + n] = aY[t][e];
+    __syncthreads();  // Y is in LDS
+    // dA = -strict-lower(Y X^T) (X_jk = 0 for k > j); dbeta_i += sum_j dA_ij P_ij;
+    // dP = diag(beta) dA over P, each lane at its own elements
+    {
+        f32x4 aA[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb > ct) continue;
+            const float4 bX = ld4(&s.x[16 * ct + n][16 * kb + 4 * gq]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (rt0 + 2 * t >= ct) mfma4(aA[t], ld4(&DX[16 * (rt0 + 2 * t) + n][16 * kb + 4 * gq]), bX);
+        }
+        const int j = 16 * ct + n;
+        float pr[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * (rt0 + 2 * t) + 4 * gq + e;
+                const float a = j < i ? -aA[t][e] : 0.f;
+                pr[4 * t + e] = a * s.p[i][j];
+                s.p[i][j] = s.beta[i] * a;
+            }
+        row_sums(pr, n);  // lane n: value n / 2, i.e. tile n / 8, row 4 gq + (n / 2) % 4
+        if ((n & 1) == 0) {
+            const int vi = n >> 1;
+            s.red[ct * kChunk + 16 * (rt0 + 2 * (vi >> 2)) + 4 * gq + (vi & 3)] = pr[0];
+        }
+    }
+    __syncthreads();  // dA's reads of Y are done; dP, dM and the dbeta partials are in LDS
+#pragma unroll
+    for (int m = 0; m < 16; ++m) A0[orow(m)][cc] = dRo[m];
     if (tid < kChunk) {
         float a = s.dbeta[tid];
-        for (int part = 0; part < kCT / kChunk; ++part) a += s.red[part * kChunk + tid];
+        for (int j = 0; j < 4; ++j) a += s.red[j * kChunk + tid];
         s.dbeta[tid] = a;
     }
-    __syncthreads();
-    for (int idx = tid; idx < kChunk * kChunk; idx += kCT) {
-        const int i = idx / kChunk, j = idx % kChunk;
-        s.p[i][j] = s.beta[i] * dX_[idx];
-    }
+    __syncthreads();  // dR is in LDS
 
-    // ---- element-wise part over [64][128] ------------------------------------
-    // Lane (n, g) of wave w owns channel cc = 16 w + n and rows 16 u + 4 g + e
-    // (u, e < 4; slot m = 4 u + e): the accumulator layout of column tile w in
-    // mmf<64, 128>, so the products below hand their results straight to it.
-    const int lane = tid & 63, wv = tid >> 6, g4 = 4 * (lane >> 4);
-    const int cc = 16 * wv + (lane & 15);
-    float dkh[16], dqh[16], dgm[16];
-    __syncthreads();  // dP is in P
-    // dQt = scale dO S^T:  dqh = e^Gam dQt,  dGam = Qt dQt
-    mmf<kChunk, kD, kCT>(
-        kD, [&](int i, int kk) { return in4(dout, i, kk); },
-        [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
-        [&](int m, int i, int j, float a) {
-            const float d = scale * a, e = ex(s.gam[i][j]);
-            dqh[m] = e * d;
-            dgm[m] = e * s.qh[i][j] * d;
-        });
-    // dKt = -dR S^T:  dkh = e^Gam dKt,  dGam += Kt dKt
-    mmf<kChunk, kD, kCT>(
-        kD, [&](int i, int kk) { return scale4(ld4(dR_ + i * kD + kk), -1.f); },
-        [&](int kk, int j) { return ld4(S + (size_t)j * kD + kk); },
-        [&](int m, int i, int j, float a) {
-            const float e = ex(s.gam[i][j]);
-            dkh[m] = e * a;
-            dgm[m] = fmaf(e * s.kh[i][j], a, dgm[m]);
-        });
-    // dKb = U dS'^T:  dkh += e^(GL - Gam) dKb,  dGam -= Kb dKb; the last row of
-    // dGam also gets sum_r Kb dKb (per channel, into red[0 .. 127])
+    // ---- dQt = scale dO S^T, dKt = -dR S^T, dKb = U dS'^T ----------------------
+    // dqh = e^Gam dQt, dkh = e^Gam dKt + e^(GL - Gam) dKb,
+    // dGam = Qt dQt + Kt dKt - Kb dKb; the last row of dGam also gets
+    // sum_r Kb dKb (per channel, pl)
+    float dqh[16], dkh[16], dgm[16], kho[16], qho[16], pl = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {  // the same products as the normalisation above
+        const int r = orow(m);
+        kho[m] = r < L ? RW::wid(kraw[m]) * s.rk[r] : 0.f;
+        qho[m] = r < L ? RW::wid(qraw[m]) * s.rq[r] : 0.f;
+    }
+    // dgamma = rowsum(dS' . S) at the lane's channel: over its row strips, then
+    // over the four lanes of the channel; the last row of dGam gets gamma dgamma
+    float dlast;
     {
-        float pl = 0.f;
-        mmf<kChunk, kD, kCT>(
-            kD, [&](int i, int kk) { return ld4(U_ + i * kD + kk); },
-            [&](int kk, int j) { return ld4(dSn + (size_t)j * kD + kk); },
-            [&](int m, int i, int j, float a) {
-                const float e = ex(s.gl[j] - s.gam[i][j]);
-                const float t = e * s.kh[i][j] * a;
-                dkh[m] = fmaf(e, a, dkh[m]);
-                dgm[m] -= t;
-                pl += t;
-            });
+        float a = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            a += srow[kb].x * drow[kb].x + srow[kb].y * drow[kb].y + srow[kb].z * drow[kb].z +
+                 srow[kb].w * drow[kb].w;
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        dlast = a * ex(s.gl[cc]);
+    }
+    {
+        f32x4 aQ[4], aK[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) aQ[u] = aK[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                mfma4(aQ[u], ld4(&A1[16 * u + n][16 * kb + 4 * gq]), srow[kb]);
+                mfma4(aK[u], ld4(&A0[16 * u + n][16 * kb + 4 * gq]), srow[kb]);
+            }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const float e = ex(gmo[m]), a = aQ[m >> 2][m & 3], bb = -aK[m >> 2][m & 3];
+            dqh[m] = e * a;
+            dkh[m] = e * bb;
+            dgm[m] = e * fmaf(qho[m], a, kho[m] * bb);
+        }
+    }
+    {
+        f32x4 aB[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) aB[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mfma4(aB[u], ld4(&A2[16 * u + n][16 * kb + 4 * gq]), drow[kb]);
+        const float glc = s.gl[cc];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const float e = ex(glc - gmo[m]), a = aB[m >> 2][m & 3];
+            const float t = e * kho[m] * a;
+            dkh[m] = fmaf(e, a, dkh[m]);
+            dgm[m] -= t;
+            pl += t;
+        }
         pl += __shfl_xor(pl, 16);
         pl += __shfl_xor(pl, 32);
-        if (lane < 16) s.red[cc] = pl;
     }
 
     // ---- the pairwise-decay terms of P and N ---------------------------------
@@ -777,148 +987,155 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     // dGam += kh a + qh b - kh c.  E is split about a reference row per
     // 16-row block, as in the forward: with g >= -5 each factor stays within
     // exp(+-75), finite in fp32.
-    //   row side, i in block b, reference e = 16 b + 15:
-    //     E = exp(Gam_r - Gam_e) exp(Gam_e - Gam_i), rows r >= 16 b;
-    //   column side, r in block a, reference s0 = 16 a:
-    //     E = exp(Gam_r - Gam_s0) exp(Gam_s0 - Gam_i), rows i <= 16 a + 15.
-    // Each block's sums are a 16-deep product on the matrix cores; the factor
-    // matrices (16 x 128) take the space of X.
-    {
-        float (*f1)[kD] = reinterpret_cast<float (*)[kD]>(&s.x[0][0]);       // [16][128]
-        float (*f2)[kD] = reinterpret_cast<float (*)[kD]>(&s.x[0][0] + kSub * kD);
-        for (int blk = 0; blk < kChunk / kSub; ++blk) {
-            const int r0 = kSub * blk, e = r0 + kSub - 1;
-            __syncthreads();  // X, or the previous block's factors, are no longer read
-            // kh_i exp(Gam_e - Gam_i) for i in block blk
-            for (int idx = tid; idx < kSub * kD; idx += kCT) {
-                const int kk = idx / kD, c = idx % kD;
-                f1[kk][c] = s.kh[r0 + kk][c] * ex(s.gam[e][c] - s.gam[r0 + kk][c]);
-            }
-            __syncthreads();
-            // a = F (dP[:, block] KG), b = F (dN[:, block] KG), F = exp(Gam_r - Gam_e)
-            mmf<kChunk, kD, kCT>(
-                kSub, [&](int i, int kk) { return ld4(&s.p[i][r0 + kk]); },
-                [&](int kk, int j) { return col4(&f1[kk][j], kD); },
-                [&](int m, int i, int j, float a) {
-                    if (i < r0) return;
-                    const float ta = ex(s.gam[i][j] - s.gam[e][j]) * a;
-                    dkh[m] += ta;
-                    dgm[m] = fmaf(s.kh[i][j], ta, dgm[m]);
-                });
-            mmf<kChunk, kD, kCT>(
-                kSub, [&](int i, int kk) { return ld4(&s.n[i][r0 + kk]); },
-                [&](int kk, int j) { return col4(&f1[kk][j], kD); },
-                [&](int m, int i, int j, float a) {
-                    if (i < r0) return;
-                    const float tb = ex(s.gam[i][j] - s.gam[e][j]) * a;
-                    dqh[m] += tb;
-                    dgm[m] = fmaf(s.qh[i][j], tb, dgm[m]);
-                });
+    //   row side, i in block bk, reference e = 16 bk + 15:
+    //     E = exp(Gam_r - Gam_e) exp(Gam_e - Gam_i), rows r >= 16 bk;
+    //   column side, r in block bk, reference s0 = 16 bk:
+    //     E = exp(Gam_r - Gam_s0) exp(Gam_s0 - Gam_i), rows i <= 16 bk + 15.
+    // Each block's sums are a 16-deep product on the matrix cores whose B
+    // operand (the block's factor rows, at the lane's channel) the lane forms
+    // from its own slots 4 bk .. 4 bk + 3; the reference Gam comes from the
+    // lane of the same channel that owns the reference row.
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+        const float ge = __shfl(gmo[4 * bk + 3], n + 48);  // Gam at row 16 bk + 15
+        const float gs = __shfl(gmo[4 * bk], n);           // Gam at row 16 bk
+        float fr[4], fk[4], fq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * bk + e;
+            fr[e] = kho[m] * ex(ge - gmo[m]);
+            const float f = ex(gmo[m] - gs);
+            fk[e] = kho[m] * f;
+            fq[e] = qho[m] * f;
         }
-        for (int blk = 0; blk < kChunk / kSub; ++blk) {
-            const int r0 = kSub * blk;
-            __syncthreads();
-            // kh_r exp(Gam_r - Gam_s0) and qh_r exp(Gam_r - Gam_s0) for r in block blk
-            for (int idx = tid; idx < kSub * kD; idx += kCT) {
-                const int kk = idx / kD, c = idx % kD;
-                const float f = ex(s.gam[r0 + kk][c] - s.gam[r0][c]);
-                f1[kk][c] = s.kh[r0 + kk][c] * f;
-                f2[kk][c] = s.qh[r0 + kk][c] * f;
+        const float4 bR = make_float4(fr[0], fr[1], fr[2], fr[3]);
+        const float4 bK = make_float4(fk[0], fk[1], fk[2], fk[3]);
+        const float4 bQ = make_float4(fq[0], fq[1], fq[2], fq[3]);
+        const int kr = 16 * bk + 4 * gq;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (u >= bk) {  // row side, rows of tile u >= the block
+                f32x4 acn = {0.f, 0.f, 0.f, 0.f};
+                mfma4(acc, ld4(&s.p[16 * u + n][kr]), bR);
+                mfma4(acn, ld4(&s.n[16 * u + n][kr]), bR);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 4 * u + e;
+                    const float f = ex(gmo[m] - ge);
+                    const float ta = f * acc[e], tb = f * acn[e];
+                    dkh[m] += ta;
+                    dqh[m] += tb;
+                    dgm[m] = fmaf(kho[m], ta, fmaf(qho[m], tb, dgm[m]));
+                }
             }
-            __syncthreads();
-            // c = H (dP[block, :]^T KR + dN[block, :]^T QR), H = exp(Gam_s0 - Gam_i)
-            mmf<kChunk, kD, kCT>(
-                2 * kSub,
-                [&](int i, int kk) {
-                    return kk < kSub ? col4(&s.p[r0 + kk][i], kChunk)
-                                     : col4(&s.n[r0 + kk - kSub][i], kChunk);
-                },
-                [&](int kk, int j) {
-                    return kk < kSub ? col4(&f1[kk][j], kD) : col4(&f2[kk - kSub][j], kD);
-                },
-                [&](int m, int i, int j, float a) {
-                    if (i > r0 + kSub - 1) return;
-                    const float tc = ex(s.gam[r0][j] - s.gam[i][j]) * a;
+            if (u <= bk) {  // column side, rows of tile u <= the block
+                f32x4 acx = {0.f, 0.f, 0.f, 0.f};
+                const int i = 16 * u + n;
+                mfma4(acx, make_float4(s.p[kr][i], s.p[kr + 1][i], s.p[kr + 2][i], s.p[kr + 3][i]), bK);
+                mfma4(acx, make_float4(s.n[kr][i], s.n[kr + 1][i], s.n[kr + 2][i], s.n[kr + 3][i]), bQ);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 4 * u + e;
+                    const float tc = ex(gs - gmo[m]) * acx[e];
                     dkh[m] += tc;
-                    dgm[m] = fmaf(-s.kh[i][j], tc, dgm[m]);
-                });
+                    dgm[m] = fmaf(-kho[m], tc, dgm[m]);
+                }
+            }
         }
     }
 
-    // ---- dg = reverse cumulative sum of dGam; the norms' backward -------------
+    // ---- the norms' backward, dg, and the stores ------------------------------
     // row dots qh . dqh and kh . dkh: over the 16 channels of the lane's column
-    // tile by shuffles, then over the 8 tiles in a fixed order
+    // tile, then over the 8 tiles in order
     {
-        float* dq_part = s.red + kD;             // [8][64]
-        float* dk_part = s.red + kD + 8 * kChunk;  // [8][64]
+        float aq[16], ak[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            const int r = 16 * (m >> 2) + g4 + (m & 3);
-            float aq = s.qh[r][cc] * dqh[m], ak = s.kh[r][cc] * dkh[m];
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                aq += __shfl_xor(aq, o);
-                ak += __shfl_xor(ak, o);
-            }
-            if ((lane & 15) == 0) {
-                dq_part[wv * kChunk + r] = aq;
-                dk_part[wv * kChunk + r] = ak;
-            }
+            aq[m] = qho[m] * dqh[m];
+            ak[m] = kho[m] * dkh[m];
         }
-        __syncthreads();  // every read of Gam is done: its space takes dGam
-        if (tid < kChunk) {
-            float aq = 0.f, ak = 0.f;
-            for (int w = 0; w < kCT / 64; ++w) {
-                aq += dq_part[w * kChunk + tid];
-                ak += dk_part[w * kChunk + tid];
-            }
-            s.dotq[tid] = aq;
-            s.dotk[tid] = ak;
-        }
-#pragma unroll
-        for (int m = 0; m < 16; ++m) s.gam[16 * (m >> 2) + g4 + (m & 3)][cc] = dgm[m];
+        row_sums(aq, n);  // lane n: slot n
+        row_sums(ak, n);
+        const int r = orow(n);
+        s.red[wv * kChunk + r] = aq[0];
+        s.red[4 * kD + wv * kChunk + r] = ak[0];
     }
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int r = 16 * (m >> 2) + g4 + (m & 3);
-        if (r >= L) continue;
-        // qh = q / sqrt(|q|^2 + eps): dq = rq (dqh - qh (qh . dqh))
-        io_st(dq + base + (size_t)r * rp + cc, s.rq[r] * fmaf(-s.qh[r][cc], s.dotq[r], dqh[m]));
-        io_st(dk + base + (size_t)r * rp + cc, s.rk[r] * fmaf(-s.kh[r][cc], s.dotk[r], dkh[m]));
-    }
-    if (tid < kD) {
-        float a = s.dlast[tid] + s.red[tid];  // Gam of the last row also enters Kb and gamma
-        for (int r = kChunk - 1; r >= 0; --r) {
-            a += s.gam[r][tid];
-            if (r < L) dg[base + (size_t)r * rp + tid] = a;
+    if (tid < kChunk) {
+        float aq = 0.f, ak = 0.f;
+        for (int w = 0; w < kCT / 64; ++w) {
+            aq += s.red[w * kChunk + tid];
+            ak += s.red[4 * kD + w * kChunk + tid];
         }
-    } else if (tid < kD + kChunk) {
-        const int r = tid - kD;
+        s.dotq[tid] = aq;
+        s.dotk[tid] = ak;
+    } else if (tid < 2 * kChunk) {
+        const int r = tid - kChunk;
         if (r < L) dbeta[((size_t)b * T + (size_t)cg * kChunk + r) * H + h] = s.dbeta[r];
     }
+    // dg = reverse cumulative sum of dGam down the chunk; the last row also gets
+    // gamma dgamma and sum_r Kb dKb.  Within the lane over e, then over the
+    // lanes of the channel (gq) and the row tiles (u).
+    {
+        float sfx[16], gt[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 3; e >= 0; --e) {
+                a += dgm[4 * u + e];
+                sfx[4 * u + e] = a;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gt[u][j] = __shfl(a, n + 16 * j);
+        }
+        float after = dlast + pl;
+#pragma unroll
+        for (int u = 3; u >= 0; --u) {
+            float later = 0.f, tot = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                later += j > gq ? gt[u][j] : 0.f;
+                tot += gt[u][j];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 4 * u + e, r = orow(m);
+                if (r < L) dg[base + (size_t)r * rp + cc] = sfx[m] + later + after;
+            }
+            after += tot;
+        }
+    }
+    __syncthreads();  // the row dots are in LDS
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int r = orow(m);
+        if (r >= L) continue;
+        // qh = q / sqrt(|q|^2 + eps): dq = rq (dqh - qh (qh . dqh))
+        io_st(dq + base + (size_t)r * rp + cc, s.rq[r] * fmaf(-qho[m], s.dotq[r], dqh[m]));
+        io_st(dk + base + (size_t)r * rp + cc, s.rk[r] * fmaf(-kho[m], s.dotk[r], dkh[m]));
+    }
 }
-
 }  // namespace
 
 size_t chunk_bwd_segment_bytes_per_chunk(int B, int H) {
     return (size_t)B * H *
-           (RF::BYTES + (2 * kStateFloats + (size_t)kChunk * kChunk + kScrFloats) * sizeof(float));
+           (RF::BYTES + (2 * kStateFloats + (size_t)kChunk * kChunk) * sizeof(float));
 }
 
 namespace {
 // Workspace of a segment of nch chunks: records, then the states entering the
-// chunks, the state gradients leaving them, X and the chunk kernels' scratch.
+// chunks, the state gradients leaving them and X.
 struct SegWs {
     uint8_t* rec;
-    float *states, *dsn, *xs, *scr;
+    float *states, *dsn, *xs;
     SegWs(void* ws, int B, int H, int nch) {
         const size_t n = (size_t)B * H * nch;
         rec = static_cast<uint8_t*>(ws);
         states = reinterpret_cast<float*>(rec + n * RF::BYTES);
         dsn = states + n * kStateFloats;
         xs = dsn + n * kStateFloats;
-        scr = xs + n * kChunk * kChunk;
     }
 };
 }  // namespace
@@ -956,7 +1173,7 @@ hipError_t launch_chunk_bwd_segment(const IO* q, const IO* k, const IO* v, const
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t n = (size_t)B * H * nch;
     hipLaunchKernelGGL(kda_bwd_chunk_kernel<IO>, dim3((unsigned)n), dim3(kCT), 0, stream, q, k, v,
-                       g, beta, dout, w.states, w.dsn, w.xs, w.scr, scale, T, H, chunk0, nch, dq,
+                       g, beta, dout, w.states, w.dsn, w.xs, scale, T, H, chunk0, nch, dq,
                        dk, dv, dg, dbeta);
     return hipGetLastError();
 }
