@@ -669,6 +669,15 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             s.n[row][col] = col <= row ? accn[u] : 0.f;
         }
     }
+    // the lane's own kh, qh and Gam, kept in registers to the end
+    float gmo[16], kho[16], qho[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int r = orow(m);
+        gmo[m] = A2[r][cc];
+        kho[m] = A0[r][cc];
+        qho[m] = A1[r][cc];
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = tid + kCT * j;
@@ -689,7 +698,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
 
     // ---- R = V - Kt S and dU = scale M^T dO + Kb dS' -------------------------
     // R starts from V, and the products add -Kt S
-    float Ro[16], dUo[16], gmo[16];
+    float Ro[16], dUo[16];
     {
         f32x4 aR[4], aU[4];
 #pragma unroll
@@ -730,10 +739,27 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         for (int m = 0; m < 16; ++m) {
             Ro[m] = aR[m >> 2][m & 3];
             dUo[m] = aU[m >> 2][m & 3];
-            gmo[m] = A2[orow(m)][cc];  // the lane's own Gam, kept to the end
         }
     }
-    __syncthreads();  // every read of Kt, Kb and Gam is done
+    __syncthreads();  // every read of Kt and Kb is done
+    // S and dS' as row strips (S[cc][*], dS'[cc][*]): the column strips pass
+    // through LDS, one matrix at a time, over the first two [64][132] arrays
+    float4 srow[8], drow[8];
+    {
+        float(*const SS)[kPB] = s.big[0];  // [128][132]
+#pragma unroll
+        for (int t = 0; t < 32; ++t) SS[16 * (t >> 2) + 4 * gq + (t & 3)][cc] = scol[t];
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) srow[kb] = ld4(&SS[cc][16 * kb + 4 * gq]);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 32; ++t) SS[16 * (t >> 2) + 4 * gq + (t & 3)][cc] = dcol[t];
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) drow[kb] = ld4(&SS[cc][16 * kb + 4 * gq]);
+        __syncthreads();
+    }
 
     // ---- U = T R and dV = dR = T^T dU, T = X diag(beta), from registers ------
     float dRo[16];
@@ -767,28 +793,6 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             A1[r][cc] = dUo[m];
             A2[r][cc] = aX[m >> 2][m & 3];
         }
-    }
-    // later B operands: the row strips S[cc][*] and dS'[cc][*]; and dO for staging
-    float4 srow[8], drow[8];
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        srow[kb] = ld4(S + (size_t)cc * kD + 16 * kb + 4 * gq);
-        drow[kb] = ld4(dSn + (size_t)cc * kD + 16 * kb + 4 * gq);
-    }
-    typename RW::four opf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid + kCT * j;
-        opf[j] = *reinterpret_cast<const typename RW::four*>(
-            dout + base + (size_t)crow(e >> 5) * rp + 4 * (e & 31));
-    }
-    // q and k at the lane's own slots, for its kh and qh in the element-wise part
-    typename RW::one kraw[16], qraw[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const size_t off = base + (size_t)crow(orow(m)) * rp + cc;
-        kraw[m] = k[off];
-        qraw[m] = q[off];
     }
     __syncthreads();  // R, dU and U are in LDS
 
@@ -826,11 +830,9 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) DX[16 * (rt0 + 2 * t) + 4 * gq + e][16 * ct + n] = dXo[4 * t + e];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid + kCT * j;
-        const int r = e >> 5;
-        *reinterpret_cast<float4*>(&A1[r][4 * (e & 31)]) =
-            r < L ? scale4(RW::wid(opf[j]), scale) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int m = 0; m < 16; ++m) {
+        const int r = orow(m);
+        A1[r][cc] = r < L ? scale * RW::wid(oraw[m]) : 0.f;
     }
     if (tid < kChunk) s.dbeta[tid] = s.red[tid] + s.red[kChunk + tid];
     __syncthreads();  // dX and scale dO are in LDS
@@ -920,13 +922,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     // dqh = e^Gam dQt, dkh = e^Gam dKt + e^(GL - Gam) dKb,
     // dGam = Qt dQt + Kt dKt - Kb dKb; the last row of dGam also gets
     // sum_r Kb dKb (per channel, pl)
-    float dqh[16], dkh[16], dgm[16], kho[16], qho[16], pl = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {  // the same products as the normalisation above
-        const int r = orow(m);
-        kho[m] = r < L ? RW::wid(kraw[m]) * s.rk[r] : 0.f;
-        qho[m] = r < L ? RW::wid(qraw[m]) * s.rq[r] : 0.f;
-    }
+    float dqh[16], dkh[16], dgm[16], pl = 0.f;
     // dgamma = rowsum(dS' . S) at the lane's channel: over its row strips, then
     // over the four lanes of the channel; the last row of dGam gets gamma dgamma
     float dlast;
