@@ -395,19 +395,22 @@ kda_status_t chunk_bwd(const IO* q, const IO* k, const IO* v, const float* g, co
     if (hipMallocFromPoolAsync(&ws, seg_bytes + extra, pool, stream) != hipSuccess)
         return KDA_ERR_NO_MEMORY;
     float* ckpt = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + seg_bytes);
+    kda::WaitCtl wait;
+    wait.abort_out = dbg.abort_word();
+    wait.spin_limit = dbg.spin_limit();
     float* dcarry = ckpt + (size_t)(nseg - 1) * sfloats;
     hipError_t e = hipSuccess;
     for (int sg = 0; sg + 1 < nseg && e == hipSuccess; ++sg)
         e = kda::launch_chunk_fwd_state<IO>(q, k, v, g, beta,
                                             sg == 0 ? h0 : ckpt + (size_t)(sg - 1) * sfloats,
                                             ckpt + (size_t)sg * sfloats, B, T, H, sg * seg, seg,
-                                            ws, stream);
+                                            ws, wait, stream);
     for (int sg = nseg - 1; sg >= 0 && e == hipSuccess; --sg) {
         const int c0 = sg * seg, n = nch - c0 < seg ? nch - c0 : seg;
         e = kda::launch_chunk_bwd_segment<IO>(
             q, k, v, g, beta, scale, sg == 0 ? h0 : ckpt + (size_t)(sg - 1) * sfloats, dout,
             sg == nseg - 1 ? dhT : dcarry, dq, dk, dv, dg, dbeta, sg == 0 ? dh0 : dcarry, B, T, H,
-            c0, n, ws, stream);
+            c0, n, ws, wait, stream);
     }
     (void)hipFreeAsync(ws, stream);
     if (e != hipSuccess) return KDA_ERR_HIP;

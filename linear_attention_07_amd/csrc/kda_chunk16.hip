@@ -570,9 +570,13 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     __shared__ u32x4 kq_s[Rec16::KB / 16];
     __shared__ u32x4 rest_s[2][kRest];
     __shared__ __align__(16) uint16_t v_s[kChunk * VP];    // V slice, [token][column]
-    // Kt/Qt/V ready; Kt/Qt/V consumed; rest ready; rest consumed; abort;
-    // output stored
-    __shared__ unsigned sync_s[6];
+    // Kt/Qt/V ready; Kt/Qt/V consumed; rest ready (per buffer, 2); abort;
+    // output stored; rest consumed (per buffer, 2).  The double-buffered rest
+    // needs a counter per buffer: waves of a role may be a chunk apart, and a
+    // shared counter would let one wave's signal for the later chunk stand in
+    // for another's for the earlier one.  The single Kt / Qt / V buffer keeps
+    // the roles in step by itself.
+    __shared__ unsigned sync_s[8];
 
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
     // both slices of a head go to one XCD, so the records that both read come
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
 
-    if (tid < 6) sync_s[tid] = 0u;
+    if (tid < 8) sync_s[tid] = 0u;
     __syncthreads();  // the only workgroup barrier: roles split below
 
     if (wv < 4) {
@@ -660,12 +664,12 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
         // beside the output stores hold those up).
         KDA_LOAD_ISSUE(0);
         for (int i = 0; i < nchunks; ++i) {
-            if (i >= 2) wait_for(&sync_s[3], 4u * (i - 1), &sync_s[4], wait.spin_limit);
+            wait_for(&sync_s[6 + (i & 1)], 4u * (unsigned)(i >> 1), &sync_s[4], wait.spin_limit);
             u32x4* rs = rest_s[i & 1];
 #pragma unroll
             for (int m = 0; m < kRestFull; ++m) rs[tid + 256 * m] = rb[m];
             if (tid < kRestTail) rs[tid + 256 * kRestFull] = rb[kRestFull];
-            signal(&sync_s[2], lane);
+            signal(&sync_s[2 + (i & 1)], lane);
             // V of the chunk, filtered before the wait below so that the
             // filter does not hold up the scan waves; tokens past the end of
             // the sequence have zero V
@@ -842,7 +846,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                 }
             }
             signal(&sync_s[1], lane);  // Kt, Qt, V consumed
-            wait_for(&sync_s[2], 4u * (i + 1), &sync_s[4], wait.spin_limit);
+            wait_for(&sync_s[2 + (i & 1)], 4u * (unsigned)((i >> 1) + 1), &sync_s[4], wait.spin_limit);
             const u32x4* rs = rest_s[i & 1];
             const u32x4* kb_s = rs;
             const u32x4* th_s = rs + (Rec16::TM - Rec16::KB + 0 * Rec16::kTM) / 16;
@@ -940,7 +944,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     }
                 }
             }
-            signal(&sync_s[3], lane);  // the rest consumed
+            signal(&sync_s[6 + (i & 1)], lane);  // the rest consumed
         }
         if (h_out) {
             float* ho = h_out + (size_t)bh * kD * kD;

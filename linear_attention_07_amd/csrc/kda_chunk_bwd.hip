@@ -35,8 +35,7 @@
 //         chunk's matrices from q, k, g, beta and writes dq, dk, dv, dg, dbeta.
 // Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
 // its operands in LDS or registers.
-#include <type_traits>
-
+#include "kda_bf16.hpp"
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -52,76 +51,10 @@ constexpr size_t kStateFloats = (size_t)kD * kD;
 
 __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// C[M][N] = sum_k A(i, k) B(k, j) on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32).  The operand functors return four values along k:
-// A4(i, k) = A(i, k .. k + 3), B4(k, j) = B(k .. k + 3, j).  The result is
-// cut into 16 x 16 tiles; wave w takes column tile w mod (N / 16) and every
-// (NT / 64) / (N / 16)-th row tile from w / (N / 16) on, so the B operand it
-// loads serves all its tiles and their loads are in flight together.  For a
-// tile at (i0, j0), lane (n = lane % 16, g = lane / 16) loads A(i0 + n, k0 +
-// 4g .. + 3) and B(k0 + 4g .. + 3, j0 + n); MFMA e of a 16-wide k block takes
-// value e of each, so lane (n, g) stands for k = k0 + 4g + e in both operands.
-// The accumulator holds C[i0 + 4g + e][j0 + n], handed to out(i, j, value).
-// K is a multiple of 16.
-template <int M, int N, int NT, class FA, class FB, class FO>
-__device__ __forceinline__ void mmf(int K, FA&& A4, FB&& B4, FO&& out) {
-    constexpr int TR = M / 16, TC = N / 16, W = NT / 64;
-    static_assert(M % 16 == 0 && N % 16 == 0 && NT % 64 == 0, "16 x 16 tiles, whole waves");
-    static_assert(W % TC == 0 && (TR * TC) % W == 0, "each wave keeps one column tile");
-    constexpr int RPW = TR * TC / W;  // row tiles per wave
-    constexpr int RSTEP = W / TC;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n = lane & 15, g = lane >> 4;
-    const int j0 = 16 * (w % TC), r0 = w / TC;
-    f32x4 acc[RPW];
-#pragma unroll
-    for (int u = 0; u < RPW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        const float4 b = B4(k0 + 4 * g, j0 + n);
-        float4 a[RPW];
-#pragma unroll
-        for (int u = 0; u < RPW; ++u) a[u] = A4(16 * (r0 + RSTEP * u) + n, k0 + 4 * g);
-#pragma unroll
-        for (int u = 0; u < RPW; ++u) {
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].x, b.x, acc[u], 0, 0, 0);
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].y, b.y, acc[u], 0, 0, 0);
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].z, b.z, acc[u], 0, 0, 0);
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].w, b.w, acc[u], 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < RPW; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * (r0 + RSTEP * u) + 4 * g + e;
-            // out(m, i, j, v) also gets the element's slot m = 4 u + e in the lane
-            if constexpr (std::is_invocable_v<FO, int, int, int, float>)
-                out(4 * u + e, i, j0 + n, acc[u][e]);
-            else
-                out(i, j0 + n, acc[u][e]);
-        }
-}
-
 __device__ __forceinline__ float4 ld4(const float* p) {
     return *reinterpret_cast<const float4*>(p);
 }
-// four values down a column of a row-major matrix
-__device__ __forceinline__ float4 col4(const float* p, size_t pitch) {
-    return make_float4(p[0], p[pitch], p[2 * pitch], p[3 * pitch]);
-}
-// q / k / v / dout in and dq / dk / dv out: fp32, or bf16 widened on load and
-// rounded to nearest even on store (8-byte aligned groups of four)
-__device__ __forceinline__ float io1(const float* p) { return *p; }
-__device__ __forceinline__ float io1(const uint16_t* p) { return bf2f(*p); }
-__device__ __forceinline__ float4 io4(const float* p) { return ld4(p); }
-__device__ __forceinline__ float4 io4(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__builtin_bit_cast(float, u.x << 16),
-                       __builtin_bit_cast(float, u.x & 0xffff0000u),
-                       __builtin_bit_cast(float, u.y << 16),
-                       __builtin_bit_cast(float, u.y & 0xffff0000u));
-}
+// dq / dk / dv out: fp32, or bf16 rounded to nearest even
 __device__ __forceinline__ void io_st(float* p, float x) { *p = x; }
 __device__ __forceinline__ void io_st(uint16_t* p, float x) { *p = f2bf(x); }
 
@@ -152,25 +85,99 @@ __device__ __forceinline__ void scan_ids(int& bh, int& slice) {
     }
 }
 
-// LDS row pitches of the staged record parts: four floats of padding per row,
-// so rows stay 16-byte aligned (float4 reads and writes) while the rows that a
-// wave reads at one k fall in different banks
-constexpr int kP64 = kChunk + 4;
-constexpr int kP128 = kD + 4;
+// ---------------------------------------------------------------------------
+// The two scans: one 512-thread workgroup per (b, h, 64 value columns), both
+// slices of a head on one XCD.  Their products run on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16) with every operand split into a bf16 pair, x =
+// hi + lo to about 2^-18 relative, and three products per pair (hi hi + hi lo
+// + lo hi): about 1e-5 relative per product, accumulated in fp32, with the
+// state (or its gradient) carried in fp32.
+//   Waves 0-3 (loaders) read each chunk's record from global memory, split it
+// and write it to LDS as k32 operand fragments: 16 rows x 32 k, 1 KB of hi
+// and 1 KB of lo, lane (n, g) of the reading wave at byte 16 (n + 16 g)
+// holding row n with k = k0 + 4 g + e (values 0..3) and k0 + 16 + 4 g + e
+// (values 4..7).  A matrix the products need with its other index as rows is
+// read column-wise from the record (64 consecutive floats per load across the
+// wave), so no transposition pass is needed.
+//   Waves 4-7 each keep a 128 x 16 fp32 slice (value columns j0 .. j0 + 15) in
+// registers as eight 16x16 accumulator tiles (rows 16 t + 4 g + e, column
+// j0 + n).  In that k order the tiles 2 s and 2 s + 1 are the B operand of
+// k32 block s, so the state and every product result feed the next product
+// from registers; V and dO come straight from global memory, a chunk ahead.
+//   The roles hand the fragments over through LDS counters, never through a
+// workgroup barrier.
+// ---------------------------------------------------------------------------
+
+using b16::mma;
+using b16::signal;
+using b16::split_b;
+using b16::wait_for;
+
+// Raw q / k / v / dout values, held in registers until they are used (widening
+// a bf16 value is an instruction, which would make the wave wait for the load
+// where it is placed).
+template <typename IO> struct RawIO;
+template <> struct RawIO<float> {
+    using one = float;
+    using four = float4;
+    static __device__ __forceinline__ float wid(float x) { return x; }
+    static __device__ __forceinline__ float4 wid(float4 x) { return x; }
+};
+template <> struct RawIO<uint16_t> {
+    using one = uint16_t;
+    using four = uint2;
+    static __device__ __forceinline__ float wid(uint16_t x) { return bf2f(x); }
+    static __device__ __forceinline__ float4 wid(uint2 u) {
+        return make_float4(__builtin_bit_cast(float, u.x << 16),
+                           __builtin_bit_cast(float, u.x & 0xffff0000u),
+                           __builtin_bit_cast(float, u.y << 16),
+                           __builtin_bit_cast(float, u.y & 0xffff0000u));
+    }
+};
+
+constexpr int kFragLanes = 64;  // u32x4 entries of one 1 KB fragment
+
+// Four values along k of fragment f at lane slot (n, g), half h (values 0..3
+// or 4..7): written as bf16 hi and lo into the two fragment arrays.
+__device__ __forceinline__ void put_frag(u32x4* hi, u32x4* lo, int f, int n, int g, int h,
+                                         float4 x) {
+    const float a[4] = {x.x, x.y, x.z, x.w};
+    uint2 vh, vl;
+    b16::split4(a, vh, vl);
+    reinterpret_cast<uint2*>(&hi[kFragLanes * f + n + 16 * g])[h] = vh;
+    reinterpret_cast<uint2*>(&lo[kFragLanes * f + n + 16 * g])[h] = vl;
+}
+__device__ __forceinline__ bf16x8 frag(const u32x4* base, int f, int lane) {
+    return __builtin_bit_cast(bf16x8, base[kFragLanes * f + lane]);
+}
+// acc += A B with both factors as hi / lo pairs
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+    acc = mma(acc, al, bh);
+    acc = mma(acc, ah, bl);
+    return mma(acc, ah, bh);
+}
+
+// The six nonzero k32 fragments of a lower-triangular [64][64] matrix (row
+// tile rt, k32 block s2): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+__host__ __device__ constexpr int tri_rt(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
+__host__ __device__ constexpr int tri_s2(int f) { return f < 2 ? 0 : (f - 2) & 1; }
 
 // ---------------------------------------------------------------------------
-// State scan: one workgroup per (b, h, 64 value columns).  For chunk c the
-// state slice entering it is stored, then S <- Diag(gamma) S + Kb^T (T V - W S).
-// Each chunk's record parts and V slice are first staged in LDS.
+// State scan: chunks in order.  For chunk c the state slice entering it is
+// stored, then Z = T V - W S and S <- Diag(gamma) S + Kb^T Z.  Each chunk's
+// fragments (W: rows token, k channel; T: rows token, k token; Kb^T: rows
+// channel, k token) and gamma sit in two LDS buffers by chunk parity, so the
+// loaders fill chunk i + 1 while chunk i is scanned.
 // ---------------------------------------------------------------------------
 struct __align__(16) StateScanLds {
-    float S[kD][kScanCols];
-    float Z[kChunk][kScanCols];
-    float Tm[kChunk * kP64];
-    float W[kChunk * kP128];
-    float KT[kD * kP64];
-    float V[kChunk][kScanCols];
-    float gam[kD];
+    u32x4 w[2][2][16 * kFragLanes];   // [buffer][hi, lo][fragment 4 rt + s]
+    u32x4 t[2][2][6 * kFragLanes];    // [buffer][hi, lo][fragment: tri_rt, tri_s2]
+    u32x4 kb[2][2][16 * kFragLanes];  // [buffer][hi, lo][fragment 2 rt + s2]
+    float gam[2][kD];
+    // per buffer: its chunks ready, its chunks consumed (+4 each); abort.  One
+    // counter per buffer: waves of a role may be a chunk apart, and a shared
+    // counter would let the later chunk's signals stand in for the earlier's.
+    unsigned sync[5];
 };
 
 // Chunks chunk0 .. chunk0 + nch - 1 of the sequence (records, states local to
@@ -178,125 +185,189 @@ struct __align__(16) StateScanLds {
 template <typename IO>
 __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
     const uint8_t* __restrict__ rec, const IO* __restrict__ v, const float* __restrict__ h0,
-    float* __restrict__ states, float* __restrict__ h_out, int T, int H, int chunk0, int nch) {
+    float* __restrict__ states, float* __restrict__ h_out, int T, int H, int chunk0, int nch,
+    WaitCtl wait) {
+    using RW = RawIO<IO>;
     __shared__ StateScanLds s;
     int bh, slice;
     scan_ids(bh, slice);
     const int b = bh / H, h = bh % H;
-    const int col0 = slice * kScanCols;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
-        const int i = e / kScanCols, j = e % kScanCols;
-        s.S[i][j] = h0 ? h0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
-    }
-    // The next chunk's record parts and V slice are loaded into registers while
-    // the current chunk computes: float4 number tid + 512 u of T (u < 2), W
-    // (u < 6), Kb^T (u < 10) and V (u < 12).
-    static_assert(kScanThreads == 512 && kScanCols == 64, "prefetch layout");
-    float4 pf[12];
-    float gpf = 0.f;
-    auto fetch = [&](int c) {
-        const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
-        const int cg = chunk0 + c;
-        const int L = min(kChunk, T - cg * kChunk);
-        const float* Tg = reinterpret_cast<const float*>(r + RF::TH);
-        const float* Wg = reinterpret_cast<const float*>(r + RF::W);
-        const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
-        const IO* Vg = v + (((size_t)b * T + (size_t)cg * kChunk) * H + h) * kD + col0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    unsigned* const ready = &s.sync[0];     // [buffer]
+    unsigned* const consumed = &s.sync[2];  // [buffer]
+    unsigned* const abort_w = &s.sync[4];
+    if (tid < 5) s.sync[tid] = 0u;
+    __syncthreads();  // the only workgroup barrier: roles split below
+
+    if (wv < 4) {
+        // ---- loaders: 16-byte pieces tid + 256 m of W (8), Kb^T (8), the
+        // nonzero T fragments (3) and gamma (threads < 32), a chunk ahead
+        static_assert(kScanThreads == 512, "four loader waves");
+        float4 rw[8], rk[8], rt[3], rg = make_float4(0.f, 0.f, 0.f, 0.f);
+        auto issue = [&](int c) {
+            const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
+            const float* Wg = reinterpret_cast<const float*>(r + RF::W);
+            const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
+            const float* Tg = reinterpret_cast<const float*>(r + RF::TH);
 #pragma unroll
-        for (int u = 0; u < 12; ++u) {
-            if (u < 2) {
-                const int e = tid + 512 * u;
-                pf[u] = ld4(Tg + (e >> 4) * kChunk + 4 * (e & 15));
-            } else if (u < 6) {
-                const int e = tid + 512 * (u - 2);
-                pf[u] = ld4(Wg + (e >> 5) * kD + 4 * (e & 31));
-            } else if (u < 10) {
-                const int e = tid + 512 * (u - 6);
-                pf[u] = ld4(Kg + (e >> 4) * kChunk + 4 * (e & 15));
-            } else {
-                const int e = tid + 512 * (u - 10), row = e >> 4;
-                pf[u] = row < L ? io4(Vg + (size_t)row * H * kD + 4 * (e & 15))
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m;
+                rw[m] = ld4(Wg + (p >> 5) * kD + 4 * (p & 31));
+                rk[m] = ld4(Kg + (p >> 4) * kChunk + 4 * (p & 15));
             }
-        }
-        if (tid < kD) gpf = reinterpret_cast<const float*>(r + RF::G)[tid];
-    };
-    auto put = [&]() {
 #pragma unroll
-        for (int u = 0; u < 12; ++u) {
-            float* d;
-            if (u < 2) {
-                const int e = tid + 512 * u;
-                d = &s.Tm[(e >> 4) * kP64 + 4 * (e & 15)];
-            } else if (u < 6) {
-                const int e = tid + 512 * (u - 2);
-                d = &s.W[(e >> 5) * kP128 + 4 * (e & 31)];
-            } else if (u < 10) {
-                const int e = tid + 512 * (u - 6);
-                d = &s.KT[(e >> 4) * kP64 + 4 * (e & 15)];
-            } else {
-                const int e = tid + 512 * (u - 10);
-                d = &s.V[e >> 4][4 * (e & 15)];
+            for (int m = 0; m < 3; ++m) {
+                const int p = tid + 256 * m, f = p >> 7, r16 = (p >> 3) & 15, q8 = p & 7;
+                rt[m] = ld4(Tg + (16 * tri_rt(f) + r16) * kChunk + 32 * tri_s2(f) + 4 * q8);
             }
-            *reinterpret_cast<float4*>(d) = pf[u];
+            if (tid < 32) rg = ld4(reinterpret_cast<const float*>(r + RF::G) + 4 * tid);
+        };
+        auto put = [&](int bf) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m;
+                {  // W: token i = p / 32, channels 4 cq ..
+                    const int i = p >> 5, cq = p & 31;
+                    put_frag(s.w[bf][0], s.w[bf][1], 4 * (i >> 4) + (cq >> 3), i & 15, cq & 3,
+                             (cq >> 2) & 1, rw[m]);
+                }
+                {  // Kb^T: channel ch = p / 16, tokens 4 tq ..
+                    const int ch = p >> 4, tq = p & 15;
+                    put_frag(s.kb[bf][0], s.kb[bf][1], 2 * (ch >> 4) + (tq >> 3), ch & 15, tq & 3,
+                             (tq >> 2) & 1, rk[m]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int p = tid + 256 * m, f = p >> 7, r16 = (p >> 3) & 15, q8 = p & 7;
+                put_frag(s.t[bf][0], s.t[bf][1], f, r16, q8 & 3, q8 >> 2, rt[m]);
+            }
+            if (tid < 32) *reinterpret_cast<float4*>(&s.gam[bf][4 * tid]) = rg;
+        };
+        // chunk i into buffer i & 1, free once chunk i - 2 (the buffer's
+        // previous chunk, its round i / 2 - 1) is consumed
+        issue(0);
+        for (int i = 0; i < nch; ++i) {
+            const int bf = i & 1;
+            wait_for(&consumed[bf], 4u * (unsigned)(i >> 1), abort_w, wait.spin_limit);
+            put(bf);
+            signal(&ready[bf], lane);
+            if (i + 1 < nch) issue(i + 1);
         }
-        if (tid < kD) s.gam[tid] = gpf;
-    };
-    fetch(0);
-    for (int c = 0; c < nch; ++c) {
-        __syncthreads();  // the previous chunk's reads of the staged parts are done
-        put();
-        float* st = states + ((size_t)bh * nch + c) * kStateFloats;
-        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
-            const int i = e / kScanCols, j = e % kScanCols;
-            st[(size_t)i * kD + col0 + j] = s.S[i][j];
+    } else {
+        // ---- scan waves
+        __builtin_amdgcn_s_setprio(3);
+        const int j0 = kScanCols * slice + 16 * (wv - 4);
+        f32x4 S[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[t][e] = h0 ? h0[(size_t)bh * kStateFloats + (size_t)(16 * t + 4 * gq + e) * kD + j0 + n]
+                             : 0.f;
+        // V at the lane's slots of a chunk (token 16 u + 4 gq + e, column j0 +
+        // n; rows past the sequence read a valid row and are zeroed on use)
+        typename RW::one vr[16];
+        auto vload = [&](int c) {
+            const int64_t t0 = (int64_t)(chunk0 + c) * kChunk;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                int64_t tk = t0 + 16 * (m >> 2) + 4 * gq + (m & 3);
+                tk = tk < T ? tk : T - 1;
+                vr[m] = v[(((int64_t)b * T + tk) * H + h) * kD + j0 + n];
+            }
+        };
+        vload(0);
+        for (int i = 0; i < nch; ++i) {
+            const int bf = i & 1;
+            const int64_t t0 = (int64_t)(chunk0 + i) * kChunk;
+            // V as hi / lo B operands (k32 block s2 = tiles 2 s2, 2 s2 + 1)
+            bf16x8 vh[2], vl[2];
+            {
+                f32x4 vt[4];
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    vt[m >> 2][m & 3] =
+                        t0 + 16 * (m >> 2) + 4 * gq + (m & 3) < T ? RW::wid(vr[m]) : 0.f;
+                split_b(vt[0], vt[1], vh[0], vl[0]);
+                split_b(vt[2], vt[3], vh[1], vl[1]);
+            }
+            if (i + 1 < nch) vload(i + 1);
+            float* st = states + ((size_t)bh * nch + i) * kStateFloats;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
+            bf16x8 sh[4], sl[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) split_b(S[2 * sb], S[2 * sb + 1], sh[sb], sl[sb]);
+            wait_for(&ready[bf], 4u * ((i >> 1) + 1), abort_w, wait.spin_limit);
+            // Z = T V - W S  (T lower triangular: six fragments)
+            f32x4 Z[4], P[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Z[rt] = P[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    P[rt] = mma3(P[rt], frag(s.w[bf][0], 4 * rt + sb, lane),
+                                 frag(s.w[bf][1], 4 * rt + sb, lane), sh[sb], sl[sb]);
+#pragma unroll
+            for (int f = 0; f < 6; ++f)
+                Z[tri_rt(f)] = mma3(Z[tri_rt(f)], frag(s.t[bf][0], f, lane),
+                                    frag(s.t[bf][1], f, lane), vh[tri_s2(f)], vl[tri_s2(f)]);
+            bf16x8 zh[2], zl[2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Z[rt] -= P[rt];
+            split_b(Z[0], Z[1], zh[0], zl[0]);
+            split_b(Z[2], Z[3], zh[1], zl[1]);
+            // S <- Diag(gamma) S + Kb^T Z
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                S[t] *= *reinterpret_cast<const f32x4*>(&s.gam[bf][16 * t + 4 * gq]);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    S[t] = mma3(S[t], frag(s.kb[bf][0], 2 * t + s2, lane),
+                                frag(s.kb[bf][1], 2 * t + s2, lane), zh[s2], zl[s2]);
+            }
+            signal(&consumed[bf], lane);
         }
-        __syncthreads();
-        if (c + 1 < nch) fetch(c + 1);
-        // Z = T V - W S
-        mmf<kChunk, kScanCols, kScanThreads>(
-            kChunk + kD,
-            [&](int i, int k) {
-                return k < kChunk ? ld4(&s.Tm[i * kP64 + k])
-                                  : scale4(ld4(&s.W[i * kP128 + (k - kChunk)]), -1.f);
-            },
-            [&](int k, int j) {
-                return k < kChunk ? col4(&s.V[k][j], kScanCols) : col4(&s.S[k - kChunk][j], kScanCols);
-            },
-            [&](int i, int j, float a) { s.Z[i][j] = a; });
-        __syncthreads();
-        // S' = Diag(gamma) S + Kb^T Z (each lane updates only its own entries)
-        mmf<kD, kScanCols, kScanThreads>(
-            kChunk, [&](int i, int k) { return ld4(&s.KT[i * kP64 + k]); },
-            [&](int k, int j) { return col4(&s.Z[k][j], kScanCols); },
-            [&](int i, int j, float a) { s.S[i][j] = fmaf(s.gam[i], s.S[i][j], a); });
+        if (h_out) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h_out[(size_t)bh * kStateFloats + (size_t)(16 * t + 4 * gq + e) * kD + j0 + n] =
+                        S[t][e];
+        }
     }
-    if (h_out) {
-        __syncthreads();
-        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
-            const int i = e / kScanCols, j = e % kScanCols;
-            h_out[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] = s.S[i][j];
-        }
-    }
+    // a wait of this wave (or of one that ended before) gave up: tell the host
+    if (wait.abort_out && lane == 0 &&
+        __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u)
+        wait.abort_out[0] = 1u;
 }
 
 // ---------------------------------------------------------------------------
 // Gradient scan: chunks in reverse.  For chunk c, dS' (the gradient of the
-// state leaving it) is stored, then
-//   dS <- Diag(gamma) dS' - W^T (Kb dS') + scale Q'^T dO.
-// After chunk 0, dS is the initial state's gradient.  Kb^T and then W take
-// turns in one LDS buffer.
+// state leaving it) is stored, then Y = Kb dS' and
+//   dS <- Diag(gamma) dS' - W^T Y + scale Q'^T dO.
+// After chunk 0, dS is the initial state's gradient.  The Kb fragments (rows
+// token, k channel; read column-wise from the Kb^T record) sit in two buffers
+// by chunk parity; -W^T and scale Q'^T (rows channel, k token; read
+// column-wise from the W and Q' records, sign and scale applied before the
+// split) and gamma in one, refilled while the next chunk forms Y.
 // ---------------------------------------------------------------------------
 struct __align__(16) GradScanLds {
-    float D[kD][kScanCols];
-    float Y[kChunk][kScanCols];
-    float KW[kD * kP64];  // Kb^T [128][64], then W [64][128] (at pitch kP128 it fits)
-    float QP[kChunk * kP128];
-    float O[kChunk][kScanCols];
+    u32x4 kb[2][2][16 * kFragLanes];  // [buffer][hi, lo][fragment 4 rt + s]
+    u32x4 wq[2][2][16 * kFragLanes];  // [-W^T, scale Q'^T][hi, lo][fragment 2 rt + s2]
     float gam[kD];
+    // Kb ready and Kb consumed per buffer, W / Q ready, W / Q consumed (+4 a
+    // chunk each), abort.  The double-buffered Kb needs a counter per buffer
+    // (waves of a role may be a chunk apart); the single W / Q buffer keeps
+    // the roles in step by itself.
+    unsigned sync[7];
 };
-static_assert(kD * kP64 >= kChunk * kP128, "W must fit in the Kb^T buffer");
 
 // Chunks chunk0 .. chunk0 + nch - 1 (records and dS' local to the segment):
 // dhT is the gradient of the state leaving the last of them, dh0 receives that
@@ -305,111 +376,168 @@ static_assert(kD * kP64 >= kChunk * kP128, "W must fit in the Kb^T buffer");
 template <typename IO>
 __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
     const uint8_t* __restrict__ rec, const IO* __restrict__ dout, const float* dhT,
-    float* __restrict__ dsn, float* dh0, float scale, int T, int H, int chunk0, int nch) {
+    float* __restrict__ dsn, float* dh0, float scale, int T, int H, int chunk0, int nch,
+    WaitCtl wait) {
+    using RW = RawIO<IO>;
     __shared__ GradScanLds s;
     int bh, slice;
     scan_ids(bh, slice);
     const int b = bh / H, h = bh % H;
-    const int col0 = slice * kScanCols;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
-        const int i = e / kScanCols, j = e % kScanCols;
-        s.D[i][j] = dhT ? dhT[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] : 0.f;
-    }
-    // The next chunk's record parts and dO slice are loaded into registers while
-    // the current chunk computes: float4 number tid + 512 u of Kb^T (u < 4),
-    // Q' (u < 8), dO (u < 10) and W (u < 14).
-    static_assert(kScanThreads == 512 && kScanCols == 64, "prefetch layout");
-    float4 pf[14];
-    float gpf = 0.f;
-    auto fetch = [&](int c) {
-        const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
-        const int cg = chunk0 + c;
-        const int L = min(kChunk, T - cg * kChunk);
-        const float* Kg = reinterpret_cast<const float*>(r + RF::KT);
-        const float* Qg = reinterpret_cast<const float*>(r + RF::QP);
-        const float* Wg = reinterpret_cast<const float*>(r + RF::W);
-        const IO* Og = dout + (((size_t)b * T + (size_t)cg * kChunk) * H + h) * kD + col0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    unsigned* const kb_ready = &s.sync[0];  // [buffer]
+    unsigned* const kb_done = &s.sync[2];   // [buffer]
+    unsigned* const wq_ready = &s.sync[4];
+    unsigned* const wq_done = &s.sync[5];
+    unsigned* const abort_w = &s.sync[6];
+    if (tid < 7) s.sync[tid] = 0u;
+    __syncthreads();  // the only workgroup barrier: roles split below
+
+    if (wv < 4) {
+        // ---- loaders: piece tid + 256 m (m < 8) of Kb (token p % 64, channels
+        // 4 (p / 64) ..) and of -W^T, scale Q'^T (channel p % 128, tokens
+        // 4 (p / 128) ..), four column-wise loads each; gamma (threads < 32)
+        float4 rk[8], rw[8], rq[8], rg = make_float4(0.f, 0.f, 0.f, 0.f);
+        auto issue_kb = [&](int c) {
+            const float* Kg = reinterpret_cast<const float*>(
+                rec + ((size_t)bh * nch + c) * RF::BYTES + RF::KT);
 #pragma unroll
-        for (int u = 0; u < 14; ++u) {
-            if (u < 4) {
-                const int e = tid + 512 * u;
-                pf[u] = ld4(Kg + (e >> 4) * kChunk + 4 * (e & 15));
-            } else if (u < 8) {
-                const int e = tid + 512 * (u - 4);
-                pf[u] = ld4(Qg + (e >> 5) * kD + 4 * (e & 31));
-            } else if (u < 10) {
-                const int e = tid + 512 * (u - 8), row = e >> 4;
-                pf[u] = row < L ? io4(Og + (size_t)row * H * kD + 4 * (e & 15))
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-            } else {
-                const int e = tid + 512 * (u - 10);
-                pf[u] = ld4(Wg + (e >> 5) * kD + 4 * (e & 31));
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, i = p & 63, c0 = 4 * (p >> 6);
+                rk[m] = make_float4(Kg[(c0 + 0) * kChunk + i], Kg[(c0 + 1) * kChunk + i],
+                                    Kg[(c0 + 2) * kChunk + i], Kg[(c0 + 3) * kChunk + i]);
             }
-        }
-        if (tid < kD) gpf = reinterpret_cast<const float*>(r + RF::G)[tid];
-    };
-    auto put4 = [&](float* d, float4 x) { *reinterpret_cast<float4*>(d) = x; };
-    auto put = [&]() {  // Kb^T, Q', dO and gamma
+        };
+        auto issue_wq = [&](int c) {
+            const uint8_t* r = rec + ((size_t)bh * nch + c) * RF::BYTES;
+            const float* Wg = reinterpret_cast<const float*>(r + RF::W);
+            const float* Qg = reinterpret_cast<const float*>(r + RF::QP);
 #pragma unroll
-        for (int u = 0; u < 10; ++u) {
-            if (u < 4) {
-                const int e = tid + 512 * u;
-                put4(&s.KW[(e >> 4) * kP64 + 4 * (e & 15)], pf[u]);
-            } else if (u < 8) {
-                const int e = tid + 512 * (u - 4);
-                put4(&s.QP[(e >> 5) * kP128 + 4 * (e & 31)], pf[u]);
-            } else {
-                const int e = tid + 512 * (u - 8);
-                put4(&s.O[e >> 4][4 * (e & 15)], pf[u]);
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, ch = p & 127, t0 = 4 * (p >> 7);
+                rw[m] = make_float4(Wg[(t0 + 0) * kD + ch], Wg[(t0 + 1) * kD + ch],
+                                    Wg[(t0 + 2) * kD + ch], Wg[(t0 + 3) * kD + ch]);
+                rq[m] = make_float4(Qg[(t0 + 0) * kD + ch], Qg[(t0 + 1) * kD + ch],
+                                    Qg[(t0 + 2) * kD + ch], Qg[(t0 + 3) * kD + ch]);
             }
-        }
-        if (tid < kD) s.gam[tid] = gpf;
-    };
-    auto put_w = [&]() {  // W, over Kb^T
+            if (tid < 32) rg = ld4(reinterpret_cast<const float*>(r + RF::G) + 4 * tid);
+        };
+        // chunk i (sequence chunk nch - 1 - i): Kb into buffer i & 1 once chunk
+        // i - 2 (the buffer's previous one) has formed its Y; -W^T, scale Q'^T
+        // and gamma once chunk i - 1 is done with them
+        issue_kb(nch - 1);
+        issue_wq(nch - 1);
+        for (int i = 0; i < nch; ++i) {
+            const int c = nch - 1 - i, bf = i & 1;
+            wait_for(&kb_done[bf], 4u * (unsigned)(i >> 1), abort_w, wait.spin_limit);
 #pragma unroll
-        for (int u = 10; u < 14; ++u) {
-            const int e = tid + 512 * (u - 10);
-            put4(&s.KW[(e >> 5) * kP128 + 4 * (e & 31)], pf[u]);
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, ti = p & 63, cq = p >> 6;
+                put_frag(s.kb[bf][0], s.kb[bf][1], 4 * (ti >> 4) + (cq >> 3), ti & 15, cq & 3,
+                         (cq >> 2) & 1, rk[m]);
+            }
+            signal(&kb_ready[bf], lane);
+            if (c > 0) issue_kb(c - 1);
+            if (i >= 1) wait_for(wq_done, 4u * i, abort_w, wait.spin_limit);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, ch = p & 127, tq = p >> 7;
+                const int f = 2 * (ch >> 4) + (tq >> 3);
+                put_frag(s.wq[0][0], s.wq[0][1], f, ch & 15, tq & 3, (tq >> 2) & 1,
+                         scale4(rw[m], -1.f));
+                put_frag(s.wq[1][0], s.wq[1][1], f, ch & 15, tq & 3, (tq >> 2) & 1,
+                         scale4(rq[m], scale));
+            }
+            if (tid < 32) *reinterpret_cast<float4*>(&s.gam[4 * tid]) = rg;
+            signal(wq_ready, lane);
+            if (c > 0) issue_wq(c - 1);
         }
-    };
-    fetch(nch - 1);
-    for (int c = nch - 1; c >= 0; --c) {
-        __syncthreads();  // the previous chunk's reads of the staged parts are done
-        put();
-        float* st = dsn + ((size_t)bh * nch + c) * kStateFloats;
-        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
-            const int i = e / kScanCols, j = e % kScanCols;
-            st[(size_t)i * kD + col0 + j] = s.D[i][j];
+    } else {
+        // ---- scan waves
+        __builtin_amdgcn_s_setprio(3);
+        const int j0 = kScanCols * slice + 16 * (wv - 4);
+        f32x4 D[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                D[t][e] = dhT ? dhT[(size_t)bh * kStateFloats + (size_t)(16 * t + 4 * gq + e) * kD + j0 + n]
+                              : 0.f;
+        typename RW::one orw[16];
+        auto oload = [&](int c) {
+            const int64_t t0 = (int64_t)(chunk0 + c) * kChunk;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                int64_t tk = t0 + 16 * (m >> 2) + 4 * gq + (m & 3);
+                tk = tk < T ? tk : T - 1;
+                orw[m] = dout[(((int64_t)b * T + tk) * H + h) * kD + j0 + n];
+            }
+        };
+        oload(nch - 1);
+        for (int i = 0; i < nch; ++i) {
+            const int c = nch - 1 - i, bf = i & 1;
+            const int64_t t0 = (int64_t)(chunk0 + c) * kChunk;
+            bf16x8 oh[2], ol[2];
+            {
+                f32x4 ot[4];
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    ot[m >> 2][m & 3] =
+                        t0 + 16 * (m >> 2) + 4 * gq + (m & 3) < T ? RW::wid(orw[m]) : 0.f;
+                split_b(ot[0], ot[1], oh[0], ol[0]);
+                split_b(ot[2], ot[3], oh[1], ol[1]);
+            }
+            if (c > 0) oload(c - 1);
+            float* st = dsn + ((size_t)bh * nch + c) * kStateFloats;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = D[t][e];
+            bf16x8 dh[4], dl[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) split_b(D[2 * sb], D[2 * sb + 1], dh[sb], dl[sb]);
+            // Y = Kb dS'
+            wait_for(&kb_ready[bf], 4u * ((i >> 1) + 1), abort_w, wait.spin_limit);
+            f32x4 Y[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Y[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    Y[rt] = mma3(Y[rt], frag(s.kb[bf][0], 4 * rt + sb, lane),
+                                 frag(s.kb[bf][1], 4 * rt + sb, lane), dh[sb], dl[sb]);
+            signal(&kb_done[bf], lane);
+            bf16x8 yh[2], yl[2];
+            split_b(Y[0], Y[1], yh[0], yl[0]);
+            split_b(Y[2], Y[3], yh[1], yl[1]);
+            // dS = Diag(gamma) dS' - W^T Y + scale Q'^T dO
+            wait_for(wq_ready, 4u * (i + 1), abort_w, wait.spin_limit);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                D[t] *= *reinterpret_cast<const f32x4*>(&s.gam[16 * t + 4 * gq]);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    D[t] = mma3(D[t], frag(s.wq[0][0], 2 * t + s2, lane),
+                                frag(s.wq[0][1], 2 * t + s2, lane), yh[s2], yl[s2]);
+                    D[t] = mma3(D[t], frag(s.wq[1][0], 2 * t + s2, lane),
+                                frag(s.wq[1][1], 2 * t + s2, lane), oh[s2], ol[s2]);
+                }
+            }
+            signal(wq_done, lane);
         }
-        __syncthreads();
-        // Y = Kb dS'   (Kb[i][k] = Kb^T[k][i])
-        mmf<kChunk, kScanCols, kScanThreads>(
-            kD, [&](int i, int k) { return col4(&s.KW[k * kP64 + i], kP64); },
-            [&](int k, int j) { return col4(&s.D[k][j], kScanCols); },
-            [&](int i, int j, float a) { s.Y[i][j] = a; });
-        __syncthreads();
-        put_w();
-        __syncthreads();
-        if (c > 0) fetch(c - 1);
-        // dS = Diag(gamma) dS' - W^T Y + scale Q'^T dO
-        mmf<kD, kScanCols, kScanThreads>(
-            2 * kChunk,
-            [&](int i, int k) {
-                return k < kChunk ? scale4(col4(&s.KW[k * kP128 + i], kP128), -1.f)
-                                  : scale4(col4(&s.QP[(k - kChunk) * kP128 + i], kP128), scale);
-            },
-            [&](int k, int j) {
-                return k < kChunk ? col4(&s.Y[k][j], kScanCols) : col4(&s.O[k - kChunk][j], kScanCols);
-            },
-            [&](int i, int j, float a) { s.D[i][j] = fmaf(s.gam[i], s.D[i][j], a); });
+        if (dh0) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dh0[(size_t)bh * kStateFloats + (size_t)(16 * t + 4 * gq + e) * kD + j0 + n] =
+                        D[t][e];
+        }
     }
-    __syncthreads();
-    if (dh0)
-        for (int e = tid; e < kD * kScanCols; e += kScanThreads) {
-            const int i = e / kScanCols, j = e % kScanCols;
-            dh0[(size_t)bh * kStateFloats + (size_t)i * kD + col0 + j] = s.D[i][j];
-        }
+    if (wait.abort_out && lane == 0 &&
+        __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u)
+        wait.abort_out[0] = 1u;
 }
 
 // ---------------------------------------------------------------------------
@@ -451,28 +579,6 @@ struct __align__(16) BwdLds {
     float red[8 * kD];  // partial sums
 };
 static_assert(kPS <= kPB, "dX, then Y, fit in one [64][128] array");
-
-// Raw q / k / v / dout values, held in registers until they are used (widening
-// a bf16 value is an instruction, which would make the wave wait for the load
-// where it is placed).
-template <typename IO> struct RawIO;
-template <> struct RawIO<float> {
-    using one = float;
-    using four = float4;
-    static __device__ __forceinline__ float wid(float x) { return x; }
-    static __device__ __forceinline__ float4 wid(float4 x) { return x; }
-};
-template <> struct RawIO<uint16_t> {
-    using one = uint16_t;
-    using four = uint2;
-    static __device__ __forceinline__ float wid(uint16_t x) { return bf2f(x); }
-    static __device__ __forceinline__ float4 wid(uint2 u) {
-        return make_float4(__builtin_bit_cast(float, u.x << 16),
-                           __builtin_bit_cast(float, u.x & 0xffff0000u),
-                           __builtin_bit_cast(float, u.y << 16),
-                           __builtin_bit_cast(float, u.y & 0xffff0000u));
-    }
-};
 
 // acc += A B over one 4-deep step per component: four fp32 MFMAs
 __device__ __forceinline__ void mfma4(f32x4& acc, float4 a, float4 b) {
@@ -1140,13 +1246,13 @@ template <typename IO>
 hipError_t launch_chunk_fwd_state(const IO* q, const IO* k, const IO* v, const float* g,
                                   const float* beta, const float* h_in, float* h_out, int B,
                                   int T, int H, int chunk0, int nch, void* ws,
-                                  hipStream_t stream) {
+                                  const WaitCtl& wait, hipStream_t stream) {
     const SegWs w(ws, B, H, nch);
     hipError_t e = launch_chunk_prep_f32(q, k, g, beta, B, T, H, chunk0, nch, w.rec, stream);
     if (e != hipSuccess) return e;
     const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
     hipLaunchKernelGGL(kda_bwd_state_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
-                       w.rec, v, h_in, w.states, h_out, T, H, chunk0, nch);
+                       w.rec, v, h_in, w.states, h_out, T, H, chunk0, nch, wait);
     return hipGetLastError();
 }
 
@@ -1155,17 +1261,18 @@ hipError_t launch_chunk_bwd_segment(const IO* q, const IO* k, const IO* v, const
                                     const float* beta, float scale, const float* h_in,
                                     const IO* dout, const float* dS_in, IO* dq, IO* dk, IO* dv,
                                     float* dg, float* dbeta, float* dS_out, int B, int T, int H,
-                                    int chunk0, int nch, void* ws, hipStream_t stream) {
+                                    int chunk0, int nch, void* ws, const WaitCtl& wait,
+                                    hipStream_t stream) {
     const SegWs w(ws, B, H, nch);
     hipError_t e =
         launch_chunk_prep_f32(q, k, g, beta, B, T, H, chunk0, nch, w.rec, stream, w.xs);
     if (e != hipSuccess) return e;
     const unsigned nscan = (unsigned)((int64_t)B * H * kScanSlices);
     hipLaunchKernelGGL(kda_bwd_state_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
-                       w.rec, v, h_in, w.states, nullptr, T, H, chunk0, nch);
+                       w.rec, v, h_in, w.states, nullptr, T, H, chunk0, nch, wait);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(kda_bwd_grad_scan_kernel<IO>, dim3(nscan), dim3(kScanThreads), 0, stream,
-                       w.rec, dout, dS_in, w.dsn, dS_out, scale, T, H, chunk0, nch);
+                       w.rec, dout, dS_in, w.dsn, dS_out, scale, T, H, chunk0, nch, wait);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t n = (size_t)B * H * nch;
     hipLaunchKernelGGL(kda_bwd_chunk_kernel<IO>, dim3((unsigned)n), dim3(kCT), 0, stream, q, k, v,
@@ -1178,11 +1285,11 @@ hipError_t launch_chunk_bwd_segment(const IO* q, const IO* k, const IO* v, const
     template hipError_t launch_chunk_fwd_state<IO>(const IO*, const IO*, const IO*,              \
                                                    const float*, const float*, const float*,     \
                                                    float*, int, int, int, int, int, void*,       \
-                                                   hipStream_t);                                 \
+                                                   const WaitCtl&, hipStream_t);                 \
     template hipError_t launch_chunk_bwd_segment<IO>(                                            \
         const IO*, const IO*, const IO*, const float*, const float*, float, const float*,        \
         const IO*, const float*, IO*, IO*, IO*, float*, float*, float*, int, int, int, int, int, \
-        void*, hipStream_t);
+        void*, const WaitCtl&, hipStream_t);
 KDA_INST_BWD(float)
 KDA_INST_BWD(uint16_t)
 #undef KDA_INST_BWD

@@ -57,6 +57,13 @@ hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_
                                  float* out, float scale, int B, int T, int H, int chunk0,
                                  int nchunks, hipStream_t stream);
 
+// The scans' bounded LDS waits: their spin limit, and where a wait that gives
+// up records it (NULL: nowhere).
+struct WaitCtl {
+    unsigned* abort_out = nullptr;
+    unsigned spin_limit = 1u << 23;
+};
+
 // Backward of the chunked prefill over one segment of chunks [chunk0, chunk0 +
 // nch): prep records, a forward scan storing the state entering each chunk
 // (from h_in, the state entering chunk0; NULL = zeros), a reverse scan storing
@@ -73,13 +80,14 @@ template <typename IO>
 hipError_t launch_chunk_fwd_state(const IO* q, const IO* k, const IO* v, const float* g,
                                   const float* beta, const float* h_in, float* h_out, int B,
                                   int T, int H, int chunk0, int nch, void* ws,
-                                  hipStream_t stream);
+                                  const WaitCtl& wait, hipStream_t stream);
 template <typename IO>
 hipError_t launch_chunk_bwd_segment(const IO* q, const IO* k, const IO* v, const float* g,
                                     const float* beta, float scale, const float* h_in,
                                     const IO* dout, const float* dS_in, IO* dq, IO* dk, IO* dv,
                                     float* dg, float* dbeta, float* dS_out, int B, int T, int H,
-                                    int chunk0, int nch, void* ws, hipStream_t stream);
+                                    int chunk0, int nch, void* ws, const WaitCtl& wait,
+                                    hipStream_t stream);
 
 // Short convolution in front of the attention: depthwise 4-tap causal filter
 // per head and channel, then SiLU, on q, k and v.  wq == NULL: none.  state:
@@ -102,12 +110,6 @@ struct ConvArgs {
 // h_out NULL = final state not stored).
 size_t chunk16_record_bytes();
 int chunk16_slices();
-// The scan's bounded LDS waits: their spin limit, and where a wait that gives
-// up records it (NULL: nowhere).
-struct WaitCtl {
-    unsigned* abort_out = nullptr;
-    unsigned spin_limit = 1u << 23;
-};
 hipError_t launch_prep16(const void* q, const void* k, const void* g, bool g_bf16,
                          const float* beta, int B, int T, int H, int chunk0, int nchunks, void* ws,
                          const ConvArgs& conv, hipStream_t stream);
