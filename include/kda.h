@@ -318,13 +318,15 @@ KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k
  * copies dhT (or zeros) to dh0.  Workspace comes from the library's
  * stream-ordered pool (KDA_ERR_NO_MEMORY if it cannot be had) and is bounded
  * by the budget, not by T: the chunk records, the state entering and the
- * state gradient leaving every chunk and per-chunk scratch (about 430 KB per
- * 64 tokens and head) are held for one segment of chunks at a time.  With more
+ * state gradient leaving every chunk (about 279 KB per 64 tokens and head)
+ * are held for one segment of chunks at a time.  With more
  * than one segment, a forward pass first keeps the state entering each
  * segment (64 KB per segment and head), and the segments are then
  * differentiated last to first, each recomputing its states from its
- * checkpoint.  Computed in fp32; g obeys the forward's bound (every entry in
- * [-5, 0]), which the chunk records that the two state scans read rely on.
+ * checkpoint.  Computed in fp32 (the two state scans' products as three bf16
+ * products of hi / lo pairs each, about 1e-5 relative per product, accumulated
+ * in fp32); g obeys the forward's bound (every entry in [-5, 0]), which the
+ * chunk records that the two state scans read rely on.
  */
 KDA_API kda_status_t kda_chunk_bwd_f32(const float *q, const float *k, const float *v,
                                const float *g, const float *beta, float scale,

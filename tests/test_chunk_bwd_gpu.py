@@ -206,8 +206,8 @@ def test_chunk_bwd_segmented_workspace(io, monkeypatch):
 
 
 def test_chunk_bwd_64k_in_a_fixed_budget():
-    """64K tokens x 96 heads (1024 chunks; about 43 GB of workspace in one
-    segment) inside the default 8 GB budget: six segments.  Two heads checked
+    """64K tokens x 96 heads (1024 chunks; about 27 GB of workspace in one
+    segment) inside the default 8 GB budget: four segments.  Two heads checked
     in full against the token-by-token oracle."""
     B, T, H = 1, 65536, 96
     say(f"chunk bwd case B={B} T={T} H={H} fp32, default budget")
