@@ -285,7 +285,7 @@ kda_status_t chunk_fwd(const void* q, const void* k, const void* v, const void* 
             e2 = e1 == hipSuccess
                      ? kda::launch_chunk_scan_f32(ws, static_cast<const float*>(v), h_in, h_out,
                                                   static_cast<float*>(out), scale, B, T, H, c0, n,
-                                                  stream)
+                                                  wait, stream)
                      : e1;
         }
         if (e2 != hipSuccess) {

@@ -95,5 +95,35 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, bf16x8 a, bf16x8 b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+// ---- k32 operand fragments held as bf16 hi / lo pairs in LDS -----------------
+// A fragment is 16 rows x 32 k: 1 KB of hi and 1 KB of lo, lane (n, g) of the
+// reading wave at u32x4 entry n + 16 g, holding row n with k = k0 + 4g + e
+// (values 0..3) and k0 + 16 + 4g + e (values 4..7).
+constexpr int kFragLanes = 64;  // u32x4 entries of one fragment
+
+// Four values along k of fragment f at lane slot (n, g), half h (values 0..3
+// or 4..7): written as bf16 hi and lo into the two fragment arrays.
+__device__ __forceinline__ void put_frag_hl(u32x4* hi, u32x4* lo, int f, int n, int g, int h,
+                                            float4 x) {
+    const float a[4] = {x.x, x.y, x.z, x.w};
+    uint2 vh, vl;
+    split4(a, vh, vl);
+    reinterpret_cast<uint2*>(&hi[kFragLanes * f + n + 16 * g])[h] = vh;
+    reinterpret_cast<uint2*>(&lo[kFragLanes * f + n + 16 * g])[h] = vl;
+}
+__device__ __forceinline__ bf16x8 frag_at(const u32x4* base, int f, int lane) {
+    return __builtin_bit_cast(bf16x8, base[kFragLanes * f + lane]);
+}
+// acc += A B with both factors as hi / lo pairs (lo hi + hi lo + hi hi)
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+    acc = mma(acc, al, bh);
+    acc = mma(acc, ah, bl);
+    return mma(acc, ah, bh);
+}
+// The six nonzero k32 fragments of a lower-triangular [64][64] matrix (row
+// tile rt, k32 block s2): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+__host__ __device__ constexpr int tri_rt(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
+__host__ __device__ constexpr int tri_s2(int f) { return f < 2 ? 0 : (f - 2) & 1; }
+
 }  // namespace b16
 }  // namespace kda

@@ -1,6 +1,7 @@
 // Chunkwise-parallel KDA prefill (the pages' chunk_kda) for fp32 q/k/v/o, in
-// fp32 arithmetic throughout (16x16x4 fp32 matrix-core products).  bf16 inputs
-// take the kernels of kda_chunk16.hip.
+// fp32 arithmetic (prep: 16x16x4 fp32 matrix-core products; scan: bf16
+// products of hi / lo pairs, fp32-like).  bf16 inputs take the kernels of
+// kda_chunk16.hip.
 //
 // The recurrence (Kimi-K3 深度解析 blog, section 三) is evaluated 64 tokens at a
 // time.  The chunk form below is an exact rearrangement of it; the blog's
@@ -31,16 +32,18 @@
 //                 5 each): finite in fp32 and bf16 because g >= -5.
 // Values that underflow are bounded by the true (tiny) products.
 //
-// Precision.  Every operand and every product is fp32 (the in-chunk inverse
-// included), so the result matches the recurrence to fp32 rounding.
+// Precision.  The prep's operands and products are fp32 (the in-chunk inverse
+// included).  The scan splits every operand into a bf16 hi + lo pair (x = hi +
+// lo to about 2^-18 relative) and takes three bf16 products per pair, about
+// 1e-5 relative per product, accumulated in fp32, with the state in fp32.
 //
 // Two kernels:
 //   prep (one workgroup per chunk, fully parallel) computes W, Q', Kb^T, T, MT
 //        and gamma from q, k, g, beta and writes them to a per-chunk record;
 //   scan (one workgroup per head and 64 value columns) walks the chunks in
-//        order with its slice of S in registers, on matrix cores, reading each
-//        record straight from global memory (this path serves small fp32
-//        problems).
+//        order with its slice of S in registers, on matrix cores, its loader
+//        waves staging each record in LDS as operand fragments.
+#include "kda_bf16.hpp"
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -55,32 +58,6 @@ using RecF = ChunkRecF32;
 
 constexpr int kScanSlices = 2;          // value-column slices per head
 constexpr int kSliceCols = kD / kScanSlices;
-constexpr int kScanThreads = 64 * (kSliceCols / 16);
-
-// k32 A-operand fragment of row `row` of a row-major matrix: values 0..3 carry
-// k = k0 + 4g + e, values 4..7 carry k = k0 + 16 + 4g + e.
-__device__ __forceinline__ F8 frag_row(const float* base, int pitch, int row, int k0, int gq) {
-    F8 f;
-    const float* p = base + (size_t)row * pitch + k0 + 4 * gq;
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 16);
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-}
-
-// k32 B-operand fragment of column `col` of a row-major [k][col] matrix, with
-// the same k order as frag_row.
-__device__ __forceinline__ F8 frag_col(const float* base, int pitch, int col, int k0, int gq) {
-    F8 f;
-    const float* p = base + (size_t)(k0 + 4 * gq) * pitch + col;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f.v[e] = p[(size_t)e * pitch];
-        f.v[4 + e] = p[(size_t)(16 + e) * pitch];
-    }
-    return f;
-}
 
 }  // namespace
 
@@ -435,23 +412,52 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (b, h, 64-column slice); wave w owns value columns
-// j0 = 64*slice + 16w .. +15 of the state, as eight 16x16 accumulator tiles
-// (key rows 16t + 4g + e, column j0 + n).  Chunks are visited in order.
-// k order of every k32 product here: values 0..3 of a lane carry k = k0 + 4g
-// + e, values 4..7 carry k = k0 + 16 + 4g + e, i.e. the rows of accumulator
-// tiles 2s and 2s+1 — so S and U feed the B operand straight from registers.
-// Each chunk's record is read from global memory directly; the V slice is
-// staged in LDS.
+// scan: one 512-thread workgroup per (b, h, 64-column slice), both slices of a
+// head on one XCD, chunks in order.  Its products run on the bf16 matrix cores
+// with both factors split into bf16 hi + lo pairs (x = hi + lo to about 2^-18
+// relative) and three products per pair: about 1e-5 relative per product,
+// accumulated in fp32, the state carried in fp32.
+//   Waves 0-3 (loaders) read each chunk's record, split it and write it to
+// LDS as k32 operand fragments (16 rows x 32 k; lane (n, g) of the reader at
+// entry n + 16 g holding row n with k = k0 + 4 g + e and k0 + 16 + 4 g + e):
+// W and Q' (rows token, k channel), T and MT (rows token, k token; their six
+// lower fragments), Kb^T (rows channel, k token) and gamma.  The first four
+// and the last two are handed over separately, each in one buffer: the first
+// four for chunk i + 1 are written while chunk i updates its state.
+//   Waves 4-7 each keep a 128 x 16 fp32 slice of the state (value columns
+// j0 .. j0 + 15) in registers as eight 16x16 accumulator tiles (rows 16 t +
+// 4 g + e, column j0 + n), which in that k order are also the B operand of
+// k32 block s = tiles 2 s, 2 s + 1; V comes straight from global memory a
+// chunk ahead, and O goes straight out:
+//   U = T V - W S,   O = scale (Q' S + MT V),   S <- Diag(gamma) S + Kb^T U.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
+constexpr int kScanThreads = 512;
+struct __align__(16) ScanLds {
+    u32x4 wq[2][2][16 * b16::kFragLanes];  // [W, Q'][hi, lo][fragment 4 rt + s]
+    u32x4 tm[2][2][6 * b16::kFragLanes];   // [T, MT][hi, lo][fragment: tri_rt, tri_s2]
+    u32x4 kb[2][16 * b16::kFragLanes];     // [hi, lo][fragment 2 rt + s2]
+    float gam[kD];
+    // first part ready, first part consumed, Kb^T ready, Kb^T consumed (+4 a
+    // chunk each; one buffer each, which keeps the roles in step), abort
+    unsigned sync[5];
+};
+
+__global__ __launch_bounds__(kScanThreads, 1) void kda_chunk_scan_kernel(
     const uint8_t* __restrict__ ws, const float* __restrict__ v, const float* h_in,
-    float* h_out, float* __restrict__ out, float scale, int T, int H, int chunk0, int nchunks) {
+    float* h_out, float* __restrict__ out, float scale, int T, int H, int chunk0, int nchunks,
+    WaitCtl wait) {
     using R = RecF;
+    using b16::frag_at;
+    using b16::mma3;
+    using b16::put_frag_hl;
+    using b16::split_b;
+    using b16::tri_rt;
+    using b16::tri_s2;
+    __shared__ ScanLds s;
 
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
-    // map ids so that all slices of one head sit on one XCD and the chunk
-    // records they all read are fetched from HBM once.
+    // both slices of a head go to one XCD, so the records both read come from
+    // HBM once.
     int slice, bh;
     {
         const int nblk = gridDim.x, id = blockIdx.x;
@@ -468,126 +474,186 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan_kernel(
     const int h = bh % H, b = bh / H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
-    const int c0 = kSliceCols * slice;       // first value column of the slice
-    const int jl = 16 * wv + n;              // this lane's column within the slice
-    const int j0 = c0 + 16 * wv;
+    unsigned* const a_ready = &s.sync[0];
+    unsigned* const a_done = &s.sync[1];
+    unsigned* const k_ready = &s.sync[2];
+    unsigned* const k_done = &s.sync[3];
+    unsigned* const abort_w = &s.sync[4];
+    if (tid < 5) s.sync[tid] = 0u;
+    __syncthreads();  // the only workgroup barrier: roles split below
 
-    constexpr int VP = kSliceCols + 8;
-    __shared__ float v_s[kChunk * VP];
-    __shared__ float gam_s[kD];
-
-    f32x4 S[8];
-    const float* hin = h_in ? h_in + (size_t)bh * kD * kD : nullptr;
+    if (wv < 4) {
+        // ---- loaders: 16-byte pieces tid + 256 m of W, Q' (8 each), the
+        // nonzero T and MT fragments (3 each), Kb^T (8) and gamma (threads < 32)
+        float4 rw[8], rq[8], rt[3], rm[3], rk[8], rg = make_float4(0.f, 0.f, 0.f, 0.f);
+        auto rec = [&](int cl) { return ws + ((size_t)bh * nchunks + cl) * R::BYTES; };
+        auto issue_a = [&](int cl) {
+            const float* Wg = reinterpret_cast<const float*>(rec(cl) + R::W);
+            const float* Qg = reinterpret_cast<const float*>(rec(cl) + R::QP);
+            const float* Tg = reinterpret_cast<const float*>(rec(cl) + R::TH);
+            const float* Mg = reinterpret_cast<const float*>(rec(cl) + R::MH);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
-
-    for (int cl = 0; cl < nchunks; ++cl) {
-        const int c = chunk0 + cl;
-        const uint8_t* rec = ws + ((size_t)bh * nchunks + cl) * R::BYTES;
-        const float* wp = reinterpret_cast<const float*>(rec + R::W);
-        const float* qpp = reinterpret_cast<const float*>(rec + R::QP);
-        const float* ktp = reinterpret_cast<const float*>(rec + R::KT);
-        const float* thp = reinterpret_cast<const float*>(rec + R::TH);
-        const float* mhp = reinterpret_cast<const float*>(rec + R::MH);
-        constexpr int ap = kD, kp = kChunk;
-        __syncthreads();
-        {
-            // V slice of this chunk (zero past the end of the sequence)
-            constexpr int VR = kSliceCols / 4;
-            for (int i = tid; i < kChunk * VR; i += kScanThreads) {
-                const int row = i / VR, cv = i % VR;
-                const int64_t tok = (int64_t)c * kChunk + row;
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (tok < T)
-                    val = *reinterpret_cast<const u32x4*>(
-                        v + (((int64_t)b * T + tok) * H + h) * kD + c0 + cv * 4);
-                *reinterpret_cast<u32x4*>(&v_s[row * VP + cv * 4]) = val;
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, off = (p >> 5) * kD + 4 * (p & 31);
+                rw[m] = *reinterpret_cast<const float4*>(Wg + off);
+                rq[m] = *reinterpret_cast<const float4*>(Qg + off);
             }
-            if (tid < kD) gam_s[tid] = reinterpret_cast<const float*>(rec + R::G)[tid];
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int p = tid + 256 * m, f = p >> 7, r16 = (p >> 3) & 15, q8 = p & 7;
+                const int off = (16 * tri_rt(f) + r16) * kChunk + 32 * tri_s2(f) + 4 * q8;
+                rt[m] = *reinterpret_cast<const float4*>(Tg + off);
+                rm[m] = *reinterpret_cast<const float4*>(Mg + off);
+            }
+        };
+        auto issue_k = [&](int cl) {
+            const float* Kg = reinterpret_cast<const float*>(rec(cl) + R::KT);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m;
+                rk[m] = *reinterpret_cast<const float4*>(Kg + (p >> 4) * kChunk + 4 * (p & 15));
+            }
+            if (tid < 32)
+                rg = *reinterpret_cast<const float4*>(
+                    reinterpret_cast<const float*>(rec(cl) + R::G) + 4 * tid);
+        };
+        issue_a(0);
+        issue_k(0);
+        for (int i = 0; i < nchunks; ++i) {
+            // W, Q', T, MT once chunk i - 1 has multiplied them
+            if (i >= 1) b16::wait_for(a_done, 4u * i, abort_w, wait.spin_limit);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, ti = p >> 5, cq = p & 31;
+                const int f = 4 * (ti >> 4) + (cq >> 3);
+                put_frag_hl(s.wq[0][0], s.wq[0][1], f, ti & 15, cq & 3, (cq >> 2) & 1, rw[m]);
+                put_frag_hl(s.wq[1][0], s.wq[1][1], f, ti & 15, cq & 3, (cq >> 2) & 1, rq[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int p = tid + 256 * m, f = p >> 7, r16 = (p >> 3) & 15, q8 = p & 7;
+                put_frag_hl(s.tm[0][0], s.tm[0][1], f, r16, q8 & 3, q8 >> 2, rt[m]);
+                put_frag_hl(s.tm[1][0], s.tm[1][1], f, r16, q8 & 3, q8 >> 2, rm[m]);
+            }
+            b16::signal(a_ready, lane);
+            if (i + 1 < nchunks) issue_a(i + 1);
+            // Kb^T and gamma once chunk i - 1 has updated its state
+            if (i >= 1) b16::wait_for(k_done, 4u * i, abort_w, wait.spin_limit);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int p = tid + 256 * m, ch = p >> 4, tq = p & 15;
+                put_frag_hl(s.kb[0], s.kb[1], 2 * (ch >> 4) + (tq >> 3), ch & 15, tq & 3,
+                            (tq >> 2) & 1, rk[m]);
+            }
+            if (tid < 32) *reinterpret_cast<float4*>(&s.gam[4 * tid]) = rg;
+            b16::signal(k_ready, lane);
+            if (i + 1 < nchunks) issue_k(i + 1);
         }
-        __syncthreads();
-
-        // S-independent: Ut = T V and Oh = MT V for this wave's 16 columns
-        f32x4 Ut[4], Oh[4];
-        {
-            const F8 vb0 = frag_col(v_s, VP, jl, 0, gq);
-            const F8 vb1 = frag_col(v_s, VP, jl, 32, gq);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 u = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
-                const int row = 16 * rt + n;
-                u = P::mma32(u, frag_row(thp, kp, row, 0, gq), vb0);
-                o = P::mma32(o, frag_row(mhp, kp, row, 0, gq), vb0);
-                if (rt >= 2) {
-                    u = P::mma32(u, frag_row(thp, kp, row, 32, gq), vb1);
-                    o = P::mma32(o, frag_row(mhp, kp, row, 32, gq), vb1);
-                }
-                Ut[rt] = u;
-                Oh[rt] = o;
-            }
-        }
-
-        // Pm = [W; Q'] S   (8 row tiles of 16 tokens x this wave's 16 columns)
-        f32x4 Pm[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) Pm[i] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const F8 bS = P::pack8(S[2 * s], S[2 * s + 1]);
-            F8 fw[4], fq[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                fw[rt] = frag_row(wp, ap, 16 * rt + n, 32 * s, gq);
-                fq[rt] = frag_row(qpp, ap, 16 * rt + n, 32 * s, gq);
-            }
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                Pm[rt] = P::mma32(Pm[rt], fw[rt], bS);
-                Pm[4 + rt] = P::mma32(Pm[4 + rt], fq[rt], bS);
-            }
-        }
-
-        // U = T V - W S ;  O = scale (Q' S + MT V)
-        f32x4 U[4];
-        const bool full = (int64_t)(c + 1) * kChunk <= T;
-        auto* outc = out + (((int64_t)b * T + (int64_t)c * kChunk) * H + h) * kD + j0 + n;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            U[rt] = Ut[rt] - Pm[rt];
-            const f32x4 o = Pm[4 + rt] + Oh[rt];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * rt + 4 * gq + e;
-                if (full || (int64_t)c * kChunk + row < T)
-                    outc[(int64_t)row * H * kD] = scale * o[e];
-            }
-        }
-
-        // S <- Diag(gamma) S + Kb^T U
-        F8 bU[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) bU[s2] = P::pack8(U[2 * s2], U[2 * s2 + 1]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[t][e] *= gam_s[16 * t + 4 * gq + e];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                S[t] = P::mma32(S[t], frag_row(ktp, kp, 16 * t + n, 32 * s2, gq), bU[s2]);
-            }
-        }
-    }
-
-    if (h_out) {
-        float* ho = h_out + (size_t)bh * kD * kD;
+    } else {
+        // ---- scan waves
+        __builtin_amdgcn_s_setprio(3);
+        const int j0 = kSliceCols * slice + 16 * (wv - 4);
+        f32x4 S[8];
+        const float* hin = h_in ? h_in + (size_t)bh * kD * kD : nullptr;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
+            for (int e = 0; e < 4; ++e)
+                S[t][e] = hin ? hin[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] : 0.f;
+        // V at the lane's slots of a chunk (token 16 u + 4 gq + e, column j0 +
+        // n; rows past the sequence read a valid row and are zeroed on use)
+        float vr[16];
+        const int64_t rstride = (int64_t)H * kD;
+        const float* vbase = v + ((int64_t)b * T * H + h) * kD + j0 + n;
+        auto vload = [&](int cl) {
+            const int64_t t0 = (int64_t)(chunk0 + cl) * kChunk;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                int64_t tk = t0 + 16 * (m >> 2) + 4 * gq + (m & 3);
+                tk = tk < T ? tk : T - 1;
+                vr[m] = vbase[tk * rstride];
+            }
+        };
+        vload(0);
+        for (int i = 0; i < nchunks; ++i) {
+            const int64_t t0 = (int64_t)(chunk0 + i) * kChunk;
+            bf16x8 vh[2], vl[2];
+            {
+                f32x4 vt[4];
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    vt[m >> 2][m & 3] = t0 + 16 * (m >> 2) + 4 * gq + (m & 3) < T ? vr[m] : 0.f;
+                split_b(vt[0], vt[1], vh[0], vl[0]);
+                split_b(vt[2], vt[3], vh[1], vl[1]);
+            }
+            if (i + 1 < nchunks) vload(i + 1);
+            bf16x8 sh[4], sl[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) split_b(S[2 * sb], S[2 * sb + 1], sh[sb], sl[sb]);
+            b16::wait_for(a_ready, 4u * (i + 1), abort_w, wait.spin_limit);
+            // P = W S (rows 0..3) and Q' S (rows 4..7); TV and MT V
+            f32x4 Pm[8], Tv[4], Mv[4];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) Pm[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tv[r] = Mv[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+                        Pm[4 * x + rt] =
+                            mma3(Pm[4 * x + rt], frag_at(s.wq[x][0], 4 * rt + sb, lane),
+                                 frag_at(s.wq[x][1], 4 * rt + sb, lane), sh[sb], sl[sb]);
+#pragma unroll
+            for (int f = 0; f < 6; ++f) {
+                Tv[tri_rt(f)] = mma3(Tv[tri_rt(f)], frag_at(s.tm[0][0], f, lane),
+                                     frag_at(s.tm[0][1], f, lane), vh[tri_s2(f)], vl[tri_s2(f)]);
+                Mv[tri_rt(f)] = mma3(Mv[tri_rt(f)], frag_at(s.tm[1][0], f, lane),
+                                     frag_at(s.tm[1][1], f, lane), vh[tri_s2(f)], vl[tri_s2(f)]);
+            }
+            b16::signal(a_done, lane);
+            // U = T V - W S as hi / lo; O = scale (Q' S + MT V)
+            bf16x8 uh[2], ul[2];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Tv[rt] -= Pm[rt];
+            split_b(Tv[0], Tv[1], uh[0], ul[0]);
+            split_b(Tv[2], Tv[3], uh[1], ul[1]);
+            float* outc = out + ((int64_t)b * T * H + h) * kD + j0 + n;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 o = scale * (Pm[4 + rt] + Mv[rt]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t tk = t0 + 16 * rt + 4 * gq + e;
+                    if (tk < T) outc[tk * rstride] = o[e];
+                }
+            }
+            // S <- Diag(gamma) S + Kb^T U
+            b16::wait_for(k_ready, 4u * (i + 1), abort_w, wait.spin_limit);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                S[t] *= *reinterpret_cast<const f32x4*>(&s.gam[16 * t + 4 * gq]);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    S[t] = mma3(S[t], frag_at(s.kb[0], 2 * t + s2, lane),
+                                frag_at(s.kb[1], 2 * t + s2, lane), uh[s2], ul[s2]);
+            }
+            b16::signal(k_done, lane);
+        }
+        if (h_out) {
+            float* ho = h_out + (size_t)bh * kD * kD;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ho[(size_t)(16 * t + 4 * gq + e) * kD + j0 + n] = S[t][e];
+        }
     }
+    // a wait of this wave (or of one that ended before) gave up: tell the host
+    if (wait.abort_out && lane == 0 &&
+        __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u)
+        wait.abort_out[0] = 1u;
 }
 
 hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
@@ -610,11 +676,11 @@ hipError_t launch_chunk_prep_f32(const uint16_t* q, const uint16_t* k, const flo
 
 hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
                                  float* out, float scale, int B, int T, int H, int chunk0,
-                                 int nchunks, hipStream_t stream) {
+                                 int nchunks, const WaitCtl& wait, hipStream_t stream) {
     const unsigned nblk = (unsigned)((int64_t)B * H * kScanSlices);
     hipLaunchKernelGGL(kda_chunk_scan_kernel, dim3(nblk), dim3(kScanThreads), 0, stream,
                        static_cast<const uint8_t*>(ws), v, h_in, h_out, out, scale, T, H, chunk0,
-                       nchunks);
+                       nchunks, wait);
     return hipGetLastError();
 }
 

@@ -112,6 +112,10 @@ using b16::mma;
 using b16::signal;
 using b16::split_b;
 using b16::wait_for;
+using b16::kFragLanes;
+using b16::mma3;
+using b16::tri_rt;
+using b16::tri_s2;
 
 // Raw q / k / v / dout values, held in registers until they are used (widening
 // a bf16 value is an instruction, which would make the wave wait for the load
@@ -134,33 +138,6 @@ template <> struct RawIO<uint16_t> {
                            __builtin_bit_cast(float, u.y & 0xffff0000u));
     }
 };
-
-constexpr int kFragLanes = 64;  // u32x4 entries of one 1 KB fragment
-
-// Four values along k of fragment f at lane slot (n, g), half h (values 0..3
-// or 4..7): written as bf16 hi and lo into the two fragment arrays.
-__device__ __forceinline__ void put_frag(u32x4* hi, u32x4* lo, int f, int n, int g, int h,
-                                         float4 x) {
-    const float a[4] = {x.x, x.y, x.z, x.w};
-    uint2 vh, vl;
-    b16::split4(a, vh, vl);
-    reinterpret_cast<uint2*>(&hi[kFragLanes * f + n + 16 * g])[h] = vh;
-    reinterpret_cast<uint2*>(&lo[kFragLanes * f + n + 16 * g])[h] = vl;
-}
-__device__ __forceinline__ bf16x8 frag(const u32x4* base, int f, int lane) {
-    return __builtin_bit_cast(bf16x8, base[kFragLanes * f + lane]);
-}
-// acc += A B with both factors as hi / lo pairs
-__device__ __forceinline__ f32x4 mma3(f32x4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
-    acc = mma(acc, al, bh);
-    acc = mma(acc, ah, bl);
-    return mma(acc, ah, bh);
-}
-
-// The six nonzero k32 fragments of a lower-triangular [64][64] matrix (row
-// tile rt, k32 block s2): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-__host__ __device__ constexpr int tri_rt(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
-__host__ __device__ constexpr int tri_s2(int f) { return f < 2 ? 0 : (f - 2) & 1; }
 
 // ---------------------------------------------------------------------------
 // State scan: chunks in order.  For chunk c the state slice entering it is
@@ -229,19 +206,19 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
                 const int p = tid + 256 * m;
                 {  // W: token i = p / 32, channels 4 cq ..
                     const int i = p >> 5, cq = p & 31;
-                    put_frag(s.w[bf][0], s.w[bf][1], 4 * (i >> 4) + (cq >> 3), i & 15, cq & 3,
+                    b16::put_frag_hl(s.w[bf][0], s.w[bf][1], 4 * (i >> 4) + (cq >> 3), i & 15, cq & 3,
                              (cq >> 2) & 1, rw[m]);
                 }
                 {  // Kb^T: channel ch = p / 16, tokens 4 tq ..
                     const int ch = p >> 4, tq = p & 15;
-                    put_frag(s.kb[bf][0], s.kb[bf][1], 2 * (ch >> 4) + (tq >> 3), ch & 15, tq & 3,
+                    b16::put_frag_hl(s.kb[bf][0], s.kb[bf][1], 2 * (ch >> 4) + (tq >> 3), ch & 15, tq & 3,
                              (tq >> 2) & 1, rk[m]);
                 }
             }
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
                 const int p = tid + 256 * m, f = p >> 7, r16 = (p >> 3) & 15, q8 = p & 7;
-                put_frag(s.t[bf][0], s.t[bf][1], f, r16, q8 & 3, q8 >> 2, rt[m]);
+                b16::put_frag_hl(s.t[bf][0], s.t[bf][1], f, r16, q8 & 3, q8 >> 2, rt[m]);
             }
             if (tid < 32) *reinterpret_cast<float4*>(&s.gam[bf][4 * tid]) = rg;
         };
@@ -311,12 +288,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
             for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
-                    P[rt] = mma3(P[rt], frag(s.w[bf][0], 4 * rt + sb, lane),
-                                 frag(s.w[bf][1], 4 * rt + sb, lane), sh[sb], sl[sb]);
+                    P[rt] = mma3(P[rt], b16::frag_at(s.w[bf][0], 4 * rt + sb, lane),
+                                 b16::frag_at(s.w[bf][1], 4 * rt + sb, lane), sh[sb], sl[sb]);
 #pragma unroll
             for (int f = 0; f < 6; ++f)
-                Z[tri_rt(f)] = mma3(Z[tri_rt(f)], frag(s.t[bf][0], f, lane),
-                                    frag(s.t[bf][1], f, lane), vh[tri_s2(f)], vl[tri_s2(f)]);
+                Z[tri_rt(f)] = mma3(Z[tri_rt(f)], b16::frag_at(s.t[bf][0], f, lane),
+                                    b16::frag_at(s.t[bf][1], f, lane), vh[tri_s2(f)], vl[tri_s2(f)]);
             bf16x8 zh[2], zl[2];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) Z[rt] -= P[rt];
@@ -328,8 +305,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_state_scan_kernel(
                 S[t] *= *reinterpret_cast<const f32x4*>(&s.gam[bf][16 * t + 4 * gq]);
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
-                    S[t] = mma3(S[t], frag(s.kb[bf][0], 2 * t + s2, lane),
-                                frag(s.kb[bf][1], 2 * t + s2, lane), zh[s2], zl[s2]);
+                    S[t] = mma3(S[t], b16::frag_at(s.kb[bf][0], 2 * t + s2, lane),
+                                b16::frag_at(s.kb[bf][1], 2 * t + s2, lane), zh[s2], zl[s2]);
             }
             signal(&consumed[bf], lane);
         }
@@ -433,7 +410,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int p = tid + 256 * m, ti = p & 63, cq = p >> 6;
-                put_frag(s.kb[bf][0], s.kb[bf][1], 4 * (ti >> 4) + (cq >> 3), ti & 15, cq & 3,
+                b16::put_frag_hl(s.kb[bf][0], s.kb[bf][1], 4 * (ti >> 4) + (cq >> 3), ti & 15, cq & 3,
                          (cq >> 2) & 1, rk[m]);
             }
             signal(&kb_ready[bf], lane);
@@ -443,9 +420,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
             for (int m = 0; m < 8; ++m) {
                 const int p = tid + 256 * m, ch = p & 127, tq = p >> 7;
                 const int f = 2 * (ch >> 4) + (tq >> 3);
-                put_frag(s.wq[0][0], s.wq[0][1], f, ch & 15, tq & 3, (tq >> 2) & 1,
+                b16::put_frag_hl(s.wq[0][0], s.wq[0][1], f, ch & 15, tq & 3, (tq >> 2) & 1,
                          scale4(rw[m], -1.f));
-                put_frag(s.wq[1][0], s.wq[1][1], f, ch & 15, tq & 3, (tq >> 2) & 1,
+                b16::put_frag_hl(s.wq[1][0], s.wq[1][1], f, ch & 15, tq & 3, (tq >> 2) & 1,
                          scale4(rq[m], scale));
             }
             if (tid < 32) *reinterpret_cast<float4*>(&s.gam[4 * tid]) = rg;
@@ -505,8 +482,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
             for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
-                    Y[rt] = mma3(Y[rt], frag(s.kb[bf][0], 4 * rt + sb, lane),
-                                 frag(s.kb[bf][1], 4 * rt + sb, lane), dh[sb], dl[sb]);
+                    Y[rt] = mma3(Y[rt], b16::frag_at(s.kb[bf][0], 4 * rt + sb, lane),
+                                 b16::frag_at(s.kb[bf][1], 4 * rt + sb, lane), dh[sb], dl[sb]);
             signal(&kb_done[bf], lane);
             bf16x8 yh[2], yl[2];
             split_b(Y[0], Y[1], yh[0], yl[0]);
@@ -518,10 +495,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
                 D[t] *= *reinterpret_cast<const f32x4*>(&s.gam[16 * t + 4 * gq]);
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    D[t] = mma3(D[t], frag(s.wq[0][0], 2 * t + s2, lane),
-                                frag(s.wq[0][1], 2 * t + s2, lane), yh[s2], yl[s2]);
-                    D[t] = mma3(D[t], frag(s.wq[1][0], 2 * t + s2, lane),
-                                frag(s.wq[1][1], 2 * t + s2, lane), oh[s2], ol[s2]);
+                    D[t] = mma3(D[t], b16::frag_at(s.wq[0][0], 2 * t + s2, lane),
+                                b16::frag_at(s.wq[0][1], 2 * t + s2, lane), yh[s2], yl[s2]);
+                    D[t] = mma3(D[t], b16::frag_at(s.wq[1][0], 2 * t + s2, lane),
+                                b16::frag_at(s.wq[1][1], 2 * t + s2, lane), oh[s2], ol[s2]);
                 }
             }
             signal(wq_done, lane);

@@ -53,9 +53,7 @@ hipError_t launch_chunk_prep_f32(const float* q, const float* k, const float* g,
 hipError_t launch_chunk_prep_f32(const uint16_t* q, const uint16_t* k, const float* g,
                                  const float* beta, int B, int T, int H, int chunk0, int nchunks,
                                  void* ws, hipStream_t stream, float* x_out = nullptr);
-hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
-                                 float* out, float scale, int B, int T, int H, int chunk0,
-                                 int nchunks, hipStream_t stream);
+
 
 // The scans' bounded LDS waits: their spin limit, and where a wait that gives
 // up records it (NULL: nowhere).
@@ -63,6 +61,10 @@ struct WaitCtl {
     unsigned* abort_out = nullptr;
     unsigned spin_limit = 1u << 23;
 };
+
+hipError_t launch_chunk_scan_f32(const void* ws, const float* v, const float* h_in, float* h_out,
+                                 float* out, float scale, int B, int T, int H, int chunk0,
+                                 int nchunks, const WaitCtl& wait, hipStream_t stream);
 
 // Backward of the chunked prefill over one segment of chunks [chunk0, chunk0 +
 // nch): prep records, a forward scan storing the state entering each chunk
