@@ -72,7 +72,7 @@ int chunk_f32_slices() { return kScanSlices; }
 // ---------------------------------------------------------------------------
 // IO: float, or uint16_t for bf16 q and k (the backward of the bf16 prefill)
 template <typename IO>
-__global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
+__global__ __launch_bounds__(256, 2) void kda_chunk_prep_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, int T, int H, int chunk0, int nchunks,
     uint8_t* __restrict__ ws, float* __restrict__ x_out) {
@@ -100,14 +100,22 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
     const int64_t rowoff = (((int64_t)b * T + tok) * H + h) * kD;
 
     constexpr int SP = kChunk + 1;   // fp32 pitch of the 64 x 64 matrices
-    constexpr int KTP = kD + 8;      // pitch of the Kt rows (st elements)
+    constexpr int KTP = kD + 4;      // pitch of the Kt rows (st elements)
     constexpr int MWP = kD + 4;      // fp32 pitch of the M W rows
     constexpr size_t kZfBytes = sizeof(F8) * 4 * 4 * 64;
     constexpr size_t kXBytes = sizeof(float) * kChunk * SP;
     constexpr size_t kKtBytes = (sizeof(st) * kChunk * KTP + 15) / 16 * 16;
     constexpr size_t kABytes = sizeof(float) * kChunk * SP;
     constexpr size_t kMwBytes = sizeof(float) * kChunk * MWP;
-    constexpr size_t kKaBytes = kKtBytes + kABytes > kMwBytes ? kKtBytes + kABytes : kMwBytes;
+    // One area, so that two workgroups fit on a CU (77 KB of LDS each): the
+    // KK / QK column operands, then X over them, with A after them; Kt after X
+    // once A is dead (after the inverse); M W over Kt once W is formed.
+    constexpr size_t kAOff = kZfBytes;
+    constexpr size_t kKtOff = (kXBytes + 15) / 16 * 16;
+    constexpr size_t kKtMw = kKtBytes > kMwBytes ? kKtBytes : kMwBytes;
+    constexpr size_t kAreaBytes =
+        kAOff + kABytes > kKtOff + kKtMw ? kAOff + kABytes : kKtOff + kKtMw;
+    static_assert(kXBytes <= kAOff, "X lies within the column operands' space");
     // decay tables per channel (exp of sums of block totals tau_a):
     //   EP_a = exp(sum_{a'<a} tau), EK_a = exp(sum_{a'>a} tau), IE_a = exp(-tau_a),
     //   TF(a,b) = exp(sum_{b<a'<a} tau) for a - b >= 2: (2,0), (3,0), (3,1)
@@ -116,16 +124,12 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
     __shared__ __align__(16) float tab_s[kTabs][kD];
     __shared__ float beta_s[kChunk];
     __shared__ float m_s[kChunk * SP];
-    // column operands of the decay-weighted products, later X = (I + A)^-1
-    // and T = X diag(beta)
-    __shared__ __align__(16) uint8_t zx_raw[kZfBytes > kXBytes ? kZfBytes : kXBytes];
-    // Kt and A, later reused for M W
-    __shared__ __align__(16) uint8_t ka_raw[kKaBytes];
-    F8(*zf_s)[4][64] = reinterpret_cast<F8(*)[4][64]>(zx_raw);
-    float* x_s = reinterpret_cast<float*>(zx_raw);
-    st* kt_s = reinterpret_cast<st*>(ka_raw);
-    float* a_s = reinterpret_cast<float*>(ka_raw + kKtBytes);
-    float* mw_s = reinterpret_cast<float*>(ka_raw);
+    __shared__ __align__(16) uint8_t area[kAreaBytes];
+    F8(*zf_s)[4][64] = reinterpret_cast<F8(*)[4][64]>(area);  // KK / QK column operands
+    float* x_s = reinterpret_cast<float*>(area);              // X, then T = X diag(beta)
+    float* a_s = reinterpret_cast<float*>(area + kAOff);      // diag(beta) strict-lower KK
+    st* kt_s = reinterpret_cast<st*>(area + kKtOff);          // Kt
+    float* mw_s = reinterpret_cast<float*>(area + kKtOff);    // M W
 
     // ---- load the lane's row: 32 channels of q, k, g -----------------------
     float qf[32], kf[32], lam[32];
@@ -217,7 +221,6 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
             *reinterpret_cast<float4*>(ek + 4) = *reinterpret_cast<const float4*>(&tab_s[kEK + wv][cb + 4]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) ta[e] = tau_s[wv][cb + e];
-            float kt8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 8 * s + e;
@@ -225,14 +228,10 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
                 const float z = fast_exp(ta[e] - lam[j]);
                 zc[j] = kf[j] * z;
                 KTg[(size_t)(cb + e) * kChunk + r] = kf[j] * z * ek[e];
-                kt8[e] = kf[j] * e0 * ep[e];
                 qtil[j] = qf[j] * e0 * ep[e];
                 kf[j] *= e0;  // rk0
                 qf[j] *= e0;  // rq0
             }
-            st* dst = kt_s + r * KTP + cb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e] = kt8[e];
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) zf_s[wv][s][lane] = P::pack8(zc + 8 * s);
@@ -329,6 +328,17 @@ __global__ __launch_bounds__(256, 1) void kda_chunk_prep_kernel(
         const float tv = (cc <= rr) ? x_s[rr * SP + cc] * beta_s[cc] : 0.f;
         x_s[rr * SP + cc] = tv;
         THg[idx] = tv;
+    }
+    // Kt = rk0 EP over the space of A, which the inverse no longer reads
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cb = 32 * s + 8 * gq;
+        float ep[8];
+        *reinterpret_cast<float4*>(ep) = *reinterpret_cast<const float4*>(&tab_s[kEP + wv][cb]);
+        *reinterpret_cast<float4*>(ep + 4) = *reinterpret_cast<const float4*>(&tab_s[kEP + wv][cb + 4]);
+        st* dst = kt_s + r * KTP + cb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = kf[8 * s + e] * ep[e];
     }
     __syncthreads();
 
