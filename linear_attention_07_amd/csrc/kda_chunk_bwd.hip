@@ -557,6 +557,25 @@ struct __align__(16) BwdLds {
 };
 static_assert(kPS <= kPB, "dX, then Y, fit in one [64][128] array");
 
+// The lane's 16 owned values of a [64][128] matrix (slot m: row 16 (m / 4) +
+// 4 gq + m % 4, channel 16 wv + n) into its hi / lo k32 fragments (rows token,
+// k channel; fragment 4 (row / 16) + channel / 32), one bf16 of each per value.
+__device__ __forceinline__ void stage_own(u32x4* hi, u32x4* lo, const float (&x)[16], int wv,
+                                          int n, int gq) {
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(hi);
+    uint16_t* l16 = reinterpret_cast<uint16_t*>(lo);
+    // within fragment wv / 2: lane slot (row % 16, (n / 4)), half wv % 2, value n % 4
+    const int base = 8 * (b16::kFragLanes * (wv >> 1) + 16 * (n >> 2)) + 4 * (wv & 1) + (n & 3);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int idx = base + 8 * (b16::kFragLanes * 4 * (m >> 2) + 4 * gq + (m & 3));
+        const __bf16 hb = (__bf16)x[m];
+        const __bf16 lb = (__bf16)(x[m] - (float)hb);
+        h16[idx] = __builtin_bit_cast(uint16_t, hb);
+        l16[idx] = __builtin_bit_cast(uint16_t, lb);
+    }
+}
+
 // acc += A B over one 4-deep step per component: four fp32 MFMAs
 __device__ __forceinline__ void mfma4(f32x4& acc, float4 a, float4 b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
@@ -602,9 +621,14 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     float* __restrict__ dbeta) {
     using RW = RawIO<IO>;
     __shared__ BwdLds s;
-    float(*const A0)[kPB] = s.big[0];  // kh, Kt, R, then dR
-    float(*const A1)[kPB] = s.big[1];  // qh, Kb, dU, then scale dO
-    float(*const A2)[kPB] = s.big[2];  // Gam, then U
+    // fp32 rows: kh, qh and Gam while P and N are formed
+    float(*const A0)[kPB] = s.big[0];
+    float(*const A1)[kPB] = s.big[1];
+    float(*const A2)[kPB] = s.big[2];
+    // then the same space as bf16 hi / lo k32 fragments (rows token, k channel):
+    // F0: -Kt, R, dR;  F1: Kb, dU, scale dO;  F2: U
+    auto fh = [&](int k) { return reinterpret_cast<u32x4*>(&s.big[k][0][0]); };
+    auto fl = [&](int k) { return reinterpret_cast<u32x4*>(&s.big[k][0][0]) + 16 * b16::kFragLanes; };
     float(*const DX)[kPS] = reinterpret_cast<float(*)[kPS]>(&s.big[0][0][0]);  // dX, then Y
 
     // chunk c of the segment (states, dS', X) is chunk cg of the sequence
@@ -767,15 +791,27 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         *reinterpret_cast<float4*>(&s.x[e >> 4][4 * (e & 15)]) = xpf[j];
     }
     __syncthreads();  // P and N are done with kh, qh and Gam
-    // -Kt = -e^Gam kh over kh and Kb = e^(GL - Gam) kh over qh, in 16-byte pieces
+    // -Kt = -e^Gam kh and Kb = e^(GL - Gam) kh, in 16-byte pieces, as hi / lo
+    // fragments over kh and qh (read first: the layouts differ)
+    {
+        float4 kt4[4], kb4[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid + kCT * j, r = e >> 5, c4 = 4 * (e & 31);
-        const float4 kh = ld4(&A0[r][c4]), gm = ld4(&A2[r][c4]), gl = ld4(&s.gl[c4]);
-        const float4 et = exp4(gm);
-        const float4 eb = exp4(make_float4(gl.x - gm.x, gl.y - gm.y, gl.z - gm.z, gl.w - gm.w));
-        *reinterpret_cast<float4*>(&A0[r][c4]) = scale4(mul4(et, kh), -1.f);
-        *reinterpret_cast<float4*>(&A1[r][c4]) = mul4(eb, kh);
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + kCT * j, r = e >> 5, c4 = 4 * (e & 31);
+            const float4 kh = ld4(&A0[r][c4]), gm = ld4(&A2[r][c4]), gl = ld4(&s.gl[c4]);
+            const float4 et = exp4(gm);
+            const float4 eb = exp4(make_float4(gl.x - gm.x, gl.y - gm.y, gl.z - gm.z, gl.w - gm.w));
+            kt4[j] = scale4(mul4(et, kh), -1.f);
+            kb4[j] = mul4(eb, kh);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + kCT * j, r = e >> 5, c4 = 4 * (e & 31);
+            const int f = 4 * (r >> 4) + (c4 >> 5);
+            b16::put_frag_hl(fh(0), fl(0), f, r & 15, (c4 >> 2) & 3, (c4 >> 4) & 1, kt4[j]);
+            b16::put_frag_hl(fh(1), fl(1), f, r & 15, (c4 >> 2) & 3, (c4 >> 4) & 1, kb4[j]);
+        }
     }
     __syncthreads();
 
@@ -791,16 +827,23 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             for (int e = 0; e < 4; ++e)
                 aR[u][e] = orow(4 * u + e) < L ? RW::wid(vraw[4 * u + e]) : 0.f;
         }
+        // -Kt S and Kb dS' on bf16 hi / lo pairs: k32 block sb takes the strip
+        // slots of 16-row blocks 2 sb and 2 sb + 1
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const float4 bs = make_float4(scol[4 * kb], scol[4 * kb + 1], scol[4 * kb + 2],
-                                          scol[4 * kb + 3]);
-            const float4 bd = make_float4(dcol[4 * kb], dcol[4 * kb + 1], dcol[4 * kb + 2],
-                                          dcol[4 * kb + 3]);
+        for (int sb = 0; sb < 4; ++sb) {
+            bf16x8 bsh, bsl, bdh, bdl;
+            split_b(f32x4{scol[8 * sb], scol[8 * sb + 1], scol[8 * sb + 2], scol[8 * sb + 3]},
+                    f32x4{scol[8 * sb + 4], scol[8 * sb + 5], scol[8 * sb + 6], scol[8 * sb + 7]},
+                    bsh, bsl);
+            split_b(f32x4{dcol[8 * sb], dcol[8 * sb + 1], dcol[8 * sb + 2], dcol[8 * sb + 3]},
+                    f32x4{dcol[8 * sb + 4], dcol[8 * sb + 5], dcol[8 * sb + 6], dcol[8 * sb + 7]},
+                    bdh, bdl);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                mfma4(aR[u], ld4(&A0[16 * u + n][16 * kb + 4 * gq]), bs);
-                mfma4(aU[u], ld4(&A1[16 * u + n][16 * kb + 4 * gq]), bd);
+                aR[u] = mma3(aR[u], b16::frag_at(fh(0), 4 * u + sb, lane),
+                             b16::frag_at(fl(0), 4 * u + sb, lane), bsh, bsl);
+                aU[u] = mma3(aU[u], b16::frag_at(fh(1), 4 * u + sb, lane),
+                             b16::frag_at(fl(1), 4 * u + sb, lane), bdh, bdl);
             }
         }
         // M^T: A(i, kk) = N[kk][i], zero for kk < i, so row tile u takes blocks kb >= u
@@ -867,15 +910,17 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
                           bd);
             }
         }
+        float Uo[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int r = orow(m);
             dRo[m] = s.beta[r] * aD[m >> 2][m & 3];
             if (r < L) io_st(dv + base + (size_t)r * rp + cc, dRo[m]);
-            A0[r][cc] = Ro[m];
-            A1[r][cc] = dUo[m];
-            A2[r][cc] = aX[m >> 2][m & 3];
+            Uo[m] = aX[m >> 2][m & 3];
         }
+        stage_own(fh(0), fl(0), Ro, wv, n, gq);
+        stage_own(fh(1), fl(1), dUo, wv, n, gq);
+        stage_own(fh(2), fl(2), Uo, wv, n, gq);
     }
     __syncthreads();  // R, dU and U are in LDS
 
@@ -886,11 +931,16 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     {
         f32x4 aT[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const float4 bR = ld4(&A0[16 * ct + n][16 * kb + 4 * gq]);
+        for (int sb = 0; sb < 4; ++sb) {
+            const bf16x8 rh = b16::frag_at(fh(0), 4 * ct + sb, lane);
+            const bf16x8 rl = b16::frag_at(fl(0), 4 * ct + sb, lane);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                if (rt0 + 2 * t >= ct) mfma4(aT[t], ld4(&A1[16 * (rt0 + 2 * t) + n][16 * kb + 4 * gq]), bR);
+            for (int t = 0; t < 2; ++t) {
+                const int rt = rt0 + 2 * t;
+                if (rt >= ct)
+                    aT[t] = mma3(aT[t], b16::frag_at(fh(1), 4 * rt + sb, lane),
+                                 b16::frag_at(fl(1), 4 * rt + sb, lane), rh, rl);
+            }
         }
         const int j = 16 * ct + n;
         float pb = 0.f;
@@ -912,10 +962,11 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) DX[16 * (rt0 + 2 * t) + 4 * gq + e][16 * ct + n] = dXo[4 * t + e];
+    {
+        float so[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int r = orow(m);
-        A1[r][cc] = r < L ? scale * RW::wid(oraw[m]) : 0.f;
+        for (int m = 0; m < 16; ++m) so[m] = orow(m) < L ? scale * RW::wid(oraw[m]) : 0.f;
+        stage_own(fh(1), fl(1), so, wv, n, gq);
     }
     if (tid < kChunk) s.dbeta[tid] = s.red[tid] + s.red[kChunk + tid];
     __syncthreads();  // dX and scale dO are in LDS
@@ -940,11 +991,16 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             }
         }
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const float4 bU = ld4(&A2[16 * ct + n][16 * kb + 4 * gq]);
+        for (int sb = 0; sb < 4; ++sb) {
+            const bf16x8 uh = b16::frag_at(fh(2), 4 * ct + sb, lane);
+            const bf16x8 ul = b16::frag_at(fl(2), 4 * ct + sb, lane);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                if (rt0 + 2 * t >= ct) mfma4(aM[t], ld4(&A1[16 * (rt0 + 2 * t) + n][16 * kb + 4 * gq]), bU);
+            for (int t = 0; t < 2; ++t) {
+                const int rt = rt0 + 2 * t;
+                if (rt >= ct)
+                    aM[t] = mma3(aM[t], b16::frag_at(fh(1), 4 * rt + sb, lane),
+                                 b16::frag_at(fl(1), 4 * rt + sb, lane), uh, ul);
+            }
         }
         // over N, whose last read was in dU
         const int j = 16 * ct + n;
@@ -992,8 +1048,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         }
     }
     __syncthreads();  // dA's reads of Y are done; dP, dM and the dbeta partials are in LDS
-#pragma unroll
-    for (int m = 0; m < 16; ++m) A0[orow(m)][cc] = dRo[m];
+    stage_own(fh(0), fl(0), dRo, wv, n, gq);
     if (tid < kChunk) {
         float a = s.dbeta[tid];
         for (int j = 0; j < 4; ++j) a += s.red[j * kChunk + tid];
@@ -1024,12 +1079,20 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) aQ[u] = aK[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
+        for (int sb = 0; sb < 4; ++sb) {
+            bf16x8 bh, bl;
+            split_b(f32x4{srow[2 * sb].x, srow[2 * sb].y, srow[2 * sb].z, srow[2 * sb].w},
+                    f32x4{srow[2 * sb + 1].x, srow[2 * sb + 1].y, srow[2 * sb + 1].z,
+                          srow[2 * sb + 1].w},
+                    bh, bl);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                mfma4(aQ[u], ld4(&A1[16 * u + n][16 * kb + 4 * gq]), srow[kb]);
-                mfma4(aK[u], ld4(&A0[16 * u + n][16 * kb + 4 * gq]), srow[kb]);
+                aQ[u] = mma3(aQ[u], b16::frag_at(fh(1), 4 * u + sb, lane),
+                             b16::frag_at(fl(1), 4 * u + sb, lane), bh, bl);
+                aK[u] = mma3(aK[u], b16::frag_at(fh(0), 4 * u + sb, lane),
+                             b16::frag_at(fl(0), 4 * u + sb, lane), bh, bl);
             }
+        }
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const float e = ex(gmo[m]), a = aQ[m >> 2][m & 3], bb = -aK[m >> 2][m & 3];
@@ -1043,9 +1106,17 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) aB[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
+        for (int sb = 0; sb < 4; ++sb) {
+            bf16x8 bh, bl;
+            split_b(f32x4{drow[2 * sb].x, drow[2 * sb].y, drow[2 * sb].z, drow[2 * sb].w},
+                    f32x4{drow[2 * sb + 1].x, drow[2 * sb + 1].y, drow[2 * sb + 1].z,
+                          drow[2 * sb + 1].w},
+                    bh, bl);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) mfma4(aB[u], ld4(&A2[16 * u + n][16 * kb + 4 * gq]), drow[kb]);
+            for (int u = 0; u < 4; ++u)
+                aB[u] = mma3(aB[u], b16::frag_at(fh(2), 4 * u + sb, lane),
+                             b16::frag_at(fl(2), 4 * u + sb, lane), bh, bl);
+        }
         const float glc = s.gl[cc];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
