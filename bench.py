@@ -414,7 +414,10 @@ def main():
                 "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "algorithmic_flop_per_call": pb_flop,
                 "traffic": measured_traffic("prefill_bwd_8k"), "algorithmic_bytes_per_call": nb,
-                "hbm_GBps_algorithmic": round(nb / (t[0] / 1e3) / 1e9, 1)}}
+                "hbm_GBps_algorithmic": round(nb / (t[0] / 1e3) / 1e9, 1),
+                "note": "algorithmic fp32 flops against the fp32 matrix peak; the scans' and "
+                        "the chunk kernel's [64][128] products run as three bf16 products of "
+                        "hi / lo pairs each (fp32-like accuracy), the rest on fp32 matrix cores"}}
         for key in ("q", "k", "v", "dout"):
             xb[key] = xb[key].to(torch.bfloat16)
         t = time_op(torch, prefill_bwd, nsteps, args.warmup)

@@ -103,3 +103,31 @@ def test_a_wait_that_gives_up_is_reported(debug):
     # the status words are cleared at the next call: a normal limit passes
     debug.delenv("KDA_DEBUG_SPIN_LIMIT")
     assert status_of(lambda: prefill(inp)) == libkda.KDA_OK
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_a_backward_scan_wait_that_gives_up_is_reported(debug, io):
+    """The backward's state and gradient scans hand each chunk from their loader
+    waves to their scan waves through bounded LDS waits too: with one poll per
+    wait the first unready one gives up, the kernels end, and the call reports
+    KDA_ERR_DEVICE; the next call with the normal limit passes."""
+    debug.setenv("KDA_DEBUG_SPIN_LIMIT", "1")
+    x = synth.prefill_inputs(1, 4096, 4, io, seed=68, h0_std=0.1, device=DEV)
+    dout = torch.randn((1, 4096, 4, 128), device=DEV).to(io)
+    run = lambda: libkda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"], dout,
+                                   h0=x["h0"])
+    say(f"debug: spin limit 1, backward T=4096 H=4 {io}")
+    assert status_of(run) == libkda.KDA_ERR_DEVICE
+    debug.delenv("KDA_DEBUG_SPIN_LIMIT")
+    assert status_of(run) == libkda.KDA_OK
+
+
+def test_an_fp32_scan_wait_that_gives_up_is_reported(debug):
+    """The fp32 prefill's scan (loader and scan waves, bounded LDS waits) reports
+    a wait that gives up the same way."""
+    debug.setenv("KDA_DEBUG_SPIN_LIMIT", "1")
+    inp = synth.prefill_inputs(1, 4096, 4, torch.float32, seed=69, h0_std=0.1, device=DEV)
+    say("debug: spin limit 1, fp32 prefill T=4096 H=4")
+    assert status_of(lambda: prefill(inp)) == libkda.KDA_ERR_DEVICE
+    debug.delenv("KDA_DEBUG_SPIN_LIMIT")
+    assert status_of(lambda: prefill(inp)) == libkda.KDA_OK
