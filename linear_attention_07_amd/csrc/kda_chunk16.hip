@@ -351,9 +351,20 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     // with a 0/1 selection matrix as B (value e of lane (j, gq) is 1 where
     // 8 gq + e = 16 h + j) returns lane (j, g) the tokens 16p + 4g .. +3 of
     // channel 32s + 16h + j, exactly: 8 bytes of Kb^T fragment (2s + h, p / 2).
+    // Lanes L and L + 32 (gq and gq + 2) hold the two 8-byte halves of the
+    // same 16-byte fragment slots, for the slot at +0 (values of k0 + 4g ..)
+    // and the one at +256 (k0 + 16 + 4g ..).  A swap of the upper 32 lanes of
+    // one register with the lower 32 of another hands lanes gq < 2 both halves
+    // of the +0 slot and lanes gq >= 2 both halves of the +256 slot, so that
+    // each lane stores one 16-byte piece.
+    auto store_pair = [](uint8_t* dst, const uint32_t (&w)[4]) {
+        const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto c = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        *reinterpret_cast<u32x4*>(dst) = u32x4{a[0], c[0], a[1], c[1]};
+    };
     float rk0[32], rq0[32];
     {
-        const size_t kq0 = (size_t)(16 * (2 * (gq & 1)) + n) * 16 + 8 * (gq >> 1);
+        const size_t kq0 = (size_t)(16 * (2 * (gq & 1)) + n) * 16 + 256 * (gq >> 1);
         uint8_t* ktg = rec + Rec16::KT + 4 * p * Rec16::kFrag + kq0;
         uint8_t* qtg = rec + Rec16::QT + 4 * p * Rec16::kFrag + kq0;
         uint8_t* kbg = rec + Rec16::KB + (p >> 1) * Rec16::kFrag + (n + 16 * gq) * 16 + 8 * (p & 1);
@@ -399,10 +410,8 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
                 qtw[w] = pack2(rq0[j] * ep[2 * w], rq0[j + 1] * ep[2 * w + 1]);
                 kbw[w] = pack2(zc[2 * w] * ek[2 * w], zc[2 * w + 1] * ek[2 * w + 1]);
             }
-            *reinterpret_cast<uint2*>(ktg + s * Rec16::kFrag) = uint2{ktw[0], ktw[1]};
-            *reinterpret_cast<uint2*>(ktg + s * Rec16::kFrag + 256) = uint2{ktw[2], ktw[3]};
-            *reinterpret_cast<uint2*>(qtg + s * Rec16::kFrag) = uint2{qtw[0], qtw[1]};
-            *reinterpret_cast<uint2*>(qtg + s * Rec16::kFrag + 256) = uint2{qtw[2], qtw[3]};
+            store_pair(ktg + s * Rec16::kFrag, ktw);
+            store_pair(qtg + s * Rec16::kFrag, qtw);
             zf_s[p][s][lane] = pack8(zc);
             const bf16x8 kbf = __builtin_bit_cast(bf16x8, u32x4{kbw[0], kbw[1], kbw[2], kbw[3]});
 #pragma unroll
@@ -506,27 +515,49 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
     // ---- the rest of the record -------------------------------------------------
     // T = X diag(beta) (zero above the diagonal) as hi / lo and M: row r,
     // columns 16ct + 4g .. +3 per lane, lower blocks (p, ct <= p) only: value
-    // half ct & 1 of lane (n, g) of fragment (p, ct / 2)
+    // half ct & 1 of lane (n, g) of fragment (p, ct / 2).  Column blocks 2cp
+    // and 2cp + 1 fill the two halves of a lane's 16 bytes of a full
+    // fragment, stored together; a half fragment (cp = p / 2 for even p) is
+    // 8 bytes per lane.
     {
         uint8_t* tm = rec + Rec16::TM;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            if (ct > p) continue;
-            const int f = p < 2 ? p : 2 + 2 * (p - 2) + (ct >> 1);
-            const size_t off = tm_off(f) + (tm_half(f) ? (size_t)lane * 8
-                                                       : (size_t)lane * 16 + 8 * (ct & 1));
-            uint2* th = reinterpret_cast<uint2*>(tm + 0 * Rec16::kTM + off);
-            uint2* tl = reinterpret_cast<uint2*>(tm + 1 * Rec16::kTM + off);
-            uint2* mh = reinterpret_cast<uint2*>(tm + 2 * Rec16::kTM + off);
-            float tv[4], mv[4];
+        for (int cp = 0; cp < 2; ++cp) {
+            if (2 * cp > p) continue;
+            const int f = p < 2 ? p : 2 + 2 * (p - 2) + cp;
+            const bool half = tm_half(f);
+            uint32_t th[4], tl[4], mh[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int col = 16 * ct + 4 * gq + e;
-                tv[e] = (col <= r) ? x_s[r * SP + col] * beta_s[col] : 0.f;
-                mv[e] = Mt[ct][e];
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ct = 2 * cp + hh;
+                if (hh == 1 && half) continue;
+                float tv[4], mv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = 16 * ct + 4 * gq + e;
+                    tv[e] = (col <= r) ? x_s[r * SP + col] * beta_s[col] : 0.f;
+                    mv[e] = Mt[ct][e];
+                }
+                uint2 h2, l2;
+                split4(tv, h2, l2);
+                th[2 * hh] = h2.x;
+                th[2 * hh + 1] = h2.y;
+                tl[2 * hh] = l2.x;
+                tl[2 * hh + 1] = l2.y;
+                mh[2 * hh] = pack2(mv[0], mv[1]);
+                mh[2 * hh + 1] = pack2(mv[2], mv[3]);
             }
-            split4(tv, *th, *tl);
-            *mh = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
+            if (half) {
+                const size_t off = tm_off(f) + (size_t)lane * 8;
+                *reinterpret_cast<uint2*>(tm + 0 * Rec16::kTM + off) = uint2{th[0], th[1]};
+                *reinterpret_cast<uint2*>(tm + 1 * Rec16::kTM + off) = uint2{tl[0], tl[1]};
+                *reinterpret_cast<uint2*>(tm + 2 * Rec16::kTM + off) = uint2{mh[0], mh[1]};
+            } else {
+                const size_t off = tm_off(f) + (size_t)lane * 16;
+                *reinterpret_cast<u32x4*>(tm + 0 * Rec16::kTM + off) = u32x4{th[0], th[1], th[2], th[3]};
+                *reinterpret_cast<u32x4*>(tm + 1 * Rec16::kTM + off) = u32x4{tl[0], tl[1], tl[2], tl[3]};
+                *reinterpret_cast<u32x4*>(tm + 2 * Rec16::kTM + off) = u32x4{mh[0], mh[1], mh[2], mh[3]};
+            }
         }
     }
     if (p == 0) {
