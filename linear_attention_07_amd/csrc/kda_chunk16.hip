@@ -197,6 +197,11 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
                   "column operands fit the shared area");
     bf16x8 (*zf_s)[4][64] = reinterpret_cast<bf16x8 (*)[4][64]>(u1_s);
     float* x_s = u1_s;
+    // Kb^T passes through a_s before a_s holds A: fragment f (1 KB) lies in
+    // the rows of wave f / 4 (16 rows of SP floats, 4,160 bytes each wave)
+    uint8_t* kb_stage = reinterpret_cast<uint8_t*>(a_s);
+    auto kb_stage_off = [](int f) { return 16 * SP * 4 * (f >> 2) + 1024 * (f & 3); };
+    static_assert(16 * SP * 4 >= 4 * 1024, "a wave's Kb^T fragments fit its rows of a_s");
 
     // Chunk-major order, XCD-aware: workgroups are dealt round-robin to the 8
     // XCDs, so the k-th workgroup of XCD x takes chunk k / (BH / 8) and head
@@ -367,7 +372,9 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
         const size_t kq0 = (size_t)(16 * (2 * (gq & 1)) + n) * 16 + 256 * (gq >> 1);
         uint8_t* ktg = rec + Rec16::KT + 4 * p * Rec16::kFrag + kq0;
         uint8_t* qtg = rec + Rec16::QT + 4 * p * Rec16::kFrag + kq0;
-        uint8_t* kbg = rec + Rec16::KB + (p >> 1) * Rec16::kFrag + (n + 16 * gq) * 16 + 8 * (p & 1);
+        // Kb^T halves go to LDS first (kb_stage); the workgroup barrier below
+        // completes every 16-byte slot
+        uint8_t* kbl = kb_stage + (n + 16 * gq) * 16 + 8 * (p & 1);
         bf16x8 sel[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -417,12 +424,21 @@ __global__ __launch_bounds__(256, 3) void kda_prep16_kernel(
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const f32x4 t = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kbf, sel[hh]);
-                *reinterpret_cast<uint2*>(kbg + 2 * (2 * s + hh) * Rec16::kFrag) =
+                *reinterpret_cast<uint2*>(kbl + kb_stage_off(2 * (2 * s + hh) + (p >> 1))) =
                     uint2{pack2(t[0], t[1]), pack2(t[2], t[3])};
             }
         }
     }
     __syncthreads();
+    // Kb^T fragments 4p .. 4p + 3 from the staging area (this wave's own rows
+    // of a_s, which it writes only at the end of the next phase) to the
+    // record, one 16-byte piece per lane each
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int fr = 4 * p + f;
+        *reinterpret_cast<u32x4*>(rec + Rec16::KB + fr * Rec16::kFrag + lane * 16) =
+            *reinterpret_cast<const u32x4*>(kb_stage + kb_stage_off(fr) + lane * 16);
+    }
 
     // ---- KK and QK blocks of row block p against column blocks cb <= p ---------
     // row factor exp(Gam_r - Gam_{16cb+15}) = e0 * f with f = IE_p (cb = p),
