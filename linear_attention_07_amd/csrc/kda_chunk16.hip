@@ -937,7 +937,9 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
             // S <- Diag(gamma) S + Kb^T U   (U as hi + lo)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) split_b(U[2 * s2], U[2 * s2 + 1], bh_[s2], bl_[s2]);
-            uint16_t* outc = out + ((int64_t)b * T * H + h) * kD + j0 + 4 * gq;
+            // after the swap below, lane (n, g) holds token 16 rt + n of tile
+            // rt = 2 pr + (g & 1) and the eight columns j0 + 8 (g / 2) ..
+            uint16_t* outc = out + ((int64_t)b * T * H + h) * kD + j0 + 8 * (gq >> 1);
             // Kb^T fragments of the first half of the state rows
             bf16x8 fkb[2][4][2];
 #pragma unroll
@@ -945,6 +947,7 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) fkb[0][t][s2] = frag(kb_s, 2 * t + s2, lane);
             __builtin_amdgcn_sched_barrier(0);
+            uint32_t ob[4][2];  // bf16 outputs per tile: columns 4g .. +1, +2 .. +3
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 o = Pq[rt];
@@ -955,12 +958,22 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
                     o = mma(o, bh_[s2], fmh[f]);
                     o = mma(o, bl_[s2], fmh[f]);
                 }
-                const int64_t tk = c0 + 16 * rt + n;
                 f32x4 y = scale * o;
                 if (gatec) y *= sg[rt];  // out = o * sigmoid(z)
+                ob[rt][0] = pack2(y[0], y[1]);
+                ob[rt][1] = pack2(y[2], y[3]);
+            }
+            // Tiles 2 pr and 2 pr + 1: a swap of the odd 16-lane rows of one
+            // register with the even rows of another hands the even rows (g =
+            // 0, 2) columns 8 (g / 2) .. +7 of the first tile and the odd rows
+            // the same columns of the second, one 16-byte store per lane.
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const auto a = __builtin_amdgcn_permlane16_swap(ob[2 * pr][0], ob[2 * pr + 1][0], false, false);
+                const auto c = __builtin_amdgcn_permlane16_swap(ob[2 * pr][1], ob[2 * pr + 1][1], false, false);
+                const int64_t tk = c0 + 16 * (2 * pr + (gq & 1)) + n;
                 if (tk < T)
-                    *reinterpret_cast<uint2*>(outc + tk * rstride) =
-                        uint2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+                    *reinterpret_cast<u32x4*>(outc + tk * rstride) = u32x4{a[0], c[0], a[1], c[1]};
             }
             signal(&sync_s[5], lane);  // the output is stored
 #pragma unroll
