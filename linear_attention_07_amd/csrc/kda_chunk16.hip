@@ -933,8 +933,8 @@ __global__ __launch_bounds__(512, 1) void kda_scan16_kernel(
 
             // O^T = (Qt S)^T + U^T M^T (U as hi + lo, M bf16), so that a lane
             // holds token 16rt + n and the four consecutive columns j0 + 4g ..
-            // +3 (one 8-byte store);
-            // S <- Diag(gamma) S + Kb^T U   (U as hi + lo)
+            // +3; then S <- Diag(gamma) S + Kb^T U (U as hi + lo).  This order
+            // (output, then state update) measured faster than the reverse.
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) split_b(U[2 * s2], U[2 * s2 + 1], bh_[s2], bl_[s2]);
             // after the swap below, lane (n, g) holds token 16 rt + n of tile
