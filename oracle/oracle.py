@@ -53,7 +53,13 @@ def _load():
         return _lib
     if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
-    lib = ctypes.CDLL(_LIB)
+    _lib = configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def configure(lib):
+    """Declares the C entry points' signatures on a loaded oracle library
+    (this one, or a copy built from a modified source by a test)."""
     dp = ctypes.POINTER(ctypes.c_double)
     lib.kda_oracle_run.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -65,7 +71,6 @@ def _load():
         dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_double, dp, dp, dp,
         dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.kda_oracle_seq_backward.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 
