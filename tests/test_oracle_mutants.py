@@ -3,7 +3,10 @@
 Each case plants one mistake in a copy of oracle/kda_oracle.c (a dropped term
 or factor, a wrong sign, a wrong operand, an off-by-one token, two steps in
 the wrong order), builds the copy with gcc and runs the pins of
-test_oracle_pins.py against it: at least one of them must fail.  The copy
+test_oracle_pins.py against it: at least one of them must fail.  The same is
+done for the Python side of the oracle (oracle/oracle.py: the short
+convolution, SiLU, the bf16 rounding, the output gate and the one-step
+backward), whose mutated copy is loaded as a module of its own.  The copy
 without a mistake passes all of them, so every failure comes from the planted
 mistake.  The forward mistakes follow the recurrence of the Kimi-K3 深度解析
 blog, section 三 (per-channel decay, prediction from the decayed state, the
@@ -14,6 +17,7 @@ its reverse-mode derivative.  Everything here runs on the CPU.
 import ctypes
 import os
 import subprocess
+import types
 
 import pytest
 
@@ -164,5 +168,91 @@ def test_pins_reject_a_planted_mistake(mutant, tmp_path, monkeypatch):
     bad = MUTANTS[mutant](src)
     assert bad != src
     failed = _failing_pins(_build(bad, tmp_path, "mutant"), monkeypatch)
+    print(f"{mutant}: caught by {failed}")
+    assert failed, f"no pin rejects the mistake '{mutant}'"
+
+
+# Mistakes in oracle/oracle.py (the same kinds), each against the pins that
+# use that part.
+PY_MUTANTS = {
+    "silu with the logistic of -x": lambda s: _nth(
+        s, "return x / (1.0 + np.exp(-x))", "return x / (1.0 + np.exp(x))"),
+    "bf16 rounding by truncation": lambda s: _nth(
+        s, "r = (bits + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)",
+        "r = bits & np.uint32(0xFFFF0000)"),
+    "bf16 rounding with ties down": lambda s: _nth(
+        s, "r = (bits + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)",
+        "r = (bits + np.uint32(0x7FFF)) & np.uint32(0xFFFF0000)"),
+    "conv taps in reverse order": lambda s: _nth(
+        s, "pre += w[None, None, :, :, j] * full[:, j:j + T]",
+        "pre += w[None, None, :, :, CONV_TAPS - 1 - j] * full[:, j:j + T]"),
+    "conv state ignored": lambda s: _nth(
+        s, "prev = np.zeros((B, CONV_TAPS - 1, H, D)) if state is None else _f64(state)",
+        "prev = np.zeros((B, CONV_TAPS - 1, H, D))"),
+    "conv state returned one token early": lambda s: _nth(
+        s, "np.ascontiguousarray(full[:, T:])", "np.ascontiguousarray(full[:, T - 1:T + 2])"),
+    "gate with the logistic of -z": lambda s: _nth(
+        s, "return _f64(o) / (1.0 + np.exp(-_f64(z)))", "return _f64(o) / (1.0 + np.exp(_f64(z)))"),
+    "step backward: dp with the wrong sign": lambda s: _nth(s, "dp = -bt * du", "dp = bt * du"),
+    "step backward: state gradient not decayed back": lambda s: _nth(
+        s, "dS_prev[b, h] = a[:, None] * dSt", "dS_prev[b, h] = dSt"),
+    "step backward: dg from the state before the decay": lambda s: _nth(
+        s, "dg[b, h] = np.sum(St * dSt, axis=1)", "dg[b, h] = np.sum(S_prev[b, h] * dSt, axis=1)"),
+    "step backward: dq without the norm's projection": lambda s: _nth(
+        s, "dq[b, h] = rq * dqh - rq ** 3 * (q[b, h] @ dqh) * q[b, h]", "dq[b, h] = rq * dqh"),
+    "step backward: dk misses the prediction's term": lambda s: _nth(
+        s, "dkh += St @ dp", "dkh += 0.0 * (St @ dp)"),
+    "step backward: read-out gradient without the scale": lambda s: _nth(
+        s, "G = dS_next[b, h] + scale * np.outer(qh, d_o[b, h])",
+        "G = dS_next[b, h] + np.outer(qh, d_o[b, h])"),
+}
+
+PY_PINS = {
+    "silu values": pins.test_silu_textbook_values,
+    "conv impulse response": pins.test_short_conv_impulse_response,
+    "conv state and split": pins.test_short_conv_state_and_split,
+    "decode conv steps": pins.test_decode_conv_steps_match_forward_conv,
+    "bf16 rounding vs torch": pins.test_round_bf16_matches_torch_conversion,
+    "rounded conv output": pins.test_short_conv_rounded_output_is_the_bf16_of_the_exact_output,
+    "gate values": pins.test_output_gate_values,
+    "gated conv": pins.test_gated_conv_forward_and_steps,
+    "step backward vs finite differences": pins.test_step_backward_against_finite_differences,
+    "step backward chained vs sequence gradient": pins.test_step_backward_chains_to_the_sequence_gradient,
+    "sequence backward vs chained step backward": pins.test_sequence_backward_equals_chained_step_backward,
+}
+
+
+def _py_module(src_text):
+    """The oracle module built from src_text; it loads the same C library."""
+    mod = types.ModuleType("oracle_copy")
+    mod.__file__ = oracle.__file__
+    exec(compile(src_text, oracle.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+def _failing_py_pins(mod, monkeypatch):
+    monkeypatch.setattr(pins, "oracle", mod)
+    failed = []
+    for name, pin in PY_PINS.items():
+        try:
+            pin()
+        except Exception:  # an assertion, or a numerical error from the mistake
+            failed.append(name)
+    return failed
+
+
+def test_python_pins_pass_on_an_unmodified_copy(monkeypatch):
+    with open(oracle.__file__) as f:
+        src = f.read()
+    assert _failing_py_pins(_py_module(src), monkeypatch) == []
+
+
+@pytest.mark.parametrize("mutant", list(PY_MUTANTS))
+def test_python_pins_reject_a_planted_mistake(mutant, monkeypatch):
+    with open(oracle.__file__) as f:
+        src = f.read()
+    bad = PY_MUTANTS[mutant](src)
+    assert bad != src
+    failed = _failing_py_pins(_py_module(bad), monkeypatch)
     print(f"{mutant}: caught by {failed}")
     assert failed, f"no pin rejects the mistake '{mutant}'"
