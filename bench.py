@@ -72,7 +72,7 @@ BWD_CHUNK_BF16_BYTES_PER_TOKEN_HEAD = 7 * 128 * 2 + 2 * 128 * 4 + 2 * 4
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="timed decode steps (default: the workload's 64 consecutive "
