@@ -191,8 +191,12 @@ KDA_API kda_status_t kda_chunk_fwd_conv(const uint16_t *q, const uint16_t *k, co
                                 float *hT, int B, int T, int H, hipStream_t stream);
 
 /*
- * kda_chunk_fwd_f32 — as kda_chunk_fwd, with fp32 q, k, v and out and fp32
- * matrix-core products throughout (the fp32-input accuracy mode).
+ * kda_chunk_fwd_f32 — as kda_chunk_fwd, with fp32 q, k, v and out (the
+ * fp32-input accuracy mode).  Prep works in fp32 throughout, the inverse
+ * included; the scan's products take each fp32 factor as a bf16 hi + lo pair
+ * (three products per pair, fp32 accumulation, about 1e-5 relative per
+ * product) and carry the state in fp32.  Measured against an fp64 reference:
+ * normalised max errors about 1.5e-5 on outputs and 2e-5 on the final state.
  */
 KDA_API kda_status_t kda_chunk_fwd_f32(const float *q, const float *k, const float *v,
                                const float *g, const float *beta, float scale,

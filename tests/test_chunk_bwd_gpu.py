@@ -205,6 +205,13 @@ def test_chunk_bwd_segmented_workspace(io, monkeypatch):
     assert torch.isfinite(r[5]).all()
 
 
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_chunk_bwd_batched_heads(io):
+    """B=2, H=8: B*H a multiple of 8, so both state scans take their XCD-aware
+    workgroup order across two batch entries; ragged T=150."""
+    check(inputs(2, 150, 8, seed=993, io=io), f"{io} B=2 T=150 H=8")
+
+
 def test_chunk_bwd_64k_in_a_fixed_budget():
     """64K tokens x 96 heads (1024 chunks; about 27 GB of workspace in one
     segment) inside the default 8 GB budget: four segments.  Two heads checked

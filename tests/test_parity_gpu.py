@@ -135,6 +135,22 @@ def test_chunk_batched_heads_segments(workspace_mb, monkeypatch):
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+@pytest.mark.parametrize("workspace_mb", [None, 2])
+def test_chunk_f32_batched_heads_segments(workspace_mb, monkeypatch):
+    """The fp32-I/O prefill with B=2, H=8 (B*H a multiple of 8: the fp32
+    scan's XCD-aware workgroup order, with two batch entries), ragged T=300,
+    nonzero initial state; in one workspace segment and in small segments."""
+    if workspace_mb is not None:
+        monkeypatch.setenv("KDA_WORKSPACE_MB", str(workspace_mb))
+    B, T, H = 2, 300, 8
+    inp = synth.prefill_inputs(B, T, H, torch.float32, seed=79, h0_std=0.1, device=DEV)
+    o_ref, h_ref = oracle_prefill(inp)
+    out, hT = _run_chunk(inp)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    say(f"fp32 B={B} H={H} T={T} workspace={workspace_mb}: out err {eo:.2e} state err {es:.2e}")
+    assert eo <= TOL_F32 and es <= TOL_F32
+
+
 def test_chunk_more_scan_workgroups_than_cus():
     """B=3, H=96: 576 scan workgroups (one per head and 64-column slice), more
     than the chip's 256 CUs hold at once, so they run in rounds; 3 x 96 x 4
