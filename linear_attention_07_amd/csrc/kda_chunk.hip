@@ -369,9 +369,11 @@ __global__ __launch_bounds__(256, 2) void kda_chunk_prep_kernel(
         }
     }
 
-    // ---- MT = M T, row block wv -------------------------------------------
+    // ---- MT = M T, row block wv (for the forward scan only: the backward,
+    // which asks for X, reads no MT) ------------------------------------------
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
+        if (x_out) break;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int kb = ct; kb <= wv; ++kb) {
             f32x4 ma, tb;
