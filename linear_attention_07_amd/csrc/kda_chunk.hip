@@ -271,11 +271,34 @@ __global__ __launch_bounds__(256, 2) void kda_chunk_prep_kernel(
             const int ri = 16 * wv + 4 * gq + e, ci = 16 * cb + n;
             const bool strict = (cb < wv) || (ci < ri);
             const bool incl = (cb < wv) || (ci <= ri);
-            a_s[ri * SP + ci] = strict ? beta_s[ri] * accK[e] : 0.f;
+            a_s[ri * SP + ci] = strict ? (x_out ? accK[e] : beta_s[ri] * accK[e]) : 0.f;
             m_s[ri * SP + ci] = incl ? accQ[e] : 0.f;
         }
     }
     __syncthreads();
+    if (x_out) {
+        // P = strict-lower(KK) and N = M, whole [64][64] (zero above the
+        // diagonal blocks), after X in the chunk's slot; then A = diag(beta) P
+        float* pg = x_out + (((size_t)bh * nchunks + cl) * 3 + 1) * kChunk * kChunk;
+        float* ng = pg + kChunk * kChunk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + 256 * j, rr = e >> 4, c4 = 4 * (e & 15);
+            const bool low = (c4 >> 4) <= (rr >> 4);
+            float pa[4], na[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pa[u] = low ? a_s[rr * SP + c4 + u] : 0.f;
+                na[u] = low ? m_s[rr * SP + c4 + u] : 0.f;
+            }
+            *reinterpret_cast<float4*>(pg + rr * kChunk + c4) = make_float4(pa[0], pa[1], pa[2], pa[3]);
+            *reinterpret_cast<float4*>(ng + rr * kChunk + c4) = make_float4(na[0], na[1], na[2], na[3]);
+            const float bt = beta_s[rr];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a_s[rr * SP + c4 + u] = pa[u] * bt;
+        }
+        __syncthreads();
+    }
 
     // ---- X = (I + A)^-1: diagonal blocks by forward substitution (fp32) ----
     {
@@ -321,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void kda_chunk_prep_kernel(
         __syncthreads();
     }
     // T = X diag(beta), zero above the diagonal (and X itself, if asked for)
-    float* xg = x_out ? x_out + ((size_t)bh * nchunks + cl) * kChunk * kChunk : nullptr;
+    float* xg = x_out ? x_out + ((size_t)bh * nchunks + cl) * 3 * kChunk * kChunk : nullptr;
     for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
         const int rr = idx >> 6, cc = idx & 63;
         if (xg) xg[idx] = (cc <= rr) ? x_s[rr * SP + cc] : 0.f;

@@ -26,15 +26,19 @@
 // gradients of a chunk follow from S and dS' alone, in parallel over chunks.
 //
 // Four launches:
-//   prep  (kda_chunk.hip) writes each chunk's record (W, Q', Kb^T, T, M T,
-//         gamma) and X = (I + A)^-1;
+//   prep  (kda_chunk.hip) writes each chunk's record (W, Q', Kb^T, T and
+//         gamma; no M T, which only the forward scan reads), X = (I + A)^-1,
+//         P = strict-lower(KK) and N = M;
 //   state scan    walks the chunks forward and stores the state entering each;
 //   gradient scan walks them in reverse and stores dS' of each chunk, and dS
 //         of the first as the initial state's gradient;
 //   chunk gradients, one workgroup per (batch, head, chunk), rebuilds the
-//         chunk's matrices from q, k, g, beta and writes dq, dk, dv, dg, dbeta.
-// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
-// its operands in LDS or registers.
+//         decay factors and the chunk's [64][128] matrices from q, k, g, beta,
+//         takes X, P and N from prep, and writes dq, dk, dv, dg, dbeta.
+// Every product runs on the matrix cores with its operands in LDS or
+// registers: the scans' products and the chunk kernel's [64][128] ones as
+// three bf16 products per hi / lo pair, the chunk kernel's [64][64] ones in
+// fp32 (v_mfma_f32_16x16x4_f32).
 #include "kda_bf16.hpp"
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void kda_bwd_grad_scan_kernel(
 // 16 columns, or its 16 rows, of S and dS') are loaded into registers one
 // phase before they are used.
 //
-// LDS: three [64][132] arrays (kh, qh and Gam while P and N are formed, then
+// LDS: three [64][132] arrays (kh, qh and Gam, then
 // Kt and Kb for R and dU, then R, dU and U, then scale dO, dX / Y and dR), P,
 // N and X at a pitch of 68 (16-byte rows that a wave reads in 8 distinct bank
 // groups), and a few vectors.  Partial sums are reduced in a fixed order, so
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     float* __restrict__ dbeta) {
     using RW = RawIO<IO>;
     __shared__ BwdLds s;
-    // fp32 rows: kh, qh and Gam while P and N are formed
+    // fp32 rows: kh, qh and Gam
     float(*const A0)[kPB] = s.big[0];
     float(*const A1)[kPB] = s.big[1];
     float(*const A2)[kPB] = s.big[2];
@@ -648,11 +652,12 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
     auto orow = [&](int m) { return 16 * (m >> 2) + 4 * gq + (m & 3); };
     auto crow = [&](int r) { return min(r, L - 1); };
 
-    // ---- loads: q, k, g (8 threads per row, 16 channels each), then X and the
-    // column strips of S and dS' (B operands of R and dU), v and dout
+    // ---- loads: q, k, g (8 threads per row, 16 channels each), X, P and N
+    // (into LDS at once), then the column strips of S and dS' (B operands of R
+    // and dU), v and dout
     float scol[32], dcol[32];  // S, dS' at [16 kb + 4 gq + e][cc], slot 4 kb + e
     typename RW::one vraw[16], oraw[16];
-    float4 xpf[2];
+    float4 xpf[2], pnf[4];
     {
         const int r = tid >> 3, part = tid & 7;
         typename RW::four qr[4], kr[4];
@@ -665,11 +670,13 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             gv[e] = ld4(g + off);
         }
         const float bt = beta[((size_t)b * T + (size_t)cg * kChunk + crow(r)) * H + h];
-        const float* Xg = xs + (size_t)blockIdx.x * kChunk * kChunk;
+        const float* Xg = xs + (size_t)blockIdx.x * 3 * kChunk * kChunk;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int e = tid + kCT * j;
             xpf[j] = ld4(Xg + (e >> 4) * kChunk + 4 * (e & 15));
+            pnf[j] = ld4(Xg + kChunk * kChunk + (e >> 4) * kChunk + 4 * (e & 15));
+            pnf[2 + j] = ld4(Xg + 2 * kChunk * kChunk + (e >> 4) * kChunk + 4 * (e & 15));
         }
 #pragma unroll
         for (int t = 0; t < 32; ++t)
@@ -705,6 +712,14 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             s.rk[r] = rk;
             s.beta[r] = ok ? bt : 0.f;
         }
+        // X, P and N as prep wrote them (P and N zero above their diagonal blocks)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + kCT * j;
+            *reinterpret_cast<float4*>(&s.x[e >> 4][4 * (e & 15)]) = xpf[j];
+            *reinterpret_cast<float4*>(&s.p[e >> 4][4 * (e & 15)]) = pnf[j];
+            *reinterpret_cast<float4*>(&s.n[e >> 4][4 * (e & 15)]) = pnf[2 + j];
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 32; ++t)
@@ -734,48 +749,9 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
             A2[16 * qq + r][ch] = pre;
         }
         if (qq == 3) s.gl[ch] = pre;
-        // the tiles of P and N above the diagonal blocks are zero
-        for (int idx = tid; idx < kChunk * kChunk; idx += kCT) {
-            const int i = idx >> 6, j = idx & 63;
-            if (j >= 16 * ((i >> 4) + 1)) {
-                s.p[i][j] = 0.f;
-                s.n[i][j] = 0.f;
-            }
-        }
     }
     __syncthreads();
 
-    // ---- P (strict lower) and N (lower incl) on the matrix cores -------------
-    // For column block cb (i in 16 cb .. 16 cb + 15, reference row e = 16 cb +
-    // 15) and rows r >= 16 cb: exp(Gam_r - Gam_i) = exp(Gam_r - Gam_e) exp(Gam_e -
-    // Gam_i), both factors within exp(+-75) for g >= -5, so
-    //   P_ri = sum_c (kh_rc exp(Gam_rc - Gam_ec)) (kh_ic exp(Gam_ec - Gam_ic)),
-    // N likewise with qh_r.
-    for (int t = wv; t < 10; t += kCT / 64) {  // the 10 tiles (rt, cb), rt >= cb
-        int cb = 0, rem = t;
-        while (rem >= 4 - cb) {
-            rem -= 4 - cb;
-            ++cb;
-        }
-        const int rt = cb + rem;
-        const int r = 16 * rt + n, i = 16 * cb + n, e = 16 * cb + 15;
-        f32x4 accp = {0.f, 0.f, 0.f, 0.f}, accn = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < kD; k0 += 16) {
-            const int col = k0 + 4 * gq;
-            const float4 gr = ld4(&A2[r][col]), ge = ld4(&A2[e][col]), gi = ld4(&A2[i][col]);
-            const float4 f = exp4(make_float4(gr.x - ge.x, gr.y - ge.y, gr.z - ge.z, gr.w - ge.w));
-            const float4 hh = exp4(make_float4(ge.x - gi.x, ge.y - gi.y, ge.z - gi.z, ge.w - gi.w));
-            const float4 bk = mul4(ld4(&A0[i][col]), hh);
-            mfma4(accp, mul4(ld4(&A0[r][col]), f), bk);
-            mfma4(accn, mul4(ld4(&A1[r][col]), f), bk);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 16 * rt + 4 * gq + u, col = 16 * cb + n;
-            s.p[row][col] = col < row ? accp[u] : 0.f;
-            s.n[row][col] = col <= row ? accn[u] : 0.f;
-        }
-    }
     // the lane's own kh, qh and Gam, kept in registers to the end
     float gmo[16], kho[16], qho[16];
 #pragma unroll
@@ -785,12 +761,6 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
         kho[m] = A0[r][cc];
         qho[m] = A1[r][cc];
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = tid + kCT * j;
-        *reinterpret_cast<float4*>(&s.x[e >> 4][4 * (e & 15)]) = xpf[j];
-    }
-    __syncthreads();  // P and N are done with kh, qh and Gam
     // -Kt = -e^Gam kh and Kb = e^(GL - Gam) kh, in 16-byte pieces, as hi / lo
     // fragments over kh and qh (read first: the layouts differ)
     {
@@ -1271,12 +1241,12 @@ __global__ __launch_bounds__(kCT, 1) void kda_bwd_chunk_kernel(
 
 size_t chunk_bwd_segment_bytes_per_chunk(int B, int H) {
     return (size_t)B * H *
-           (RF::BYTES + (2 * kStateFloats + (size_t)kChunk * kChunk) * sizeof(float));
+           (RF::BYTES + (2 * kStateFloats + (size_t)3 * kChunk * kChunk) * sizeof(float));
 }
 
 namespace {
 // Workspace of a segment of nch chunks: records, then the states entering the
-// chunks, the state gradients leaving them and X.
+// chunks, the state gradients leaving them, and X, P and N of each chunk.
 struct SegWs {
     uint8_t* rec;
     float *states, *dsn, *xs;

@@ -32,8 +32,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 // of chunks [chunk0, chunk0 + nchunks) into ws, from q, k, g, beta; scan walks
 // them in order, reading v, the records and h_in (NULL = zero state), and
 // writes out and, if h_out is not NULL, the final state.  x_out (or NULL)
-// receives X = (I + A)^-1 of every chunk, [64][64] fp32 each, zero above the
-// diagonal, in record order.
+// receives three [64][64] fp32 matrices per chunk, in record order: X = (I +
+// A)^-1 (zero above the diagonal), P = strict-lower(KK) and N = M =
+// lower-incl(QK) (zero above their diagonal blocks); prep then forms no M T.
 size_t chunk_f32_record_bytes();
 int chunk_f32_slices();
 // Byte offsets inside one fp32 record (64-token chunks, 128 channels).
