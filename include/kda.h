@@ -321,9 +321,9 @@ KDA_API kda_status_t kda_recurrent_step_bwd(const uint16_t *q, const uint16_t *k
  * 16-byte aligned (beta, dbeta 4).  B == 0 or H == 0 is a no-op; T == 0
  * copies dhT (or zeros) to dh0.  Workspace comes from the library's
  * stream-ordered pool (KDA_ERR_NO_MEMORY if it cannot be had) and is bounded
- * by the budget, not by T: the chunk records, the state entering and the
- * state gradient leaving every chunk (about 279 KB per 64 tokens and head)
- * are held for one segment of chunks at a time.  With more
+ * by the budget, not by T: the chunk records, three 64 x 64 matrices, the
+ * state entering and the state gradient leaving every chunk (about 305 KB per
+ * 64 tokens and head) are held for one segment of chunks at a time.  With more
  * than one segment, a forward pass first keeps the state entering each
  * segment (64 KB per segment and head), and the segments are then
  * differentiated last to first, each recomputing its states from its
@@ -356,7 +356,7 @@ KDA_API kda_status_t kda_chunk_bwd(const uint16_t *q, const uint16_t *k, const u
 /*
  * kda_trim_workspace — hands back to the driver the device memory that the
  * library's workspace pools keep cached between calls (one pool per device;
- * a 64K-token prefill keeps about 4 GB, an 8K-token backward about 5 GB).
+ * a 64K-token prefill keeps about 4 GB, an 8K-token backward about 4 GB).
  * Call it when no work of this library is in flight (after synchronising the
  * streams it ran on); memory still in use is not touched.  Returns KDA_OK, or
  * KDA_ERR_HIP.  Not needed before exit.
