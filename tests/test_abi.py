@@ -106,6 +106,16 @@ def test_chunk_empty_is_a_no_op(lib, fn):
     assert chunk(lib, fn, T=0, h0=P[7], hT=P[7]) == libkda.KDA_OK
 
 
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_fwd_f32", "kda_chunk_fwd_g16"])
+def test_chunk_refuses_more_scan_workgroups_than_a_launch_takes(lib, fn):
+    # two value slices per head: past 2^23 scan workgroups the call is refused
+    # before any HIP call (buffers far apart, so no overlap check trips first)
+    far = [ctypes.c_void_p((i + 1) << 44) for i in range(6)]
+    H = (1 << 22) + 1
+    assert chunk(lib, fn, q=far[0], k=far[1], v=far[2], g=far[3], beta=far[4], out=far[5],
+                 H=H) == libkda.KDA_ERR_UNSUPPORTED
+
+
 def conv(lib, q=P[0], k=P[1], v=P[2], wq=P[8], wk=P[9], wv=P[10], conv_in=NULL, conv_out=NULL,
          g=P[3], beta=P[4], scale=1.0, h0=NULL, gate=NULL, out=P[5], hT=NULL, B=1, T=4, H=1):
     return lib.kda_chunk_fwd_conv(q, k, v, wq, wk, wv, conv_in, conv_out, g, beta, scale, h0, gate,
