@@ -133,11 +133,12 @@ def workload_inputs(w: Workload, device="cuda"):
     return prefill_inputs(w.B, w.T, w.H, w.io, w.seed, w.g_shift, w.h0_std, device)
 
 
-def conv_inputs(B, T, H, seed=0, with_state=True, h0_std=0.1, device="cuda"):
+def conv_inputs(B, T, H, seed=0, with_state=True, h0_std=0.1, device="cuda", g_shift=4.0):
     """Inputs of the attention with its short convolution: raw q, k, v
     [B, T, H, 128] bf16; wq, wk, wv [H, 128, 4] fp32; conv_in
     [3, B, 3, H, 128] bf16 or None; g, beta, h0, scale as prefill_inputs."""
-    inp = prefill_inputs(B, T, H, torch.bfloat16, seed, h0_std=h0_std, device=device)
+    inp = prefill_inputs(B, T, H, torch.bfloat16, seed, g_shift=g_shift, h0_std=h0_std,
+                         device=device)
     dev = torch.device(device)
     gen = _gen(dev, 7_919 * (int(seed) + 1) + 17)
     shp = (B, T, H, HEAD_DIM)

@@ -9,6 +9,12 @@ one-chunk segments.
 
   forward : kda_chunk_fwd (bf16), kda_chunk_fwd_g16 (g in bf16) and
             kda_chunk_fwd_f32 (fp32 I/O) against the oracle's recurrence;
+  layer   : kda_chunk_fwd_conv (short convolution in front, with or without
+            the output gate and a carried conv state) against the oracle with
+            the filtered q, k, v rounded to bf16, as the layer defines them (the
+            error against the plain fp64 filter is printed beside it; fixed
+            cases in test_conv_gpu hold that one to the bar); the conv state
+            out bit-exact;
   backward: kda_chunk_bwd_f32 and kda_chunk_bwd (bf16 I/O) against the
             oracle's token-by-token reverse of the recurrence.
 
@@ -22,6 +28,7 @@ from kda_check import TOL_BF16, TOL_F32, host64, oracle_prefill, rel_out, rel_st
 from linear_attention_07_amd import libkda, synth
 from test_chunk_bwd_gpu import NAMES, gpu as bwd_gpu, inputs as bwd_inputs, ref as bwd_ref
 from test_chunk_bwd_gpu import rel, tol as bwd_tol
+from test_conv_gpu import oracle_conv, run as conv_run
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -38,6 +45,7 @@ def _draws(n, seed):
 
 FWD = _draws(12, 20261203)
 BWD = _draws(8, 20261204)
+CONV = _draws(8, 20261205)
 
 
 @pytest.mark.parametrize("mode", ["bf16", "g16", "f32"])
@@ -80,3 +88,25 @@ def test_chunk_bwd_random_shapes(case, io, monkeypatch):
         assert torch.isfinite(a.float()).all(), n
     for n, e in errs.items():
         assert e <= bwd_tol(n, io), (n, e)
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+@pytest.mark.parametrize("case", CONV, ids=[f"c{i}" for i in range(len(CONV))])
+def test_chunk_fwd_conv_random_shapes(case, gated, monkeypatch):
+    say(f"layer gated={gated} {case}")
+    if case["small_segments"]:
+        monkeypatch.setenv("KDA_WORKSPACE_MB", "1")  # one chunk per segment
+    inp = synth.conv_inputs(case["B"], case["T"], case["H"], seed=case["seed"],
+                            with_state=case["state"], h0_std=0.1 if case["state"] else 0.0,
+                            device=DEV, g_shift=case["g_shift"])
+    z = (synth.gate_logits((case["B"], case["T"], case["H"], 128), seed=case["seed"] + 1,
+                           device=DEV) if gated else None)
+    out, hT, cout = conv_run(inp, gate=z)
+    o_ref, h_ref, c_ref = oracle_conv(inp, gate=z, rounded=True)
+    eo, es = rel_out(host64(out), o_ref), rel_state(host64(hT), h_ref)
+    u_ref, uh_ref, _ = oracle_conv(inp, gate=z, rounded=False)
+    eu, eus = rel_out(host64(out), u_ref), rel_state(host64(hT), uh_ref)
+    say(f"  out err {eo:.2e} state err {es:.2e} (plain fp64 filter: {eu:.2e} / {eus:.2e})")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for i in range(3):
+        assert np.array_equal(host64(cout[i]), c_ref[i]), i
