@@ -55,11 +55,12 @@ GATE_BYTES_PER_TOKEN_HEAD = 128 * 2
 BWD_STEP_BYTES_PER_SEQ_HEAD = 3 * STATE_BYTES + 9 * 128 * 4 + 2 * 4
 # backward of the fp32 chunked prefill (kda_chunk_bwd_f32), algorithmic work
 # per 64-token chunk and head, in units of one 64x64x128 product (MACs):
-# record prep 4.5 (W, the two decayed key products, M W, M T); state scan 5
+# record prep 4 (W, the two decayed key products P and N, M W); state scan 5
 # (T V - W S, Kb^T Z); gradient scan 6 (Kb dS', W^T Y + Q'^T dO); chunk
-# gradients 22 (P and N 2, R 2, U 1, dU 3, dR 1, dT 1, dM 1, X^T dX and
-# its product with X^T 1, dQt dKt dKb 6, the pairwise-decay terms 4)
-BWD_CHUNK_FLOP_PER_CHUNK_HEAD = int(2 * 37.5 * 64 * 64 * 128)
+# gradients 20 (R 2, U 1, dU 3, dR 1, dT 1, dM 1, X^T dX and its product
+# with X^T 1, dQt dKt dKb 6, the pairwise-decay terms 4).  P and N count
+# once: the chunk gradients read them from prep.
+BWD_CHUNK_FLOP_PER_CHUNK_HEAD = int(2 * 35 * 64 * 64 * 128)
 # its algorithmic HBM bytes per token-head: q, k, v, g, dout read and dq, dk,
 # dv, dg written (fp32), beta read and dbeta written; per head h0 and dhT
 # read, dh0 written
